@@ -1,0 +1,232 @@
+"""Byte layouts of the quantized cache, written out plainly for the oracle.
+
+Test infrastructure: see the package docstring.
+
+The pages fix no byte layout (the TurboQuant page's bit format in section 3.3
+is garbled), so the layout is this library's own contract.  It is stated
+here, independently of the HIP code, and pinned by tests on hand-built
+examples.  Head dimension d = 128.
+
+Segment packing -- 32 codes u = 8*m + e (block m = 0..3, element e = 0..7)
+into 4*bits bytes:
+
+* 8-bit: byte u holds code u (two's complement for q8_0).
+* 4-bit: byte j holds code 2j in its low nibble and code 2j+1 in its high
+  nibble (so the little-endian dword m holds block m, element e at bits 4e).
+* 3-bit: three little-endian dwords D0, D1, D2.  For block m and r = 0..3
+  the pair (u_a, u_b) = (8m + r, 8m + r + 4) is stored as: the low two bits
+  of u_a at bit 2p and of u_b at bit 16 + 2p of D[m // 2], where
+  p = 4 * (m % 2) + r; the high bit of u_a at bit P and of u_b at bit 16 + P
+  of D2, where P = 4m + r.
+
+Key rows ("K-row" layout): every token has a row of 16*bits bytes made of 4
+segments q = 0..3; segment q holds channels c = 32m + 8q + e.
+
+Value tiles ("V-tile" layout): tokens are grouped in tiles of 32.  A tile is
+64 "lanes" L = 16q + i of 8*bits bytes each (two segments s = 0, 1).  In lane
+L, segment s, block m holds channel 16*(4s + m) + i; element e of that block
+is token 4q + e (e < 4) or 16 + 4q + (e - 4) (e >= 4) of the tile.
+
+Capacity: the cache holds Tcap = round_up(max_ctx, 32) tokens per sequence.
+"""
+from __future__ import annotations
+
+from typing import Dict
+
+import numpy as np
+
+D = 128
+
+
+def round_up(x: int, m: int) -> int:
+    return (x + m - 1) // m * m
+
+
+def capacity(max_ctx: int) -> int:
+    return round_up(max_ctx, 32)
+
+
+def row_bytes(bits: int) -> int:
+    return D * bits // 8
+
+
+def pack_segment(codes: np.ndarray, bits: int) -> np.ndarray:
+    """codes [..., 32] (ints, already reduced to ``bits`` bits) -> bytes [..., 4*bits]."""
+    c = np.asarray(codes).astype(np.int64) & ((1 << bits) - 1)
+    lead = c.shape[:-1]
+    if bits == 8:
+        return c.astype(np.uint8)
+    if bits == 4:
+        return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+    if bits == 3:
+        dw = np.zeros(lead + (3,), dtype=np.int64)
+        for m in range(4):
+            for r in range(4):
+                ua, ub = 8 * m + r, 8 * m + r + 4
+                p = 4 * (m % 2) + r
+                P = 4 * m + r
+                dw[..., m // 2] |= (c[..., ua] & 3) << (2 * p)
+                dw[..., m // 2] |= (c[..., ub] & 3) << (16 + 2 * p)
+                dw[..., 2] |= (c[..., ua] >> 2) << P
+                dw[..., 2] |= (c[..., ub] >> 2) << (16 + P)
+        out = np.zeros(lead + (12,), dtype=np.uint8)
+        for w in range(3):
+            for b in range(4):
+                out[..., 4 * w + b] = (dw[..., w] >> (8 * b)) & 0xFF
+        return out
+    raise ValueError(bits)
+
+
+def unpack_segment(data: np.ndarray, bits: int) -> np.ndarray:
+    """Inverse of pack_segment: bytes [..., 4*bits] -> unsigned codes [..., 32]."""
+    b = np.asarray(data).astype(np.int64)
+    lead = b.shape[:-1]
+    if bits == 8:
+        return b
+    if bits == 4:
+        out = np.empty(lead + (32,), dtype=np.int64)
+        out[..., 0::2] = b & 15
+        out[..., 1::2] = b >> 4
+        return out
+    if bits == 3:
+        dw = [b[..., 4 * w] | (b[..., 4 * w + 1] << 8) | (b[..., 4 * w + 2] << 16)
+              | (b[..., 4 * w + 3] << 24) for w in range(3)]
+        out = np.empty(lead + (32,), dtype=np.int64)
+        for m in range(4):
+            for r in range(4):
+                ua, ub = 8 * m + r, 8 * m + r + 4
+                p = 4 * (m % 2) + r
+                P = 4 * m + r
+                out[..., ua] = ((dw[m // 2] >> (2 * p)) & 3) | (((dw[2] >> P) & 1) << 2)
+                out[..., ub] = ((dw[m // 2] >> (16 + 2 * p)) & 3) | (((dw[2] >> (16 + P)) & 1) << 2)
+        return out
+    raise ValueError(bits)
+
+
+def k_row_channel(q: int, u: int) -> int:
+    """Channel stored at code u of segment q of a K row."""
+    return 32 * (u // 8) + 8 * q + (u % 8)
+
+
+def v_tile_position(lane: int, s: int, u: int):
+    """(token-in-tile, channel) stored at code u of segment s of lane ``lane``."""
+    q, i = lane // 16, lane % 16
+    m, e = u // 8, u % 8
+    tok = 4 * q + e if e < 4 else 16 + 4 * q + (e - 4)
+    return tok, 16 * (4 * s + m) + i
+
+
+def pack_k_rows(codes: np.ndarray, bits: int) -> np.ndarray:
+    """codes [..., T, 128] -> bytes [..., T, 16*bits] in the K-row layout."""
+    codes = np.asarray(codes)
+    segs = []
+    for q in range(4):
+        idx = [k_row_channel(q, u) for u in range(32)]
+        segs.append(pack_segment(codes[..., idx], bits))
+    return np.concatenate(segs, axis=-1)
+
+
+def pack_v_tiles(codes: np.ndarray, bits: int) -> np.ndarray:
+    """codes [..., T, 128] with T a multiple of 32 -> bytes [..., T/32, 64*8*bits]."""
+    codes = np.asarray(codes)
+    T = codes.shape[-2]
+    assert T % 32 == 0
+    tiles = codes.reshape(codes.shape[:-2] + (T // 32, 32, D))
+    lanes = []
+    for lane in range(64):
+        for s in range(2):
+            toks, chans = zip(*[v_tile_position(lane, s, u) for u in range(32)])
+            seg_codes = tiles[..., list(toks), list(chans)]     # [..., ntiles, 32]
+            lanes.append(pack_segment(seg_codes, bits))
+    return np.concatenate(lanes, axis=-1)
+
+
+def expected_regions(fmt: Dict, enc: Dict[str, np.ndarray], *, batch: int, n_kv_heads: int,
+                     n_ctx: int, max_ctx: int, kv_dtype: str, is_key: bool) -> Dict[str, np.ndarray]:
+    """Byte-exact image of one tensor's cache regions after ``n_ctx`` tokens.
+
+    Region arrays (unwritten entries are zero):
+
+    * ``codes`` uint8 [B, H, Tcap * row_bytes]: K-row layout for keys,
+      V-tile layout for values (NONE stores raw fp16/bf16 rows instead);
+    * ``params``: per-token asymmetric fp16 [B, H, Tcap, d/G, 2] (scale,
+      zero); q8_0 fp16 [B, H, Tcap, d/G]; per-channel fp16
+      [B, H, Tcap // G, d, 2];
+    * ``tail`` (per-channel): [B, H, G, d] raw bits of the unfinished group
+      (uint16), zero beyond it;
+    * ``row_ptr`` int32 [B * Tcap + 1], ``col`` uint16 and ``val`` fp16
+      [B * Tcap * k]: CSR over rows r = b * Tcap + t, with
+      row_ptr[b * Tcap + t] = k * (b * Tcap + t) for t = 0..n_ctx.
+    """
+    B, H = batch, n_kv_heads
+    Tcap = capacity(max_ctx)
+    q = fmt["quantizer"]
+    bits = fmt["bits"]
+    G = fmt.get("group_size", 0)
+    out: Dict[str, np.ndarray] = {}
+    if q == "none":
+        raise ValueError("raw format has no quantized regions")
+    rb = row_bytes(bits)
+    codes = np.zeros((B, H, Tcap, D), dtype=np.int64)
+    c = np.asarray(enc["codes"]).astype(np.int64)
+    codes[:, :, :c.shape[2], :] = c
+    if is_key:
+        packed = pack_k_rows(codes, bits)                          # [B, H, Tcap, rb]
+    else:
+        packed = pack_v_tiles(codes, bits)                         # [B, H, Tcap/32, 32*rb]
+    # tokens that are not yet quantized must leave their bytes at zero
+    if is_key:
+        packed[:, :, c.shape[2]:, :] = 0
+    out["codes"] = packed.reshape(B, H, Tcap * rb)
+    layout = fmt.get("layout", "per_token")
+    if q in ("asym_minmax", "asym_absmax_offset"):
+        if layout == "per_token":
+            p = np.zeros((B, H, Tcap, D // G, 2), dtype=np.float16)
+            p[:, :, :n_ctx, :, 0] = enc["scale"]
+            p[:, :, :n_ctx, :, 1] = enc["zero"]
+        else:
+            p = np.zeros((B, H, Tcap // G, D, 2), dtype=np.float16)
+            ng = enc["scale"].shape[2]
+            p[:, :, :ng, :, 0] = enc["scale"]
+            p[:, :, :ng, :, 1] = enc["zero"]
+            tail = np.zeros((B, H, G, D), dtype=np.uint16)
+            t = enc["tail"]
+            tail[:, :, :t.shape[2], :] = to_bits(t, kv_dtype)
+            out["tail"] = tail
+        out["params"] = p
+    elif q == "sym_q8_0":
+        p = np.zeros((B, H, Tcap, D // G), dtype=np.float16)
+        p[:, :, :n_ctx, :] = enc["scale"]
+        out["params"] = p
+    if q == "codebook" and "cols" in enc:
+        k = enc["cols"].shape[-1]
+        row_ptr = np.zeros(B * Tcap + 1, dtype=np.int64)
+        col = np.zeros(B * Tcap * k, dtype=np.uint16)
+        val = np.zeros(B * Tcap * k, dtype=np.float16)
+        for b in range(B):
+            r0 = b * Tcap
+            row_ptr[r0:r0 + n_ctx + 1] = k * np.arange(r0, r0 + n_ctx + 1)
+            col[k * r0:k * (r0 + n_ctx)] = enc["cols"][b].reshape(-1)
+            val[k * r0:k * (r0 + n_ctx)] = enc["vals"][b].reshape(-1).astype(np.float16)
+        out["row_ptr"] = row_ptr.astype(np.int32)
+        out["col"] = col
+        out["val"] = val
+    return out
+
+
+def to_bits(x: np.ndarray, kv_dtype: str) -> np.ndarray:
+    """Raw 16-bit patterns of float32 values that are exact fp16/bf16 numbers."""
+    x = np.asarray(x, dtype=np.float32)
+    if kv_dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    u = x.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "values are not bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def from_bits(b: np.ndarray, kv_dtype: str) -> np.ndarray:
+    """float32 values of raw fp16/bf16 bit patterns."""
+    b = np.asarray(b, dtype=np.uint16)
+    if kv_dtype == "f16":
+        return b.view(np.float16).astype(np.float32)
+    return (b.astype(np.uint32) << 16).view(np.float32)

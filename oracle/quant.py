@@ -1,0 +1,224 @@
+"""Quantizers of the oracle (float32 encode, round-half-even, float64 decode).
+
+Test infrastructure: see the package docstring.
+
+Common rules (readings where the pages are silent):
+
+* Inputs are fp16 or bf16 and enter as their exact float32 values.
+* ``f16(.)`` rounds float32 to fp16 to nearest-even; scales and zero points
+  are rounded to fp16 *before* codes are computed, so the stored parameters
+  reproduce the dequantized values.
+* ``rint`` is round-half-even, the rounding of the TurboQuant page's Python
+  ``round`` (section 3.1).
+* Each step is one IEEE float32 operation: ``(x - z)`` then ``/ s``, never a
+  multiply by a reciprocal, never a fused multiply-add.
+* A degenerate group whose fp16 scale is 0 gets code 0 everywhere, so it
+  dequantizes to its zero point.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Tuple
+
+import numpy as np
+
+F32 = np.float32
+
+
+def f16(x: np.ndarray) -> np.ndarray:
+    """Round float32 to fp16, nearest-even."""
+    return np.asarray(x, dtype=F32).astype(np.float16)
+
+
+def _div_codes(num: np.ndarray, s16: np.ndarray, lo: int, hi: int) -> np.ndarray:
+    """code = clamp(rint(num / s), lo, hi) in float32, 0 where s == 0."""
+    s32 = s16.astype(F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        qf = num / s32
+    r = np.rint(qf)
+    r = np.where(s32 == 0, F32(0), r)
+    r = np.clip(r, lo, hi)
+    return r.astype(np.int32)
+
+
+def asym_minmax(x: np.ndarray, bits: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Group-wise asymmetric min/max quantization over the last axis.
+
+    Each group gets its own range and scale (Survey page, section 2.4: a
+    scale and a zero point per group; Memory-killer page, section 2.3: every
+    group measures its own value range).  scale = f16((max - min) / (2^b - 1)),
+    zero = f16(min), code = clamp(rint((x - zero) / scale), 0, 2^b - 1).
+    Returns (codes int32, scale fp16, zero fp16); parameters drop the last axis.
+    """
+    x = np.asarray(x, dtype=F32)
+    lo = x.min(axis=-1)
+    hi = x.max(axis=-1)
+    qmax = F32(2 ** bits - 1)
+    s = f16((hi - lo) / qmax)
+    z = f16(lo)
+    codes = _div_codes(x - z.astype(F32)[..., None], s[..., None], 0, 2 ** bits - 1)
+    return codes, s, z
+
+
+def asym_absmax_offset(x: np.ndarray, bits: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """TurboQuant's dynamic asymmetric quantizer (TurboQuant page, section 3.1),
+    with fixed non-overlapping groups in place of sliding windows:
+    scale = f16(max|x| / (2^(b-1) - 1)), offset = f16(min),
+    code = clamp(rint((x - offset) / scale), 0, 2^b - 1).
+    """
+    x = np.asarray(x, dtype=F32)
+    lo = x.min(axis=-1)
+    amax = np.abs(x).max(axis=-1)
+    s = f16(amax / F32(2 ** (bits - 1) - 1))
+    z = f16(lo)
+    codes = _div_codes(x - z.astype(F32)[..., None], s[..., None], 0, 2 ** bits - 1)
+    return codes, s, z
+
+
+def sym_q8_0(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """q8_0: symmetric int8, zero point fixed at 0, range [-128, 127] (NIAH
+    page, section 1.2), one fp16 scale per block: scale = f16(max|x| / 127),
+    code = clamp(rint(x / scale), -128, 127).  Returns (codes int32, scale fp16).
+    """
+    x = np.asarray(x, dtype=F32)
+    amax = np.abs(x).max(axis=-1)
+    s = f16(amax / F32(127))
+    codes = _div_codes(x, s[..., None], -128, 127)
+    return codes, s
+
+
+def codebook_midpoints(cb: np.ndarray) -> np.ndarray:
+    """Decision thresholds between neighbouring centroids: m_i = f32(C_i + C_{i+1}) * 0.5
+    for i = 0..14 (float32).  ``cb`` is fp16 [..., 16] ascending."""
+    c = np.asarray(cb, dtype=np.float16).astype(F32)
+    return (c[..., :-1] + c[..., 1:]) * F32(0.5)
+
+
+def codebook_codes(x: np.ndarray, cb: np.ndarray) -> np.ndarray:
+    """Non-uniform quantization (KVQuant page, section 2.2): each value maps to
+    the nearest of 16 per-channel centroids, ties to the lower index, computed
+    as the number of midpoints strictly below x.  ``x`` [..., H, d] float32,
+    ``cb`` fp16 [H, d, 16]."""
+    m = codebook_midpoints(cb)                       # [H, d, 15]
+    x = np.asarray(x, dtype=F32)
+    return (x[..., None] > m).sum(axis=-1).astype(np.int32)
+
+
+def outlier_count(frac: float, n: int) -> int:
+    """Number of outliers kept per token: ceil(frac * n), frac taken as float32."""
+    if frac <= 0:
+        return 0
+    return int(math.ceil(float(np.float32(frac)) * n))
+
+
+def select_outliers(x: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Dense-and-sparse split (KVQuant page, section 2.2; section 3.3's
+    outlier_threshold_ratio): per token (row of ``x``, all heads flattened,
+    float32) keep the ``k`` entries of largest |x|, ties to the lower flat
+    index.  Returns (cols [N, k] ascending, int64; vals [N, k] float32)."""
+    x = np.asarray(x, dtype=F32)
+    order = np.argsort(-np.abs(x), axis=1, kind="stable")   # stable: ties keep index order
+    cols = np.sort(order[:, :k], axis=1).astype(np.int64)
+    vals = np.take_along_axis(x, cols, axis=1)
+    return cols, vals
+
+
+# --------------------------------------------------------------------------
+# Whole-tensor encoding (logical codes; byte layouts live in layout.py)
+# --------------------------------------------------------------------------
+
+def encode_tensor(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None) -> Dict[str, np.ndarray]:
+    """Bulk-encode one cache tensor.
+
+    ``x`` is float32 [B, T, H, d] holding fp16/bf16 values.  ``fmt`` has
+    quantizer, bits, group_size, layout, outlier_frac.  Returns logical arrays:
+
+    * ``codes`` int32 [B, H, Tq, d] for the Tq quantized tokens
+      (Tq = T, except per-channel layout: Tq = floor(T / G) * G),
+    * ``scale``/``zero`` fp16: per-token [B, H, T, d/G]; per-channel
+      [B, H, T/G, d]; q8_0 has no zero,
+    * ``tail`` float32 [B, H, T - Tq, d]: per-channel keys of the unfinished
+      group stay unquantized (reading: the pages quantize only complete
+      groups of appended rows -- NIAH page section 1.1, KVQuant page
+      section 3.4 -- and say nothing of partial groups),
+    * ``cols``/``vals`` for codebook outliers ([B, T, k]),
+    * ``deq`` float64 [B, H, T, d]: the values attention sees.
+    """
+    x = np.asarray(x, dtype=F32)
+    B, T, H, d = x.shape
+    q = fmt["quantizer"]
+    bits = fmt["bits"]
+    G = fmt.get("group_size", 0)
+    layout = fmt.get("layout", "per_token")
+    xt = np.transpose(x, (0, 2, 1, 3))                  # [B, H, T, d]
+    out: Dict[str, np.ndarray] = {}
+    if q == "none":
+        out["deq"] = xt.astype(np.float64)
+        return out
+    if q == "codebook":
+        if codebook is None:
+            raise ValueError("codebook format needs a codebook")
+        codes = codebook_codes(x, codebook)             # [B, T, H, d]
+        cbf = np.asarray(codebook, dtype=np.float16).astype(np.float64)
+        hh = np.arange(H)[None, None, :, None]
+        cc = np.arange(d)[None, None, None, :]
+        deq = cbf[hh, cc, codes]                        # [B, T, H, d]
+        k = outlier_count(fmt.get("outlier_frac", 0.0), H * d)
+        if k > 0:
+            flat = x.reshape(B * T, H * d)
+            cols, vals = select_outliers(flat, k)
+            dflat = deq.reshape(B * T, H * d)
+            rows = np.arange(B * T)[:, None]
+            dflat[rows, cols] = vals.astype(np.float64)  # replacement semantics
+            deq = dflat.reshape(B, T, H, d)
+            out["cols"] = cols.reshape(B, T, k)
+            out["vals"] = vals.reshape(B, T, k)
+        out["codes"] = np.transpose(codes, (0, 2, 1, 3))
+        out["deq"] = np.transpose(deq, (0, 2, 1, 3))
+        return out
+
+    if layout == "per_token":
+        if d % G:
+            raise ValueError("group size must divide head_dim")
+        g = xt.reshape(B, H, T, d // G, G)
+        if q == "asym_minmax":
+            c, s, z = asym_minmax(g, bits)
+        elif q == "asym_absmax_offset":
+            c, s, z = asym_absmax_offset(g, bits)
+        elif q == "sym_q8_0":
+            c, s = sym_q8_0(g)
+            z = None
+        else:
+            raise ValueError(q)
+        out["codes"] = c.reshape(B, H, T, d)
+        out["scale"] = s
+        if z is not None:
+            out["zero"] = z
+        deq = c.astype(np.float64) * s.astype(np.float64)[..., None]
+        if z is not None:
+            deq = deq + z.astype(np.float64)[..., None]
+        out["deq"] = deq.reshape(B, H, T, d)
+        return out
+
+    if layout == "per_channel":
+        # Per-channel keys, groups of G consecutive tokens (KVQuant page,
+        # section 2.2; Survey page, section 2.4's per-position groups).
+        nq = (T // G) * G
+        g = xt[:, :, :nq, :].reshape(B, H, T // G, G, d)
+        g = np.swapaxes(g, -1, -2)                      # [B, H, ng, d, G]
+        if q == "asym_minmax":
+            c, s, z = asym_minmax(g, bits)
+        elif q == "asym_absmax_offset":
+            c, s, z = asym_absmax_offset(g, bits)
+        else:
+            raise ValueError(f"{q} has no per-channel form")
+        deq_q = c.astype(np.float64) * s.astype(np.float64)[..., None] + z.astype(np.float64)[..., None]
+        out["codes"] = np.swapaxes(c, -1, -2).reshape(B, H, nq, d)
+        out["scale"] = s                                  # [B, H, ng, d]
+        out["zero"] = z
+        out["tail"] = xt[:, :, nq:, :].copy()
+        deq = np.concatenate([np.swapaxes(deq_q, -1, -2).reshape(B, H, nq, d),
+                              xt[:, :, nq:, :].astype(np.float64)], axis=2)
+        out["deq"] = deq
+        return out
+    raise ValueError(layout)

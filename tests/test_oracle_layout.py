@@ -1,0 +1,91 @@
+"""Pins for the oracle's byte layouts against hand-derived bytes (CPU only)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import layout
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "layout_examples.json")))
+
+
+def test_segment_4bit_nibble_order():
+    for ex in GOLD["segment_4bit"]:
+        c = np.zeros(32, dtype=np.int64)
+        c[:len(ex["codes_first"])] = ex["codes_first"]
+        b = layout.pack_segment(c, 4)
+        assert b[:len(ex["bytes_first"])].tolist() == ex["bytes_first"]
+
+
+def test_segment_3bit_examples():
+    for ex in GOLD["segment_3bit"]:
+        c = np.zeros(32, dtype=np.int64)
+        c[ex["code_index"]] = ex["code"]
+        assert layout.pack_segment(c, 3).tolist() == ex["bytes"], ex["why"]
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_segment_round_trip(bits):
+    rng = np.random.default_rng(bits)
+    c = rng.integers(0, 2 ** bits, size=(100, 32))
+    b = layout.pack_segment(c, bits)
+    assert b.shape == (100, 4 * bits)
+    assert np.array_equal(layout.unpack_segment(b, bits), c)
+    # every bit of the segment is used by exactly one code: all-ones codes give all-ones bytes
+    full = layout.pack_segment(np.full(32, 2 ** bits - 1), bits)
+    assert np.all(full == 255)
+
+
+def test_k_row_is_a_permutation_and_examples():
+    chans = sorted(layout.k_row_channel(q, u) for q in range(4) for u in range(32))
+    assert chans == list(range(128))
+    for ex in GOLD["k_row_4bit"]:
+        codes = np.zeros((1, 128), dtype=np.int64)
+        codes[0, ex["channel"]] = ex["code"]
+        row = layout.pack_k_rows(codes, 4)[0]
+        nz = np.nonzero(row)[0].tolist()
+        assert nz == [ex["byte_index"]] and row[ex["byte_index"]] == ex["byte"], ex["why"]
+    for ex in GOLD["k_row_8bit"]:
+        codes = np.zeros((1, 128), dtype=np.int64)
+        codes[0, ex["channel"]] = ex["code"]
+        row = layout.pack_k_rows(codes, 8)[0]
+        assert np.nonzero(row)[0].tolist() == [ex["byte_index"]]
+        assert row[ex["byte_index"]] == ex["byte"], ex["why"]
+
+
+def test_v_tile_is_a_bijection_and_examples():
+    pos = sorted(layout.v_tile_position(L, s, u) for L in range(64) for s in range(2)
+                 for u in range(32))
+    assert pos == [(t, c) for t in range(32) for c in range(128)]
+    for ex in GOLD["v_tile_4bit"]:
+        codes = np.zeros((32, 128), dtype=np.int64)
+        codes[ex["token_in_tile"], ex["channel"]] = ex["code"]
+        tile = layout.pack_v_tiles(codes, 4)[0]
+        assert tile.shape == (2048,)
+        assert np.nonzero(tile)[0].tolist() == [ex["byte_index"]], ex["why"]
+        assert tile[ex["byte_index"]] == ex["byte"], ex["why"]
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_v_tile_unpacks_back(bits):
+    rng = np.random.default_rng(10 + bits)
+    codes = rng.integers(0, 2 ** bits, size=(64, 128))
+    tiles = layout.pack_v_tiles(codes, bits)              # [2, 64 * 8 * bits]
+    assert tiles.shape == (2, 64 * 8 * bits)
+    lb = 8 * bits
+    for tix in range(2):
+        for L in range(64):
+            for s in range(2):
+                seg = tiles[tix, L * lb + s * 4 * bits: L * lb + (s + 1) * 4 * bits]
+                got = layout.unpack_segment(seg, bits)
+                for u in range(32):
+                    t, c = layout.v_tile_position(L, s, u)
+                    assert got[u] == codes[32 * tix + t, c]
+
+
+def test_bits_round_trip():
+    x = np.array([1.5, -2.25, 0.0, 65504.0], dtype=np.float32)
+    assert np.array_equal(layout.from_bits(layout.to_bits(x, "f16"), "f16"), x)
+    y = np.array([1.5, -3.0, 2.0 ** 100, -1.0 / 1024], dtype=np.float32)
+    assert np.array_equal(layout.from_bits(layout.to_bits(y, "bf16"), "bf16"), y)

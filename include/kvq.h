@@ -1,0 +1,262 @@
+/*
+ * kvq.h -- C ABI of a low-bit KV-cache library for decode attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  Keys and values appended to a decode cache are quantized
+ * group-wise to 3, 4 or 8 bits (or to a 16-entry non-uniform codebook with
+ * fp16 outliers), and decode attention reads the packed codes directly:
+ * dequantization happens inside the score, online-softmax and value-product
+ * pass, so every code byte is read from HBM exactly once per step.
+ *
+ * Sources.  The operations follow five web pages on KV-cache quantization:
+ *   - "NIAH" page (www.cf-1.com/news/5482713): q8_0 KV cache in llama.cpp,
+ *     quantizing only the appended row (sections 1.1, 1.2, 2.2).
+ *   - "TurboQuant" page (www.dpshk.com/news/6341316): per-token cache size
+ *     2*L*d*h*bytes (section 2.1); 3-bit dynamic asymmetric quantization with
+ *     scale = absmax/(2^(b-1)-1) and a min offset (section 3.1).
+ *   - "KVQuant" page (www.cf-1.com/news/2306543): per-channel pre-RoPE keys,
+ *     non-uniform codebooks, dense-and-sparse fp16 outliers with a bounded
+ *     count per token, quantize-on-append and fused dequantization
+ *     (sections 2.1, 2.2, 3.3, 3.4).
+ *   - "Survey" page (www.discosf.com/news/4854722): per-head, per-position
+ *     groups with a scale and zero point per group (section 2.4); keeping
+ *     scores, softmax and the value product on chip (section 2.3).
+ *   - "Memory-killer" page (www.demingchina.com/news/57821): decode is bound
+ *     by streaming the cache (sections 1.3, 4.2); group-wise scaling and
+ *     dequantization fused into the attention product (section 2.3); the
+ *     8B / 128K element count (section 1.2).
+ *
+ * Conventions for every call.
+ *   - All pointers are device pointers unless stated; the caller owns every
+ *     buffer.  The library never allocates or frees memory.
+ *   - Device pointers must be 16-byte aligned.
+ *   - Work is enqueued on the given HIP stream (a hipStream_t passed as
+ *     void*, NULL = the default stream) and never synchronizes the host.
+ *   - Every argument is checked on the host before anything is launched.  A
+ *     non-OK status leaves all state unchanged and sets a message readable
+ *     with kvq_last_error().  No C++ exception crosses this interface.
+ *   - head_dim must be 128.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+typedef int32_t kvq_status;
+#define KVQ_OK                    0
+#define KVQ_ERR_INVALID_ARGUMENT (-1) /* NULL/misaligned pointer, bad size    */
+#define KVQ_ERR_UNSUPPORTED      (-2) /* valid but not implemented here       */
+#define KVQ_ERR_CAPACITY         (-3) /* append would exceed max_ctx          */
+#define KVQ_ERR_DEVICE           (-4) /* a HIP launch reported an error       */
+
+/* ---- element types ----------------------------------------------------- */
+#define KVQ_F16   0
+#define KVQ_BF16  1
+#define KVQ_F32   2
+
+/* ---- quantizers (per tensor) ------------------------------------------- */
+/* NONE: raw fp16/bf16 storage (bits = 16).
+ * ASYM_MINMAX: per group scale = f16((max-min)/(2^b-1)), zero = f16(min),
+ *   code = clamp(rint((x-zero)/scale), 0, 2^b-1)  [Survey page 2.4,
+ *   Memory-killer page 2.3].  bits 3, 4 or 8.
+ * ASYM_ABSMAX_OFFSET: scale = f16(max|x|/(2^(b-1)-1)), offset = f16(min),
+ *   code as above [TurboQuant page 3.1, fixed groups instead of sliding
+ *   windows].  bits 3, 4 or 8.
+ * SYM_Q8_0: scale = f16(max|x|/127), zero 0, code = clamp(rint(x/scale),
+ *   -128, 127) [NIAH page 1.2].  bits 8, per-token groups of group_size.
+ * CODEBOOK: 4-bit index of the nearest of 16 fp16 centroids of that
+ *   (kv head, channel), ties to the lower index; optionally the
+ *   ceil(outlier_frac * n_kv_heads * head_dim) entries of largest |x| of each
+ *   token are kept exactly in fp16 (CSR) and replace the dense value
+ *   [KVQuant page 2.2, 3.3].
+ * All arithmetic of the encoders is IEEE float32 with round-half-even;
+ * scales and zeros are rounded to fp16 before codes are computed; a group
+ * whose fp16 scale is 0 stores code 0 everywhere. */
+#define KVQ_QUANT_NONE                0
+#define KVQ_QUANT_ASYM_MINMAX         1
+#define KVQ_QUANT_ASYM_ABSMAX_OFFSET  2
+#define KVQ_QUANT_SYM_Q8_0            3
+#define KVQ_QUANT_CODEBOOK            4
+
+/* ---- group layouts ----------------------------------------------------- */
+/* PER_TOKEN: groups of group_size consecutive channels of one token
+ *   (group_size in {32, 64, 128}).
+ * PER_CHANNEL: keys only; groups of group_size consecutive tokens of one
+ *   channel [KVQuant page 2.2 per-channel keys, Survey page 2.4 per-position
+ *   groups]; group_size a multiple of 32, at most 256.  Tokens of the
+ *   unfinished last group stay unquantized in an fp16/bf16 tail until the
+ *   group fills. */
+#define KVQ_LAYOUT_PER_TOKEN    0
+#define KVQ_LAYOUT_PER_CHANNEL  1
+
+/* ---- decode kernel selection ------------------------------------------- */
+/* AUTO picks the matrix-core kernel when the formats allow it (uniform
+ * quantizers or raw storage for both tensors, no RoPE, no codebook, at most
+ * 8 query heads per KV head) and the vector-ALU kernel otherwise.  VALU and
+ * MFMA force a kernel; MFMA on a configuration it cannot run is
+ * KVQ_ERR_UNSUPPORTED.  Both compute the same attention to rounding. */
+#define KVQ_PATH_AUTO 0
+#define KVQ_PATH_VALU 1
+#define KVQ_PATH_MFMA 2
+
+/* ---- kvq_cache_bytes selectors ----------------------------------------- */
+#define KVQ_BYTES_PAYLOAD 0   /* bytes that hold n_ctx tokens, x n_layers    */
+#define KVQ_BYTES_ALLOC   1   /* one layer's allocation at max_ctx            */
+
+typedef struct kvq_tensor_format {
+  int32_t quantizer;      /* KVQ_QUANT_*                                     */
+  int32_t bits;           /* 3, 4, 8 (16 for NONE)                           */
+  int32_t group_size;     /* see the layouts; ignored by NONE and CODEBOOK   */
+  int32_t layout;         /* KVQ_LAYOUT_*                                    */
+  float   outlier_frac;   /* CODEBOOK only: 0 or a fraction in (0, 0.25]     */
+} kvq_tensor_format;
+
+typedef struct kvq_config {
+  int32_t batch;          /* sequences B                                     */
+  int32_t n_q_heads;      /* query heads Hq; a multiple of n_kv_heads        */
+  int32_t n_kv_heads;     /* KV heads Hkv; query head j reads KV head j/(Hq/Hkv) */
+  int32_t head_dim;       /* d, must be 128                                  */
+  int64_t max_ctx;        /* capacity in tokens per sequence                 */
+  int32_t kv_dtype;       /* KVQ_F16 or KVQ_BF16: dtype of K, V and q        */
+  int32_t rope;           /* 1: keys are stored pre-RoPE and both q and k are
+                             rotated at decode time (rotate-half pairs
+                             (i, i+d/2), theta_i = rope_base^(-2i/d)) [KVQuant
+                             page 2.1-2.2]                                    */
+  float   rope_base;      /* e.g. 10000                                      */
+  int32_t decode_splits;  /* 0 = automatic; otherwise the maximum number of
+                             token splits per (sequence, KV head)            */
+  int32_t decode_path;    /* KVQ_PATH_AUTO, KVQ_PATH_VALU or KVQ_PATH_MFMA    */
+  kvq_tensor_format k;    /* key format                                      */
+  kvq_tensor_format v;    /* value format (PER_TOKEN only)                   */
+} kvq_config;
+
+typedef struct kvq_cache {
+  void*       base;       /* device buffer of kvq_cache_bytes(KVQ_BYTES_ALLOC)
+                             bytes, zero-filled before first use (all zero =
+                             empty cache).  The decode call also uses a
+                             workspace region inside it.                     */
+  const void* k_codebook; /* CODEBOOK keys: fp16 [n_kv_heads, head_dim, 16],
+                             ascending per (head, channel); else NULL         */
+  const void* v_codebook; /* same for values                                 */
+  int64_t     n_ctx;      /* tokens held per sequence (host state; advanced
+                             by kvq_quantize_append on success)              */
+} kvq_cache;
+
+/* Location of one array inside the cache allocation (bytes from base). */
+typedef struct kvq_region {
+  uint64_t offset;
+  uint64_t bytes;
+} kvq_region;
+
+typedef struct kvq_tensor_regions {
+  kvq_region codes;    /* packed codes (raw rows for NONE)                  */
+  kvq_region params;   /* fp16 scale/zero pairs (q8_0: scales)              */
+  kvq_region tail;     /* per-channel keys: fp16/bf16 [B, Hkv, G, d]        */
+  kvq_region row_ptr;  /* outliers: int32 [B*Tcap + 1]                      */
+  kvq_region col;      /* outliers: uint16 column h*d + c                   */
+  kvq_region val;      /* outliers: fp16 value                              */
+} kvq_tensor_regions;
+
+typedef struct kvq_layout_info {
+  kvq_tensor_regions k;
+  kvq_tensor_regions v;
+  kvq_region workspace;     /* split-K partials and counters                */
+  uint64_t   total_bytes;   /* == kvq_cache_bytes(..., KVQ_BYTES_ALLOC)     */
+  int64_t    capacity;      /* Tcap = max_ctx rounded up to 32              */
+  int32_t    max_splits;    /* split-K partial slots per (b, query head)   */
+  int32_t    reserved;
+} kvq_layout_info;
+
+/*
+ * kvq_cache_bytes -- size of the cache.  Host only; touches no device.
+ *   what = KVQ_BYTES_PAYLOAD: bytes that hold n_ctx tokens (packed codes,
+ *     scale/zero parameters, the unquantized per-channel tail, CSR outliers,
+ *     codebooks), times n_layers.  With NONE for both tensors this is
+ *     exactly 2 * n_layers * n_kv_heads * head_dim * 2 * n_ctx * batch, the
+ *     per-token formula of the TurboQuant page (section 2.1), which gives
+ *     327,680 bytes per token for Llama-2-70B (L = 80, h = 8, d = 128).
+ *     This is also the number of bytes one decode step must read.
+ *   what = KVQ_BYTES_ALLOC: size of one layer's allocation at max_ctx,
+ *     including padding and the decode workspace (n_ctx, n_layers ignored).
+ *   Errors: INVALID_ARGUMENT (NULL, negative sizes, bad config, unknown
+ *   selector), UNSUPPORTED (head_dim != 128 or an unsupported format).
+ */
+kvq_status kvq_cache_bytes(const kvq_config* cfg, int64_t n_ctx, int64_t n_layers,
+                           int32_t what, uint64_t* out_bytes);
+
+/*
+ * kvq_cache_layout -- offsets of every array inside one layer's allocation,
+ * for callers that checkpoint or inspect the cache.  Host only.
+ * Byte layouts (d = 128):
+ *   segment of 32 codes u = 8m + e (block m, element e): 8-bit: byte u;
+ *     4-bit: byte j = code 2j | code 2j+1 << 4; 3-bit: three little-endian
+ *     dwords D0, D1, D2 -- for block m and r = 0..3 the pair (8m+r, 8m+r+4)
+ *     keeps its low two bits at bits 2p and 16+2p of D[m/2], p = 4(m%2)+r,
+ *     and its high bits at bits P and 16+P of D2, P = 4m+r.
+ *   keys: a row of 16*bits bytes per token, segment q = 0..3 holding
+ *     channels 32m + 8q + e; codes [B][Hkv][Tcap][row].
+ *   values: tiles of 32 tokens, 64 lanes L = 16q + i of 8*bits bytes (two
+ *     segments s); segment s, block m of lane L holds channel 16(4s+m) + i,
+ *     element e is token 4q+e (e < 4) or 16+4q+e-4 of the tile.
+ *   params: per-token [B][Hkv][Tcap][d/G] of (scale, zero) fp16 pairs
+ *     (q8_0: scales only); per-channel [B][Hkv][Tcap/G][d] pairs.
+ *   NONE: raw rows [B][Hkv][Tcap][d] of kv_dtype for keys and values.
+ * Errors: as kvq_cache_bytes.
+ */
+kvq_status kvq_cache_layout(const kvq_config* cfg, kvq_layout_info* out);
+
+/*
+ * kvq_quantize_append -- quantize n_new new tokens of every sequence and
+ * append them at position cache->n_ctx; on success n_ctx += n_new.
+ * Only the new rows are encoded; existing codes are never re-quantized
+ * (NIAH page 1.1 and 2.2: quantize just the appended row; KVQuant page 3.4:
+ * new keys and values are quantized with fixed parameters and stored as
+ * codes plus fp16 outliers).  Appending in several calls gives exactly the
+ * bytes of one call with all tokens.
+ *   k_new, v_new: device [B][n_new][Hkv][d] of kv_dtype, contiguous.
+ *   n_new = 0 is a no-op.  Bulk prefill is one call with n_new = T.
+ * Errors: INVALID_ARGUMENT (NULL/misaligned pointers, n_new < 0, bad config,
+ *   codebook pointer missing or present when the format says otherwise),
+ *   UNSUPPORTED, CAPACITY (n_ctx + n_new > max_ctx; checked before any
+ *   launch), DEVICE.
+ */
+kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new,
+                               const void* v_new, int32_t n_new, void* stream);
+
+/*
+ * kvq_decode_attention -- one decode step of attention over the cached
+ * tokens [0, n_ctx) for every sequence and query head:
+ *   out[b, j, :] = sum_t softmax_t(sm_scale * q'_j . k'_t) * v_t
+ * with k, v the dequantized cache of KV head j / (Hq / Hkv) (outliers
+ * replacing their dense values), q' = R(q_pos) q and k'_t = R(t) k_t when
+ * rope is on (identity otherwise).  Dequantization is fused into the pass
+ * (Memory-killer page 2.3; KVQuant page 3.4); the token axis is split over
+ * the GPU and the partial softmax states are merged by log-sum-exp.
+ *   q: device [B][Hq][d] of kv_dtype.  q_pos: device int32 [B] or NULL
+ *   (= n_ctx - 1).  sm_scale <= 0 selects 1/sqrt(d).
+ *   out: device [B][Hq][d] of out_dtype (KVQ_F32, KVQ_F16 or KVQ_BF16).
+ * The call writes the workspace region of cache->base: decode calls on the
+ * same cache must not overlap in time (same stream or synchronized).
+ * Errors: INVALID_ARGUMENT (NULL/misaligned pointers, n_ctx == 0 or beyond
+ *   max_ctx, bad out_dtype), UNSUPPORTED, DEVICE.
+ */
+kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                                const int32_t* q_pos, float sm_scale, void* out,
+                                int32_t out_dtype, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* kvq_last_error(void);
+
+/* Version of this interface (major * 100 + minor). */
+int32_t kvq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -1,0 +1,96 @@
+// Device helpers shared by the libkvq kernels: element conversions and the
+// addressing of the packed cache layouts (see include/kvq.h,
+// kvq_cache_layout, for the layout contract).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ float bf2f(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+__device__ __forceinline__ float elem2f(uint16_t h, int is_bf16) {
+  return is_bf16 ? bf2f(h) : h2f(h);
+}
+// Round-to-nearest-even conversions.
+__device__ __forceinline__ uint16_t f2h_rn(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ uint16_t f2bf_rn(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---- segment of 32 codes (u = 8m + e) ---------------------------------------
+// 8-bit: byte u.  4-bit: nibble u (low nibble = even u).  3-bit: see kvq.h.
+__device__ __forceinline__ uint32_t seg_code(const uint8_t* seg, int bits, int u) {
+  if (bits == 8) return seg[u];
+  if (bits == 4) return (seg[u >> 1] >> ((u & 1) * 4)) & 15u;
+  const int m = u >> 3, e = u & 7, r = e & 3, hi16 = (e >> 2) * 16;
+  const int p = 4 * (m & 1) + r, P = 4 * m + r;
+  const uint32_t* dw = reinterpret_cast<const uint32_t*>(seg);
+  const uint32_t lo2 = (dw[m >> 1] >> (2 * p + hi16)) & 3u;
+  const uint32_t hi1 = (dw[2] >> (P + hi16)) & 1u;
+  return lo2 | (hi1 << 2);
+}
+
+// Key rows: segment q holds channels 32m + 8q + e.
+__device__ __forceinline__ uint32_t k_row_code(const uint8_t* row, int bits, int c) {
+  const int q = (c & 31) >> 3, u = ((c >> 5) << 3) | (c & 7);
+  return seg_code(row + q * 4 * bits, bits, u);
+}
+
+// Value tiles: token tau of the tile and channel c.
+__device__ __forceinline__ uint32_t v_tile_code(const uint8_t* tile, int bits, int tau, int c) {
+  const int q = (tau & 15) >> 2, e = (tau & 3) + 4 * (tau >> 4);
+  const int nb = c >> 4, i = c & 15;
+  const int lane = 16 * q + i, s = nb >> 2, m = nb & 3;
+  return seg_code(tile + lane * 8 * bits + s * 4 * bits, bits, 8 * m + e);
+}
+
+// Bit fields of dword j of a segment: calls f(u, shift, width, field) where
+// ``field`` is 0 for the whole code, 1 for the low two bits, 2 for the high
+// bit (3-bit packing).
+template <typename F>
+__device__ __forceinline__ void seg_dword_fields(int bits, int j, F&& f) {
+  if (bits == 8) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f(4 * j + e, 8 * e, 8, 0);
+  } else if (bits == 4) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f(8 * j + e, 4 * e, 4, 0);
+  } else if (j < 2) {
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 2 * j + mm, p = 4 * mm + r;
+        f(8 * m + r, 2 * p, 2, 1);
+        f(8 * m + r + 4, 16 + 2 * p, 2, 1);
+      }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int P = 4 * m + r;
+        f(8 * m + r, P, 1, 2);
+        f(8 * m + r + 4, 16 + P, 1, 2);
+      }
+  }
+}
+
+__device__ __forceinline__ uint32_t field_value(uint32_t code, int field) {
+  return field == 0 ? code : (field == 1 ? (code & 3u) : (code >> 2) & 1u);
+}
+
+}  // namespace kvq

@@ -1,0 +1,368 @@
+// Encode kernels of libkvq: quantize appended K/V rows into the packed cache.
+//
+// Compiled with -ffp-contract=off: every step is one IEEE float32 operation
+// with round-to-nearest-even -- (x - zero) then / scale, scale and zero
+// rounded to fp16 before any code is computed -- so the packed bytes are
+// reproducible bit for bit.
+//
+// Quantizers (include/kvq.h): group-wise asymmetric min/max (Survey page,
+// section 2.4; Memory-killer page, section 2.3), TurboQuant's absmax scale
+// with a min offset (TurboQuant page, section 3.1), q8_0 (NIAH page, section
+// 1.2), and the KVQuant codebook with dense-and-sparse outliers (KVQuant
+// page, section 2.2).  Only appended rows are encoded (NIAH page, sections
+// 1.1 and 2.2; KVQuant page, section 3.4).
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kD = kHeadDim;
+
+__device__ __forceinline__ float load_elem(const void* base, int64_t idx, int is_bf16) {
+  return elem2f(static_cast<const uint16_t*>(base)[idx], is_bf16);
+}
+
+// Quantize the two channels (2*lane, 2*lane + 1) of one row held by a full
+// wave.  For per-token uniform formats the group statistics are reduced over
+// the G/2 lanes of the group.  Writes the group's parameters (first lane of
+// each group) at ``prm_row`` (the row's parameter record array) and returns
+// the two codes (two's complement byte for q8_0).
+__device__ __forceinline__ void encode_pair(const DevTensor& t, int h, int lane, float x0,
+                                            float x1, void* prm_row, uint32_t& q0,
+                                            uint32_t& q1) {
+  const int c0 = 2 * lane, c1 = c0 + 1;
+  if (t.quant == KVQ_QUANT_CODEBOOK) {
+    const uint16_t* cb0 = t.codebook + ((int64_t)h * kD + c0) * 16;
+    const uint16_t* cb1 = cb0 + 16;
+    uint32_t a = 0, b = 0;
+#pragma unroll
+    for (int i = 0; i < 15; ++i) {
+      const float m0 = (h2f(cb0[i]) + h2f(cb0[i + 1])) * 0.5f;
+      const float m1 = (h2f(cb1[i]) + h2f(cb1[i + 1])) * 0.5f;
+      a += x0 > m0;
+      b += x1 > m1;
+    }
+    q0 = a;
+    q1 = b;
+    return;
+  }
+  float lo = fminf(x0, x1), hi = fmaxf(x0, x1), am = fmaxf(fabsf(x0), fabsf(x1));
+  const int half_lanes = t.G >> 1;
+  for (int off = 1; off < half_lanes; off <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, off, 64));
+    hi = fmaxf(hi, __shfl_xor(hi, off, 64));
+    am = fmaxf(am, __shfl_xor(am, off, 64));
+  }
+  const bool writer = (lane & (half_lanes - 1)) == 0;
+  const int grp = c0 / t.G;
+  if (t.quant == KVQ_QUANT_SYM_Q8_0) {
+    const uint16_t sh = f2h_rn(am / 127.0f);
+    const float s = h2f(sh);
+    auto code = [&](float x) -> uint32_t {
+      if (s == 0.0f) return 0u;
+      float v = rintf(x / s);
+      v = fminf(fmaxf(v, -128.0f), 127.0f);
+      return (uint32_t)((int)v & 0xff);
+    };
+    q0 = code(x0);
+    q1 = code(x1);
+    if (writer) static_cast<uint16_t*>(prm_row)[grp] = sh;
+    return;
+  }
+  const float qmax = (float)((1 << t.bits) - 1);
+  uint16_t sh;
+  if (t.quant == KVQ_QUANT_ASYM_MINMAX)
+    sh = f2h_rn((hi - lo) / qmax);
+  else
+    sh = f2h_rn(am / (float)((1 << (t.bits - 1)) - 1));
+  const uint16_t zh = f2h_rn(lo);
+  const float s = h2f(sh), z = h2f(zh);
+  auto code = [&](float x) -> uint32_t {
+    if (s == 0.0f) return 0u;
+    float v = rintf((x - z) / s);
+    v = fminf(fmaxf(v, 0.0f), qmax);
+    return (uint32_t)v;
+  };
+  q0 = code(x0);
+  q1 = code(x1);
+  if (writer) static_cast<uint32_t*>(prm_row)[grp] = (uint32_t)sh | ((uint32_t)zh << 16);
+}
+
+// Dword W of a key row, assembled from the row's codes in LDS.
+__device__ __forceinline__ uint32_t k_row_dword(const uint8_t* rowc, int bits, int W) {
+  const int q = W / bits, j = W % bits;
+  uint32_t dw = 0;
+  seg_dword_fields(bits, j, [&](int u, int sh, int, int field) {
+    const int c = 32 * (u >> 3) + 8 * q + (u & 7);
+    dw |= field_value(rowc[c], field) << sh;
+  });
+  return dw;
+}
+
+// ---- per-token rows: keys (K-row layout) and raw rows for NONE --------------
+// One wave per row (b, new token, kv head); 4 rows per 256-thread block.
+__global__ __launch_bounds__(256) void enc_rows_kernel(DevShape sh, DevTensor t, const void* x_new,
+                                                       int64_t n_ctx, int n_new) {
+  __shared__ uint8_t rowc[4][kD];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t nrows = (int64_t)sh.B * n_new * sh.Hkv;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+  const bool active = r < nrows;
+  int b = 0, h = 0;
+  int64_t tpos = 0;
+  uint32_t q0 = 0, q1 = 0;
+  if (active) {
+    h = (int)(r % sh.Hkv);
+    const int64_t bt = r / sh.Hkv;
+    b = (int)(bt / n_new);
+    tpos = n_ctx + bt % n_new;
+    const uint32_t pair = static_cast<const uint32_t*>(x_new)[r * (kD / 2) + lane];
+    const int64_t row = ((int64_t)b * sh.Hkv + h) * sh.Tcap + tpos;
+    if (t.quant == KVQ_QUANT_NONE) {
+      reinterpret_cast<uint32_t*>(t.codes)[row * (kD / 2) + lane] = pair;
+    } else {
+      const float x0 = elem2f((uint16_t)(pair & 0xffff), sh.kv_bf16);
+      const float x1 = elem2f((uint16_t)(pair >> 16), sh.kv_bf16);
+      void* prm = nullptr;
+      if (t.params) prm = static_cast<uint8_t*>(t.params) + row * (int64_t)t.ng *
+                          (t.quant == KVQ_QUANT_SYM_Q8_0 ? 2 : 4);
+      encode_pair(t, h, lane, x0, x1, prm, q0, q1);
+      rowc[wave][2 * lane] = (uint8_t)q0;
+      rowc[wave][2 * lane + 1] = (uint8_t)q1;
+    }
+  }
+  if (t.quant == KVQ_QUANT_NONE) return;
+  __syncthreads();
+  if (active && lane < 4 * t.bits) {
+    const int64_t row = ((int64_t)b * sh.Hkv + h) * sh.Tcap + tpos;
+    reinterpret_cast<uint32_t*>(t.codes + row * t.row_bytes)[lane] =
+        k_row_dword(rowc[wave], t.bits, lane);
+  }
+}
+
+// ---- value tiles --------------------------------------------------------------
+// One block per (tile, b*Hkv + h) touched by the append.  New tokens of the
+// tile are encoded into LDS, then every dword of the tile that holds a new
+// code is rewritten; bits of older tokens are preserved.
+__global__ __launch_bounds__(256) void enc_vtile_kernel(DevShape sh, DevTensor t, const void* x_new,
+                                                        int64_t n_ctx, int n_new, int64_t tile0) {
+  __shared__ uint8_t codes[kTile][kD];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int bh = blockIdx.y;
+  const int b = bh / sh.Hkv, h = bh % sh.Hkv;
+  const int64_t tile = tile0 + blockIdx.x;
+  const int64_t t_begin = tile * kTile;
+  const int64_t lo_new = n_ctx, hi_new = n_ctx + n_new;
+  for (int tau = wave; tau < kTile; tau += 4) {
+    const int64_t tpos = t_begin + tau;
+    if (tpos < lo_new || tpos >= hi_new) continue;       // wave-uniform
+    const int64_t rin = (((int64_t)b * n_new + (tpos - n_ctx)) * sh.Hkv + h);
+    const uint32_t pair = static_cast<const uint32_t*>(x_new)[rin * (kD / 2) + lane];
+    const float x0 = elem2f((uint16_t)(pair & 0xffff), sh.kv_bf16);
+    const float x1 = elem2f((uint16_t)(pair >> 16), sh.kv_bf16);
+    const int64_t row = ((int64_t)b * sh.Hkv + h) * sh.Tcap + tpos;
+    void* prm = nullptr;
+    if (t.params) prm = static_cast<uint8_t*>(t.params) + row * (int64_t)t.ng *
+                        (t.quant == KVQ_QUANT_SYM_Q8_0 ? 2 : 4);
+    uint32_t q0, q1;
+    encode_pair(t, h, lane, x0, x1, prm, q0, q1);
+    codes[tau][2 * lane] = (uint8_t)q0;
+    codes[tau][2 * lane + 1] = (uint8_t)q1;
+  }
+  __syncthreads();
+  const int bits = t.bits;
+  uint32_t* tile_dw = reinterpret_cast<uint32_t*>(
+      t.codes + (((int64_t)b * sh.Hkv + h) * sh.Tcap + t_begin) * t.row_bytes);
+  for (int W = threadIdx.x; W < 128 * bits; W += 256) {
+    const int L = W / (2 * bits), s = (W / bits) & 1, j = W % bits;
+    const int q = L >> 4, i = L & 15;
+    uint32_t nb = 0, nm = 0;
+    seg_dword_fields(bits, j, [&](int u, int shf, int wd, int field) {
+      const int m = u >> 3, e = u & 7;
+      const int tau = e < 4 ? 4 * q + e : 16 + 4 * q + (e - 4);
+      const int c = 16 * (4 * s + m) + i;
+      const int64_t tpos = t_begin + tau;
+      if (tpos >= lo_new && tpos < hi_new) {
+        nb |= field_value(codes[tau][c], field) << shf;
+        nm |= ((1u << wd) - 1u) << shf;
+      }
+    });
+    if (nm == 0) continue;
+    if (nm != 0xffffffffu) nb |= tile_dw[W] & ~nm;
+    tile_dw[W] = nb;
+  }
+}
+
+// ---- per-channel keys ---------------------------------------------------------
+// Quantize completed token groups: one block of 128 threads (one per
+// channel) per (group, b*Hkv + h).  Values of the group that arrived in
+// earlier calls come from the fp16/bf16 tail.
+__global__ __launch_bounds__(128) void enc_kchan_flush_kernel(DevShape sh, DevTensor t,
+                                                              const void* x_new, int64_t n_ctx,
+                                                              int n_new, int64_t g0) {
+  extern __shared__ uint8_t gcodes[];                     // [G][128]
+  const int c = threadIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / sh.Hkv, h = bh % sh.Hkv;
+  const int G = t.G;
+  const int64_t gi = g0 + blockIdx.x;
+  const int64_t p0 = gi * G;
+  const uint16_t* tail = t.tail + (int64_t)bh * G * kD;
+  auto value = [&](int k) -> float {
+    const int64_t p = p0 + k;
+    if (p < n_ctx) return elem2f(tail[(int64_t)k * kD + c], sh.kv_bf16);
+    const int64_t rin = ((int64_t)b * n_new + (p - n_ctx)) * sh.Hkv + h;
+    return load_elem(x_new, rin * kD + c, sh.kv_bf16);
+  };
+  float lo = INFINITY, hi = -INFINITY, am = 0.0f;
+  for (int k = 0; k < G; ++k) {
+    const float x = value(k);
+    lo = fminf(lo, x);
+    hi = fmaxf(hi, x);
+    am = fmaxf(am, fabsf(x));
+  }
+  const float qmax = (float)((1 << t.bits) - 1);
+  uint16_t shh;
+  if (t.quant == KVQ_QUANT_ASYM_MINMAX)
+    shh = f2h_rn((hi - lo) / qmax);
+  else
+    shh = f2h_rn(am / (float)((1 << (t.bits - 1)) - 1));
+  const uint16_t zh = f2h_rn(lo);
+  const float s = h2f(shh), z = h2f(zh);
+  static_cast<uint32_t*>(t.params)[((int64_t)bh * (sh.Tcap / G) + gi) * kD + c] =
+      (uint32_t)shh | ((uint32_t)zh << 16);
+  for (int k = 0; k < G; ++k) {
+    uint32_t q = 0;
+    if (s != 0.0f) {
+      float v = rintf((value(k) - z) / s);
+      q = (uint32_t)fminf(fmaxf(v, 0.0f), qmax);
+    }
+    gcodes[k * kD + c] = (uint8_t)q;
+  }
+  __syncthreads();
+  const int dw_per_row = 4 * t.bits;
+  uint8_t* rows = t.codes + ((int64_t)bh * sh.Tcap + p0) * t.row_bytes;
+  for (int idx = threadIdx.x; idx < G * dw_per_row; idx += blockDim.x) {
+    const int k = idx / dw_per_row, W = idx % dw_per_row;
+    reinterpret_cast<uint32_t*>(rows + (int64_t)k * t.row_bytes)[W] =
+        k_row_dword(gcodes + k * kD, t.bits, W);
+  }
+  // The tail's tokens are now quantized: clear the slots they used.
+  if (p0 < n_ctx) {
+    const int used = (int)(n_ctx - p0);
+    uint16_t* tw = t.tail + (int64_t)bh * G * kD;
+    for (int k = 0; k < used; ++k) tw[(int64_t)k * kD + c] = 0;
+  }
+}
+
+// Copy tokens of the unfinished last group into the tail.
+__global__ __launch_bounds__(64) void enc_kchan_tail_kernel(DevShape sh, DevTensor t,
+                                                            const void* x_new, int64_t n_ctx,
+                                                            int n_new, int64_t p_first,
+                                                            int64_t group_start) {
+  const int bh = blockIdx.y;
+  const int b = bh / sh.Hkv, h = bh % sh.Hkv;
+  const int64_t p = p_first + blockIdx.x;
+  const int64_t rin = ((int64_t)b * n_new + (p - n_ctx)) * sh.Hkv + h;
+  const uint32_t pair = static_cast<const uint32_t*>(x_new)[rin * (kD / 2) + threadIdx.x];
+  uint32_t* dst = reinterpret_cast<uint32_t*>(t.tail + ((int64_t)bh * t.G + (p - group_start)) * kD);
+  dst[threadIdx.x] = pair;
+}
+
+// ---- dense-and-sparse outliers (CODEBOOK) ----------------------------------
+// One block per (new token, b).  Keys (|x| bits << 16 | 0xffff - index) are
+// unique, so the k largest are found exactly by a most-significant-bit-first
+// search for the k-th largest key; they are then written in index order.
+__global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTensor t,
+                                                           const void* x_new, int64_t n_ctx,
+                                                           int n_new) {
+  extern __shared__ uint32_t keys[];                      // [n]
+  __shared__ uint32_t red[8];
+  __shared__ uint32_t scan[256];
+  const int n = sh.Hkv * kD;
+  const int k = t.k_out;
+  const int tn = blockIdx.x, b = blockIdx.y;
+  const int64_t tpos = n_ctx + tn;
+  const uint16_t* xr = static_cast<const uint16_t*>(x_new) + ((int64_t)b * n_new + tn) * n;
+  for (int i = threadIdx.x; i < n; i += 256)
+    keys[i] = ((uint32_t)(xr[i] & 0x7fffu) << 16) | (0xffffu - (uint32_t)i);
+  __syncthreads();
+  const int per = (n + 255) / 256;
+  const int i0 = threadIdx.x * per, i1 = min(n, i0 + per);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t prefix = 0;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    uint32_t cnt = 0;
+    for (int i = i0; i < i1; ++i) cnt += keys[i] >= cand;
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+    if (lane == 0) red[wave] = cnt;
+    __syncthreads();
+    const uint32_t tot = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    if (tot >= (uint32_t)k) prefix = cand;
+  }
+  uint32_t mine = 0;
+  for (int i = i0; i < i1; ++i) mine += keys[i] >= prefix;
+  scan[threadIdx.x] = mine;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const uint32_t v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0u;
+    __syncthreads();
+    scan[threadIdx.x] += v;
+    __syncthreads();
+  }
+  uint32_t pos = scan[threadIdx.x] - mine;
+  const int64_t r = (int64_t)b * sh.Tcap + tpos;
+  for (int i = i0; i < i1; ++i) {
+    if (keys[i] >= prefix) {
+      t.col[r * k + pos] = (uint16_t)i;
+      t.val[r * k + pos] = xr[i];
+      ++pos;
+    }
+  }
+  if (threadIdx.x == 0) {
+    t.row_ptr[r + 1] = (int32_t)(k * (r + 1));
+    if (tn == 0) t.row_ptr[r] = (int32_t)(k * r);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_encode_tensor(const DevShape& sh, const DevTensor& t, bool is_key,
+                                const void* x_new, int64_t n_ctx, int n_new,
+                                hipStream_t stream) {
+  const int64_t nrows = (int64_t)sh.B * n_new * sh.Hkv;
+  if (t.quant == KVQ_QUANT_NONE || (is_key && !t.per_channel)) {
+    const int64_t blocks = (nrows + 3) / 4;
+    hipLaunchKernelGGL(enc_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, sh, t, x_new,
+                       n_ctx, n_new);
+  } else if (is_key) {
+    const int G = t.G;
+    const int64_t n1 = n_ctx + n_new;
+    const int64_t g_first = n_ctx / G, g_end = n1 / G;   // groups [g_first, g_end) complete now
+    if (g_end > g_first) {
+      hipLaunchKernelGGL(enc_kchan_flush_kernel, dim3((unsigned)(g_end - g_first), sh.B * sh.Hkv),
+                         dim3(128), (size_t)G * kD, stream, sh, t, x_new, n_ctx, n_new, g_first);
+    }
+    const int64_t group_start = g_end * G;
+    const int64_t p_first = n_ctx > group_start ? n_ctx : group_start;
+    if (n1 > p_first) {
+      hipLaunchKernelGGL(enc_kchan_tail_kernel, dim3((unsigned)(n1 - p_first), sh.B * sh.Hkv),
+                         dim3(64), 0, stream, sh, t, x_new, n_ctx, n_new, p_first, group_start);
+    }
+  } else {
+    const int64_t tile0 = n_ctx / kTile, tile1 = (n_ctx + n_new - 1) / kTile;
+    hipLaunchKernelGGL(enc_vtile_kernel, dim3((unsigned)(tile1 - tile0 + 1), sh.B * sh.Hkv),
+                       dim3(256), 0, stream, sh, t, x_new, n_ctx, n_new, tile0);
+  }
+  if (t.k_out > 0) {
+    hipLaunchKernelGGL(enc_outliers_kernel, dim3(n_new, sh.B), dim3(256),
+                       (size_t)sh.Hkv * kD * 4, stream, sh, t, x_new, n_ctx, n_new);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,369 @@
+// Host side of libkvq: argument checks, cache layout, cache sizes and the
+// dispatch of the HIP kernels.  Everything here runs before any launch, so
+// a rejected call leaves the device and the cache untouched.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include <hip/hip_runtime_api.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+thread_local std::string g_last_error;
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int outlier_count(float frac, int n) {
+  if (!(frac > 0.0f)) return 0;
+  return (int)ceil((double)frac * (double)n);
+}
+
+kvq_status check_format(const kvq_tensor_format& f, const kvq_config& c, bool is_key,
+                        const char* name) {
+  const int d = c.head_dim;
+  if (f.quantizer != KVQ_QUANT_CODEBOOK && f.outlier_frac != 0.0f)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: outlier_frac is only valid for CODEBOOK", name);
+  if (f.layout != KVQ_LAYOUT_PER_TOKEN && f.layout != KVQ_LAYOUT_PER_CHANNEL)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: unknown layout %d", name, f.layout);
+  switch (f.quantizer) {
+    case KVQ_QUANT_NONE:
+      if (f.bits != 16) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: NONE needs bits = 16", name);
+      if (f.layout != KVQ_LAYOUT_PER_TOKEN)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: NONE has no per-channel layout", name);
+      return KVQ_OK;
+    case KVQ_QUANT_ASYM_MINMAX:
+    case KVQ_QUANT_ASYM_ABSMAX_OFFSET:
+      if (f.bits != 3 && f.bits != 4 && f.bits != 8)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: bits must be 3, 4 or 8 (got %d)", name, f.bits);
+      break;
+    case KVQ_QUANT_SYM_Q8_0:
+      if (f.bits != 8) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: q8_0 needs bits = 8", name);
+      if (f.layout != KVQ_LAYOUT_PER_TOKEN)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: q8_0 blocks run along head_dim", name);
+      break;
+    case KVQ_QUANT_CODEBOOK:
+      if (f.bits != 4) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: CODEBOOK needs bits = 4", name);
+      if (f.layout != KVQ_LAYOUT_PER_TOKEN)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: CODEBOOK uses per-(head, channel) codebooks "
+                    "and the per-token layout", name);
+      if (!(f.outlier_frac >= 0.0f && f.outlier_frac <= 0.25f))
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: outlier_frac must be in [0, 0.25]", name);
+      if (f.outlier_frac > 0.0f && (int64_t)c.n_kv_heads * d > 8192)
+        return fail(KVQ_ERR_UNSUPPORTED, "%s: outlier selection needs n_kv_heads * head_dim <= 8192",
+                    name);
+      return KVQ_OK;
+    default:
+      return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: unknown quantizer %d", name, f.quantizer);
+  }
+  if (f.layout == KVQ_LAYOUT_PER_TOKEN) {
+    if (f.group_size != 32 && f.group_size != 64 && f.group_size != 128)
+      return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: per-token group_size must be 32, 64 or 128 "
+                  "(got %d)", name, f.group_size);
+  } else {
+    if (!is_key)
+      return fail(KVQ_ERR_UNSUPPORTED, "%s: per-channel layout is supported for keys only", name);
+    if (f.group_size < 32 || f.group_size > 256 || f.group_size % 32)
+      return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: per-channel group_size must be a multiple of 32 "
+                  "in [32, 256] (got %d)", name, f.group_size);
+  }
+  return KVQ_OK;
+}
+
+kvq_status check_config(const kvq_config* c) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARGUMENT, "config is NULL");
+  if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "batch and head counts must be >= 1");
+  if (c->n_q_heads % c->n_kv_heads)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                c->n_q_heads, c->n_kv_heads);
+  if (c->head_dim != kHeadDim)
+    return fail(KVQ_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", c->head_dim);
+  if (c->max_ctx < 1 || c->max_ctx > (int64_t)1 << 30)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "max_ctx must be in [1, 2^30] (got %lld)",
+                (long long)c->max_ctx);
+  if (c->kv_dtype != KVQ_F16 && c->kv_dtype != KVQ_BF16)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "kv_dtype must be KVQ_F16 or KVQ_BF16");
+  if (c->rope != 0 && c->rope != 1) return fail(KVQ_ERR_INVALID_ARGUMENT, "rope must be 0 or 1");
+  if (c->rope && !(c->rope_base > 1.0f))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "rope_base must be > 1");
+  if (c->decode_splits < 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "decode_splits must be >= 0");
+  if (c->decode_path < KVQ_PATH_AUTO || c->decode_path > KVQ_PATH_MFMA)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "unknown decode_path %d", c->decode_path);
+  if ((uint64_t)c->batch * (uint64_t)c->max_ctx > ((uint64_t)1 << 31))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "batch * max_ctx must be <= 2^31");
+  kvq_status st = check_format(c->k, *c, true, "k");
+  if (st != KVQ_OK) return st;
+  return check_format(c->v, *c, false, "v");
+}
+
+void fill_tensor(TensorLayout& t, const kvq_tensor_format& f, const kvq_config& c, int64_t Tcap,
+                 uint64_t& off) {
+  const uint64_t B = c.batch, H = c.n_kv_heads, d = c.head_dim;
+  t.quant = f.quantizer;
+  t.bits = f.quantizer == KVQ_QUANT_NONE ? 16 : f.bits;
+  t.per_channel = f.layout == KVQ_LAYOUT_PER_CHANNEL;
+  t.G = (f.quantizer == KVQ_QUANT_NONE || f.quantizer == KVQ_QUANT_CODEBOOK) ? 0 : f.group_size;
+  t.row_bytes = (int)(d * t.bits / 8);
+  t.ng = (t.G && !t.per_channel) ? (int)(d / t.G) : 0;
+  t.psize = f.quantizer == KVQ_QUANT_SYM_Q8_0 ? 2 : 4;
+  t.k_out = f.quantizer == KVQ_QUANT_CODEBOOK ? outlier_count(f.outlier_frac, (int)(H * d)) : 0;
+  auto put = [&](uint64_t& o, uint64_t& sz, uint64_t bytes) {
+    o = off;
+    sz = bytes;
+    off = align_up(off + bytes, 256);
+  };
+  put(t.codes_off, t.codes_bytes, B * H * (uint64_t)Tcap * t.row_bytes);
+  if (t.G) {
+    if (t.per_channel)
+      put(t.params_off, t.params_bytes, B * H * (uint64_t)(Tcap / t.G) * d * 4);
+    else
+      put(t.params_off, t.params_bytes, B * H * (uint64_t)Tcap * t.ng * t.psize);
+  }
+  if (t.per_channel) put(t.tail_off, t.tail_bytes, B * H * (uint64_t)t.G * d * 2);
+  if (t.k_out) {
+    put(t.rowptr_off, t.rowptr_bytes, (B * (uint64_t)Tcap + 1) * 4);
+    put(t.col_off, t.col_bytes, B * (uint64_t)Tcap * t.k_out * 2);
+    put(t.val_off, t.val_bytes, B * (uint64_t)Tcap * t.k_out * 2);
+  }
+}
+
+Layout make_layout(const kvq_config& c) {
+  Layout L;
+  L.Tcap = (int64_t)align_up((uint64_t)c.max_ctx, kTile);
+  uint64_t off = 0;
+  fill_tensor(L.k, c.k, c, L.Tcap, off);
+  fill_tensor(L.v, c.v, c, L.Tcap, off);
+  int64_t s = (L.Tcap + 63) / 64;
+  L.S_max = (int)(s < 1 ? 1 : (s > 256 ? 256 : s));
+  L.ws_off = off;
+  L.partial_off = off;
+  off = align_up(off + (uint64_t)c.batch * c.n_q_heads * L.S_max * (c.head_dim + 2) * 4, 256);
+  L.counter_off = off;
+  off = align_up(off + (uint64_t)c.batch * c.n_kv_heads * 4, 256);
+  L.ws_bytes = off - L.ws_off;
+  L.total = off;
+  return L;
+}
+
+uint64_t tensor_payload(const TensorLayout& t, const kvq_config& c, int64_t n) {
+  const uint64_t B = c.batch, H = c.n_kv_heads, d = c.head_dim;
+  if (t.quant == KVQ_QUANT_NONE) return B * H * (uint64_t)n * d * 2;
+  uint64_t total;
+  if (t.quant == KVQ_QUANT_CODEBOOK) {
+    total = B * H * (uint64_t)n * t.row_bytes + H * d * 16 * 2;
+    if (t.k_out) total += B * (uint64_t)n * (4 + 4 * (uint64_t)t.k_out);
+    return total;
+  }
+  if (t.per_channel) {
+    uint64_t nf = (uint64_t)(n / t.G) * t.G;
+    return B * H * (nf * t.row_bytes + (nf / t.G) * d * 4 + ((uint64_t)n - nf) * d * 2);
+  }
+  return B * H * (uint64_t)n * (t.row_bytes + (uint64_t)t.ng * t.psize);
+}
+
+void fill_regions(kvq_tensor_regions& r, const TensorLayout& t) {
+  r.codes = {t.codes_off, t.codes_bytes};
+  r.params = {t.params_off, t.params_bytes};
+  r.tail = {t.tail_off, t.tail_bytes};
+  r.row_ptr = {t.rowptr_off, t.rowptr_bytes};
+  r.col = {t.col_off, t.col_bytes};
+  r.val = {t.val_off, t.val_bytes};
+}
+
+kvq_status check_codebooks(const kvq_config& c, const kvq_cache& cache) {
+  const bool kc = c.k.quantizer == KVQ_QUANT_CODEBOOK, vc = c.v.quantizer == KVQ_QUANT_CODEBOOK;
+  if (kc != (cache.k_codebook != nullptr))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "k_codebook must be given iff keys use CODEBOOK");
+  if (vc != (cache.v_codebook != nullptr))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "v_codebook must be given iff values use CODEBOOK");
+  if ((cache.k_codebook && !aligned16(cache.k_codebook)) ||
+      (cache.v_codebook && !aligned16(cache.v_codebook)))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "codebook pointers must be 16-byte aligned");
+  return KVQ_OK;
+}
+
+kvq_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(KVQ_ERR_DEVICE, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+  return KVQ_OK;
+}
+
+}  // namespace
+
+DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebook) {
+  uint8_t* b = static_cast<uint8_t*>(base);
+  DevTensor t;
+  t.quant = tl.quant;
+  t.bits = tl.bits;
+  t.G = tl.G;
+  t.per_channel = tl.per_channel;
+  t.row_bytes = tl.row_bytes;
+  t.ng = tl.ng;
+  t.k_out = tl.k_out;
+  t.codes = b + tl.codes_off;
+  t.params = tl.params_bytes ? b + tl.params_off : nullptr;
+  t.tail = tl.tail_bytes ? reinterpret_cast<uint16_t*>(b + tl.tail_off) : nullptr;
+  t.row_ptr = tl.rowptr_bytes ? reinterpret_cast<int32_t*>(b + tl.rowptr_off) : nullptr;
+  t.col = tl.col_bytes ? reinterpret_cast<uint16_t*>(b + tl.col_off) : nullptr;
+  t.val = tl.val_bytes ? reinterpret_cast<uint16_t*>(b + tl.val_off) : nullptr;
+  t.codebook = static_cast<const uint16_t*>(codebook);
+  return t;
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+const char* kvq_last_error(void) { return g_last_error.c_str(); }
+
+int32_t kvq_abi_version(void) { return 100; }
+
+kvq_status kvq_cache_bytes(const kvq_config* cfg, int64_t n_ctx, int64_t n_layers, int32_t what,
+                           uint64_t* out_bytes) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!out_bytes) return fail(KVQ_ERR_INVALID_ARGUMENT, "out_bytes is NULL");
+  Layout L = make_layout(*cfg);
+  if (what == KVQ_BYTES_ALLOC) {
+    *out_bytes = L.total;
+    return KVQ_OK;
+  }
+  if (what != KVQ_BYTES_PAYLOAD) return fail(KVQ_ERR_INVALID_ARGUMENT, "unknown selector %d", what);
+  if (n_ctx < 0 || n_layers < 0)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "n_ctx and n_layers must be >= 0");
+  *out_bytes = (uint64_t)n_layers * (tensor_payload(L.k, *cfg, n_ctx) + tensor_payload(L.v, *cfg, n_ctx));
+  return KVQ_OK;
+}
+
+kvq_status kvq_cache_layout(const kvq_config* cfg, kvq_layout_info* out) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!out) return fail(KVQ_ERR_INVALID_ARGUMENT, "out is NULL");
+  Layout L = make_layout(*cfg);
+  memset(out, 0, sizeof *out);
+  fill_regions(out->k, L.k);
+  fill_regions(out->v, L.v);
+  out->workspace = {L.ws_off, L.ws_bytes};
+  out->total_bytes = L.total;
+  out->capacity = L.Tcap;
+  out->max_splits = L.S_max;
+  return KVQ_OK;
+}
+
+kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new,
+                               const void* v_new, int32_t n_new, void* stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!cache) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (!cache->base || !aligned16(cache->base))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "cache->base must be a 16-byte aligned device pointer");
+  if (n_new < 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "n_new must be >= 0");
+  if (cache->n_ctx < 0 || cache->n_ctx > cfg->max_ctx)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "cache->n_ctx out of range");
+  st = check_codebooks(*cfg, *cache);
+  if (st != KVQ_OK) return st;
+  if (n_new == 0) return KVQ_OK;
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "k_new and v_new must be 16-byte aligned device pointers");
+  if (cache->n_ctx + n_new > cfg->max_ctx)
+    return fail(KVQ_ERR_CAPACITY, "append of %d tokens at n_ctx %lld exceeds max_ctx %lld", n_new,
+                (long long)cache->n_ctx, (long long)cfg->max_ctx);
+  Layout L = make_layout(*cfg);
+  DevShape sh{cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, cfg->n_q_heads / cfg->n_kv_heads,
+              cfg->kv_dtype == KVQ_BF16, L.Tcap};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DevTensor kt = make_dev_tensor(L.k, cache->base, cache->k_codebook);
+  DevTensor vt = make_dev_tensor(L.v, cache->base, cache->v_codebook);
+  st = device_status(launch_encode_tensor(sh, kt, true, k_new, cache->n_ctx, n_new, s), "encode keys");
+  if (st != KVQ_OK) return st;
+  st = device_status(launch_encode_tensor(sh, vt, false, v_new, cache->n_ctx, n_new, s),
+                     "encode values");
+  if (st != KVQ_OK) return st;
+  cache->n_ctx += n_new;
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                                const int32_t* q_pos, float sm_scale, void* out,
+                                int32_t out_dtype, void* stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!cache) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (!cache->base || !aligned16(cache->base))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "cache->base must be a 16-byte aligned device pointer");
+  if (cache->n_ctx < 1 || cache->n_ctx > cfg->max_ctx)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "n_ctx must be in [1, max_ctx] (got %lld): attention "
+                "over an empty cache is undefined", (long long)cache->n_ctx);
+  st = check_codebooks(*cfg, *cache);
+  if (st != KVQ_OK) return st;
+  if (!q || !out || !aligned16(q) || !aligned16(out))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "q and out must be 16-byte aligned device pointers");
+  if (q_pos && !aligned16(q_pos))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "q_pos must be 16-byte aligned");
+  if (out_dtype != KVQ_F32 && out_dtype != KVQ_F16 && out_dtype != KVQ_BF16)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "out_dtype must be KVQ_F32, KVQ_F16 or KVQ_BF16");
+  if (!isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+
+  Layout L = make_layout(*cfg);
+  DecodeArgs a;
+  a.sh = DevShape{cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, cfg->n_q_heads / cfg->n_kv_heads,
+                  cfg->kv_dtype == KVQ_BF16, L.Tcap};
+  a.k = make_dev_tensor(L.k, cache->base, cache->k_codebook);
+  a.v = make_dev_tensor(L.v, cache->base, cache->v_codebook);
+  a.q = q;
+  a.q_pos = q_pos;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)cfg->head_dim));
+  a.rope = cfg->rope;
+  a.rope_base = cfg->rope_base;
+  a.n_ctx = (int)cache->n_ctx;
+  a.S_max = L.S_max;
+  a.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(cache->base) + L.partial_off);
+  a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(cache->base) + L.counter_off);
+
+  // Split the token axis so that the grid covers the GPU several times:
+  // about 2048 workgroups, each with at least two 32-token blocks per wave.
+  const int64_t nblocks = (a.n_ctx + kTile - 1) / kTile;
+  const int64_t pairs = (int64_t)cfg->batch * cfg->n_kv_heads;
+  int64_t want = (2048 + pairs - 1) / pairs;
+  int64_t by_len = nblocks / 8;
+  if (want > by_len) want = by_len;
+  if (cfg->decode_splits > 0 && want > cfg->decode_splits) want = cfg->decode_splits;
+  if (want > L.S_max) want = L.S_max;
+  if (want < 1) want = 1;
+  a.blocks_per_split = (int)((nblocks + want - 1) / want);
+  a.splits = (int)((nblocks + a.blocks_per_split - 1) / a.blocks_per_split);
+
+  const bool mfma_ok = mfma_supported(a);
+  if (cfg->decode_path == KVQ_PATH_MFMA && !mfma_ok)
+    return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core decode kernel needs uniform or raw formats, "
+                "no RoPE and at most 8 query heads per KV head");
+  const bool use_mfma = mfma_ok && cfg->decode_path != KVQ_PATH_VALU;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = use_mfma ? launch_decode_mfma(a, s) : launch_decode_generic(a, s);
+  return device_status(e, "decode attention");
+}
+
+}  // extern "C"

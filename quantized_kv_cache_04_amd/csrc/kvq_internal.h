@@ -1,0 +1,91 @@
+// Internal declarations shared by the host entry points and the kernel
+// launchers of libkvq.  Not part of the public interface (include/kvq.h).
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int kHeadDim = 128;
+constexpr int kTile = 32;          // tokens per value tile / decode block
+
+// Host-side description of one cache tensor (keys or values) and where its
+// arrays sit in the allocation.
+struct TensorLayout {
+  int quant = 0;        // KVQ_QUANT_*
+  int bits = 16;
+  int G = 0;            // group size (0 for NONE / CODEBOOK)
+  int per_channel = 0;  // 1: groups along tokens (keys only)
+  int row_bytes = 0;    // bytes of one token's codes (raw: d * 2)
+  int ng = 0;           // groups per token (per-token layouts)
+  int psize = 0;        // bytes per group parameter record (4: scale+zero, 2: scale)
+  int k_out = 0;        // outliers kept per token (CODEBOOK)
+  uint64_t codes_off = 0, codes_bytes = 0;
+  uint64_t params_off = 0, params_bytes = 0;
+  uint64_t tail_off = 0, tail_bytes = 0;
+  uint64_t rowptr_off = 0, rowptr_bytes = 0;
+  uint64_t col_off = 0, col_bytes = 0;
+  uint64_t val_off = 0, val_bytes = 0;
+};
+
+struct Layout {
+  TensorLayout k, v;
+  int64_t Tcap = 0;          // token capacity per sequence (multiple of 32)
+  int S_max = 1;             // partial slots per (b, query head)
+  uint64_t partial_off = 0;  // float [B][Hq][S_max][d + 2]
+  uint64_t counter_off = 0;  // uint32 [B][Hkv]
+  uint64_t ws_off = 0, ws_bytes = 0;
+  uint64_t total = 0;
+};
+
+// Device-side view of one tensor, passed by value to kernels.
+struct DevTensor {
+  int quant, bits, G, per_channel, row_bytes, ng, k_out;
+  uint8_t* codes;
+  void* params;
+  uint16_t* tail;
+  int32_t* row_ptr;
+  uint16_t* col;
+  uint16_t* val;
+  const uint16_t* codebook;   // fp16 [Hkv][d][16]
+};
+
+struct DevShape {
+  int B, Hq, Hkv, g, kv_bf16;
+  int64_t Tcap;
+};
+
+DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebook);
+
+// ---- encode launchers (encode.hip) ----------------------------------------
+hipError_t launch_encode_tensor(const DevShape& sh, const DevTensor& t, bool is_key,
+                                const void* x_new, int64_t n_ctx, int n_new,
+                                hipStream_t stream);
+
+// ---- decode launchers ------------------------------------------------------
+struct DecodeArgs {
+  DevShape sh;
+  DevTensor k, v;
+  const void* q;
+  const int32_t* q_pos;
+  void* out;
+  int out_dtype;
+  float sm_scale;       // softmax scale (already resolved)
+  int rope;
+  float rope_base;
+  int n_ctx;
+  int splits;           // splits actually used (>= 1)
+  int blocks_per_split; // 32-token blocks per split
+  int S_max;
+  float* partial;       // [B][Hq][S_max][d + 2]
+  uint32_t* counters;   // [B][Hkv]
+};
+
+hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
+bool mfma_supported(const DecodeArgs& a);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,209 @@
+"""ctypes binding of libkvq (include/kvq.h): argument marshalling only.
+
+Every step of the quantized-cache path runs in the HIP library; this module
+converts Python/torch arguments into the C structs and device pointers the
+C ABI expects, and raises ``KvqError`` on a non-OK status.  torch is used
+for device memory and the current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Any, Dict, Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvq.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvq.h")
+
+# ---- constants mirrored from kvq.h -------------------------------------------
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_DEVICE = 0, -1, -2, -3, -4
+F16, BF16, F32 = 0, 1, 2
+QUANT = {"none": 0, "asym_minmax": 1, "asym_absmax_offset": 2, "sym_q8_0": 3, "codebook": 4}
+LAYOUT = {"per_token": 0, "per_channel": 1}
+BYTES_PAYLOAD, BYTES_ALLOC = 0, 1
+PATHS = {"auto": 0, "valu": 1, "mfma": 2}
+DTYPES = {"f16": F16, "bf16": BF16, "f32": F32}
+
+
+class TensorFormat(ctypes.Structure):
+    _fields_ = [("quantizer", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("outlier_frac", ctypes.c_float)]
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("max_ctx", ctypes.c_int64), ("kv_dtype", ctypes.c_int32),
+                ("rope", ctypes.c_int32), ("rope_base", ctypes.c_float),
+                ("decode_splits", ctypes.c_int32), ("decode_path", ctypes.c_int32),
+                ("k", TensorFormat), ("v", TensorFormat)]
+
+
+class CacheStruct(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("k_codebook", ctypes.c_void_p),
+                ("v_codebook", ctypes.c_void_p), ("n_ctx", ctypes.c_int64)]
+
+
+class Region(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_uint64), ("bytes", ctypes.c_uint64)]
+
+
+class TensorRegions(ctypes.Structure):
+    _fields_ = [("codes", Region), ("params", Region), ("tail", Region), ("row_ptr", Region),
+                ("col", Region), ("val", Region)]
+
+
+class LayoutInfo(ctypes.Structure):
+    _fields_ = [("k", TensorRegions), ("v", TensorRegions), ("workspace", Region),
+                ("total_bytes", ctypes.c_uint64), ("capacity", ctypes.c_int64),
+                ("max_splits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"kvq status {status}: {msg}")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree libkvq.so (built by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.kvq_cache_bytes.argtypes = [ctypes.POINTER(Config), ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]
+        L.kvq_cache_layout.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(LayoutInfo)]
+        L.kvq_quantize_append.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(CacheStruct),
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_void_p]
+        L.kvq_decode_attention.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(CacheStruct),
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+                                           ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+        for fn in ("kvq_cache_bytes", "kvq_cache_layout", "kvq_quantize_append",
+                   "kvq_decode_attention"):
+            getattr(L, fn).restype = ctypes.c_int32
+        L.kvq_last_error.restype = ctypes.c_char_p
+        L.kvq_last_error.argtypes = []
+        L.kvq_abi_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def declared_symbols() -> list:
+    """Names of the functions include/kvq.h declares."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"^\s*(?:kvq_status|const char\*|int32_t)\s+(kvq_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def _check(st: int) -> None:
+    if st != OK:
+        raise KvqError(st, lib().kvq_last_error().decode())
+
+
+def fmt_struct(f: Dict[str, Any]) -> TensorFormat:
+    return TensorFormat(QUANT[f["quantizer"]], int(f["bits"]), int(f.get("group_size", 0)),
+                        LAYOUT[f.get("layout", "per_token")], float(f.get("outlier_frac", 0.0)))
+
+
+def make_config(*, batch: int, n_q_heads: int, n_kv_heads: int, max_ctx: int,
+                kv_dtype: str, k: Dict[str, Any], v: Dict[str, Any], head_dim: int = 128,
+                rope: bool = False, rope_base: float = 10000.0, decode_splits: int = 0,
+                decode_path: str = "auto") -> Config:
+    return Config(batch, n_q_heads, n_kv_heads, head_dim, max_ctx, DTYPES[kv_dtype],
+                  int(bool(rope)), float(rope_base), int(decode_splits), PATHS[decode_path],
+                  fmt_struct(k), fmt_struct(v))
+
+
+def config_from_workload(w, max_ctx: Optional[int] = None, decode_splits: int = 0,
+                         decode_path: str = "auto") -> Config:
+    return make_config(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                       max_ctx=max_ctx if max_ctx is not None else w.ctx, kv_dtype=w.kv_dtype,
+                       k=w.k, v=w.v, head_dim=w.head_dim, rope=w.rope, rope_base=w.rope_base,
+                       decode_splits=decode_splits, decode_path=decode_path)
+
+
+def cache_bytes(cfg: Config, n_ctx: int = 0, n_layers: int = 1, what: int = BYTES_PAYLOAD) -> int:
+    out = ctypes.c_uint64(0)
+    _check(lib().kvq_cache_bytes(ctypes.byref(cfg), int(n_ctx), int(n_layers), int(what),
+                                 ctypes.byref(out)))
+    return int(out.value)
+
+
+def cache_layout(cfg: Config) -> LayoutInfo:
+    info = LayoutInfo()
+    _check(lib().kvq_cache_layout(ctypes.byref(cfg), ctypes.byref(info)))
+    return info
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class Cache:
+    """A cache allocation (zero-filled torch uint8 device buffer) plus the
+    host-side token count.  Codebooks, when used, are fp16 [Hkv, d, 16]
+    device tensors that must outlive the cache."""
+
+    def __init__(self, cfg: Config, device="cuda", k_codebook=None, v_codebook=None):
+        import torch
+        self.cfg = cfg
+        self.layout = cache_layout(cfg)
+        self.buffer = torch.zeros(int(self.layout.total_bytes), dtype=torch.uint8, device=device)
+        self.k_codebook = k_codebook.contiguous() if k_codebook is not None else None
+        self.v_codebook = v_codebook.contiguous() if v_codebook is not None else None
+        self.n_ctx = 0
+
+    def struct(self) -> CacheStruct:
+        return CacheStruct(self.buffer.data_ptr(),
+                           self.k_codebook.data_ptr() if self.k_codebook is not None else None,
+                           self.v_codebook.data_ptr() if self.v_codebook is not None else None,
+                           self.n_ctx)
+
+    def region(self, tensor: str, name: str):
+        """uint8 view of one array of the allocation (e.g. ("k", "codes"))."""
+        r = getattr(getattr(self.layout, tensor), name)
+        return self.buffer[r.offset:r.offset + r.bytes]
+
+    def append(self, k_new, v_new, stream=None) -> None:
+        quantize_append(self, k_new, v_new, stream)
+
+    def decode(self, q, q_pos=None, sm_scale: float = 0.0, out=None, out_dtype: str = "f32",
+               stream=None):
+        return decode_attention(self, q, q_pos=q_pos, sm_scale=sm_scale, out=out,
+                                out_dtype=out_dtype, stream=stream)
+
+
+def quantize_append(cache: Cache, k_new, v_new, stream=None) -> None:
+    """Append k_new/v_new ([B, n_new, Hkv, d], cache dtype, contiguous, on the device)."""
+    n_new = int(k_new.shape[1])
+    cs = cache.struct()
+    _check(lib().kvq_quantize_append(ctypes.byref(cache.cfg), ctypes.byref(cs),
+                                     k_new.data_ptr(), v_new.data_ptr(), n_new,
+                                     _stream_ptr(stream)))
+    cache.n_ctx = int(cs.n_ctx)
+
+
+def decode_attention(cache: Cache, q, q_pos=None, sm_scale: float = 0.0, out=None,
+                     out_dtype: str = "f32", stream=None):
+    """One decode step: q [B, Hq, d] -> out [B, Hq, d] of ``out_dtype``."""
+    import torch
+    if out is None:
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[out_dtype]
+        out = torch.empty(q.shape, dtype=tdt, device=q.device)
+    cs = cache.struct()
+    _check(lib().kvq_decode_attention(ctypes.byref(cache.cfg), ctypes.byref(cs), q.data_ptr(),
+                                      q_pos.data_ptr() if q_pos is not None else None,
+                                      float(sm_scale), out.data_ptr(), DTYPES[out_dtype],
+                                      _stream_ptr(stream)))
+    return out

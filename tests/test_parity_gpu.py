@@ -1,0 +1,128 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Packed codes, scales, zero points, tails and CSR outliers must match the
+oracle byte for byte (including the untouched zero bytes of the capacity);
+decode attention must match the oracle's float64 attention over the same
+dequantized cache to max-abs <= 2e-3 and relative L2 <= 1e-3.
+
+Sizes here are small enough for the oracle to finish in seconds, yet span
+several 32-token tiles, several quantization groups and a ragged tail.
+"""
+import numpy as np
+import pytest
+import torch
+
+from synth import make_inputs, make_workload
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from parity import (MAX_ABS, REL_L2, attention_errors, compare_regions,  # noqa: E402
+                    gpu_cache, oracle_attention, oracle_encode)
+
+# (name, config id, workload overrides, append chunks)
+CASES = [
+    ("tiny_full", 1, {}, [512]),
+    ("tiny_ragged_chunks", 1, dict(ctx=500), [1, 30, 33, 64, 100, 272]),
+    ("tiny_single_token", 1, dict(ctx=1), [1]),
+    ("q8_0_4k", 2, dict(ctx=4096), [4096]),
+    ("q8_0_16k_chunks", 2, dict(ctx=16384), [8000, 1, 8383]),
+    ("q8_0_ragged", 2, dict(ctx=77), [77]),
+    ("u3_b2", 3, dict(batch=2, n_kv_heads=2, ctx=1000), [1000]),
+    ("u3_chunks", 3, dict(batch=2, n_kv_heads=2, ctx=333), [7, 100, 226]),
+    ("nuq_4heads", 4, dict(n_kv_heads=4, ctx=700), [700]),
+    ("nuq_32heads_chunks", 4, dict(ctx=300), [100, 1, 199]),
+    ("serving_small", 5, dict(batch=3, n_kv_heads=2, ctx=1000), [900] + [1] * 100),
+    ("serving_group_edge", 5, dict(batch=2, n_kv_heads=2, ctx=384), [127, 1, 128, 128]),
+]
+
+
+def _run(name, cfg_id, over, chunks, decode_path="auto", decode_splits=0, max_extra=37):
+    print(f"[parity] case={name} cfg={cfg_id} over={over} path={decode_path}", flush=True)
+    w = make_workload(cfg_id, **over)
+    inputs = make_inputs(w, "cpu")
+    n = w.ctx
+    assert sum(chunks) == n
+    max_ctx = n + max_extra
+    cache = gpu_cache(w, inputs, chunks, max_ctx, decode_splits=decode_splits,
+                      decode_path=decode_path)
+    exp, kdeq, vdeq = oracle_encode(w, inputs, n, max_ctx)
+    return w, inputs, cache, exp, kdeq, vdeq
+
+
+@pytest.mark.parametrize("name,cfg_id,over,chunks", CASES, ids=[c[0] for c in CASES])
+def test_encode_bytes_and_attention(name, cfg_id, over, chunks):
+    w, inputs, cache, exp, kdeq, vdeq = _run(name, cfg_id, over, chunks)
+    bad = compare_regions(cache, exp)
+    assert not bad, "\n".join(bad)
+    q = inputs["q"]
+    out = cache.decode(q.cuda()).cpu().numpy()
+    ref = oracle_attention(w, q, kdeq, vdeq, w.ctx)
+    ma, rel = attention_errors(out, ref)
+    print(f"[parity] {name}: max_abs={ma:.3e} rel_l2={rel:.3e}", flush=True)
+    assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)
+
+
+@pytest.mark.parametrize("name,cfg_id,over,chunks", [c for c in CASES if c[1] in (1, 2, 3, 5)],
+                         ids=[c[0] for c in CASES if c[1] in (1, 2, 3, 5)])
+def test_both_decode_kernels_agree_with_oracle(name, cfg_id, over, chunks):
+    w, inputs, cache, exp, kdeq, vdeq = _run(name, cfg_id, over, chunks, decode_path="valu")
+    q = inputs["q"]
+    ref = oracle_attention(w, q, kdeq, vdeq, w.ctx)
+    out_valu = cache.decode(q.cuda()).cpu().numpy()
+    ma, rel = attention_errors(out_valu, ref)
+    assert ma <= MAX_ABS and rel <= REL_L2, ("valu", ma, rel)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7])
+def test_split_count_invariance(splits):
+    w, inputs, cache, exp, kdeq, vdeq = _run(f"splits{splits}", 5,
+                                             dict(batch=2, n_kv_heads=2, ctx=2000), [2000],
+                                             decode_splits=splits)
+    q = inputs["q"]
+    out = cache.decode(q.cuda()).cpu().numpy()
+    ref = oracle_attention(w, q, kdeq, vdeq, w.ctx)
+    ma, rel = attention_errors(out, ref)
+    assert ma <= MAX_ABS and rel <= REL_L2, (splits, ma, rel)
+
+
+def test_rope_explicit_query_position():
+    w, inputs, cache, exp, kdeq, vdeq = _run("nuq_qpos", 4, dict(n_kv_heads=2, ctx=257), [257])
+    q = inputs["q"]
+    q_pos = np.array([1000], dtype=np.int32)
+    out = cache.decode(q.cuda(), q_pos=torch.from_numpy(q_pos).cuda()).cpu().numpy()
+    ref = oracle_attention(w, q, kdeq, vdeq, w.ctx, q_pos=q_pos)
+    ma, rel = attention_errors(out, ref)
+    assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)
+
+
+@pytest.mark.parametrize("odt,tdt", [("f16", torch.float16), ("bf16", torch.bfloat16)])
+def test_half_outputs_are_rounded_f32_outputs(odt, tdt):
+    w, inputs, cache, exp, kdeq, vdeq = _run("tiny_out", 1, {}, [512])
+    q = inputs["q"].cuda()
+    o32 = cache.decode(q)
+    oh = cache.decode(q, out_dtype=odt)
+    assert oh.dtype == tdt
+    assert torch.equal(oh, o32.to(tdt))
+
+
+def test_repeated_decode_is_deterministic_and_counters_reset():
+    w, inputs, cache, exp, kdeq, vdeq = _run("repeat", 2, dict(ctx=4096), [4096])
+    q = inputs["q"].cuda()
+    a = cache.decode(q)
+    for _ in range(3):
+        b = cache.decode(q)
+    assert torch.equal(a, b)
+
+
+def test_bf16_raw_cache_matches_oracle():
+    none = {"quantizer": "none", "bits": 16}
+    w, inputs, cache, exp, kdeq, vdeq = _run("raw_bf16", 3, dict(batch=1, n_kv_heads=2, ctx=300,
+                                                                 k=none, v=none), [300])
+    q = inputs["q"]
+    out = cache.decode(q.cuda()).cpu().numpy()
+    ref = oracle_attention(w, q, kdeq, vdeq, w.ctx)
+    ma, rel = attention_errors(out, ref)
+    assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)

@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of fused quantized decode attention on one MI355X.
+
+Default workload (``--config 5``): an 8B-shaped serving layer, batch 16,
+32 query / 8 KV heads, head_dim 128, 65536 cached tokens per sequence,
+4-bit asymmetric keys (per-channel groups of 128 tokens) and values
+(per-token groups of 128 channels).  One step = quantize-append one new
+token per sequence, then one decode-attention step over the whole cache.
+
+Other configs (``--config 1..4``) time the decode step over a prefilled
+cache; caches smaller than 1 GB are replicated and rotated so that every
+step streams from HBM rather than the 256 MB last-level cache.
+
+Prints ONE JSON line on stdout.  ``value`` is the effective HBM bandwidth
+of the step: the bytes the step must read (packed codes, scales and zeros,
+outliers, tail; ``kvq_cache_bytes``) divided by the step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused quantized decode attention: effective HBM GB/s (% of peak), µs/step"
+PEAK_HBM_GBS = 8000.0
+DECODE_KERNELS = {"valu": "dec_generic_kernel", "mfma": "dec_mfma_kernel"}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_kv_cache_04_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str, kernel: str):
+    """Per-launch HBM bytes of the decode kernel from committed rocprofv3
+    counter runs (profiles/traffic.json), if they were taken on the current
+    kernel sources; None otherwise."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path)).get(f"{workload}/{kernel}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float = 12.0):
+    """Time the CPU oracle (float32 encode + float64 decode attention) on a
+    bounded sample of the workload: whole (sequence, KV head) slices at the
+    full context, as many as fit in ``seconds``."""
+    import numpy as np
+    import torch
+    from oracle import attention as oatt
+    from oracle import cache_bytes as ocb
+    from oracle import quant as oq
+    from synth import make_workload
+    from synth.workloads import make_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    w1 = make_workload(w.cfg_id, batch=1, n_kv_heads=1, ctx=w.ctx, gqa=w.gqa, seed=7)
+    inputs = make_inputs(w1, "cpu")
+    x_k = inputs["k"].float().numpy()
+    x_v = inputs["v"].float().numpy()
+    kcb = inputs["k_codebook"].numpy() if inputs["k_codebook"] is not None else None
+    vcb = inputs["v_codebook"].numpy() if inputs["v_codebook"] is not None else None
+    q = inputs["q"].float().numpy()
+    slice_bytes = ocb.payload_bytes(w1.k, w1.v, batch=1, n_kv_heads=1, head_dim=128,
+                                    n_ctx=w1.ctx, kv_dtype=w1.kv_dtype)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        ek = oq.encode_tensor(x_k, w1.k, kcb)
+        ev = oq.encode_tensor(x_v, w1.v, vcb)
+        oatt.decode_attention(q, ek["deq"], ev["deq"], rope=w1.rope, rope_base=w1.rope_base)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= 64:
+            break
+    return {"value": round(done * slice_bytes / el / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} x (1 sequence, 1 KV head, {w1.gqa} query heads, T={w1.ctx}) slices: "
+                      f"float32 encode + float64 dequant and attention, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--ctx", type=int, default=None, help="context (config 2: 4096/8192/16384)")
+    ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the decode step of one GPU's share runs on a "
+              f"single MI355X (asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_kv_cache_04_amd as kvq_pkg
+    from quantized_kv_cache_04_amd import kvq
+    from synth import make_workload
+    from synth.workloads import make_inputs, make_step_tokens
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kvq_pkg.lib()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = make_workload(args.config, ctx=args.ctx)
+    serving = args.config == 5
+    K, W = args.steps, args.warmup
+    max_ctx = w.ctx + (K + W + 1 if serving else 0)
+    cfg = kvq.config_from_workload(w, max_ctx=max_ctx, decode_path=args.path)
+    stream = torch.cuda.Stream()
+    log(f"workload cfg{w.cfg_id} {CONFIG_NAME(w)}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} "
+        f"T={w.ctx}; generating inputs on the GPU")
+
+    with torch.cuda.stream(stream):
+        inputs = make_inputs(w, dev)
+        payload0 = kvq.cache_bytes(cfg, w.ctx)
+        copies = 1 if serving else max(1, math.ceil(1.0e9 / payload0))
+        caches = []
+        for i in range(copies):
+            c = kvq.Cache(cfg, device=dev, k_codebook=inputs["k_codebook"],
+                          v_codebook=inputs["v_codebook"])
+            c.append(inputs["k"], inputs["v"], stream=stream)
+            caches.append(c)
+        q = inputs["q"]
+        del inputs["k"], inputs["v"]
+        if serving:
+            steps_tok = [make_step_tokens(w, s, 1, dev) for s in range(W + K)]
+    torch.cuda.synchronize()
+    log(f"cache built: {copies} cop{'y' if copies == 1 else 'ies'} x {payload0 / 1e9:.3f} GB payload")
+
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    dec_s = [ev() for _ in range(K)]
+    dec_e = [ev() for _ in range(K)]
+    step_bytes = []
+
+    def step(i, timed_idx=None):
+        c = caches[i % copies]
+        if serving:
+            kn, vn, qn = steps_tok[i]
+            c.append(kn, vn, stream=stream)
+            qq = qn
+        else:
+            qq = q
+        if timed_idx is not None:
+            dec_s[timed_idx].record(stream)
+        c.decode(qq, out=out, stream=stream)
+        if timed_idx is not None:
+            dec_e[timed_idx].record(stream)
+            step_bytes.append(kvq.cache_bytes(cfg, c.n_ctx))
+
+    with torch.cuda.stream(stream):
+        for i in range(W):
+            step(i)
+    torch.cuda.synchronize()
+    t_start, t_end = ev(), ev()
+    with torch.cuda.stream(stream):
+        t_start.record(stream)
+        for k in range(K):
+            step(W + k, k)
+        t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / K
+    dec_ms = [a.elapsed_time(b) for a, b in zip(dec_s, dec_e)]
+    dec_ms_sorted = sorted(dec_ms)
+    dec_avg = sum(dec_ms) / K
+    bytes_avg = sum(step_bytes) / K
+    value = bytes_avg / (ms_step * 1e-3) / 1e9
+    achieved = bytes_avg / (dec_avg * 1e-3) / 1e9
+    path = kvq.decode_path(cfg)
+    kernel = DECODE_KERNELS[path]
+    wl = CONFIG_NAME(w)
+    traffic = counter_traffic(wl, kernel)
+    log(f"step {ms_step * 1e3:.1f} us, decode avg {dec_avg * 1e3:.1f} us "
+        f"(p10 {dec_ms_sorted[K // 10] * 1e3:.1f}, p90 {dec_ms_sorted[(9 * K) // 10] * 1e3:.1f}), "
+        f"{bytes_avg / 1e6:.1f} MB/step -> {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.1%} of peak)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16-mfma/f32" if path == "mfma" else "f32",
+        "data": "synthetic (seeded normal K/V with the workload's outlier structure)",
+        "config": {"workload": wl, "batch": w.batch, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ctx": w.ctx,
+                   "k_format": _fmt(w.k), "v_format": _fmt(w.v),
+                   "step": "append 1 token/sequence + decode" if serving else "decode",
+                   "decode_kernel": kernel, "cache_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": kernel, "avg_launch_us": round(dec_avg * 1e3, 2),
+                     "algorithmic_bytes_per_launch": int(bytes_avg)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def CONFIG_NAME(w) -> str:
+    from synth.workloads import CONFIGS
+    return CONFIGS[w.cfg_id]["name"] + (f"_t{w.ctx}" if w.cfg_id == 2 else "")
+
+
+def _fmt(f) -> str:
+    s = f"{f['quantizer']}-{f['bits']}bit"
+    if f.get("group_size"):
+        s += f"-{f.get('layout', 'per_token')}-g{f['group_size']}"
+    if f.get("outlier_frac"):
+        s += f"-outliers{f['outlier_frac']}"
+    return s
+
+
+if __name__ == "__main__":
+    main()

@@ -250,6 +250,14 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
                                 const int32_t* q_pos, float sm_scale, void* out,
                                 int32_t out_dtype, void* stream);
 
+/*
+ * kvq_decode_path -- which decode kernel kvq_decode_attention runs for this
+ * configuration: KVQ_PATH_VALU or KVQ_PATH_MFMA (what KVQ_PATH_AUTO resolves
+ * to, or the forced path).  Host only.  Returns a negative status for an
+ * invalid configuration or a forced path it cannot run.
+ */
+int32_t kvq_decode_path(const kvq_config* cfg);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* kvq_last_error(void);
 

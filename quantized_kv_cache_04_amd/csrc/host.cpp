@@ -237,6 +237,17 @@ extern "C" {
 
 const char* kvq_last_error(void) { return g_last_error.c_str(); }
 
+int32_t kvq_decode_path(const kvq_config* cfg) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  const bool ok = mfma_config_supported(*cfg);
+  if (cfg->decode_path == KVQ_PATH_MFMA && !ok)
+    return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core decode kernel needs uniform or raw formats "
+                "for keys and values, no RoPE and at most 8 query heads per KV head");
+  if (cfg->decode_path == KVQ_PATH_VALU || !ok) return KVQ_PATH_VALU;
+  return KVQ_PATH_MFMA;
+}
+
 int32_t kvq_abi_version(void) { return 100; }
 
 kvq_status kvq_cache_bytes(const kvq_config* cfg, int64_t n_ctx, int64_t n_layers, int32_t what,
@@ -356,11 +367,9 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   a.blocks_per_split = (int)((nblocks + want - 1) / want);
   a.splits = (int)((nblocks + a.blocks_per_split - 1) / a.blocks_per_split);
 
-  const bool mfma_ok = mfma_supported(a);
-  if (cfg->decode_path == KVQ_PATH_MFMA && !mfma_ok)
-    return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core decode kernel needs uniform or raw formats, "
-                "no RoPE and at most 8 query heads per KV head");
-  const bool use_mfma = mfma_ok && cfg->decode_path != KVQ_PATH_VALU;
+  const int32_t path = kvq_decode_path(cfg);
+  if (path < 0) return path;
+  const bool use_mfma = path == KVQ_PATH_MFMA;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = use_mfma ? launch_decode_mfma(a, s) : launch_decode_generic(a, s);
   return device_status(e, "decode attention");

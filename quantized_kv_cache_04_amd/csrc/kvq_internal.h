@@ -85,7 +85,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
-bool mfma_supported(const DecodeArgs& a);
+// Whether the matrix-core kernel handles this configuration's formats.
+bool mfma_config_supported(const kvq_config& c);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace kvq

@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_last_error.restype = ctypes.c_char_p
         L.kvq_last_error.argtypes = []
         L.kvq_abi_version.restype = ctypes.c_int32
+        L.kvq_decode_path.restype = ctypes.c_int32
+        L.kvq_decode_path.argtypes = [ctypes.POINTER(Config)]
         _lib = L
     return _lib
 
@@ -135,6 +137,14 @@ def cache_bytes(cfg: Config, n_ctx: int = 0, n_layers: int = 1, what: int = BYTE
     _check(lib().kvq_cache_bytes(ctypes.byref(cfg), int(n_ctx), int(n_layers), int(what),
                                  ctypes.byref(out)))
     return int(out.value)
+
+
+def decode_path(cfg: Config) -> str:
+    """"valu" or "mfma": the decode kernel the library runs for ``cfg``."""
+    r = lib().kvq_decode_path(ctypes.byref(cfg))
+    if r < 0:
+        _check(r)
+    return {PATHS["valu"]: "valu", PATHS["mfma"]: "mfma"}[r]
 
 
 def cache_layout(cfg: Config) -> LayoutInfo:

@@ -166,7 +166,7 @@ typedef struct kvq_tensor_regions {
 typedef struct kvq_layout_info {
   kvq_tensor_regions k;
   kvq_tensor_regions v;
-  kvq_region workspace;     /* split-K partials and counters                */
+  kvq_region workspace;     /* split-K partial softmax states               */
   uint64_t   total_bytes;   /* == kvq_cache_bytes(..., KVQ_BYTES_ALLOC)     */
   int64_t    capacity;      /* Tcap = max_ctx rounded up to 32              */
   int32_t    max_splits;    /* split-K partial slots per (b, query head)   */
@@ -257,6 +257,18 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
  * invalid configuration or a forced path it cannot run.
  */
 int32_t kvq_decode_path(const kvq_config* cfg);
+
+/*
+ * kvq_set_decode_events -- optional instrumentation for profiling.  With
+ * start and stop non-NULL hipEvent_t handles (created by the caller, which
+ * keeps ownership), the next kvq_decode_attention call on this host thread
+ * records start on its stream right before the token-streaming kernel and
+ * stop right after it, so that start..stop brackets that kernel alone (not
+ * the split merge).  The next call that passes validation and launches
+ * uses them and clears them; NULL, NULL clears them without a launch.  Host only; returns KVQ_OK, or INVALID_ARGUMENT when exactly
+ * one of the two is NULL.
+ */
+kvq_status kvq_set_decode_events(void* start, void* stop);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* kvq_last_error(void);

@@ -5,4 +5,4 @@ the C ABI in include/kvq.h); this package only exposes that ABI to Python.
 """
 from .kvq import (Cache, Config, KvqError, cache_bytes, cache_layout,  # noqa: F401
                   config_from_workload, decode_attention, lib, make_config,
-                  quantize_append)
+                  quantize_append, set_decode_events)

@@ -17,10 +17,13 @@ ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           "-Wno-unused-variable", "-I", os.path.join(ROOT, "include"),
           # packed fp32 VALU instructions are disabled on purpose
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # keep MFMA accumulators in ordinary VGPRs (no AGPR copies around
+          # the rarely taken rescale branches)
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 # per-source extra flags: the encoder must not contract (x - z) / s chains
 EXTRA = {"encode.hip": ["-ffp-contract=off"]}
-SOURCES = ["host.cpp", "encode.hip", "decode_generic.hip", "decode_mfma.hip"]
+SOURCES = ["host.cpp", "encode.hip", "decode_generic.hip", "decode_mfma.hip", "combine.hip"]
 
 
 def hipcc() -> str:

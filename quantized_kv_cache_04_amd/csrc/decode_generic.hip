@@ -80,7 +80,6 @@ __global__ __launch_bounds__(256) void dec_generic_kernel(DecodeArgs a) {
   __shared__ double theta[kD / 2];
   __shared__ float wm[4][JB], wl[4][JB];
   __shared__ float wo[4][JB][kD];
-  __shared__ int flag;
   const int split = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.sh.Hkv, h = bh % a.sh.Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -227,13 +226,17 @@ __global__ __launch_bounds__(256) void dec_generic_kernel(DecodeArgs a) {
           L += wt * wl[w][jj];
         }
       }
-      float* rec = partial_rec(a, b, h * g + j0 + jj, split);
-      rec[c] = O;
-      if (c == 0) { rec[kD] = M; rec[kD + 1] = L; }
+      if (a.splits == 1) {
+        // a single split: normalize and write the output directly
+        store_out(a, ((int64_t)b * a.sh.Hq + h * g + j0 + jj) * kD + c, L > 0.f ? O / L : 0.f);
+      } else {
+        float* rec = partial_rec(a, b, h * g + j0 + jj, split);
+        rec[c] = O;
+        if (c == 0) { rec[kD] = M; rec[kD + 1] = L; }
+      }
     }
     __syncthreads();
   }
-  splitk_finish(a, b, h, &flag);
 }
 
 }  // namespace

@@ -54,24 +54,54 @@ __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
 // value of lane (lane + 8) mod 16 within each row of 16 lanes
 __device__ __forceinline__ float dpp_ror8(float x) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ float rows_max(float x) {  // over the 4 rows of 16 lanes
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  return fmaxf(x, __shfl_xor(x, 32, 64));
+// Reductions over the 4 rows of 16 lanes (lanes l, l^16, l^32, l^48) with
+// the gfx950 row-swap permutes: of the pair returned by permlane{16,32}_swap
+// of (x, x), one element is x[l] and the other x[l ^ 16] (resp. 32).
+__device__ __forceinline__ float rows_max(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  auto a = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  x = fmaxf(__builtin_bit_cast(float, (int)a[0]), __builtin_bit_cast(float, (int)a[1]));
+  const int yi = __builtin_bit_cast(int, x);
+  auto c = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)c[0]), __builtin_bit_cast(float, (int)c[1]));
 }
 __device__ __forceinline__ float rows_sum(float x) {
-  x += __shfl_xor(x, 16, 64);
-  return x + __shfl_xor(x, 32, 64);
+  const int xi = __builtin_bit_cast(int, x);
+  auto a = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  x = __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
+  const int yi = __builtin_bit_cast(int, x);
+  auto c = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
+  return __builtin_bit_cast(float, (int)c[0]) + __builtin_bit_cast(float, (int)c[1]);
 }
+// maximum over the whole wave: rotations within each row of 16, then rows
 __device__ __forceinline__ float wave_max(float x) {
-  for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
+  x = fmaxf(x, dpp_f<0x128>(x));   // row_ror:8
+  x = fmaxf(x, dpp_f<0x124>(x));   // row_ror:4
+  x = fmaxf(x, dpp_f<0x122>(x));   // row_ror:2
+  x = fmaxf(x, dpp_f<0x121>(x));   // row_ror:1
+  return rows_max(x);
 }
+
+// x of lane l ^ 32 (the other half of the wave)
+__device__ __forceinline__ float swap_halves(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  auto c = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  const bool upper = (__lane_id() & 32) != 0;
+  return __builtin_bit_cast(float, (int)(upper ? c[0] : c[1]));
+}
+
 
 // 2^e for integer e in [-126, 127]
 __device__ __forceinline__ float pow2i(int e) {
@@ -86,11 +116,14 @@ __device__ __forceinline__ int ceil_log2(float x) {
   return e < -126 ? -126 : e;
 }
 
-// fp16 high part (lo = false) or low part (lo = true) of x, as raw bits
-__device__ __forceinline__ uint32_t split16(float x, bool lo) {
-  const _Float16 h = (_Float16)x;
-  const _Float16 r = lo ? (_Float16)(x - (float)h) : h;
-  return (uint32_t)__builtin_bit_cast(uint16_t, r);
+// Two fp32 values as the fp16 high parts (lo_mask = 0) or low parts
+// (lo_mask = 1) of a high/low pair: hi = x rounded toward zero to fp16,
+// lo = (x - hi) rounded toward zero; hi + lo keeps about 21 bits of x.
+__device__ __forceinline__ uint32_t hilo2(float x0, float x1, float lo_mask) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+  const float y0 = x0 - lo_mask * (float)h[0];
+  const float y1 = x1 - lo_mask * (float)h[1];
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(y0, y1));
 }
 
 // ---- code unpacking: block of 8 codes -> 4 dwords of subnormal fp16 pairs ---
@@ -163,12 +196,12 @@ __device__ __forceinline__ float pair_factor(int r) {
 // each divided by the unpack factor of the other operand, scaled by ``sc`` and
 // split into the high or low fp16 part.
 template <int BITS>
-__device__ __forceinline__ half8 pair_operand(const float x[8], float sc, bool lo) {
+__device__ __forceinline__ half8 pair_operand(const float x[8], float sc, float lo_mask) {
   uint32_t o[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float f = sc * pair_factor<BITS>(r);
-    o[r] = split16(x[r] * f, lo) | (split16(x[r + 4] * f, lo) << 16);
+    o[r] = hilo2(x[r] * f, x[r + 4] * f, lo_mask);
   }
   return as_h8(o[0], o[1], o[2], o[3]);
 }
@@ -189,61 +222,32 @@ __device__ __forceinline__ void load_dw(const uint8_t* p, uint32_t* out) {
   }
 }
 
-// Parameters of this lane's 8 tokens (4q + r and 16 + 4q + r of the block):
-// NG groups per token; scale (and zero unless Q8) as float.
-template <bool Q8, int NG>
-__device__ __forceinline__ void load_token_params(const void* params, int64_t rec0, int q4,
-                                                  int valid_to, float s[2][4][NG],
-                                                  float z[2][4][NG]) {
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int64_t t4 = rec0 + 16 * mb + 4 * q4;      // first of 4 consecutive tokens
-    if constexpr (Q8) {
-      // 4 * NG fp16 scales = 2 * NG dwords
-      const uint16_t* p = static_cast<const uint16_t*>(params) + t4 * NG;
-      uint32_t d[2 * NG];
-      load_dw<2 * NG>(reinterpret_cast<const uint8_t*>(p), d);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-          const int idx = r * NG + gi;
-          s[mb][r][gi] = h2f((uint16_t)(d[idx >> 1] >> (16 * (idx & 1))));
-          z[mb][r][gi] = 0.f;
-        }
-    } else {
-      const uint32_t* p = static_cast<const uint32_t*>(params) + t4 * NG;
-      uint32_t d[4 * NG];
-      load_dw<4 * NG>(reinterpret_cast<const uint8_t*>(p), d);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-          s[mb][r][gi] = h2f((uint16_t)(d[r * NG + gi] & 0xffff));
-          z[mb][r][gi] = h2f((uint16_t)(d[r * NG + gi] >> 16));
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (16 * mb + 4 * q4 + r >= valid_to) {
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) { s[mb][r][gi] = 0.f; z[mb][r][gi] = 0.f; }
-      }
-  }
-}
-
 template <int KB, bool KCH, bool KQ8, int NGK, int VB, bool VQ8, int NGV>
 __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
+  // raw dwords of one 32-token block for this lane
+  constexpr int VPD = VQ8 ? 2 * NGV : 4 * NGV;                 // value params of 4 tokens
+  constexpr int KPD = KCH ? 1 : (KQ8 ? 2 * NGK : 4 * NGK);     // key params of 4 tokens
+  struct Buf {
+    uint32_t k[2][KB];      // key codes, rows 16*mb + n, segment q4
+    uint32_t v[2 * VB];     // value tile, this lane's 8*VB bytes
+    uint32_t vp[2][VPD];    // value scale(/zero) of tokens 16*mb + 4*q4 + r
+    uint32_t kp[2][KPD];    // key scale(/zero) (per-token keys)
+  };
+  constexpr float kLazy = 8.0f;   // log2 headroom before the running max moves
+
   __shared__ float wm[4][8], wl[4][8];
   __shared__ float wo[4][8][kD];
   __shared__ float wb[4][8][NGV];   // per wave, head, value group: additive term
-  __shared__ int flag;
+  extern __shared__ u32x4 kp_lds[];  // per-channel keys: [4 waves][a.kp_groups][32]
 
   const int split = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.sh.Hkv, h = bh % a.sh.Hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform: keep it (and all block bookkeeping) scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int q4 = lane >> 4, n = lane & 15, j = n & 7;
-  const bool lo_lane = n >= 8;
+  const float lo_mask = n >= 8 ? 1.0f : 0.0f;   // 1 in the low-part columns/rows
+  const bool hi_lane = n < 8;
   const int g = a.sh.g;
   const int nctx = a.n_ctx;
   const int64_t Tcap = a.sh.Tcap;
@@ -252,6 +256,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   const int Gk = K.G;
   const int n_full = KCH ? (nctx / Gk) * Gk : nctx;
   const int64_t prow = (int64_t)bh * Tcap;   // token record of token 0 of (b, h)
+  const float sm2 = a.sm_scale * kLog2e;
 
   // ---- token range of this wave (whole 32-token blocks) ----------------------
   const int blk0 = split * a.blocks_per_split;
@@ -261,231 +266,185 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   const int per_wave = (nb_split + 3) / 4;
   const int wb0 = blk0 + min(nb_split, wave * per_wave);
   const int wb1 = blk0 + min(nb_split, (wave + 1) * per_wave);
+  // blocks [wb0, wq1) have quantized keys; [wq1, wb1) read the unquantized tail
+  const int wq1 = KCH ? max(wb0, min(wb1, n_full / kTile)) : wb1;
 
-  // ---- query of this lane's column: head j, channels 32m + 8*q4 + e -------------
+  // query of this lane's column: head j, channels 32m + 8*q4 + e
   const bool head_ok = j < g;
-  float qv[4][8];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         ((int64_t)b * a.sh.Hq + h * g + (head_ok ? j : 0)) * kD;
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                       ((int64_t)b * a.sh.Hq + h * g + (head_ok ? j : 0)) * kD + 8 * q4;
+  auto load_q = [&](int m, float x[8]) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 32 * m);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 32 * m + 8 * q4);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t bits = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-        qv[m][e] = head_ok ? elem2f(bits, a.sh.kv_bf16) : 0.0f;
-      }
-    }
-  }
-  const float sm2 = a.sm_scale * kLog2e;
+    for (int e = 0; e < 8; ++e)
+      x[e] = head_ok ? elem2f((uint16_t)(w[e >> 1] >> (16 * (e & 1))), a.sh.kv_bf16) : 0.0f;
+  };
 
   // ---- per-token keys: fixed B operand, scaled by 2^Eq ---------------------------
   half8 bq[4];
-  float qsum[NGK];   // per key group: sum of q (high lanes only), true units
+  float qsum[NGK];   // per key group: sm2 * sum of q (high lanes only)
   float qoff[NGK];   // q8_0: 128 * 2^-24 * sum of the fed operand (MFMA output units)
-  float kq = 0.f;    // MFMA output units -> true units
+  float kq = 0.f;    // MFMA output units -> sm2 * true units
   if constexpr (!KCH) {
+    float qv[4][8];
     float mx = 0.f;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 4; ++m) {
+      load_q(m, qv[m]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qv[m][e]));
+    }
     mx = wave_max(mx);
     int Eq = 14 - ceil_log2(mx);
     if (Eq > 100) Eq = 100;
-    kq = pow2i(24 - Eq > 126 ? 126 : 24 - Eq);
+    kq = pow2i(24 - Eq > 126 ? 126 : 24 - Eq) * sm2;
     const float sc = pow2i(Eq);
 #pragma unroll
     for (int gi = 0; gi < NGK; ++gi) { qsum[gi] = 0.f; qoff[gi] = 0.f; }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      bq[m] = pair_operand<KB>(qv[m], sc, lo_lane);
-      const int grp = m * NGK / 4;
       float s = 0.f, so = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += qv[m][e];
+      bq[m] = pair_operand<KB>(qv[m], sc, lo_mask);
       if constexpr (KQ8) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) so += (float)bq[m][e];
       }
-      qsum[grp] += s;
-      qoff[grp] += so;
+      qsum[m * NGK / 4] += s;
+      qoff[m * NGK / 4] += so;
     }
 #pragma unroll
     for (int gi = 0; gi < NGK; ++gi) {
-      qsum[gi] = lo_lane ? 0.f : rows_sum(qsum[gi]);
+      qsum[gi] = hi_lane ? rows_sum(qsum[gi]) * sm2 : 0.f;
       qoff[gi] = 128.0f * 0x1p-24f * rows_sum(qoff[gi]);
     }
   }
 
-  // ---- value scale exponent of this wave's range: p * scale * 2^(24-Ev) <= 2^14
-  int Ev;
-  {
-    float mx = 0.f;
-    const int t_lo = wb0 * kTile, t_hi = min(nctx, wb1 * kTile);
-    for (int t = t_lo + lane; t < t_hi; t += 64) {
+  // ---- per-channel keys: stage this wave's key-group parameters in LDS -----------
+  const int gblk = KCH ? Gk / kTile : 1;   // blocks per key group
+  const int g_first = wb0 / gblk;
+  const bool kp_staged = KCH && a.kp_groups > 0;
+  const uint32_t* kgrp_base = KCH ? static_cast<const uint32_t*>(K.params) +
+                                        (int64_t)bh * (Tcap / Gk) * kD
+                                  : nullptr;
+  if constexpr (KCH) {
+    if (kp_staged && wq1 > wb0) {
+      const int ng_w = (wq1 - 1) / gblk - g_first + 1;
+      const u32x4* src = reinterpret_cast<const u32x4*>(kgrp_base + (int64_t)g_first * kD);
+      u32x4* dst = kp_lds + wave * a.kp_groups * 32;
+      for (int c0 = 0; c0 < ng_w * 32; c0 += 256) {
+        u32x4 v[4];
 #pragma unroll
-      for (int gi = 0; gi < NGV; ++gi) {
-        float s;
-        if (VQ8) s = h2f(static_cast<const uint16_t*>(V.params)[(prow + t) * NGV + gi]);
-        else s = h2f((uint16_t)(static_cast<const uint32_t*>(V.params)[(prow + t) * NGV + gi] & 0xffff));
-        mx = fmaxf(mx, s);
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + u * 64 + lane;
+          if (c < ng_w * 32) v[u] = src[c];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + u * 64 + lane;
+          if (c < ng_w * 32) dst[c] = v[u];
+        }
       }
     }
-    mx = wave_max(mx);
-    Ev = ceil_log2(mx) + 10;
+    __syncthreads();
   }
-  const int pexp = 24 - Ev > 126 ? 126 : 24 - Ev;
-  const float pscale = pow2i(pexp);           // fed P operand = p * scale * pscale
-  const float vscale = pow2i(-pexp);          // fed units -> true units (with 2^-24 codes: x 2^24)
 
   // ---- running state -----------------------------------------------------------
   f32x4 oacc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // per column head j (lanes n, n + 8 agree)
+  float m_run = -INFINITY;   // reference maximum of head j (lanes n, n + 8 agree)
   float l_run = 0.f;         // partial over this lane's tokens
   float vbias[NGV];          // sum p * zero (values), true units
   float voff[NGV];           // q8_0: sum of the fed P operand
 #pragma unroll
   for (int gi = 0; gi < NGV; ++gi) { vbias[gi] = 0.f; voff[gi] = 0.f; }
+  // value operand scale: fed P = p * scale * 2^pexp <= 2^12 (p <= 2^kLazy);
+  // pexp only decreases, when a block brings a larger value scale (the
+  // accumulators are then rescaled by the exact power of two)
+  int pexp = 100;
+  float sbound = 0.f;
+  float cpair[2];            // 2^pexp times the unpack factor of even/odd pairs
+  cpair[0] = pow2i(pexp);
+  cpair[1] = cpair[0] * pair_factor<VB>(1);
 
   // per-channel keys: B operand of the current key group
   half8 bk[4];
-  float kbias = 0.f;
-  float kscale = 0.f;
-  int cur_group = -1;
+  float kbias = 0.f;         // sm2 * sum_c q_c z_c (high lanes)
+  float kscale = 0.f;        // sm2 * 2^(24 - E)
+  int grp_end = -1;          // first block after the current key group
 
-  const uint8_t* kcodes = K.codes + prow * K.row_bytes;
-  const uint8_t* vcodes = V.codes + prow * V.row_bytes;
+  const uint8_t* kcodes = K.codes + prow * (4 * KB * 4);
+  const uint8_t* vcodes = V.codes + prow * (4 * VB * 4);
+  const uint8_t* vprm = static_cast<const uint8_t*>(V.params) + prow * NGV * (VQ8 ? 2 : 4);
+  const uint8_t* kprm = KCH ? nullptr
+                            : static_cast<const uint8_t*>(K.params) + prow * NGK * (KQ8 ? 2 : 4);
+  const uint32_t k_lane_off = (uint32_t)n * (16 * KB) + (uint32_t)q4 * (4 * KB);
+  const uint32_t v_lane_off = (uint32_t)lane * (8 * VB);
+  const uint32_t p_lane_tok = 4u * (uint32_t)q4;
 
-  for (int blk = wb0; blk < wb1; ++blk) {
-    const int t0 = blk * kTile;
-    const int valid = nctx - t0;            // tokens of this block that exist
-    // ---------------- loads ----------------
-    uint32_t kseg[2][KB];
-    uint32_t vlane[2 * VB];
-    const bool tail_blk = KCH && t0 >= n_full;
-    if (!tail_blk) {
+  auto load = [&](Buf& B, int blk) {
+    const uint32_t t0 = (uint32_t)blk * kTile;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        load_dw<KB>(kcodes + (int64_t)(t0 + 16 * mb + n) * K.row_bytes + q4 * 4 * KB, kseg[mb]);
+    for (int mb = 0; mb < 2; ++mb) {
+      load_dw<KB>(kcodes + (t0 + 16 * mb) * (16 * KB) + k_lane_off, B.k[mb]);
+      const uint32_t tok = t0 + 16 * mb + p_lane_tok;
+      load_dw<VPD>(vprm + tok * (NGV * (VQ8 ? 2 : 4)), B.vp[mb]);
+      if constexpr (!KCH) load_dw<KPD>(kprm + tok * (NGK * (KQ8 ? 2 : 4)), B.kp[mb]);
     }
-    load_dw<2 * VB>(vcodes + (int64_t)t0 * V.row_bytes + lane * 8 * VB, vlane);
-    float vs[2][4][NGV], vz[2][4][NGV];
-    load_token_params<VQ8, NGV>(V.params, prow + t0, q4, valid, vs, vz);
+    load_dw<2 * VB>(vcodes + t0 * (16 * VB) + v_lane_off, B.v);
+  };
 
-    // ---------------- scores: QK^T ----------------
-    float sc[2][4];
-    if constexpr (KCH) {
-      if (tail_blk) {
-        // unquantized tail: A = fp16 keys, B = q (exact in fp16), natural order
-        const uint16_t* tail = K.tail + ((int64_t)bh * Gk + (t0 - n_full)) * kD;
-        half8 bt[4];
+  // per-channel keys: B operand and zero-point term of key group ``grp``
+  auto key_group = [&](int grp) {
+    const u32x4* prm4 = kp_staged ? kp_lds + (wave * a.kp_groups + (grp - g_first)) * 32
+                                  : reinterpret_cast<const u32x4*>(kgrp_base + (int64_t)grp * kD);
+    float mx = 0.f, zb = 0.f;
+    float qs[4][8];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          uint32_t o[4];
+    for (int m = 0; m < 4; ++m) {
+      float qv[8];
+      load_q(m, qv);
+      const u32x4 p0 = prm4[8 * m + 2 * q4];
+      const u32x4 p1 = prm4[8 * m + 2 * q4 + 1];
+      const uint32_t pz[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            o[r] = split16(lo_lane ? 0.f : qv[m][2 * r], false) |
-                   (split16(lo_lane ? 0.f : qv[m][2 * r + 1], false) << 16);
-          bt[m] = as_h8(o[0], o[1], o[2], o[3]);
-        }
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          f32x4 c = {0.f, 0.f, 0.f, 0.f};
-          const int tt = 16 * mb + n;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(tail + (int64_t)tt * kD + 32 * m + 8 * q4);
-            c = mfma16(__builtin_bit_cast(half8, v), bt[m], c);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[mb][r] = c[r];
-        }
-      } else {
-        const int grp = t0 / Gk;
-        if (grp != cur_group) {
-          cur_group = grp;
-          // scale/zero of this lane's 32 channels for key group ``grp``
-          const uint32_t* prm = static_cast<const uint32_t*>(K.params) +
-                                ((int64_t)bh * (Tcap / Gk) + grp) * kD;
-          float qs[4][8];
-          float mx = 0.f, zb = 0.f;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const u32x4 p0 = *reinterpret_cast<const u32x4*>(prm + 32 * m + 8 * q4);
-            const u32x4 p1 = *reinterpret_cast<const u32x4*>(prm + 32 * m + 8 * q4 + 4);
-            const uint32_t pz[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float s = h2f((uint16_t)(pz[e] & 0xffff));
-              const float z = h2f((uint16_t)(pz[e] >> 16));
-              qs[m][e] = qv[m][e] * s;
-              mx = fmaxf(mx, fabsf(qs[m][e]));
-              zb += qv[m][e] * z;
-            }
-          }
-          mx = wave_max(mx);
-          int E = 14 - ceil_log2(mx);
-          if (E > 100) E = 100;
-          kscale = pow2i(24 - E > 126 ? 126 : 24 - E);
-          const float s2 = pow2i(E);
-#pragma unroll
-          for (int m = 0; m < 4; ++m) bk[m] = pair_operand<KB>(qs[m], s2, lo_lane);
-          kbias = lo_lane ? 0.f : rows_sum(zb);
-        }
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int m = 0; m < 4; ++m) c = mfma16(seg_block<KB, KQ8>(kseg[mb], m), bk[m], c);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[mb][r] = c[r] * kscale + kbias;
-        }
-      }
-    } else {
-      // per-token keys: one accumulator per key group, then scale and zero
-      float ks[2][4][NGK], kz[2][4][NGK];
-      load_token_params<KQ8, NGK>(K.params, prow + t0, q4, valid, ks, kz);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int gi = 0; gi < NGK; ++gi) {
-          f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m)
-            c = mfma16(seg_block<KB, KQ8>(kseg[mb], m), bq[m], c);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float dot = (c[r] - (KQ8 ? qoff[gi] : 0.f)) * kq;
-            acc[r] += ks[mb][r][gi] * dot + kz[mb][r][gi] * qsum[gi];
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[mb][r] = acc[r];
+      for (int e = 0; e < 8; ++e) {
+        qs[m][e] = qv[e] * h2f((uint16_t)(pz[e] & 0xffff));
+        mx = fmaxf(mx, fabsf(qs[m][e]));
+        zb += qv[e] * h2f((uint16_t)(pz[e] >> 16));
       }
     }
+    mx = wave_max(mx);
+    int E = 14 - ceil_log2(mx);
+    if (E > 100) E = 100;
+    kscale = pow2i(24 - E > 126 ? 126 : 24 - E) * sm2;
+    const float s2 = pow2i(E);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) bk[m] = pair_operand<KB>(qs[m], s2, lo_mask);
+    zb = rows_sum(zb);
+    kbias = hi_lane ? zb * sm2 : 0.f;
+  };
 
-    // ---------------- online softmax ----------------
+  // softmax + P.V for one block; sc holds base-2 scores before the sum of
+  // the high/low columns
+  auto softmax_pv = [&](float sc[2][4], const uint32_t* vl, const uint32_t (*vp)[VPD], int valid) {
     float bmax = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float s = (sc[mb][r] + dpp_ror8(sc[mb][r])) * sm2;
-        if (16 * mb + 4 * q4 + r >= valid) s = -INFINITY;
+        float s = sc[mb][r] + dpp_ror8(sc[mb][r]);
+        if (valid < kTile && 16 * mb + 4 * q4 + r >= valid) s = -INFINITY;
         sc[mb][r] = s;
         bmax = fmaxf(bmax, s);
       }
-    bmax = rows_max(bmax);
-    const float m_new = fmaxf(m_run, bmax);
-    if (__any(m_new > m_run)) {
-      // rescale when any head's maximum grew (wave-uniform branch)
-      const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+    if (__any(bmax > m_run + kLazy)) {
+      // move the reference maximum (wave-uniform branch, rare after warm-up)
+      const float m_new = fmaxf(m_run, rows_max(bmax));
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int gi = 0; gi < NGV; ++gi) { vbias[gi] *= alpha; voff[gi] *= alpha; }
@@ -503,28 +462,65 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
       m_run = m_new;
     }
     float p[2][4];
-    float lsum = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[mb][r] = exp2f(sc[mb][r] - m_run);
-        lsum += p[mb][r];
+        p[mb][r] = __builtin_amdgcn_exp2f(sc[mb][r] - m_run);
+        l_run += p[mb][r];
       }
-    l_run += lsum;
-
-    // ---------------- P.V ----------------
+    // value scales (and zeros) of this lane's 8 tokens
+    float vsc[NGV][8], vze[NGV][8];
+    float smax = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < NGV; ++gi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const uint32_t* d = vp[mb];
+          float s, z = 0.f;
+          if constexpr (VQ8) {
+            const int idx = r * NGV + gi;
+            s = h2f((uint16_t)(d[idx >> 1] >> (16 * (idx & 1))));
+          } else {
+            s = h2f((uint16_t)(d[r * NGV + gi] & 0xffff));
+            z = h2f((uint16_t)(d[r * NGV + gi] >> 16));
+          }
+          if (valid < kTile && 16 * mb + 4 * q4 + r >= valid) { s = 0.f; z = 0.f; }
+          vsc[gi][r + 4 * mb] = s;
+          vze[gi][r + 4 * mb] = z;
+          smax = fmaxf(smax, s);
+        }
+      }
+    if (__any(smax > sbound)) {
+      smax = rows_max(smax);                   // same tokens in every column
+      int np = 12 - (int)kLazy - ceil_log2(smax);
+      np = np < -100 ? -100 : (np > 126 ? 126 : np);
+      const int e = np - pexp;                 // rescale what was fed so far
+      const float f = e < -126 ? 0.f : (e > 126 ? 1.f : pow2i(e));
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[nb][r] *= f;
+#pragma unroll
+      for (int gi = 0; gi < NGV; ++gi) voff[gi] *= f;
+      pexp = np;
+      sbound = pow2i(12 - (int)kLazy - np);
+      cpair[0] = pow2i(np);
+      cpair[1] = cpair[0] * pair_factor<VB>(1);
+    }
     half8 pa[NGV];
 #pragma unroll
     for (int gi = 0; gi < NGV; ++gi) {
-      float x[8];
+      uint32_t o[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        x[r] = p[0][r] * vs[0][r][gi];
-        x[r + 4] = p[1][r] * vs[1][r][gi];
-        if constexpr (!VQ8) vbias[gi] += p[0][r] * vz[0][r][gi] + p[1][r] * vz[1][r][gi];
+        const float c = cpair[r & 1];
+        o[r] = hilo2(p[0][r] * (vsc[gi][r] * c), p[1][r] * (vsc[gi][r + 4] * c), lo_mask);
+        if constexpr (!VQ8) vbias[gi] += p[0][r] * vze[gi][r] + p[1][r] * vze[gi][r + 4];
       }
-      pa[gi] = pair_operand<VB>(x, pscale, lo_lane);
+      pa[gi] = as_h8(o[0], o[1], o[2], o[3]);
       if constexpr (VQ8) {
         float so = 0.f;
 #pragma unroll
@@ -534,8 +530,102 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int nbk = 0; nbk < 8; ++nbk) {
-      const uint32_t* seg = vlane + (nbk >> 2) * VB;
+      const uint32_t* seg = vl + (nbk >> 2) * VB;
       oacc[nbk] = mfma16(pa[nbk * NGV / 8], seg_block<VB, VQ8>(seg, nbk & 3), oacc[nbk]);
+    }
+  };
+
+  // one block with quantized keys
+  auto compute = [&](const Buf& B, int blk) {
+    const int valid = nctx - blk * kTile;
+    float sc[2][4];
+    if constexpr (KCH) {
+      if (blk >= grp_end) {     // wave-uniform: once per key group
+        const int grp = blk / gblk;
+        grp_end = (grp + 1) * gblk;
+        key_group(grp);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) c = mfma16(seg_block<KB, KQ8>(B.k[mb], m), bk[m], c);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[mb][r] = c[r] * kscale + kbias;
+      }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int gi = 0; gi < NGK; ++gi) {
+          f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m)
+            c = mfma16(seg_block<KB, KQ8>(B.k[mb], m), bq[m], c);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t* d = B.kp[mb];
+            float s, z = 0.f;
+            if constexpr (KQ8) {
+              const int idx = r * NGK + gi;
+              s = h2f((uint16_t)(d[idx >> 1] >> (16 * (idx & 1))));
+            } else {
+              s = h2f((uint16_t)(d[r * NGK + gi] & 0xffff));
+              z = h2f((uint16_t)(d[r * NGK + gi] >> 16));
+            }
+            const float dot = (c[r] - (KQ8 ? qoff[gi] : 0.f)) * kq;
+            acc[r] += s * dot + z * qsum[gi];
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[mb][r] = acc[r];
+      }
+    }
+    softmax_pv(sc, B.v, B.vp, valid);
+  };
+
+  // ---- hot loop: two-stage register pipeline over quantized-key blocks -----------
+  if (wq1 > wb0) {
+    const int last = wq1 - 1;
+    Buf b0, b1;
+    load(b0, wb0);
+    for (int blk = wb0; blk < wq1; blk += 2) {
+      load(b1, min(blk + 1, last));
+      compute(b0, blk);
+      load(b0, min(blk + 2, last));
+      if (blk + 1 < wq1) compute(b1, blk + 1);
+    }
+  }
+
+  // ---- per-channel keys: blocks of the unquantized tail ---------------------------
+  if constexpr (KCH) {
+    for (int blk = wq1; blk < wb1; ++blk) {
+      const int t0 = blk * kTile;
+      const uint16_t* tail = K.tail + ((int64_t)bh * Gk + (t0 - n_full)) * kD;
+      half8 bt[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 32 * m);
+        const bool z = !hi_lane || !head_ok;
+        bt[m] = as_h8(z ? 0u : v.x, z ? 0u : v.y, z ? 0u : v.z, z ? 0u : v.w);
+      }
+      float sc[2][4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+        const int tt = 16 * mb + n;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(tail + (int64_t)tt * kD + 32 * m + 8 * q4);
+          c = mfma16(__builtin_bit_cast(half8, v), bt[m], c);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[mb][r] = c[r] * sm2;
+      }
+      Buf B;
+      load(B, blk);
+      softmax_pv(sc, B.v, B.vp, nctx - t0);
     }
   }
 
@@ -546,8 +636,9 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int nbk = 0; nbk < 8; ++nbk)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) oacc[nbk][r] += __shfl_xor(oacc[nbk][r], 32, 64);
-  const float oscale = 0x1p24f * vscale;    // codes are fed as code * 2^-24
+    for (int r = 0; r < 4; ++r) oacc[nbk][r] += swap_halves(oacc[nbk][r]);
+  const float vscale = pow2i(-pexp);          // fed units -> true units
+  const float oscale = 0x1p24f * vscale;      // codes are fed as code * 2^-24
   if (q4 < 2) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -586,18 +677,23 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
         L += wt * wl[w][jj];
       }
     }
-    float* rec = partial_rec(a, b, h * g + jj, split);
-    rec[c] = O;
-    if (c == 0) { rec[kD] = M; rec[kD + 1] = L; }
+    if (a.splits == 1) {
+      // a single split: normalize and write the output directly
+      store_out(a, ((int64_t)b * a.sh.Hq + h * g + jj) * kD + c, L > 0.f ? O / L : 0.f);
+    } else {
+      float* rec = partial_rec(a, b, h * g + jj, split);
+      rec[c] = O;
+      if (c == 0) { rec[kD] = M; rec[kD + 1] = L; }
+    }
   }
-  splitk_finish(a, b, h, &flag);
 }
 
 // ---- dispatch ---------------------------------------------------------------------
 template <int KB, bool KCH, bool KQ8, int NGK, int VB, bool VQ8, int NGV>
 void launch_t(const DecodeArgs& a, hipStream_t s) {
+  const size_t lds = KCH ? (size_t)4 * a.kp_groups * 32 * sizeof(u32x4) : 0;
   hipLaunchKernelGGL((dec_mfma_kernel<KB, KCH, KQ8, NGK, VB, VQ8, NGV>),
-                     dim3(a.splits, a.sh.B * a.sh.Hkv), dim3(256), 0, s, a);
+                     dim3(a.splits, a.sh.B * a.sh.Hkv), dim3(256), lds, s, a);
 }
 
 template <int KB, bool KCH, bool KQ8, int NGK, int NGV>
@@ -648,7 +744,16 @@ bool mfma_config_supported(const kvq_config& c) {
   return c.k.group_size == c.v.group_size;
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_mfma(const DecodeArgs& a_in, hipStream_t s) {
+  DecodeArgs a = a_in;
+  a.kp_groups = 0;
+  if (a.k.per_channel) {
+    // key groups one wave can touch: its blocks plus one partial group
+    const int per_wave = (a.blocks_per_split + 3) / 4;
+    const int gblk = a.k.G / kTile;
+    const int groups = (per_wave + gblk - 1) / gblk + 1;
+    if ((size_t)4 * groups * kD * 4 <= 64 * 1024) a.kp_groups = groups;
+  }
   bool ok = false;
   if (a.k.per_channel) {
     switch (a.k.bits) {

@@ -16,6 +16,8 @@ namespace kvq {
 namespace {
 
 thread_local std::string g_last_error;
+// events recorded around the next decode's streaming kernel (kvq_set_decode_events)
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 kvq_status fail(kvq_status st, const char* fmt, ...) {
   char buf[512];
@@ -156,8 +158,6 @@ Layout make_layout(const kvq_config& c) {
   L.ws_off = off;
   L.partial_off = off;
   off = align_up(off + (uint64_t)c.batch * c.n_q_heads * L.S_max * (c.head_dim + 2) * 4, 256);
-  L.counter_off = off;
-  off = align_up(off + (uint64_t)c.batch * c.n_kv_heads * 4, 256);
   L.ws_bytes = off - L.ws_off;
   L.total = off;
   return L;
@@ -249,6 +249,14 @@ int32_t kvq_decode_path(const kvq_config* cfg) {
 }
 
 int32_t kvq_abi_version(void) { return 100; }
+
+kvq_status kvq_set_decode_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "start and stop events must both be set or both NULL");
+  g_ev_start = static_cast<hipEvent_t>(start);
+  g_ev_stop = static_cast<hipEvent_t>(stop);
+  return KVQ_OK;
+}
 
 kvq_status kvq_cache_bytes(const kvq_config* cfg, int64_t n_ctx, int64_t n_layers, int32_t what,
                            uint64_t* out_bytes) {
@@ -351,8 +359,8 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   a.rope_base = cfg->rope_base;
   a.n_ctx = (int)cache->n_ctx;
   a.S_max = L.S_max;
+  a.kp_groups = 0;
   a.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(cache->base) + L.partial_off);
-  a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(cache->base) + L.counter_off);
 
   // Split the token axis so that the grid covers the GPU several times:
   // about 2048 workgroups, each with at least two 32-token blocks per wave.
@@ -371,7 +379,12 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   if (path < 0) return path;
   const bool use_mfma = path == KVQ_PATH_MFMA;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = use_mfma ? launch_decode_mfma(a, s) : launch_decode_generic(a, s);
+  hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
+  g_ev_start = g_ev_stop = nullptr;
+  hipError_t e = ev0 ? hipEventRecord(ev0, s) : hipSuccess;
+  if (e == hipSuccess) e = use_mfma ? launch_decode_mfma(a, s) : launch_decode_generic(a, s);
+  if (e == hipSuccess && ev1) e = hipEventRecord(ev1, s);
+  if (e == hipSuccess && a.splits > 1) e = launch_combine(a, s);
   return device_status(e, "decode attention");
 }
 

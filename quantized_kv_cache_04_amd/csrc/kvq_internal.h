@@ -36,7 +36,6 @@ struct Layout {
   int64_t Tcap = 0;          // token capacity per sequence (multiple of 32)
   int S_max = 1;             // partial slots per (b, query head)
   uint64_t partial_off = 0;  // float [B][Hq][S_max][d + 2]
-  uint64_t counter_off = 0;  // uint32 [B][Hkv]
   uint64_t ws_off = 0, ws_bytes = 0;
   uint64_t total = 0;
 };
@@ -81,10 +80,12 @@ struct DecodeArgs {
   int blocks_per_split; // 32-token blocks per split
   int S_max;
   float* partial;       // [B][Hq][S_max][d + 2]
-  uint32_t* counters;   // [B][Hkv]
+  int kp_groups;        // matrix-core kernel: key groups staged in LDS per wave (0 = none)
 };
 
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
+// merge of the split-K partials (only when a.splits > 1)
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
 // Whether the matrix-core kernel handles this configuration's formats.
 bool mfma_config_supported(const kvq_config& c);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);

@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_last_error.restype = ctypes.c_char_p
         L.kvq_last_error.argtypes = []
         L.kvq_abi_version.restype = ctypes.c_int32
+        L.kvq_set_decode_events.restype = ctypes.c_int32
+        L.kvq_set_decode_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.kvq_decode_path.restype = ctypes.c_int32
         L.kvq_decode_path.argtypes = [ctypes.POINTER(Config)]
         _lib = L
@@ -192,6 +194,21 @@ class Cache:
                stream=None):
         return decode_attention(self, q, q_pos=q_pos, sm_scale=sm_scale, out=out,
                                 out_dtype=out_dtype, stream=stream)
+
+
+def set_decode_events(start=None, stop=None) -> None:
+    """Have the next decode call on this thread record ``start`` and ``stop``
+    (torch.cuda.Event objects or raw hipEvent_t handles) right around its
+    token-streaming kernel.  A torch event exists only once it has been
+    recorded, so record each one once before passing it here."""
+    def handle(e):
+        if e is None:
+            return None
+        h = int(e.cuda_event) if hasattr(e, "cuda_event") else int(e)
+        if not h:
+            raise ValueError("the event has not been created yet: record it once first")
+        return h
+    _check(lib().kvq_set_decode_events(handle(start), handle(stop)))
 
 
 def quantize_append(cache: Cache, k_new, v_new, stream=None) -> None:

@@ -172,3 +172,10 @@ def test_decode_errors_before_launch():
     assert kvq.lib().kvq_decode_attention(ctypes.byref(cfg), ctypes.byref(ok), FAKE, None,
                                           float("nan"), FAKE, kvq.F32, None) == \
         kvq.ERR_INVALID_ARGUMENT
+
+
+def test_decode_events_hook():
+    L = kvq.lib()
+    assert L.kvq_set_decode_events(FAKE, None) == kvq.ERR_INVALID_ARGUMENT
+    assert L.kvq_set_decode_events(None, FAKE) == kvq.ERR_INVALID_ARGUMENT
+    assert L.kvq_set_decode_events(None, None) == kvq.OK

@@ -108,7 +108,7 @@ def test_half_outputs_are_rounded_f32_outputs(odt, tdt):
     assert torch.equal(oh, o32.to(tdt))
 
 
-def test_repeated_decode_is_deterministic_and_counters_reset():
+def test_repeated_decode_is_deterministic():
     w, inputs, cache, exp, kdeq, vdeq = _run("repeat", 2, dict(ctx=4096), [4096])
     q = inputs["q"].cuda()
     a = cache.decode(q)
@@ -126,3 +126,25 @@ def test_bf16_raw_cache_matches_oracle():
     ref = oracle_attention(w, q, kdeq, vdeq, w.ctx)
     ma, rel = attention_errors(out, ref)
     assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)
+
+
+def test_decode_events_bracket_the_streaming_kernel():
+    """kvq_set_decode_events: the recorded interval lies inside the decode
+    call and the output is the same as without the events."""
+    from quantized_kv_cache_04_amd import kvq as K
+    w, inputs, cache, exp, kdeq, vdeq = _run("events", 5, dict(batch=2, n_kv_heads=2, ctx=4000),
+                                             [4000])
+    q = inputs["q"].cuda()
+    ref = cache.decode(q)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    s = torch.cuda.current_stream()
+    for e in ev:
+        e.record(s)
+    ev[0].record(s)
+    K.set_decode_events(ev[1], ev[2])
+    out = cache.decode(q)
+    ev[3].record(s)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    k_ms, call_ms = ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
+    assert 0.0 < k_ms <= call_ms, (k_ms, call_ms)

@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 launches), the reference "
+                         "point for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -130,6 +133,19 @@ def main():
     kvq_pkg.lib()
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        # an elementwise kernel (dst = src * 1 in float32): it reads and
+        # writes n bytes once each (a same-type copy_ would go to a DMA copy,
+        # not a kernel dispatch)
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "elementwise copy", "bytes_read": n, "bytes_written": n,
+                          "launches": 3}), flush=True)
+        return
     w = make_workload(args.config, ctx=args.ctx)
     serving = args.config == 5
     K, W = args.steps, args.warmup

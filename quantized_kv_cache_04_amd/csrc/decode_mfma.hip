@@ -32,6 +32,8 @@
 // partials by the last block (splitk.h).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "splitk.h"
 
 namespace kvq {
@@ -41,6 +43,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 constexpr int kD = kHeadDim;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -120,6 +123,14 @@ __device__ __forceinline__ int ceil_log2(float x) {
 // (lo_mask = 1) of a high/low pair: hi = x rounded toward zero to fp16,
 // lo = (x - hi) rounded toward zero; hi + lo keeps about 21 bits of x.
 __device__ __forceinline__ uint32_t hilo2(float x0, float x1, float lo_mask) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+  const float y0 = x0 - lo_mask * (float)h[0];
+  const float y1 = x1 - lo_mask * (float)h[1];
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(y0, y1));
+}
+
+// hi/lo split of two fp32 values without scaling (see hilo2)
+__device__ __forceinline__ uint32_t hilo_split(float x0, float x1, float lo_mask) {
   const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
   const float y0 = x0 - lo_mask * (float)h[0];
   const float y1 = x1 - lo_mask * (float)h[1];
@@ -234,10 +245,15 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     uint32_t kp[2][KPD];    // key scale(/zero) (per-token keys)
   };
   constexpr float kLazy = 8.0f;   // log2 headroom before the running max moves
+  // register pipeline depth: three buffers where the registers allow
+  // (per-channel keys, small blocks, single-group values), else two
+  constexpr int kBufDwords = 2 * KB + 2 * VB + 2 * VPD + 2 * KPD;
+  constexpr int kStages = (KCH && kBufDwords <= 32 && NGV == 1) ? 3 : 2;
 
   __shared__ float wm[4][8], wl[4][8];
   __shared__ float wo[4][8][kD];
   __shared__ float wb[4][8][NGV];   // per wave, head, value group: additive term
+  __shared__ float q_lds[8][kD + 4];   // the group's queries as fp32 (zero rows for j >= g)
   extern __shared__ u32x4 kp_lds[];  // per-channel keys: [4 waves][a.kp_groups][32]
 
   const int split = blockIdx.x, bh = blockIdx.y;
@@ -273,12 +289,19 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   const bool head_ok = j < g;
   const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
                        ((int64_t)b * a.sh.Hq + h * g + (head_ok ? j : 0)) * kD + 8 * q4;
+  {
+    const uint16_t* qg = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.sh.Hq + h * g) * kD;
+    for (int idx = threadIdx.x; idx < 8 * kD; idx += blockDim.x) {
+      const int jj = idx / kD, c = idx % kD;
+      q_lds[jj][c] = jj < g ? elem2f(qg[jj * kD + c], a.sh.kv_bf16) : 0.0f;
+    }
+  }
+  __syncthreads();
   auto load_q = [&](int m, float x[8]) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 32 * m);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      x[e] = head_ok ? elem2f((uint16_t)(w[e >> 1] >> (16 * (e & 1))), a.sh.kv_bf16) : 0.0f;
+    const f32x4 u = *reinterpret_cast<const f32x4*>(&q_lds[j][32 * m + 8 * q4]);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(&q_lds[j][32 * m + 8 * q4 + 4]);
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+    x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
   };
 
   // ---- per-token keys: fixed B operand, scaled by 2^Eq ---------------------------
@@ -322,57 +345,76 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- per-channel keys: stage this wave's key-group parameters in LDS -----------
+  // ---- per-channel keys: the wave's key-group parameters, staged in LDS ----------
+  // A ring of a.kp_groups groups per wave, refilled (by the wave alone) when
+  // the next group lies past the staged run.
   const int gblk = KCH ? Gk / kTile : 1;   // blocks per key group
-  const int g_first = wb0 / gblk;
-  const bool kp_staged = KCH && a.kp_groups > 0;
+  const int last_grp = KCH ? max(wq1 - 1, 0) / gblk : 0;
   const uint32_t* kgrp_base = KCH ? static_cast<const uint32_t*>(K.params) +
                                         (int64_t)bh * (Tcap / Gk) * kD
                                   : nullptr;
-  if constexpr (KCH) {
-    if (kp_staged && wq1 > wb0) {
-      const int ng_w = (wq1 - 1) / gblk - g_first + 1;
-      const u32x4* src = reinterpret_cast<const u32x4*>(kgrp_base + (int64_t)g_first * kD);
-      u32x4* dst = kp_lds + wave * a.kp_groups * 32;
-      for (int c0 = 0; c0 < ng_w * 32; c0 += 256) {
-        u32x4 v[4];
+  u32x4* const kp_w = kp_lds + wave * a.kp_groups * 32;
+  int kp_lo = 0, kp_hi = 0;    // staged groups [kp_lo, kp_hi)
+  auto stage_kp = [&](int g0) {
+    const int g1 = min(g0 + a.kp_groups, last_grp + 1);
+    const u32x4* src = reinterpret_cast<const u32x4*>(kgrp_base + (int64_t)g0 * kD);
+    const int n4 = (g1 - g0) * 32;
+    for (int c0 = 0; c0 < n4; c0 += 256) {
+      u32x4 v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int c = c0 + u * 64 + lane;
-          if (c < ng_w * 32) v[u] = src[c];
-        }
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < n4) v[u] = src[c];
+      }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int c = c0 + u * 64 + lane;
-          if (c < ng_w * 32) dst[c] = v[u];
-        }
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < n4) kp_w[c] = v[u];
       }
     }
-    __syncthreads();
-  }
+    kp_lo = g0;
+    kp_hi = g1;
+    // LDS accesses of one wave complete in order: the reads that follow see
+    // these writes from every lane
+    __builtin_amdgcn_wave_barrier();
+  };
 
   // ---- running state -----------------------------------------------------------
   f32x4 oacc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Probabilities are kept in "fed units": p' = 2^(s - m_run + pexp) for the
+  // even pairs of the P operand and 2^-kOdd times that for the odd pairs
+  // (4-bit values: the nibble of an odd pair is unpacked 4 bits up).  The
+  // bias -(m_run - pexp) is folded into the key products of the high
+  // columns, so one exp2 of t = s - mref (- kOdd) yields p'.
+  constexpr float kOdd = VB == 4 ? 4.0f : 0.0f;
   float m_run = -INFINITY;   // reference maximum of head j (lanes n, n + 8 agree)
-  float l_run = 0.f;         // partial over this lane's tokens
-  float vbias[NGV];          // sum p * zero (values), true units
-  float voff[NGV];           // q8_0: sum of the fed P operand
+  float mref = 0.f;          // bias folded into t (m_run - pexp once m_run is set)
+  float thr = -INFINITY;     // rescale when t > thr (= kLazy + m_run - mref)
+  float l_run[2] = {0.f, 0.f};   // sum of p' over this lane's even / odd tokens
+  float vbias[NGV][2];       // sum p' * zero over even / odd tokens (values)
+  float voff[NGV];           // q8_0: sum of the P operand before its fp16 split
 #pragma unroll
-  for (int gi = 0; gi < NGV; ++gi) { vbias[gi] = 0.f; voff[gi] = 0.f; }
+  for (int gi = 0; gi < NGV; ++gi) { vbias[gi][0] = vbias[gi][1] = 0.f; voff[gi] = 0.f; }
   // value operand scale: fed P = p * scale * 2^pexp <= 2^12 (p <= 2^kLazy);
-  // pexp only decreases, when a block brings a larger value scale (the
-  // accumulators are then rescaled by the exact power of two)
-  int pexp = 100;
+  // pexp changes when a block brings a scale above sbound (the accumulators
+  // are then rescaled by the exact power of two)
+  int pexp = 0;
   float sbound = 0.f;
-  float cpair[2];            // 2^pexp times the unpack factor of even/odd pairs
-  cpair[0] = pow2i(pexp);
-  cpair[1] = cpair[0] * pair_factor<VB>(1);
 
   // per-channel keys: B operand of the current key group
   half8 bk[4];
   float kbias = 0.f;         // sm2 * sum_c q_c z_c (high lanes)
+  float tbias[2] = {0.f, -kOdd};   // high lanes: -mref, -mref - kOdd
+  float kb2[2] = {0.f, 0.f};       // kbias + tbias
+  if (!hi_lane) tbias[1] = 0.f;
+  auto set_bias = [&]() {
+    tbias[0] = hi_lane ? -mref : 0.f;
+    tbias[1] = hi_lane ? -mref - kOdd : 0.f;
+    kb2[0] = kbias + tbias[0];
+    kb2[1] = kbias + tbias[1];
+  };
   float kscale = 0.f;        // sm2 * 2^(24 - E)
   int grp_end = -1;          // first block after the current key group
 
@@ -399,8 +441,8 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 
   // per-channel keys: B operand and zero-point term of key group ``grp``
   auto key_group = [&](int grp) {
-    const u32x4* prm4 = kp_staged ? kp_lds + (wave * a.kp_groups + (grp - g_first)) * 32
-                                  : reinterpret_cast<const u32x4*>(kgrp_base + (int64_t)grp * kD);
+    if (grp >= kp_hi) stage_kp(grp);   // wave-uniform
+    const u32x4* prm4 = kp_w + (grp - kp_lo) * 32;
     float mx = 0.f, zb = 0.f;
     float qs[4][8];
 #pragma unroll
@@ -412,9 +454,10 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
       const uint32_t pz[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        qs[m][e] = qv[e] * h2f((uint16_t)(pz[e] & 0xffff));
+        const half2v sz = __builtin_bit_cast(half2v, pz[e]);   // (scale, zero)
+        qs[m][e] = __builtin_fmaf(qv[e], (float)sz[0], 0.f);
         mx = fmaxf(mx, fabsf(qs[m][e]));
-        zb += qv[e] * h2f((uint16_t)(pz[e] >> 16));
+        zb = __builtin_fmaf(qv[e], (float)sz[1], zb);
       }
     }
     mx = wave_max(mx);
@@ -426,107 +469,149 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     for (int m = 0; m < 4; ++m) bk[m] = pair_operand<KB>(qs[m], s2, lo_mask);
     zb = rows_sum(zb);
     kbias = hi_lane ? zb * sm2 : 0.f;
+    kb2[0] = kbias + tbias[0];
+    kb2[1] = kbias + tbias[1];
   };
 
-  // softmax + P.V for one block; sc holds base-2 scores before the sum of
-  // the high/low columns
-  auto softmax_pv = [&](float sc[2][4], const uint32_t* vl, const uint32_t (*vp)[VPD], int valid) {
+  // Softmax and P.V for one block.  sc: per-column partial scores (the bias
+  // tbias sits in the high columns), so that the sum of a lane's high and
+  // low columns is t = s - mref (- kOdd for odd pairs).  RAGGED (an
+  // integral_constant) is true only for a block with fewer than 32 cached
+  // tokens: the others skip the masking.
+  auto softmax_pv = [&](auto ragged, float sc[2][4], const uint32_t* vl,
+                        const uint32_t (*vp_in)[VPD], int valid) {
+    constexpr bool RAGGED = decltype(ragged)::value;
+    auto tok_ok = [&](int mb, int r) { return !RAGGED || 16 * mb + 4 * q4 + r < valid; };
+    float t[2][4];
     float bmax = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float s = sc[mb][r] + dpp_ror8(sc[mb][r]);
-        if (valid < kTile && 16 * mb + 4 * q4 + r >= valid) s = -INFINITY;
-        sc[mb][r] = s;
-        bmax = fmaxf(bmax, s);
+        const float x = sc[mb][r] + dpp_ror8(sc[mb][r]);
+        t[mb][r] = tok_ok(mb, r) ? x : -INFINITY;
+        bmax = fmaxf(bmax, t[mb][r]);
       }
-    if (__any(bmax > m_run + kLazy)) {
+    if (__any(bmax > thr)) {
       // move the reference maximum (wave-uniform branch, rare after warm-up)
-      const float m_new = fmaxf(m_run, rows_max(bmax));
+      const float m_new = fmaxf(m_run, rows_max(bmax) + mref);
       const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+      l_run[0] *= alpha;
+      l_run[1] *= alpha;
 #pragma unroll
-      for (int gi = 0; gi < NGV; ++gi) { vbias[gi] *= alpha; voff[gi] *= alpha; }
-      // accumulator row r of this lane belongs to head (4 q4 + r) & 7
-      float al[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        al[jj] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), jj));
+      for (int gi = 0; gi < NGV; ++gi) {
+        vbias[gi][0] *= alpha;
+        vbias[gi][1] *= alpha;
+        voff[gi] *= alpha;
+      }
+      // accumulator row r of this lane belongs to head (4 q4 + r) & 7, whose
+      // factor sits in lane (4 q4 + r) & 7 (a lane shuffle: a per-lane pick
+      // from an array would go through scratch memory)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float f = (q4 & 1) ? al[4 + r] : al[r];
+        const float f = __shfl(alpha, 4 * (q4 & 1) + r, 64);
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) oacc[nb][r] *= f;
       }
       m_run = m_new;
+      const float mref_new = m_run - (float)pexp;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[mb][r] += mref - mref_new;
+      mref = mref_new;
+      thr = kLazy + (float)pexp;
+      set_bias();
     }
-    float p[2][4];
+
+    // value parameters of this lane's 8 tokens (zeroed past the context)
+    uint32_t vp[2][VPD];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[mb][r] = __builtin_amdgcn_exp2f(sc[mb][r] - m_run);
-        l_run += p[mb][r];
-      }
-    // value scales (and zeros) of this lane's 8 tokens
-    float vsc[NGV][8], vze[NGV][8];
-    float smax = 0.f;
-#pragma unroll
-    for (int gi = 0; gi < NGV; ++gi)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const uint32_t* d = vp[mb];
-          float s, z = 0.f;
-          if constexpr (VQ8) {
-            const int idx = r * NGV + gi;
-            s = h2f((uint16_t)(d[idx >> 1] >> (16 * (idx & 1))));
-          } else {
-            s = h2f((uint16_t)(d[r * NGV + gi] & 0xffff));
-            z = h2f((uint16_t)(d[r * NGV + gi] >> 16));
+      for (int w = 0; w < VPD; ++w) {
+        uint32_t d = vp_in[mb][w];
+        if constexpr (RAGGED) {
+          if constexpr (VQ8) {   // two entries (token r = entry / NGV) per dword
+            const uint32_t lo = tok_ok(mb, (2 * w) / NGV) ? 0x0000ffffu : 0u;
+            const uint32_t hi = tok_ok(mb, (2 * w + 1) / NGV) ? 0xffff0000u : 0u;
+            d &= lo | hi;
+          } else {               // scale | zero << 16 of token r = w / NGV
+            d = tok_ok(mb, w / NGV) ? d : 0u;
           }
-          if (valid < kTile && 16 * mb + 4 * q4 + r >= valid) { s = 0.f; z = 0.f; }
-          vsc[gi][r + 4 * mb] = s;
-          vze[gi][r + 4 * mb] = z;
-          smax = fmaxf(smax, s);
         }
+        vp[mb][w] = d;
       }
+    // largest value scale of the block (scales are non-negative fp16)
+    half2v smx = __builtin_bit_cast(half2v, vp[0][0]);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int w = 0; w < VPD; ++w) smx = __builtin_elementwise_max(smx, __builtin_bit_cast(half2v, vp[mb][w]));
+    const float smax = VQ8 ? fmaxf((float)smx[0], (float)smx[1]) : (float)smx[0];
     if (__any(smax > sbound)) {
-      smax = rows_max(smax);                   // same tokens in every column
-      int np = 12 - (int)kLazy - ceil_log2(smax);
-      np = np < -100 ? -100 : (np > 126 ? 126 : np);
+      const float sm = rows_max(smax);         // same tokens in every column
+      int np = 12 - (int)kLazy - ceil_log2(sm);
+      np = np < -60 ? -60 : (np > 60 ? 60 : np);
       const int e = np - pexp;                 // rescale what was fed so far
-      const float f = e < -126 ? 0.f : (e > 126 ? 1.f : pow2i(e));
+      const float f = pow2i(e);
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) oacc[nb][r] *= f;
+      l_run[0] *= f;
+      l_run[1] *= f;
 #pragma unroll
-      for (int gi = 0; gi < NGV; ++gi) voff[gi] *= f;
+      for (int gi = 0; gi < NGV; ++gi) {
+        vbias[gi][0] *= f;
+        vbias[gi][1] *= f;
+        voff[gi] *= f;
+      }
       pexp = np;
       sbound = pow2i(12 - (int)kLazy - np);
-      cpair[0] = pow2i(np);
-      cpair[1] = cpair[0] * pair_factor<VB>(1);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[mb][r] += (float)e;
+      mref -= (float)e;
+      thr = kLazy + (float)pexp;
+      set_bias();
     }
+
+    // probabilities in fed units
+    float pr[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[mb][r] = __builtin_amdgcn_exp2f(t[mb][r]);
+        l_run[r & 1] += pr[mb][r];
+      }
+    // P operand: pair r = tokens (4 q4 + r, 16 + 4 q4 + r), p' * scale split
+    // into fp16 high / low parts; zero points enter through vbias
     half8 pa[NGV];
 #pragma unroll
     for (int gi = 0; gi < NGV; ++gi) {
       uint32_t o[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float c = cpair[r & 1];
-        o[r] = hilo2(p[0][r] * (vsc[gi][r] * c), p[1][r] * (vsc[gi][r + 4] * c), lo_mask);
-        if constexpr (!VQ8) vbias[gi] += p[0][r] * vze[gi][r] + p[1][r] * vze[gi][r + 4];
+        float x[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          if constexpr (VQ8) {
+            const int idx = r * NGV + gi;
+            const half2v h = __builtin_bit_cast(half2v, vp[mb][idx >> 1]);
+            x[mb] = __builtin_fmaf(pr[mb][r], (float)h[idx & 1], 0.f);
+          } else {
+            const half2v h = __builtin_bit_cast(half2v, vp[mb][r * NGV + gi]);
+            x[mb] = __builtin_fmaf(pr[mb][r], (float)h[0], 0.f);
+            vbias[gi][r & 1] = __builtin_fmaf(pr[mb][r], (float)h[1], vbias[gi][r & 1]);
+          }
+        }
+        o[r] = hilo_split(x[0], x[1], lo_mask);
+        if constexpr (VQ8) voff[gi] += x[0] + x[1];
       }
       pa[gi] = as_h8(o[0], o[1], o[2], o[3]);
-      if constexpr (VQ8) {
-        float so = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) so += (float)pa[gi][e];
-        voff[gi] += so;
-      }
     }
 #pragma unroll
     for (int nbk = 0; nbk < 8; ++nbk) {
@@ -536,7 +621,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   };
 
   // one block with quantized keys
-  auto compute = [&](const Buf& B, int blk) {
+  auto compute = [&](auto ragged, const Buf& B, int blk) {
     const int valid = nctx - blk * kTile;
     float sc[2][4];
     if constexpr (KCH) {
@@ -551,12 +636,12 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) c = mfma16(seg_block<KB, KQ8>(B.k[mb], m), bk[m], c);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[mb][r] = c[r] * kscale + kbias;
+        for (int r = 0; r < 4; ++r) sc[mb][r] = c[r] * kscale + kb2[r & 1];
       }
     } else {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        float acc[4] = {tbias[0], tbias[1], tbias[0], tbias[1]};
 #pragma unroll
         for (int gi = 0; gi < NGK; ++gi) {
           f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -582,19 +667,47 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
         for (int r = 0; r < 4; ++r) sc[mb][r] = acc[r];
       }
     }
-    softmax_pv(sc, B.v, B.vp, valid);
+    softmax_pv(ragged, sc, B.v, B.vp, valid);
   };
 
-  // ---- hot loop: two-stage register pipeline over quantized-key blocks -----------
-  if (wq1 > wb0) {
-    const int last = wq1 - 1;
-    Buf b0, b1;
-    load(b0, wb0);
-    for (int blk = wb0; blk < wq1; blk += 2) {
-      load(b1, min(blk + 1, last));
-      compute(b0, blk);
-      load(b0, min(blk + 2, last));
-      if (blk + 1 < wq1) compute(b1, blk + 1);
+  // ---- hot loop: register pipeline over the blocks with 32 cached tokens and
+  // quantized keys; kStages - 1 blocks are in flight while one is computed.
+  // (Prefetches past the end re-read the last block.)
+  const int wfull = KCH ? wq1 : max(wb0, min(wq1, nctx / kTile));
+  if (wfull > wb0) {
+    const int last = wfull - 1;
+    if constexpr (kStages == 3) {
+      Buf b0, b1, b2;
+      load(b0, wb0);
+      load(b1, min(wb0 + 1, last));
+      for (int blk = wb0; blk < wfull; blk += 3) {
+        load(b2, min(blk + 2, last));
+        compute(std::false_type{}, b0, blk);
+        if (blk + 1 >= wfull) break;
+        load(b0, min(blk + 3, last));
+        compute(std::false_type{}, b1, blk + 1);
+        if (blk + 2 >= wfull) break;
+        load(b1, min(blk + 4, last));
+        compute(std::false_type{}, b2, blk + 2);
+      }
+    } else {
+      Buf b0, b1;
+      load(b0, wb0);
+      for (int blk = wb0; blk < wfull; blk += 2) {
+        load(b1, min(blk + 1, last));
+        compute(std::false_type{}, b0, blk);
+        if (blk + 1 >= wfull) break;
+        load(b0, min(blk + 2, last));
+        compute(std::false_type{}, b1, blk + 1);
+      }
+    }
+  }
+  // per-token keys: the ragged last block of the context
+  if constexpr (!KCH) {
+    if (wq1 > wfull) {
+      Buf br;
+      load(br, wfull);
+      compute(std::true_type{}, br, wfull);
     }
   }
 
@@ -621,23 +734,23 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
           c = mfma16(__builtin_bit_cast(half8, v), bt[m], c);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[mb][r] = c[r] * sm2;
+        for (int r = 0; r < 4; ++r) sc[mb][r] = c[r] * sm2 + tbias[r & 1];
       }
       Buf B;
       load(B, blk);
-      softmax_pv(sc, B.v, B.vp, nctx - t0);
+      softmax_pv(std::true_type{}, sc, B.v, B.vp, nctx - t0);
     }
   }
 
   // ---- wave result -> LDS (true units) ------------------------------------------
-  const float l_tot = rows_sum(l_run);
+  const float vscale = pow2i(-pexp);          // fed units -> true units
+  const float l_tot = rows_sum(l_run[0] + l_run[1] * pow2i((int)kOdd)) * vscale;
   // high + low rows: lanes q4 = 0, 1 hold the high parts of heads 4*q4 + r,
   // lanes q4 + 2 the low parts.
 #pragma unroll
   for (int nbk = 0; nbk < 8; ++nbk)
 #pragma unroll
     for (int r = 0; r < 4; ++r) oacc[nbk][r] += swap_halves(oacc[nbk][r]);
-  const float vscale = pow2i(-pexp);          // fed units -> true units
   const float oscale = 0x1p24f * vscale;      // codes are fed as code * 2^-24
   if (q4 < 2) {
 #pragma unroll
@@ -650,9 +763,8 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   float vb_tot[NGV], vo_tot[NGV];
 #pragma unroll
   for (int gi = 0; gi < NGV; ++gi) {
-    vb_tot[gi] = rows_sum(vbias[gi]);
+    vb_tot[gi] = rows_sum(vbias[gi][0] + vbias[gi][1] * pow2i((int)kOdd)) * vscale;
     vo_tot[gi] = rows_sum(voff[gi]);
-    vo_tot[gi] += dpp_ror8(vo_tot[gi]);   // rows (j, hi) + (j, lo)
   }
   if (q4 == 0 && n < 8) {
     wm[wave][j] = m_run;
@@ -748,11 +860,13 @@ hipError_t launch_decode_mfma(const DecodeArgs& a_in, hipStream_t s) {
   DecodeArgs a = a_in;
   a.kp_groups = 0;
   if (a.k.per_channel) {
-    // key groups one wave can touch: its blocks plus one partial group
+    // key groups one wave can touch (its blocks plus one partial group), up
+    // to a ring of kMaxKpGroups per wave (32 KB of LDS for the 4 waves)
+    constexpr int kMaxKpGroups = 16;
     const int per_wave = (a.blocks_per_split + 3) / 4;
     const int gblk = a.k.G / kTile;
     const int groups = (per_wave + gblk - 1) / gblk + 1;
-    if ((size_t)4 * groups * kD * 4 <= 64 * 1024) a.kp_groups = groups;
+    a.kp_groups = groups < kMaxKpGroups ? groups : kMaxKpGroups;
   }
   bool ok = false;
   if (a.k.per_channel) {

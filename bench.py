@@ -108,6 +108,8 @@ def main():
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--ctx", type=int, default=None, help="context (config 2: 4096/8192/16384)")
     ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="upper bound on split-K partitions of the token axis (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -150,7 +152,8 @@ def main():
     serving = args.config == 5
     K, W = args.steps, args.warmup
     max_ctx = w.ctx + (K + W + 1 if serving else 0)
-    cfg = kvq.config_from_workload(w, max_ctx=max_ctx, decode_path=args.path)
+    cfg = kvq.config_from_workload(w, max_ctx=max_ctx, decode_path=args.path,
+                                   decode_splits=args.splits)
     stream = torch.cuda.Stream()
     log(f"workload cfg{w.cfg_id} {CONFIG_NAME(w)}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} "
         f"T={w.ctx}; generating inputs on the GPU")

@@ -362,11 +362,14 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   a.kp_groups = 0;
   a.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(cache->base) + L.partial_off);
 
-  // Split the token axis so that the grid covers the GPU several times:
-  // about 2048 workgroups, each with at least two 32-token blocks per wave.
+  // Split the token axis so that the grid is about one resident round of
+  // workgroups (256 CUs x 2 workgroups of 4 waves): fewer, longer
+  // workgroups amortize each one's set-up and merge, and more rounds only
+  // add a ragged tail.  Each split keeps at least 8 blocks of 32 tokens.
   const int64_t nblocks = (a.n_ctx + kTile - 1) / kTile;
   const int64_t pairs = (int64_t)cfg->batch * cfg->n_kv_heads;
-  int64_t want = (2048 + pairs - 1) / pairs;
+  constexpr int64_t kTargetWorkgroups = 512;
+  int64_t want = (kTargetWorkgroups + pairs - 1) / pairs;
   int64_t by_len = nblocks / 8;
   if (want > by_len) want = by_len;
   if (cfg->decode_splits > 0 && want > cfg->decode_splits) want = cfg->decode_splits;

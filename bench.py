@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused quantized decode attention: effective HBM GB/s (% of peak), µs/step"
 PEAK_HBM_GBS = 8000.0
-DECODE_KERNELS = {"valu": "dec_generic_kernel", "mfma": "dec_mfma_kernel"}
+DECODE_KERNELS = {"valu": "dec_generic_kernel", "mfma": "dec_mfma_kernel", "lut": "dec_lut_kernel"}
 
 
 def log(*a):
@@ -107,7 +107,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--ctx", type=int, default=None, help="context (config 2: 4096/8192/16384)")
-    ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--path", choices=["auto", "valu", "mfma", "lut"], default="auto")
     ap.add_argument("--splits", type=int, default=0,
                     help="upper bound on split-K partitions of the token axis (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

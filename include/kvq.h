@@ -98,12 +98,15 @@ typedef int32_t kvq_status;
 /* ---- decode kernel selection ------------------------------------------- */
 /* AUTO picks the matrix-core kernel when the formats allow it (uniform
  * quantizers or raw storage for both tensors, no RoPE, no codebook, at most
- * 8 query heads per KV head) and the vector-ALU kernel otherwise.  VALU and
- * MFMA force a kernel; MFMA on a configuration it cannot run is
- * KVQ_ERR_UNSUPPORTED.  Both compute the same attention to rounding. */
+ * 8 query heads per KV head), the lookup-table kernel for 4-bit codebook
+ * keys and values with one query head per KV head (with or without
+ * outliers and RoPE), and the general vector-ALU kernel otherwise.  VALU,
+ * MFMA and LUT force a kernel; MFMA or LUT on a configuration it cannot run
+ * is KVQ_ERR_UNSUPPORTED.  All compute the same attention to rounding. */
 #define KVQ_PATH_AUTO 0
 #define KVQ_PATH_VALU 1
 #define KVQ_PATH_MFMA 2
+#define KVQ_PATH_LUT  3
 
 /* ---- kvq_cache_bytes selectors ----------------------------------------- */
 #define KVQ_BYTES_PAYLOAD 0   /* bytes that hold n_ctx tokens, x n_layers    */
@@ -204,6 +207,9 @@ kvq_status kvq_cache_bytes(const kvq_config* cfg, int64_t n_ctx, int64_t n_layer
  *   values: tiles of 32 tokens, 64 lanes L = 16q + i of 8*bits bytes (two
  *     segments s); segment s, block m of lane L holds channel 16(4s+m) + i,
  *     element e is token 4q+e (e < 4) or 16+4q+e-4 of the tile.
+ *   CODEBOOK values: tiles of 32 tokens (2048 bytes); byte 32l + tau holds
+ *     channel l in its low nibble and channel l+64 in its high nibble of
+ *     token tau (l = 0..63).
  *   params: per-token [B][Hkv][Tcap][d/G] of (scale, zero) fp16 pairs
  *     (q8_0: scales only); per-channel [B][Hkv][Tcap/G][d] pairs.
  *   NONE: raw rows [B][Hkv][Tcap][d] of kv_dtype for keys and values.
@@ -252,7 +258,7 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
 
 /*
  * kvq_decode_path -- which decode kernel kvq_decode_attention runs for this
- * configuration: KVQ_PATH_VALU or KVQ_PATH_MFMA (what KVQ_PATH_AUTO resolves
+ * configuration: KVQ_PATH_VALU, KVQ_PATH_MFMA or KVQ_PATH_LUT (what KVQ_PATH_AUTO resolves
  * to, or the forced path).  Host only.  Returns a negative status for an
  * invalid configuration or a forced path it cannot run.
  */

@@ -141,6 +141,27 @@ def pack_v_tiles(codes: np.ndarray, bits: int) -> np.ndarray:
     return np.concatenate(lanes, axis=-1)
 
 
+def v_pair_position(byte: int, half: int):
+    """(token-in-tile, channel) held by nibble ``half`` (0 low, 1 high) of byte
+    ``byte`` of a codebook value tile: byte 32*l + tau holds channel l (low
+    nibble) and channel l + 64 (high nibble) of token tau, l = 0..63."""
+    lane, tau = byte // 32, byte % 32
+    return tau, lane + 64 * half
+
+
+def pack_v_pair_tiles(codes: np.ndarray) -> np.ndarray:
+    """4-bit codes [..., T, 128] with T a multiple of 32 -> bytes
+    [..., T/32, 2048] in the codebook value-tile layout (v_pair_position)."""
+    codes = np.asarray(codes)
+    T = codes.shape[-2]
+    assert T % 32 == 0
+    tiles = codes.reshape(codes.shape[:-2] + (T // 32, 32, D))
+    lo = tiles[..., :, :64]                          # [..., ntiles, tau, l]
+    hi = tiles[..., :, 64:]
+    b = (lo | (hi << 4)).astype(np.uint8)
+    return np.swapaxes(b, -1, -2).reshape(codes.shape[:-2] + (T // 32, 2048))
+
+
 def expected_regions(fmt: Dict, enc: Dict[str, np.ndarray], *, batch: int, n_kv_heads: int,
                      n_ctx: int, max_ctx: int, kv_dtype: str, is_key: bool) -> Dict[str, np.ndarray]:
     """Byte-exact image of one tensor's cache regions after ``n_ctx`` tokens.
@@ -148,7 +169,8 @@ def expected_regions(fmt: Dict, enc: Dict[str, np.ndarray], *, batch: int, n_kv_
     Region arrays (unwritten entries are zero):
 
     * ``codes`` uint8 [B, H, Tcap * row_bytes]: K-row layout for keys,
-      V-tile layout for values (NONE stores raw fp16/bf16 rows instead);
+      V-tile layout for values, the pair-tile layout for codebook values
+      (NONE stores raw fp16/bf16 rows instead);
     * ``params``: per-token asymmetric fp16 [B, H, Tcap, d/G, 2] (scale,
       zero); q8_0 fp16 [B, H, Tcap, d/G]; per-channel fp16
       [B, H, Tcap // G, d, 2];
@@ -172,6 +194,8 @@ def expected_regions(fmt: Dict, enc: Dict[str, np.ndarray], *, batch: int, n_kv_
     codes[:, :, :c.shape[2], :] = c
     if is_key:
         packed = pack_k_rows(codes, bits)                          # [B, H, Tcap, rb]
+    elif q == "codebook":
+        packed = pack_v_pair_tiles(codes)                          # [B, H, Tcap/32, 2048]
     else:
         packed = pack_v_tiles(codes, bits)                         # [B, H, Tcap/32, 32*rb]
     # tokens that are not yet quantized must leave their bytes at zero

@@ -169,7 +169,10 @@ def encode_tensor(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None) -> Dict
             cols, vals = select_outliers(flat, k)
             dflat = deq.reshape(B * T, H * d)
             rows = np.arange(B * T)[:, None]
-            dflat[rows, cols] = vals.astype(np.float64)  # replacement semantics
+            # replacement semantics with the stored fp16 value (KVQuant page,
+            # section 3.3: outliers are kept in fp16; exact for fp16 inputs,
+            # the nearest-even fp16 of a bf16 input)
+            dflat[rows, cols] = f16(vals).astype(np.float64)
             deq = dflat.reshape(B, T, H, d)
             out["cols"] = cols.reshape(B, T, k)
             out["vals"] = vals.reshape(B, T, k)

@@ -54,8 +54,11 @@ __device__ float deq_v(const DecodeArgs& a, int bh, int h, int t, int c) {
   if (v.quant == KVQ_QUANT_NONE)
     return elem2f(reinterpret_cast<const uint16_t*>(v.codes)[row * kD + c], a.sh.kv_bf16);
   const uint8_t* tile = v.codes + ((int64_t)bh * a.sh.Tcap + (t & ~(kTile - 1))) * v.row_bytes;
+  if (v.quant == KVQ_QUANT_CODEBOOK) {
+    const uint32_t code = v_pair_code(tile, t & (kTile - 1), c);
+    return h2f(v.codebook[((int64_t)h * kD + c) * 16 + code]);
+  }
   const uint32_t code = v_tile_code(tile, v.bits, t & (kTile - 1), c);
-  if (v.quant == KVQ_QUANT_CODEBOOK) return h2f(v.codebook[((int64_t)h * kD + c) * 16 + code]);
   return deq_uniform(code, v.quant, v.params, row * v.ng + c / v.G);
 }
 

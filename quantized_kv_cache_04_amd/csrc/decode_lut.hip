@@ -1,0 +1,379 @@
+// Lookup-table decode kernel of libkvq: codebook keys and values (4-bit
+// indices into 16 fp16 centroids per KV head and channel), one query head
+// per KV head, optional dense-and-sparse outliers and RoPE on the keys.
+//
+// The non-uniform codebooks and the sparse fp16 outliers follow the KVQuant
+// page (sections 2.2 and 3.3), with keys quantized before the rotary
+// embedding (sections 2.1-2.2) so that the rotation is applied at decode
+// time; dequantization stays fused into the single pass over the cache
+// (Memory-killer page, section 2.3).  Without a GQA group there is no dense
+// contraction to give the matrix cores, so everything runs on the vector
+// ALUs; the kernel is shaped so that every centroid lookup is an LDS read
+// without bank conflicts:
+//
+//  * workgroup = 4 waves = 4 KV heads over one range of tokens, walked in
+//    chunks of 64 tokens;
+//  * keys, lane = token: the score of token t is
+//      sum_i a_i (x_i cos + y_i sin) + b_i (y_i cos - x_i sin)
+//    over the rotate-half pairs (a_i, b_i) = (k_i, k_{i+64}) of the
+//    dequantized key and (x_i, y_i) of the query, at the angle
+//    (t - q_pos) theta_i.  All lanes of one lookup read the same channel, so
+//    the 16 centroids (one 32-byte row) serve every lane by broadcast;
+//  * values, lane = channel pair (l, l + 64): the codebook value tiles hold
+//    both 4-bit indices of a lane in one byte per token, and one LDS dword
+//    per (centroid, lane) holds both channels' centroids, so lane l always
+//    reads bank l;
+//  * the (cos, sin) table of a chunk (64 pairs x 64 tokens) is shared by the
+//    4 heads and advanced by one complex multiplication per entry and chunk,
+//    re-anchored from float64 angles every 32 chunks;
+//  * outliers (CSR rows of one token over all heads) are filtered by the
+//    whole workgroup and enter as (val - centroid) corrections: to the
+//    chunk's scores for keys, to LDS channel sums for values.
+//
+// Each wave leaves an (o, m, l) partial per split, or the output when the
+// context is one split.
+#include <hip/hip_runtime.h>
+
+#include "splitk.h"
+
+namespace kvq {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+constexpr int kD = kHeadDim;
+constexpr int kChunk = 64;      // tokens per chunk: one per lane on the key side
+constexpr int kHeads = 4;       // KV heads per workgroup, one per wave
+constexpr int kPairs = kD / 2;
+constexpr int kResync = 32;     // chunks between exact re-anchorings of the table
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct __align__(16) LutLds {
+  float2 e[kPairs][kChunk];        // (cos, sin) of (t0 + tau - p) theta_i       32 KB
+  uint16_t kt[kHeads][kD][16];     // key centroids, fp16 [head][channel][index]   16 KB
+  uint32_t vt[kHeads][16][64];     // value centroids: (index, l) -> C(l) | C(l+64) << 16
+  float qs[kHeads][kD];            // query * sm_scale * log2(e)
+  float scorr[kHeads][kChunk];     // key outlier corrections of the chunk's scores
+  float p[kHeads][kChunk];         // probabilities of the chunk
+  float vcorr[kHeads][kD];         // value outlier sums of the chunk
+  float2 estep[kPairs];            // (cos, sin) of kChunk * theta_i
+  double theta[kPairs];
+};
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// (cos, sin) of dt * theta, the angle formed and reduced in float64
+__device__ __forceinline__ float2 rope_cs(double theta, int64_t dt) {
+  const double ang = (double)dt * theta;
+  const double two_pi = 6.283185307179586476925286766559;
+  const double red = ang - two_pi * rint(ang / two_pi);
+  float sn, cs;
+  sincosf((float)red, &sn, &cs);
+  return make_float2(cs, sn);
+}
+
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(half2v, w)[0];
+}
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(half2v, w)[1];
+}
+
+template <bool ROPE, bool KOUT, bool VOUT>
+__global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
+  __shared__ LutLds S;
+  const DevTensor& K = a.k;
+  const DevTensor& V = a.v;
+  const int Hkv = a.sh.Hkv;
+  const int nhg = (Hkv + kHeads - 1) / kHeads;
+
+  // workgroup -> (sequence and range r, head group hg): the head groups of
+  // one range take consecutive ids of one residue mod 8, so that they run
+  // close together on one chiplet and share its L2 for the outlier rows
+  const int w = blockIdx.x;
+  const int hg = (w % (8 * nhg)) / 8;
+  const int r = (w / (8 * nhg)) * 8 + (w % 8);
+  if (r >= a.sh.B * a.splits) return;            // padding workgroup (whole block)
+  const int b = r / a.splits, split = r % a.splits;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int h = hg * kHeads + wave;
+  const bool head_ok = h < Hkv;                  // wave-uniform
+  const int nctx = a.n_ctx;
+  const int64_t Tcap = a.sh.Tcap;
+  const int t_begin = split * a.blocks_per_split * kTile;
+  const int t_end = min(nctx, t_begin + a.blocks_per_split * kTile);
+  const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
+  const int qpos = a.q_pos ? a.q_pos[b] : nctx - 1;
+  const float sm2 = a.sm_scale * kLog2e;
+
+  // ---- tables ------------------------------------------------------------------
+  if (head_ok) {
+    // key centroids: the head's [128][16] fp16 block, copied as dwords
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(K.codebook) + (int64_t)h * kD * 8;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(&S.kt[wave][0][0]);
+    for (int i = lane; i < kD * 8; i += 64) dst[i] = src[i];
+    // value centroids of channels lane and lane + 64, interleaved per index
+    const uint16_t* vc = V.codebook + (int64_t)h * kD * 16;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      S.vt[wave][e][lane] = (uint32_t)vc[lane * 16 + e] | ((uint32_t)vc[(lane + 64) * 16 + e] << 16);
+    const uint16_t* qg = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.sh.Hq + h) * kD;
+    S.qs[wave][lane] = elem2f(qg[lane], a.sh.kv_bf16) * sm2;
+    S.qs[wave][lane + 64] = elem2f(qg[lane + 64], a.sh.kv_bf16) * sm2;
+  }
+  if constexpr (ROPE) {
+    if (tid < kPairs) S.theta[tid] = pow((double)a.rope_base, -2.0 * (double)tid / (double)kD);
+  }
+  for (int i = tid; i < kHeads * kChunk; i += 256) (&S.scorr[0][0])[i] = 0.f;
+  for (int i = tid; i < kHeads * kD; i += 256) (&S.vcorr[0][0])[i] = 0.f;
+  __syncthreads();
+  auto anchor = [&](int t0) {   // exact (cos, sin) of the chunk starting at t0
+    for (int idx = tid; idx < kPairs * kChunk; idx += 256) {
+      const int i = idx / kChunk, tau = idx % kChunk;
+      S.e[i][tau] = rope_cs(S.theta[i], (int64_t)t0 + tau - qpos);
+    }
+  };
+  if constexpr (ROPE) {
+    if (tid < kPairs) S.estep[tid] = rope_cs(S.theta[tid], kChunk);
+    anchor(t_begin);
+    __syncthreads();
+  }
+
+  // ---- per-wave state ------------------------------------------------------------
+  float m_run = -INFINITY, l_lane = 0.f;
+  float acc0 = 0.f, acc1 = 0.f;                  // channels lane, lane + 64
+  const uint8_t* krows = K.codes + ((int64_t)b * Hkv + (head_ok ? h : 0)) * Tcap * 64;
+  const uint8_t* vtiles = V.codes + ((int64_t)b * Hkv + (head_ok ? h : 0)) * Tcap * 64;
+
+  // codes of one chunk: key row of token (lane), value bytes of channel pair (lane)
+  u32x4 kc[4], vc[4];
+  auto load_chunk = [&](int t0, u32x4* kk, u32x4* vv) {
+    const int tk = min(t0 + lane, nctx - 1);          // clamp past the end (masked later)
+    const u32x4* kr = reinterpret_cast<const u32x4*>(krows + (int64_t)tk * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kk[i] = kr[i];
+    // two tiles of 32 tokens; lane owns 32 bytes of each (a tile past the
+    // range is not read: its probabilities are zero)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      if (t0 + 32 * tt < t_end) {
+        const u32x4* vr = reinterpret_cast<const u32x4*>(vtiles + (int64_t)(t0 + 32 * tt) * 64 + lane * 32);
+        vv[2 * tt] = vr[0];
+        vv[2 * tt + 1] = vr[1];
+      } else {
+        vv[2 * tt] = u32x4{0u, 0u, 0u, 0u};
+        vv[2 * tt + 1] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  if (head_ok && n_chunks > 0) load_chunk(t_begin, kc, vc);
+
+  for (int ci = 0; ci < n_chunks; ++ci) {
+    const int t0 = t_begin + ci * kChunk;
+    const int nt = min(kChunk, t_end - t0);      // tokens of this chunk
+    const int64_t row0 = (int64_t)b * Tcap + t0; // CSR row of token t0
+
+    // ---- key outliers: score corrections ---------------------------------------
+    if constexpr (KOUT) {
+      const int ko = K.k_out;
+      const int tau = tid & 63;
+      if (tau < nt) {
+        for (int jj = tid >> 6; jj < ko; jj += 4) {
+          const int64_t e = (row0 + tau) * ko + jj;
+          const int col = K.col[e];
+          const int hh = col >> 7, ww = hh - hg * kHeads;
+          if (ww < 0 || ww >= kHeads || hh >= Hkv) continue;
+          const int c = col & (kD - 1);
+          const uint8_t* row = K.codes + (((int64_t)b * Hkv + hh) * Tcap + t0 + tau) * 64;
+          const uint32_t code = k_row_code(row, 4, c);
+          const float delta = h2f(K.val[e]) - h2f(S.kt[ww][c][code]);
+          float coef;
+          if constexpr (ROPE) {
+            const int i = c & (kPairs - 1);
+            const float2 cs = S.e[i][tau];
+            const float x = S.qs[ww][i], y = S.qs[ww][i + kPairs];
+            coef = c < kPairs ? x * cs.x + y * cs.y : y * cs.x - x * cs.y;
+          } else {
+            coef = S.qs[ww][c];
+          }
+          atomicAdd(&S.scorr[ww][tau], delta * coef);
+        }
+      }
+      __syncthreads();
+    }
+
+    u32x4 kn[4], vn[4];
+    if (head_ok && ci + 1 < n_chunks) load_chunk(t0 + kChunk, kn, vn);
+
+    float alpha = 1.f;
+    if (head_ok) {
+      // ---- keys: lane = token ------------------------------------------------------
+      const uint32_t kw[16] = {kc[0].x, kc[0].y, kc[0].z, kc[0].w, kc[1].x, kc[1].y, kc[1].z, kc[1].w,
+                               kc[2].x, kc[2].y, kc[2].z, kc[2].w, kc[3].x, kc[3].y, kc[3].z, kc[3].w};
+      // centroid of channel c with index field at bit 4*e of dword w
+      auto cent = [&](uint32_t wd, int e, int c) -> float {
+        const uint32_t code = (wd >> (4 * e)) & 15u;
+        return (float)__builtin_bit_cast(_Float16, S.kt[wave][c][code]);
+      };
+      float s = 0.f;
+      // dword 4q + m of the row holds channels 32m + 8q + e (e = 0..7)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int i = 32 * m + 8 * q + e;          // pair (i, i + 64)
+            const float av = cent(kw[4 * q + m], e, i);
+            const float bv = cent(kw[4 * q + m + 2], e, i + kPairs);
+            const float x = S.qs[wave][i], y = S.qs[wave][i + kPairs];
+            if constexpr (ROPE) {
+              const float2 cs = S.e[i][lane];
+              s = __builtin_fmaf(av, x * cs.x + y * cs.y, s);
+              s = __builtin_fmaf(bv, y * cs.x - x * cs.y, s);
+            } else {
+              s = __builtin_fmaf(av, x, s);
+              s = __builtin_fmaf(bv, y, s);
+            }
+          }
+      if constexpr (KOUT) s += S.scorr[wave][lane];
+      if (lane >= nt) s = -INFINITY;
+
+      // ---- online softmax ----------------------------------------------------------
+      const float m_new = fmaxf(m_run, wave_max(s));
+      alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float pt = lane < nt ? __builtin_amdgcn_exp2f(s - m_new) : 0.f;
+      l_lane = l_lane * alpha + pt;
+      m_run = m_new;
+      S.p[wave][lane] = pt;
+      acc0 *= alpha;
+      acc1 *= alpha;
+      // LDS accesses of one wave complete in order: the reads below see p
+      __builtin_amdgcn_wave_barrier();
+
+      // ---- values: lane = channel pair ----------------------------------------------
+      const uint32_t vw[16] = {vc[0].x, vc[0].y, vc[0].z, vc[0].w, vc[1].x, vc[1].y, vc[1].z, vc[1].w,
+                               vc[2].x, vc[2].y, vc[2].z, vc[2].w, vc[3].x, vc[3].y, vc[3].z, vc[3].w};
+#pragma unroll
+      for (int d4 = 0; d4 < 16; ++d4) {
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(&S.p[wave][4 * d4]);
+        const uint32_t wd = vw[d4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t lo = (wd >> (8 * k)) & 15u, hi = (wd >> (8 * k + 4)) & 15u;
+          const uint32_t c0 = S.vt[wave][lo][lane];
+          const uint32_t c1 = S.vt[wave][hi][lane];
+          acc0 = __builtin_fmaf(p4[k], half_lo(c0), acc0);
+          acc1 = __builtin_fmaf(p4[k], half_hi(c1), acc1);
+        }
+      }
+    }
+
+    if constexpr (KOUT || VOUT || ROPE) __syncthreads();   // p complete; scorr and e consumed
+
+    // ---- value outliers, next chunk's table ----------------------------------------
+    if constexpr (VOUT) {
+      const int ko = V.k_out;
+      const int tau = tid & 63;
+      if (tau < nt) {
+        for (int jj = tid >> 6; jj < ko; jj += 4) {
+          const int64_t e = (row0 + tau) * ko + jj;
+          const int col = V.col[e];
+          const int hh = col >> 7, ww = hh - hg * kHeads;
+          if (ww < 0 || ww >= kHeads || hh >= Hkv) continue;
+          const int c = col & (kD - 1);
+          const uint8_t* tile = V.codes + (((int64_t)b * Hkv + hh) * Tcap + (t0 & ~(kTile - 1)) +
+                                           (tau & ~(kTile - 1))) * 64;
+          const uint32_t code = v_pair_code(tile, tau & (kTile - 1), c);
+          const uint32_t cc = S.vt[ww][code][c & (kPairs - 1)];
+          const float dense = c < kPairs ? half_lo(cc) : half_hi(cc);
+          atomicAdd(&S.vcorr[ww][c], S.p[ww][tau] * (h2f(V.val[e]) - dense));
+        }
+      }
+    }
+    if constexpr (KOUT) {
+      for (int i = tid; i < kHeads * kChunk; i += 256) (&S.scorr[0][0])[i] = 0.f;
+    }
+    if constexpr (ROPE) {
+      if (ci + 1 < n_chunks) {
+        if ((ci + 1) % kResync == 0) {
+          anchor(t0 + kChunk);
+        } else {
+          for (int idx = tid; idx < kPairs * kChunk; idx += 256) {
+            const int i = idx / kChunk, tau = idx % kChunk;
+            const float2 e0 = S.e[i][tau], st = S.estep[i];
+            S.e[i][tau] = make_float2(e0.x * st.x - e0.y * st.y, e0.x * st.y + e0.y * st.x);
+          }
+        }
+      }
+    }
+    if constexpr (VOUT) {
+      __syncthreads();                               // value outlier sums complete
+      if (head_ok) {
+        acc0 += S.vcorr[wave][lane];
+        acc1 += S.vcorr[wave][lane + 64];
+        S.vcorr[wave][lane] = 0.f;
+        S.vcorr[wave][lane + 64] = 0.f;
+      }
+    }
+    if constexpr (KOUT || ROPE) __syncthreads();     // zeroed scorr, next table visible
+
+    if (head_ok && ci + 1 < n_chunks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { kc[i] = kn[i]; vc[i] = vn[i]; }
+    }
+  }
+
+  // ---- partial of this split ---------------------------------------------------------
+  if (!head_ok) return;
+  const float L = wave_sum(l_lane);
+  if (a.splits == 1) {
+    const int64_t o = ((int64_t)b * a.sh.Hq + h) * kD;
+    store_out(a, o + lane, L > 0.f ? acc0 / L : 0.f);
+    store_out(a, o + lane + 64, L > 0.f ? acc1 / L : 0.f);
+  } else {
+    float* rec = partial_rec(a, b, h, split);
+    rec[lane] = acc0;
+    rec[lane + 64] = acc1;
+    if (lane == 0) { rec[kD] = m_run; rec[kD + 1] = L; }
+  }
+}
+
+template <bool ROPE>
+void launch_r(const DecodeArgs& a, unsigned grid, hipStream_t s) {
+  const bool ko = a.k.k_out > 0, vo = a.v.k_out > 0;
+  if (ko && vo) hipLaunchKernelGGL((dec_lut_kernel<ROPE, true, true>), dim3(grid), dim3(256), 0, s, a);
+  else if (ko) hipLaunchKernelGGL((dec_lut_kernel<ROPE, true, false>), dim3(grid), dim3(256), 0, s, a);
+  else if (vo) hipLaunchKernelGGL((dec_lut_kernel<ROPE, false, true>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((dec_lut_kernel<ROPE, false, false>), dim3(grid), dim3(256), 0, s, a);
+}
+
+}  // namespace
+
+bool lut_config_supported(const kvq_config& c) {
+  return c.k.quantizer == KVQ_QUANT_CODEBOOK && c.v.quantizer == KVQ_QUANT_CODEBOOK &&
+         c.k.bits == 4 && c.v.bits == 4 && c.n_q_heads == c.n_kv_heads &&
+         c.k.layout == KVQ_LAYOUT_PER_TOKEN && c.v.layout == KVQ_LAYOUT_PER_TOKEN;
+}
+
+hipError_t launch_decode_lut(const DecodeArgs& a, hipStream_t s) {
+  const int nhg = (a.sh.Hkv + kHeads - 1) / kHeads;
+  const int64_t ranges = (int64_t)a.sh.B * a.splits;
+  const unsigned grid = (unsigned)(((ranges + 7) / 8) * 8 * nhg);
+  if (a.rope) launch_r<true>(a, grid, s);
+  else launch_r<false>(a, grid, s);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -57,6 +57,12 @@ __device__ __forceinline__ uint32_t v_tile_code(const uint8_t* tile, int bits, i
   return seg_code(tile + lane * 8 * bits + s * 4 * bits, bits, 8 * m + e);
 }
 
+// Codebook value tiles: byte 32 l + tau holds channel l (low nibble) and
+// channel l + 64 (high nibble) of token tau.
+__device__ __forceinline__ uint32_t v_pair_code(const uint8_t* tile, int tau, int c) {
+  return (tile[(c & 63) * 32 + tau] >> (4 * (c >> 6))) & 15u;
+}
+
 // Bit fields of dword j of a segment: calls f(u, shift, width, field) where
 // ``field`` is 0 for the whole code, 1 for the low two bits, 2 for the high
 // bit (3-bit packing).

@@ -175,6 +175,26 @@ __global__ __launch_bounds__(256) void enc_vtile_kernel(DevShape sh, DevTensor t
   const int bits = t.bits;
   uint32_t* tile_dw = reinterpret_cast<uint32_t*>(
       t.codes + (((int64_t)b * sh.Hkv + h) * sh.Tcap + t_begin) * t.row_bytes);
+  if (t.quant == KVQ_QUANT_CODEBOOK) {
+    // pair tiles: byte 32 l + tau = code(tau, l) | code(tau, l + 64) << 4
+    for (int W = threadIdx.x; W < 512; W += 256) {
+      const int l = W >> 3, j = W & 7;
+      uint32_t nb = 0, nm = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int tau = 4 * j + k;
+        const int64_t tpos = t_begin + tau;
+        if (tpos >= lo_new && tpos < hi_new) {
+          nb |= (uint32_t)(codes[tau][l] | (codes[tau][l + 64] << 4)) << (8 * k);
+          nm |= 0xffu << (8 * k);
+        }
+      }
+      if (nm == 0) continue;
+      if (nm != 0xffffffffu) nb |= tile_dw[W] & ~nm;
+      tile_dw[W] = nb;
+    }
+    return;
+  }
   for (int W = threadIdx.x; W < 128 * bits; W += 256) {
     const int L = W / (2 * bits), s = (W / bits) & 1, j = W % bits;
     const int q = L >> 4, i = L & 15;
@@ -319,7 +339,8 @@ __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTenso
   for (int i = i0; i < i1; ++i) {
     if (keys[i] >= prefix) {
       t.col[r * k + pos] = (uint16_t)i;
-      t.val[r * k + pos] = xr[i];
+      // outliers are kept in fp16: a bf16 input is rounded to nearest-even
+      t.val[r * k + pos] = sh.kv_bf16 ? f2h_rn(bf2f(xr[i])) : xr[i];
       ++pos;
     }
   }

@@ -107,7 +107,7 @@ kvq_status check_config(const kvq_config* c) {
   if (c->rope && !(c->rope_base > 1.0f))
     return fail(KVQ_ERR_INVALID_ARGUMENT, "rope_base must be > 1");
   if (c->decode_splits < 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "decode_splits must be >= 0");
-  if (c->decode_path < KVQ_PATH_AUTO || c->decode_path > KVQ_PATH_MFMA)
+  if (c->decode_path < KVQ_PATH_AUTO || c->decode_path > KVQ_PATH_LUT)
     return fail(KVQ_ERR_INVALID_ARGUMENT, "unknown decode_path %d", c->decode_path);
   if ((uint64_t)c->batch * (uint64_t)c->max_ctx > ((uint64_t)1 << 31))
     return fail(KVQ_ERR_INVALID_ARGUMENT, "batch * max_ctx must be <= 2^31");
@@ -241,11 +241,17 @@ int32_t kvq_decode_path(const kvq_config* cfg) {
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
   const bool ok = mfma_config_supported(*cfg);
+  const bool lut = lut_config_supported(*cfg);
   if (cfg->decode_path == KVQ_PATH_MFMA && !ok)
     return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core decode kernel needs uniform or raw formats "
                 "for keys and values, no RoPE and at most 8 query heads per KV head");
-  if (cfg->decode_path == KVQ_PATH_VALU || !ok) return KVQ_PATH_VALU;
-  return KVQ_PATH_MFMA;
+  if (cfg->decode_path == KVQ_PATH_LUT && !lut)
+    return fail(KVQ_ERR_UNSUPPORTED, "the lookup-table decode kernel needs 4-bit codebook keys "
+                "and values and one query head per KV head");
+  if (cfg->decode_path == KVQ_PATH_VALU) return KVQ_PATH_VALU;
+  if (cfg->decode_path == KVQ_PATH_LUT || (cfg->decode_path == KVQ_PATH_AUTO && lut))
+    return KVQ_PATH_LUT;
+  return ok ? KVQ_PATH_MFMA : KVQ_PATH_VALU;
 }
 
 int32_t kvq_abi_version(void) { return 100; }
@@ -380,12 +386,30 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
 
   const int32_t path = kvq_decode_path(cfg);
   if (path < 0) return path;
-  const bool use_mfma = path == KVQ_PATH_MFMA;
+  if (path == KVQ_PATH_LUT) {
+    // ranges of whole 64-token chunks; a workgroup serves 4 KV heads, so
+    // about 512 workgroups take 512 / (batch * ceil(Hkv / 4)) ranges per
+    // sequence, each at least 4 chunks long
+    const int64_t nchunks = (a.n_ctx + 63) / 64;
+    const int64_t units = (int64_t)cfg->batch * ((cfg->n_kv_heads + 3) / 4);
+    int64_t r = (kTargetWorkgroups + units - 1) / units;
+    if (r > nchunks / 4) r = nchunks / 4;
+    if (cfg->decode_splits > 0 && r > cfg->decode_splits) r = cfg->decode_splits;
+    if (r > L.S_max) r = L.S_max;
+    if (r < 1) r = 1;
+    const int64_t per = (nchunks + r - 1) / r;
+    a.blocks_per_split = (int)(2 * per);
+    a.splits = (int)((nchunks + per - 1) / per);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
   g_ev_start = g_ev_stop = nullptr;
   hipError_t e = ev0 ? hipEventRecord(ev0, s) : hipSuccess;
-  if (e == hipSuccess) e = use_mfma ? launch_decode_mfma(a, s) : launch_decode_generic(a, s);
+  if (e == hipSuccess) {
+    e = path == KVQ_PATH_MFMA ? launch_decode_mfma(a, s)
+        : path == KVQ_PATH_LUT ? launch_decode_lut(a, s)
+                               : launch_decode_generic(a, s);
+  }
   if (e == hipSuccess && ev1) e = hipEventRecord(ev1, s);
   if (e == hipSuccess && a.splits > 1) e = launch_combine(a, s);
   return device_status(e, "decode attention");

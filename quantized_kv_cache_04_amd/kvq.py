@@ -22,7 +22,7 @@ F16, BF16, F32 = 0, 1, 2
 QUANT = {"none": 0, "asym_minmax": 1, "asym_absmax_offset": 2, "sym_q8_0": 3, "codebook": 4}
 LAYOUT = {"per_token": 0, "per_channel": 1}
 BYTES_PAYLOAD, BYTES_ALLOC = 0, 1
-PATHS = {"auto": 0, "valu": 1, "mfma": 2}
+PATHS = {"auto": 0, "valu": 1, "mfma": 2, "lut": 3}
 DTYPES = {"f16": F16, "bf16": BF16, "f32": F32}
 
 
@@ -142,11 +142,11 @@ def cache_bytes(cfg: Config, n_ctx: int = 0, n_layers: int = 1, what: int = BYTE
 
 
 def decode_path(cfg: Config) -> str:
-    """"valu" or "mfma": the decode kernel the library runs for ``cfg``."""
+    """"valu", "mfma" or "lut": the decode kernel the library runs for ``cfg``."""
     r = lib().kvq_decode_path(ctypes.byref(cfg))
     if r < 0:
         _check(r)
-    return {PATHS["valu"]: "valu", PATHS["mfma"]: "mfma"}[r]
+    return {PATHS["valu"]: "valu", PATHS["mfma"]: "mfma", PATHS["lut"]: "lut"}[r]
 
 
 def cache_layout(cfg: Config) -> LayoutInfo:

@@ -179,3 +179,20 @@ def test_decode_events_hook():
     assert L.kvq_set_decode_events(FAKE, None) == kvq.ERR_INVALID_ARGUMENT
     assert L.kvq_set_decode_events(None, FAKE) == kvq.ERR_INVALID_ARGUMENT
     assert L.kvq_set_decode_events(None, None) == kvq.OK
+
+
+def test_decode_path_selection():
+    from synth import make_workload
+    w4 = make_workload(4, n_kv_heads=4, ctx=64)
+    assert kvq.decode_path(kvq.config_from_workload(w4)) == "lut"
+    assert kvq.decode_path(kvq.config_from_workload(w4, decode_path="valu")) == "valu"
+    w4g = make_workload(4, n_kv_heads=2, gqa=2, ctx=64)       # codebook with a GQA group
+    assert kvq.decode_path(kvq.config_from_workload(w4g)) == "valu"
+    w5 = make_workload(5, batch=1, n_kv_heads=2, ctx=256)
+    assert kvq.decode_path(kvq.config_from_workload(w5)) == "mfma"
+    for cfg in (kvq.config_from_workload(w5, decode_path="lut"),
+                kvq.config_from_workload(w4g, decode_path="lut"),
+                kvq.config_from_workload(w4, decode_path="mfma")):
+        with pytest.raises(kvq.KvqError) as ei:
+            kvq.decode_path(cfg)
+        assert ei.value.status == kvq.ERR_UNSUPPORTED

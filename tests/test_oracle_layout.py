@@ -84,6 +84,30 @@ def test_v_tile_unpacks_back(bits):
                     assert got[u] == codes[32 * tix + t, c]
 
 
+def test_v_pair_tile_is_a_bijection_and_examples():
+    pos = sorted(layout.v_pair_position(byte, half) for byte in range(2048) for half in range(2))
+    assert pos == [(t, c) for t in range(32) for c in range(128)]
+    for ex in GOLD["v_pair_tile_4bit"]:
+        codes = np.zeros((32, 128), dtype=np.int64)
+        codes[ex["token_in_tile"], ex["channel"]] = ex["code"]
+        tile = layout.pack_v_pair_tiles(codes)[0]
+        assert tile.shape == (2048,)
+        assert np.nonzero(tile)[0].tolist() == [ex["byte_index"]], ex["why"]
+        assert tile[ex["byte_index"]] == ex["byte"], ex["why"]
+
+
+def test_v_pair_tile_unpacks_back():
+    rng = np.random.default_rng(44)
+    codes = rng.integers(0, 16, size=(64, 128))
+    tiles = layout.pack_v_pair_tiles(codes)
+    assert tiles.shape == (2, 2048)
+    for tix in range(2):
+        for byte in range(2048):
+            for half in range(2):
+                t, c = layout.v_pair_position(byte, half)
+                assert (int(tiles[tix, byte]) >> (4 * half)) & 15 == codes[32 * tix + t, c]
+
+
 def test_bits_round_trip():
     x = np.array([1.5, -2.25, 0.0, 65504.0], dtype=np.float32)
     assert np.array_equal(layout.from_bits(layout.to_bits(x, "f16"), "f16"), x)

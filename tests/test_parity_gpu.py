@@ -76,6 +76,47 @@ def test_both_decode_kernels_agree_with_oracle(name, cfg_id, over, chunks):
     assert ma <= MAX_ABS and rel <= REL_L2, ("valu", ma, rel)
 
 
+# lookup-table kernel (codebook keys and values, one query head per KV head):
+# (name, workload overrides of config 4, append chunks, decode_splits)
+LUT_CASES = [
+    ("lut_nuq_4heads", dict(n_kv_heads=4, ctx=700), [700], 0),
+    ("lut_nuq_32heads_chunks", dict(ctx=300), [100, 1, 199], 0),
+    # one range of 65 chunks: the rotation table is re-anchored at chunks 32
+    # and 64, and the last chunk holds a single token
+    ("lut_one_range_resync", dict(n_kv_heads=4, ctx=4097), [4097], 1),
+    # 6 KV heads: the second group of 4 has two empty waves
+    ("lut_no_outliers_no_rope", dict(n_kv_heads=6, ctx=333, rope=False,
+                                     k=dict(outlier_frac=0.0), v=dict(outlier_frac=0.0)), [333], 0),
+    ("lut_key_outliers_only", dict(n_kv_heads=4, ctx=200, v=dict(outlier_frac=0.0)), [200], 0),
+    ("lut_value_outliers_rope", dict(n_kv_heads=4, ctx=260, k=dict(outlier_frac=0.0)), [260], 0),
+    ("lut_bf16_batch2", dict(batch=2, n_kv_heads=4, ctx=500, kv_dtype="bf16"), [500], 3),
+]
+
+
+@pytest.mark.parametrize("name,over,chunks,splits", LUT_CASES, ids=[c[0] for c in LUT_CASES])
+def test_lookup_table_kernel(name, over, chunks, splits):
+    w, inputs, cache, exp, kdeq, vdeq = _run(name, 4, over, chunks, decode_path="lut",
+                                             decode_splits=splits)
+    bad = compare_regions(cache, exp)
+    assert not bad, "\n".join(bad)
+    q = inputs["q"]
+    out = cache.decode(q.cuda()).cpu().numpy()
+    ref = oracle_attention(w, q, kdeq, vdeq, w.ctx)
+    ma, rel = attention_errors(out, ref)
+    print(f"[parity] {name}: max_abs={ma:.3e} rel_l2={rel:.3e}", flush=True)
+    assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)
+
+
+def test_codebook_on_the_general_kernel():
+    w, inputs, cache, exp, kdeq, vdeq = _run("nuq_valu", 4, dict(n_kv_heads=4, ctx=700), [700],
+                                             decode_path="valu")
+    q = inputs["q"]
+    out = cache.decode(q.cuda()).cpu().numpy()
+    ref = oracle_attention(w, q, kdeq, vdeq, w.ctx)
+    ma, rel = attention_errors(out, ref)
+    assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 7])
 def test_split_count_invariance(splits):
     w, inputs, cache, exp, kdeq, vdeq = _run(f"splits{splits}", 5,

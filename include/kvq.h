@@ -73,7 +73,8 @@ typedef int32_t kvq_status;
  * CODEBOOK: 4-bit index of the nearest of 16 fp16 centroids of that
  *   (kv head, channel), ties to the lower index; optionally the
  *   ceil(outlier_frac * n_kv_heads * head_dim) entries of largest |x| of each
- *   token are kept exactly in fp16 (CSR) and replace the dense value
+ *   token are kept in fp16 (CSR; n_kv_heads * head_dim <= 4096) and replace
+ *   the dense value
  *   [KVQuant page 2.2, 3.3].
  * All arithmetic of the encoders is IEEE float32 with round-half-even;
  * scales and zeros are rounded to fp16 before codes are computed; a group
@@ -162,7 +163,8 @@ typedef struct kvq_tensor_regions {
   kvq_region params;   /* fp16 scale/zero pairs (q8_0: scales)              */
   kvq_region tail;     /* per-channel keys: fp16/bf16 [B, Hkv, G, d]        */
   kvq_region row_ptr;  /* outliers: int32 [B*Tcap + 1]                      */
-  kvq_region col;      /* outliers: uint16 column h*d + c                   */
+  kvq_region col;      /* outliers: uint16, bits 0-11 column h*d + c, bits
+                          12-15 the dense codebook index at that position  */
   kvq_region val;      /* outliers: fp16 value                              */
 } kvq_tensor_regions;
 

@@ -178,7 +178,9 @@ def expected_regions(fmt: Dict, enc: Dict[str, np.ndarray], *, batch: int, n_kv_
       (uint16), zero beyond it;
     * ``row_ptr`` int32 [B * Tcap + 1], ``col`` uint16 and ``val`` fp16
       [B * Tcap * k]: CSR over rows r = b * Tcap + t, with
-      row_ptr[b * Tcap + t] = k * (b * Tcap + t) for t = 0..n_ctx.
+      row_ptr[b * Tcap + t] = k * (b * Tcap + t) for t = 0..n_ctx; a column
+      entry holds h * d + c in bits 0-11 and the dense codebook index of that
+      position in bits 12-15.
     """
     B, H = batch, n_kv_heads
     Tcap = capacity(max_ctx)
@@ -227,10 +229,16 @@ def expected_regions(fmt: Dict, enc: Dict[str, np.ndarray], *, batch: int, n_kv_
         row_ptr = np.zeros(B * Tcap + 1, dtype=np.int64)
         col = np.zeros(B * Tcap * k, dtype=np.uint16)
         val = np.zeros(B * Tcap * k, dtype=np.float16)
+        # bits 12-15 of a column entry repeat the dense index it replaces
+        cols = np.asarray(enc["cols"]).astype(np.int64)            # [B, n_ctx, k]
+        dense = np.asarray(enc["codes"]).astype(np.int64)          # [B, H, n_ctx, d]
+        bb = np.arange(B)[:, None, None]
+        tt = np.arange(cols.shape[1])[None, :, None]
+        packed_cols = cols | (dense[bb, cols // D, tt, cols % D] << 12)
         for b in range(B):
             r0 = b * Tcap
             row_ptr[r0:r0 + n_ctx + 1] = k * np.arange(r0, r0 + n_ctx + 1)
-            col[k * r0:k * (r0 + n_ctx)] = enc["cols"][b].reshape(-1)
+            col[k * r0:k * (r0 + n_ctx)] = packed_cols[b].reshape(-1)
             val[k * r0:k * (r0 + n_ctx)] = enc["vals"][b].reshape(-1).astype(np.float16)
         out["row_ptr"] = row_ptr.astype(np.int32)
         out["col"] = col

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void dec_generic_kernel(DecodeArgs a) {
           const int64_t r = (int64_t)b * a.sh.Tcap + t;
           const int e0 = a.k.row_ptr[r], e1 = a.k.row_ptr[r + 1];
           for (int e = e0; e < e1; ++e) {
-            const int col = a.k.col[e] - h * kD;
+            const int col = (a.k.col[e] & 0xfff) - h * kD;
             if (col < 0 || col >= kD) continue;
             const float delta = h2f(a.k.val[e]) - deq_k(a, bh, h, t, col, n_full);
             const int i = col & (kD / 2 - 1);
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void dec_generic_kernel(DecodeArgs a) {
           const int64_t r = (int64_t)b * a.sh.Tcap + t2;
           const int e0 = a.v.row_ptr[r], e1 = a.v.row_ptr[r + 1];
           for (int e = e0; e < e1; ++e) {
-            const int col = a.v.col[e] - h * kD;
+            const int col = (a.v.col[e] & 0xfff) - h * kD;
             if (col < 0 || col >= kD || (col & 63) != lane) continue;
             const float delta = h2f(a.v.val[e]) - deq_v(a, bh, h, t2, col);
 #pragma unroll

@@ -179,46 +179,69 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
   };
   if (head_ok && n_chunks > 0) load_chunk(t_begin, kc, vc);
 
+  // Outlier entries of a chunk: the CSR rows of its tokens are contiguous
+  // (k entries per token), read as 16-byte vectors of 8 entries.  Thread j
+  // takes vectors j and j + 256; a vector may run up to 7 entries past the
+  // chunk's rows (still inside the allocation: every outlier array is
+  // followed by another region), and those entries are skipped.
+  constexpr int kVec = 2;                        // vectors per thread and tensor
+  struct OutVec { u32x4 col, val; };
+  auto load_out = [&](const DevTensor& T, int64_t row0, int nt, OutVec* o) {
+    const int64_t e0 = row0 * T.k_out;
+    const int nv = (nt * T.k_out + 7) / 8;
+    const u32x4* cv = reinterpret_cast<const u32x4*>(T.col + e0);
+    const u32x4* vv = reinterpret_cast<const u32x4*>(T.val + e0);
+#pragma unroll
+    for (int u = 0; u < kVec; ++u) {
+      const int vi = tid + 256 * u;
+      if (vi < nv) {
+        o[u].col = cv[vi];
+        o[u].val = vv[vi];
+      } else {
+        o[u].col = u32x4{0u, 0u, 0u, 0u};
+        o[u].val = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  // calls f(ww, tau, c, dense index, value) for the entries of this
+  // workgroup's heads
+  auto for_entries = [&](const DevTensor& T, int nt, const OutVec* o, auto&& f) {
+    const int ko = T.k_out;
+    const int n_ent = nt * ko;
+    const float inv_k = 1.0f / (float)ko;
+#pragma unroll
+    for (int u = 0; u < kVec; ++u) {
+      const uint32_t cw[4] = {o[u].col.x, o[u].col.y, o[u].col.z, o[u].col.w};
+      const uint32_t vw[4] = {o[u].val.x, o[u].val.y, o[u].val.z, o[u].val.w};
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int e = 8 * (tid + 256 * u) + x;     // entry index within the chunk
+        const uint32_t col = (cw[x >> 1] >> (16 * (x & 1))) & 0xffffu;
+        const int hh = (int)((col & 0xfffu) >> 7), ww = hh - hg * kHeads;
+        if (e < n_ent && ww >= 0 && ww < kHeads && hh < Hkv) {
+          // token of entry e: floor(e / k), exact in float for e < 2^16
+          const int tau = (int)(((float)e + 0.5f) * inv_k);
+          const float val = h2f((uint16_t)((vw[x >> 1] >> (16 * (x & 1))) & 0xffffu));
+          f(ww, tau, (int)(col & (kD - 1)), col >> 12, val);
+        }
+      }
+    }
+  };
+
   for (int ci = 0; ci < n_chunks; ++ci) {
     const int t0 = t_begin + ci * kChunk;
     const int nt = min(kChunk, t_end - t0);      // tokens of this chunk
     const int64_t row0 = (int64_t)b * Tcap + t0; // CSR row of token t0
 
-    // ---- key outliers: score corrections ---------------------------------------
-    if constexpr (KOUT) {
-      const int ko = K.k_out;
-      const int tau = tid & 63;
-      if (tau < nt) {
-        for (int jj = tid >> 6; jj < ko; jj += 4) {
-          const int64_t e = (row0 + tau) * ko + jj;
-          const int col = K.col[e];
-          const int hh = col >> 7, ww = hh - hg * kHeads;
-          if (ww < 0 || ww >= kHeads || hh >= Hkv) continue;
-          const int c = col & (kD - 1);
-          const uint8_t* row = K.codes + (((int64_t)b * Hkv + hh) * Tcap + t0 + tau) * 64;
-          const uint32_t code = k_row_code(row, 4, c);
-          const float delta = h2f(K.val[e]) - h2f(S.kt[ww][c][code]);
-          float coef;
-          if constexpr (ROPE) {
-            const int i = c & (kPairs - 1);
-            const float2 cs = S.e[i][tau];
-            const float x = S.qs[ww][i], y = S.qs[ww][i + kPairs];
-            coef = c < kPairs ? x * cs.x + y * cs.y : y * cs.x - x * cs.y;
-          } else {
-            coef = S.qs[ww][c];
-          }
-          atomicAdd(&S.scorr[ww][tau], delta * coef);
-        }
-      }
-      __syncthreads();
-    }
-
+    OutVec ko_v[kVec], vo_v[kVec];
+    if constexpr (KOUT) load_out(K, row0, nt, ko_v);
+    if constexpr (VOUT) load_out(V, row0, nt, vo_v);
     u32x4 kn[4], vn[4];
     if (head_ok && ci + 1 < n_chunks) load_chunk(t0 + kChunk, kn, vn);
 
-    float alpha = 1.f;
+    // ---- keys: lane = token (dense part) ------------------------------------------
+    float s = 0.f;
     if (head_ok) {
-      // ---- keys: lane = token ------------------------------------------------------
       const uint32_t kw[16] = {kc[0].x, kc[0].y, kc[0].z, kc[0].w, kc[1].x, kc[1].y, kc[1].z, kc[1].w,
                                kc[2].x, kc[2].y, kc[2].z, kc[2].w, kc[3].x, kc[3].y, kc[3].z, kc[3].w};
       // centroid of channel c with index field at bit 4*e of dword w
@@ -226,7 +249,6 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
         const uint32_t code = (wd >> (4 * e)) & 15u;
         return (float)__builtin_bit_cast(_Float16, S.kt[wave][c][code]);
       };
-      float s = 0.f;
       // dword 4q + m of the row holds channels 32m + 8q + e (e = 0..7)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -247,12 +269,50 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
               s = __builtin_fmaf(bv, y, s);
             }
           }
-      if constexpr (KOUT) s += S.scorr[wave][lane];
-      if (lane >= nt) s = -INFINITY;
+    }
 
+    // ---- key outliers: (value - centroid) * coefficient into the scores ----------------
+    if constexpr (KOUT) {
+      for_entries(K, nt, ko_v, [&](int ww, int tau, int c, uint32_t code, float val) {
+        const float delta = val - h2f(S.kt[ww][c][code]);
+        float coef;
+        if constexpr (ROPE) {
+          const int i = c & (kPairs - 1);
+          const float2 cs = S.e[i][tau];
+          const float x = S.qs[ww][i], y = S.qs[ww][i + kPairs];
+          coef = c < kPairs ? x * cs.x + y * cs.y : y * cs.x - x * cs.y;
+        } else {
+          coef = S.qs[ww][c];
+        }
+        atomicAdd(&S.scorr[ww][tau], delta * coef);
+      });
+    }
+    if constexpr (KOUT || VOUT || ROPE) __syncthreads();   // scores complete; e consumed
+
+    // ---- next chunk's rotation table ---------------------------------------------------
+    if constexpr (ROPE) {
+      if (ci + 1 < n_chunks) {
+        if ((ci + 1) % kResync == 0) {
+          anchor(t0 + kChunk);
+        } else {
+          for (int idx = tid; idx < kPairs * kChunk; idx += 256) {
+            const int i = idx / kChunk, tau = idx % kChunk;
+            const float2 e0 = S.e[i][tau], st = S.estep[i];
+            S.e[i][tau] = make_float2(e0.x * st.x - e0.y * st.y, e0.x * st.y + e0.y * st.x);
+          }
+        }
+      }
+    }
+
+    if (head_ok) {
       // ---- online softmax ----------------------------------------------------------
+      if constexpr (KOUT) {
+        s += S.scorr[wave][lane];
+        S.scorr[wave][lane] = 0.f;
+      }
+      if (lane >= nt) s = -INFINITY;
       const float m_new = fmaxf(m_run, wave_max(s));
-      alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       const float pt = lane < nt ? __builtin_amdgcn_exp2f(s - m_new) : 0.f;
       l_lane = l_lane * alpha + pt;
       m_run = m_new;
@@ -280,46 +340,15 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
       }
     }
 
-    if constexpr (KOUT || VOUT || ROPE) __syncthreads();   // p complete; scorr and e consumed
-
-    // ---- value outliers, next chunk's table ----------------------------------------
+    // ---- value outliers: p * (value - centroid) into LDS channel sums ------------------
     if constexpr (VOUT) {
-      const int ko = V.k_out;
-      const int tau = tid & 63;
-      if (tau < nt) {
-        for (int jj = tid >> 6; jj < ko; jj += 4) {
-          const int64_t e = (row0 + tau) * ko + jj;
-          const int col = V.col[e];
-          const int hh = col >> 7, ww = hh - hg * kHeads;
-          if (ww < 0 || ww >= kHeads || hh >= Hkv) continue;
-          const int c = col & (kD - 1);
-          const uint8_t* tile = V.codes + (((int64_t)b * Hkv + hh) * Tcap + (t0 & ~(kTile - 1)) +
-                                           (tau & ~(kTile - 1))) * 64;
-          const uint32_t code = v_pair_code(tile, tau & (kTile - 1), c);
-          const uint32_t cc = S.vt[ww][code][c & (kPairs - 1)];
-          const float dense = c < kPairs ? half_lo(cc) : half_hi(cc);
-          atomicAdd(&S.vcorr[ww][c], S.p[ww][tau] * (h2f(V.val[e]) - dense));
-        }
-      }
-    }
-    if constexpr (KOUT) {
-      for (int i = tid; i < kHeads * kChunk; i += 256) (&S.scorr[0][0])[i] = 0.f;
-    }
-    if constexpr (ROPE) {
-      if (ci + 1 < n_chunks) {
-        if ((ci + 1) % kResync == 0) {
-          anchor(t0 + kChunk);
-        } else {
-          for (int idx = tid; idx < kPairs * kChunk; idx += 256) {
-            const int i = idx / kChunk, tau = idx % kChunk;
-            const float2 e0 = S.e[i][tau], st = S.estep[i];
-            S.e[i][tau] = make_float2(e0.x * st.x - e0.y * st.y, e0.x * st.y + e0.y * st.x);
-          }
-        }
-      }
-    }
-    if constexpr (VOUT) {
-      __syncthreads();                               // value outlier sums complete
+      __syncthreads();                               // p of every head complete
+      for_entries(V, nt, vo_v, [&](int ww, int tau, int c, uint32_t code, float val) {
+        const uint32_t cc = S.vt[ww][code][c & (kPairs - 1)];
+        const float dense = c < kPairs ? half_lo(cc) : half_hi(cc);
+        atomicAdd(&S.vcorr[ww][c], S.p[ww][tau] * (val - dense));
+      });
+      __syncthreads();                               // sums complete
       if (head_ok) {
         acc0 += S.vcorr[wave][lane];
         acc1 += S.vcorr[wave][lane + 64];
@@ -327,7 +356,9 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
         S.vcorr[wave][lane + 64] = 0.f;
       }
     }
-    if constexpr (KOUT || ROPE) __syncthreads();     // zeroed scorr, next table visible
+    // next table complete; score corrections read and cleared before the
+    // next chunk adds to them (with value outliers, their barriers order this)
+    if constexpr ((ROPE || KOUT) && !VOUT) __syncthreads();
 
     if (head_ok && ci + 1 < n_chunks) {
 #pragma unroll
@@ -361,10 +392,13 @@ void launch_r(const DecodeArgs& a, unsigned grid, hipStream_t s) {
 
 }  // namespace
 
-bool lut_config_supported(const kvq_config& c) {
+bool lut_config_supported(const kvq_config& c, int k_out_k, int k_out_v) {
+  // a chunk's outlier rows are read as 2 vectors of 8 entries per thread:
+  // at most 64 outliers per token
   return c.k.quantizer == KVQ_QUANT_CODEBOOK && c.v.quantizer == KVQ_QUANT_CODEBOOK &&
          c.k.bits == 4 && c.v.bits == 4 && c.n_q_heads == c.n_kv_heads &&
-         c.k.layout == KVQ_LAYOUT_PER_TOKEN && c.v.layout == KVQ_LAYOUT_PER_TOKEN;
+         c.k.layout == KVQ_LAYOUT_PER_TOKEN && c.v.layout == KVQ_LAYOUT_PER_TOKEN &&
+         k_out_k <= 64 && k_out_v <= 64;
 }
 
 hipError_t launch_decode_lut(const DecodeArgs& a, hipStream_t s) {

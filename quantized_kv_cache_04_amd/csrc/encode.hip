@@ -29,23 +29,23 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t idx, int is
 // the G/2 lanes of the group.  Writes the group's parameters (first lane of
 // each group) at ``prm_row`` (the row's parameter record array) and returns
 // the two codes (two's complement byte for q8_0).
+// Codebook index of x: the number of midpoints between consecutive centroids
+// that lie below x (nearest centroid, ties to the lower index).
+__device__ __forceinline__ uint32_t cb_code(const uint16_t* cb, float x) {
+  uint32_t n = 0;
+#pragma unroll
+  for (int i = 0; i < 15; ++i) n += x > (h2f(cb[i]) + h2f(cb[i + 1])) * 0.5f;
+  return n;
+}
+
 __device__ __forceinline__ void encode_pair(const DevTensor& t, int h, int lane, float x0,
                                             float x1, void* prm_row, uint32_t& q0,
                                             uint32_t& q1) {
   const int c0 = 2 * lane, c1 = c0 + 1;
   if (t.quant == KVQ_QUANT_CODEBOOK) {
     const uint16_t* cb0 = t.codebook + ((int64_t)h * kD + c0) * 16;
-    const uint16_t* cb1 = cb0 + 16;
-    uint32_t a = 0, b = 0;
-#pragma unroll
-    for (int i = 0; i < 15; ++i) {
-      const float m0 = (h2f(cb0[i]) + h2f(cb0[i + 1])) * 0.5f;
-      const float m1 = (h2f(cb1[i]) + h2f(cb1[i + 1])) * 0.5f;
-      a += x0 > m0;
-      b += x1 > m1;
-    }
-    q0 = a;
-    q1 = b;
+    q0 = cb_code(cb0, x0);
+    q1 = cb_code(cb0 + 16, x1);
     return;
   }
   float lo = fminf(x0, x1), hi = fmaxf(x0, x1), am = fmaxf(fabsf(x0), fabsf(x1));
@@ -338,7 +338,9 @@ __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTenso
   const int64_t r = (int64_t)b * sh.Tcap + tpos;
   for (int i = i0; i < i1; ++i) {
     if (keys[i] >= prefix) {
-      t.col[r * k + pos] = (uint16_t)i;
+      // column h*d + c in bits 0-11, the replaced dense index in bits 12-15
+      const uint32_t dense = cb_code(t.codebook + (int64_t)i * 16, elem2f(xr[i], sh.kv_bf16));
+      t.col[r * k + pos] = (uint16_t)(i | (dense << 12));
       // outliers are kept in fp16: a bf16 input is rounded to nearest-even
       t.val[r * k + pos] = sh.kv_bf16 ? f2h_rn(bf2f(xr[i])) : xr[i];
       ++pos;

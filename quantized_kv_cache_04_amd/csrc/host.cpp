@@ -68,8 +68,8 @@ kvq_status check_format(const kvq_tensor_format& f, const kvq_config& c, bool is
                     "and the per-token layout", name);
       if (!(f.outlier_frac >= 0.0f && f.outlier_frac <= 0.25f))
         return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: outlier_frac must be in [0, 0.25]", name);
-      if (f.outlier_frac > 0.0f && (int64_t)c.n_kv_heads * d > 8192)
-        return fail(KVQ_ERR_UNSUPPORTED, "%s: outlier selection needs n_kv_heads * head_dim <= 8192",
+      if (f.outlier_frac > 0.0f && (int64_t)c.n_kv_heads * d > 4096)
+        return fail(KVQ_ERR_UNSUPPORTED, "%s: outliers need n_kv_heads * head_dim <= 4096",
                     name);
       return KVQ_OK;
     default:
@@ -241,13 +241,14 @@ int32_t kvq_decode_path(const kvq_config* cfg) {
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
   const bool ok = mfma_config_supported(*cfg);
-  const bool lut = lut_config_supported(*cfg);
+  const Layout L = make_layout(*cfg);
+  const bool lut = lut_config_supported(*cfg, L.k.k_out, L.v.k_out);
   if (cfg->decode_path == KVQ_PATH_MFMA && !ok)
     return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core decode kernel needs uniform or raw formats "
                 "for keys and values, no RoPE and at most 8 query heads per KV head");
   if (cfg->decode_path == KVQ_PATH_LUT && !lut)
     return fail(KVQ_ERR_UNSUPPORTED, "the lookup-table decode kernel needs 4-bit codebook keys "
-                "and values and one query head per KV head");
+                "and values, one query head per KV head and at most 64 outliers per token");
   if (cfg->decode_path == KVQ_PATH_VALU) return KVQ_PATH_VALU;
   if (cfg->decode_path == KVQ_PATH_LUT || (cfg->decode_path == KVQ_PATH_AUTO && lut))
     return KVQ_PATH_LUT;

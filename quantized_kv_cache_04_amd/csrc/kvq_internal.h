@@ -90,8 +90,9 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
 bool mfma_config_supported(const kvq_config& c);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // Whether the lookup-table kernel handles this configuration (4-bit codebook
-// keys and values, one query head per KV head).
-bool lut_config_supported(const kvq_config& c);
+// keys and values, one query head per KV head, at most 64 outliers per token;
+// k_out_*: outliers per token of keys and values).
+bool lut_config_supported(const kvq_config& c, int k_out_k, int k_out_v);
 // a.splits = token ranges per sequence, a.blocks_per_split even (64-token chunks)
 hipError_t launch_decode_lut(const DecodeArgs& a, hipStream_t stream);
 

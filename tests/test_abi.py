@@ -104,7 +104,7 @@ def _status(fn):
     (dict(k={"quantizer": "codebook", "bits": 4, "outlier_frac": 0.5}), kvq.ERR_INVALID_ARGUMENT,
      "outlier_frac"),
     (dict(n_q_heads=128, n_kv_heads=128, k={"quantizer": "codebook", "bits": 4, "outlier_frac": 0.01}),
-     kvq.ERR_UNSUPPORTED, "8192"),
+     kvq.ERR_UNSUPPORTED, "4096"),
     (dict(rope=True, rope_base=0.5), kvq.ERR_INVALID_ARGUMENT, "rope_base"),
 ])
 def test_config_errors(mut, code, needle):
@@ -188,6 +188,9 @@ def test_decode_path_selection():
     assert kvq.decode_path(kvq.config_from_workload(w4, decode_path="valu")) == "valu"
     w4g = make_workload(4, n_kv_heads=2, gqa=2, ctx=64)       # codebook with a GQA group
     assert kvq.decode_path(kvq.config_from_workload(w4g)) == "valu"
+    # more than 64 outliers per token: the general kernel
+    w4k = make_workload(4, n_kv_heads=4, ctx=64, k={"outlier_frac": 0.25})
+    assert kvq.decode_path(kvq.config_from_workload(w4k)) == "valu"
     w5 = make_workload(5, batch=1, n_kv_heads=2, ctx=256)
     assert kvq.decode_path(kvq.config_from_workload(w5)) == "mfma"
     for cfg in (kvq.config_from_workload(w5, decode_path="lut"),

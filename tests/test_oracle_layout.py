@@ -113,3 +113,19 @@ def test_bits_round_trip():
     assert np.array_equal(layout.from_bits(layout.to_bits(x, "f16"), "f16"), x)
     y = np.array([1.5, -3.0, 2.0 ** 100, -1.0 / 1024], dtype=np.float32)
     assert np.array_equal(layout.from_bits(layout.to_bits(y, "bf16"), "bf16"), y)
+
+
+def test_outlier_column_carries_the_dense_index():
+    # one token, one head: the outlier at channel 5 replaced dense index 9,
+    # so its column entry is 5 | 9 << 12 = 36869 (hand-derived)
+    codes = np.zeros((1, 1, 1, 128), dtype=np.int64)
+    codes[0, 0, 0, 5] = 9
+    codes[0, 0, 0, 77] = 3
+    enc = {"codes": codes, "cols": np.array([[[5, 77]]]),
+           "vals": np.array([[[7.5, -6.0]]], dtype=np.float32)}
+    fmt = {"quantizer": "codebook", "bits": 4, "outlier_frac": 2 / 128}
+    reg = layout.expected_regions(fmt, enc, batch=1, n_kv_heads=1, n_ctx=1, max_ctx=32,
+                                  kv_dtype="f16", is_key=True)
+    assert reg["col"][:2].tolist() == [36869, 77 | 3 << 12]
+    assert reg["val"][:2].tolist() == [7.5, -6.0]
+    assert reg["row_ptr"][:3].tolist() == [0, 2, 0]

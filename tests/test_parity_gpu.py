@@ -81,6 +81,8 @@ def test_both_decode_kernels_agree_with_oracle(name, cfg_id, over, chunks):
 LUT_CASES = [
     ("lut_nuq_4heads", dict(n_kv_heads=4, ctx=700), [700], 0),
     ("lut_nuq_32heads_chunks", dict(ctx=300), [100, 1, 199], 0),
+    # 41 outliers per token over 24 chunks (rows straddle the 8-entry vectors)
+    ("lut_32heads_multichunk", dict(ctx=1500), [1500], 0),
     # one range of 65 chunks: the rotation table is re-anchored at chunks 32
     # and 64, and the last chunk holds a single token
     ("lut_one_range_resync", dict(n_kv_heads=4, ctx=4097), [4097], 1),

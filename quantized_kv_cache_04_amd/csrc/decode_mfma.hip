@@ -217,6 +217,23 @@ __device__ __forceinline__ half8 pair_operand(const float x[8], float sc, float 
   return as_h8(o[0], o[1], o[2], o[3]);
 }
 
+// Both fp16 parts of the pair-order operand of 8 values (see pair_operand):
+// hi = x rounded toward zero, lo = (x - hi) rounded toward zero.
+template <int BITS>
+__device__ __forceinline__ void pair_operand_hilo(const float x[8], float sc, u32x4& hi, u32x4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float f = sc * pair_factor<BITS>(r);
+    const float a = x[r] * f, b = x[r + 4] * f;
+    const auto hv = __builtin_amdgcn_cvt_pkrtz(a, b);
+    h[r] = __builtin_bit_cast(uint32_t, hv);
+    l[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a - (float)hv[0], b - (float)hv[1]));
+  }
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
 // Load ``N`` dwords from a 4-byte aligned address.
 template <int N>
 __device__ __forceinline__ void load_dw(const uint8_t* p, uint32_t* out) {
@@ -254,6 +271,11 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   __shared__ float wo[4][8][kD];
   __shared__ float wb[4][8][NGV];   // per wave, head, value group: additive term
   __shared__ float q_lds[8][kD + 4];   // the group's queries as fp32 (zero rows for j >= g)
+  // per-channel keys: the B operand of each wave's current key group,
+  // [wave][head][high/low part][8-channel block] in MFMA pair order, and the
+  // zero-point sums sum_c q_c z_c of its heads
+  __shared__ u32x4 kb_tab[KCH ? 4 : 1][8][2][16];
+  __shared__ float zb_tab[4][8];
   extern __shared__ u32x4 kp_lds[];  // per-channel keys: [4 waves][a.kp_groups][32]
 
   const int split = blockIdx.x, bh = blockIdx.y;
@@ -440,24 +462,36 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   };
 
   // per-channel keys: B operand and zero-point term of key group ``grp``
+  // The g * 16 blocks of 8 channels of the group's heads are shared out over
+  // the lanes (lane L takes blocks L and L + 64): each block's q * scale
+  // products are split into fp16 high/low parts in pair order and written
+  // to the wave's table, from which every lane reads its own operand.
   auto key_group = [&](int grp) {
     if (grp >= kp_hi) stage_kp(grp);   // wave-uniform
     const u32x4* prm4 = kp_w + (grp - kp_lo) * 32;
-    float mx = 0.f, zb = 0.f;
-    float qs[4][8];
+    const int nblocks = g * 16;
+    float xs[2][8];
+    float zb[2] = {0.f, 0.f};
+    float mx = 0.f;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      float qv[8];
-      load_q(m, qv);
-      const u32x4 p0 = prm4[8 * m + 2 * q4];
-      const u32x4 p1 = prm4[8 * m + 2 * q4 + 1];
-      const uint32_t pz[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    for (int u = 0; u < 2; ++u) {
+      const int bi = lane + 64 * u;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const half2v sz = __builtin_bit_cast(half2v, pz[e]);   // (scale, zero)
-        qs[m][e] = __builtin_fmaf(qv[e], (float)sz[0], 0.f);
-        mx = fmaxf(mx, fabsf(qs[m][e]));
-        zb = __builtin_fmaf(qv[e], (float)sz[1], zb);
+      for (int e = 0; e < 8; ++e) xs[u][e] = 0.f;
+      if (bi < nblocks) {
+        const int hd = bi >> 4, cb = bi & 15;
+        const f32x4 qa = *reinterpret_cast<const f32x4*>(&q_lds[hd][8 * cb]);
+        const f32x4 qb = *reinterpret_cast<const f32x4*>(&q_lds[hd][8 * cb + 4]);
+        const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        const u32x4 p0 = prm4[2 * cb], p1 = prm4[2 * cb + 1];
+        const uint32_t pz[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const half2v sz = __builtin_bit_cast(half2v, pz[e]);   // (scale, zero)
+          xs[u][e] = __builtin_fmaf(qv[e], (float)sz[0], 0.f);
+          mx = fmaxf(mx, fabsf(xs[u][e]));
+          zb[u] = __builtin_fmaf(qv[e], (float)sz[1], zb[u]);
+        }
       }
     }
     mx = wave_max(mx);
@@ -465,10 +499,32 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     if (E > 100) E = 100;
     kscale = pow2i(24 - E > 126 ? 126 : 24 - E) * sm2;
     const float s2 = pow2i(E);
+    // zero-point sums: the 16 lanes of a row hold the 16 blocks of one head
 #pragma unroll
-    for (int m = 0; m < 4; ++m) bk[m] = pair_operand<KB>(qs[m], s2, lo_mask);
-    zb = rows_sum(zb);
-    kbias = hi_lane ? zb * sm2 : 0.f;
+    for (int u = 0; u < 2; ++u) {
+      float z = zb[u];
+      z += dpp_ror8(z);
+      z += dpp_f<0x124>(z);
+      z += dpp_f<0x122>(z);
+      z += dpp_f<0x121>(z);
+      const int bi = lane + 64 * u;
+      if (bi < nblocks) {
+        const int hd = bi >> 4, cb = bi & 15;
+        if (cb == 0) zb_tab[wave][hd] = z;
+        u32x4 hi, lo;
+        pair_operand_hilo<KB>(xs[u], s2, hi, lo);
+        kb_tab[wave][hd][0][cb] = hi;
+        kb_tab[wave][hd][1][cb] = lo;
+      }
+    }
+    // LDS accesses of one wave complete in order: the reads see the table
+    __builtin_amdgcn_wave_barrier();
+    const int hl = n >> 3;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      bk[m] = head_ok ? __builtin_bit_cast(half8, kb_tab[wave][j][hl][4 * m + q4])
+                      : as_h8(0u, 0u, 0u, 0u);
+    kbias = (hi_lane && head_ok) ? zb_tab[wave][j] * sm2 : 0.f;
     kb2[0] = kbias + tbias[0];
     kb2[1] = kbias + tbias[1];
   };

@@ -123,6 +123,20 @@ def select_outliers(x: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
     return cols, vals
 
 
+def outlier_mask(x: np.ndarray, k: int) -> np.ndarray:
+    """The set select_outliers keeps, as a boolean mask [N, n], found through
+    the k-th largest magnitude of each row instead of a full sort: every
+    entry above it, then the entries equal to it in index order until k are
+    taken (ties to the lower index).  For long contexts."""
+    a = np.abs(np.asarray(x, dtype=F32))
+    n = a.shape[1]
+    kth = np.partition(a, n - k, axis=1)[:, n - k][:, None]
+    above = a > kth
+    need = k - above.sum(axis=1, keepdims=True)
+    ties = a == kth
+    return above | (ties & (np.cumsum(ties, axis=1) <= need))
+
+
 # --------------------------------------------------------------------------
 # Whole-tensor encoding (logical codes; byte layouts live in layout.py)
 # --------------------------------------------------------------------------

@@ -293,3 +293,16 @@ def test_per_channel_groups_and_tail():
     assert np.array_equal(enc["codes"][0, 0, 64:128, 9], c[0])
     assert enc["scale"][0, 0, 1, 9] == s[0] and enc["zero"][0, 0, 1, 9] == z[0]
     assert np.array_equal(enc["deq"][0, 0, 128:, :], x[0, 128:, 0, :].astype(np.float64))
+
+
+def test_outlier_mask_is_the_selected_set():
+    # tie-heavy rows (few distinct magnitudes) and plain normal rows
+    rng = np.random.default_rng(99)
+    ties = rng.integers(-4, 5, size=(300, 512)).astype(np.float32)
+    normal = rng.standard_normal((300, 512)).astype(np.float16).astype(np.float32)
+    for x in (ties, normal):
+        for k in (1, 6, 41):
+            cols, _ = quant.select_outliers(x, k)
+            want = np.zeros(x.shape, dtype=bool)
+            np.put_along_axis(want, cols, True, axis=1)
+            assert np.array_equal(quant.outlier_mask(x, k), want)

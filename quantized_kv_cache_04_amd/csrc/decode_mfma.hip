@@ -44,6 +44,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = kHeadDim;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -119,22 +120,26 @@ __device__ __forceinline__ int ceil_log2(float x) {
   return e < -126 ? -126 : e;
 }
 
+// Two fp32 values rounded to the nearest fp16 (one v_cvt_pk_f16_f32)
+__device__ __forceinline__ half2v cvt_pk_rn(float x0, float x1) {
+  return __builtin_convertvector(f32x2{x0, x1}, half2v);
+}
+
 // Two fp32 values as the fp16 high parts (lo_mask = 0) or low parts
-// (lo_mask = 1) of a high/low pair: hi = x rounded toward zero to fp16,
-// lo = (x - hi) rounded toward zero; hi + lo keeps about 21 bits of x.
+// (lo_mask = 1) of a high/low pair: hi = x rounded to the nearest fp16,
+// lo = (x - hi) rounded to nearest.  Both roundings are unbiased, so the
+// error of hi + lo does not pile up in one direction over long sums, even
+// where lo (or hi) is an fp16 subnormal.
 __device__ __forceinline__ uint32_t hilo2(float x0, float x1, float lo_mask) {
-  const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+  const half2v h = cvt_pk_rn(x0, x1);
   const float y0 = x0 - lo_mask * (float)h[0];
   const float y1 = x1 - lo_mask * (float)h[1];
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(y0, y1));
+  return __builtin_bit_cast(uint32_t, cvt_pk_rn(y0, y1));
 }
 
 // hi/lo split of two fp32 values without scaling (see hilo2)
 __device__ __forceinline__ uint32_t hilo_split(float x0, float x1, float lo_mask) {
-  const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
-  const float y0 = x0 - lo_mask * (float)h[0];
-  const float y1 = x1 - lo_mask * (float)h[1];
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(y0, y1));
+  return hilo2(x0, x1, lo_mask);
 }
 
 // ---- code unpacking: block of 8 codes -> 4 dwords of subnormal fp16 pairs ---
@@ -146,12 +151,13 @@ struct Unpack;
 template <>
 struct Unpack<4> {
   static constexpr float f[4] = {1.0f, 1.0f / 16.0f, 1.0f, 1.0f / 16.0f};
+  template <bool FLIP>
   __device__ static __forceinline__ void run(uint32_t w, uint32_t out[4]) {
     const uint32_t w8 = w >> 8;
     out[0] = w & 0x000f000fu;
-    out[1] = w & 0x00f000f0u;
+    out[1] = (FLIP ? ~w : w) & 0x00f000f0u;     // one v_bitop3 either way
     out[2] = w8 & 0x000f000fu;
-    out[3] = w8 & 0x00f000f0u;
+    out[3] = (FLIP ? ~w8 : w8) & 0x00f000f0u;
   }
 };
 
@@ -159,7 +165,12 @@ template <>
 struct Unpack<3> {
   static constexpr float f[4] = {1.0f, 1.0f, 1.0f, 1.0f};
   // dlo: dword with the low two bits of block m (D[m / 2]); d2: high bits
+  // FLIP complements the odd pairs: their low bits sit at bit pairs 2p with
+  // p odd (mask 0xcccc per half), their high bits at the odd bits P of d2
+  // (mask 0xaaaa), so two XORs of the source dwords do it
+  template <bool FLIP>
   __device__ static __forceinline__ void run(uint32_t dlo, uint32_t d2, int m, uint32_t out[4]) {
+    if (FLIP) { dlo ^= 0xccccccccu; d2 ^= 0xaaaaaaaau; }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int p = 4 * (m & 1) + r, P = 4 * m + r;
@@ -181,17 +192,21 @@ struct Unpack<8> {
   }
 };
 
-// codes of block m of a segment of BITS-bit codes held in ``seg`` dwords
-template <int BITS, bool SIGNED>
+// codes of block m of a segment of BITS-bit codes held in ``seg`` dwords.
+// FLIP: the odd pairs hold the complemented codes (2^BITS - 1) - c (signed
+// 8-bit: 127 - q, the complement of the offset code q + 128).
+template <int BITS, bool SIGNED, bool FLIP = false>
 __device__ __forceinline__ half8 seg_block(const uint32_t* seg, int m) {
   uint32_t o[4];
   if constexpr (BITS == 4) {
-    Unpack<4>::run(seg[m], o);
+    Unpack<4>::run<FLIP>(seg[m], o);
   } else if constexpr (BITS == 3) {
-    Unpack<3>::run(seg[m >> 1], seg[2], m, o);
+    Unpack<3>::run<FLIP>(seg[m >> 1], seg[2], m, o);
   } else {
-    uint32_t d0 = seg[2 * m], d1 = seg[2 * m + 1];
-    if (SIGNED) { d0 ^= 0x80808080u; d1 ^= 0x80808080u; }
+    // pair r takes byte r of both dwords: bytes 1 and 3 are the odd pairs
+    constexpr uint32_t kFlipMask = SIGNED ? 0x7f807f80u : 0xff00ff00u;
+    constexpr uint32_t kX = FLIP ? kFlipMask : (SIGNED ? 0x80808080u : 0u);
+    const uint32_t d0 = seg[2 * m] ^ kX, d1 = seg[2 * m + 1] ^ kX;
     Unpack<8>::run(d0, d1, o);
   }
   return as_h8(o[0], o[1], o[2], o[3]);
@@ -218,7 +233,7 @@ __device__ __forceinline__ half8 pair_operand(const float x[8], float sc, float 
 }
 
 // Both fp16 parts of the pair-order operand of 8 values (see pair_operand):
-// hi = x rounded toward zero, lo = (x - hi) rounded toward zero.
+// hi = x rounded to nearest, lo = (x - hi) rounded to nearest.
 template <int BITS>
 __device__ __forceinline__ void pair_operand_hilo(const float x[8], float sc, u32x4& hi, u32x4& lo) {
   uint32_t h[4], l[4];
@@ -226,9 +241,9 @@ __device__ __forceinline__ void pair_operand_hilo(const float x[8], float sc, u3
   for (int r = 0; r < 4; ++r) {
     const float f = sc * pair_factor<BITS>(r);
     const float a = x[r] * f, b = x[r + 4] * f;
-    const auto hv = __builtin_amdgcn_cvt_pkrtz(a, b);
+    const half2v hv = cvt_pk_rn(a, b);
     h[r] = __builtin_bit_cast(uint32_t, hv);
-    l[r] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a - (float)hv[0], b - (float)hv[1]));
+    l[r] = __builtin_bit_cast(uint32_t, cvt_pk_rn(a - (float)hv[0], b - (float)hv[1]));
   }
   hi = u32x4{h[0], h[1], h[2], h[3]};
   lo = u32x4{l[0], l[1], l[2], l[3]};
@@ -262,6 +277,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     uint32_t kp[2][KPD];    // key scale(/zero) (per-token keys)
   };
   constexpr float kLazy = 8.0f;   // log2 headroom before the running max moves
+  constexpr int kFedLog2 = 15;    // fed P operand entries stay below 2^kFedLog2
   // register pipeline depth: three buffers where the registers allow
   // (per-channel keys, small blocks, single-group values), else two
   constexpr int kBufDwords = 2 * KB + 2 * VB + 2 * VPD + 2 * KPD;
@@ -319,6 +335,8 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
+  // the wave's running output sums (true units, relative to m_run)
+  for (int i = lane; i < 8 * kD; i += 64) (&wo[wave][0][0])[i] = 0.f;
   auto load_q = [&](int m, float x[8]) {
     const f32x4 u = *reinterpret_cast<const f32x4*>(&q_lds[j][32 * m + 8 * q4]);
     const f32x4 v = *reinterpret_cast<const f32x4*>(&q_lds[j][32 * m + 8 * q4 + 4]);
@@ -411,15 +429,23 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   // bias -(m_run - pexp) is folded into the key products of the high
   // columns, so one exp2 of t = s - mref (- kOdd) yields p'.
   constexpr float kOdd = VB == 4 ? 4.0f : 0.0f;
+  // Value codes are unsigned, so without care every P.V product would be
+  // positive, and the matrix cores drop the parts of products that sit far
+  // below the largest product of a dot product: those losses would add up
+  // in one direction over thousands of tokens.  Odd pairs therefore feed
+  // -P against the complemented codes cmax - c (q8_0: 255 - (q + 128)):
+  // their products are p c - cmax p, the signs alternate from token to
+  // token, and the fixed part cmax p goes into the exact fp32 zero term.
+  constexpr float kCmax = VQ8 ? 127.0f : (float)((1 << VB) - 1);
   float m_run = -INFINITY;   // reference maximum of head j (lanes n, n + 8 agree)
   float mref = 0.f;          // bias folded into t (m_run - pexp once m_run is set)
   float thr = -INFINITY;     // rescale when t > thr (= kLazy + m_run - mref)
   float l_run[2] = {0.f, 0.f};   // sum of p' over this lane's even / odd tokens
   float vbias[NGV][2];       // sum p' * zero over even / odd tokens (values)
-  float voff[NGV];           // q8_0: sum of the P operand before its fp16 split
+  float voff[NGV];           // q8_0: offset term of the fp16 P operand parts this lane fed
 #pragma unroll
   for (int gi = 0; gi < NGV; ++gi) { vbias[gi][0] = vbias[gi][1] = 0.f; voff[gi] = 0.f; }
-  // value operand scale: fed P = p * scale * 2^pexp <= 2^12 (p <= 2^kLazy);
+  // value operand scale: fed P = p * scale * 2^pexp <= 2^kFedLog2 (p <= 2^kLazy);
   // pexp changes when a block brings a scale above sbound (the accumulators
   // are then rescaled by the exact power of two)
   int pexp = 0;
@@ -568,6 +594,10 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
         const float f = __shfl(alpha, 4 * (q4 & 1) + r, 64);
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) oacc[nb][r] *= f;
+        if (q4 < 2) {
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) wo[wave][4 * q4 + r][16 * nb + n] *= f;
+        }
       }
       m_run = m_new;
       const float mref_new = m_run - (float)pexp;
@@ -607,7 +637,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     const float smax = VQ8 ? fmaxf((float)smx[0], (float)smx[1]) : (float)smx[0];
     if (__any(smax > sbound)) {
       const float sm = rows_max(smax);         // same tokens in every column
-      int np = 12 - (int)kLazy - ceil_log2(sm);
+      int np = kFedLog2 - (int)kLazy - ceil_log2(sm);
       np = np < -60 ? -60 : (np > 60 ? 60 : np);
       const int e = np - pexp;                 // rescale what was fed so far
       const float f = pow2i(e);
@@ -624,7 +654,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
         voff[gi] *= f;
       }
       pexp = np;
-      sbound = pow2i(12 - (int)kLazy - np);
+      sbound = pow2i(kFedLog2 - (int)kLazy - np);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -657,23 +687,68 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
           if constexpr (VQ8) {
             const int idx = r * NGV + gi;
             const half2v h = __builtin_bit_cast(half2v, vp[mb][idx >> 1]);
-            x[mb] = __builtin_fmaf(pr[mb][r], (float)h[idx & 1], 0.f);
+            const float sc_h = (float)h[idx & 1];
+            x[mb] = __builtin_fmaf(pr[mb][r], (r & 1) ? -sc_h : sc_h, 0.f);
           } else {
             const half2v h = __builtin_bit_cast(half2v, vp[mb][r * NGV + gi]);
-            x[mb] = __builtin_fmaf(pr[mb][r], (float)h[0], 0.f);
-            vbias[gi][r & 1] = __builtin_fmaf(pr[mb][r], (float)h[1], vbias[gi][r & 1]);
+            const float sc_h = (float)h[0];
+            x[mb] = __builtin_fmaf(pr[mb][r], (r & 1) ? -sc_h : sc_h, 0.f);
+            // odd pairs: + cmax p' scale (x holds -p' scale there)
+            const float vb = (r & 1) ? __builtin_fmaf(-kCmax, x[mb], vbias[gi][1]) : vbias[gi][0];
+            vbias[gi][r & 1] = __builtin_fmaf(pr[mb][r], (float)h[1], vb);
           }
         }
         o[r] = hilo_split(x[0], x[1], lo_mask);
-        if constexpr (VQ8) voff[gi] += x[0] + x[1];
+        if constexpr (VQ8) {   // the offset term must cancel what was fed, not x
+          // even pairs: P (q + 128) -> -128 P; odd: -P (127 - q) -> +127 P
+          const half2v f = __builtin_bit_cast(half2v, o[r]);
+          voff[gi] = __builtin_fmaf((float)f[0] + (float)f[1], (r & 1) ? -kCmax : -128.0f, voff[gi]);
+        }
       }
       pa[gi] = as_h8(o[0], o[1], o[2], o[3]);
     }
 #pragma unroll
     for (int nbk = 0; nbk < 8; ++nbk) {
       const uint32_t* seg = vl + (nbk >> 2) * VB;
-      oacc[nbk] = mfma16(pa[nbk * NGV / 8], seg_block<VB, VQ8>(seg, nbk & 3), oacc[nbk]);
+      oacc[nbk] = mfma16(pa[nbk * NGV / 8], seg_block<VB, VQ8, true>(seg, nbk & 3), oacc[nbk]);
     }
+  };
+
+  // Move the accumulators into the wave's LDS sums and restart them: the
+  // high + low rows times 2^24 (codes are fed as code * 2^-24) plus the zero
+  // or offset term, in true units.  The code products are much larger than
+  // the attention output that remains once the zero term is added; settling
+  // that difference every kFlush blocks bounds the size of the fp32 sums
+  // the matrix cores keep adding into.
+  constexpr int kFlush = 16;
+  int since_flush = 0;
+  auto flush = [&]() {
+    const float vscale = pow2i(-pexp);
+    float vb_row[NGV][4];
+#pragma unroll
+    for (int gi = 0; gi < NGV; ++gi) {
+      const float tot = VQ8 ? rows_sum(voff[gi] + dpp_ror8(voff[gi]))
+                            : rows_sum(vbias[gi][0] + vbias[gi][1] * pow2i((int)kOdd));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vb_row[gi][r] = __shfl(tot, 4 * (q4 & 1) + r, 64);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oacc[nb][r] += swap_halves(oacc[nb][r]);
+    if (q4 < 2) {       // lanes q4 = 0, 1 now hold heads 4 q4 + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+          wo[wave][4 * q4 + r][16 * nb + n] +=
+              (oacc[nb][r] * 0x1p24f + vb_row[nb * NGV / 8][r]) * vscale;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int gi = 0; gi < NGV; ++gi) { vbias[gi][0] = vbias[gi][1] = 0.f; voff[gi] = 0.f; }
+    since_flush = 0;
   };
 
   // one block with quantized keys
@@ -724,6 +799,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
       }
     }
     softmax_pv(ragged, sc, B.v, B.vp, valid);
+    if (++since_flush == kFlush) flush();
   };
 
   // ---- hot loop: register pipeline over the blocks with 32 cached tokens and
@@ -799,35 +875,13 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   }
 
   // ---- wave result -> LDS (true units) ------------------------------------------
-  const float vscale = pow2i(-pexp);          // fed units -> true units
-  const float l_tot = rows_sum(l_run[0] + l_run[1] * pow2i((int)kOdd)) * vscale;
-  // high + low rows: lanes q4 = 0, 1 hold the high parts of heads 4*q4 + r,
-  // lanes q4 + 2 the low parts.
-#pragma unroll
-  for (int nbk = 0; nbk < 8; ++nbk)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) oacc[nbk][r] += swap_halves(oacc[nbk][r]);
-  const float oscale = 0x1p24f * vscale;      // codes are fed as code * 2^-24
-  if (q4 < 2) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int jj = 4 * q4 + r;
-#pragma unroll
-      for (int nbk = 0; nbk < 8; ++nbk) wo[wave][jj][16 * nbk + n] = oacc[nbk][r] * oscale;
-    }
-  }
-  float vb_tot[NGV], vo_tot[NGV];
-#pragma unroll
-  for (int gi = 0; gi < NGV; ++gi) {
-    vb_tot[gi] = rows_sum(vbias[gi][0] + vbias[gi][1] * pow2i((int)kOdd)) * vscale;
-    vo_tot[gi] = rows_sum(voff[gi]);
-  }
+  flush();
+  const float l_tot = rows_sum(l_run[0] + l_run[1] * pow2i((int)kOdd)) * pow2i(-pexp);
   if (q4 == 0 && n < 8) {
     wm[wave][j] = m_run;
     wl[wave][j] = l_tot;
 #pragma unroll
-    for (int gi = 0; gi < NGV; ++gi)
-      wb[wave][j][gi] = VQ8 ? -128.0f * vo_tot[gi] * vscale : vb_tot[gi];
+    for (int gi = 0; gi < NGV; ++gi) wb[wave][j][gi] = 0.f;   // the zero terms are in wo
   }
   __syncthreads();
 

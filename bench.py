@@ -37,12 +37,19 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
+KERNEL_SOURCES = {"dec_mfma_kernel": "decode_mfma.hip", "dec_lut_kernel": "decode_lut.hip",
+                  "dec_generic_kernel": "decode_generic.hip"}
+
+
+def kernel_source_sha(kernel: str) -> str:
+    """Hash of the sources a decode kernel is compiled from: its own .hip
+    file and every header of the library."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_kv_cache_04_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        if name == KERNEL_SOURCES[kernel] or name.endswith(".h"):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
@@ -55,7 +62,7 @@ def counter_traffic(workload: str, kernel: str):
         rec = json.load(open(path)).get(f"{workload}/{kernel}")
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_source_sha") != kernel_source_sha():
+    if not rec or rec.get("kernel_source_sha") != kernel_source_sha(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -63,19 +70,15 @@ def counter_traffic(workload: str, kernel: str):
 def cpu_baseline(w, seconds: float = 12.0):
     """Time the CPU oracle (float32 encode + float64 decode attention) on a
     bounded sample of the workload: whole (sequence, KV head) slices at the
-    full context, as many as fit in ``seconds``."""
-    import numpy as np
-    import torch
+    full context, as many as fit in half of ``seconds``, once with the
+    BLAS / OpenMP pools at their default size and once limited to one
+    thread.  Encode and attention are timed separately."""
     from oracle import attention as oatt
     from oracle import cache_bytes as ocb
     from oracle import quant as oq
     from synth import make_workload
     from synth.workloads import make_inputs
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    from threadpoolctl import threadpool_info, threadpool_limits
     w1 = make_workload(w.cfg_id, batch=1, n_kv_heads=1, ctx=w.ctx, gqa=w.gqa, seed=7)
     inputs = make_inputs(w1, "cpu")
     x_k = inputs["k"].float().numpy()
@@ -85,25 +88,41 @@ def cpu_baseline(w, seconds: float = 12.0):
     q = inputs["q"].float().numpy()
     slice_bytes = ocb.payload_bytes(w1.k, w1.v, batch=1, n_kv_heads=1, head_dim=128,
                                     n_ctx=w1.ctx, kv_dtype=w1.kv_dtype)
-    done, t0 = 0, time.perf_counter()
-    while True:
-        ek = oq.encode_tensor(x_k, w1.k, kcb)
-        ev = oq.encode_tensor(x_v, w1.v, vcb)
-        oatt.decode_attention(q, ek["deq"], ev["deq"], rope=w1.rope, rope_base=w1.rope_base)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or done >= 64:
-            break
-    return {"value": round(done * slice_bytes / el / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{done} x (1 sequence, 1 KV head, {w1.gqa} query heads, T={w1.ctx}) slices: "
-                      f"float32 encode + float64 dequant and attention, {el:.1f} s"}
+
+    def run(budget):
+        done, t_enc, t_att = 0, 0.0, 0.0
+        while True:
+            t0 = time.perf_counter()
+            ek = oq.encode_tensor(x_k, w1.k, kcb)
+            ev = oq.encode_tensor(x_v, w1.v, vcb)
+            t1 = time.perf_counter()
+            oatt.decode_attention(q, ek["deq"], ev["deq"], rope=w1.rope, rope_base=w1.rope_base)
+            t2 = time.perf_counter()
+            done, t_enc, t_att = done + 1, t_enc + (t1 - t0), t_att + (t2 - t1)
+            if t_enc + t_att >= budget or done >= 64:
+                return done, t_enc, t_att
+
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    n_all, enc_all, att_all = run(seconds / 2)
+    with threadpool_limits(limits=1):
+        n_one, enc_one, att_one = run(seconds / 2)
+    per = lambda n, t: round(t / n, 3)  # noqa: E731
+    return {"value": round(n_all * slice_bytes / (enc_all + att_all) / 1e9, 4), "unit": "GB/s",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_all} x (1 sequence, 1 KV head, {w1.gqa} query heads, T={w1.ctx}) slices: "
+                      f"float32 encode + float64 dequant and attention, {enc_all + att_all:.1f} s "
+                      f"(host reports {os.cpu_count()} CPUs)",
+            "encode_s_per_slice": per(n_all, enc_all), "attention_s_per_slice": per(n_all, att_all),
+            "single_thread": {"value": round(n_one * slice_bytes / (enc_one + att_one) / 1e9, 4),
+                              "slices": n_one, "encode_s_per_slice": per(n_one, enc_one),
+                              "attention_s_per_slice": per(n_one, att_one)}}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=256,
+                    help="timed steps (the serving workload flushes a key group every 128)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--ctx", type=int, default=None, help="context (config 2: 4096/8192/16384)")
@@ -179,6 +198,9 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     dec_s = [ev() for _ in range(K)]
     dec_e = [ev() for _ in range(K)]
+    st_s = [ev() for _ in range(K)]    # whole step (append + decode)
+    st_e = [ev() for _ in range(K)]
+    flush_step = []                    # the append filled a per-channel key group
     # events around the token-streaming kernel alone (recorded once here so
     # that they exist before their handles go to the library)
     ker_s = [ev() for _ in range(K)]
@@ -187,11 +209,17 @@ def main():
         e.record(stream)
     step_bytes = []
 
+    k_group = w.k.get("group_size", 0) if w.k.get("layout") == "per_channel" else 0
+
     def step(i, timed_idx=None):
         c = caches[i % copies]
+        if timed_idx is not None:
+            st_s[timed_idx].record(stream)
         if serving:
             kn, vn, qn = steps_tok[i]
             c.append(kn, vn, stream=stream)
+            if timed_idx is not None:
+                flush_step.append(bool(k_group) and c.n_ctx % k_group == 0)
             qq = qn
         else:
             qq = q
@@ -201,6 +229,7 @@ def main():
         c.decode(qq, out=out, stream=stream)
         if timed_idx is not None:
             dec_e[timed_idx].record(stream)
+            st_e[timed_idx].record(stream)
             step_bytes.append(kvq.cache_bytes(cfg, c.n_ctx))
 
     with torch.cuda.stream(stream):
@@ -230,6 +259,19 @@ def main():
     log(f"step {ms_step * 1e3:.1f} us, decode call {dec_avg * 1e3:.1f} us, {kernel} avg "
         f"{ker_avg * 1e3:.1f} us (p10 {ker_ms[K // 10] * 1e3:.1f}, p90 {ker_ms[(9 * K) // 10] * 1e3:.1f}), "
         f"{bytes_avg / 1e6:.1f} MB/step -> {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.1%} of peak)")
+
+    cycle = None
+    if serving:
+        st_ms = [a.elapsed_time(b) for a, b in zip(st_s, st_e)]
+        fl = [t for t, f in zip(st_ms, flush_step) if f]
+        other = sorted(t for t, f in zip(st_ms, flush_step) if not f)
+        cycle = {"key_group_tokens": k_group, "timed_steps": K, "flush_steps": len(fl),
+                 "flush_step_us": round(sum(fl) / len(fl) * 1e3, 2) if fl else None,
+                 "other_step_us_mean": round(sum(other) / len(other) * 1e3, 2),
+                 "other_step_us_p10": round(other[len(other) // 10] * 1e3, 2),
+                 "other_step_us_p90": round(other[(9 * len(other)) // 10] * 1e3, 2)}
+        log(f"serving cycle: {len(fl)} flush step(s) of {K}: "
+            f"{cycle['flush_step_us']} us; other steps {cycle['other_step_us_mean']} us mean")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -264,6 +306,8 @@ def main():
                      "algorithmic_bytes_per_launch": int(bytes_avg)},
         "cpu_baseline": cpu,
     }
+    if cycle is not None:
+        res["serving_cycle"] = cycle
     print(json.dumps(res), flush=True)
 
 

@@ -60,6 +60,7 @@ struct __align__(16) LutLds {
   float vcorr[kHeads][kD];         // value outlier sums of the chunk
   float2 estep[kPairs];            // (cos, sin) of kChunk * theta_i
   double theta[kPairs];
+  uint2 ring[kHeads][64];          // per wave: outlier entries of its head group, compacted
 };
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -203,12 +204,30 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
       }
     }
   };
-  // calls f(ww, tau, c, dense index, value) for the entries of this
-  // workgroup's heads
+  // Calls f(ww, tau, c, dense index, value) for the entries of this
+  // workgroup's heads.  Each wave compacts the matching entries among those
+  // its threads loaded into its ring (ballot + lane count) and works through
+  // the ring once it holds a wave's worth: about one entry in eight belongs
+  // to the workgroup, so the per-entry work then runs on full waves.
   auto for_entries = [&](const DevTensor& T, int nt, const OutVec* o, auto&& f) {
     const int ko = T.k_out;
     const int n_ent = nt * ko;
     const float inv_k = 1.0f / (float)ko;
+    int qn = 0;                                    // ring fill, wave-uniform
+    auto drain = [&]() {
+      __builtin_amdgcn_wave_barrier();             // ring writes of this wave land first
+      if (lane < qn) {
+        const uint2 r = S.ring[wave][lane];
+        const uint32_t col = r.x & 0xffffu;
+        const int e = (int)(r.x >> 16);
+        // token of entry e: floor(e / k), exact in float for e < 2^16
+        const int tau = (int)(((float)e + 0.5f) * inv_k);
+        const int ww = (int)((col & 0xfffu) >> 7) - hg * kHeads;
+        f(ww, tau, (int)(col & (kD - 1)), col >> 12, h2f((uint16_t)r.y));
+      }
+      __builtin_amdgcn_wave_barrier();             // reads done before the ring refills
+      qn = 0;
+    };
 #pragma unroll
     for (int u = 0; u < kVec; ++u) {
       const uint32_t cw[4] = {o[u].col.x, o[u].col.y, o[u].col.z, o[u].col.w};
@@ -217,15 +236,20 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
       for (int x = 0; x < 8; ++x) {
         const int e = 8 * (tid + 256 * u) + x;     // entry index within the chunk
         const uint32_t col = (cw[x >> 1] >> (16 * (x & 1))) & 0xffffu;
-        const int hh = (int)((col & 0xfffu) >> 7), ww = hh - hg * kHeads;
-        if (e < n_ent && ww >= 0 && ww < kHeads && hh < Hkv) {
-          // token of entry e: floor(e / k), exact in float for e < 2^16
-          const int tau = (int)(((float)e + 0.5f) * inv_k);
-          const float val = h2f((uint16_t)((vw[x >> 1] >> (16 * (x & 1))) & 0xffffu));
-          f(ww, tau, (int)(col & (kD - 1)), col >> 12, val);
+        // head of the flat index (col & 0xfff) >> 7; its group: bits 9-11
+        const bool hit = e < n_ent && ((col >> 9) & 7u) == (uint32_t)hg;
+        const uint64_t mask = __ballot(hit);
+        const int cnt = __popcll(mask);
+        if (qn + cnt > 64) drain();
+        if (hit) {
+          const int slot = qn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+          S.ring[wave][slot] = make_uint2(col | ((uint32_t)e << 16), (vw[x >> 1] >> (16 * (x & 1))) & 0xffffu);
         }
+        qn += cnt;
       }
     }
+    if (qn > 0) drain();
   };
 
   for (int ci = 0; ci < n_chunks; ++ci) {
@@ -244,21 +268,34 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
     if (head_ok) {
       const uint32_t kw[16] = {kc[0].x, kc[0].y, kc[0].z, kc[0].w, kc[1].x, kc[1].y, kc[1].z, kc[1].w,
                                kc[2].x, kc[2].y, kc[2].z, kc[2].w, kc[3].x, kc[3].y, kc[3].z, kc[3].w};
-      // centroid of channel c with index field at bit 4*e of dword w
-      auto cent = [&](uint32_t wd, int e, int c) -> float {
-        const uint32_t code = (wd >> (4 * e)) & 15u;
-        return (float)__builtin_bit_cast(_Float16, S.kt[wave][c][code]);
+      // Centroid lookups: the byte offset of S.kt[wave][c][code] is
+      // c * 32 (a constant of the unrolled loop) + wave * 4096 + code * 2.
+      // The codes of a dword are first spread as code * 2 into the bytes of
+      // two words (even and odd nibbles); one byte permute then joins a
+      // code byte with the wave's byte into the offset.
+      const uint8_t* ktb = reinterpret_cast<const uint8_t*>(&S.kt[0][0][0]);
+      const uint32_t wvb = (uint32_t)wave << 12;
+      auto spread = [](uint32_t wd, uint32_t out[2]) {
+        out[0] = (wd << 1) & 0x1e1e1e1eu;     // nibbles 0, 2, 4, 6
+        out[1] = (wd >> 3) & 0x1e1e1e1eu;     // nibbles 1, 3, 5, 7
+      };
+      auto cent = [&](const uint32_t x[2], int e, int c) -> float {
+        const uint32_t off = __builtin_amdgcn_perm(x[e & 1], wvb, 0x0c0c0100u | (uint32_t)(4 + (e >> 1)));
+        return (float)*reinterpret_cast<const _Float16*>(ktb + c * 32 + off);
       };
       // dword 4q + m of the row holds channels 32m + 8q + e (e = 0..7)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m) {
+          uint32_t xa[2], xb[2];
+          spread(kw[4 * q + m], xa);
+          spread(kw[4 * q + m + 2], xb);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int i = 32 * m + 8 * q + e;          // pair (i, i + 64)
-            const float av = cent(kw[4 * q + m], e, i);
-            const float bv = cent(kw[4 * q + m + 2], e, i + kPairs);
+            const float av = cent(xa, e, i);
+            const float bv = cent(xb, e, i + kPairs);
             const float x = S.qs[wave][i], y = S.qs[wave][i + kPairs];
             if constexpr (ROPE) {
               const float2 cs = S.e[i][lane];
@@ -269,6 +306,7 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
               s = __builtin_fmaf(bv, y, s);
             }
           }
+        }
     }
 
     // ---- key outliers: (value - centroid) * coefficient into the scores ----------------
@@ -325,15 +363,23 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
       // ---- values: lane = channel pair ----------------------------------------------
       const uint32_t vw[16] = {vc[0].x, vc[0].y, vc[0].z, vc[0].w, vc[1].x, vc[1].y, vc[1].z, vc[1].w,
                                vc[2].x, vc[2].y, vc[2].z, vc[2].w, vc[3].x, vc[3].y, vc[3].z, vc[3].w};
+      // byte offset of S.vt[wave][code][lane] = lane * 4 + (16 wave + code) * 256:
+      // the code bytes of a dword (16 wave added in every byte) are joined
+      // with the lane's byte by one byte permute per lookup
+      const uint8_t* vtb = reinterpret_cast<const uint8_t*>(&S.vt[0][0][0]);
+      const uint32_t l4 = (uint32_t)lane << 2;
+      const uint32_t wpat = (uint32_t)wave * 0x10101010u;
 #pragma unroll
       for (int d4 = 0; d4 < 16; ++d4) {
         const f32x4 p4 = *reinterpret_cast<const f32x4*>(&S.p[wave][4 * d4]);
         const uint32_t wd = vw[d4];
+        const uint32_t xlo = (wd & 0x0f0f0f0fu) | wpat;
+        const uint32_t xhi = ((wd >> 4) & 0x0f0f0f0fu) | wpat;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const uint32_t lo = (wd >> (8 * k)) & 15u, hi = (wd >> (8 * k + 4)) & 15u;
-          const uint32_t c0 = S.vt[wave][lo][lane];
-          const uint32_t c1 = S.vt[wave][hi][lane];
+          const uint32_t sel = 0x0c0c0000u | ((uint32_t)(4 + k) << 8);
+          const uint32_t c0 = *reinterpret_cast<const uint32_t*>(vtb + __builtin_amdgcn_perm(xlo, l4, sel));
+          const uint32_t c1 = *reinterpret_cast<const uint32_t*>(vtb + __builtin_amdgcn_perm(xhi, l4, sel));
           acc0 = __builtin_fmaf(p4[k], half_lo(c0), acc0);
           acc1 = __builtin_fmaf(p4[k], half_hi(c1), acc1);
         }

@@ -203,7 +203,7 @@ kvq_status kvq_cache_bytes(const kvq_config* cfg, int64_t n_ctx, int64_t n_layer
  *     4-bit: byte j = code 2j | code 2j+1 << 4; 3-bit: three little-endian
  *     dwords D0, D1, D2 -- for block m and r = 0..3 the pair (8m+r, 8m+r+4)
  *     keeps its low two bits at bits 2p and 16+2p of D[m/2], p = 4(m%2)+r,
- *     and its high bits at bits P and 16+P of D2, P = 4m+r.
+ *     and its high bits at bits H and 16+H of D2, H = 8(m/2) + 2r + m%2.
  *   keys: a row of 16*bits bytes per token, segment q = 0..3 holding
  *     channels 32m + 8q + e; codes [B][Hkv][Tcap][row].
  *   values: tiles of 32 tokens, 64 lanes L = 16q + i of 8*bits bytes (two

@@ -16,8 +16,10 @@ into 4*bits bytes:
 * 3-bit: three little-endian dwords D0, D1, D2.  For block m and r = 0..3
   the pair (u_a, u_b) = (8m + r, 8m + r + 4) is stored as: the low two bits
   of u_a at bit 2p and of u_b at bit 16 + 2p of D[m // 2], where
-  p = 4 * (m % 2) + r; the high bit of u_a at bit P and of u_b at bit 16 + P
-  of D2, where P = 4m + r.
+  p = 4 * (m % 2) + r; the high bit of u_a at bit H and of u_b at bit 16 + H
+  of D2, where H = 8 * (m // 2) + 2r + (m % 2).  (After one shift per block,
+  pair r's low bits sit at 2r and its high bit at 2r + 2, so both planes
+  carry the same per-pair factor 4^r.)
 
 Key rows ("K-row" layout): every token has a row of 16*bits bytes made of 4
 segments q = 0..3; segment q holds channels c = 32m + 8q + e.
@@ -64,11 +66,11 @@ def pack_segment(codes: np.ndarray, bits: int) -> np.ndarray:
             for r in range(4):
                 ua, ub = 8 * m + r, 8 * m + r + 4
                 p = 4 * (m % 2) + r
-                P = 4 * m + r
+                H = 8 * (m // 2) + 2 * r + (m % 2)
                 dw[..., m // 2] |= (c[..., ua] & 3) << (2 * p)
                 dw[..., m // 2] |= (c[..., ub] & 3) << (16 + 2 * p)
-                dw[..., 2] |= (c[..., ua] >> 2) << P
-                dw[..., 2] |= (c[..., ub] >> 2) << (16 + P)
+                dw[..., 2] |= (c[..., ua] >> 2) << H
+                dw[..., 2] |= (c[..., ub] >> 2) << (16 + H)
         out = np.zeros(lead + (12,), dtype=np.uint8)
         for w in range(3):
             for b in range(4):
@@ -96,9 +98,9 @@ def unpack_segment(data: np.ndarray, bits: int) -> np.ndarray:
             for r in range(4):
                 ua, ub = 8 * m + r, 8 * m + r + 4
                 p = 4 * (m % 2) + r
-                P = 4 * m + r
-                out[..., ua] = ((dw[m // 2] >> (2 * p)) & 3) | (((dw[2] >> P) & 1) << 2)
-                out[..., ub] = ((dw[m // 2] >> (16 + 2 * p)) & 3) | (((dw[2] >> (16 + P)) & 1) << 2)
+                H = 8 * (m // 2) + 2 * r + (m % 2)
+                out[..., ua] = ((dw[m // 2] >> (2 * p)) & 3) | (((dw[2] >> H) & 1) << 2)
+                out[..., ub] = ((dw[m // 2] >> (16 + 2 * p)) & 3) | (((dw[2] >> (16 + H)) & 1) << 2)
         return out
     raise ValueError(bits)
 

@@ -163,20 +163,24 @@ struct Unpack<4> {
 
 template <>
 struct Unpack<3> {
-  static constexpr float f[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-  // dlo: dword with the low two bits of block m (D[m / 2]); d2: high bits
-  // FLIP complements the odd pairs: their low bits sit at bit pairs 2p with
-  // p odd (mask 0xcccc per half), their high bits at the odd bits P of d2
-  // (mask 0xaaaa), so two XORs of the source dwords do it
+  // Two operands (bit planes): pair r's low two bits as lo2 * 4^r and its
+  // high bit as hi1 * 4 * 4^r, so the two products add up to code * 4^r (the
+  // factor 4^-r sits in the other operand).  dlo = D[m / 2] holds the low
+  // bits of pair r at bit 2r (+ 8 for odd m); d2 holds the high bit at
+  // H = 8 (m / 2) + 2r + (m % 2), which one shift per block moves to 2r + 2.
+  // FLIP complements the odd pairs: their low and high bits both sit under
+  // the mask 0xcccc of each half.
   template <bool FLIP>
-  __device__ static __forceinline__ void run(uint32_t dlo, uint32_t d2, int m, uint32_t out[4]) {
-    if (FLIP) { dlo ^= 0xccccccccu; d2 ^= 0xaaaaaaaau; }
+  __device__ static __forceinline__ void run(uint32_t dlo, uint32_t d2, int m, uint32_t lo[4],
+                                             uint32_t hi[4]) {
+    if (FLIP) { dlo ^= 0xccccccccu; d2 ^= 0xccccccccu; }
+    const uint32_t l = (m & 1) ? (dlo >> 8) : dlo;
+    const int sh = 8 * (m >> 1) + (m & 1) - 2;
+    const uint32_t h = sh >= 0 ? (d2 >> sh) : (d2 << (-sh));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int p = 4 * (m & 1) + r, P = 4 * m + r;
-      const uint32_t lo2 = (dlo >> (2 * p)) & 0x00030003u;
-      const uint32_t hi1 = (P >= 2 ? (d2 >> (P - 2)) : (d2 << (2 - P))) & 0x00040004u;
-      out[r] = lo2 | hi1;
+      lo[r] = l & (0x00030003u << (2 * r));
+      hi[r] = h & (0x00010001u << (2 * r + 2));
     }
   }
 };
@@ -197,11 +201,10 @@ struct Unpack<8> {
 // 8-bit: 127 - q, the complement of the offset code q + 128).
 template <int BITS, bool SIGNED, bool FLIP = false>
 __device__ __forceinline__ half8 seg_block(const uint32_t* seg, int m) {
+  static_assert(BITS != 3, "3-bit codes unpack into two planes: code_planes");
   uint32_t o[4];
   if constexpr (BITS == 4) {
     Unpack<4>::run<FLIP>(seg[m], o);
-  } else if constexpr (BITS == 3) {
-    Unpack<3>::run<FLIP>(seg[m >> 1], seg[2], m, o);
   } else {
     // pair r takes byte r of both dwords: bytes 1 and 3 are the odd pairs
     constexpr uint32_t kFlipMask = SIGNED ? 0x7f807f80u : 0xff00ff00u;
@@ -212,11 +215,38 @@ __device__ __forceinline__ half8 seg_block(const uint32_t* seg, int m) {
   return as_h8(o[0], o[1], o[2], o[3]);
 }
 
+// MFMA operands per block of BITS-bit codes (3-bit codes: two bit planes)
+template <int BITS>
+constexpr int kPlanes = BITS == 3 ? 2 : 1;
+
+template <int BITS, bool SIGNED, bool FLIP = false>
+__device__ __forceinline__ void code_planes(const uint32_t* seg, int m, half8 out[kPlanes<BITS>]) {
+  if constexpr (BITS == 3) {
+    uint32_t lo[4], hi[4];
+    Unpack<3>::run<FLIP>(seg[m >> 1], seg[2], m, lo, hi);
+    out[0] = as_h8(lo[0], lo[1], lo[2], lo[3]);
+    out[1] = as_h8(hi[0], hi[1], hi[2], hi[3]);
+  } else {
+    out[0] = seg_block<BITS, SIGNED, FLIP>(seg, m);
+  }
+}
+
+// factor of pair r that the other operand of a code operand must carry
 template <int BITS>
 __device__ __forceinline__ float pair_factor(int r) {
   if constexpr (BITS == 4) return (r & 1) ? 1.0f / 16.0f : 1.0f;
+  if constexpr (BITS == 3) return r == 0 ? 1.0f : (r == 1 ? 0.25f : (r == 2 ? 0.0625f : 0.015625f));
   return 1.0f;
 }
+
+// P operand pairs with the same factor share an exponent class: 4-bit values
+// (odd pairs unpack 4 bits up: 2^-4) and 3-bit values (pair r: 4^-r)
+template <int VB>
+constexpr int kClasses = VB == 3 ? 4 : 2;
+template <int VB>
+__device__ __forceinline__ constexpr int pe_class(int r) { return VB == 3 ? r : (r & 1); }
+template <int VB>
+__device__ __forceinline__ constexpr int pe_exp(int cls) { return VB == 3 ? 2 * cls : (VB == 4 ? 4 * cls : 0); }
 
 // Operand in "pair order" from 8 values x[e] (e = 0..7): pair r = (x[r], x[r + 4])
 // each divided by the unpack factor of the other operand, scaled by ``sc`` and
@@ -423,12 +453,12 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   f32x4 oacc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Probabilities are kept in "fed units": p' = 2^(s - m_run + pexp) for the
-  // even pairs of the P operand and 2^-kOdd times that for the odd pairs
-  // (4-bit values: the nibble of an odd pair is unpacked 4 bits up).  The
-  // bias -(m_run - pexp) is folded into the key products of the high
-  // columns, so one exp2 of t = s - mref (- kOdd) yields p'.
-  constexpr float kOdd = VB == 4 ? 4.0f : 0.0f;
+  // Probabilities are kept in "fed units": p' = 2^(s - m_run + pexp) times
+  // 2^-pe_exp of the pair's class (4-bit values: the nibble of an odd pair
+  // is unpacked 4 bits up; 3-bit values: pair r carries 4^r).  The bias
+  // -(m_run - pexp) - pe_exp is folded into the key products of the high
+  // columns, so one exp2 of t = s - mref - pe_exp yields p'.
+  constexpr int NC = kClasses<VB>;
   // Value codes are unsigned, so without care every P.V product would be
   // positive, and the matrix cores drop the parts of products that sit far
   // below the largest product of a dot product: those losses would add up
@@ -440,11 +470,17 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   float m_run = -INFINITY;   // reference maximum of head j (lanes n, n + 8 agree)
   float mref = 0.f;          // bias folded into t (m_run - pexp once m_run is set)
   float thr = -INFINITY;     // rescale when t > thr (= kLazy + m_run - mref)
-  float l_run[2] = {0.f, 0.f};   // sum of p' over this lane's even / odd tokens
-  float vbias[NGV][2];       // sum p' * zero over even / odd tokens (values)
+  float l_run[NC];           // sum of p' over this lane's tokens of each class
+  float vbias[NGV][NC];      // sum p' * zero over the tokens of each class (values)
   float voff[NGV];           // q8_0: offset term of the fp16 P operand parts this lane fed
 #pragma unroll
-  for (int gi = 0; gi < NGV; ++gi) { vbias[gi][0] = vbias[gi][1] = 0.f; voff[gi] = 0.f; }
+  for (int c = 0; c < NC; ++c) l_run[c] = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < NGV; ++gi) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) vbias[gi][c] = 0.f;
+    voff[gi] = 0.f;
+  }
   // value operand scale: fed P = p * scale * 2^pexp <= 2^kFedLog2 (p <= 2^kLazy);
   // pexp changes when a block brings a scale above sbound (the accumulators
   // are then rescaled by the exact power of two)
@@ -454,15 +490,16 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   // per-channel keys: B operand of the current key group
   half8 bk[4];
   float kbias = 0.f;         // sm2 * sum_c q_c z_c (high lanes)
-  float tbias[2] = {0.f, -kOdd};   // high lanes: -mref, -mref - kOdd
-  float kb2[2] = {0.f, 0.f};       // kbias + tbias
-  if (!hi_lane) tbias[1] = 0.f;
+  float tbias[NC];           // high lanes: -mref - pe_exp(class)
+  float kb2[NC];             // kbias + tbias
   auto set_bias = [&]() {
-    tbias[0] = hi_lane ? -mref : 0.f;
-    tbias[1] = hi_lane ? -mref - kOdd : 0.f;
-    kb2[0] = kbias + tbias[0];
-    kb2[1] = kbias + tbias[1];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      tbias[c] = hi_lane ? -mref - (float)pe_exp<VB>(c) : 0.f;
+      kb2[c] = kbias + tbias[c];
+    }
   };
+  set_bias();
   float kscale = 0.f;        // sm2 * 2^(24 - E)
   int grp_end = -1;          // first block after the current key group
 
@@ -551,13 +588,13 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
       bk[m] = head_ok ? __builtin_bit_cast(half8, kb_tab[wave][j][hl][4 * m + q4])
                       : as_h8(0u, 0u, 0u, 0u);
     kbias = (hi_lane && head_ok) ? zb_tab[wave][j] * sm2 : 0.f;
-    kb2[0] = kbias + tbias[0];
-    kb2[1] = kbias + tbias[1];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kb2[c] = kbias + tbias[c];
   };
 
   // Softmax and P.V for one block.  sc: per-column partial scores (the bias
   // tbias sits in the high columns), so that the sum of a lane's high and
-  // low columns is t = s - mref (- kOdd for odd pairs).  RAGGED (an
+  // low columns is t = s - mref - pe_exp.  RAGGED (an
   // integral_constant) is true only for a block with fewer than 32 cached
   // tokens: the others skip the masking.
   auto softmax_pv = [&](auto ragged, float sc[2][4], const uint32_t* vl,
@@ -578,12 +615,12 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
       // move the reference maximum (wave-uniform branch, rare after warm-up)
       const float m_new = fmaxf(m_run, rows_max(bmax) + mref);
       const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run[0] *= alpha;
-      l_run[1] *= alpha;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) l_run[c] *= alpha;
 #pragma unroll
       for (int gi = 0; gi < NGV; ++gi) {
-        vbias[gi][0] *= alpha;
-        vbias[gi][1] *= alpha;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) vbias[gi][c] *= alpha;
         voff[gi] *= alpha;
       }
       // accumulator row r of this lane belongs to head (4 q4 + r) & 7, whose
@@ -645,12 +682,12 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
       for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) oacc[nb][r] *= f;
-      l_run[0] *= f;
-      l_run[1] *= f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) l_run[c] *= f;
 #pragma unroll
       for (int gi = 0; gi < NGV; ++gi) {
-        vbias[gi][0] *= f;
-        vbias[gi][1] *= f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) vbias[gi][c] *= f;
         voff[gi] *= f;
       }
       pexp = np;
@@ -671,7 +708,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         pr[mb][r] = __builtin_amdgcn_exp2f(t[mb][r]);
-        l_run[r & 1] += pr[mb][r];
+        l_run[pe_class<VB>(r)] += pr[mb][r];
       }
     // P operand: pair r = tokens (4 q4 + r, 16 + 4 q4 + r), p' * scale split
     // into fp16 high / low parts; zero points enter through vbias
@@ -694,8 +731,9 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
             const float sc_h = (float)h[0];
             x[mb] = __builtin_fmaf(pr[mb][r], (r & 1) ? -sc_h : sc_h, 0.f);
             // odd pairs: + cmax p' scale (x holds -p' scale there)
-            const float vb = (r & 1) ? __builtin_fmaf(-kCmax, x[mb], vbias[gi][1]) : vbias[gi][0];
-            vbias[gi][r & 1] = __builtin_fmaf(pr[mb][r], (float)h[1], vb);
+            const int cl = pe_class<VB>(r);
+            const float vb = (r & 1) ? __builtin_fmaf(-kCmax, x[mb], vbias[gi][cl]) : vbias[gi][cl];
+            vbias[gi][cl] = __builtin_fmaf(pr[mb][r], (float)h[1], vb);
           }
         }
         o[r] = hilo_split(x[0], x[1], lo_mask);
@@ -710,7 +748,10 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int nbk = 0; nbk < 8; ++nbk) {
       const uint32_t* seg = vl + (nbk >> 2) * VB;
-      oacc[nbk] = mfma16(pa[nbk * NGV / 8], seg_block<VB, VQ8, true>(seg, nbk & 3), oacc[nbk]);
+      half8 vcode[kPlanes<VB>];
+      code_planes<VB, VQ8, true>(seg, nbk & 3, vcode);
+#pragma unroll
+      for (int pl = 0; pl < kPlanes<VB>; ++pl) oacc[nbk] = mfma16(pa[nbk * NGV / 8], vcode[pl], oacc[nbk]);
     }
   };
 
@@ -727,8 +768,10 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     float vb_row[NGV][4];
 #pragma unroll
     for (int gi = 0; gi < NGV; ++gi) {
-      const float tot = VQ8 ? rows_sum(voff[gi] + dpp_ror8(voff[gi]))
-                            : rows_sum(vbias[gi][0] + vbias[gi][1] * pow2i((int)kOdd));
+      float vb = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) vb = __builtin_fmaf(vbias[gi][c], pow2i(pe_exp<VB>(c)), vb);
+      const float tot = VQ8 ? rows_sum(voff[gi] + dpp_ror8(voff[gi])) : rows_sum(vb);
 #pragma unroll
       for (int r = 0; r < 4; ++r) vb_row[gi][r] = __shfl(tot, 4 * (q4 & 1) + r, 64);
     }
@@ -747,7 +790,11 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int gi = 0; gi < NGV; ++gi) { vbias[gi][0] = vbias[gi][1] = 0.f; voff[gi] = 0.f; }
+    for (int gi = 0; gi < NGV; ++gi) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) vbias[gi][c] = 0.f;
+      voff[gi] = 0.f;
+    }
     since_flush = 0;
   };
 
@@ -765,20 +812,31 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
       for (int mb = 0; mb < 2; ++mb) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < 4; ++m) c = mfma16(seg_block<KB, KQ8>(B.k[mb], m), bk[m], c);
+        for (int m = 0; m < 4; ++m) {
+          half8 kcode[kPlanes<KB>];
+          code_planes<KB, KQ8>(B.k[mb], m, kcode);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[mb][r] = c[r] * kscale + kb2[r & 1];
+          for (int pl = 0; pl < kPlanes<KB>; ++pl) c = mfma16(kcode[pl], bk[m], c);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[mb][r] = c[r] * kscale + kb2[pe_class<VB>(r)];
       }
     } else {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        float acc[4] = {tbias[0], tbias[1], tbias[0], tbias[1]};
+        float acc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = tbias[pe_class<VB>(r)];
 #pragma unroll
         for (int gi = 0; gi < NGK; ++gi) {
           f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m)
-            c = mfma16(seg_block<KB, KQ8>(B.k[mb], m), bq[m], c);
+          for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m) {
+            half8 kcode[kPlanes<KB>];
+            code_planes<KB, KQ8>(B.k[mb], m, kcode);
+#pragma unroll
+            for (int pl = 0; pl < kPlanes<KB>; ++pl) c = mfma16(kcode[pl], bq[m], c);
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const uint32_t* d = B.kp[mb];
@@ -866,7 +924,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
           c = mfma16(__builtin_bit_cast(half8, v), bt[m], c);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[mb][r] = c[r] * sm2 + tbias[r & 1];
+        for (int r = 0; r < 4; ++r) sc[mb][r] = c[r] * sm2 + tbias[pe_class<VB>(r)];
       }
       Buf B;
       load(B, blk);
@@ -876,7 +934,10 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 
   // ---- wave result -> LDS (true units) ------------------------------------------
   flush();
-  const float l_tot = rows_sum(l_run[0] + l_run[1] * pow2i((int)kOdd)) * pow2i(-pexp);
+  float l_sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) l_sum = __builtin_fmaf(l_run[c], pow2i(pe_exp<VB>(c)), l_sum);
+  const float l_tot = rows_sum(l_sum) * pow2i(-pexp);
   if (q4 == 0 && n < 8) {
     wm[wave][j] = m_run;
     wl[wave][j] = l_tot;

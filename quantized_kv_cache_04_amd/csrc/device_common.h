@@ -36,10 +36,10 @@ __device__ __forceinline__ uint32_t seg_code(const uint8_t* seg, int bits, int u
   if (bits == 8) return seg[u];
   if (bits == 4) return (seg[u >> 1] >> ((u & 1) * 4)) & 15u;
   const int m = u >> 3, e = u & 7, r = e & 3, hi16 = (e >> 2) * 16;
-  const int p = 4 * (m & 1) + r, P = 4 * m + r;
+  const int p = 4 * (m & 1) + r, H = 8 * (m >> 1) + 2 * r + (m & 1);
   const uint32_t* dw = reinterpret_cast<const uint32_t*>(seg);
   const uint32_t lo2 = (dw[m >> 1] >> (2 * p + hi16)) & 3u;
-  const uint32_t hi1 = (dw[2] >> (P + hi16)) & 1u;
+  const uint32_t hi1 = (dw[2] >> (H + hi16)) & 1u;
   return lo2 | (hi1 << 2);
 }
 
@@ -88,9 +88,9 @@ __device__ __forceinline__ void seg_dword_fields(int bits, int j, F&& f) {
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int P = 4 * m + r;
-        f(8 * m + r, P, 1, 2);
-        f(8 * m + r + 4, 16 + P, 1, 2);
+        const int H = 8 * (m >> 1) + 2 * r + (m & 1);
+        f(8 * m + r, H, 1, 2);
+        f(8 * m + r + 4, 16 + H, 1, 2);
       }
   }
 }

@@ -824,9 +824,11 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     } else {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        float acc[4];
+        // score = kq * sum_g scale_g * dot_g + sum_g zero_g * qsum_g + bias:
+        // the fp16 scale and zero enter v_fma_mix straight from their halves
+        float sd[4], zq[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = tbias[pe_class<VB>(r)];
+        for (int r = 0; r < 4; ++r) { sd[r] = 0.f; zq[r] = tbias[pe_class<VB>(r)]; }
 #pragma unroll
         for (int gi = 0; gi < NGK; ++gi) {
           f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -840,20 +842,19 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const uint32_t* d = B.kp[mb];
-            float s, z = 0.f;
             if constexpr (KQ8) {
               const int idx = r * NGK + gi;
-              s = h2f((uint16_t)(d[idx >> 1] >> (16 * (idx & 1))));
+              const half2v sv = __builtin_bit_cast(half2v, d[idx >> 1]);
+              sd[r] = __builtin_fmaf((float)sv[idx & 1], c[r] - qoff[gi], sd[r]);
             } else {
-              s = h2f((uint16_t)(d[r * NGK + gi] & 0xffff));
-              z = h2f((uint16_t)(d[r * NGK + gi] >> 16));
+              const half2v sz = __builtin_bit_cast(half2v, d[r * NGK + gi]);   // (scale, zero)
+              sd[r] = __builtin_fmaf((float)sz[0], c[r], sd[r]);
+              zq[r] = __builtin_fmaf((float)sz[1], qsum[gi], zq[r]);
             }
-            const float dot = (c[r] - (KQ8 ? qoff[gi] : 0.f)) * kq;
-            acc[r] += s * dot + z * qsum[gi];
           }
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[mb][r] = acc[r];
+        for (int r = 0; r < 4; ++r) sc[mb][r] = __builtin_fmaf(sd[r], kq, zq[r]);
       }
     }
     softmax_pv(ragged, sc, B.v, B.vp, valid);

@@ -8,27 +8,29 @@
 // time; dequantization stays fused into the single pass over the cache
 // (Memory-killer page, section 2.3).  Without a GQA group there is no dense
 // contraction to give the matrix cores, so everything runs on the vector
-// ALUs; the kernel is shaped so that every centroid lookup is an LDS read
-// without bank conflicts:
+// ALUs, and the lookups are LDS reads.  The kernel is latency-bound, so it
+// is shaped to keep three workgroups (12 waves) on a CU: 54.5 KB of LDS and
+// at most 168 registers per lane.
 //
 //  * workgroup = 4 waves = 4 KV heads over one range of tokens, walked in
-//    chunks of 64 tokens;
-//  * keys, lane = token: the score of token t is
-//      sum_i a_i (x_i cos + y_i sin) + b_i (y_i cos - x_i sin)
-//    over the rotate-half pairs (a_i, b_i) = (k_i, k_{i+64}) of the
-//    dequantized key and (x_i, y_i) of the query, at the angle
-//    (t - q_pos) theta_i.  All lanes of one lookup read the same channel, so
-//    the 16 centroids (one 32-byte row) serve every lane by broadcast;
+//    chunks of 32 tokens (one value tile);
+//  * keys: lanes tau and tau + 32 share token tau, each taking half of the
+//    64 rotate-half pairs (a_i, b_i) = (k_i, k_{i+64}) (two 16-byte
+//    segments of the key row); the score of token t is
+//      sum_i a_i (X_i cos + Y_i sin) + b_i (Y_i cos - X_i sin)
+//    with (cos, sin) of tau theta_i from a fixed table and (X_i, Y_i) the
+//    query pair rotated by (t0 - q_pos) theta_i once per chunk, every angle
+//    reduced in float64, so no rounding carries over from chunk to chunk.
+//    All lanes of one half read the same channel's 16 centroids (one
+//    32-byte row): a broadcast;
 //  * values, lane = channel pair (l, l + 64): the codebook value tiles hold
 //    both 4-bit indices of a lane in one byte per token, and one LDS dword
 //    per (centroid, lane) holds both channels' centroids, so lane l always
 //    reads bank l;
-//  * the (cos, sin) table of a chunk (64 pairs x 64 tokens) is shared by the
-//    4 heads and advanced by one complex multiplication per entry and chunk,
-//    re-anchored from float64 angles every 32 chunks;
-//  * outliers (CSR rows of one token over all heads) are filtered by the
-//    whole workgroup and enter as (val - centroid) corrections: to the
-//    chunk's scores for keys, to LDS channel sums for values.
+//  * outliers (CSR rows of one token over all heads) are compacted per wave
+//    to the entries of the workgroup's heads and enter as (val - centroid)
+//    corrections: to the chunk's scores for keys, to LDS channel sums for
+//    values.
 //
 // Each wave leaves an (o, m, l) partial per split, or the output when the
 // context is one split.
@@ -44,34 +46,65 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 constexpr int kD = kHeadDim;
-constexpr int kChunk = 64;      // tokens per chunk: one per lane on the key side
+constexpr int kChunk = 32;      // tokens per chunk: one value tile
 constexpr int kHeads = 4;       // KV heads per workgroup, one per wave
 constexpr int kPairs = kD / 2;
-constexpr int kResync = 32;     // chunks between exact re-anchorings of the table
+constexpr int kRingK = 16;      // compacted key outlier slots per wave
+constexpr int kResync = 32;     // chunks between exact evaluations of the query rotation
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct __align__(16) LutLds {
-  float2 e[kPairs][kChunk];        // (cos, sin) of (t0 + tau - p) theta_i       32 KB
-  uint16_t kt[kHeads][kD][16];     // key centroids, fp16 [head][channel][index]   16 KB
-  uint32_t vt[kHeads][16][64];     // value centroids: (index, l) -> C(l) | C(l+64) << 16
-  float qs[kHeads][kD];            // query * sm_scale * log2(e)
-  float scorr[kHeads][kChunk];     // key outlier corrections of the chunk's scores
-  float p[kHeads][kChunk];         // probabilities of the chunk
-  float vcorr[kHeads][kD];         // value outlier sums of the chunk
-  float2 estep[kPairs];            // (cos, sin) of kChunk * theta_i
-  double theta[kPairs];
-  uint2 ring[kHeads][64];          // per wave: outlier entries of its head group, compacted
+  float2 e[kPairs][kChunk];        // (cos, sin) of tau * theta_i, fixed                 16 KB
+  uint16_t kt[kHeads][kD][16];     // key centroids, fp16 [head][channel][index]         16 KB
+  uint32_t vt[kHeads][16][64];     // value centroids: (index, l) -> C(l) | C(l+64) << 16 16 KB
+  float2 qr[kHeads][kPairs];       // query pairs * sm_scale * log2(e), rotated to the chunk
+  union {                          // wave w only ever touches row w of either
+    float p[kHeads][kChunk];       // probabilities of the chunk (value phase)
+    uint32_t ring_k[kHeads][kRingK][2];   // compacted key outliers (key phase)
+  };
+  // Value outlier sums of the chunk.  Entries [h][0, 32) double as head h's
+  // key outlier corrections of the chunk's scores: the two are live in turn
+  // (key phase up to the softmax, then value phase), each is cleared by the
+  // head's wave after use, and barriers order every clear before the next use.
+  float vcorr[kHeads][kD];
 };
+// three workgroups per CU: the 160 KB of LDS is allocated in units of 1280 bytes
+static_assert(sizeof(LutLds) <= 42 * 1280, "three workgroups per CU");
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// the pair (x[l], x[l ^ 16]) and (x[l], x[l ^ 32]) by the gfx950 row swaps
+__device__ __forceinline__ float swap16(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  auto c = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  return __builtin_bit_cast(float, (int)((__lane_id() & 16) ? c[0] : c[1]));
+}
+// x of lane l ^ 32
+__device__ __forceinline__ float swap_halves(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  auto c = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __builtin_bit_cast(float, (int)((__lane_id() & 32) ? c[0] : c[1]));
+}
+// maximum / sum over the wave: rotations within each row of 16, then rows
 __device__ __forceinline__ float wave_max(float x) {
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
+  x = fmaxf(x, dpp_f<0x128>(x));   // row_ror:8
+  x = fmaxf(x, dpp_f<0x124>(x));   // row_ror:4
+  x = fmaxf(x, dpp_f<0x122>(x));   // row_ror:2
+  x = fmaxf(x, dpp_f<0x121>(x));   // row_ror:1
+  x = fmaxf(x, swap16(x));
+  return fmaxf(x, swap_halves(x));
 }
 __device__ __forceinline__ float wave_sum(float x) {
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+  x += dpp_f<0x128>(x);
+  x += dpp_f<0x124>(x);
+  x += dpp_f<0x122>(x);
+  x += dpp_f<0x121>(x);
+  x += swap16(x);
+  return x + swap_halves(x);
 }
-
 // (cos, sin) of dt * theta, the angle formed and reduced in float64
 __device__ __forceinline__ float2 rope_cs(double theta, int64_t dt) {
   const double ang = (double)dt * theta;
@@ -90,7 +123,7 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
 }
 
 template <bool ROPE, bool KOUT, bool VOUT>
-__global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
   __shared__ LutLds S;
   const DevTensor& K = a.k;
   const DevTensor& V = a.v;
@@ -107,6 +140,7 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
   const int b = r / a.splits, split = r % a.splits;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  const int tau = lane & 31, half = lane >> 5;   // key side: token, half of the pairs
   const int tid = threadIdx.x;
   const int h = hg * kHeads + wave;
   const bool head_ok = h < Hkv;                  // wave-uniform
@@ -129,27 +163,47 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       S.vt[wave][e][lane] = (uint32_t)vc[lane * 16 + e] | ((uint32_t)vc[(lane + 64) * 16 + e] << 16);
-    const uint16_t* qg = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.sh.Hq + h) * kD;
-    S.qs[wave][lane] = elem2f(qg[lane], a.sh.kv_bf16) * sm2;
-    S.qs[wave][lane + 64] = elem2f(qg[lane + 64], a.sh.kv_bf16) * sm2;
   }
-  if constexpr (ROPE) {
-    if (tid < kPairs) S.theta[tid] = pow((double)a.rope_base, -2.0 * (double)tid / (double)kD);
+  // thread (head qw, pair qi) owns one query pair: q * sm_scale * log2(e)
+  const int qw = tid >> 6, qi = tid & 63, qh = hg * kHeads + qw;
+  float qx = 0.f, qy = 0.f;
+  if (qh < Hkv) {
+    const uint16_t* qg = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.sh.Hq + qh) * kD;
+    qx = elem2f(qg[qi], a.sh.kv_bf16) * sm2;
+    qy = elem2f(qg[qi + kPairs], a.sh.kv_bf16) * sm2;
   }
-  for (int i = tid; i < kHeads * kChunk; i += 256) (&S.scorr[0][0])[i] = 0.f;
-  for (int i = tid; i < kHeads * kD; i += 256) (&S.vcorr[0][0])[i] = 0.f;
-  __syncthreads();
-  auto anchor = [&](int t0) {   // exact (cos, sin) of the chunk starting at t0
-    for (int idx = tid; idx < kPairs * kChunk; idx += 256) {
-      const int i = idx / kChunk, tau = idx % kChunk;
-      S.e[i][tau] = rope_cs(S.theta[i], (int64_t)t0 + tau - qpos);
+  double theta = 0.0;                            // theta of pair qi
+  if constexpr (ROPE) theta = pow((double)a.rope_base, -2.0 * (double)qi / (double)kD);
+  // The query pair rotated by (t0 - q_pos) theta: then the key of token
+  // t0 + tau needs only the rotation by tau theta from the fixed table.  The
+  // rotation advances by one complex multiplication per chunk and is
+  // evaluated exactly from a float64 angle every kResync chunks.
+  float2 rot = make_float2(1.f, 0.f), rstep = make_float2(1.f, 0.f);
+  if constexpr (ROPE) rstep = rope_cs(theta, kChunk);
+  auto set_q = [&](int ci) {
+    if constexpr (ROPE) {
+      if (ci % kResync == 0) {
+        rot = rope_cs(theta, (int64_t)t_begin + (int64_t)ci * kChunk - qpos);
+      } else {
+        rot = make_float2(rot.x * rstep.x - rot.y * rstep.y, rot.x * rstep.y + rot.y * rstep.x);
+      }
+      S.qr[qw][qi] = make_float2(qx * rot.x + qy * rot.y, qy * rot.x - qx * rot.y);
+    } else {
+      S.qr[qw][qi] = make_float2(qx, qy);
     }
   };
   if constexpr (ROPE) {
-    if (tid < kPairs) S.estep[tid] = rope_cs(S.theta[tid], kChunk);
-    anchor(t_begin);
-    __syncthreads();
+    // wave w fills pairs 16w .. 16w + 15; lane (tau, half) two of them per step
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = 16 * wave + 2 * k + half;
+      const double th = __shfl(theta, i, 64);
+      S.e[i][tau] = rope_cs(th, tau);
+    }
   }
+  set_q(0);
+  for (int i = tid; i < kHeads * kD; i += 256) (&S.vcorr[0][0])[i] = 0.f;
+  __syncthreads();
 
   // ---- per-wave state ------------------------------------------------------------
   float m_run = -INFINITY, l_lane = 0.f;
@@ -157,94 +211,90 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
   const uint8_t* krows = K.codes + ((int64_t)b * Hkv + (head_ok ? h : 0)) * Tcap * 64;
   const uint8_t* vtiles = V.codes + ((int64_t)b * Hkv + (head_ok ? h : 0)) * Tcap * 64;
 
-  // codes of one chunk: key row of token (lane), value bytes of channel pair (lane)
-  u32x4 kc[4], vc[4];
-  auto load_chunk = [&](int t0, u32x4* kk, u32x4* vv) {
-    const int tk = min(t0 + lane, nctx - 1);          // clamp past the end (masked later)
-    const u32x4* kr = reinterpret_cast<const u32x4*>(krows + (int64_t)tk * 64);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kk[i] = kr[i];
-    // two tiles of 32 tokens; lane owns 32 bytes of each (a tile past the
-    // range is not read: its probabilities are zero)
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      if (t0 + 32 * tt < t_end) {
-        const u32x4* vr = reinterpret_cast<const u32x4*>(vtiles + (int64_t)(t0 + 32 * tt) * 64 + lane * 32);
-        vv[2 * tt] = vr[0];
-        vv[2 * tt + 1] = vr[1];
-      } else {
-        vv[2 * tt] = u32x4{0u, 0u, 0u, 0u};
-        vv[2 * tt + 1] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+  // Codes of one chunk: segments 2 half and 2 half + 1 (32 bytes) of the key
+  // row of token tau, and the 32 value bytes of channel pair (lane).  Every
+  // load is unconditional, with addresses clamped into the cache, so that
+  // the compiler can count outstanding loads exactly: past the end, keys are
+  // masked and values meet zero probabilities.  The key codes of chunk
+  // ci + 1 load during the value phase of chunk ci; the value codes of a
+  // chunk load at its start.
+  const int last_tile = (nctx - 1) & ~31;
+  auto load_k = [&](int t0, u32x4* kk) {
+    const int tk = min(t0 + tau, nctx - 1);
+    const u32x4* kr = reinterpret_cast<const u32x4*>(krows + (int64_t)tk * 64) + 2 * half;
+    kk[0] = kr[0];
+    kk[1] = kr[1];
   };
-  if (head_ok && n_chunks > 0) load_chunk(t_begin, kc, vc);
+  auto load_v = [&](int t0, u32x4* vv) {
+    const int ts = min(t0, last_tile);
+    const u32x4* vr = reinterpret_cast<const u32x4*>(vtiles + (int64_t)ts * 64 + lane * 32);
+    vv[0] = vr[0];
+    vv[1] = vr[1];
+  };
+  u32x4 kc[2];
+  load_k(t_begin, kc);
 
   // Outlier entries of a chunk: the CSR rows of its tokens are contiguous
-  // (k entries per token), read as 16-byte vectors of 8 entries.  Thread j
-  // takes vectors j and j + 256; a vector may run up to 7 entries past the
-  // chunk's rows (still inside the allocation: every outlier array is
-  // followed by another region), and those entries are skipped.
-  constexpr int kVec = 2;                        // vectors per thread and tensor
+  // (k entries per token), read as 16-byte vectors of 8 entries, vector j by
+  // thread j (32 tokens x at most 64 entries: 256 vectors).  A vector may run
+  // up to 7 entries past the chunk's rows (still inside the allocation: every
+  // outlier array is followed by another region); vectors past the chunk
+  // re-read its last one.  Entries past the chunk fail the e < n_ent test.
   struct OutVec { u32x4 col, val; };
-  auto load_out = [&](const DevTensor& T, int64_t row0, int nt, OutVec* o) {
+  auto load_out = [&](const DevTensor& T, int64_t row0, int nt, OutVec& o) {
     const int64_t e0 = row0 * T.k_out;
     const int nv = (nt * T.k_out + 7) / 8;
     const u32x4* cv = reinterpret_cast<const u32x4*>(T.col + e0);
     const u32x4* vv = reinterpret_cast<const u32x4*>(T.val + e0);
-#pragma unroll
-    for (int u = 0; u < kVec; ++u) {
-      const int vi = tid + 256 * u;
-      if (vi < nv) {
-        o[u].col = cv[vi];
-        o[u].val = vv[vi];
-      } else {
-        o[u].col = u32x4{0u, 0u, 0u, 0u};
-        o[u].val = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+    const int vi = min(tid, nv - 1);
+    o.col = cv[vi];
+    o.val = vv[vi];
   };
   // Calls f(ww, tau, c, dense index, value) for the entries of this
   // workgroup's heads.  Each wave compacts the matching entries among those
   // its threads loaded into its ring (ballot + lane count) and works through
-  // the ring once it holds a wave's worth: about one entry in eight belongs
-  // to the workgroup, so the per-entry work then runs on full waves.
-  auto for_entries = [&](const DevTensor& T, int nt, const OutVec* o, auto&& f) {
+  // the ring once it is full: about one entry in eight belongs to the
+  // workgroup, so the per-entry work then runs on a ring's worth of lanes.
+  // A step that matches more entries than the ring holds applies them in
+  // place.
+  auto for_entries = [&](const DevTensor& T, int nt, const OutVec& o, uint32_t (*ring)[2],
+                         int slots, auto&& f) {
     const int ko = T.k_out;
     const int n_ent = nt * ko;
     const float inv_k = 1.0f / (float)ko;
+    auto apply = [&](uint32_t col, int e, uint32_t valbits) {
+      // token of entry e: floor(e / k), exact in float for e < 2^16
+      const int te = (int)(((float)e + 0.5f) * inv_k);
+      const int ww = (int)((col & 0xfffu) >> 7) - hg * kHeads;
+      f(ww, te, (int)(col & (kD - 1)), col >> 12, h2f((uint16_t)valbits));
+    };
     int qn = 0;                                    // ring fill, wave-uniform
     auto drain = [&]() {
       __builtin_amdgcn_wave_barrier();             // ring writes of this wave land first
-      if (lane < qn) {
-        const uint2 r = S.ring[wave][lane];
-        const uint32_t col = r.x & 0xffffu;
-        const int e = (int)(r.x >> 16);
-        // token of entry e: floor(e / k), exact in float for e < 2^16
-        const int tau = (int)(((float)e + 0.5f) * inv_k);
-        const int ww = (int)((col & 0xfffu) >> 7) - hg * kHeads;
-        f(ww, tau, (int)(col & (kD - 1)), col >> 12, h2f((uint16_t)r.y));
-      }
+      if (lane < qn) apply(ring[lane][0] & 0xffffu, (int)(ring[lane][0] >> 16), ring[lane][1]);
       __builtin_amdgcn_wave_barrier();             // reads done before the ring refills
       qn = 0;
     };
+    const uint32_t cw[4] = {o.col.x, o.col.y, o.col.z, o.col.w};
+    const uint32_t vw[4] = {o.val.x, o.val.y, o.val.z, o.val.w};
 #pragma unroll
-    for (int u = 0; u < kVec; ++u) {
-      const uint32_t cw[4] = {o[u].col.x, o[u].col.y, o[u].col.z, o[u].col.w};
-      const uint32_t vw[4] = {o[u].val.x, o[u].val.y, o[u].val.z, o[u].val.w};
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int e = 8 * (tid + 256 * u) + x;     // entry index within the chunk
-        const uint32_t col = (cw[x >> 1] >> (16 * (x & 1))) & 0xffffu;
-        // head of the flat index (col & 0xfff) >> 7; its group: bits 9-11
-        const bool hit = e < n_ent && ((col >> 9) & 7u) == (uint32_t)hg;
-        const uint64_t mask = __ballot(hit);
-        const int cnt = __popcll(mask);
-        if (qn + cnt > 64) drain();
+    for (int x = 0; x < 8; ++x) {
+      const int e = 8 * tid + x;                   // entry index within the chunk
+      const uint32_t col = (cw[x >> 1] >> (16 * (x & 1))) & 0xffffu;
+      // head of the flat index (col & 0xfff) >> 7; its group: bits 9-11
+      const bool hit = e < n_ent && ((col >> 9) & 7u) == (uint32_t)hg;
+      const uint32_t valbits = (vw[x >> 1] >> (16 * (x & 1))) & 0xffffu;
+      const uint64_t mask = __ballot(hit);
+      const int cnt = __popcll(mask);
+      if (slots > 0 && qn + cnt > slots) drain();
+      if (cnt > slots) {                           // more than the ring holds: in place
+        if (hit) apply(col, e, valbits);
+      } else {
         if (hit) {
           const int slot = qn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-          S.ring[wave][slot] = make_uint2(col | ((uint32_t)e << 16), (vw[x >> 1] >> (16 * (x & 1))) & 0xffffu);
+          ring[slot][0] = col | ((uint32_t)e << 16);
+          ring[slot][1] = valbits;
         }
         qn += cnt;
       }
@@ -257,24 +307,25 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
     const int nt = min(kChunk, t_end - t0);      // tokens of this chunk
     const int64_t row0 = (int64_t)b * Tcap + t0; // CSR row of token t0
 
-    OutVec ko_v[kVec], vo_v[kVec];
+    OutVec ko_v, vo_v;
     if constexpr (KOUT) load_out(K, row0, nt, ko_v);
-    if constexpr (VOUT) load_out(V, row0, nt, vo_v);
-    u32x4 kn[4], vn[4];
-    if (head_ok && ci + 1 < n_chunks) load_chunk(t0 + kChunk, kn, vn);
+    u32x4 vc[2], kn[2];
+    load_v(t0, vc);
 
-    // ---- keys: lane = token (dense part) ------------------------------------------
+    // ---- keys: lanes (tau, half), pairs i = 32m + 16 half + 8qq + e --------------------
     float s = 0.f;
     if (head_ok) {
-      const uint32_t kw[16] = {kc[0].x, kc[0].y, kc[0].z, kc[0].w, kc[1].x, kc[1].y, kc[1].z, kc[1].w,
-                               kc[2].x, kc[2].y, kc[2].z, kc[2].w, kc[3].x, kc[3].y, kc[3].z, kc[3].w};
+      // segment 2 half + qq: dword 4qq + m' holds channel 32m' + 8(2 half + qq) + e
+      const uint32_t kw[8] = {kc[0].x, kc[0].y, kc[0].z, kc[0].w, kc[1].x, kc[1].y, kc[1].z, kc[1].w};
       // Centroid lookups: the byte offset of S.kt[wave][c][code] is
-      // c * 32 (a constant of the unrolled loop) + wave * 4096 + code * 2.
-      // The codes of a dword are first spread as code * 2 into the bytes of
-      // two words (even and odd nibbles); one byte permute then joins a
-      // code byte with the wave's byte into the offset.
+      // c * 32 + wave * 4096 + code * 2, with c * 32 = (a constant of the
+      // unrolled loop) + 512 half.  The codes of a dword are first spread as
+      // code * 2 into the bytes of two words (even and odd nibbles); one byte
+      // permute then joins a code byte with the lane's (wave, half) byte.
       const uint8_t* ktb = reinterpret_cast<const uint8_t*>(&S.kt[0][0][0]);
-      const uint32_t wvb = (uint32_t)wave << 12;
+      const uint32_t wvb = (uint32_t)(16 * wave + 2 * half) << 8;
+      const float2* qb = &S.qr[wave][16 * half];
+      const float2* eb = &S.e[16 * half][tau];
       auto spread = [](uint32_t wd, uint32_t out[2]) {
         out[0] = (wd << 1) & 0x1e1e1e1eu;     // nibbles 0, 2, 4, 6
         out[1] = (wd >> 3) & 0x1e1e1e1eu;     // nibbles 1, 3, 5, 7
@@ -283,86 +334,76 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
         const uint32_t off = __builtin_amdgcn_perm(x[e & 1], wvb, 0x0c0c0100u | (uint32_t)(4 + (e >> 1)));
         return (float)*reinterpret_cast<const _Float16*>(ktb + c * 32 + off);
       };
-      // dword 4q + m of the row holds channels 32m + 8q + e (e = 0..7)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           uint32_t xa[2], xb[2];
-          spread(kw[4 * q + m], xa);
-          spread(kw[4 * q + m + 2], xb);
+          spread(kw[4 * qq + m], xa);
+          spread(kw[4 * qq + m + 2], xb);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int i = 32 * m + 8 * q + e;          // pair (i, i + 64)
-            const float av = cent(xa, e, i);
-            const float bv = cent(xb, e, i + kPairs);
-            const float x = S.qs[wave][i], y = S.qs[wave][i + kPairs];
+            const int ic = 32 * m + 8 * qq + e;        // pair (ic + 16 half) less 16 half
+            const float av = cent(xa, e, ic);
+            const float bv = cent(xb, e, ic + kPairs);
+            const float2 q2 = qb[ic];
             if constexpr (ROPE) {
-              const float2 cs = S.e[i][lane];
-              s = __builtin_fmaf(av, x * cs.x + y * cs.y, s);
-              s = __builtin_fmaf(bv, y * cs.x - x * cs.y, s);
+              const float2 cs = eb[ic * kChunk];
+              s = __builtin_fmaf(av, q2.x * cs.x + q2.y * cs.y, s);
+              s = __builtin_fmaf(bv, q2.y * cs.x - q2.x * cs.y, s);
             } else {
-              s = __builtin_fmaf(av, x, s);
-              s = __builtin_fmaf(bv, y, s);
+              s = __builtin_fmaf(av, q2.x, s);
+              s = __builtin_fmaf(bv, q2.y, s);
             }
           }
         }
+      s += swap_halves(s);                           // both halves of token tau
     }
 
     // ---- key outliers: (value - centroid) * coefficient into the scores ----------------
     if constexpr (KOUT) {
-      for_entries(K, nt, ko_v, [&](int ww, int tau, int c, uint32_t code, float val) {
+      for_entries(K, nt, ko_v, S.ring_k[wave], kRingK,
+                  [&](int ww, int te, int c, uint32_t code, float val) {
         const float delta = val - h2f(S.kt[ww][c][code]);
+        const int i = c & (kPairs - 1);
+        const float2 q2 = S.qr[ww][i];
         float coef;
         if constexpr (ROPE) {
-          const int i = c & (kPairs - 1);
-          const float2 cs = S.e[i][tau];
-          const float x = S.qs[ww][i], y = S.qs[ww][i + kPairs];
-          coef = c < kPairs ? x * cs.x + y * cs.y : y * cs.x - x * cs.y;
+          const float2 cs = S.e[i][te];
+          coef = c < kPairs ? q2.x * cs.x + q2.y * cs.y : q2.y * cs.x - q2.x * cs.y;
         } else {
-          coef = S.qs[ww][c];
+          coef = c < kPairs ? q2.x : q2.y;
         }
-        atomicAdd(&S.scorr[ww][tau], delta * coef);
+        atomicAdd(&S.vcorr[ww][te], delta * coef);    // key correction of token te
       });
     }
-    if constexpr (KOUT || VOUT || ROPE) __syncthreads();   // scores complete; e consumed
+    if constexpr (KOUT || ROPE) __syncthreads();   // scores complete; rotated queries consumed
 
-    // ---- next chunk's rotation table ---------------------------------------------------
-    if constexpr (ROPE) {
-      if (ci + 1 < n_chunks) {
-        if ((ci + 1) % kResync == 0) {
-          anchor(t0 + kChunk);
-        } else {
-          for (int idx = tid; idx < kPairs * kChunk; idx += 256) {
-            const int i = idx / kChunk, tau = idx % kChunk;
-            const float2 e0 = S.e[i][tau], st = S.estep[i];
-            S.e[i][tau] = make_float2(e0.x * st.x - e0.y * st.y, e0.x * st.y + e0.y * st.x);
-          }
-        }
-      }
-    }
+    // value outliers of this chunk, key codes and rotated queries of the next one
+    if constexpr (VOUT) load_out(V, row0, nt, vo_v);
+    load_k(t0 + kChunk, kn);
+    if constexpr (ROPE) set_q(ci + 1);
 
     if (head_ok) {
       // ---- online softmax ----------------------------------------------------------
       if constexpr (KOUT) {
-        s += S.scorr[wave][lane];
-        S.scorr[wave][lane] = 0.f;
+        s += S.vcorr[wave][tau];                   // key correction; both halves read first
+        if (half == 0) S.vcorr[wave][tau] = 0.f;
       }
-      if (lane >= nt) s = -INFINITY;
+      if (tau >= nt) s = -INFINITY;
       const float m_new = fmaxf(m_run, wave_max(s));
       const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      const float pt = lane < nt ? __builtin_amdgcn_exp2f(s - m_new) : 0.f;
-      l_lane = l_lane * alpha + pt;
+      const float pt = tau < nt ? __builtin_amdgcn_exp2f(s - m_new) : 0.f;
+      l_lane = l_lane * alpha + (half == 0 ? pt : 0.f);
       m_run = m_new;
-      S.p[wave][lane] = pt;
+      if (half == 0) S.p[wave][tau] = pt;
       acc0 *= alpha;
       acc1 *= alpha;
       // LDS accesses of one wave complete in order: the reads below see p
       __builtin_amdgcn_wave_barrier();
 
       // ---- values: lane = channel pair ----------------------------------------------
-      const uint32_t vw[16] = {vc[0].x, vc[0].y, vc[0].z, vc[0].w, vc[1].x, vc[1].y, vc[1].z, vc[1].w,
-                               vc[2].x, vc[2].y, vc[2].z, vc[2].w, vc[3].x, vc[3].y, vc[3].z, vc[3].w};
+      const uint32_t vw[8] = {vc[0].x, vc[0].y, vc[0].z, vc[0].w, vc[1].x, vc[1].y, vc[1].z, vc[1].w};
       // byte offset of S.vt[wave][code][lane] = lane * 4 + (16 wave + code) * 256:
       // the code bytes of a dword (16 wave added in every byte) are joined
       // with the lane's byte by one byte permute per lookup
@@ -370,7 +411,7 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
       const uint32_t l4 = (uint32_t)lane << 2;
       const uint32_t wpat = (uint32_t)wave * 0x10101010u;
 #pragma unroll
-      for (int d4 = 0; d4 < 16; ++d4) {
+      for (int d4 = 0; d4 < 8; ++d4) {
         const f32x4 p4 = *reinterpret_cast<const f32x4*>(&S.p[wave][4 * d4]);
         const uint32_t wd = vw[d4];
         const uint32_t xlo = (wd & 0x0f0f0f0fu) | wpat;
@@ -389,10 +430,11 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
     // ---- value outliers: p * (value - centroid) into LDS channel sums ------------------
     if constexpr (VOUT) {
       __syncthreads();                               // p of every head complete
-      for_entries(V, nt, vo_v, [&](int ww, int tau, int c, uint32_t code, float val) {
+      for_entries(V, nt, vo_v, S.ring_k[wave], 0,   // no ring: p is live
+                  [&](int ww, int te, int c, uint32_t code, float val) {
         const uint32_t cc = S.vt[ww][code][c & (kPairs - 1)];
         const float dense = c < kPairs ? half_lo(cc) : half_hi(cc);
-        atomicAdd(&S.vcorr[ww][c], S.p[ww][tau] * (val - dense));
+        atomicAdd(&S.vcorr[ww][c], S.p[ww][te] * (val - dense));
       });
       __syncthreads();                               // sums complete
       if (head_ok) {
@@ -401,15 +443,15 @@ __global__ __launch_bounds__(256, 2) void dec_lut_kernel(DecodeArgs a) {
         S.vcorr[wave][lane] = 0.f;
         S.vcorr[wave][lane + 64] = 0.f;
       }
+      if constexpr (KOUT) __syncthreads();           // cleared before the next key corrections
     }
-    // next table complete; score corrections read and cleared before the
-    // next chunk adds to them (with value outliers, their barriers order this)
+    // next rotated queries complete; score corrections read and cleared
+    // before the next chunk adds to them (with value outliers, their
+    // barriers order this)
     if constexpr ((ROPE || KOUT) && !VOUT) __syncthreads();
 
-    if (head_ok && ci + 1 < n_chunks) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { kc[i] = kn[i]; vc[i] = vn[i]; }
-    }
+    for (int i = 0; i < 2; ++i) kc[i] = kn[i];
   }
 
   // ---- partial of this split ---------------------------------------------------------
@@ -439,7 +481,7 @@ void launch_r(const DecodeArgs& a, unsigned grid, hipStream_t s) {
 }  // namespace
 
 bool lut_config_supported(const kvq_config& c, int k_out_k, int k_out_v) {
-  // a chunk's outlier rows are read as 2 vectors of 8 entries per thread:
+  // a chunk's outlier rows are read as one vector of 8 entries per thread:
   // at most 64 outliers per token
   return c.k.quantizer == KVQ_QUANT_CODEBOOK && c.v.quantizer == KVQ_QUANT_CODEBOOK &&
          c.k.bits == 4 && c.v.bits == 4 && c.n_q_heads == c.n_kv_heads &&

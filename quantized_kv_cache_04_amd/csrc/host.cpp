@@ -388,18 +388,20 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   const int32_t path = kvq_decode_path(cfg);
   if (path < 0) return path;
   if (path == KVQ_PATH_LUT) {
-    // ranges of whole 64-token chunks; a workgroup serves 4 KV heads, so
-    // about 512 workgroups take 512 / (batch * ceil(Hkv / 4)) ranges per
-    // sequence, each at least 4 chunks long
-    const int64_t nchunks = (a.n_ctx + 63) / 64;
+    // ranges of whole 32-token chunks; a workgroup serves 4 KV heads and
+    // three of them fit on a CU, so about 768 workgroups take
+    // 768 / (batch * ceil(Hkv / 4)) ranges per sequence, each at least 4
+    // chunks long
+    constexpr int64_t kLutWorkgroups = 768;
+    const int64_t nchunks = nblocks;
     const int64_t units = (int64_t)cfg->batch * ((cfg->n_kv_heads + 3) / 4);
-    int64_t r = (kTargetWorkgroups + units - 1) / units;
+    int64_t r = (kLutWorkgroups + units - 1) / units;
     if (r > nchunks / 4) r = nchunks / 4;
     if (cfg->decode_splits > 0 && r > cfg->decode_splits) r = cfg->decode_splits;
     if (r > L.S_max) r = L.S_max;
     if (r < 1) r = 1;
     const int64_t per = (nchunks + r - 1) / r;
-    a.blocks_per_split = (int)(2 * per);
+    a.blocks_per_split = (int)per;
     a.splits = (int)((nchunks + per - 1) / per);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);

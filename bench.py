@@ -170,7 +170,9 @@ def main():
     w = make_workload(args.config, ctx=args.ctx)
     serving = args.config == 5
     K, W = args.steps, args.warmup
-    max_ctx = w.ctx + (K + W + 1 if serving else 0)
+    # warm-up, the timed steps, then as many instrumented steps (serving: one
+    # token per sequence appended at each)
+    max_ctx = w.ctx + (W + 2 * K + 1 if serving else 0)
     cfg = kvq.config_from_workload(w, max_ctx=max_ctx, decode_path=args.path,
                                    decode_splits=args.splits)
     stream = torch.cuda.Stream()
@@ -190,7 +192,7 @@ def main():
         q = inputs["q"]
         del inputs["k"], inputs["v"]
         if serving:
-            steps_tok = [make_step_tokens(w, s, 1, dev) for s in range(W + K)]
+            steps_tok = [make_step_tokens(w, s, 1, dev) for s in range(W + 2 * K)]
     torch.cuda.synchronize()
     log(f"cache built: {copies} cop{'y' if copies == 1 else 'ies'} x {payload0 / 1e9:.3f} GB payload")
 
@@ -211,47 +213,62 @@ def main():
 
     k_group = w.k.get("group_size", 0) if w.k.get("layout") == "per_channel" else 0
 
-    def step(i, timed_idx=None):
+    inst_bytes = []
+
+    def step(i, inst=None):
+        """One step; ``inst`` = index of an instrumented step, which records
+        HIP events around the whole step, the decode call and the streaming
+        kernel."""
         c = caches[i % copies]
-        if timed_idx is not None:
-            st_s[timed_idx].record(stream)
+        if inst is not None:
+            st_s[inst].record(stream)
         if serving:
             kn, vn, qn = steps_tok[i]
             c.append(kn, vn, stream=stream)
-            if timed_idx is not None:
+            if inst is not None:
                 flush_step.append(bool(k_group) and c.n_ctx % k_group == 0)
             qq = qn
         else:
             qq = q
-        if timed_idx is not None:
-            dec_s[timed_idx].record(stream)
-            kvq.set_decode_events(ker_s[timed_idx], ker_e[timed_idx])
+        if inst is not None:
+            dec_s[inst].record(stream)
+            kvq.set_decode_events(ker_s[inst], ker_e[inst])
         c.decode(qq, out=out, stream=stream)
-        if timed_idx is not None:
-            dec_e[timed_idx].record(stream)
-            st_e[timed_idx].record(stream)
+        if inst is not None:
+            dec_e[inst].record(stream)
+            st_e[inst].record(stream)
+            inst_bytes.append(kvq.cache_bytes(cfg, c.n_ctx))
+        else:
             step_bytes.append(kvq.cache_bytes(cfg, c.n_ctx))
 
     with torch.cuda.stream(stream):
         for i in range(W):
             step(i)
     torch.cuda.synchronize()
+    step_bytes.clear()
+    # the timed region: K plain steps
     t_start, t_end = ev(), ev()
     with torch.cuda.stream(stream):
         t_start.record(stream)
         for k in range(K):
-            step(W + k, k)
+            step(W + k)
         t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / K
+    bytes_avg = sum(step_bytes) / K
+    value = bytes_avg / (ms_step * 1e-3) / 1e9
+    # then K instrumented steps for the kernel-level figures (their events
+    # would lengthen the timed steps)
+    with torch.cuda.stream(stream):
+        for k in range(K):
+            step(W + K + k, k)
+    torch.cuda.synchronize()
     dec_ms = [a.elapsed_time(b) for a, b in zip(dec_s, dec_e)]
     ker_ms = sorted(a.elapsed_time(b) for a, b in zip(ker_s, ker_e))
     dec_avg = sum(dec_ms) / K
     ker_avg = sum(ker_ms) / K
-    bytes_avg = sum(step_bytes) / K
-    value = bytes_avg / (ms_step * 1e-3) / 1e9
-    achieved = bytes_avg / (ker_avg * 1e-3) / 1e9
+    achieved = (sum(inst_bytes) / K) / (ker_avg * 1e-3) / 1e9
     path = kvq.decode_path(cfg)
     kernel = DECODE_KERNELS[path]
     wl = CONFIG_NAME(w)
@@ -303,7 +320,7 @@ def main():
                      "traffic": traffic,
                      "kernel": kernel, "avg_launch_us": round(ker_avg * 1e3, 2),
                      "decode_call_us": round(dec_avg * 1e3, 2),
-                     "algorithmic_bytes_per_launch": int(bytes_avg)},
+                     "algorithmic_bytes_per_launch": int(sum(inst_bytes) / K)},
         "cpu_baseline": cpu,
     }
     if cycle is not None:

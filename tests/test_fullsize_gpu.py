@@ -61,7 +61,7 @@ def test_full_size_sampled_slices(cfg_id, ctx, slices):
     w = make_workload(cfg_id, ctx=ctx)
     print(f"[fullsize] cfg={cfg_id} B={w.batch} Hkv={w.n_kv_heads} T={w.ctx} "
           f"path={kvq.decode_path(kvq.config_from_workload(w))}", flush=True)
-    extra = 64 if cfg_id == 5 else 0                 # bench.py's serving headroom
+    extra = 518 if cfg_id == 5 else 0   # bench.py default serving headroom: 5 + 2 x 256 + 1
     inputs, cache, out = _full_cache(w, extra)
     g = w.gqa
     for b, h in slices:

@@ -8,7 +8,9 @@ counts follow the Memory-killer page's section 1.2 (2 * L * H * D * S).
 Quantized formats count packed codes, fp16 scale (+ zero) per group, the
 fp16 tail of an unfinished per-channel group, the CSR outliers (4-byte row
 pointer + 2-byte column + 2-byte value per kept entry) and the fp16
-codebooks.
+codebooks.  With an attention sink of S tokens (KVQuant page, "Attention
+Sink"), the first min(S, n) tokens cost their raw fp16/bf16 bytes and the
+format applies to the remaining n - min(S, n) tokens.
 """
 from __future__ import annotations
 
@@ -42,7 +44,9 @@ def tensor_payload(fmt: Dict, *, batch: int, n_kv_heads: int, head_dim: int, n_c
 
 
 def payload_bytes(k_fmt: Dict, v_fmt: Dict, *, batch: int, n_kv_heads: int, head_dim: int,
-                  n_ctx: int, n_layers: int = 1, kv_dtype: str = "f16") -> int:
-    kw = dict(batch=batch, n_kv_heads=n_kv_heads, head_dim=head_dim, n_ctx=n_ctx,
+                  n_ctx: int, n_layers: int = 1, kv_dtype: str = "f16", sink: int = 0) -> int:
+    s = min(int(sink), n_ctx)
+    kw = dict(batch=batch, n_kv_heads=n_kv_heads, head_dim=head_dim, n_ctx=n_ctx - s,
               kv_dtype=kv_dtype)
-    return n_layers * (tensor_payload(k_fmt, **kw) + tensor_payload(v_fmt, **kw))
+    raw = batch * n_kv_heads * s * head_dim * ESIZE[kv_dtype]
+    return n_layers * (tensor_payload(k_fmt, **kw) + tensor_payload(v_fmt, **kw) + 2 * raw)

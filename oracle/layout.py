@@ -264,3 +264,15 @@ def from_bits(b: np.ndarray, kv_dtype: str) -> np.ndarray:
     if kv_dtype == "f16":
         return b.view(np.float16).astype(np.float32)
     return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def sink_region(x: np.ndarray, sink: int, *, kv_dtype: str) -> np.ndarray:
+    """Byte image of one tensor's attention-sink region: [B, H, sink, d] raw
+    fp16/bf16 bits of tokens [0, min(sink, T)) of ``x`` (float32 [B, T, H, d]
+    holding fp16/bf16 values), zero beyond."""
+    x = np.asarray(x, dtype=np.float32)
+    B, T, H, d = x.shape
+    s = min(int(sink), T)
+    out = np.zeros((B, H, int(sink), d), dtype=np.uint16)
+    out[:, :, :s, :] = to_bits(np.transpose(x[:, :s], (0, 2, 1, 3)), kv_dtype)
+    return out

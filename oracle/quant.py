@@ -239,3 +239,27 @@ def encode_tensor(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None) -> Dict
         out["deq"] = deq
         return out
     raise ValueError(layout)
+
+
+def encode_with_sink(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None,
+                     sink: int = 0) -> Dict:
+    """Bulk-encode one cache tensor whose first ``sink`` tokens are an
+    attention sink (KVQuant page, "Attention Sink": the keys and values of
+    the first few tokens, which draw very high attention, are kept in full
+    precision at quantization and inference time; ``num_sink_tokens``).
+
+    Reading: tokens [0, s), s = min(sink, T), keep their fp16/bf16 values and
+    are attended exactly; tokens [s, T) form an ordinary quantized cache of
+    their own, encoded by ``encode_tensor`` as a sequence that starts at
+    token s (so per-channel key groups start at token s).  Positions (RoPE)
+    stay absolute.  Returns ``sink`` float64 [B, H, s, d] (the raw prefix),
+    ``rest`` (the encoding of the quantized tokens, or None when every token
+    is in the sink) and ``deq`` float64 [B, H, T, d] (what attention sees).
+    """
+    x = np.asarray(x, dtype=F32)
+    B, T, H, d = x.shape
+    s = min(int(sink), T)
+    pre = np.transpose(x[:, :s], (0, 2, 1, 3)).astype(np.float64)
+    rest = encode_tensor(x[:, s:], fmt, codebook) if T > s else None
+    deq = pre if rest is None else np.concatenate([pre, rest["deq"]], axis=2)
+    return {"sink": pre, "rest": rest, "deq": deq}

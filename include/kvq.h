@@ -138,6 +138,16 @@ typedef struct kvq_config {
   int32_t decode_path;    /* KVQ_PATH_AUTO, KVQ_PATH_VALU or KVQ_PATH_MFMA    */
   kvq_tensor_format k;    /* key format                                      */
   kvq_tensor_format v;    /* value format (PER_TOKEN only)                   */
+  int32_t sink_tokens;    /* attention sink [KVQuant page, Attention Sink]:
+                             tokens [0, sink_tokens) of every sequence keep
+                             their kv_dtype keys and values and are attended
+                             exactly; the formats apply to the later tokens,
+                             which form a quantized cache that starts at token
+                             sink_tokens (per-channel key groups start there).
+                             A position threshold (quantize only positions
+                             >= N [NIAH page 5.2, its threshold parameter])
+                             is this with sink_tokens = N.
+                             0 .. 4096; 0 = none                              */
 } kvq_config;
 
 typedef struct kvq_cache {
@@ -166,6 +176,7 @@ typedef struct kvq_tensor_regions {
   kvq_region col;      /* outliers: uint16, bits 0-11 column h*d + c, bits
                           12-15 the dense codebook index at that position  */
   kvq_region val;      /* outliers: fp16 value                              */
+  kvq_region sink;     /* attention sink: kv_dtype [B, Hkv, sink_tokens, d] */
 } kvq_tensor_regions;
 
 typedef struct kvq_layout_info {
@@ -186,6 +197,8 @@ typedef struct kvq_layout_info {
  *     exactly 2 * n_layers * n_kv_heads * head_dim * 2 * n_ctx * batch, the
  *     per-token formula of the TurboQuant page (section 2.1), which gives
  *     327,680 bytes per token for Llama-2-70B (L = 80, h = 8, d = 128).
+ *     With an attention sink, the first min(sink_tokens, n_ctx) tokens
+ *     count their raw kv_dtype bytes and the formats the rest.
  *     This is also the number of bytes one decode step must read.
  *   what = KVQ_BYTES_ALLOC: size of one layer's allocation at max_ctx,
  *     including padding and the decode workspace (n_ctx, n_layers ignored).
@@ -229,6 +242,8 @@ kvq_status kvq_cache_layout(const kvq_config* cfg, kvq_layout_info* out);
  * bytes of one call with all tokens.
  *   k_new, v_new: device [B][n_new][Hkv][d] of kv_dtype, contiguous.
  *   n_new = 0 is a no-op.  Bulk prefill is one call with n_new = T.
+ *   Tokens that fall below cfg->sink_tokens are copied raw to the sink;
+ *   the others are quantized at their position in the quantized cache.
  * Errors: INVALID_ARGUMENT (NULL/misaligned pointers, n_new < 0, bad config,
  *   codebook pointer missing or present when the format says otherwise),
  *   UNSUPPORTED, CAPACITY (n_ctx + n_new > max_ctx; checked before any
@@ -249,6 +264,10 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const vo
  *   q: device [B][Hq][d] of kv_dtype.  q_pos: device int32 [B] or NULL
  *   (= n_ctx - 1).  sm_scale <= 0 selects 1/sqrt(d).
  *   out: device [B][Hq][d] of out_dtype (KVQ_F32, KVQ_F16 or KVQ_BF16).
+ * With an attention sink, its raw tokens are streamed as a raw cache of
+ * their own whose partial softmax states (one per split of at least 256
+ * tokens) join the merge, and positions stay absolute (token t of the
+ * quantized cache is at position sink_tokens + t).
  * The call writes the workspace region of cache->base: decode calls on the
  * same cache must not overlap in time (same stream or synchronized).
  * Errors: INVALID_ARGUMENT (NULL/misaligned pointers, n_ctx == 0 or beyond
@@ -281,7 +300,8 @@ kvq_status kvq_set_decode_events(void* start, void* stop);
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* kvq_last_error(void);
 
-/* Version of this interface (major * 100 + minor). */
+/* Version of this interface (major * 100 + minor); 101 since kvq_config
+   gained sink_tokens and kvq_tensor_regions gained sink. */
 int32_t kvq_abi_version(void);
 
 #ifdef __cplusplus

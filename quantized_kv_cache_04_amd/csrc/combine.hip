@@ -15,7 +15,7 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(DecodeArgs a) {
   __shared__ float f_red[2][2][2];   // [head of the block][wave of the head][max, sum]
   const int half = threadIdx.x >> 7, c = threadIdx.x & (kHeadDim - 1);
   const int w2 = (threadIdx.x >> 6) & 1, lane = threadIdx.x & 63;
-  const int S = a.splits;
+  const int S = a.n_partials;
   const int64_t heads = (int64_t)a.sh.B * a.sh.Hq;
   const int64_t hq = (int64_t)blockIdx.x * 2 + half;
   const bool act = hq < heads;

@@ -12,6 +12,10 @@
 // (value - dense) times the score's derivative for keys, and p times
 // (value - dense) for values.
 //
+// The same kernel streams the raw attention-sink prefix (KVQuant page,
+// "Attention Sink"), launched over the sink region as a raw cache whose
+// partial states follow those of the quantized cache.
+//
 // Grid: (splits, B * Hkv); 256 threads = 4 waves; each wave takes chunks of
 // 64 tokens of the block's range.
 #include <hip/hip_runtime.h>
@@ -89,7 +93,8 @@ __global__ __launch_bounds__(256) void dec_generic_kernel(DecodeArgs a) {
   const int n = a.n_ctx;
   const int t_begin = split * a.blocks_per_split * kTile;
   const int t_end = min(n, t_begin + a.blocks_per_split * kTile);
-  const int p = a.q_pos ? a.q_pos[b] : n - 1;
+  // positions are absolute: token t of this cache sits at a.pos0 + t
+  const int p = a.q_pos ? a.q_pos[b] : a.q_last;
   const int g = a.sh.g;
   const int n_full = a.k.per_channel ? (n / a.k.G) * a.k.G : n;
   const float scale = a.sm_scale * 1.4426950408889634f;   // base-2 scores
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(256) void dec_generic_kernel(DecodeArgs a) {
           const float k1 = deq_k(a, bh, h, t, i + kD / 2, n_full);
           if (a.rope) {
             float cs, sn;
-            rope_cs(theta, t - p, i, cs, sn);
+            rope_cs(theta, a.pos0 + t - p, i, cs, sn);
 #pragma unroll
             for (int jj = 0; jj < JB; ++jj) {
               if (jj < nj) {
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(256) void dec_generic_kernel(DecodeArgs a) {
             const int i = col & (kD / 2 - 1);
             const bool upper = col >= kD / 2;
             float cs = 1.f, sn = 0.f;
-            if (a.rope) rope_cs(theta, t - p, i, cs, sn);
+            if (a.rope) rope_cs(theta, a.pos0 + t - p, i, cs, sn);
 #pragma unroll
             for (int jj = 0; jj < JB; ++jj) {
               if (jj < nj) {
@@ -229,11 +234,11 @@ __global__ __launch_bounds__(256) void dec_generic_kernel(DecodeArgs a) {
           L += wt * wl[w][jj];
         }
       }
-      if (a.splits == 1) {
-        // a single split: normalize and write the output directly
+      if (a.direct) {
+        // the only partial state (one split, no sink): normalize and write the output
         store_out(a, ((int64_t)b * a.sh.Hq + h * g + j0 + jj) * kD + c, L > 0.f ? O / L : 0.f);
       } else {
-        float* rec = partial_rec(a, b, h * g + j0 + jj, split);
+        float* rec = partial_rec(a, b, h * g + j0 + jj, a.slot0 + split);
         rec[c] = O;
         if (c == 0) { rec[kD] = M; rec[kD + 1] = L; }
       }

@@ -33,7 +33,7 @@
 //    values.
 //
 // Each wave leaves an (o, m, l) partial per split, or the output when the
-// context is one split.
+// context is one split and there is no attention sink.
 #include <hip/hip_runtime.h>
 
 #include "splitk.h"
@@ -149,7 +149,8 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
   const int t_begin = split * a.blocks_per_split * kTile;
   const int t_end = min(nctx, t_begin + a.blocks_per_split * kTile);
   const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
-  const int qpos = a.q_pos ? a.q_pos[b] : nctx - 1;
+  // positions are absolute: token t of this cache sits at a.pos0 + t
+  const int qpos = a.q_pos ? a.q_pos[b] : a.q_last;
   const float sm2 = a.sm_scale * kLog2e;
 
   // ---- tables ------------------------------------------------------------------
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
   auto set_q = [&](int ci) {
     if constexpr (ROPE) {
       if (ci % kResync == 0) {
-        rot = rope_cs(theta, (int64_t)t_begin + (int64_t)ci * kChunk - qpos);
+        rot = rope_cs(theta, (int64_t)a.pos0 + t_begin + (int64_t)ci * kChunk - qpos);
       } else {
         rot = make_float2(rot.x * rstep.x - rot.y * rstep.y, rot.x * rstep.y + rot.y * rstep.x);
       }
@@ -457,7 +458,7 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
   // ---- partial of this split ---------------------------------------------------------
   if (!head_ok) return;
   const float L = wave_sum(l_lane);
-  if (a.splits == 1) {
+  if (a.direct) {
     const int64_t o = ((int64_t)b * a.sh.Hq + h) * kD;
     store_out(a, o + lane, L > 0.f ? acc0 / L : 0.f);
     store_out(a, o + lane + 64, L > 0.f ? acc1 / L : 0.f);

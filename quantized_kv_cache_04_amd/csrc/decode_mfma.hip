@@ -961,8 +961,8 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
         L += wt * wl[w][jj];
       }
     }
-    if (a.splits == 1) {
-      // a single split: normalize and write the output directly
+    if (a.direct) {
+      // the only partial state (one split, no sink): normalize and write the output
       store_out(a, ((int64_t)b * a.sh.Hq + h * g + jj) * kD + c, L > 0.f ? O / L : 0.f);
     } else {
       float* rec = partial_rec(a, b, h * g + jj, split);

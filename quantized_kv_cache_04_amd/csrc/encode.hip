@@ -118,7 +118,8 @@ __global__ __launch_bounds__(256) void enc_rows_kernel(DevShape sh, DevTensor t,
     const int64_t bt = r / sh.Hkv;
     b = (int)(bt / n_new);
     tpos = n_ctx + bt % n_new;
-    const uint32_t pair = static_cast<const uint32_t*>(x_new)[r * (kD / 2) + lane];
+    const int64_t rin = ((int64_t)b * sh.in_tok + sh.in_off + bt % n_new) * sh.Hkv + h;
+    const uint32_t pair = static_cast<const uint32_t*>(x_new)[rin * (kD / 2) + lane];
     const int64_t row = ((int64_t)b * sh.Hkv + h) * sh.Tcap + tpos;
     if (t.quant == KVQ_QUANT_NONE) {
       reinterpret_cast<uint32_t*>(t.codes)[row * (kD / 2) + lane] = pair;
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(256) void enc_vtile_kernel(DevShape sh, DevTensor t
   for (int tau = wave; tau < kTile; tau += 4) {
     const int64_t tpos = t_begin + tau;
     if (tpos < lo_new || tpos >= hi_new) continue;       // wave-uniform
-    const int64_t rin = (((int64_t)b * n_new + (tpos - n_ctx)) * sh.Hkv + h);
+    const int64_t rin = (((int64_t)b * sh.in_tok + sh.in_off + (tpos - n_ctx)) * sh.Hkv + h);
     const uint32_t pair = static_cast<const uint32_t*>(x_new)[rin * (kD / 2) + lane];
     const float x0 = elem2f((uint16_t)(pair & 0xffff), sh.kv_bf16);
     const float x1 = elem2f((uint16_t)(pair >> 16), sh.kv_bf16);
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(128) void enc_kchan_flush_kernel(DevShape sh, DevTe
   auto value = [&](int k) -> float {
     const int64_t p = p0 + k;
     if (p < n_ctx) return elem2f(tail[(int64_t)k * kD + c], sh.kv_bf16);
-    const int64_t rin = ((int64_t)b * n_new + (p - n_ctx)) * sh.Hkv + h;
+    const int64_t rin = ((int64_t)b * sh.in_tok + sh.in_off + (p - n_ctx)) * sh.Hkv + h;
     return load_elem(x_new, rin * kD + c, sh.kv_bf16);
   };
   float lo = INFINITY, hi = -INFINITY, am = 0.0f;
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(64) void enc_kchan_tail_kernel(DevShape sh, DevTens
   const int bh = blockIdx.y;
   const int b = bh / sh.Hkv, h = bh % sh.Hkv;
   const int64_t p = p_first + blockIdx.x;
-  const int64_t rin = ((int64_t)b * n_new + (p - n_ctx)) * sh.Hkv + h;
+  const int64_t rin = ((int64_t)b * sh.in_tok + sh.in_off + (p - n_ctx)) * sh.Hkv + h;
   const uint32_t pair = static_cast<const uint32_t*>(x_new)[rin * (kD / 2) + threadIdx.x];
   uint32_t* dst = reinterpret_cast<uint32_t*>(t.tail + ((int64_t)bh * t.G + (p - group_start)) * kD);
   dst[threadIdx.x] = pair;
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTenso
   const int k = t.k_out;
   const int tn = blockIdx.x, b = blockIdx.y;
   const int64_t tpos = n_ctx + tn;
-  const uint16_t* xr = static_cast<const uint16_t*>(x_new) + ((int64_t)b * n_new + tn) * n;
+  const uint16_t* xr = static_cast<const uint16_t*>(x_new) + ((int64_t)b * sh.in_tok + sh.in_off + tn) * n;
   for (int i = threadIdx.x; i < n; i += 256)
     keys[i] = ((uint32_t)(xr[i] & 0x7fffu) << 16) | (0xffffu - (uint32_t)i);
   __syncthreads();
@@ -385,6 +386,33 @@ hipError_t launch_encode_tensor(const DevShape& sh, const DevTensor& t, bool is_
     hipLaunchKernelGGL(enc_outliers_kernel, dim3(n_new, sh.B), dim3(256),
                        (size_t)sh.Hkv * kD * 4, stream, sh, t, x_new, n_ctx, n_new);
   }
+  return hipGetLastError();
+}
+
+// ---- attention sink: raw rows ----------------------------------------------
+// One thread per 4 elements (8 bytes) of a row: input token in_off + i of
+// sequence b, KV head h goes to sink row pos + i.
+__global__ __launch_bounds__(256) void enc_sink_kernel(DevShape sh, uint16_t* sink, int sink_cap,
+                                                       const void* x_new, int64_t pos, int n) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)sh.B * n * sh.Hkv * (kD / 4);
+  if (idx >= total) return;
+  const int c4 = (int)(idx % (kD / 4));
+  const int64_t r = idx / (kD / 4);
+  const int h = (int)(r % sh.Hkv);
+  const int64_t bt = r / sh.Hkv;
+  const int b = (int)(bt / n), i = (int)(bt % n);
+  const int64_t rin = ((int64_t)b * sh.in_tok + sh.in_off + i) * sh.Hkv + h;
+  const uint2 v = reinterpret_cast<const uint2*>(x_new)[rin * (kD / 4) + c4];
+  const int64_t row = ((int64_t)b * sh.Hkv + h) * sink_cap + pos + i;
+  reinterpret_cast<uint2*>(sink)[row * (kD / 4) + c4] = v;
+}
+
+hipError_t launch_encode_sink(const DevShape& sh, uint16_t* sink, int sink_cap, const void* x_new,
+                              int64_t pos, int n, hipStream_t stream) {
+  const int64_t total = (int64_t)sh.B * n * sh.Hkv * (kD / 4);
+  hipLaunchKernelGGL(enc_sink_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                     sh, sink, sink_cap, x_new, pos, n);
   return hipGetLastError();
 }
 

@@ -31,6 +31,9 @@ kvq_status fail(kvq_status st, const char* fmt, ...) {
 
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
+// partial slots the attention sink may need: one per kSinkSplitTokens
+int64_t sink_slots(int64_t sink) { return (sink + kSinkSplitTokens - 1) / kSinkSplitTokens; }
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int outlier_count(float frac, int n) {
@@ -111,6 +114,9 @@ kvq_status check_config(const kvq_config* c) {
     return fail(KVQ_ERR_INVALID_ARGUMENT, "unknown decode_path %d", c->decode_path);
   if ((uint64_t)c->batch * (uint64_t)c->max_ctx > ((uint64_t)1 << 31))
     return fail(KVQ_ERR_INVALID_ARGUMENT, "batch * max_ctx must be <= 2^31");
+  if (c->sink_tokens < 0 || c->sink_tokens > kMaxSink)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "sink_tokens must be in [0, %d] (got %d)", kMaxSink,
+                c->sink_tokens);
   kvq_status st = check_format(c->k, *c, true, "k");
   if (st != KVQ_OK) return st;
   return check_format(c->v, *c, false, "v");
@@ -153,7 +159,19 @@ Layout make_layout(const kvq_config& c) {
   uint64_t off = 0;
   fill_tensor(L.k, c.k, c, L.Tcap, off);
   fill_tensor(L.v, c.v, c, L.Tcap, off);
-  int64_t s = (L.Tcap + 63) / 64;
+  L.sink = c.sink_tokens;
+  if (L.sink) {
+    const uint64_t sb = (uint64_t)c.batch * c.n_kv_heads * L.sink * c.head_dim * 2;
+    L.k.sink_off = off;
+    L.k.sink_bytes = sb;
+    off = align_up(off + sb, 256);
+    L.v.sink_off = off;
+    L.v.sink_bytes = sb;
+    off = align_up(off + sb, 256);
+  }
+  // partial slots: the splits of the quantized cache and those of the sink
+  // (the merge reads at most 256)
+  int64_t s = (L.Tcap + 63) / 64 + sink_slots(L.sink);
   L.S_max = (int)(s < 1 ? 1 : (s > 256 ? 256 : s));
   L.ws_off = off;
   L.partial_off = off;
@@ -186,6 +204,7 @@ void fill_regions(kvq_tensor_regions& r, const TensorLayout& t) {
   r.row_ptr = {t.rowptr_off, t.rowptr_bytes};
   r.col = {t.col_off, t.col_bytes};
   r.val = {t.val_off, t.val_bytes};
+  r.sink = {t.sink_off, t.sink_bytes};
 }
 
 kvq_status check_codebooks(const kvq_config& c, const kvq_cache& cache) {
@@ -255,7 +274,7 @@ int32_t kvq_decode_path(const kvq_config* cfg) {
   return ok ? KVQ_PATH_MFMA : KVQ_PATH_VALU;
 }
 
-int32_t kvq_abi_version(void) { return 100; }
+int32_t kvq_abi_version(void) { return 101; }
 
 kvq_status kvq_set_decode_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr))
@@ -278,7 +297,11 @@ kvq_status kvq_cache_bytes(const kvq_config* cfg, int64_t n_ctx, int64_t n_layer
   if (what != KVQ_BYTES_PAYLOAD) return fail(KVQ_ERR_INVALID_ARGUMENT, "unknown selector %d", what);
   if (n_ctx < 0 || n_layers < 0)
     return fail(KVQ_ERR_INVALID_ARGUMENT, "n_ctx and n_layers must be >= 0");
-  *out_bytes = (uint64_t)n_layers * (tensor_payload(L.k, *cfg, n_ctx) + tensor_payload(L.v, *cfg, n_ctx));
+  // the attention sink holds min(sink, n_ctx) raw tokens; the formats apply to the rest
+  const int64_t ns = n_ctx < L.sink ? n_ctx : L.sink;
+  const uint64_t raw = (uint64_t)cfg->batch * cfg->n_kv_heads * ns * cfg->head_dim * 2;
+  *out_bytes = (uint64_t)n_layers * (tensor_payload(L.k, *cfg, n_ctx - ns) +
+                                     tensor_payload(L.v, *cfg, n_ctx - ns) + 2 * raw);
   return KVQ_OK;
 }
 
@@ -318,14 +341,33 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const vo
   Layout L = make_layout(*cfg);
   DevShape sh{cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, cfg->n_q_heads / cfg->n_kv_heads,
               cfg->kv_dtype == KVQ_BF16, L.Tcap};
+  sh.in_tok = n_new;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  DevTensor kt = make_dev_tensor(L.k, cache->base, cache->k_codebook);
-  DevTensor vt = make_dev_tensor(L.v, cache->base, cache->v_codebook);
-  st = device_status(launch_encode_tensor(sh, kt, true, k_new, cache->n_ctx, n_new, s), "encode keys");
-  if (st != KVQ_OK) return st;
-  st = device_status(launch_encode_tensor(sh, vt, false, v_new, cache->n_ctx, n_new, s),
-                     "encode values");
-  if (st != KVQ_OK) return st;
+  // input tokens that fall below the sink length are copied raw; the rest
+  // are quantized at their position in the quantized cache
+  const int64_t n0 = cache->n_ctx;
+  const int n_sink_new = n0 >= L.sink ? 0 : (int)(L.sink - n0 < n_new ? L.sink - n0 : n_new);
+  const int n_q_new = n_new - n_sink_new;
+  const int64_t n_q0 = n0 > L.sink ? n0 - L.sink : 0;
+  if (n_sink_new > 0) {
+    uint8_t* base = static_cast<uint8_t*>(cache->base);
+    st = device_status(launch_encode_sink(sh, reinterpret_cast<uint16_t*>(base + L.k.sink_off),
+                                          L.sink, k_new, n0, n_sink_new, s), "sink keys");
+    if (st != KVQ_OK) return st;
+    st = device_status(launch_encode_sink(sh, reinterpret_cast<uint16_t*>(base + L.v.sink_off),
+                                          L.sink, v_new, n0, n_sink_new, s), "sink values");
+    if (st != KVQ_OK) return st;
+  }
+  if (n_q_new > 0) {
+    sh.in_off = n_sink_new;
+    DevTensor kt = make_dev_tensor(L.k, cache->base, cache->k_codebook);
+    DevTensor vt = make_dev_tensor(L.v, cache->base, cache->v_codebook);
+    st = device_status(launch_encode_tensor(sh, kt, true, k_new, n_q0, n_q_new, s), "encode keys");
+    if (st != KVQ_OK) return st;
+    st = device_status(launch_encode_tensor(sh, vt, false, v_new, n_q0, n_q_new, s),
+                       "encode values");
+    if (st != KVQ_OK) return st;
+  }
   cache->n_ctx += n_new;
   return KVQ_OK;
 }
@@ -364,57 +406,104 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   a.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)cfg->head_dim));
   a.rope = cfg->rope;
   a.rope_base = cfg->rope_base;
-  a.n_ctx = (int)cache->n_ctx;
+  // the attention sink holds tokens [0, n_sink); the quantized cache the rest
+  const int n_sink = (int)(cache->n_ctx < L.sink ? cache->n_ctx : L.sink);
+  a.n_ctx = (int)(cache->n_ctx - n_sink);
+  a.pos0 = n_sink;
+  a.q_last = (int)cache->n_ctx - 1;
+  a.slot0 = 0;
   a.S_max = L.S_max;
   a.kp_groups = 0;
   a.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(cache->base) + L.partial_off);
+  // partial slots left for the quantized cache's splits
+  const int64_t max_q_splits = L.S_max - sink_slots(L.sink);
 
   // Split the token axis so that the grid is about one resident round of
   // workgroups (256 CUs x 2 workgroups of 4 waves): fewer, longer
   // workgroups amortize each one's set-up and merge, and more rounds only
   // add a ragged tail.  Each split keeps at least 8 blocks of 32 tokens.
-  const int64_t nblocks = (a.n_ctx + kTile - 1) / kTile;
-  const int64_t pairs = (int64_t)cfg->batch * cfg->n_kv_heads;
-  constexpr int64_t kTargetWorkgroups = 512;
-  int64_t want = (kTargetWorkgroups + pairs - 1) / pairs;
-  int64_t by_len = nblocks / 8;
-  if (want > by_len) want = by_len;
-  if (cfg->decode_splits > 0 && want > cfg->decode_splits) want = cfg->decode_splits;
-  if (want > L.S_max) want = L.S_max;
-  if (want < 1) want = 1;
-  a.blocks_per_split = (int)((nblocks + want - 1) / want);
-  a.splits = (int)((nblocks + a.blocks_per_split - 1) / a.blocks_per_split);
-
   const int32_t path = kvq_decode_path(cfg);
   if (path < 0) return path;
-  if (path == KVQ_PATH_LUT) {
-    // ranges of whole 32-token chunks; a workgroup serves 4 KV heads and
-    // three of them fit on a CU, so about 768 workgroups take
-    // 768 / (batch * ceil(Hkv / 4)) ranges per sequence, each at least 4
-    // chunks long
-    constexpr int64_t kLutWorkgroups = 768;
-    const int64_t nchunks = nblocks;
-    const int64_t units = (int64_t)cfg->batch * ((cfg->n_kv_heads + 3) / 4);
-    int64_t r = (kLutWorkgroups + units - 1) / units;
-    if (r > nchunks / 4) r = nchunks / 4;
-    if (cfg->decode_splits > 0 && r > cfg->decode_splits) r = cfg->decode_splits;
-    if (r > L.S_max) r = L.S_max;
-    if (r < 1) r = 1;
-    const int64_t per = (nchunks + r - 1) / r;
-    a.blocks_per_split = (int)per;
-    a.splits = (int)((nchunks + per - 1) / per);
+  a.splits = 0;
+  a.blocks_per_split = 0;
+  if (a.n_ctx > 0) {
+    const int64_t nblocks = (a.n_ctx + kTile - 1) / kTile;
+    const int64_t pairs = (int64_t)cfg->batch * cfg->n_kv_heads;
+    constexpr int64_t kTargetWorkgroups = 512;
+    int64_t want = (kTargetWorkgroups + pairs - 1) / pairs;
+    int64_t by_len = nblocks / 8;
+    if (want > by_len) want = by_len;
+    if (cfg->decode_splits > 0 && want > cfg->decode_splits) want = cfg->decode_splits;
+    if (want > max_q_splits) want = max_q_splits;
+    if (want < 1) want = 1;
+    a.blocks_per_split = (int)((nblocks + want - 1) / want);
+    a.splits = (int)((nblocks + a.blocks_per_split - 1) / a.blocks_per_split);
+    if (path == KVQ_PATH_LUT) {
+      // ranges of whole 32-token chunks; a workgroup serves 4 KV heads and
+      // three of them fit on a CU, so about 768 workgroups take
+      // 768 / (batch * ceil(Hkv / 4)) ranges per sequence, each at least 4
+      // chunks long
+      constexpr int64_t kLutWorkgroups = 768;
+      const int64_t nchunks = nblocks;
+      const int64_t units = (int64_t)cfg->batch * ((cfg->n_kv_heads + 3) / 4);
+      int64_t r = (kLutWorkgroups + units - 1) / units;
+      if (r > nchunks / 4) r = nchunks / 4;
+      if (cfg->decode_splits > 0 && r > cfg->decode_splits) r = cfg->decode_splits;
+      if (r > max_q_splits) r = max_q_splits;
+      if (r < 1) r = 1;
+      const int64_t per = (nchunks + r - 1) / r;
+      a.blocks_per_split = (int)per;
+      a.splits = (int)((nchunks + per - 1) / per);
+    }
   }
+  // The sink is a raw cache of its own, [B, Hkv, sink, d], streamed by the
+  // general kernel with positions from 0; its partial states follow those
+  // of the quantized cache.  Each of its splits spans at least
+  // kSinkSplitTokens tokens.
+  DecodeArgs sa = a;
+  if (n_sink > 0) {
+    uint8_t* base = static_cast<uint8_t*>(cache->base);
+    for (int i = 0; i < 2; ++i) {
+      DevTensor raw{};
+      raw.quant = KVQ_QUANT_NONE;
+      raw.bits = 16;
+      raw.row_bytes = cfg->head_dim * 2;
+      raw.codes = base + (i == 0 ? L.k.sink_off : L.v.sink_off);
+      (i == 0 ? sa.k : sa.v) = raw;
+    }
+    sa.sh.Tcap = L.sink;
+    sa.n_ctx = n_sink;
+    sa.pos0 = 0;
+    sa.slot0 = a.splits;
+    const int64_t nblocks = (n_sink + kTile - 1) / kTile;
+    const int64_t pairs = (int64_t)cfg->batch * cfg->n_kv_heads;
+    int64_t want = (512 + pairs - 1) / pairs;
+    const int64_t by_len = nblocks / (kSinkSplitTokens / kTile);
+    if (want > by_len) want = by_len;
+    if (want > sink_slots(L.sink)) want = sink_slots(L.sink);
+    if (want < 1) want = 1;
+    sa.blocks_per_split = (int)((nblocks + want - 1) / want);
+    sa.splits = (int)((nblocks + sa.blocks_per_split - 1) / sa.blocks_per_split);
+  } else {
+    sa.splits = 0;
+  }
+  // a streaming kernel writes the output itself only when its one split
+  // holds every token; otherwise the partial states are merged
+  a.n_partials = sa.n_partials = a.splits + sa.splits;
+  a.direct = sa.direct = a.n_partials == 1 ? 1 : 0;
+
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
   g_ev_start = g_ev_stop = nullptr;
   hipError_t e = ev0 ? hipEventRecord(ev0, s) : hipSuccess;
-  if (e == hipSuccess) {
+  if (e == hipSuccess && a.n_ctx > 0) {
     e = path == KVQ_PATH_MFMA ? launch_decode_mfma(a, s)
         : path == KVQ_PATH_LUT ? launch_decode_lut(a, s)
                                : launch_decode_generic(a, s);
   }
   if (e == hipSuccess && ev1) e = hipEventRecord(ev1, s);
-  if (e == hipSuccess && a.splits > 1) e = launch_combine(a, s);
+  if (e == hipSuccess && n_sink > 0) e = launch_decode_generic(sa, s);
+  if (e == hipSuccess && !a.direct) e = launch_combine(a, s);
   return device_status(e, "decode attention");
 }
 

@@ -11,6 +11,8 @@ namespace kvq {
 
 constexpr int kHeadDim = 128;
 constexpr int kTile = 32;          // tokens per value tile / decode block
+constexpr int kMaxSink = 4096;     // attention-sink tokens kept raw per sequence
+constexpr int kSinkSplitTokens = 256;   // a split of the sink spans at least this many tokens
 
 // Host-side description of one cache tensor (keys or values) and where its
 // arrays sit in the allocation.
@@ -29,11 +31,13 @@ struct TensorLayout {
   uint64_t rowptr_off = 0, rowptr_bytes = 0;
   uint64_t col_off = 0, col_bytes = 0;
   uint64_t val_off = 0, val_bytes = 0;
+  uint64_t sink_off = 0, sink_bytes = 0;   // attention sink: raw [B, Hkv, sink, d]
 };
 
 struct Layout {
   TensorLayout k, v;
   int64_t Tcap = 0;          // token capacity per sequence (multiple of 32)
+  int sink = 0;              // attention-sink tokens kept raw per sequence
   int S_max = 1;             // partial slots per (b, query head)
   uint64_t partial_off = 0;  // float [B][Hq][S_max][d + 2]
   uint64_t ws_off = 0, ws_bytes = 0;
@@ -55,6 +59,9 @@ struct DevTensor {
 struct DevShape {
   int B, Hq, Hkv, g, kv_bf16;
   int64_t Tcap;
+  // appends: the input holds in_tok tokens per sequence; the call encodes
+  // input tokens [in_off, in_off + n_new)
+  int64_t in_tok = 0, in_off = 0;
 };
 
 DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebook);
@@ -63,6 +70,9 @@ DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebo
 hipError_t launch_encode_tensor(const DevShape& sh, const DevTensor& t, bool is_key,
                                 const void* x_new, int64_t n_ctx, int n_new,
                                 hipStream_t stream);
+// raw copy of input tokens [in_off, in_off + n) to sink rows [pos, pos + n)
+hipError_t launch_encode_sink(const DevShape& sh, uint16_t* sink, int sink_cap, const void* x_new,
+                              int64_t pos, int n, hipStream_t stream);
 
 // ---- decode launchers ------------------------------------------------------
 struct DecodeArgs {
@@ -75,16 +85,21 @@ struct DecodeArgs {
   float sm_scale;       // softmax scale (already resolved)
   int rope;
   float rope_base;
-  int n_ctx;
-  int splits;           // splits actually used (>= 1)
+  int n_ctx;            // tokens this launch streams
+  int pos0;             // absolute position of its token 0
+  int q_last;           // absolute position of the sequence's last token (default query position)
+  int splits;           // splits of the token axis this launch uses
   int blocks_per_split; // 32-token blocks per split
+  int slot0;            // partial slot of split 0 (general kernel; the others start at 0)
+  int direct;           // 1: the streaming kernel writes the output itself (one split, no sink)
+  int n_partials;       // partial states the combine merges
   int S_max;
   float* partial;       // [B][Hq][S_max][d + 2]
   int kp_groups;        // matrix-core kernel: key groups staged in LDS per wave (0 = none)
 };
 
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
-// merge of the split-K partials (only when a.splits > 1)
+// merge of the split-K partials, the sink's included (when a.direct is 0)
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
 // Whether the matrix-core kernel handles this configuration's formats.
 bool mfma_config_supported(const kvq_config& c);
@@ -93,7 +108,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // keys and values, one query head per KV head, at most 64 outliers per token;
 // k_out_*: outliers per token of keys and values).
 bool lut_config_supported(const kvq_config& c, int k_out_k, int k_out_v);
-// a.splits = token ranges per sequence, a.blocks_per_split even (64-token chunks)
+// a.splits = token ranges per sequence, each of a.blocks_per_split 32-token chunks
 hipError_t launch_decode_lut(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace kvq

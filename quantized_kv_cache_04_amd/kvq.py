@@ -15,6 +15,8 @@ from typing import Any, Dict, Optional
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvq.h")
+# interface version the structures below follow (major * 100 + minor)
+ABI_VERSION = 101
 
 # ---- constants mirrored from kvq.h -------------------------------------------
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_DEVICE = 0, -1, -2, -3, -4
@@ -38,7 +40,7 @@ class Config(ctypes.Structure):
                 ("max_ctx", ctypes.c_int64), ("kv_dtype", ctypes.c_int32),
                 ("rope", ctypes.c_int32), ("rope_base", ctypes.c_float),
                 ("decode_splits", ctypes.c_int32), ("decode_path", ctypes.c_int32),
-                ("k", TensorFormat), ("v", TensorFormat)]
+                ("k", TensorFormat), ("v", TensorFormat), ("sink_tokens", ctypes.c_int32)]
 
 
 class CacheStruct(ctypes.Structure):
@@ -52,7 +54,7 @@ class Region(ctypes.Structure):
 
 class TensorRegions(ctypes.Structure):
     _fields_ = [("codes", Region), ("params", Region), ("tail", Region), ("row_ptr", Region),
-                ("col", Region), ("val", Region)]
+                ("col", Region), ("val", Region), ("sink", Region)]
 
 
 class LayoutInfo(ctypes.Structure):
@@ -92,6 +94,9 @@ def lib() -> ctypes.CDLL:
         L.kvq_last_error.restype = ctypes.c_char_p
         L.kvq_last_error.argtypes = []
         L.kvq_abi_version.restype = ctypes.c_int32
+        if L.kvq_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH}: interface version {L.kvq_abi_version()}, "
+                               f"this binding expects {ABI_VERSION}; rebuild the library")
         L.kvq_set_decode_events.restype = ctypes.c_int32
         L.kvq_set_decode_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.kvq_decode_path.restype = ctypes.c_int32
@@ -120,18 +125,20 @@ def fmt_struct(f: Dict[str, Any]) -> TensorFormat:
 def make_config(*, batch: int, n_q_heads: int, n_kv_heads: int, max_ctx: int,
                 kv_dtype: str, k: Dict[str, Any], v: Dict[str, Any], head_dim: int = 128,
                 rope: bool = False, rope_base: float = 10000.0, decode_splits: int = 0,
-                decode_path: str = "auto") -> Config:
+                decode_path: str = "auto", sink_tokens: int = 0) -> Config:
     return Config(batch, n_q_heads, n_kv_heads, head_dim, max_ctx, DTYPES[kv_dtype],
                   int(bool(rope)), float(rope_base), int(decode_splits), PATHS[decode_path],
-                  fmt_struct(k), fmt_struct(v))
+                  fmt_struct(k), fmt_struct(v), int(sink_tokens))
 
 
 def config_from_workload(w, max_ctx: Optional[int] = None, decode_splits: int = 0,
-                         decode_path: str = "auto") -> Config:
+                         decode_path: str = "auto", sink_tokens: Optional[int] = None) -> Config:
     return make_config(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
                        max_ctx=max_ctx if max_ctx is not None else w.ctx, kv_dtype=w.kv_dtype,
                        k=w.k, v=w.v, head_dim=w.head_dim, rope=w.rope, rope_base=w.rope_base,
-                       decode_splits=decode_splits, decode_path=decode_path)
+                       decode_splits=decode_splits, decode_path=decode_path,
+                       sink_tokens=(sink_tokens if sink_tokens is not None
+                                    else getattr(w, "sink_tokens", 0)))
 
 
 def cache_bytes(cfg: Config, n_ctx: int = 0, n_layers: int = 1, what: int = BYTES_PAYLOAD) -> int:

@@ -81,6 +81,7 @@ class Workload:
     v: Dict[str, Any]
     values: Dict[str, Any]
     seed: int = 0
+    sink_tokens: int = 0    # attention-sink tokens kept raw (0 = none)
 
     @property
     def gqa(self) -> int:

@@ -25,8 +25,13 @@ def to_np32(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy()
 
 
-def oracle_encode(w, inputs: Dict[str, Optional[torch.Tensor]], n_ctx: int, max_ctx: int):
-    """Oracle encode of the first n_ctx tokens -> (expected regions per tensor, deq K, deq V)."""
+def oracle_encode(w, inputs: Dict[str, Optional[torch.Tensor]], n_ctx: int, max_ctx: int,
+                  sink: int = 0):
+    """Oracle encode of the first n_ctx tokens -> (expected regions per tensor, deq K, deq V).
+
+    With an attention sink of ``sink`` tokens the first min(sink, n_ctx)
+    tokens are expected raw in the "sink" region and the rest as a quantized
+    cache of their own."""
     res = {}
     deq = {}
     for name in ("k", "v"):
@@ -34,22 +39,29 @@ def oracle_encode(w, inputs: Dict[str, Optional[torch.Tensor]], n_ctx: int, max_
         x = to_np32(inputs[name][:, :n_ctx])
         cb = inputs[f"{name}_codebook"]
         cbn = cb.cpu().numpy() if cb is not None else None
-        enc = oq.encode_tensor(x, fmt, cbn)
-        deq[name] = enc["deq"]
-        if fmt["quantizer"] == "none":
-            res[name] = None
-            continue
-        res[name] = olay.expected_regions(fmt, enc, batch=w.batch, n_kv_heads=w.n_kv_heads,
-                                          n_ctx=n_ctx, max_ctx=max_ctx, kv_dtype=w.kv_dtype,
-                                          is_key=(name == "k"))
+        if sink:
+            both = oq.encode_with_sink(x, fmt, cbn, sink)
+            enc, n_q = both["rest"], n_ctx - min(sink, n_ctx)
+            deq[name] = both["deq"]
+        else:
+            enc, n_q = oq.encode_tensor(x, fmt, cbn), n_ctx
+            deq[name] = enc["deq"]
+        exp = {}
+        if fmt["quantizer"] != "none" and enc is not None:
+            exp = olay.expected_regions(fmt, enc, batch=w.batch, n_kv_heads=w.n_kv_heads,
+                                        n_ctx=n_q, max_ctx=max_ctx, kv_dtype=w.kv_dtype,
+                                        is_key=(name == "k"))
+        if sink:
+            exp["sink"] = olay.sink_region(x, sink, kv_dtype=w.kv_dtype)
+        res[name] = exp or None
     return res, deq["k"], deq["v"]
 
 
 def gpu_cache(w, inputs, chunks: Sequence[int], max_ctx: int, decode_splits: int = 0,
-              decode_path: str = "auto", device: str = "cuda") -> kvq.Cache:
+              decode_path: str = "auto", device: str = "cuda", sink: int = 0) -> kvq.Cache:
     """Build the cache on the GPU by appending the inputs in ``chunks`` token counts."""
     cfg = kvq.config_from_workload(w, max_ctx=max_ctx, decode_splits=decode_splits,
-                                   decode_path=decode_path)
+                                   decode_path=decode_path, sink_tokens=sink)
     kcb = inputs["k_codebook"].to(device) if inputs["k_codebook"] is not None else None
     vcb = inputs["v_codebook"].to(device) if inputs["v_codebook"] is not None else None
     cache = kvq.Cache(cfg, device=device, k_codebook=kcb, v_codebook=vcb)
@@ -75,7 +87,7 @@ def compare_regions(cache: kvq.Cache, expected) -> List[str]:
         exp = expected[name]
         if exp is None:
             continue
-        for reg in ("codes", "params", "tail", "row_ptr", "col", "val"):
+        for reg in ("codes", "params", "tail", "row_ptr", "col", "val", "sink"):
             if reg not in exp:
                 continue
             got = cache.region(name, reg).cpu().numpy()

@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
                           "kvq_decode_attention", "kvq_last_error", "kvq_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvq_abi_version() == 100
+    assert L.kvq_abi_version() == kvq.ABI_VERSION == 101
 
 
 def _none_cfg(**kw):
@@ -80,6 +80,49 @@ def test_layout_regions_fit_and_do_not_overlap(cfg_id):
     assert li.k.codes.bytes == w.batch * w.n_kv_heads * li.capacity * 16 * bits
 
 
+@pytest.mark.parametrize("cfg_id", sorted(CONFIGS))
+@pytest.mark.parametrize("sink", [1, 4, 64, 1000, 4096])
+@pytest.mark.parametrize("n", [0, 1, 3, 64, 65, 100, 1000, 5000])
+def test_payload_with_a_sink_matches_oracle(cfg_id, sink, n):
+    w = make_workload(cfg_id)
+    cfg = kvq.config_from_workload(w, sink_tokens=sink)
+    want = ocb.payload_bytes(w.k, w.v, batch=w.batch, n_kv_heads=w.n_kv_heads,
+                             head_dim=w.head_dim, n_ctx=n, kv_dtype=w.kv_dtype, sink=sink)
+    assert kvq.cache_bytes(cfg, n, 2) == 2 * want
+
+
+@pytest.mark.parametrize("cfg_id", sorted(CONFIGS))
+@pytest.mark.parametrize("sink", [0, 1, 64, 4096])
+def test_sink_regions(cfg_id, sink):
+    w = make_workload(cfg_id)
+    cfg = kvq.config_from_workload(w, sink_tokens=sink)
+    li = kvq.cache_layout(cfg)
+    base = kvq.cache_layout(kvq.config_from_workload(w))
+    want = w.batch * w.n_kv_heads * sink * w.head_dim * 2
+    regs = []
+    for t in ("k", "v"):
+        r = getattr(li, t).sink
+        assert r.bytes == want
+        if sink:
+            assert r.offset % 256 == 0
+        for name in ("codes", "params", "tail", "row_ptr", "col", "val", "sink"):
+            rr = getattr(getattr(li, t), name)
+            if rr.bytes:
+                regs.append((rr.offset, rr.offset + rr.bytes))
+            if name != "sink":   # the quantized regions do not move
+                b = getattr(getattr(base, t), name)
+                assert (rr.offset, rr.bytes) == (b.offset, b.bytes)
+    regs.append((li.workspace.offset, li.workspace.offset + li.workspace.bytes))
+    regs.sort()
+    for (a0, a1), (b0, b1) in zip(regs, regs[1:]):
+        assert a1 <= b0
+    assert regs[-1][1] <= li.total_bytes == kvq.cache_bytes(cfg, what=kvq.BYTES_ALLOC)
+    # partial slots for the sink's softmax states: one per 256 sink tokens,
+    # within the merge's 256
+    want_slots = min(256, -(-li.capacity // 64) + -(-sink // 256))
+    assert li.max_splits == want_slots
+
+
 def _status(fn):
     with pytest.raises(kvq.KvqError) as ei:
         fn()
@@ -106,6 +149,8 @@ def _status(fn):
     (dict(n_q_heads=128, n_kv_heads=128, k={"quantizer": "codebook", "bits": 4, "outlier_frac": 0.01}),
      kvq.ERR_UNSUPPORTED, "4096"),
     (dict(rope=True, rope_base=0.5), kvq.ERR_INVALID_ARGUMENT, "rope_base"),
+    (dict(sink_tokens=-1), kvq.ERR_INVALID_ARGUMENT, "sink_tokens"),
+    (dict(sink_tokens=4097), kvq.ERR_INVALID_ARGUMENT, "sink_tokens"),
 ])
 def test_config_errors(mut, code, needle):
     cfg = _none_cfg(**mut)

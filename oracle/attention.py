@@ -67,3 +67,51 @@ def decode_attention(q: np.ndarray, k_deq: np.ndarray, v_deq: np.ndarray, *,
                 w = w / w.sum()
                 out[b, j] = w @ V
     return out
+
+
+def prefill_attention(q: np.ndarray, k_deq: np.ndarray, v_deq: np.ndarray, *,
+                      n_ctx: Optional[int] = None, sm_scale: Optional[float] = None,
+                      rope: bool = False, rope_base: float = 10000.0) -> np.ndarray:
+    """Causal attention of the last n_q tokens of the cache (chunked prefill).
+
+    The prefill step builds the cache and scores every new token's query
+    against the keys before it (NIAH page, section 4.2: first-token latency
+    comes from the prefill pass; Survey page, sections 2.3 and 5.3: QK^T,
+    softmax and the value product of prefill kept on chip).  Here the new
+    tokens have already been appended, so they are the last n_q tokens of a
+    cache of n_ctx: query i (position n_ctx - n_q + i) attends tokens
+    [0, n_ctx - n_q + i], each row exactly as ``decode_attention`` with that
+    context and query position.
+
+    q [B, n_q, Hq, d]; k_deq, v_deq [B, Hkv, T, d] (float64 dequantized
+    cache).  Returns float64 [B, n_q, Hq, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, n_q, Hq, d = q.shape
+    Hkv = k_deq.shape[1]
+    T = k_deq.shape[2] if n_ctx is None else n_ctx
+    if not 1 <= n_q <= T:
+        raise ValueError("need 1 <= n_q <= n_ctx")
+    g = Hq // Hkv
+    sm = 1.0 / np.sqrt(d) if sm_scale is None or sm_scale <= 0 else float(sm_scale)
+    base = T - n_q
+    out = np.empty((B, n_q, Hq, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hkv):
+            K = np.asarray(k_deq[b, h, :T], dtype=np.float64)
+            V = np.asarray(v_deq[b, h, :T], dtype=np.float64)
+            if rope:
+                K = rope_rotate(K, np.arange(T), rope_base)
+            for i in range(n_q):
+                p = base + i                      # query position; keys 0..p
+                for jj in range(g):
+                    j = h * g + jj
+                    qj = q[b, i, j]
+                    if rope:
+                        qj = rope_rotate(qj[None, :], np.array([p]), rope_base)[0]
+                    s = sm * (K[:p + 1] @ qj)
+                    s = s - s.max()
+                    w = np.exp(s)
+                    w = w / w.sum()
+                    out[b, i, j] = w @ V[:p + 1]
+    return out

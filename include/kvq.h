@@ -278,6 +278,31 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
                                 int32_t out_dtype, void* stream);
 
 /*
+ * kvq_prefill_attention -- causal attention of the last n_q tokens of every
+ * sequence over the cache: the attention of a prefill chunk (chunked
+ * prefill) once its keys and values have been appended with
+ * kvq_quantize_append [NIAH page 4.2: first-token latency is the prefill
+ * pass; Survey page 2.3 and 5.3: QK^T, softmax and the value product of
+ * prefill kept on chip].
+ *   out[b, i, j, :] = sum_{t <= p_i} softmax_t(sm_scale * q'_{i,j} . k'_t) * v_t,
+ *   p_i = n_ctx - n_q + i,
+ * with k, v the cache exactly as kvq_decode_attention reads it (dequantized,
+ * outliers, per-channel tail, raw attention-sink tokens) and the same RoPE
+ * convention, the query of row i at position p_i.
+ *   q: device [B][n_q][Hq][d] of kv_dtype (query i is that of token
+ *   n_ctx - n_q + i).  1 <= n_q <= n_ctx.  sm_scale <= 0 selects 1/sqrt(d).
+ *   out: device [B][n_q][Hq][d] of out_dtype (KVQ_F32, KVQ_F16 or KVQ_BF16).
+ * Runs on the matrix cores for every cache format; the query heads per KV
+ * head (Hq / Hkv) must divide 64.  Reads the cache only: it may overlap
+ * with other reads of the same cache, not with appends to it.
+ * Errors: INVALID_ARGUMENT (NULL/misaligned pointers, n_ctx == 0, n_q out
+ *   of range, bad out_dtype), UNSUPPORTED (group size), DEVICE.
+ */
+kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                                 int32_t n_q, float sm_scale, void* out, int32_t out_dtype,
+                                 void* stream);
+
+/*
  * kvq_decode_path -- which decode kernel kvq_decode_attention runs for this
  * configuration: KVQ_PATH_VALU, KVQ_PATH_MFMA or KVQ_PATH_LUT (what KVQ_PATH_AUTO resolves
  * to, or the forced path).  Host only.  Returns a negative status for an
@@ -301,7 +326,8 @@ kvq_status kvq_set_decode_events(void* start, void* stop);
 const char* kvq_last_error(void);
 
 /* Version of this interface (major * 100 + minor); 101 since kvq_config
-   gained sink_tokens and kvq_tensor_regions gained sink. */
+   gained sink_tokens and kvq_tensor_regions gained sink; 102 adds
+   kvq_prefill_attention. */
 int32_t kvq_abi_version(void);
 
 #ifdef __cplusplus

@@ -29,41 +29,13 @@ constexpr int kD = kHeadDim;
 constexpr int JB = 8;   // query heads per pass
 constexpr int CH = 64;  // tokens per wave chunk
 
-__device__ __forceinline__ float deq_uniform(uint32_t code, int quant, const void* params,
-                                             int64_t rec) {
-  if (quant == KVQ_QUANT_SYM_Q8_0)
-    return (float)(int8_t)code * h2f(static_cast<const uint16_t*>(params)[rec]);
-  const uint32_t pz = static_cast<const uint32_t*>(params)[rec];
-  return (float)code * h2f((uint16_t)(pz & 0xffff)) + h2f((uint16_t)(pz >> 16));
-}
-
 // Dense (codebook or uniform) value of key channel c of token t.
-__device__ float deq_k(const DecodeArgs& a, int bh, int h, int t, int c, int n_full) {
-  const DevTensor& k = a.k;
-  const int64_t row = (int64_t)bh * a.sh.Tcap + t;
-  if (k.quant == KVQ_QUANT_NONE)
-    return elem2f(reinterpret_cast<const uint16_t*>(k.codes)[row * kD + c], a.sh.kv_bf16);
-  if (k.per_channel && t >= n_full)
-    return elem2f(k.tail[((int64_t)bh * k.G + (t - n_full)) * kD + c], a.sh.kv_bf16);
-  const uint32_t code = k_row_code(k.codes + row * k.row_bytes, k.bits, c);
-  if (k.quant == KVQ_QUANT_CODEBOOK) return h2f(k.codebook[((int64_t)h * kD + c) * 16 + code]);
-  if (k.per_channel)
-    return deq_uniform(code, k.quant, k.params, ((int64_t)bh * (a.sh.Tcap / k.G) + t / k.G) * kD + c);
-  return deq_uniform(code, k.quant, k.params, row * k.ng + c / k.G);
+__device__ __forceinline__ float deq_k(const DecodeArgs& a, int bh, int h, int t, int c, int n_full) {
+  return deq_key(a.k, a.sh, bh, h, t, c, n_full);
 }
 
-__device__ float deq_v(const DecodeArgs& a, int bh, int h, int t, int c) {
-  const DevTensor& v = a.v;
-  const int64_t row = (int64_t)bh * a.sh.Tcap + t;
-  if (v.quant == KVQ_QUANT_NONE)
-    return elem2f(reinterpret_cast<const uint16_t*>(v.codes)[row * kD + c], a.sh.kv_bf16);
-  const uint8_t* tile = v.codes + ((int64_t)bh * a.sh.Tcap + (t & ~(kTile - 1))) * v.row_bytes;
-  if (v.quant == KVQ_QUANT_CODEBOOK) {
-    const uint32_t code = v_pair_code(tile, t & (kTile - 1), c);
-    return h2f(v.codebook[((int64_t)h * kD + c) * 16 + code]);
-  }
-  const uint32_t code = v_tile_code(tile, v.bits, t & (kTile - 1), c);
-  return deq_uniform(code, v.quant, v.params, row * v.ng + c / v.G);
+__device__ __forceinline__ float deq_v(const DecodeArgs& a, int bh, int h, int t, int c) {
+  return deq_value(a.v, a.sh, bh, h, t, c);
 }
 
 __device__ __forceinline__ float wave_max(float x) {

@@ -99,4 +99,45 @@ __device__ __forceinline__ uint32_t field_value(uint32_t code, int field) {
   return field == 0 ? code : (field == 1 ? (code & 3u) : (code >> 2) & 1u);
 }
 
+// ---- element-wise dequantization (general kernel, prefill staging) --------
+__device__ __forceinline__ float deq_uniform(uint32_t code, int quant, const void* params,
+                                             int64_t rec) {
+  if (quant == KVQ_QUANT_SYM_Q8_0)
+    return (float)(int8_t)code * h2f(static_cast<const uint16_t*>(params)[rec]);
+  const uint32_t pz = static_cast<const uint32_t*>(params)[rec];
+  return (float)code * h2f((uint16_t)(pz & 0xffff)) + h2f((uint16_t)(pz >> 16));
+}
+
+// Dense (codebook or uniform) value of key channel c of token t of KV head h
+// (bh = b * Hkv + h); per-channel keys past n_full come from the tail.
+__device__ inline float deq_key(const DevTensor& k, const DevShape& sh, int bh, int h, int64_t t,
+                                int c, int64_t n_full) {
+  const int64_t row = (int64_t)bh * sh.Tcap + t;
+  if (k.quant == KVQ_QUANT_NONE)
+    return elem2f(reinterpret_cast<const uint16_t*>(k.codes)[row * kHeadDim + c], sh.kv_bf16);
+  if (k.per_channel && t >= n_full)
+    return elem2f(k.tail[((int64_t)bh * k.G + (t - n_full)) * kHeadDim + c], sh.kv_bf16);
+  const uint32_t code = k_row_code(k.codes + row * k.row_bytes, k.bits, c);
+  if (k.quant == KVQ_QUANT_CODEBOOK) return h2f(k.codebook[((int64_t)h * kHeadDim + c) * 16 + code]);
+  if (k.per_channel)
+    return deq_uniform(code, k.quant, k.params,
+                       ((int64_t)bh * (sh.Tcap / k.G) + t / k.G) * kHeadDim + c);
+  return deq_uniform(code, k.quant, k.params, row * k.ng + c / k.G);
+}
+
+// Dense value of value channel c of token t of KV head h.
+__device__ inline float deq_value(const DevTensor& v, const DevShape& sh, int bh, int h, int64_t t,
+                                  int c) {
+  const int64_t row = (int64_t)bh * sh.Tcap + t;
+  if (v.quant == KVQ_QUANT_NONE)
+    return elem2f(reinterpret_cast<const uint16_t*>(v.codes)[row * kHeadDim + c], sh.kv_bf16);
+  const uint8_t* tile = v.codes + ((int64_t)bh * sh.Tcap + (t & ~(int64_t)(kTile - 1))) * v.row_bytes;
+  if (v.quant == KVQ_QUANT_CODEBOOK) {
+    const uint32_t code = v_pair_code(tile, (int)(t & (kTile - 1)), c);
+    return h2f(v.codebook[((int64_t)h * kHeadDim + c) * 16 + code]);
+  }
+  const uint32_t code = v_tile_code(tile, v.bits, (int)(t & (kTile - 1)), c);
+  return deq_uniform(code, v.quant, v.params, row * v.ng + c / v.G);
+}
+
 }  // namespace kvq

@@ -274,7 +274,7 @@ int32_t kvq_decode_path(const kvq_config* cfg) {
   return ok ? KVQ_PATH_MFMA : KVQ_PATH_VALU;
 }
 
-int32_t kvq_abi_version(void) { return 101; }
+int32_t kvq_abi_version(void) { return 102; }
 
 kvq_status kvq_set_decode_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr))
@@ -505,6 +505,52 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   if (e == hipSuccess && n_sink > 0) e = launch_decode_generic(sa, s);
   if (e == hipSuccess && !a.direct) e = launch_combine(a, s);
   return device_status(e, "decode attention");
+}
+
+kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                                 int32_t n_q, float sm_scale, void* out, int32_t out_dtype,
+                                 void* stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!cache) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (!cache->base || !aligned16(cache->base))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "cache->base must be a 16-byte aligned device pointer");
+  if (cache->n_ctx < 1 || cache->n_ctx > cfg->max_ctx)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "n_ctx must be in [1, max_ctx] (got %lld)",
+                (long long)cache->n_ctx);
+  if (n_q < 1 || n_q > cache->n_ctx)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "n_q must be in [1, n_ctx] (got %d, n_ctx %lld): the "
+                "queries are those of the last n_q cached tokens", n_q, (long long)cache->n_ctx);
+  const int g = cfg->n_q_heads / cfg->n_kv_heads;
+  if (64 % g != 0)
+    return fail(KVQ_ERR_UNSUPPORTED, "prefill needs n_q_heads / n_kv_heads to divide 64 (got %d)", g);
+  st = check_codebooks(*cfg, *cache);
+  if (st != KVQ_OK) return st;
+  if (!q || !out || !aligned16(q) || !aligned16(out))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "q and out must be 16-byte aligned device pointers");
+  if (out_dtype != KVQ_F32 && out_dtype != KVQ_F16 && out_dtype != KVQ_BF16)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "out_dtype must be KVQ_F32, KVQ_F16 or KVQ_BF16");
+  if (!isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+
+  Layout L = make_layout(*cfg);
+  PrefillArgs a;
+  a.sh = DevShape{cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, g, cfg->kv_dtype == KVQ_BF16, L.Tcap};
+  a.k = make_dev_tensor(L.k, cache->base, cache->k_codebook);
+  a.v = make_dev_tensor(L.v, cache->base, cache->v_codebook);
+  uint8_t* base = static_cast<uint8_t*>(cache->base);
+  a.k_sink = L.sink ? reinterpret_cast<const uint16_t*>(base + L.k.sink_off) : nullptr;
+  a.v_sink = L.sink ? reinterpret_cast<const uint16_t*>(base + L.v.sink_off) : nullptr;
+  a.sink_cap = L.sink;
+  a.n_sink = (int)(cache->n_ctx < L.sink ? cache->n_ctx : L.sink);
+  a.n_total = (int)cache->n_ctx;
+  a.n_q = n_q;
+  a.q = q;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)cfg->head_dim));
+  a.rope = cfg->rope;
+  a.rope_base = cfg->rope_base;
+  return device_status(launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill attention");
 }
 
 }  // extern "C"

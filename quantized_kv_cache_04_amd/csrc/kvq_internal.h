@@ -111,4 +111,23 @@ bool lut_config_supported(const kvq_config& c, int k_out_k, int k_out_v);
 // a.splits = token ranges per sequence, each of a.blocks_per_split 32-token chunks
 hipError_t launch_decode_lut(const DecodeArgs& a, hipStream_t stream);
 
+// ---- chunked-prefill launcher ------------------------------------------------
+struct PrefillArgs {
+  DevShape sh;
+  DevTensor k, v;            // quantized cache: tokens [n_sink, n_total)
+  const uint16_t* k_sink;    // raw [B][Hkv][sink_cap][d]: tokens [0, n_sink)
+  const uint16_t* v_sink;
+  int sink_cap, n_sink;
+  int n_total;               // tokens in the cache, sink included
+  int n_q;                   // queries: the last n_q tokens, positions n_total - n_q + i
+  const void* q;             // [B][n_q][Hq][d], kv dtype
+  void* out;                 // [B][n_q][Hq][d], out_dtype
+  int out_dtype;
+  float sm_scale;            // resolved
+  int rope;
+  float rope_base;
+};
+// 64 query rows per workgroup: Hq / Hkv must divide 64
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
 }  // namespace kvq

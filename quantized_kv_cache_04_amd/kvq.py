@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvq.h")
 # interface version the structures below follow (major * 100 + minor)
-ABI_VERSION = 101
+ABI_VERSION = 102
 
 # ---- constants mirrored from kvq.h -------------------------------------------
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_DEVICE = 0, -1, -2, -3, -4
@@ -88,8 +88,11 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attention.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(CacheStruct),
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+        L.kvq_prefill_attention.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(CacheStruct),
+                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
         for fn in ("kvq_cache_bytes", "kvq_cache_layout", "kvq_quantize_append",
-                   "kvq_decode_attention"):
+                   "kvq_decode_attention", "kvq_prefill_attention"):
             getattr(L, fn).restype = ctypes.c_int32
         L.kvq_last_error.restype = ctypes.c_char_p
         L.kvq_last_error.argtypes = []
@@ -202,6 +205,10 @@ class Cache:
         return decode_attention(self, q, q_pos=q_pos, sm_scale=sm_scale, out=out,
                                 out_dtype=out_dtype, stream=stream)
 
+    def prefill(self, q, sm_scale: float = 0.0, out=None, out_dtype: str = "f32", stream=None):
+        return prefill_attention(self, q, sm_scale=sm_scale, out=out, out_dtype=out_dtype,
+                                 stream=stream)
+
 
 def set_decode_events(start=None, stop=None) -> None:
     """Have the next decode call on this thread record ``start`` and ``stop``
@@ -240,4 +247,19 @@ def decode_attention(cache: Cache, q, q_pos=None, sm_scale: float = 0.0, out=Non
                                       q_pos.data_ptr() if q_pos is not None else None,
                                       float(sm_scale), out.data_ptr(), DTYPES[out_dtype],
                                       _stream_ptr(stream)))
+    return out
+
+
+def prefill_attention(cache: Cache, q, sm_scale: float = 0.0, out=None, out_dtype: str = "f32",
+                      stream=None):
+    """Causal attention of the last n_q cached tokens: q [B, n_q, Hq, d] ->
+    out [B, n_q, Hq, d] of ``out_dtype``."""
+    import torch
+    if out is None:
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[out_dtype]
+        out = torch.empty(q.shape, dtype=tdt, device=q.device)
+    cs = cache.struct()
+    _check(lib().kvq_prefill_attention(ctypes.byref(cache.cfg), ctypes.byref(cs), q.data_ptr(),
+                                       int(q.shape[1]), float(sm_scale), out.data_ptr(),
+                                       DTYPES[out_dtype], _stream_ptr(stream)))
     return out

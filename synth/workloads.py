@@ -62,7 +62,7 @@ CONFIGS: Dict[int, Dict[str, Any]] = {
 }
 
 _STREAMS = {"k": 0, "v": 1, "q": 2, "mask": 3, "kcb": 4, "vcb": 5, "step_k": 6, "step_v": 7,
-            "step_q": 8}
+            "step_q": 8, "prefill_q": 9}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -191,3 +191,11 @@ def make_step_tokens(w: Workload, step: int, n_new: int = 1, device: str = "cpu"
     q = torch.randn((B, w.n_q_heads, d), generator=_gen(w, "step_q", device, step),
                     device=device, dtype=torch.float32).to(dt)
     return k.contiguous(), v.contiguous(), q.contiguous()
+
+
+def make_prefill_queries(w: Workload, n_q: int, device: str = "cpu") -> torch.Tensor:
+    """Queries [B, n_q, Hq, d] of the last n_q cached tokens for chunked
+    prefill: N(0, 1) in the cache dtype, like the decode query."""
+    q = torch.randn((w.batch, n_q, w.n_q_heads, w.head_dim), generator=_gen(w, "prefill_q", device),
+                    device=device, dtype=torch.float32)
+    return q.to(w.torch_dtype).contiguous()

@@ -113,3 +113,9 @@ def oracle_attention(w, q: torch.Tensor, kdeq, vdeq, n_ctx: int, q_pos=None):
     return oatt.decode_attention(to_np32(q), kdeq, vdeq, n_ctx=n_ctx, rope=w.rope,
                                  rope_base=w.rope_base,
                                  q_pos=None if q_pos is None else np.asarray(q_pos))
+
+
+def oracle_prefill(w, q: torch.Tensor, kdeq, vdeq, n_ctx: int):
+    """Oracle causal attention of the last q.shape[1] tokens of an n_ctx cache."""
+    return oatt.prefill_attention(to_np32(q), kdeq, vdeq, n_ctx=n_ctx, rope=w.rope,
+                                  rope_base=w.rope_base)

@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
                           "kvq_decode_attention", "kvq_last_error", "kvq_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvq_abi_version() == kvq.ABI_VERSION == 101
+    assert L.kvq_abi_version() == kvq.ABI_VERSION == 102
 
 
 def _none_cfg(**kw):
@@ -217,6 +217,32 @@ def test_decode_errors_before_launch():
     assert kvq.lib().kvq_decode_attention(ctypes.byref(cfg), ctypes.byref(ok), FAKE, None,
                                           float("nan"), FAKE, kvq.F32, None) == \
         kvq.ERR_INVALID_ARGUMENT
+
+
+def _prefill(cfg, cs, q, n_q, out, odt=kvq.F32):
+    return kvq.lib().kvq_prefill_attention(ctypes.byref(cfg), ctypes.byref(cs), q, n_q, 0.0, out,
+                                           odt, None)
+
+
+def test_prefill_errors_before_launch():
+    cfg = _none_cfg(max_ctx=100)
+    empty = kvq.CacheStruct(FAKE, None, None, 0)
+    assert _prefill(cfg, empty, FAKE, 1, FAKE) == kvq.ERR_INVALID_ARGUMENT
+    ok = kvq.CacheStruct(FAKE, None, None, 10)
+    assert _prefill(cfg, ok, FAKE, 0, FAKE) == kvq.ERR_INVALID_ARGUMENT
+    assert _prefill(cfg, ok, FAKE, 11, FAKE) == kvq.ERR_INVALID_ARGUMENT
+    assert "n_q" in kvq.lib().kvq_last_error().decode()
+    assert _prefill(cfg, ok, FAKE + 8, 5, FAKE) == kvq.ERR_INVALID_ARGUMENT
+    assert _prefill(cfg, ok, FAKE, 5, None) == kvq.ERR_INVALID_ARGUMENT
+    assert _prefill(cfg, ok, FAKE, 5, FAKE, odt=9) == kvq.ERR_INVALID_ARGUMENT
+    assert kvq.lib().kvq_prefill_attention(ctypes.byref(cfg), ctypes.byref(ok), FAKE, 5,
+                                           float("inf"), FAKE, kvq.F32, None) == \
+        kvq.ERR_INVALID_ARGUMENT
+    # query heads per KV head must divide the 64-row tile
+    for hq, hkv in ((12, 4), (96, 1)):
+        c = _none_cfg(n_q_heads=hq, n_kv_heads=hkv, max_ctx=100)
+        assert _prefill(c, ok, FAKE, 5, FAKE) == kvq.ERR_UNSUPPORTED
+        assert "divide 64" in kvq.lib().kvq_last_error().decode()
 
 
 def test_decode_events_hook():

@@ -31,6 +31,8 @@ sys.path.insert(0, ROOT)
 METRIC = "fused quantized decode attention: effective HBM GB/s (% of peak), µs/step"
 PEAK_HBM_GBS = 8000.0
 DECODE_KERNELS = {"valu": "dec_generic_kernel", "mfma": "dec_mfma_kernel", "lut": "dec_lut_kernel"}
+PREFILL_METRIC = "chunked prefill attention over the quantized cache: TFLOP/s (QK^T + PV, causal)"
+PEAK_MFMA_F16_TFLOPS = 2500.0
 
 
 def log(*a):
@@ -38,7 +40,7 @@ def log(*a):
 
 
 KERNEL_SOURCES = {"dec_mfma_kernel": "decode_mfma.hip", "dec_lut_kernel": "decode_lut.hip",
-                  "dec_generic_kernel": "decode_generic.hip"}
+                  "dec_generic_kernel": "decode_generic.hip", "pre_mfma_kernel": "prefill_mfma.hip"}
 
 
 def kernel_source_sha(kernel: str) -> str:
@@ -131,6 +133,9 @@ def main():
                     help="upper bound on split-K partitions of the token axis (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--prefill", type=int, default=0, metavar="N",
+                    help="measure chunked prefill instead: each step appends an N-token chunk to "
+                         "a cache of ctx - N tokens and runs causal attention for its N queries")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 launches), the reference "
                          "point for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -168,6 +173,9 @@ def main():
                           "launches": 3}), flush=True)
         return
     w = make_workload(args.config, ctx=args.ctx)
+    if args.prefill:
+        bench_prefill(args, w, dev)
+        return
     serving = args.config == 5
     K, W = args.steps, args.warmup
     # warm-up, the timed steps, then as many instrumented steps (serving: one
@@ -325,6 +333,116 @@ def main():
     }
     if cycle is not None:
         res["serving_cycle"] = cycle
+    print(json.dumps(res), flush=True)
+
+
+def prefill_flops(batch: int, n_q_heads: int, head_dim: int, n_ctx: int, n_q: int) -> int:
+    """Algorithmic flops of causal prefill attention: query i of the last n_q
+    tokens scores n_ctx - n_q + i + 1 keys (2 d flops each) and sums as many
+    values (2 d flops each)."""
+    keys = n_q * (n_ctx - n_q + 1) + n_q * (n_q - 1) // 2
+    return 4 * head_dim * batch * n_q_heads * keys
+
+
+def bench_prefill(args, w, dev):
+    """Chunked prefill: a step appends one chunk of N tokens (keys and values)
+    to a cache of ctx - N tokens and runs causal attention for the chunk's N
+    queries over all ctx tokens; the cache is then cut back to ctx - N so
+    that every step does the same work (the next append rewrites the same
+    rows)."""
+    import torch
+    from quantized_kv_cache_04_amd import kvq
+    from synth import make_prefill_queries
+    from synth.workloads import make_inputs
+
+    N, K, W = args.prefill, args.steps, args.warmup
+    T = w.ctx
+    T0 = T - N
+    if not 0 < N <= T:
+        print("--prefill N needs 0 < N <= ctx", file=sys.stderr)
+        sys.exit(2)
+    cfg = kvq.config_from_workload(w, max_ctx=T)
+    stream = torch.cuda.Stream()
+    wl = f"{CONFIG_NAME(w)}_prefill{N}"
+    log(f"workload {wl}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} T={T} chunk={N}")
+    with torch.cuda.stream(stream):
+        inputs = make_inputs(w, dev)
+        c = kvq.Cache(cfg, device=dev, k_codebook=inputs["k_codebook"],
+                      v_codebook=inputs["v_codebook"])
+        if T0:
+            c.append(inputs["k"][:, :T0].contiguous(), inputs["v"][:, :T0].contiguous(),
+                     stream=stream)
+        kc = inputs["k"][:, T0:].contiguous()
+        vc = inputs["v"][:, T0:].contiguous()
+        del inputs
+        q = make_prefill_queries(w, N, dev)
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        c.append(kc, vc, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        c.prefill(q, out=out, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        c.n_ctx = T0
+
+    with torch.cuda.stream(stream):
+        for _ in range(W):
+            step()
+    torch.cuda.synchronize()
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    t_start, t_end = mk(), mk()
+    with torch.cuda.stream(stream):
+        t_start.record(stream)
+        for _ in range(K):
+            step()
+        t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / K
+    evs = [[mk(), mk(), mk()] for _ in range(K)]
+    with torch.cuda.stream(stream):
+        for k in range(K):
+            step(evs[k])
+    torch.cuda.synchronize()
+    app_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    pre_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    app_avg, pre_avg = sum(app_ms) / K, sum(pre_ms) / K
+    flops = prefill_flops(w.batch, w.n_q_heads, w.head_dim, T, N)
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (pre_avg * 1e-3) / 1e12
+    log(f"step {ms_step * 1e3:.1f} us: append {app_avg * 1e3:.1f} us, prefill attention "
+        f"{pre_avg * 1e3:.1f} us (p10 {pre_ms[K // 10] * 1e3:.1f}, p90 {pre_ms[(9 * K) // 10] * 1e3:.1f})"
+        f" -> {achieved:.1f} TFLOP/s ({achieved / PEAK_MFMA_F16_TFLOPS:.1%} of the fp16 MFMA peak)")
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16-mfma/f32",
+        "data": "synthetic (seeded normal K/V with the workload's outlier structure)",
+        "config": {"workload": wl, "batch": w.batch, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ctx": T, "chunk": N,
+                   "k_format": _fmt(w.k), "v_format": _fmt(w.v),
+                   "step": "append an N-token chunk + causal prefill attention for it"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
+                     "traffic": None, "kernel": "pre_mfma_kernel",
+                     "avg_launch_us": round(pre_avg * 1e3, 2),
+                     "append_us": round(app_avg * 1e3, 2),
+                     "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": None,
+    }
     print(json.dumps(res), flush=True)
 
 

@@ -55,6 +55,7 @@ struct PreLds {
   float kf[kBlk][kD + 4];                          // 16.5 KB
   uint4 khi[kBlk][kD / 8], klo[kBlk][kD / 8];     // 2 x 8 KB
   uint4 vhi[kD][kBlk / 8], vlo[kD][kBlk / 8];     // 2 x 8 KB
+  uint16_t cbk[kD][16], cbv[kD][16];               // codebooks of the KV head
   double theta[kD / 2];
 };
 
@@ -90,19 +91,112 @@ __device__ __forceinline__ void load8(const uint16_t* p, int bf16, float x[8]) {
   for (int e = 0; e < 8; ++e) x[e] = elem2f((uint16_t)(w[e >> 1] >> (16 * (e & 1))), bf16);
 }
 
-// Outliers replace their dense value in the staged block: entry e of the
-// CSR row of token tk (all heads of the token) per thread; entries of other
-// heads are skipped.  Keys go to the fp32 stage (RoPE follows), values to
-// the fp16 planes.
+// The 8 codes of block m (codes 8 m .. 8 m + 7) of the 32-code segment at p,
+// in the packing of include/kvq.h: bytes (8-bit), nibbles (4-bit) or, for 3
+// bits, the two low bits of pair (8m + r, 8m + r + 4) at bits 2p and
+// 16 + 2p of D[m / 2] (p = 4 (m % 2) + r) and the high bits at bits P and
+// 16 + P of D2 (P = 8 (m / 2) + 2r + m % 2).  Only the dwords holding block m
+// are read.
+template <int BITS>
+__device__ __forceinline__ void block_codes(const uint8_t* p, int m, uint32_t c[8]) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+  if (BITS == 8) {
+    const uint2 v = reinterpret_cast<const uint2*>(p)[m];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = ((e < 4 ? v.x : v.y) >> (8 * (e & 3))) & 255u;
+  } else if (BITS == 4) {
+    const uint32_t v = w[m];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = (v >> (4 * e)) & 15u;
+  } else {
+    const uint32_t lo = w[m >> 1] >> (8 * (m & 1)), hi = w[2] >> (8 * (m >> 1) + (m & 1));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = 2 * (e & 3) + 16 * (e >> 2);
+      c[e] = ((lo >> sh) & 3u) | (((hi >> sh) & 1u) << 2);
+    }
+  }
+}
+
+__device__ __forceinline__ float uniform_x(uint32_t code, uint32_t pz) {
+  return fmaf((float)code, h2f((uint16_t)(pz & 0xffff)), h2f((uint16_t)(pz >> 16)));
+}
+
+// Keys of quantized token tq: channels 32 m + 8 sq + e of blocks m = 2 hm and
+// 2 hm + 1 (one 32-code segment of the key row), dense values in fp32.
+template <int BITS>
+__device__ __forceinline__ void key_codes(const DevTensor& k, const DevShape& sh, const PreLds& S,
+                                          int bh, int64_t tq, int sq, int hm, float x[2][8]) {
+  const uint8_t* seg = k.codes + ((int64_t)bh * sh.Tcap + tq) * k.row_bytes + sq * 4 * BITS;
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm) {
+    const int m = 2 * hm + mm, c0 = 32 * m + 8 * sq;
+    uint32_t cd[8];
+    block_codes<BITS>(seg, m, cd);
+    if (k.quant == KVQ_QUANT_CODEBOOK) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[mm][e] = h2f(S.cbk[c0 + e][cd[e]]);
+    } else if (k.per_channel) {
+      const uint4* pp = reinterpret_cast<const uint4*>(
+          static_cast<const uint32_t*>(k.params) +
+          ((int64_t)bh * (sh.Tcap / k.G) + tq / k.G) * kHeadDim + c0);
+      const uint4 p0 = pp[0], p1 = pp[1];
+      const uint32_t pz[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[mm][e] = uniform_x(cd[e], pz[e]);
+    } else if (k.quant == KVQ_QUANT_SYM_Q8_0) {
+      const float sc = h2f(static_cast<const uint16_t*>(k.params)[((int64_t)bh * sh.Tcap + tq) * k.ng + c0 / k.G]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[mm][e] = (float)(int8_t)cd[e] * sc;
+    } else {
+      const uint32_t pz = static_cast<const uint32_t*>(k.params)[((int64_t)bh * sh.Tcap + tq) * k.ng + c0 / k.G];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[mm][e] = uniform_x(cd[e], pz);
+    }
+  }
+}
+
+// Values of channel c for tokens 16 hv + u (u < 16) of the 32-token value
+// tile that starts at quantized token tq0; tokens at or past n_valid are 0.
+// Token 4q + r (+16 hv) of channel c is code 8m + r + 4hv of segment c / 64
+// of tile lane 16q + c % 16 (m = (c / 16) % 4).
+template <int BITS>
+__device__ __forceinline__ void value_codes(const DevTensor& v, const DevShape& sh, int bh,
+                                            int64_t tq0, int c, int hv, int n_valid, float x[16]) {
+  const uint8_t* tile = v.codes + ((int64_t)bh * sh.Tcap + tq0) * v.row_bytes;
+  const int i = c & 15, sg = c >> 6, m = (c >> 4) & 3;
+  uint32_t cd[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t blk[8];
+    block_codes<BITS>(tile + (16 * q + i) * 8 * BITS + sg * 4 * BITS, m, blk);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cd[4 * q + r] = hv ? blk[4 + r] : blk[r];
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int tk = 16 * hv + u;
+    const int64_t rec = ((int64_t)bh * sh.Tcap + tq0 + tk) * v.ng + c / v.G;
+    float y;
+    if (v.quant == KVQ_QUANT_SYM_Q8_0)
+      y = (float)(int8_t)cd[u] * h2f(static_cast<const uint16_t*>(v.params)[rec]);
+    else
+      y = uniform_x(cd[u], static_cast<const uint32_t*>(v.params)[rec]);
+    x[u] = tk < n_valid ? y : 0.f;
+  }
+}
+
+// Outliers replace their dense value in the staged tile (quantized tokens
+// tq0 + tk, tk < n_valid): entry e of the CSR row of token tk (all heads of
+// the token) per thread; entries of other heads are skipped.  Keys go to the
+// fp32 stage (RoPE follows), values to the fp16 planes.
 template <bool KEY>
 __device__ __forceinline__ void stage_outliers(const DevTensor& ten, PreLds& S, int tid, int b,
-                                               int h, int t0, int n_sink, int p_max,
-                                               int64_t Tcap) {
+                                               int h, int64_t tq0, int n_valid, int64_t Tcap) {
   const int ko = ten.k_out;
-  for (int idx = tid; idx < kBlk * ko; idx += 256) {
-    const int tk = idx / ko, t = t0 + tk;
-    if (t < n_sink || t > p_max) continue;
-    const int64_t rr = (int64_t)b * Tcap + (t - n_sink);
+  for (int idx = tid; idx < n_valid * ko; idx += 256) {
+    const int tk = idx / ko;
+    const int64_t rr = (int64_t)b * Tcap + tq0 + tk;
     const int e = ten.row_ptr[rr] + idx % ko;
     if (e >= ten.row_ptr[rr + 1]) continue;
     const int cc = (ten.col[e] & 0xfff) - h * kD;
@@ -133,6 +227,12 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
   const int n_qc = a.n_total - a.n_sink;               // quantized tokens
   const int64_t n_full = a.k.per_channel ? (int64_t)(n_qc / a.k.G) * a.k.G : n_qc;
   if (a.rope && tid < kD / 2) S.theta[tid] = pow((double)a.rope_base, -2.0 * tid / (double)kD);
+  if (a.k.quant == KVQ_QUANT_CODEBOOK)
+    for (int idx = tid; idx < kD * 16; idx += 256)
+      S.cbk[idx >> 4][idx & 15] = a.k.codebook[(int64_t)h * kD * 16 + idx];
+  if (a.v.quant == KVQ_QUANT_CODEBOOK)
+    for (int idx = tid; idx < kD * 16; idx += 256)
+      S.cbv[idx >> 4][idx & 15] = a.v.codebook[(int64_t)h * kD * 16 + idx];
   __syncthreads();
 
   // ---- this lane's query row ------------------------------------------------
@@ -186,50 +286,98 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
   for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int n_blocks = p_max / kBlk + 1;
+  // Blocks: the attention sink in 32-token blocks, then the quantized cache
+  // in its own 32-token tiles (so that value tiles and per-channel key
+  // groups stay aligned); positions stay absolute.
+  const int n_sb = (a.n_sink + kBlk - 1) / kBlk;
+  const int n_qb = p_max >= a.n_sink ? (p_max - a.n_sink) / kBlk + 1 : 0;
   const int64_t sink_row0 = (int64_t)bh * a.sink_cap;
-  for (int blk = 0; blk < n_blocks; ++blk) {
-    const int t0 = blk * kBlk;
+  for (int blk = 0; blk < n_sb + n_qb; ++blk) {
+    const bool sinkb = blk < n_sb;
+    const int t0 = sinkb ? blk * kBlk : a.n_sink + (blk - n_sb) * kBlk;   // position of token 0
+    const int64_t tq0 = sinkb ? 0 : (int64_t)(blk - n_sb) * kBlk;         // quantized index of token 0
+    // tokens t0 + tk with tk < n_valid are in this block and visible to the tile
+    const int n_valid = min(kBlk, (sinkb ? min(a.n_sink, p_max + 1) : p_max + 1) - t0);
     __syncthreads();   // the previous block's operand reads are done
-    // ---- phase 1: dense keys to fp32 (token tk, channels 16 kc .. 16 kc + 15)
-    // and values to fp16 planes (channel c, tokens 16 hv .. 16 hv + 15) ------
+    // ---- phase 1: dense keys to fp32 (token tk, channels 32 m + 8 sq + e of
+    // blocks m = 2 hm, 2 hm + 1) and values to fp16 planes (channel c,
+    // tokens 16 hv .. 16 hv + 15) --------------------------------------------
     {
-      const int tk = tid >> 3, kc = tid & 7, t = t0 + tk;
-#pragma unroll 2
-      for (int u = 0; u < 16; ++u) {
-        const int c = 16 * kc + u;
-        float x = 0.f;
-        if (t <= p_max)
-          x = t < a.n_sink ? elem2f(a.k_sink[(sink_row0 + t) * kD + c], a.sh.kv_bf16)
-                           : deq_key(a.k, a.sh, bh, h, t - a.n_sink, c, n_full);
-        S.kf[tk][c] = x;
+      const int tk = tid >> 3, sq = (tid & 7) >> 1, hm = tid & 1;
+      float x[2][8];
+      const int64_t tq = tq0 + tk;
+      if (tk >= n_valid) {
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[mm][e] = 0.f;
+      } else if (sinkb || a.k.quant == KVQ_QUANT_NONE ||
+                 (a.k.per_channel && tq >= n_full)) {
+        // raw rows: the sink, a raw cache, or the per-channel tail
+        const uint16_t* row =
+            sinkb ? a.k_sink + (sink_row0 + t0 + tk) * kD
+            : a.k.quant == KVQ_QUANT_NONE
+                ? reinterpret_cast<const uint16_t*>(a.k.codes) + ((int64_t)bh * a.sh.Tcap + tq) * kD
+                : a.k.tail + ((int64_t)bh * a.k.G + (tq - n_full)) * kD;
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) load8(row + 32 * (2 * hm + mm) + 8 * sq, a.sh.kv_bf16, x[mm]);
+      } else if (a.k.bits == 4) {
+        key_codes<4>(a.k, a.sh, S, bh, tq, sq, hm, x);
+      } else if (a.k.bits == 3) {
+        key_codes<3>(a.k, a.sh, S, bh, tq, sq, hm, x);
+      } else {
+        key_codes<8>(a.k, a.sh, S, bh, tq, sq, hm, x);
+      }
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        float4* dst = reinterpret_cast<float4*>(&S.kf[tk][32 * (2 * hm + mm) + 8 * sq]);
+        dst[0] = float4{x[mm][0], x[mm][1], x[mm][2], x[mm][3]};
+        dst[1] = float4{x[mm][4], x[mm][5], x[mm][6], x[mm][7]};
       }
     }
     {
-      const int c = tid >> 1, hv = tid & 1, sw = (c >> 2) & 3;
-      _Float16* vh = reinterpret_cast<_Float16*>(&S.vhi[c][0]);
-      _Float16* vl = reinterpret_cast<_Float16*>(&S.vlo[c][0]);
-#pragma unroll 2
-      for (int u = 0; u < 16; ++u) {
-        const int tk = 16 * hv + u, t = t0 + tk;
-        float x = 0.f;
-        if (t <= p_max)
-          x = t < a.n_sink ? elem2f(a.v_sink[(sink_row0 + t) * kD + c], a.sh.kv_bf16)
-                           : deq_value(a.v, a.sh, bh, h, t - a.n_sink, c);
-        const _Float16 xh = (_Float16)x;
-        const int at = 8 * ((tk >> 3) ^ sw) + (tk & 7);
-        vh[at] = xh;
-        vl[at] = (_Float16)(x - (float)xh);
+      const int c = tid >> 1, hv = tid & 1;
+      float x[16];
+      if (sinkb || a.v.quant == KVQ_QUANT_NONE) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int tk = 16 * hv + u;
+          const uint16_t* row =
+              sinkb ? a.v_sink + (sink_row0 + t0 + tk) * kD
+                    : reinterpret_cast<const uint16_t*>(a.v.codes) + ((int64_t)bh * a.sh.Tcap + tq0 + tk) * kD;
+          x[u] = tk < n_valid ? elem2f(row[c], a.sh.kv_bf16) : 0.f;
+        }
+      } else if (a.v.quant == KVQ_QUANT_CODEBOOK) {
+        // pair tiles: byte 32 l + tau holds channels l (low nibble) and l + 64
+        const uint4 w = *reinterpret_cast<const uint4*>(
+            a.v.codes + ((int64_t)bh * a.sh.Tcap + tq0) * a.v.row_bytes + 32 * (c & 63) + 16 * hv);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const uint32_t code = (ww[u >> 2] >> (8 * (u & 3) + 4 * (c >> 6))) & 15u;
+          x[u] = 16 * hv + u < n_valid ? h2f(S.cbv[c][code]) : 0.f;
+        }
+      } else if (a.v.bits == 4) {
+        value_codes<4>(a.v, a.sh, bh, tq0, c, hv, n_valid, x);
+      } else if (a.v.bits == 3) {
+        value_codes<3>(a.v, a.sh, bh, tq0, c, hv, n_valid, x);
+      } else {
+        value_codes<8>(a.v, a.sh, bh, tq0, c, hv, n_valid, x);
       }
+      const int sw = (c >> 2) & 3;
+      uint4 hi, lo;
+      split8(x, hi, lo);
+      S.vhi[c][(2 * hv) ^ sw] = hi;
+      S.vlo[c][(2 * hv) ^ sw] = lo;
+      split8(x + 8, hi, lo);
+      S.vhi[c][(2 * hv + 1) ^ sw] = hi;
+      S.vlo[c][(2 * hv + 1) ^ sw] = lo;
     }
-    // ---- phase 2: outliers replace their dense value (CSR row of a token
-    // over all heads; entry e of token tk per thread) ---------------------------
-    if (a.k.k_out > 0 || a.v.k_out > 0) {
+    // ---- phase 2: outliers replace their dense value -------------------------
+    if (!sinkb && (a.k.k_out > 0 || a.v.k_out > 0)) {
       __syncthreads();
-      if (a.k.k_out > 0)
-        stage_outliers<true>(a.k, S, tid, b, h, t0, a.n_sink, p_max, a.sh.Tcap);
-      if (a.v.k_out > 0)
-        stage_outliers<false>(a.v, S, tid, b, h, t0, a.n_sink, p_max, a.sh.Tcap);
+      if (a.k.k_out > 0) stage_outliers<true>(a.k, S, tid, b, h, tq0, n_valid, a.sh.Tcap);
+      if (a.v.k_out > 0) stage_outliers<false>(a.v, S, tid, b, h, tq0, n_valid, a.sh.Tcap);
     }
     __syncthreads();
     // ---- phase 3: RoPE at the key's position, then fp16 planes (token tk,
@@ -244,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
       x0[4] = a1.x; x0[5] = a1.y; x0[6] = a1.z; x0[7] = a1.w;
       x1[0] = b0.x; x1[1] = b0.y; x1[2] = b0.z; x1[3] = b0.w;
       x1[4] = b1.x; x1[5] = b1.y; x1[6] = b1.z; x1[7] = b1.w;
-      if (a.rope && t <= p_max) {
+      if (a.rope && tk < n_valid) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float cs, sn;
@@ -286,8 +434,8 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
     float mloc = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int t = t0 + 8 * q4 + j;
-      s[j] = t <= p_row ? acc[j >> 2][j & 3] : -INFINITY;
+      const int tk = 8 * q4 + j;
+      s[j] = tk < n_valid && t0 + tk <= p_row ? acc[j >> 2][j & 3] : -INFINITY;
       mloc = fmaxf(mloc, s[j]);
     }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));

@@ -136,6 +136,9 @@ def main():
     ap.add_argument("--prefill", type=int, default=0, metavar="N",
                     help="measure chunked prefill instead: each step appends an N-token chunk to "
                          "a cache of ctx - N tokens and runs causal attention for its N queries")
+    ap.add_argument("--encode", type=int, default=0, metavar="N",
+                    help="measure bulk encode instead: each step appends N tokens per sequence "
+                         "to an empty cache")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 launches), the reference "
                          "point for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -175,6 +178,9 @@ def main():
     w = make_workload(args.config, ctx=args.ctx)
     if args.prefill:
         bench_prefill(args, w, dev)
+        return
+    if args.encode:
+        bench_encode(args, w, dev)
         return
     serving = args.config == 5
     K, W = args.steps, args.warmup
@@ -444,6 +450,66 @@ def bench_prefill(args, w, dev):
         "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
+
+
+def bench_encode(args, w, dev):
+    """Bulk encode (the prefill append): a step appends N tokens per sequence
+    to an empty cache (the cache is cut back to 0 tokens after each step).
+    Bytes per step: the fp16/bf16 keys and values read plus the payload
+    written."""
+    import torch
+    from quantized_kv_cache_04_amd import kvq
+    from synth import make_workload
+    from synth.workloads import make_inputs
+
+    N, K, W = args.encode, args.steps, args.warmup
+    wn = make_workload(w.cfg_id, ctx=N, batch=w.batch, n_kv_heads=w.n_kv_heads)
+    cfg = kvq.config_from_workload(wn, max_ctx=N)
+    stream = torch.cuda.Stream()
+    wl = f"{CONFIG_NAME(w)}_encode{N}"
+    with torch.cuda.stream(stream):
+        inputs = make_inputs(wn, dev)
+        c = kvq.Cache(cfg, device=dev, k_codebook=inputs["k_codebook"],
+                      v_codebook=inputs["v_codebook"])
+        kin, vin = inputs["k"], inputs["v"]
+    torch.cuda.synchronize()
+
+    def step():
+        c.n_ctx = 0
+        c.append(kin, vin, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(W):
+            step()
+    torch.cuda.synchronize()
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    evs = [[mk(), mk()] for _ in range(K)]
+    with torch.cuda.stream(stream):
+        for e in evs:
+            e[0].record(stream)
+            step()
+            e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    ms_avg = sum(ms) / K
+    in_bytes = 2 * kin.numel() * kin.element_size()
+    out_bytes = kvq.cache_bytes(cfg, N)
+    gbs = (in_bytes + out_bytes) / (ms_avg * 1e-3) / 1e9
+    log(f"{wl}: append of {N} tokens x {wn.batch} sequences: {ms_avg * 1e3:.1f} us "
+        f"(p10 {ms[K // 10] * 1e3:.1f}, p90 {ms[(9 * K) // 10] * 1e3:.1f}); "
+        f"{in_bytes / 1e6:.1f} MB in + {out_bytes / 1e6:.1f} MB out -> {gbs:.0f} GB/s "
+        f"({gbs / PEAK_HBM_GBS:.1%} of peak)")
+    print(json.dumps({
+        "metric": "bulk encode (append) GB/s: K/V read + payload written", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_avg, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded normal K/V with the workload's outlier structure)",
+        "config": {"workload": wl, "batch": wn.batch, "n_kv_heads": wn.n_kv_heads, "tokens": N,
+                   "k_format": _fmt(wn.k), "v_format": _fmt(wn.v)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "encode launches of one append", "bytes_per_step": in_bytes + out_bytes},
+        "cpu_baseline": None}), flush=True)
 
 
 def CONFIG_NAME(w) -> str:

@@ -90,6 +90,72 @@ __device__ __forceinline__ void encode_pair(const DevTensor& t, int h, int lane,
   if (writer) static_cast<uint32_t*>(prm_row)[grp] = (uint32_t)sh | ((uint32_t)zh << 16);
 }
 
+// Quantize channels c0 .. c0 + 7 (c0 = 8 j8) of one row whose 128 channels
+// are held by 16 lanes (j8 = lane % 16; the row segment is lane / 16).  For
+// per-token uniform formats the group statistics are reduced over the G/8
+// lanes of the group.  Writes the group's parameters (first lane of each
+// group) at ``prm_row`` unless it is null, and returns the 8 codes as bytes
+// (two's complement for q8_0).
+__device__ __forceinline__ uint2 encode8(const DevTensor& t, int h, int j8, const float x[8],
+                                         void* prm_row) {
+  const int c0 = 8 * j8;
+  uint32_t q[8];
+  if (t.quant == KVQ_QUANT_CODEBOOK) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = cb_code(t.codebook + ((int64_t)h * kD + c0 + e) * 16, x[e]);
+  } else {
+    float lo = x[0], hi = x[0], am = fabsf(x[0]);
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+      lo = fminf(lo, x[e]);
+      hi = fmaxf(hi, x[e]);
+      am = fmaxf(am, fabsf(x[e]));
+    }
+    const int gl = t.G >> 3;   // lanes of a group
+    for (int off = 1; off < gl; off <<= 1) {
+      lo = fminf(lo, __shfl_xor(lo, off, 64));
+      hi = fmaxf(hi, __shfl_xor(hi, off, 64));
+      am = fmaxf(am, __shfl_xor(am, off, 64));
+    }
+    const bool writer = prm_row != nullptr && (j8 & (gl - 1)) == 0;
+    const int grp = c0 / t.G;
+    if (t.quant == KVQ_QUANT_SYM_Q8_0) {
+      const uint16_t sh = f2h_rn(am / 127.0f);
+      const float s = h2f(sh);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = s == 0.0f ? 0.0f : rintf(x[e] / s);
+        v = fminf(fmaxf(v, -128.0f), 127.0f);
+        q[e] = (uint32_t)((int)v & 0xff);
+      }
+      if (writer) static_cast<uint16_t*>(prm_row)[grp] = sh;
+    } else {
+      const float qmax = (float)((1 << t.bits) - 1);
+      uint16_t sh;
+      if (t.quant == KVQ_QUANT_ASYM_MINMAX)
+        sh = f2h_rn((hi - lo) / qmax);
+      else
+        sh = f2h_rn(am / (float)((1 << (t.bits - 1)) - 1));
+      const uint16_t zh = f2h_rn(lo);
+      const float s = h2f(sh), z = h2f(zh);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = s == 0.0f ? 0.0f : rintf((x[e] - z) / s);
+        q[e] = (uint32_t)fminf(fmaxf(v, 0.0f), qmax);
+      }
+      if (writer) static_cast<uint32_t*>(prm_row)[grp] = (uint32_t)sh | ((uint32_t)zh << 16);
+    }
+  }
+  return uint2{q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
+               q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24)};
+}
+
+__device__ __forceinline__ void unpack8(uint4 v, int is_bf16, float x[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = elem2f((uint16_t)(w[e >> 1] >> (16 * (e & 1))), is_bf16);
+}
+
 // Dword W of a key row, assembled from the row's codes in LDS.
 __device__ __forceinline__ uint32_t k_row_dword(const uint8_t* rowc, int bits, int W) {
   const int q = W / bits, j = W % bits;
@@ -102,44 +168,50 @@ __device__ __forceinline__ uint32_t k_row_dword(const uint8_t* rowc, int bits, i
 }
 
 // ---- per-token rows: keys (K-row layout) and raw rows for NONE --------------
-// One wave per row (b, new token, kv head); 4 rows per 256-thread block.
+// 16 lanes per row (b, new token, kv head), 8 channels a lane; 16 rows per
+// 256-thread block.
 __global__ __launch_bounds__(256) void enc_rows_kernel(DevShape sh, DevTensor t, const void* x_new,
                                                        int64_t n_ctx, int n_new) {
-  __shared__ uint8_t rowc[4][kD];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ uint8_t rowc[16][kD];
+  const int tid = threadIdx.x, rl = tid >> 4, j8 = tid & 15;
   const int64_t nrows = (int64_t)sh.B * n_new * sh.Hkv;
-  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-  const bool active = r < nrows;
-  int b = 0, h = 0;
-  int64_t tpos = 0;
-  uint32_t q0 = 0, q1 = 0;
-  if (active) {
+  auto row_of = [&](int64_t r, int& h) -> int64_t {   // cache row of block row r
     h = (int)(r % sh.Hkv);
     const int64_t bt = r / sh.Hkv;
-    b = (int)(bt / n_new);
-    tpos = n_ctx + bt % n_new;
-    const int64_t rin = ((int64_t)b * sh.in_tok + sh.in_off + bt % n_new) * sh.Hkv + h;
-    const uint32_t pair = static_cast<const uint32_t*>(x_new)[rin * (kD / 2) + lane];
-    const int64_t row = ((int64_t)b * sh.Hkv + h) * sh.Tcap + tpos;
-    if (t.quant == KVQ_QUANT_NONE) {
-      reinterpret_cast<uint32_t*>(t.codes)[row * (kD / 2) + lane] = pair;
-    } else {
-      const float x0 = elem2f((uint16_t)(pair & 0xffff), sh.kv_bf16);
-      const float x1 = elem2f((uint16_t)(pair >> 16), sh.kv_bf16);
-      void* prm = nullptr;
-      if (t.params) prm = static_cast<uint8_t*>(t.params) + row * (int64_t)t.ng *
-                          (t.quant == KVQ_QUANT_SYM_Q8_0 ? 2 : 4);
-      encode_pair(t, h, lane, x0, x1, prm, q0, q1);
-      rowc[wave][2 * lane] = (uint8_t)q0;
-      rowc[wave][2 * lane + 1] = (uint8_t)q1;
-    }
+    const int b = (int)(bt / n_new);
+    return ((int64_t)b * sh.Hkv + h) * sh.Tcap + n_ctx + bt % n_new;
+  };
+  const int64_t r = (int64_t)blockIdx.x * 16 + rl;
+  const bool active = r < nrows;
+  uint4 v = uint4{0u, 0u, 0u, 0u};
+  int h = 0;
+  int64_t row = 0;
+  if (active) {
+    row = row_of(r, h);
+    const int64_t bt = r / sh.Hkv;
+    const int64_t rin = ((int64_t)(bt / n_new) * sh.in_tok + sh.in_off + bt % n_new) * sh.Hkv + h;
+    v = reinterpret_cast<const uint4*>(x_new)[rin * (kD / 8) + j8];
   }
-  if (t.quant == KVQ_QUANT_NONE) return;
+  if (t.quant == KVQ_QUANT_NONE) {
+    if (active) reinterpret_cast<uint4*>(t.codes)[row * (kD / 8) + j8] = v;
+    return;
+  }
+  float x[8];
+  unpack8(v, sh.kv_bf16, x);
+  void* prm = nullptr;
+  if (active && t.params)
+    prm = static_cast<uint8_t*>(t.params) + row * (int64_t)t.ng * (t.quant == KVQ_QUANT_SYM_Q8_0 ? 2 : 4);
+  const uint2 cq = encode8(t, h, j8, x, prm);
+  *reinterpret_cast<uint2*>(&rowc[rl][8 * j8]) = cq;
   __syncthreads();
-  if (active && lane < 4 * t.bits) {
-    const int64_t row = ((int64_t)b * sh.Hkv + h) * sh.Tcap + tpos;
-    reinterpret_cast<uint32_t*>(t.codes + row * t.row_bytes)[lane] =
-        k_row_dword(rowc[wave], t.bits, lane);
+  const int dw_row = 4 * t.bits;
+  for (int idx = tid; idx < 16 * dw_row; idx += 256) {
+    const int r2 = idx / dw_row, W = idx % dw_row;
+    const int64_t rr = (int64_t)blockIdx.x * 16 + r2;
+    if (rr >= nrows) continue;
+    int h2;
+    const int64_t row2 = row_of(rr, h2);
+    reinterpret_cast<uint32_t*>(t.codes + row2 * t.row_bytes)[W] = k_row_dword(rowc[r2], t.bits, W);
   }
 }
 
@@ -156,21 +228,32 @@ __global__ __launch_bounds__(256) void enc_vtile_kernel(DevShape sh, DevTensor t
   const int64_t tile = tile0 + blockIdx.x;
   const int64_t t_begin = tile * kTile;
   const int64_t lo_new = n_ctx, hi_new = n_ctx + n_new;
-  for (int tau = wave; tau < kTile; tau += 4) {
+  // 16 lanes per token, 8 channels a lane: the wave takes tokens
+  // tau = 8 wave + 4 p + (lane / 16), p = 0, 1; both loads first
+  const int sub = lane >> 4, j8 = lane & 15;
+  uint4 xin[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int64_t tpos = t_begin + 8 * wave + 4 * p + sub;
+    xin[p] = uint4{0u, 0u, 0u, 0u};
+    if (tpos >= lo_new && tpos < hi_new) {
+      const int64_t rin = (((int64_t)b * sh.in_tok + sh.in_off + (tpos - n_ctx)) * sh.Hkv + h);
+      xin[p] = reinterpret_cast<const uint4*>(x_new)[rin * (kD / 8) + j8];
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int tau = 8 * wave + 4 * p + sub;
     const int64_t tpos = t_begin + tau;
-    if (tpos < lo_new || tpos >= hi_new) continue;       // wave-uniform
-    const int64_t rin = (((int64_t)b * sh.in_tok + sh.in_off + (tpos - n_ctx)) * sh.Hkv + h);
-    const uint32_t pair = static_cast<const uint32_t*>(x_new)[rin * (kD / 2) + lane];
-    const float x0 = elem2f((uint16_t)(pair & 0xffff), sh.kv_bf16);
-    const float x1 = elem2f((uint16_t)(pair >> 16), sh.kv_bf16);
+    const bool fresh = tpos >= lo_new && tpos < hi_new;
+    float x[8];
+    unpack8(xin[p], sh.kv_bf16, x);
     const int64_t row = ((int64_t)b * sh.Hkv + h) * sh.Tcap + tpos;
     void* prm = nullptr;
-    if (t.params) prm = static_cast<uint8_t*>(t.params) + row * (int64_t)t.ng *
-                        (t.quant == KVQ_QUANT_SYM_Q8_0 ? 2 : 4);
-    uint32_t q0, q1;
-    encode_pair(t, h, lane, x0, x1, prm, q0, q1);
-    codes[tau][2 * lane] = (uint8_t)q0;
-    codes[tau][2 * lane + 1] = (uint8_t)q1;
+    if (fresh && t.params)
+      prm = static_cast<uint8_t*>(t.params) + row * (int64_t)t.ng * (t.quant == KVQ_QUANT_SYM_Q8_0 ? 2 : 4);
+    const uint2 cq = encode8(t, h, j8, x, prm);
+    if (fresh) *reinterpret_cast<uint2*>(&codes[tau][8 * j8]) = cq;
   }
   __syncthreads();
   const int bits = t.bits;
@@ -217,47 +300,75 @@ __global__ __launch_bounds__(256) void enc_vtile_kernel(DevShape sh, DevTensor t
 }
 
 // ---- per-channel keys ---------------------------------------------------------
-// Quantize completed token groups: one block of 128 threads (one per
-// channel) per (group, b*Hkv + h).  Values of the group that arrived in
-// earlier calls come from the fp16/bf16 tail.
-__global__ __launch_bounds__(128) void enc_kchan_flush_kernel(DevShape sh, DevTensor t,
+// Quantize completed token groups: one block of 256 threads per (group,
+// b*Hkv + h).  The group's G rows (tokens that arrived in earlier calls come
+// from the fp16/bf16 tail) are staged in LDS with 16-byte loads; two threads
+// per channel reduce min / max / absmax over half of the tokens each and
+// encode them.
+__global__ __launch_bounds__(256) void enc_kchan_flush_kernel(DevShape sh, DevTensor t,
                                                               const void* x_new, int64_t n_ctx,
                                                               int n_new, int64_t g0) {
-  extern __shared__ uint8_t gcodes[];                     // [G][128]
-  const int c = threadIdx.x;
+  extern __shared__ uint4 kch_lds[];                      // raw [G][128] elements, codes [G][128]
+  __shared__ float red[3][kD];
+  const int G = t.G;
+  uint16_t* raw = reinterpret_cast<uint16_t*>(kch_lds);
+  uint8_t* gcodes = reinterpret_cast<uint8_t*>(raw + (int64_t)G * kD);
+  const int tid = threadIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / sh.Hkv, h = bh % sh.Hkv;
-  const int G = t.G;
   const int64_t gi = g0 + blockIdx.x;
   const int64_t p0 = gi * G;
   const uint16_t* tail = t.tail + (int64_t)bh * G * kD;
-  auto value = [&](int k) -> float {
+  for (int idx = tid; idx < G * (kD / 8); idx += 256) {
+    const int k = idx / (kD / 8), u = idx % (kD / 8);
     const int64_t p = p0 + k;
-    if (p < n_ctx) return elem2f(tail[(int64_t)k * kD + c], sh.kv_bf16);
-    const int64_t rin = ((int64_t)b * sh.in_tok + sh.in_off + (p - n_ctx)) * sh.Hkv + h;
-    return load_elem(x_new, rin * kD + c, sh.kv_bf16);
-  };
+    const uint4* src;
+    if (p < n_ctx) {
+      src = reinterpret_cast<const uint4*>(tail + (int64_t)k * kD);
+    } else {
+      const int64_t rin = ((int64_t)b * sh.in_tok + sh.in_off + (p - n_ctx)) * sh.Hkv + h;
+      src = reinterpret_cast<const uint4*>(x_new) + rin * (kD / 8);
+    }
+    kch_lds[idx] = src[u];
+  }
+  __syncthreads();
+  const int c = tid & (kD - 1), half = tid >> 7;
+  const int k0 = half * (G / 2), k1 = k0 + G / 2;
   float lo = INFINITY, hi = -INFINITY, am = 0.0f;
-  for (int k = 0; k < G; ++k) {
-    const float x = value(k);
+  for (int k = k0; k < k1; ++k) {
+    const float x = elem2f(raw[k * kD + c], sh.kv_bf16);
     lo = fminf(lo, x);
     hi = fmaxf(hi, x);
     am = fmaxf(am, fabsf(x));
   }
+  if (half) {
+    red[0][c] = lo;
+    red[1][c] = hi;
+    red[2][c] = am;
+  }
+  __syncthreads();
   const float qmax = (float)((1 << t.bits) - 1);
-  uint16_t shh;
-  if (t.quant == KVQ_QUANT_ASYM_MINMAX)
-    shh = f2h_rn((hi - lo) / qmax);
-  else
-    shh = f2h_rn(am / (float)((1 << (t.bits - 1)) - 1));
-  const uint16_t zh = f2h_rn(lo);
-  const float s = h2f(shh), z = h2f(zh);
-  static_cast<uint32_t*>(t.params)[((int64_t)bh * (sh.Tcap / G) + gi) * kD + c] =
-      (uint32_t)shh | ((uint32_t)zh << 16);
-  for (int k = 0; k < G; ++k) {
+  if (!half) {
+    lo = fminf(lo, red[0][c]);
+    hi = fmaxf(hi, red[1][c]);
+    am = fmaxf(am, red[2][c]);
+    uint16_t shh;
+    if (t.quant == KVQ_QUANT_ASYM_MINMAX)
+      shh = f2h_rn((hi - lo) / qmax);
+    else
+      shh = f2h_rn(am / (float)((1 << (t.bits - 1)) - 1));
+    const uint16_t zh = f2h_rn(lo);
+    static_cast<uint32_t*>(t.params)[((int64_t)bh * (sh.Tcap / G) + gi) * kD + c] =
+        (uint32_t)shh | ((uint32_t)zh << 16);
+    red[0][c] = h2f(shh);
+    red[1][c] = h2f(zh);
+  }
+  __syncthreads();
+  const float s = red[0][c], z = red[1][c];
+  for (int k = k0; k < k1; ++k) {
     uint32_t q = 0;
     if (s != 0.0f) {
-      float v = rintf((value(k) - z) / s);
+      const float v = rintf((elem2f(raw[k * kD + c], sh.kv_bf16) - z) / s);
       q = (uint32_t)fminf(fmaxf(v, 0.0f), qmax);
     }
     gcodes[k * kD + c] = (uint8_t)q;
@@ -265,7 +376,7 @@ __global__ __launch_bounds__(128) void enc_kchan_flush_kernel(DevShape sh, DevTe
   __syncthreads();
   const int dw_per_row = 4 * t.bits;
   uint8_t* rows = t.codes + ((int64_t)bh * sh.Tcap + p0) * t.row_bytes;
-  for (int idx = threadIdx.x; idx < G * dw_per_row; idx += blockDim.x) {
+  for (int idx = tid; idx < G * dw_per_row; idx += 256) {
     const int k = idx / dw_per_row, W = idx % dw_per_row;
     reinterpret_cast<uint32_t*>(rows + (int64_t)k * t.row_bytes)[W] =
         k_row_dword(gcodes + k * kD, t.bits, W);
@@ -274,7 +385,7 @@ __global__ __launch_bounds__(128) void enc_kchan_flush_kernel(DevShape sh, DevTe
   if (p0 < n_ctx) {
     const int used = (int)(n_ctx - p0);
     uint16_t* tw = t.tail + (int64_t)bh * G * kD;
-    for (int k = 0; k < used; ++k) tw[(int64_t)k * kD + c] = 0;
+    for (int idx = tid; idx < used * kD; idx += 256) tw[idx] = 0;
   }
 }
 
@@ -360,7 +471,7 @@ hipError_t launch_encode_tensor(const DevShape& sh, const DevTensor& t, bool is_
                                 hipStream_t stream) {
   const int64_t nrows = (int64_t)sh.B * n_new * sh.Hkv;
   if (t.quant == KVQ_QUANT_NONE || (is_key && !t.per_channel)) {
-    const int64_t blocks = (nrows + 3) / 4;
+    const int64_t blocks = (nrows + 15) / 16;
     hipLaunchKernelGGL(enc_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, sh, t, x_new,
                        n_ctx, n_new);
   } else if (is_key) {
@@ -369,7 +480,7 @@ hipError_t launch_encode_tensor(const DevShape& sh, const DevTensor& t, bool is_
     const int64_t g_first = n_ctx / G, g_end = n1 / G;   // groups [g_first, g_end) complete now
     if (g_end > g_first) {
       hipLaunchKernelGGL(enc_kchan_flush_kernel, dim3((unsigned)(g_end - g_first), sh.B * sh.Hkv),
-                         dim3(128), (size_t)G * kD, stream, sh, t, x_new, n_ctx, n_new, g_first);
+                         dim3(256), (size_t)G * kD * 3, stream, sh, t, x_new, n_ctx, n_new, g_first);
     }
     const int64_t group_start = g_end * G;
     const int64_t p_first = n_ctx > group_start ? n_ctx : group_start;

@@ -405,48 +405,85 @@ __global__ __launch_bounds__(64) void enc_kchan_tail_kernel(DevShape sh, DevTens
 
 // ---- dense-and-sparse outliers (CODEBOOK) ----------------------------------
 // One block per (new token, b).  Keys (|x| bits << 16 | 0xffff - index) are
-// unique, so the k largest are found exactly by a most-significant-bit-first
-// search for the k-th largest key; they are then written in index order.
+// unique, so the k-th largest key is found exactly by a radix select over
+// four digits (bits 30-23, 22-15, 14-7, 6-0), each from LDS histograms (one
+// per wave, to spread atomic contention); the k keys at or above it are then
+// written in index order.
 __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTensor t,
                                                            const void* x_new, int64_t n_ctx,
                                                            int n_new) {
   extern __shared__ uint32_t keys[];                      // [n]
-  __shared__ uint32_t red[8];
-  __shared__ uint32_t scan[256];
+  __shared__ uint32_t hist[4][256];
+  __shared__ uint32_t sel[2];                             // digit, remaining rank
+  __shared__ uint32_t wsum[4];
   const int n = sh.Hkv * kD;
   const int k = t.k_out;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int tn = blockIdx.x, b = blockIdx.y;
   const int64_t tpos = n_ctx + tn;
   const uint16_t* xr = static_cast<const uint16_t*>(x_new) + ((int64_t)b * sh.in_tok + sh.in_off + tn) * n;
-  for (int i = threadIdx.x; i < n; i += 256)
+  for (int i = tid; i < n; i += 256)
     keys[i] = ((uint32_t)(xr[i] & 0x7fffu) << 16) | (0xffffu - (uint32_t)i);
-  __syncthreads();
-  const int per = (n + 255) / 256;
-  const int i0 = threadIdx.x * per, i1 = min(n, i0 + per);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  uint32_t prefix = 0;
-  for (int bit = 30; bit >= 0; --bit) {
-    const uint32_t cand = prefix | (1u << bit);
-    uint32_t cnt = 0;
-    for (int i = i0; i < i1; ++i) cnt += keys[i] >= cand;
-    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
-    if (lane == 0) red[wave] = cnt;
+  uint32_t prefix = 0, mask = 0, kk = (uint32_t)k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = pass < 3 ? 23 - 8 * pass : 0;
+    const uint32_t dmask = pass < 3 ? 0xffu : 0x7fu;
+    for (int i = tid; i < 4 * 256; i += 256) (&hist[0][0])[i] = 0u;
     __syncthreads();
-    const uint32_t tot = red[0] + red[1] + red[2] + red[3];
+    for (int i = tid; i < n; i += 256) {
+      const uint32_t key = keys[i];
+      if ((key & mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & dmask], 1u);
+    }
     __syncthreads();
-    if (tot >= (uint32_t)k) prefix = cand;
+    if (wave == 0) {
+      // lane l holds bins 4l .. 4l + 3; suffix sums over the lanes find the
+      // digit d with count(digit > d) < kk <= count(digit >= d)
+      uint32_t c[4], tot = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int bin = 4 * lane + j;
+        c[j] = hist[0][bin] + hist[1][bin] + hist[2][bin] + hist[3][bin];
+        tot += c[j];
+      }
+      uint32_t suf = tot;                                  // sum over lanes >= this lane
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_down(suf, off, 64);
+        if (lane + off < 64) suf += v;
+      }
+      const uint32_t above = suf - tot;                    // lanes > this lane
+      if (above < kk && kk <= suf) {
+        uint32_t run = above;
+        for (int j = 3; j >= 0; --j) {
+          if (run + c[j] >= kk) {
+            sel[0] = (uint32_t)(4 * lane + j);
+            sel[1] = kk - run;
+            break;
+          }
+          run += c[j];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= sel[0] << shift;
+    mask |= dmask << shift;
+    kk = sel[1];
+    __syncthreads();
   }
+  // prefix is now the k-th largest key: write the k keys >= prefix in index
+  // order (thread tid owns indices per * tid .. per * tid + per - 1)
+  const int per = (n + 255) / 256;
+  const int i0 = tid * per, i1 = min(n, i0 + per);
   uint32_t mine = 0;
   for (int i = i0; i < i1; ++i) mine += keys[i] >= prefix;
-  scan[threadIdx.x] = mine;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const uint32_t v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0u;
-    __syncthreads();
-    scan[threadIdx.x] += v;
-    __syncthreads();
+  uint32_t incl = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
   }
-  uint32_t pos = scan[threadIdx.x] - mine;
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t pos = incl - mine;
+  for (int w = 0; w < wave; ++w) pos += wsum[w];
   const int64_t r = (int64_t)b * sh.Tcap + tpos;
   for (int i = i0; i < i1; ++i) {
     if (keys[i] >= prefix) {
@@ -458,7 +495,7 @@ __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTenso
       ++pos;
     }
   }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     t.row_ptr[r + 1] = (int32_t)(k * (r + 1));
     if (tn == 0) t.row_ptr[r] = (int32_t)(k * r);
   }

@@ -30,6 +30,9 @@ def tensor_payload(fmt: Dict, *, batch: int, n_kv_heads: int, head_dim: int, n_c
     bits = fmt["bits"]
     rb = d * bits // 8
     G = fmt.get("group_size", 0)
+    if q == "fp8_e5m2":
+        # one byte per element and the per-head float32 scales decode reads
+        return B * H * n * d + H * 4
     if q == "codebook":
         total = B * H * n * rb + H * d * 16 * 2
         k = outlier_count(fmt.get("outlier_frac", 0.0), H * d)

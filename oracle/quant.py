@@ -87,6 +87,26 @@ def sym_q8_0(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return codes, s
 
 
+E5M2_MAX = 57344.0
+
+
+def fp8_e5m2_codes(v: np.ndarray) -> np.ndarray:
+    """float32 -> FP8 E5M2 bytes (sign, 5 exponent bits, 2 mantissa bits; the
+    format of the Survey page, section 3.4, for vLLM's fp8 KV cache), round
+    to nearest even; magnitudes past the largest finite value (57344)
+    saturate to it.  The rounding is torch's float8_e5m2 conversion."""
+    import torch
+    v = np.clip(np.asarray(v, dtype=F32), -E5M2_MAX, E5M2_MAX)
+    return torch.from_numpy(np.ascontiguousarray(v)).to(torch.float8_e5m2).view(torch.uint8).numpy()
+
+
+def fp8_e5m2_values(codes: np.ndarray) -> np.ndarray:
+    """FP8 E5M2 bytes -> float64 values."""
+    import torch
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    return torch.from_numpy(c).view(torch.float8_e5m2).to(torch.float64).numpy()
+
+
 def codebook_midpoints(cb: np.ndarray) -> np.ndarray:
     """Decision thresholds between neighbouring centroids: m_i = f32(C_i + C_{i+1}) * 0.5
     for i = 0..14 (float32).  ``cb`` is fp16 [..., 16] ascending."""
@@ -141,7 +161,8 @@ def outlier_mask(x: np.ndarray, k: int) -> np.ndarray:
 # Whole-tensor encoding (logical codes; byte layouts live in layout.py)
 # --------------------------------------------------------------------------
 
-def encode_tensor(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None) -> Dict[str, np.ndarray]:
+def encode_tensor(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None,
+                  head_scale: np.ndarray = None) -> Dict[str, np.ndarray]:
     """Bulk-encode one cache tensor.
 
     ``x`` is float32 [B, T, H, d] holding fp16/bf16 values.  ``fmt`` has
@@ -157,6 +178,11 @@ def encode_tensor(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None) -> Dict
       section 3.4 -- and say nothing of partial groups),
     * ``cols``/``vals`` for codebook outliers ([B, T, k]),
     * ``deq`` float64 [B, H, T, d]: the values attention sees.
+
+    ``fp8_e5m2`` stores code = E5M2(x / s_h) with one float32 scale s_h per
+    KV head (``head_scale``, default 1; reading of the Survey page, section
+    3.4: fp8 KV cache "with scale computation per head") and dequantizes to
+    E5M2 value * s_h.
     """
     x = np.asarray(x, dtype=F32)
     B, T, H, d = x.shape
@@ -168,6 +194,12 @@ def encode_tensor(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None) -> Dict
     out: Dict[str, np.ndarray] = {}
     if q == "none":
         out["deq"] = xt.astype(np.float64)
+        return out
+    if q == "fp8_e5m2":
+        sc = np.ones(H, dtype=F32) if head_scale is None else np.asarray(head_scale, dtype=F32)
+        codes = fp8_e5m2_codes(xt / sc[None, :, None, None])      # float32 division
+        out["codes"] = codes.astype(np.int32)
+        out["deq"] = fp8_e5m2_values(codes) * sc.astype(np.float64)[None, :, None, None]
         return out
     if q == "codebook":
         if codebook is None:
@@ -242,7 +274,7 @@ def encode_tensor(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None) -> Dict
 
 
 def encode_with_sink(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None,
-                     sink: int = 0) -> Dict:
+                     sink: int = 0, head_scale: np.ndarray = None) -> Dict:
     """Bulk-encode one cache tensor whose first ``sink`` tokens are an
     attention sink (KVQuant page, "Attention Sink": the keys and values of
     the first few tokens, which draw very high attention, are kept in full
@@ -260,6 +292,6 @@ def encode_with_sink(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None,
     B, T, H, d = x.shape
     s = min(int(sink), T)
     pre = np.transpose(x[:, :s], (0, 2, 1, 3)).astype(np.float64)
-    rest = encode_tensor(x[:, s:], fmt, codebook) if T > s else None
+    rest = encode_tensor(x[:, s:], fmt, codebook, head_scale) if T > s else None
     deq = pre if rest is None else np.concatenate([pre, rest["deq"]], axis=2)
     return {"sink": pre, "rest": rest, "deq": deq}

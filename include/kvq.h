@@ -76,6 +76,12 @@ typedef int32_t kvq_status;
  *   token are kept in fp16 (CSR; n_kv_heads * head_dim <= 4096) and replace
  *   the dense value
  *   [KVQuant page 2.2, 3.3].
+ * FP8_E5M2: each element is the FP8 E5M2 byte (sign, 5 exponent bits, 2
+ *   mantissa bits: the high byte of an fp16) of x / s_h, rounded to nearest
+ *   even and saturated at +-57344, with one float32 scale s_h per KV head
+ *   (kvq_cache.k_scale / v_scale; NULL = 1) [Survey page 3.4: vLLM's fp8
+ *   KV cache, scale per head].  bits 8, PER_TOKEN, group_size 0.  Stored
+ *   in the 8-bit key-row and value-tile layouts; no parameter region.
  * All arithmetic of the encoders is IEEE float32 with round-half-even;
  * scales and zeros are rounded to fp16 before codes are computed; a group
  * whose fp16 scale is 0 stores code 0 everywhere. */
@@ -84,6 +90,7 @@ typedef int32_t kvq_status;
 #define KVQ_QUANT_ASYM_ABSMAX_OFFSET  2
 #define KVQ_QUANT_SYM_Q8_0            3
 #define KVQ_QUANT_CODEBOOK            4
+#define KVQ_QUANT_FP8_E5M2            5
 
 /* ---- group layouts ----------------------------------------------------- */
 /* PER_TOKEN: groups of group_size consecutive channels of one token
@@ -160,6 +167,10 @@ typedef struct kvq_cache {
   const void* v_codebook; /* same for values                                 */
   int64_t     n_ctx;      /* tokens held per sequence (host state; advanced
                              by kvq_quantize_append on success)              */
+  const float* k_scale;   /* FP8_E5M2 keys: device float32 [n_kv_heads]
+                             scales (finite, > 0), or NULL for 1; ignored by
+                             the other formats                               */
+  const float* v_scale;   /* same for values                                 */
 } kvq_cache;
 
 /* Location of one array inside the cache allocation (bytes from base). */
@@ -327,7 +338,8 @@ const char* kvq_last_error(void);
 
 /* Version of this interface (major * 100 + minor); 101 since kvq_config
    gained sink_tokens and kvq_tensor_regions gained sink; 102 adds
-   kvq_prefill_attention. */
+   kvq_prefill_attention; 103 adds KVQ_QUANT_FP8_E5M2 and the kvq_cache
+   scale pointers. */
 int32_t kvq_abi_version(void);
 
 #ifdef __cplusplus

@@ -99,6 +99,35 @@ __device__ __forceinline__ uint32_t field_value(uint32_t code, int field) {
   return field == 0 ? code : (field == 1 ? (code & 3u) : (code >> 2) & 1u);
 }
 
+// ---- FP8 E5M2 -----------------------------------------------------------------
+// E5M2 is the high byte of an fp16: decoding is exact.
+__device__ __forceinline__ float e5m2_to_f(uint32_t code) {
+  return h2f((uint16_t)((code & 0xffu) << 8));
+}
+// float32 -> E5M2 byte, round to nearest even, magnitudes of 57344 and
+// beyond saturate to 57344; the sign is kept (also for zero).  NaN inputs
+// are outside the cache contract.
+__device__ __forceinline__ uint32_t f_to_e5m2(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  const uint32_t sign = (u >> 24) & 0x80u, a = u & 0x7fffffffu;
+  uint32_t r;
+  if (a >= 0x47600000u) {
+    r = 0x7bu;
+  } else if (a >= 0x38800000u) {
+    // normal: rebias the exponent (127 -> 15) and round the mantissa to 2 bits
+    const uint32_t b = a - (112u << 23);
+    r = (b + 0x000fffffu + ((b >> 21) & 1u)) >> 21;
+  } else {
+    // below 2^-14: multiples of 2^-16 (4 is the smallest normal)
+    r = (uint32_t)rintf(__builtin_bit_cast(float, a) * 65536.0f);
+  }
+  return sign | r;
+}
+
+__device__ __forceinline__ float fp8_scale(const DevTensor& t, int h) {
+  return t.hscale ? t.hscale[h] : 1.0f;
+}
+
 // ---- element-wise dequantization (general kernel, prefill staging) --------
 __device__ __forceinline__ float deq_uniform(uint32_t code, int quant, const void* params,
                                              int64_t rec) {
@@ -119,6 +148,7 @@ __device__ inline float deq_key(const DevTensor& k, const DevShape& sh, int bh, 
     return elem2f(k.tail[((int64_t)bh * k.G + (t - n_full)) * kHeadDim + c], sh.kv_bf16);
   const uint32_t code = k_row_code(k.codes + row * k.row_bytes, k.bits, c);
   if (k.quant == KVQ_QUANT_CODEBOOK) return h2f(k.codebook[((int64_t)h * kHeadDim + c) * 16 + code]);
+  if (k.quant == KVQ_QUANT_FP8_E5M2) return e5m2_to_f(code) * fp8_scale(k, h);
   if (k.per_channel)
     return deq_uniform(code, k.quant, k.params,
                        ((int64_t)bh * (sh.Tcap / k.G) + t / k.G) * kHeadDim + c);
@@ -137,6 +167,7 @@ __device__ inline float deq_value(const DevTensor& v, const DevShape& sh, int bh
     return h2f(v.codebook[((int64_t)h * kHeadDim + c) * 16 + code]);
   }
   const uint32_t code = v_tile_code(tile, v.bits, (int)(t & (kTile - 1)), c);
+  if (v.quant == KVQ_QUANT_FP8_E5M2) return e5m2_to_f(code) * fp8_scale(v, h);
   return deq_uniform(code, v.quant, v.params, row * v.ng + c / v.G);
 }
 

@@ -20,15 +20,6 @@ namespace {
 
 constexpr int kD = kHeadDim;
 
-__device__ __forceinline__ float load_elem(const void* base, int64_t idx, int is_bf16) {
-  return elem2f(static_cast<const uint16_t*>(base)[idx], is_bf16);
-}
-
-// Quantize the two channels (2*lane, 2*lane + 1) of one row held by a full
-// wave.  For per-token uniform formats the group statistics are reduced over
-// the G/2 lanes of the group.  Writes the group's parameters (first lane of
-// each group) at ``prm_row`` (the row's parameter record array) and returns
-// the two codes (two's complement byte for q8_0).
 // Codebook index of x: the number of midpoints between consecutive centroids
 // that lie below x (nearest centroid, ties to the lower index).
 __device__ __forceinline__ uint32_t cb_code(const uint16_t* cb, float x) {
@@ -36,58 +27,6 @@ __device__ __forceinline__ uint32_t cb_code(const uint16_t* cb, float x) {
 #pragma unroll
   for (int i = 0; i < 15; ++i) n += x > (h2f(cb[i]) + h2f(cb[i + 1])) * 0.5f;
   return n;
-}
-
-__device__ __forceinline__ void encode_pair(const DevTensor& t, int h, int lane, float x0,
-                                            float x1, void* prm_row, uint32_t& q0,
-                                            uint32_t& q1) {
-  const int c0 = 2 * lane, c1 = c0 + 1;
-  if (t.quant == KVQ_QUANT_CODEBOOK) {
-    const uint16_t* cb0 = t.codebook + ((int64_t)h * kD + c0) * 16;
-    q0 = cb_code(cb0, x0);
-    q1 = cb_code(cb0 + 16, x1);
-    return;
-  }
-  float lo = fminf(x0, x1), hi = fmaxf(x0, x1), am = fmaxf(fabsf(x0), fabsf(x1));
-  const int half_lanes = t.G >> 1;
-  for (int off = 1; off < half_lanes; off <<= 1) {
-    lo = fminf(lo, __shfl_xor(lo, off, 64));
-    hi = fmaxf(hi, __shfl_xor(hi, off, 64));
-    am = fmaxf(am, __shfl_xor(am, off, 64));
-  }
-  const bool writer = (lane & (half_lanes - 1)) == 0;
-  const int grp = c0 / t.G;
-  if (t.quant == KVQ_QUANT_SYM_Q8_0) {
-    const uint16_t sh = f2h_rn(am / 127.0f);
-    const float s = h2f(sh);
-    auto code = [&](float x) -> uint32_t {
-      if (s == 0.0f) return 0u;
-      float v = rintf(x / s);
-      v = fminf(fmaxf(v, -128.0f), 127.0f);
-      return (uint32_t)((int)v & 0xff);
-    };
-    q0 = code(x0);
-    q1 = code(x1);
-    if (writer) static_cast<uint16_t*>(prm_row)[grp] = sh;
-    return;
-  }
-  const float qmax = (float)((1 << t.bits) - 1);
-  uint16_t sh;
-  if (t.quant == KVQ_QUANT_ASYM_MINMAX)
-    sh = f2h_rn((hi - lo) / qmax);
-  else
-    sh = f2h_rn(am / (float)((1 << (t.bits - 1)) - 1));
-  const uint16_t zh = f2h_rn(lo);
-  const float s = h2f(sh), z = h2f(zh);
-  auto code = [&](float x) -> uint32_t {
-    if (s == 0.0f) return 0u;
-    float v = rintf((x - z) / s);
-    v = fminf(fmaxf(v, 0.0f), qmax);
-    return (uint32_t)v;
-  };
-  q0 = code(x0);
-  q1 = code(x1);
-  if (writer) static_cast<uint32_t*>(prm_row)[grp] = (uint32_t)sh | ((uint32_t)zh << 16);
 }
 
 // Quantize channels c0 .. c0 + 7 (c0 = 8 j8) of one row whose 128 channels
@@ -103,6 +42,11 @@ __device__ __forceinline__ uint2 encode8(const DevTensor& t, int h, int j8, cons
   if (t.quant == KVQ_QUANT_CODEBOOK) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[e] = cb_code(t.codebook + ((int64_t)h * kD + c0 + e) * 16, x[e]);
+  } else if (t.quant == KVQ_QUANT_FP8_E5M2) {
+    // one float32 division per element, as the format defines it
+    const float s = fp8_scale(t, h);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = f_to_e5m2(x[e] / s);
   } else {
     float lo = x[0], hi = x[0], am = fabsf(x[0]);
 #pragma unroll

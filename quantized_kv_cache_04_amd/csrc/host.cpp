@@ -75,6 +75,12 @@ kvq_status check_format(const kvq_tensor_format& f, const kvq_config& c, bool is
         return fail(KVQ_ERR_UNSUPPORTED, "%s: outliers need n_kv_heads * head_dim <= 4096",
                     name);
       return KVQ_OK;
+    case KVQ_QUANT_FP8_E5M2:
+      if (f.bits != 8) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: FP8_E5M2 needs bits = 8", name);
+      if (f.layout != KVQ_LAYOUT_PER_TOKEN || f.group_size != 0)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: FP8_E5M2 takes the per-token layout and "
+                    "group_size 0 (its scale is per KV head)", name);
+      return KVQ_OK;
     default:
       return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: unknown quantizer %d", name, f.quantizer);
   }
@@ -128,7 +134,8 @@ void fill_tensor(TensorLayout& t, const kvq_tensor_format& f, const kvq_config& 
   t.quant = f.quantizer;
   t.bits = f.quantizer == KVQ_QUANT_NONE ? 16 : f.bits;
   t.per_channel = f.layout == KVQ_LAYOUT_PER_CHANNEL;
-  t.G = (f.quantizer == KVQ_QUANT_NONE || f.quantizer == KVQ_QUANT_CODEBOOK) ? 0 : f.group_size;
+  t.G = (f.quantizer == KVQ_QUANT_NONE || f.quantizer == KVQ_QUANT_CODEBOOK ||
+         f.quantizer == KVQ_QUANT_FP8_E5M2) ? 0 : f.group_size;
   t.row_bytes = (int)(d * t.bits / 8);
   t.ng = (t.G && !t.per_channel) ? (int)(d / t.G) : 0;
   t.psize = f.quantizer == KVQ_QUANT_SYM_Q8_0 ? 2 : 4;
@@ -184,6 +191,8 @@ Layout make_layout(const kvq_config& c) {
 uint64_t tensor_payload(const TensorLayout& t, const kvq_config& c, int64_t n) {
   const uint64_t B = c.batch, H = c.n_kv_heads, d = c.head_dim;
   if (t.quant == KVQ_QUANT_NONE) return B * H * (uint64_t)n * d * 2;
+  // FP8: a byte per element and the per-head float32 scales decode reads
+  if (t.quant == KVQ_QUANT_FP8_E5M2) return B * H * (uint64_t)n * d + H * 4;
   uint64_t total;
   if (t.quant == KVQ_QUANT_CODEBOOK) {
     total = B * H * (uint64_t)n * t.row_bytes + H * d * 16 * 2;
@@ -216,6 +225,9 @@ kvq_status check_codebooks(const kvq_config& c, const kvq_cache& cache) {
   if ((cache.k_codebook && !aligned16(cache.k_codebook)) ||
       (cache.v_codebook && !aligned16(cache.v_codebook)))
     return fail(KVQ_ERR_INVALID_ARGUMENT, "codebook pointers must be 16-byte aligned");
+  if ((cache.k_scale && (reinterpret_cast<uintptr_t>(cache.k_scale) & 3u)) ||
+      (cache.v_scale && (reinterpret_cast<uintptr_t>(cache.v_scale) & 3u)))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "scale pointers must be 4-byte aligned");
   return KVQ_OK;
 }
 
@@ -228,7 +240,8 @@ kvq_status device_status(hipError_t e, const char* what) {
 
 }  // namespace
 
-DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebook) {
+DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebook,
+                          const float* scale) {
   uint8_t* b = static_cast<uint8_t*>(base);
   DevTensor t;
   t.quant = tl.quant;
@@ -245,6 +258,7 @@ DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebo
   t.col = tl.col_bytes ? reinterpret_cast<uint16_t*>(b + tl.col_off) : nullptr;
   t.val = tl.val_bytes ? reinterpret_cast<uint16_t*>(b + tl.val_off) : nullptr;
   t.codebook = static_cast<const uint16_t*>(codebook);
+  t.hscale = tl.quant == KVQ_QUANT_FP8_E5M2 ? scale : nullptr;
   return t;
 }
 
@@ -274,7 +288,7 @@ int32_t kvq_decode_path(const kvq_config* cfg) {
   return ok ? KVQ_PATH_MFMA : KVQ_PATH_VALU;
 }
 
-int32_t kvq_abi_version(void) { return 102; }
+int32_t kvq_abi_version(void) { return 103; }
 
 kvq_status kvq_set_decode_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr))
@@ -360,8 +374,8 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const vo
   }
   if (n_q_new > 0) {
     sh.in_off = n_sink_new;
-    DevTensor kt = make_dev_tensor(L.k, cache->base, cache->k_codebook);
-    DevTensor vt = make_dev_tensor(L.v, cache->base, cache->v_codebook);
+    DevTensor kt = make_dev_tensor(L.k, cache->base, cache->k_codebook, cache->k_scale);
+    DevTensor vt = make_dev_tensor(L.v, cache->base, cache->v_codebook, cache->v_scale);
     st = device_status(launch_encode_tensor(sh, kt, true, k_new, n_q0, n_q_new, s), "encode keys");
     if (st != KVQ_OK) return st;
     st = device_status(launch_encode_tensor(sh, vt, false, v_new, n_q0, n_q_new, s),
@@ -397,8 +411,8 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   DecodeArgs a;
   a.sh = DevShape{cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, cfg->n_q_heads / cfg->n_kv_heads,
                   cfg->kv_dtype == KVQ_BF16, L.Tcap};
-  a.k = make_dev_tensor(L.k, cache->base, cache->k_codebook);
-  a.v = make_dev_tensor(L.v, cache->base, cache->v_codebook);
+  a.k = make_dev_tensor(L.k, cache->base, cache->k_codebook, cache->k_scale);
+  a.v = make_dev_tensor(L.v, cache->base, cache->v_codebook, cache->v_scale);
   a.q = q;
   a.q_pos = q_pos;
   a.out = out;
@@ -535,8 +549,8 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
   Layout L = make_layout(*cfg);
   PrefillArgs a;
   a.sh = DevShape{cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, g, cfg->kv_dtype == KVQ_BF16, L.Tcap};
-  a.k = make_dev_tensor(L.k, cache->base, cache->k_codebook);
-  a.v = make_dev_tensor(L.v, cache->base, cache->v_codebook);
+  a.k = make_dev_tensor(L.k, cache->base, cache->k_codebook, cache->k_scale);
+  a.v = make_dev_tensor(L.v, cache->base, cache->v_codebook, cache->v_scale);
   uint8_t* base = static_cast<uint8_t*>(cache->base);
   a.k_sink = L.sink ? reinterpret_cast<const uint16_t*>(base + L.k.sink_off) : nullptr;
   a.v_sink = L.sink ? reinterpret_cast<const uint16_t*>(base + L.v.sink_off) : nullptr;

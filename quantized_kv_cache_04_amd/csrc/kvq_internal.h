@@ -54,6 +54,7 @@ struct DevTensor {
   uint16_t* col;
   uint16_t* val;
   const uint16_t* codebook;   // fp16 [Hkv][d][16]
+  const float* hscale;        // FP8: float32 scale per KV head (null = 1)
 };
 
 struct DevShape {
@@ -64,7 +65,8 @@ struct DevShape {
   int64_t in_tok = 0, in_off = 0;
 };
 
-DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebook);
+DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebook,
+                          const float* scale);
 
 // ---- encode launchers (encode.hip) ----------------------------------------
 hipError_t launch_encode_tensor(const DevShape& sh, const DevTensor& t, bool is_key,

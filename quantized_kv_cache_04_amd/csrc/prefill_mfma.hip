@@ -118,6 +118,8 @@ __device__ __forceinline__ void block_codes(const uint8_t* p, int m, uint32_t c[
   }
 }
 
+__device__ __forceinline__ int h_of(int bh, const DevShape& sh) { return bh % sh.Hkv; }
+
 __device__ __forceinline__ float uniform_x(uint32_t code, uint32_t pz) {
   return fmaf((float)code, h2f((uint16_t)(pz & 0xffff)), h2f((uint16_t)(pz >> 16)));
 }
@@ -136,6 +138,10 @@ __device__ __forceinline__ void key_codes(const DevTensor& k, const DevShape& sh
     if (k.quant == KVQ_QUANT_CODEBOOK) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[mm][e] = h2f(S.cbk[c0 + e][cd[e]]);
+    } else if (k.quant == KVQ_QUANT_FP8_E5M2) {
+      const float sc = fp8_scale(k, h_of(bh, sh));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[mm][e] = e5m2_to_f(cd[e]) * sc;
     } else if (k.per_channel) {
       const uint4* pp = reinterpret_cast<const uint4*>(
           static_cast<const uint32_t*>(k.params) +
@@ -176,12 +182,16 @@ __device__ __forceinline__ void value_codes(const DevTensor& v, const DevShape& 
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int tk = 16 * hv + u;
-    const int64_t rec = ((int64_t)bh * sh.Tcap + tq0 + tk) * v.ng + c / v.G;
     float y;
-    if (v.quant == KVQ_QUANT_SYM_Q8_0)
-      y = (float)(int8_t)cd[u] * h2f(static_cast<const uint16_t*>(v.params)[rec]);
-    else
-      y = uniform_x(cd[u], static_cast<const uint32_t*>(v.params)[rec]);
+    if (v.quant == KVQ_QUANT_FP8_E5M2) {
+      y = e5m2_to_f(cd[u]) * fp8_scale(v, h_of(bh, sh));
+    } else {
+      const int64_t rec = ((int64_t)bh * sh.Tcap + tq0 + tk) * v.ng + c / v.G;
+      if (v.quant == KVQ_QUANT_SYM_Q8_0)
+        y = (float)(int8_t)cd[u] * h2f(static_cast<const uint16_t*>(v.params)[rec]);
+      else
+        y = uniform_x(cd[u], static_cast<const uint32_t*>(v.params)[rec]);
+    }
     x[u] = tk < n_valid ? y : 0.f;
   }
 }

@@ -16,12 +16,13 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvq.h")
 # interface version the structures below follow (major * 100 + minor)
-ABI_VERSION = 102
+ABI_VERSION = 103
 
 # ---- constants mirrored from kvq.h -------------------------------------------
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_DEVICE = 0, -1, -2, -3, -4
 F16, BF16, F32 = 0, 1, 2
-QUANT = {"none": 0, "asym_minmax": 1, "asym_absmax_offset": 2, "sym_q8_0": 3, "codebook": 4}
+QUANT = {"none": 0, "asym_minmax": 1, "asym_absmax_offset": 2, "sym_q8_0": 3, "codebook": 4,
+         "fp8_e5m2": 5}
 LAYOUT = {"per_token": 0, "per_channel": 1}
 BYTES_PAYLOAD, BYTES_ALLOC = 0, 1
 PATHS = {"auto": 0, "valu": 1, "mfma": 2, "lut": 3}
@@ -45,7 +46,8 @@ class Config(ctypes.Structure):
 
 class CacheStruct(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("k_codebook", ctypes.c_void_p),
-                ("v_codebook", ctypes.c_void_p), ("n_ctx", ctypes.c_int64)]
+                ("v_codebook", ctypes.c_void_p), ("n_ctx", ctypes.c_int64),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 class Region(ctypes.Structure):
@@ -175,22 +177,25 @@ def _stream_ptr(stream) -> Optional[int]:
 class Cache:
     """A cache allocation (zero-filled torch uint8 device buffer) plus the
     host-side token count.  Codebooks, when used, are fp16 [Hkv, d, 16]
-    device tensors that must outlive the cache."""
+    device tensors, FP8 scales float32 [Hkv] device tensors; both must
+    outlive the cache."""
 
-    def __init__(self, cfg: Config, device="cuda", k_codebook=None, v_codebook=None):
+    def __init__(self, cfg: Config, device="cuda", k_codebook=None, v_codebook=None,
+                 k_scale=None, v_scale=None):
         import torch
         self.cfg = cfg
         self.layout = cache_layout(cfg)
         self.buffer = torch.zeros(int(self.layout.total_bytes), dtype=torch.uint8, device=device)
         self.k_codebook = k_codebook.contiguous() if k_codebook is not None else None
         self.v_codebook = v_codebook.contiguous() if v_codebook is not None else None
+        self.k_scale = k_scale.contiguous() if k_scale is not None else None
+        self.v_scale = v_scale.contiguous() if v_scale is not None else None
         self.n_ctx = 0
 
     def struct(self) -> CacheStruct:
-        return CacheStruct(self.buffer.data_ptr(),
-                           self.k_codebook.data_ptr() if self.k_codebook is not None else None,
-                           self.v_codebook.data_ptr() if self.v_codebook is not None else None,
-                           self.n_ctx)
+        ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        return CacheStruct(self.buffer.data_ptr(), ptr(self.k_codebook), ptr(self.v_codebook),
+                           self.n_ctx, ptr(self.k_scale), ptr(self.v_scale))
 
     def region(self, tensor: str, name: str):
         """uint8 view of one array of the allocation (e.g. ("k", "codes"))."""

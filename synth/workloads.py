@@ -62,7 +62,7 @@ CONFIGS: Dict[int, Dict[str, Any]] = {
 }
 
 _STREAMS = {"k": 0, "v": 1, "q": 2, "mask": 3, "kcb": 4, "vcb": 5, "step_k": 6, "step_v": 7,
-            "step_q": 8, "prefill_q": 9}
+            "step_q": 8, "prefill_q": 9, "kscale": 10, "vscale": 11}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -166,6 +166,14 @@ def _codebook(w: Workload, stream: str, device: str) -> torch.Tensor:
     return torch.sort(c.half(), dim=-1).values.contiguous()
 
 
+def _head_scales(w: Workload, stream: str, device: str) -> torch.Tensor:
+    """float32 [Hkv] scales of an FP8 tensor: seeded log-uniform in [1/4, 4]
+    (arbitrary, not powers of two, so that the division x / s rounds)."""
+    g = _gen(w, stream, device)
+    u = torch.rand((w.n_kv_heads,), generator=g, device=device, dtype=torch.float32)
+    return torch.exp2(u * 4.0 - 2.0).contiguous()
+
+
 def make_inputs(w: Workload, device: str = "cpu") -> Dict[str, Optional[torch.Tensor]]:
     """K and V of shape [B, T, Hkv, d] and q of shape [B, Hq, d] in the cache
     dtype, plus fp16 codebooks [Hkv, d, 16] for codebook formats."""
@@ -177,8 +185,10 @@ def make_inputs(w: Workload, device: str = "cpu") -> Dict[str, Optional[torch.Te
                     dtype=torch.float32).to(dt)
     kcb = _codebook(w, "kcb", device) if w.k["quantizer"] == "codebook" else None
     vcb = _codebook(w, "vcb", device) if w.v["quantizer"] == "codebook" else None
+    ksc = _head_scales(w, "kscale", device) if w.k["quantizer"] == "fp8_e5m2" else None
+    vsc = _head_scales(w, "vscale", device) if w.v["quantizer"] == "fp8_e5m2" else None
     return {"k": k.contiguous(), "v": v.contiguous(), "q": q.contiguous(),
-            "k_codebook": kcb, "v_codebook": vcb}
+            "k_codebook": kcb, "v_codebook": vcb, "k_scale": ksc, "v_scale": vsc}
 
 
 def make_step_tokens(w: Workload, step: int, n_new: int = 1, device: str = "cpu"):

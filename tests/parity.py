@@ -39,12 +39,14 @@ def oracle_encode(w, inputs: Dict[str, Optional[torch.Tensor]], n_ctx: int, max_
         x = to_np32(inputs[name][:, :n_ctx])
         cb = inputs[f"{name}_codebook"]
         cbn = cb.cpu().numpy() if cb is not None else None
+        sc = inputs.get(f"{name}_scale")
+        scn = sc.cpu().numpy() if sc is not None else None
         if sink:
-            both = oq.encode_with_sink(x, fmt, cbn, sink)
+            both = oq.encode_with_sink(x, fmt, cbn, sink, scn)
             enc, n_q = both["rest"], n_ctx - min(sink, n_ctx)
             deq[name] = both["deq"]
         else:
-            enc, n_q = oq.encode_tensor(x, fmt, cbn), n_ctx
+            enc, n_q = oq.encode_tensor(x, fmt, cbn, scn), n_ctx
             deq[name] = enc["deq"]
         exp = {}
         if fmt["quantizer"] != "none" and enc is not None:
@@ -62,9 +64,10 @@ def gpu_cache(w, inputs, chunks: Sequence[int], max_ctx: int, decode_splits: int
     """Build the cache on the GPU by appending the inputs in ``chunks`` token counts."""
     cfg = kvq.config_from_workload(w, max_ctx=max_ctx, decode_splits=decode_splits,
                                    decode_path=decode_path, sink_tokens=sink)
-    kcb = inputs["k_codebook"].to(device) if inputs["k_codebook"] is not None else None
-    vcb = inputs["v_codebook"].to(device) if inputs["v_codebook"] is not None else None
-    cache = kvq.Cache(cfg, device=device, k_codebook=kcb, v_codebook=vcb)
+    dev = lambda t: t.to(device) if t is not None else None  # noqa: E731
+    cache = kvq.Cache(cfg, device=device, k_codebook=dev(inputs["k_codebook"]),
+                      v_codebook=dev(inputs["v_codebook"]), k_scale=dev(inputs.get("k_scale")),
+                      v_scale=dev(inputs.get("v_scale")))
     kd = inputs["k"].to(device)
     vd = inputs["v"].to(device)
     t = 0

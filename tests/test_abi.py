@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
                           "kvq_decode_attention", "kvq_last_error", "kvq_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvq_abi_version() == kvq.ABI_VERSION == 102
+    assert L.kvq_abi_version() == kvq.ABI_VERSION == 103
 
 
 def _none_cfg(**kw):
@@ -123,6 +123,21 @@ def test_sink_regions(cfg_id, sink):
     assert li.max_splits == want_slots
 
 
+@pytest.mark.parametrize("n", [0, 1, 33, 1000])
+@pytest.mark.parametrize("sink", [0, 8])
+def test_fp8_payload_matches_oracle(n, sink):
+    fp8 = {"quantizer": "fp8_e5m2", "bits": 8, "group_size": 0, "layout": "per_token"}
+    q8 = {"quantizer": "sym_q8_0", "bits": 8, "group_size": 32}
+    for k, v in ((fp8, fp8), (fp8, q8)):
+        cfg = _none_cfg(batch=3, n_q_heads=8, n_kv_heads=2, k=k, v=v, sink_tokens=sink)
+        want = ocb.payload_bytes(k, v, batch=3, n_kv_heads=2, head_dim=128, n_ctx=n,
+                                 kv_dtype="f16", sink=sink)
+        assert kvq.cache_bytes(cfg, n, 1) == want
+        li = kvq.cache_layout(cfg)
+        assert li.k.params.bytes == 0 and li.k.codes.bytes == 3 * 2 * li.capacity * 128
+    assert kvq.decode_path(_none_cfg(k=fp8, v=fp8)) == "valu"
+
+
 def _status(fn):
     with pytest.raises(kvq.KvqError) as ei:
         fn()
@@ -149,6 +164,11 @@ def _status(fn):
     (dict(n_q_heads=128, n_kv_heads=128, k={"quantizer": "codebook", "bits": 4, "outlier_frac": 0.01}),
      kvq.ERR_UNSUPPORTED, "4096"),
     (dict(rope=True, rope_base=0.5), kvq.ERR_INVALID_ARGUMENT, "rope_base"),
+    (dict(k={"quantizer": "fp8_e5m2", "bits": 4}), kvq.ERR_INVALID_ARGUMENT, "FP8_E5M2"),
+    (dict(k={"quantizer": "fp8_e5m2", "bits": 8, "group_size": 32}), kvq.ERR_INVALID_ARGUMENT,
+     "group_size 0"),
+    (dict(k={"quantizer": "fp8_e5m2", "bits": 8, "layout": "per_channel"}), kvq.ERR_INVALID_ARGUMENT,
+     "per-token"),
     (dict(sink_tokens=-1), kvq.ERR_INVALID_ARGUMENT, "sink_tokens"),
     (dict(sink_tokens=4097), kvq.ERR_INVALID_ARGUMENT, "sink_tokens"),
 ])

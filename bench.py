@@ -81,7 +81,7 @@ def cpu_baseline(w, seconds: float = 12.0):
     from synth import make_workload
     from synth.workloads import make_inputs
     from threadpoolctl import threadpool_info, threadpool_limits
-    w1 = make_workload(w.cfg_id, batch=1, n_kv_heads=1, ctx=w.ctx, gqa=w.gqa, seed=7)
+    w1 = make_workload(w.cfg_id, batch=1, n_kv_heads=1, ctx=w.ctx, gqa=w.gqa, seed=7, k=w.k, v=w.v)
     inputs = make_inputs(w1, "cpu")
     x_k = inputs["k"].float().numpy()
     x_v = inputs["v"].float().numpy()
@@ -133,6 +133,9 @@ def main():
                     help="upper bound on split-K partitions of the token axis (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--kv-format", choices=["workload", "fp8_e5m2"], default="workload",
+                    help="fp8_e5m2: store keys and values of the workload's shape as FP8 E5M2 "
+                         "with per-head scales instead of its own formats")
     ap.add_argument("--prefill", type=int, default=0, metavar="N",
                     help="measure chunked prefill instead: each step appends an N-token chunk to "
                          "a cache of ctx - N tokens and runs causal attention for its N queries")
@@ -175,7 +178,11 @@ def main():
         print(json.dumps({"calibration": "elementwise copy", "bytes_read": n, "bytes_written": n,
                           "launches": 3}), flush=True)
         return
-    w = make_workload(args.config, ctx=args.ctx)
+    over = {}
+    if args.kv_format == "fp8_e5m2":
+        fp8 = dict(quantizer="fp8_e5m2", bits=8, group_size=0, layout="per_token", outlier_frac=0.0)
+        over = dict(k=fp8, v=fp8)
+    w = make_workload(args.config, ctx=args.ctx, **over)
     if args.prefill:
         bench_prefill(args, w, dev)
         return
@@ -200,7 +207,8 @@ def main():
         caches = []
         for i in range(copies):
             c = kvq.Cache(cfg, device=dev, k_codebook=inputs["k_codebook"],
-                          v_codebook=inputs["v_codebook"])
+                          v_codebook=inputs["v_codebook"], k_scale=inputs["k_scale"],
+                          v_scale=inputs["v_scale"])
             c.append(inputs["k"], inputs["v"], stream=stream)
             caches.append(c)
         q = inputs["q"]
@@ -374,7 +382,8 @@ def bench_prefill(args, w, dev):
     with torch.cuda.stream(stream):
         inputs = make_inputs(w, dev)
         c = kvq.Cache(cfg, device=dev, k_codebook=inputs["k_codebook"],
-                      v_codebook=inputs["v_codebook"])
+                      v_codebook=inputs["v_codebook"], k_scale=inputs["k_scale"],
+                      v_scale=inputs["v_scale"])
         if T0:
             c.append(inputs["k"][:, :T0].contiguous(), inputs["v"][:, :T0].contiguous(),
                      stream=stream)
@@ -463,14 +472,15 @@ def bench_encode(args, w, dev):
     from synth.workloads import make_inputs
 
     N, K, W = args.encode, args.steps, args.warmup
-    wn = make_workload(w.cfg_id, ctx=N, batch=w.batch, n_kv_heads=w.n_kv_heads)
+    wn = make_workload(w.cfg_id, ctx=N, batch=w.batch, n_kv_heads=w.n_kv_heads, k=w.k, v=w.v)
     cfg = kvq.config_from_workload(wn, max_ctx=N)
     stream = torch.cuda.Stream()
     wl = f"{CONFIG_NAME(w)}_encode{N}"
     with torch.cuda.stream(stream):
         inputs = make_inputs(wn, dev)
         c = kvq.Cache(cfg, device=dev, k_codebook=inputs["k_codebook"],
-                      v_codebook=inputs["v_codebook"])
+                      v_codebook=inputs["v_codebook"], k_scale=inputs["k_scale"],
+                      v_scale=inputs["v_scale"])
         kin, vin = inputs["k"], inputs["v"]
     torch.cuda.synchronize()
 
@@ -514,7 +524,10 @@ def bench_encode(args, w, dev):
 
 def CONFIG_NAME(w) -> str:
     from synth.workloads import CONFIGS
-    return CONFIGS[w.cfg_id]["name"] + (f"_t{w.ctx}" if w.cfg_id == 2 else "")
+    name = CONFIGS[w.cfg_id]["name"] + (f"_t{w.ctx}" if w.cfg_id == 2 else "")
+    if w.k["quantizer"] == "fp8_e5m2" and CONFIGS[w.cfg_id]["k"]["quantizer"] != "fp8_e5m2":
+        name += "_fp8e5m2"
+    return name
 
 
 def _fmt(f) -> str:

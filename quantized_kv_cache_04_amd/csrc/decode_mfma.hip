@@ -231,6 +231,18 @@ __device__ __forceinline__ void code_planes(const uint32_t* seg, int m, half8 ou
   }
 }
 
+// FP8 E5M2 block m of a segment of byte codes: the bytes become the high
+// bytes of fp16 values (exact); pair r = (byte r of dword 2m, byte r of
+// dword 2m + 1), the pair order of the byte unpack above.
+__device__ __forceinline__ half8 fp8_block(const uint32_t* seg, int m) {
+  const uint32_t d0 = seg[2 * m], d1 = seg[2 * m + 1];
+  uint32_t o[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    o[r] = __builtin_amdgcn_perm(d1, d0, ((uint32_t)(4 + r) << 24) | 0x000c0000u | ((uint32_t)r << 8) | 0x0cu);
+  return as_h8(o[0], o[1], o[2], o[3]);
+}
+
 // factor of pair r that the other operand of a code operand must carry
 template <int BITS>
 __device__ __forceinline__ float pair_factor(int r) {
@@ -295,11 +307,16 @@ __device__ __forceinline__ void load_dw(const uint8_t* p, uint32_t* out) {
   }
 }
 
-template <int KB, bool KCH, bool KQ8, int NGK, int VB, bool VQ8, int NGV>
+// F8: keys and values are FP8 E5M2 (KB = VB = 8, one group, no per-token
+// parameters): codes enter as fp16 values, the per-head scales multiply the
+// scores and the value sums.
+template <int KB, bool KCH, bool KQ8, int NGK, int VB, bool VQ8, int NGV, bool F8 = false>
 __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
+  static_assert(!F8 || (KB == 8 && VB == 8 && !KCH && !KQ8 && !VQ8 && NGK == 1 && NGV == 1),
+                "FP8 keys and values: one shape");
   // raw dwords of one 32-token block for this lane
-  constexpr int VPD = VQ8 ? 2 * NGV : 4 * NGV;                 // value params of 4 tokens
-  constexpr int KPD = KCH ? 1 : (KQ8 ? 2 * NGK : 4 * NGK);     // key params of 4 tokens
+  constexpr int VPD = F8 ? 1 : (VQ8 ? 2 * NGV : 4 * NGV);       // value params of 4 tokens
+  constexpr int KPD = (KCH || F8) ? 1 : (KQ8 ? 2 * NGK : 4 * NGK);   // key params of 4 tokens
   struct Buf {
     uint32_t k[2][KB];      // key codes, rows 16*mb + n, segment q4
     uint32_t v[2 * VB];     // value tile, this lane's 8*VB bytes
@@ -391,7 +408,8 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     mx = wave_max(mx);
     int Eq = 14 - ceil_log2(mx);
     if (Eq > 100) Eq = 100;
-    kq = pow2i(24 - Eq > 126 ? 126 : 24 - Eq) * sm2;
+    // FP8 values are fed as they are, integer codes as code * 2^-24
+    kq = F8 ? pow2i(-Eq) * sm2 * fp8_scale(K, h) : pow2i(24 - Eq > 126 ? 126 : 24 - Eq) * sm2;
     const float sc = pow2i(Eq);
 #pragma unroll
     for (int gi = 0; gi < NGK; ++gi) { qsum[gi] = 0.f; qoff[gi] = 0.f; }
@@ -505,9 +523,10 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 
   const uint8_t* kcodes = K.codes + prow * (4 * KB * 4);
   const uint8_t* vcodes = V.codes + prow * (4 * VB * 4);
-  const uint8_t* vprm = static_cast<const uint8_t*>(V.params) + prow * NGV * (VQ8 ? 2 : 4);
-  const uint8_t* kprm = KCH ? nullptr
-                            : static_cast<const uint8_t*>(K.params) + prow * NGK * (KQ8 ? 2 : 4);
+  const uint8_t* vprm = F8 ? nullptr
+                           : static_cast<const uint8_t*>(V.params) + prow * NGV * (VQ8 ? 2 : 4);
+  const uint8_t* kprm = (KCH || F8) ? nullptr
+                                    : static_cast<const uint8_t*>(K.params) + prow * NGK * (KQ8 ? 2 : 4);
   const uint32_t k_lane_off = (uint32_t)n * (16 * KB) + (uint32_t)q4 * (4 * KB);
   const uint32_t v_lane_off = (uint32_t)lane * (8 * VB);
   const uint32_t p_lane_tok = 4u * (uint32_t)q4;
@@ -518,8 +537,13 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     for (int mb = 0; mb < 2; ++mb) {
       load_dw<KB>(kcodes + (t0 + 16 * mb) * (16 * KB) + k_lane_off, B.k[mb]);
       const uint32_t tok = t0 + 16 * mb + p_lane_tok;
-      load_dw<VPD>(vprm + tok * (NGV * (VQ8 ? 2 : 4)), B.vp[mb]);
-      if constexpr (!KCH) load_dw<KPD>(kprm + tok * (NGK * (KQ8 ? 2 : 4)), B.kp[mb]);
+      if constexpr (F8) {
+        B.vp[mb][0] = 0u;
+        B.kp[mb][0] = 0u;
+      } else {
+        load_dw<VPD>(vprm + tok * (NGV * (VQ8 ? 2 : 4)), B.vp[mb]);
+        if constexpr (!KCH) load_dw<KPD>(kprm + tok * (NGK * (KQ8 ? 2 : 4)), B.kp[mb]);
+      }
     }
     load_dw<2 * VB>(vcodes + t0 * (16 * VB) + v_lane_off, B.v);
   };
@@ -671,7 +695,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int w = 0; w < VPD; ++w) smx = __builtin_elementwise_max(smx, __builtin_bit_cast(half2v, vp[mb][w]));
-    const float smax = VQ8 ? fmaxf((float)smx[0], (float)smx[1]) : (float)smx[0];
+    const float smax = F8 ? 1.0f : (VQ8 ? fmaxf((float)smx[0], (float)smx[1]) : (float)smx[0]);
     if (__any(smax > sbound)) {
       const float sm = rows_max(smax);         // same tokens in every column
       int np = kFedLog2 - (int)kLazy - ceil_log2(sm);
@@ -721,7 +745,9 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
         float x[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          if constexpr (VQ8) {
+          if constexpr (F8) {
+            x[mb] = pr[mb][r];   // signed values: no complement, no scale
+          } else if constexpr (VQ8) {
             const int idx = r * NGV + gi;
             const half2v h = __builtin_bit_cast(half2v, vp[mb][idx >> 1]);
             const float sc_h = (float)h[idx & 1];
@@ -749,7 +775,10 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     for (int nbk = 0; nbk < 8; ++nbk) {
       const uint32_t* seg = vl + (nbk >> 2) * VB;
       half8 vcode[kPlanes<VB>];
-      code_planes<VB, VQ8, true>(seg, nbk & 3, vcode);
+      if constexpr (F8)
+        vcode[0] = fp8_block(seg, nbk & 3);
+      else
+        code_planes<VB, VQ8, true>(seg, nbk & 3, vcode);
 #pragma unroll
       for (int pl = 0; pl < kPlanes<VB>; ++pl) oacc[nbk] = mfma16(pa[nbk * NGV / 8], vcode[pl], oacc[nbk]);
     }
@@ -763,6 +792,9 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   // the matrix cores keep adding into.
   constexpr int kFlush = 16;
   int since_flush = 0;
+  // accumulator units -> true units: integer codes were fed as code * 2^-24,
+  // FP8 values as they are (times the per-head value scale)
+  const float ofac = F8 ? fp8_scale(V, h) : 0x1p24f;
   auto flush = [&]() {
     const float vscale = pow2i(-pexp);
     float vb_row[NGV][4];
@@ -785,7 +817,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb)
           wo[wave][4 * q4 + r][16 * nb + n] +=
-              (oacc[nb][r] * 0x1p24f + vb_row[nb * NGV / 8][r]) * vscale;
+              (oacc[nb][r] * ofac + vb_row[nb * NGV / 8][r]) * vscale;
     }
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -835,14 +867,19 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 #pragma unroll
           for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m) {
             half8 kcode[kPlanes<KB>];
-            code_planes<KB, KQ8>(B.k[mb], m, kcode);
+            if constexpr (F8)
+              kcode[0] = fp8_block(B.k[mb], m);
+            else
+              code_planes<KB, KQ8>(B.k[mb], m, kcode);
 #pragma unroll
             for (int pl = 0; pl < kPlanes<KB>; ++pl) c = mfma16(kcode[pl], bq[m], c);
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const uint32_t* d = B.kp[mb];
-            if constexpr (KQ8) {
+            if constexpr (F8) {
+              sd[r] += c[r];
+            } else if constexpr (KQ8) {
               const int idx = r * NGK + gi;
               const half2v sv = __builtin_bit_cast(half2v, d[idx >> 1]);
               sd[r] = __builtin_fmaf((float)sv[idx & 1], c[r] - qoff[gi], sd[r]);
@@ -973,10 +1010,10 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 }
 
 // ---- dispatch ---------------------------------------------------------------------
-template <int KB, bool KCH, bool KQ8, int NGK, int VB, bool VQ8, int NGV>
+template <int KB, bool KCH, bool KQ8, int NGK, int VB, bool VQ8, int NGV, bool F8 = false>
 void launch_t(const DecodeArgs& a, hipStream_t s) {
   const size_t lds = KCH ? (size_t)4 * a.kp_groups * 32 * sizeof(u32x4) : 0;
-  hipLaunchKernelGGL((dec_mfma_kernel<KB, KCH, KQ8, NGK, VB, VQ8, NGV>),
+  hipLaunchKernelGGL((dec_mfma_kernel<KB, KCH, KQ8, NGK, VB, VQ8, NGV, F8>),
                      dim3(a.splits, a.sh.B * a.sh.Hkv), dim3(256), lds, s, a);
 }
 
@@ -1022,6 +1059,8 @@ bool uniform(const kvq_tensor_format& f) {
 }  // namespace
 
 bool mfma_config_supported(const kvq_config& c) {
+  if (c.k.quantizer == KVQ_QUANT_FP8_E5M2 && c.v.quantizer == KVQ_QUANT_FP8_E5M2)
+    return !c.rope && c.n_q_heads / c.n_kv_heads <= 8;
   if (!uniform(c.k) || !uniform(c.v) || c.rope) return false;
   if (c.n_q_heads / c.n_kv_heads > 8) return false;
   if (c.k.layout == KVQ_LAYOUT_PER_CHANNEL) return c.kv_dtype == KVQ_F16;
@@ -1041,7 +1080,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a_in, hipStream_t s) {
     a.kp_groups = groups < kMaxKpGroups ? groups : kMaxKpGroups;
   }
   bool ok = false;
-  if (a.k.per_channel) {
+  if (a.k.quant == KVQ_QUANT_FP8_E5M2 && a.v.quant == KVQ_QUANT_FP8_E5M2) {
+    launch_t<8, false, false, 1, 8, false, 1, true>(a, s);
+    ok = true;
+  } else if (a.k.per_channel) {
     switch (a.k.bits) {
       case 3: ok = launch_kch<3>(a, s); break;
       case 4: ok = launch_kch<4>(a, s); break;

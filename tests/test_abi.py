@@ -135,7 +135,9 @@ def test_fp8_payload_matches_oracle(n, sink):
         assert kvq.cache_bytes(cfg, n, 1) == want
         li = kvq.cache_layout(cfg)
         assert li.k.params.bytes == 0 and li.k.codes.bytes == 3 * 2 * li.capacity * 128
-    assert kvq.decode_path(_none_cfg(k=fp8, v=fp8)) == "valu"
+    assert kvq.decode_path(_none_cfg(k=fp8, v=fp8)) == "mfma"
+    assert kvq.decode_path(_none_cfg(k=fp8, v=q8)) == "valu"
+    assert kvq.decode_path(_none_cfg(k=fp8, v=fp8, rope=True)) == "valu"
 
 
 def _status(fn):

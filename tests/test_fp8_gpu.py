@@ -34,15 +34,15 @@ CASES = [
 ]
 
 
-def _build(name, cfg_id, over, chunks, sink, unit, max_extra=37):
-    print(f"[fp8] case={name} cfg={cfg_id} sink={sink} unit_scales={unit}", flush=True)
+def _build(name, cfg_id, over, chunks, sink, unit, max_extra=37, path="auto"):
+    print(f"[fp8] case={name} cfg={cfg_id} sink={sink} unit_scales={unit} path={path}", flush=True)
     w = make_workload(cfg_id, **over)
     inputs = make_inputs(w, "cpu")
     if unit:
         inputs["k_scale"] = inputs["v_scale"] = None
     assert sum(chunks) == w.ctx
     max_ctx = w.ctx + max_extra
-    cache = gpu_cache(w, inputs, chunks, max_ctx, sink=sink)
+    cache = gpu_cache(w, inputs, chunks, max_ctx, sink=sink, decode_path=path)
     exp, kdeq, vdeq = oracle_encode(w, inputs, w.ctx, max_ctx, sink=sink)
     return w, inputs, cache, exp, kdeq, vdeq
 
@@ -63,3 +63,32 @@ def test_fp8_bytes_decode_and_prefill(name, cfg_id, over, chunks, sink, unit):
     ma, rel = attention_errors(outp, oracle_prefill(w, qp, kdeq, vdeq, w.ctx))
     print(f"[fp8] {name} prefill: max_abs={ma:.3e} rel_l2={rel:.3e}", flush=True)
     assert ma <= MAX_ABS and rel <= REL_L2, ("prefill", ma, rel)
+
+
+# FP8 keys and values without RoPE (config 4 carries RoPE): the matrix-core cases
+MFMA_CASES = [c for c in CASES if c[2]["v"] is FP8 and c[1] != 4]
+
+
+@pytest.mark.parametrize("name,cfg_id,over,chunks,sink,unit", MFMA_CASES,
+                         ids=[c[0] for c in MFMA_CASES])
+def test_fp8_decode_on_the_general_kernel(name, cfg_id, over, chunks, sink, unit):
+    """FP8 keys and values decode on the matrix cores by default; the general
+    kernel must agree with the oracle too."""
+    w, inputs, cache, exp, kdeq, vdeq = _build(name, cfg_id, over, chunks, sink, unit, path="valu")
+    q = inputs["q"]
+    out = cache.decode(q.cuda()).cpu().numpy()
+    ma, rel = attention_errors(out, oracle_attention(w, q, kdeq, vdeq, w.ctx))
+    print(f"[fp8] {name} valu decode: max_abs={ma:.3e} rel_l2={rel:.3e}", flush=True)
+    assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_fp8_mfma_long_context_and_splits(splits):
+    over = dict(batch=2, n_kv_heads=2, ctx=3000, k=FP8, v=FP8)
+    w, inputs, cache, exp, kdeq, vdeq = _build(f"fp8_splits{splits}", 5, over, [3000], 0, False)
+    cache.cfg.decode_splits = splits
+    q = inputs["q"]
+    out = cache.decode(q.cuda()).cpu().numpy()
+    ma, rel = attention_errors(out, oracle_attention(w, q, kdeq, vdeq, w.ctx))
+    print(f"[fp8] splits={splits}: max_abs={ma:.3e} rel_l2={rel:.3e}", flush=True)
+    assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)

@@ -195,7 +195,10 @@ typedef struct kvq_layout_info {
   kvq_tensor_regions v;
   kvq_region workspace;     /* split-K partial softmax states               */
   uint64_t   total_bytes;   /* == kvq_cache_bytes(..., KVQ_BYTES_ALLOC)     */
-  int64_t    capacity;      /* Tcap = max_ctx rounded up to 32              */
+  int64_t    capacity;      /* Tcap = max_ctx rounded up to 1024 (a
+                               multiple of the 32-token tile; the stride
+                               between (sequence, head) streams stays a
+                               multiple of 1024 tokens)                      */
   int32_t    max_splits;    /* split-K partial slots per (b, query head)   */
   int32_t    reserved;
 } kvq_layout_info;

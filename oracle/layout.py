@@ -45,7 +45,11 @@ def round_up(x: int, m: int) -> int:
 
 
 def capacity(max_ctx: int) -> int:
-    return round_up(max_ctx, 32)
+    """Token capacity per (sequence, KV head) of the library's allocation:
+    max_ctx rounded up to a multiple of 1024 (a layout choice of the
+    library: the row stride between (sequence, head) streams then stays a
+    multiple of 1024 tokens)."""
+    return round_up(max_ctx, 1024)
 
 
 def row_bytes(bits: int) -> int:

@@ -162,7 +162,11 @@ void fill_tensor(TensorLayout& t, const kvq_tensor_format& f, const kvq_config& 
 
 Layout make_layout(const kvq_config& c) {
   Layout L;
-  L.Tcap = (int64_t)align_up((uint64_t)c.max_ctx, kTile);
+  // Capacity: max_ctx rounded up to 1024 tokens.  The decode kernels stream
+  // B * Hkv rows of Tcap tokens side by side; with FP8 rows some strides of
+  // 4 KB granularity (e.g. 66,016 and 66,080 tokens) ran 15 % slower on
+  // MI355X than any multiple of 1024 tokens measured.
+  L.Tcap = (int64_t)align_up((uint64_t)c.max_ctx, kCapAlign);
   uint64_t off = 0;
   fill_tensor(L.k, c.k, c, L.Tcap, off);
   fill_tensor(L.v, c.v, c, L.Tcap, off);

@@ -11,6 +11,7 @@ namespace kvq {
 
 constexpr int kHeadDim = 128;
 constexpr int kTile = 32;          // tokens per value tile / decode block
+constexpr int kCapAlign = 1024;    // token capacity granularity (a multiple of kTile)
 constexpr int kMaxSink = 4096;     // attention-sink tokens kept raw per sequence
 constexpr int kSinkSplitTokens = 256;   // a split of the sink spans at least this many tokens
 

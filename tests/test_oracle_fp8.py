@@ -106,7 +106,7 @@ def test_regions_and_payload():
         reg = olay.expected_regions(FP8, enc, batch=1, n_kv_heads=2, n_ctx=40, max_ctx=64,
                                     kv_dtype="f16", is_key=is_key)
         assert set(reg) == {"codes"}
-        assert reg["codes"].shape == (1, 2, 64 * 128)
+        assert reg["codes"].shape == (1, 2, olay.capacity(64) * 128)
         # 8-bit packing: every code byte appears exactly once in the two
         # 32-token rows / tiles the 40 tokens touch, the rest is zero
         c = enc["codes"].astype(np.uint8)

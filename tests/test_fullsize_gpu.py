@@ -44,7 +44,8 @@ def _full_cache(w, max_extra=0):
     inputs = make_inputs(w, "cuda")
     cfg = kvq.config_from_workload(w, max_ctx=w.ctx + max_extra)
     cache = kvq.Cache(cfg, device="cuda", k_codebook=inputs["k_codebook"],
-                      v_codebook=inputs["v_codebook"])
+                      v_codebook=inputs["v_codebook"], k_scale=inputs["k_scale"],
+                      v_scale=inputs["v_scale"])
     cache.append(inputs["k"], inputs["v"])
     out = cache.decode(inputs["q"])
     torch.cuda.synchronize()
@@ -132,3 +133,67 @@ def test_full_size_codebook_workload():
     ma, rel = attention_errors(got, ref)
     print(f"[fullsize] cfg=4 heads={heads} max_abs={ma:.2e} rel_l2={rel:.2e}", flush=True)
     assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)
+
+
+FP8 = dict(quantizer="fp8_e5m2", bits=8, group_size=0, layout="per_token", outlier_frac=0.0)
+
+
+def test_full_size_fp8_serving():
+    """The serving shape (16 x 65536 tokens, 8 KV heads, g = 4) stored as FP8
+    E5M2 with per-head scales, in bench.py's launch configuration (the
+    matrix-core kernel, 518 tokens of serving headroom)."""
+    w = make_workload(5, k=FP8, v=FP8)
+    extra = 518
+    print(f"[fullsize] fp8 serving T={w.ctx} path={kvq.decode_path(kvq.config_from_workload(w))}",
+          flush=True)
+    inputs, cache, out = _full_cache(w, extra)
+    g = w.gqa
+    for b, h in [(0, 0), (7, 5), (15, 7)]:
+        enc = {}
+        for name in ("k", "v"):
+            x = to_np32(inputs[name][b:b + 1, :, h:h + 1, :])
+            sc = inputs[f"{name}_scale"][h:h + 1].cpu().numpy()
+            enc[name] = oq.encode_tensor(x, FP8, None, sc)
+            exp = olay.expected_regions(FP8, enc[name], batch=1, n_kv_heads=1, n_ctx=w.ctx,
+                                        max_ctx=w.ctx + extra, kv_dtype=w.kv_dtype,
+                                        is_key=(name == "k"))
+            got = _slice_bytes(cache, w, name, "codes", b, h)
+            assert np.array_equal(got, _as_bytes(exp["codes"])), (name, b, h)
+        q = to_np32(inputs["q"][b:b + 1, h * g:(h + 1) * g])
+        ref = oatt.decode_attention(q, enc["k"]["deq"], enc["v"]["deq"], n_ctx=w.ctx)
+        ma, rel = attention_errors(out[b:b + 1, h * g:(h + 1) * g].cpu().numpy(), ref)
+        print(f"[fullsize] fp8 slice=({b},{h}) max_abs={ma:.2e} rel_l2={rel:.2e}", flush=True)
+        assert ma <= MAX_ABS and rel <= REL_L2, (b, h, ma, rel)
+
+
+def test_full_size_chunked_prefill():
+    """bench.py --prefill 512: the serving workload's last 512 tokens appended
+    as a chunk to 65,024 cached tokens, then causal attention for the chunk's
+    queries; sampled rows of sampled slices against the oracle's decode
+    definition at each row's position."""
+    from synth import make_prefill_queries
+    w = make_workload(5)
+    N, T = 512, w.ctx
+    inputs = make_inputs(w, "cuda")
+    cfg = kvq.config_from_workload(w, max_ctx=T)
+    cache = kvq.Cache(cfg, device="cuda")
+    cache.append(inputs["k"][:, :T - N].contiguous(), inputs["v"][:, :T - N].contiguous())
+    cache.append(inputs["k"][:, T - N:].contiguous(), inputs["v"][:, T - N:].contiguous())
+    q = make_prefill_queries(w, N, "cuda")
+    out = cache.prefill(q)
+    torch.cuda.synchronize()
+    g = w.gqa
+    for b, h in [(0, 0), (11, 6)]:
+        deq = {}
+        for name, fmt in (("k", w.k), ("v", w.v)):
+            x = to_np32(inputs[name][b:b + 1, :, h:h + 1, :])
+            deq[name] = oq.encode_tensor(x, fmt, None)["deq"]
+        for i in (0, 1, 255, N - 1):
+            p = T - N + i
+            qi = to_np32(q[b:b + 1, i, h * g:(h + 1) * g])
+            ref = oatt.decode_attention(qi, deq["k"], deq["v"], n_ctx=p + 1, q_pos=np.array([p]))
+            got = out[b:b + 1, i, h * g:(h + 1) * g].cpu().numpy()
+            ma, rel = attention_errors(got, ref)
+            print(f"[fullsize] prefill slice=({b},{h}) row={i} max_abs={ma:.2e} rel_l2={rel:.2e}",
+                  flush=True)
+            assert ma <= MAX_ABS and rel <= REL_L2, (b, h, i, ma, rel)

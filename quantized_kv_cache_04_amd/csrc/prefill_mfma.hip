@@ -91,25 +91,51 @@ __device__ __forceinline__ void load8(const uint16_t* p, int bf16, float x[8]) {
   for (int e = 0; e < 8; ++e) x[e] = elem2f((uint16_t)(w[e >> 1] >> (16 * (e & 1))), bf16);
 }
 
-// The 8 codes of block m (codes 8 m .. 8 m + 7) of the 32-code segment at p,
-// in the packing of include/kvq.h: bytes (8-bit), nibbles (4-bit) or, for 3
-// bits, the two low bits of pair (8m + r, 8m + r + 4) at bits 2p and
-// 16 + 2p of D[m / 2] (p = 4 (m % 2) + r) and the high bits at bits P and
-// 16 + P of D2 (P = 8 (m / 2) + 2r + m % 2).  Only the dwords holding block m
-// are read.
+// Cache formats the kernel is specialized for (F_ANY: read from the tensor
+// at run time).  The two asymmetric quantizers dequantize alike (c * s + z).
+enum : int { F_ANY = 0, F_PC4 = 1, F_U4 = 2, F_U3 = 3, F_Q8 = 4, F_CB = 5, F_F8 = 6 };
+template <int F>
+__device__ __forceinline__ int fmt_kind(const DevTensor& t) {
+  if constexpr (F == F_ANY)
+    return t.quant == KVQ_QUANT_ASYM_ABSMAX_OFFSET ? KVQ_QUANT_ASYM_MINMAX : t.quant;
+  else if constexpr (F == F_Q8) return KVQ_QUANT_SYM_Q8_0;
+  else if constexpr (F == F_CB) return KVQ_QUANT_CODEBOOK;
+  else if constexpr (F == F_F8) return KVQ_QUANT_FP8_E5M2;
+  else return KVQ_QUANT_ASYM_MINMAX;
+}
+template <int F>
+__device__ __forceinline__ int fmt_bits(const DevTensor& t) {
+  if constexpr (F == F_ANY) return t.bits;
+  else if constexpr (F == F_U3) return 3;
+  else if constexpr (F == F_Q8 || F == F_F8) return 8;
+  else return 4;
+}
+template <int F>
+__device__ __forceinline__ bool fmt_pc(const DevTensor& t) {
+  if constexpr (F == F_ANY) return t.per_channel != 0;
+  else return F == F_PC4;
+}
+
+__device__ __forceinline__ float uniform_x(uint32_t code, uint32_t pz) {
+  return fmaf((float)code, h2f((uint16_t)(pz & 0xffff)), h2f((uint16_t)(pz >> 16)));
+}
+
+// The 8 codes of block m (codes 8 m .. 8 m + 7) of a 32-code segment, in the
+// packing of include/kvq.h, from the dwords that hold the block: 8-bit: two
+// dwords (bytes 8m .. 8m + 7); 4-bit: dword m (nibbles); 3-bit: lo = D[m/2]
+// and hi = D2, the two low bits of pair (8m + r, 8m + r + 4) sitting at bits
+// 2p and 16 + 2p of lo (p = 4 (m % 2) + r) and the high bits at bits P and
+// 16 + P of hi (P = 8 (m / 2) + 2r + m % 2).
 template <int BITS>
-__device__ __forceinline__ void block_codes(const uint8_t* p, int m, uint32_t c[8]) {
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+__device__ __forceinline__ void block_codes(uint32_t w0, uint32_t w1, int m, uint32_t c[8]) {
   if (BITS == 8) {
-    const uint2 v = reinterpret_cast<const uint2*>(p)[m];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = ((e < 4 ? v.x : v.y) >> (8 * (e & 3))) & 255u;
+    for (int e = 0; e < 8; ++e) c[e] = ((e < 4 ? w0 : w1) >> (8 * (e & 3))) & 255u;
   } else if (BITS == 4) {
-    const uint32_t v = w[m];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = (v >> (4 * e)) & 15u;
+    for (int e = 0; e < 8; ++e) c[e] = (w0 >> (4 * e)) & 15u;
   } else {
-    const uint32_t lo = w[m >> 1] >> (8 * (m & 1)), hi = w[2] >> (8 * (m >> 1) + (m & 1));
+    const uint32_t lo = w0 >> (8 * (m & 1)), hi = w1 >> (8 * (m >> 1) + (m & 1));
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int sh = 2 * (e & 3) + 16 * (e >> 2);
@@ -118,81 +144,96 @@ __device__ __forceinline__ void block_codes(const uint8_t* p, int m, uint32_t c[
   }
 }
 
-__device__ __forceinline__ int h_of(int bh, const DevShape& sh) { return bh % sh.Hkv; }
+// Raw words of one 32-token block for one thread, fetched a block ahead so
+// that their loads run under the previous block's matrix-core work.
+//  keys (token tk, the 8-channel runs c0 = 32 mp + 8 sq and c0 + 64):
+//    kc: the code dwords (4-bit: runs' dwords; 8-bit: two each; 3-bit: the
+//        segment's D0, D1, D2), kq: per-channel (scale, zero) pairs of both
+//        runs, or the raw rows of the sink / a raw cache / the per-channel
+//        tail (kq[0], kq[1]), kpz: per-token parameters of both runs;
+//  values (channel c, tokens 16 hv + u): vc: the code dwords of block m of
+//    the four tile lanes 16q + c % 16 (two each for 8 and 3 bits; codebook
+//    pair tiles: 16 bytes), vp: the per-token parameters, or raw elements.
+struct Raw {
+  uint32_t kc[4];
+  uint4 kq[4];
+  uint32_t kpz[2];
+  uint32_t vc[8];
+  uint32_t vp[16];
+};
 
-__device__ __forceinline__ float uniform_x(uint32_t code, uint32_t pz) {
-  return fmaf((float)code, h2f((uint16_t)(pz & 0xffff)), h2f((uint16_t)(pz >> 16)));
-}
-
-// Keys of quantized token tq: channels 32 m + 8 sq + e of blocks m = 2 hm and
-// 2 hm + 1 (one 32-code segment of the key row), dense values in fp32.
-template <int BITS>
-__device__ __forceinline__ void key_codes(const DevTensor& k, const DevShape& sh, const PreLds& S,
-                                          int bh, int64_t tq, int sq, int hm, float x[2][8]) {
-  const uint8_t* seg = k.codes + ((int64_t)bh * sh.Tcap + tq) * k.row_bytes + sq * 4 * BITS;
+// fp32 keys of one 8-channel run (channels cr .. cr + 7; run 0 or 1 of the
+// thread's two) from its codes
+__device__ __forceinline__ void key_run(int kind, bool pc, const PreLds& S, const Raw& R,
+                                        const uint32_t cd[8], int cr, int run, float h_scale,
+                                        float x[8]) {
+  if (kind == KVQ_QUANT_CODEBOOK) {
 #pragma unroll
-  for (int mm = 0; mm < 2; ++mm) {
-    const int m = 2 * hm + mm, c0 = 32 * m + 8 * sq;
-    uint32_t cd[8];
-    block_codes<BITS>(seg, m, cd);
-    if (k.quant == KVQ_QUANT_CODEBOOK) {
+    for (int e = 0; e < 8; ++e) x[e] = h2f(S.cbk[cr + e][cd[e]]);
+  } else if (kind == KVQ_QUANT_FP8_E5M2) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[mm][e] = h2f(S.cbk[c0 + e][cd[e]]);
-    } else if (k.quant == KVQ_QUANT_FP8_E5M2) {
-      const float sc = fp8_scale(k, h_of(bh, sh));
+    for (int e = 0; e < 8; ++e) x[e] = e5m2_to_f(cd[e]) * h_scale;
+  } else if (pc) {
+    const uint4 p0 = run ? R.kq[2] : R.kq[0], p1 = run ? R.kq[3] : R.kq[1];
+    const uint32_t pz[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[mm][e] = e5m2_to_f(cd[e]) * sc;
-    } else if (k.per_channel) {
-      const uint4* pp = reinterpret_cast<const uint4*>(
-          static_cast<const uint32_t*>(k.params) +
-          ((int64_t)bh * (sh.Tcap / k.G) + tq / k.G) * kHeadDim + c0);
-      const uint4 p0 = pp[0], p1 = pp[1];
-      const uint32_t pz[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    for (int e = 0; e < 8; ++e) x[e] = uniform_x(cd[e], pz[e]);
+  } else if (kind == KVQ_QUANT_SYM_Q8_0) {
+    const float sc = h2f((uint16_t)(run ? R.kpz[1] : R.kpz[0]));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[mm][e] = uniform_x(cd[e], pz[e]);
-    } else if (k.quant == KVQ_QUANT_SYM_Q8_0) {
-      const float sc = h2f(static_cast<const uint16_t*>(k.params)[((int64_t)bh * sh.Tcap + tq) * k.ng + c0 / k.G]);
+    for (int e = 0; e < 8; ++e) x[e] = (float)(int8_t)cd[e] * sc;
+  } else {
+    const uint32_t pz = run ? R.kpz[1] : R.kpz[0];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[mm][e] = (float)(int8_t)cd[e] * sc;
-    } else {
-      const uint32_t pz = static_cast<const uint32_t*>(k.params)[((int64_t)bh * sh.Tcap + tq) * k.ng + c0 / k.G];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[mm][e] = uniform_x(cd[e], pz);
-    }
+    for (int e = 0; e < 8; ++e) x[e] = uniform_x(cd[e], pz);
   }
 }
 
-// Values of channel c for tokens 16 hv + u (u < 16) of the 32-token value
-// tile that starts at quantized token tq0; tokens at or past n_valid are 0.
-// Token 4q + r (+16 hv) of channel c is code 8m + r + 4hv of segment c / 64
-// of tile lane 16q + c % 16 (m = (c / 16) % 4).
+// fp32 keys of runs c0 and c0 + 64 of the token from its raw words
 template <int BITS>
-__device__ __forceinline__ void value_codes(const DevTensor& v, const DevShape& sh, int bh,
-                                            int64_t tq0, int c, int hv, int n_valid, float x[16]) {
-  const uint8_t* tile = v.codes + ((int64_t)bh * sh.Tcap + tq0) * v.row_bytes;
-  const int i = c & 15, sg = c >> 6, m = (c >> 4) & 3;
-  uint32_t cd[16];
+__device__ __forceinline__ void key_values(int kind, bool pc, const PreLds& S, const Raw& R,
+                                           int mp, int sq, float h_scale, float x0[8], float x1[8]) {
+  uint32_t cd[2][8];
+  if (BITS == 3) {
+    block_codes<3>(R.kc[0], R.kc[2], mp, cd[0]);
+    block_codes<3>(R.kc[1], R.kc[2], mp + 2, cd[1]);
+  } else if (BITS == 8) {
+    block_codes<8>(R.kc[0], R.kc[1], mp, cd[0]);
+    block_codes<8>(R.kc[2], R.kc[3], mp + 2, cd[1]);
+  } else {
+    block_codes<4>(R.kc[0], 0u, mp, cd[0]);
+    block_codes<4>(R.kc[1], 0u, mp + 2, cd[1]);
+  }
+  const int c0 = 32 * mp + 8 * sq;
+  key_run(kind, pc, S, R, cd[0], c0, 0, h_scale, x0);
+  key_run(kind, pc, S, R, cd[1], c0 + 64, 1, h_scale, x1);
+}
+
+// fp32 values of channel c, tokens 16 hv + u, from the raw words
+template <int BITS>
+__device__ __forceinline__ void value_values(int kind, const Raw& R, int c, int hv,
+                                             float h_scale, int n_valid, float x[16]) {
+  const int m = (c >> 4) & 3;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     uint32_t blk[8];
-    block_codes<BITS>(tile + (16 * q + i) * 8 * BITS + sg * 4 * BITS, m, blk);
+    if (BITS == 4)
+      block_codes<4>(R.vc[q], 0u, m, blk);
+    else
+      block_codes<BITS>(R.vc[2 * q], R.vc[2 * q + 1], m, blk);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) cd[4 * q + r] = hv ? blk[4 + r] : blk[r];
-  }
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int tk = 16 * hv + u;
-    float y;
-    if (v.quant == KVQ_QUANT_FP8_E5M2) {
-      y = e5m2_to_f(cd[u]) * fp8_scale(v, h_of(bh, sh));
-    } else {
-      const int64_t rec = ((int64_t)bh * sh.Tcap + tq0 + tk) * v.ng + c / v.G;
-      if (v.quant == KVQ_QUANT_SYM_Q8_0)
-        y = (float)(int8_t)cd[u] * h2f(static_cast<const uint16_t*>(v.params)[rec]);
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t code = hv ? blk[4 + r] : blk[r];
+      const int u = 4 * q + r;
+      float y;
+      if (kind == KVQ_QUANT_FP8_E5M2)
+        y = e5m2_to_f(code) * h_scale;
+      else if (kind == KVQ_QUANT_SYM_Q8_0)
+        y = (float)(int8_t)code * h2f((uint16_t)R.vp[u]);
       else
-        y = uniform_x(cd[u], static_cast<const uint32_t*>(v.params)[rec]);
+        y = uniform_x(code, R.vp[u]);
+      x[u] = 16 * hv + u < n_valid ? y : 0.f;
     }
-    x[u] = tk < n_valid ? y : 0.f;
   }
 }
 
@@ -223,7 +264,12 @@ __device__ __forceinline__ void stage_outliers(const DevTensor& ten, PreLds& S, 
   }
 }
 
+// KF, VF: key and value formats (F_ANY: any, read at run time).  The
+// specialized kernels fetch a block's raw words one block ahead, under the
+// previous block's products; the general one fetches them just in time.
+template <int KF, int VF>
 __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
+  constexpr bool PIPE = KF != F_ANY && VF != F_ANY;
   __shared__ PreLds S;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, q4 = lane >> 4;
@@ -237,10 +283,10 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
   const int n_qc = a.n_total - a.n_sink;               // quantized tokens
   const int64_t n_full = a.k.per_channel ? (int64_t)(n_qc / a.k.G) * a.k.G : n_qc;
   if (a.rope && tid < kD / 2) S.theta[tid] = pow((double)a.rope_base, -2.0 * tid / (double)kD);
-  if (a.k.quant == KVQ_QUANT_CODEBOOK)
+  if (fmt_kind<KF>(a.k) == KVQ_QUANT_CODEBOOK)
     for (int idx = tid; idx < kD * 16; idx += 256)
       S.cbk[idx >> 4][idx & 15] = a.k.codebook[(int64_t)h * kD * 16 + idx];
-  if (a.v.quant == KVQ_QUANT_CODEBOOK)
+  if (fmt_kind<VF>(a.v) == KVQ_QUANT_CODEBOOK)
     for (int idx = tid; idx < kD * 16; idx += 256)
       S.cbv[idx >> 4][idx & 15] = a.v.codebook[(int64_t)h * kD * 16 + idx];
   __syncthreads();
@@ -301,127 +347,247 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
   // groups stay aligned); positions stay absolute.
   const int n_sb = (a.n_sink + kBlk - 1) / kBlk;
   const int n_qb = p_max >= a.n_sink ? (p_max - a.n_sink) / kBlk + 1 : 0;
+  const int n_blk = n_sb + n_qb;
   const int64_t sink_row0 = (int64_t)bh * a.sink_cap;
-  for (int blk = 0; blk < n_sb + n_qb; ++blk) {
-    const bool sinkb = blk < n_sb;
-    const int t0 = sinkb ? blk * kBlk : a.n_sink + (blk - n_sb) * kBlk;   // position of token 0
-    const int64_t tq0 = sinkb ? 0 : (int64_t)(blk - n_sb) * kBlk;         // quantized index of token 0
+  const int64_t Tcap = a.sh.Tcap;
+  const int kkind = fmt_kind<KF>(a.k), vkind = fmt_kind<VF>(a.v);
+  const int kbits = fmt_bits<KF>(a.k), vbits = fmt_bits<VF>(a.v);
+  const bool kpc = fmt_pc<KF>(a.k);
+  const bool kraw = kkind == KVQ_QUANT_NONE, vraw = vkind == KVQ_QUANT_NONE;
+  const bool kstage = a.k.k_out > 0;   // keys go through the fp32 stage (outliers, then RoPE)
+  const float ksc = fp8_scale(a.k, h), vsc = fp8_scale(a.v, h);
+  // thread roles in staging: keys of token ktk, runs 32 kmp + 8 ksq (+64);
+  // values of channel vch, tokens 16 vhv .. 16 vhv + 15
+  const int ktk = tid >> 3, ksq = (tid >> 1) & 3, kmp = tid & 1;
+  const int vch = tid >> 1, vhv = tid & 1;
+  struct Desc { bool sinkb; int t0; int64_t tq0; int n_valid; };
+  auto desc = [&](int blk) {
+    Desc d;
+    d.sinkb = blk < n_sb;
+    d.t0 = d.sinkb ? blk * kBlk : a.n_sink + (blk - n_sb) * kBlk;   // position of token 0
+    d.tq0 = d.sinkb ? 0 : (int64_t)(blk - n_sb) * kBlk;            // quantized index of token 0
     // tokens t0 + tk with tk < n_valid are in this block and visible to the tile
-    const int n_valid = min(kBlk, (sinkb ? min(a.n_sink, p_max + 1) : p_max + 1) - t0);
-    __syncthreads();   // the previous block's operand reads are done
-    // ---- phase 1: dense keys to fp32 (token tk, channels 32 m + 8 sq + e of
-    // blocks m = 2 hm, 2 hm + 1) and values to fp16 planes (channel c,
-    // tokens 16 hv .. 16 hv + 15) --------------------------------------------
-    {
-      const int tk = tid >> 3, sq = (tid & 7) >> 1, hm = tid & 1;
-      float x[2][8];
-      const int64_t tq = tq0 + tk;
-      if (tk >= n_valid) {
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[mm][e] = 0.f;
-      } else if (sinkb || a.k.quant == KVQ_QUANT_NONE ||
-                 (a.k.per_channel && tq >= n_full)) {
-        // raw rows: the sink, a raw cache, or the per-channel tail
+    d.n_valid = min(kBlk, (d.sinkb ? min(a.n_sink, p_max + 1) : p_max + 1) - d.t0);
+    return d;
+  };
+  // issue the loads of block blk's raw words
+  auto fetch = [&](int blk, Raw& R) {
+    if (blk >= n_blk) return;
+    const Desc d = desc(blk);
+    if (ktk < d.n_valid) {
+      const int64_t tq = d.tq0 + ktk;
+      if (d.sinkb || kraw || (kpc && tq >= n_full)) {
         const uint16_t* row =
-            sinkb ? a.k_sink + (sink_row0 + t0 + tk) * kD
-            : a.k.quant == KVQ_QUANT_NONE
-                ? reinterpret_cast<const uint16_t*>(a.k.codes) + ((int64_t)bh * a.sh.Tcap + tq) * kD
-                : a.k.tail + ((int64_t)bh * a.k.G + (tq - n_full)) * kD;
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) load8(row + 32 * (2 * hm + mm) + 8 * sq, a.sh.kv_bf16, x[mm]);
-      } else if (a.k.bits == 4) {
-        key_codes<4>(a.k, a.sh, S, bh, tq, sq, hm, x);
-      } else if (a.k.bits == 3) {
-        key_codes<3>(a.k, a.sh, S, bh, tq, sq, hm, x);
+            d.sinkb ? a.k_sink + (sink_row0 + d.t0 + ktk) * kD
+            : kraw  ? reinterpret_cast<const uint16_t*>(a.k.codes) + ((int64_t)bh * Tcap + tq) * kD
+                    : a.k.tail + ((int64_t)bh * a.k.G + (tq - n_full)) * kD;
+        R.kq[0] = *reinterpret_cast<const uint4*>(row + 32 * kmp + 8 * ksq);
+        R.kq[1] = *reinterpret_cast<const uint4*>(row + 64 + 32 * kmp + 8 * ksq);
       } else {
-        key_codes<8>(a.k, a.sh, S, bh, tq, sq, hm, x);
-      }
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        float4* dst = reinterpret_cast<float4*>(&S.kf[tk][32 * (2 * hm + mm) + 8 * sq]);
-        dst[0] = float4{x[mm][0], x[mm][1], x[mm][2], x[mm][3]};
-        dst[1] = float4{x[mm][4], x[mm][5], x[mm][6], x[mm][7]};
+        const int bits = kbits;
+        const uint8_t* seg = a.k.codes + ((int64_t)bh * Tcap + tq) * a.k.row_bytes + ksq * 4 * bits;
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(seg);
+        if (bits == 4) {
+          R.kc[0] = w[kmp];
+          R.kc[1] = w[kmp + 2];
+        } else if (bits == 8) {
+          const uint2 u0 = reinterpret_cast<const uint2*>(seg)[kmp];
+          const uint2 u1 = reinterpret_cast<const uint2*>(seg)[kmp + 2];
+          R.kc[0] = u0.x; R.kc[1] = u0.y; R.kc[2] = u1.x; R.kc[3] = u1.y;
+        } else {
+          R.kc[0] = w[0]; R.kc[1] = w[1]; R.kc[2] = w[2];
+        }
+        const int c0 = 32 * kmp + 8 * ksq;
+        if (kpc) {
+          const uint4* pp = reinterpret_cast<const uint4*>(
+              static_cast<const uint32_t*>(a.k.params) + ((int64_t)bh * (Tcap / a.k.G) + tq / a.k.G) * kD + c0);
+          R.kq[0] = pp[0]; R.kq[1] = pp[1]; R.kq[2] = pp[16]; R.kq[3] = pp[17];
+        } else if (kkind == KVQ_QUANT_SYM_Q8_0) {
+          const uint16_t* pp = static_cast<const uint16_t*>(a.k.params) + ((int64_t)bh * Tcap + tq) * a.k.ng;
+          R.kpz[0] = pp[c0 / a.k.G];
+          R.kpz[1] = pp[(c0 + 64) / a.k.G];
+        } else if (kkind != KVQ_QUANT_CODEBOOK && kkind != KVQ_QUANT_FP8_E5M2) {
+          const uint32_t* pp = static_cast<const uint32_t*>(a.k.params) + ((int64_t)bh * Tcap + tq) * a.k.ng;
+          R.kpz[0] = pp[c0 / a.k.G];
+          R.kpz[1] = pp[(c0 + 64) / a.k.G];
+        }
       }
     }
-    {
-      const int c = tid >> 1, hv = tid & 1;
-      float x[16];
-      if (sinkb || a.v.quant == KVQ_QUANT_NONE) {
+    if (d.sinkb || vraw) {
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int tk = 16 * hv + u;
-          const uint16_t* row =
-              sinkb ? a.v_sink + (sink_row0 + t0 + tk) * kD
-                    : reinterpret_cast<const uint16_t*>(a.v.codes) + ((int64_t)bh * a.sh.Tcap + tq0 + tk) * kD;
-          x[u] = tk < n_valid ? elem2f(row[c], a.sh.kv_bf16) : 0.f;
-        }
-      } else if (a.v.quant == KVQ_QUANT_CODEBOOK) {
-        // pair tiles: byte 32 l + tau holds channels l (low nibble) and l + 64
-        const uint4 w = *reinterpret_cast<const uint4*>(
-            a.v.codes + ((int64_t)bh * a.sh.Tcap + tq0) * a.v.row_bytes + 32 * (c & 63) + 16 * hv);
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const uint32_t code = (ww[u >> 2] >> (8 * (u & 3) + 4 * (c >> 6))) & 15u;
-          x[u] = 16 * hv + u < n_valid ? h2f(S.cbv[c][code]) : 0.f;
-        }
-      } else if (a.v.bits == 4) {
-        value_codes<4>(a.v, a.sh, bh, tq0, c, hv, n_valid, x);
-      } else if (a.v.bits == 3) {
-        value_codes<3>(a.v, a.sh, bh, tq0, c, hv, n_valid, x);
-      } else {
-        value_codes<8>(a.v, a.sh, bh, tq0, c, hv, n_valid, x);
+      for (int u = 0; u < 16; ++u) {
+        const int tk = 16 * vhv + u;
+        const uint16_t* row =
+            d.sinkb ? a.v_sink + (sink_row0 + d.t0 + tk) * kD
+                    : reinterpret_cast<const uint16_t*>(a.v.codes) + ((int64_t)bh * Tcap + d.tq0 + tk) * kD;
+        R.vp[u] = tk < d.n_valid ? row[vch] : 0u;
       }
-      const int sw = (c >> 2) & 3;
+    } else {
+      const uint8_t* tile = a.v.codes + ((int64_t)bh * Tcap + d.tq0) * a.v.row_bytes;
+      if (vkind == KVQ_QUANT_CODEBOOK) {
+        // pair tiles: byte 32 l + tau holds channels l (low nibble) and l + 64
+        const uint4 w = *reinterpret_cast<const uint4*>(tile + 32 * (vch & 63) + 16 * vhv);
+        R.vc[0] = w.x; R.vc[1] = w.y; R.vc[2] = w.z; R.vc[3] = w.w;
+      } else {
+        const int bits = vbits, i = vch & 15, sg = vch >> 6, m = (vch >> 4) & 3;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint8_t* seg = tile + (16 * q + i) * 8 * bits + sg * 4 * bits;
+          const uint32_t* w = reinterpret_cast<const uint32_t*>(seg);
+          if (bits == 4) {
+            R.vc[q] = w[m];
+          } else if (bits == 8) {
+            R.vc[2 * q] = w[2 * m];
+            R.vc[2 * q + 1] = w[2 * m + 1];
+          } else {
+            R.vc[2 * q] = w[m >> 1];
+            R.vc[2 * q + 1] = w[2];
+          }
+        }
+        if (vkind == KVQ_QUANT_SYM_Q8_0) {
+          const uint16_t* pp = static_cast<const uint16_t*>(a.v.params);
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            R.vp[u] = pp[((int64_t)bh * Tcap + d.tq0 + 16 * vhv + u) * a.v.ng + vch / a.v.G];
+        } else if (vkind != KVQ_QUANT_FP8_E5M2) {
+          const uint32_t* pp = static_cast<const uint32_t*>(a.v.params);
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            R.vp[u] = pp[((int64_t)bh * Tcap + d.tq0 + 16 * vhv + u) * a.v.ng + vch / a.v.G];
+        }
+      }
+    }
+  };
+
+  Raw R;
+  if (PIPE) fetch(0, R);
+  for (int blk = 0; blk < n_blk; ++blk) {
+    const Desc d = desc(blk);
+    const bool sinkb = d.sinkb;
+    const int t0 = d.t0, n_valid = d.n_valid;
+    const int64_t tq0 = d.tq0;
+    __syncthreads();   // the previous block's operand reads are done
+    if (!PIPE) fetch(blk, R);
+    // ---- keys: decode, then RoPE at the key's position and fp16 planes ---------
+    {
+      float x0[8], x1[8];
+      const int64_t tq = tq0 + ktk;
+      if (ktk >= n_valid) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x0[e] = x1[e] = 0.f;
+      } else if (sinkb || kraw || (kpc && tq >= n_full)) {
+        const uint4 r0 = R.kq[0], r1 = R.kq[1];
+        const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w}, w1[4] = {r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x0[e] = elem2f((uint16_t)(w0[e >> 1] >> (16 * (e & 1))), a.sh.kv_bf16);
+          x1[e] = elem2f((uint16_t)(w1[e >> 1] >> (16 * (e & 1))), a.sh.kv_bf16);
+        }
+      } else if (kbits == 4) {
+        key_values<4>(kkind, kpc, S, R, kmp, ksq, ksc, x0, x1);
+      } else if (kbits == 3) {
+        key_values<3>(kkind, kpc, S, R, kmp, ksq, ksc, x0, x1);
+      } else {
+        key_values<8>(kkind, kpc, S, R, kmp, ksq, ksc, x0, x1);
+      }
+      const int c0 = 32 * kmp + 8 * ksq;
+      if (kstage) {
+        // outliers overwrite some of these before RoPE: stage in fp32
+        float4* d0 = reinterpret_cast<float4*>(&S.kf[ktk][c0]);
+        float4* d1 = reinterpret_cast<float4*>(&S.kf[ktk][c0 + 64]);
+        d0[0] = float4{x0[0], x0[1], x0[2], x0[3]};
+        d0[1] = float4{x0[4], x0[5], x0[6], x0[7]};
+        d1[0] = float4{x1[0], x1[1], x1[2], x1[3]};
+        d1[1] = float4{x1[4], x1[5], x1[6], x1[7]};
+      } else {
+        if (a.rope && ktk < n_valid) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float cs, sn;
+            rope_cs(S.theta[c0 + e], t0 + ktk, cs, sn);
+            const float y0 = x0[e], y1 = x1[e];
+            x0[e] = y0 * cs - y1 * sn;
+            x1[e] = y1 * cs + y0 * sn;
+          }
+        }
+        uint4 hi, lo;
+        const int sw = kswz(ktk);
+        split8(x0, hi, lo);
+        S.khi[ktk][(c0 >> 3) ^ sw] = hi;
+        S.klo[ktk][(c0 >> 3) ^ sw] = lo;
+        split8(x1, hi, lo);
+        S.khi[ktk][((c0 >> 3) + 8) ^ sw] = hi;
+        S.klo[ktk][((c0 >> 3) + 8) ^ sw] = lo;
+      }
+    }
+    // ---- values: channel vch, tokens 16 vhv .. 16 vhv + 15 -------------------------
+    {
+      float x[16];
+      if (sinkb || vraw) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) x[u] = elem2f((uint16_t)R.vp[u], a.sh.kv_bf16);
+      } else if (vkind == KVQ_QUANT_CODEBOOK) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const uint32_t code = (R.vc[u >> 2] >> (8 * (u & 3) + 4 * (vch >> 6))) & 15u;
+          x[u] = 16 * vhv + u < n_valid ? h2f(S.cbv[vch][code]) : 0.f;
+        }
+      } else if (vbits == 4) {
+        value_values<4>(vkind, R, vch, vhv, vsc, n_valid, x);
+      } else if (vbits == 3) {
+        value_values<3>(vkind, R, vch, vhv, vsc, n_valid, x);
+      } else {
+        value_values<8>(vkind, R, vch, vhv, vsc, n_valid, x);
+      }
+      const int sw = (vch >> 2) & 3;
       uint4 hi, lo;
       split8(x, hi, lo);
-      S.vhi[c][(2 * hv) ^ sw] = hi;
-      S.vlo[c][(2 * hv) ^ sw] = lo;
+      S.vhi[vch][(2 * vhv) ^ sw] = hi;
+      S.vlo[vch][(2 * vhv) ^ sw] = lo;
       split8(x + 8, hi, lo);
-      S.vhi[c][(2 * hv + 1) ^ sw] = hi;
-      S.vlo[c][(2 * hv + 1) ^ sw] = lo;
+      S.vhi[vch][(2 * vhv + 1) ^ sw] = hi;
+      S.vlo[vch][(2 * vhv + 1) ^ sw] = lo;
     }
-    // ---- phase 2: outliers replace their dense value -------------------------
+    // ---- outliers replace their dense value ------------------------------------
     if (!sinkb && (a.k.k_out > 0 || a.v.k_out > 0)) {
       __syncthreads();
-      if (a.k.k_out > 0) stage_outliers<true>(a.k, S, tid, b, h, tq0, n_valid, a.sh.Tcap);
-      if (a.v.k_out > 0) stage_outliers<false>(a.v, S, tid, b, h, tq0, n_valid, a.sh.Tcap);
+      if (a.k.k_out > 0) stage_outliers<true>(a.k, S, tid, b, h, tq0, n_valid, Tcap);
+      if (a.v.k_out > 0) stage_outliers<false>(a.v, S, tid, b, h, tq0, n_valid, Tcap);
     }
-    __syncthreads();
-    // ---- phase 3: RoPE at the key's position, then fp16 planes (token tk,
-    // channel pairs (i, i + 64) for i = 8 pb .. 8 pb + 7) ----------------------
-    {
-      const int tk = tid >> 3, pb = tid & 7, t = t0 + tk;
+    if (kstage) {
+      // RoPE at the key's position, then fp16 planes (token ktk, pairs (i, i + 64)
+      // for i = 8 pb .. 8 pb + 7)
+      __syncthreads();
+      const int pb = tid & 7;
       float x0[8], x1[8];
-      const float4* r0 = reinterpret_cast<const float4*>(&S.kf[tk][8 * pb]);
-      const float4* r1 = reinterpret_cast<const float4*>(&S.kf[tk][64 + 8 * pb]);
+      const float4* r0 = reinterpret_cast<const float4*>(&S.kf[ktk][8 * pb]);
+      const float4* r1 = reinterpret_cast<const float4*>(&S.kf[ktk][64 + 8 * pb]);
       const float4 a0 = r0[0], a1 = r0[1], b0 = r1[0], b1 = r1[1];
       x0[0] = a0.x; x0[1] = a0.y; x0[2] = a0.z; x0[3] = a0.w;
       x0[4] = a1.x; x0[5] = a1.y; x0[6] = a1.z; x0[7] = a1.w;
       x1[0] = b0.x; x1[1] = b0.y; x1[2] = b0.z; x1[3] = b0.w;
       x1[4] = b1.x; x1[5] = b1.y; x1[6] = b1.z; x1[7] = b1.w;
-      if (a.rope && tk < n_valid) {
+      if (a.rope && ktk < n_valid) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float cs, sn;
-          rope_cs(S.theta[8 * pb + e], t, cs, sn);
+          rope_cs(S.theta[8 * pb + e], t0 + ktk, cs, sn);
           const float y0 = x0[e], y1 = x1[e];
           x0[e] = y0 * cs - y1 * sn;
           x1[e] = y1 * cs + y0 * sn;
         }
       }
       uint4 hi, lo;
-      const int sw = kswz(tk);
+      const int sw = kswz(ktk);
       split8(x0, hi, lo);
-      S.khi[tk][pb ^ sw] = hi;
-      S.klo[tk][pb ^ sw] = lo;
+      S.khi[ktk][pb ^ sw] = hi;
+      S.klo[ktk][pb ^ sw] = lo;
       split8(x1, hi, lo);
-      S.khi[tk][(pb + 8) ^ sw] = hi;
-      S.klo[tk][(pb + 8) ^ sw] = lo;
+      S.khi[ktk][(pb + 8) ^ sw] = hi;
+      S.klo[ktk][(pb + 8) ^ sw] = lo;
     }
     __syncthreads();
+    if (PIPE) fetch(blk + 1, R);   // the next block's loads run under this block's products
     if (!wave_ok || t0 > p_wave) continue;   // nothing of this block is visible to the wave
 
     // ---- scores: tokens 8 q4 + 4T + i for T = 0, 1 --------------------------
@@ -509,8 +675,23 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (g < 1 || kRows % g != 0 || a.n_q < 1 || a.n_q > a.n_total) return hipErrorInvalidValue;
   const int qt = kRows / g;
   const int tiles = (a.n_q + qt - 1) / qt;
-  hipLaunchKernelGGL(pre_mfma_kernel, dim3((unsigned)tiles, (unsigned)(a.sh.B * a.sh.Hkv)),
-                     dim3(256), 0, stream, a);
+  const dim3 grid((unsigned)tiles, (unsigned)(a.sh.B * a.sh.Hkv));
+  const DevTensor &k = a.k, &v = a.v;
+  auto asym = [](const DevTensor& t, int bits) {
+    return (t.quant == KVQ_QUANT_ASYM_MINMAX || t.quant == KVQ_QUANT_ASYM_ABSMAX_OFFSET) && t.bits == bits;
+  };
+  if (asym(k, 4) && k.per_channel && asym(v, 4))
+    hipLaunchKernelGGL((pre_mfma_kernel<F_PC4, F_U4>), grid, dim3(256), 0, stream, a);
+  else if (asym(k, 3) && !k.per_channel && asym(v, 3))
+    hipLaunchKernelGGL((pre_mfma_kernel<F_U3, F_U3>), grid, dim3(256), 0, stream, a);
+  else if (k.quant == KVQ_QUANT_SYM_Q8_0 && v.quant == KVQ_QUANT_SYM_Q8_0)
+    hipLaunchKernelGGL((pre_mfma_kernel<F_Q8, F_Q8>), grid, dim3(256), 0, stream, a);
+  else if (k.quant == KVQ_QUANT_CODEBOOK && v.quant == KVQ_QUANT_CODEBOOK)
+    hipLaunchKernelGGL((pre_mfma_kernel<F_CB, F_CB>), grid, dim3(256), 0, stream, a);
+  else if (k.quant == KVQ_QUANT_FP8_E5M2 && v.quant == KVQ_QUANT_FP8_E5M2)
+    hipLaunchKernelGGL((pre_mfma_kernel<F_F8, F_F8>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((pre_mfma_kernel<F_ANY, F_ANY>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

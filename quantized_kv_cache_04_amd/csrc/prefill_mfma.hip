@@ -57,6 +57,11 @@ struct PreLds {
   uint4 vhi[kD][kBlk / 8], vlo[kD][kBlk / 8];     // 2 x 8 KB
   uint16_t cbk[kD][16], cbv[kD][16];               // codebooks of the KV head
   double theta[kD / 2];
+  // RoPE of keys by angle addition: rt[tk][i] = (cos, sin) of tk * theta_i
+  // for the 32 offsets of a block, rb[parity][i] = (cos, sin) of t0 * theta_i
+  // for the block's first position (double-buffered by block parity)
+  float2 rt[kBlk][kD / 2];
+  float2 rb[2][kD / 2];
 };
 
 __device__ __forceinline__ int kswz(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
@@ -82,6 +87,12 @@ __device__ __forceinline__ void rope_cs(double theta, int64_t pos, float& cs, fl
   const double ang = (double)pos * theta;
   const double two_pi = 6.283185307179586476925286766559;
   sincosf((float)(ang - two_pi * rint(ang / two_pi)), &sn, &cs);
+}
+
+// rotation by the sum of two angles given as (cos, sin) pairs
+__device__ __forceinline__ void rot_add(float2 a, float2 b, float& cs, float& sn) {
+  cs = a.x * b.x - a.y * b.y;
+  sn = a.y * b.x + a.x * b.y;
 }
 
 __device__ __forceinline__ void load8(const uint16_t* p, int bf16, float x[8]) {
@@ -283,6 +294,14 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
   const int n_qc = a.n_total - a.n_sink;               // quantized tokens
   const int64_t n_full = a.k.per_channel ? (int64_t)(n_qc / a.k.G) * a.k.G : n_qc;
   if (a.rope && tid < kD / 2) S.theta[tid] = pow((double)a.rope_base, -2.0 * tid / (double)kD);
+  if (a.rope) {
+    __syncthreads();
+    for (int idx = tid; idx < kBlk * (kD / 2); idx += 256) {
+      float cs, sn;
+      rope_cs(S.theta[idx % (kD / 2)], idx / (kD / 2), cs, sn);
+      S.rt[idx / (kD / 2)][idx % (kD / 2)] = float2{cs, sn};
+    }
+  }
   if (fmt_kind<KF>(a.k) == KVQ_QUANT_CODEBOOK)
     for (int idx = tid; idx < kD * 16; idx += 256)
       S.cbk[idx >> 4][idx & 15] = a.k.codebook[(int64_t)h * kD * 16 + idx];
@@ -459,6 +478,15 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
     }
   };
 
+  // (cos, sin) of the first position of block blk into rb[blk & 1]
+  auto base_rot = [&](int blk) {
+    if (a.rope && blk < n_blk && tid < kD / 2) {
+      float cs, sn;
+      rope_cs(S.theta[tid], desc(blk).t0, cs, sn);
+      S.rb[blk & 1][tid] = float2{cs, sn};
+    }
+  };
+  base_rot(0);
   Raw R;
   if (PIPE) fetch(0, R);
   for (int blk = 0; blk < n_blk; ++blk) {
@@ -504,7 +532,7 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             float cs, sn;
-            rope_cs(S.theta[c0 + e], t0 + ktk, cs, sn);
+            rot_add(S.rb[blk & 1][c0 + e], S.rt[ktk][c0 + e], cs, sn);
             const float y0 = x0[e], y1 = x1[e];
             x0[e] = y0 * cs - y1 * sn;
             x1[e] = y1 * cs + y0 * sn;
@@ -571,7 +599,7 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float cs, sn;
-          rope_cs(S.theta[8 * pb + e], t0 + ktk, cs, sn);
+          rot_add(S.rb[blk & 1][8 * pb + e], S.rt[ktk][8 * pb + e], cs, sn);
           const float y0 = x0[e], y1 = x1[e];
           x0[e] = y0 * cs - y1 * sn;
           x1[e] = y1 * cs + y0 * sn;
@@ -588,6 +616,7 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
     }
     __syncthreads();
     if (PIPE) fetch(blk + 1, R);   // the next block's loads run under this block's products
+    base_rot(blk + 1);             // read after the next block's first barrier
     if (!wave_ok || t0 > p_wave) continue;   // nothing of this block is visible to the wave
 
     // ---- scores: tokens 8 q4 + 4T + i for T = 0, 1 --------------------------

@@ -306,6 +306,12 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
  *   q: device [B][n_q][Hq][d] of kv_dtype (query i is that of token
  *   n_ctx - n_q + i).  1 <= n_q <= n_ctx.  sm_scale <= 0 selects 1/sqrt(d).
  *   out: device [B][n_q][Hq][d] of out_dtype (KVQ_F32, KVQ_F16 or KVQ_BF16).
+ *   workspace: device scratch of workspace_bytes bytes (16-byte aligned) for
+ *   the partial softmax states of a token axis split over several
+ *   workgroups; the call splits the axis only as far as the workspace holds
+ *   (kvq_prefill_workspace_bytes gives the size for the library's own
+ *   choice); NULL / 0 = no split.  The caller owns it; calls that share it
+ *   must not overlap in time.
  * Runs on the matrix cores for every cache format; the query heads per KV
  * head (Hq / Hkv) must divide 64.  Reads the cache only: it may overlap
  * with other reads of the same cache, not with appends to it.
@@ -314,7 +320,16 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
  */
 kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q,
                                  int32_t n_q, float sm_scale, void* out, int32_t out_dtype,
-                                 void* stream);
+                                 void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * kvq_prefill_workspace_bytes -- workspace size for the token-axis split
+ * kvq_prefill_attention would choose for n_q queries over a cache of n_ctx
+ * tokens (0 when it would not split).
+ * Errors: INVALID_ARGUMENT (bad config, NULL out, n_q or n_ctx out of range).
+ */
+kvq_status kvq_prefill_workspace_bytes(const kvq_config* cfg, int32_t n_q, int64_t n_ctx,
+                                       uint64_t* out_bytes);
 
 /*
  * kvq_decode_path -- which decode kernel kvq_decode_attention runs for this
@@ -342,7 +357,8 @@ const char* kvq_last_error(void);
 /* Version of this interface (major * 100 + minor); 101 since kvq_config
    gained sink_tokens and kvq_tensor_regions gained sink; 102 adds
    kvq_prefill_attention; 103 adds KVQ_QUANT_FP8_E5M2 and the kvq_cache
-   scale pointers. */
+   scale pointers; 104 gives kvq_prefill_attention a workspace and adds
+   kvq_prefill_workspace_bytes. */
 int32_t kvq_abi_version(void);
 
 #ifdef __cplusplus

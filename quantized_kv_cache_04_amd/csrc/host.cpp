@@ -292,7 +292,7 @@ int32_t kvq_decode_path(const kvq_config* cfg) {
   return ok ? KVQ_PATH_MFMA : KVQ_PATH_VALU;
 }
 
-int32_t kvq_abi_version(void) { return 103; }
+int32_t kvq_abi_version(void) { return 104; }
 
 kvq_status kvq_set_decode_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr))
@@ -525,9 +525,44 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   return device_status(e, "decode attention");
 }
 
+namespace {
+// Token-axis split of prefill: about 512 workgroups (two per CU), at least
+// 8 blocks of 32 tokens per split, at most 64 splits (and decode_splits,
+// when set).
+int prefill_splits(const kvq_config& c, int32_t n_q, int64_t n_ctx) {
+  const int g = c.n_q_heads / c.n_kv_heads;
+  const int64_t qt = 64 / g;
+  const int64_t tiles = (n_q + qt - 1) / qt;
+  const int64_t wgs = tiles * c.batch * c.n_kv_heads;
+  const int64_t ns = n_ctx < c.sink_tokens ? n_ctx : c.sink_tokens;
+  const int64_t nblk = (ns + kTile - 1) / kTile + (n_ctx - ns + kTile - 1) / kTile;
+  int64_t want = (512 + wgs - 1) / wgs;
+  if (want > nblk / 8) want = nblk / 8;
+  if (want > 64) want = 64;
+  if (c.decode_splits > 0 && want > c.decode_splits) want = c.decode_splits;
+  if (want < 1) want = 1;
+  return (int)want;
+}
+
+uint64_t prefill_ws_bytes(const kvq_config& c, int32_t n_q, int splits) {
+  return splits > 1 ? (uint64_t)c.batch * n_q * c.n_q_heads * splits * (c.head_dim + 2) * 4 : 0;
+}
+}  // namespace
+
+kvq_status kvq_prefill_workspace_bytes(const kvq_config* cfg, int32_t n_q, int64_t n_ctx,
+                                       uint64_t* out_bytes) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!out_bytes) return fail(KVQ_ERR_INVALID_ARGUMENT, "out_bytes is NULL");
+  if (n_ctx < 1 || n_ctx > cfg->max_ctx || n_q < 1 || n_q > n_ctx)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "need 1 <= n_q <= n_ctx <= max_ctx");
+  *out_bytes = prefill_ws_bytes(*cfg, n_q, prefill_splits(*cfg, n_q, n_ctx));
+  return KVQ_OK;
+}
+
 kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q,
                                  int32_t n_q, float sm_scale, void* out, int32_t out_dtype,
-                                 void* stream) {
+                                 void* workspace, uint64_t workspace_bytes, void* stream) {
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
   if (!cache) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache is NULL");
@@ -549,6 +584,8 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
   if (out_dtype != KVQ_F32 && out_dtype != KVQ_F16 && out_dtype != KVQ_BF16)
     return fail(KVQ_ERR_INVALID_ARGUMENT, "out_dtype must be KVQ_F32, KVQ_F16 or KVQ_BF16");
   if (!isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+  if (workspace && !aligned16(workspace))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
 
   Layout L = make_layout(*cfg);
   PrefillArgs a;
@@ -568,7 +605,30 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
   a.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)cfg->head_dim));
   a.rope = cfg->rope;
   a.rope_base = cfg->rope_base;
-  return device_status(launch_prefill(a, static_cast<hipStream_t>(stream)), "prefill attention");
+  // the split, as far as the workspace holds it
+  int splits = prefill_splits(*cfg, n_q, cache->n_ctx);
+  const uint64_t per_split = prefill_ws_bytes(*cfg, n_q, 2) / 2;
+  const uint64_t fit = workspace ? workspace_bytes / per_split : 0;
+  if ((uint64_t)splits > fit) splits = fit > 1 ? (int)fit : 1;
+  const int64_t nblk = (a.n_sink + kTile - 1) / kTile + (a.n_total - a.n_sink + kTile - 1) / kTile;
+  a.blocks_per_split = (int)((nblk + splits - 1) / splits);
+  a.splits = (int)((nblk + a.blocks_per_split - 1) / a.blocks_per_split);
+  a.partial = a.splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_prefill(a, s);
+  if (e == hipSuccess && a.splits > 1) {
+    // merge the splits' partial states: rows (b, i) as sequences of Hq heads
+    DecodeArgs c{};
+    c.sh = a.sh;
+    c.sh.B = cfg->batch * n_q;
+    c.partial = a.partial;
+    c.S_max = a.splits;
+    c.n_partials = a.splits;
+    c.out = out;
+    c.out_dtype = out_dtype;
+    e = launch_combine(c, s);
+  }
+  return device_status(e, "prefill attention");
 }
 
 }  // extern "C"

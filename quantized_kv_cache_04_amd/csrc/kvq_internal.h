@@ -129,6 +129,9 @@ struct PrefillArgs {
   float sm_scale;            // resolved
   int rope;
   float rope_base;
+  int splits;                // token-axis splits (grid z); > 1: partial states to partial
+  int blocks_per_split;      // 32-token blocks per split
+  float* partial;            // [B][n_q][Hq][splits][d + 2] (o, m, l) when splits > 1
 };
 // 64 query rows per workgroup: Hq / Hkv must divide 64
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

@@ -486,10 +486,13 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
       S.rb[blk & 1][tid] = float2{cs, sn};
     }
   };
-  base_rot(0);
+  // this workgroup's split of the blocks
+  const int blk_lo = blockIdx.z * a.blocks_per_split;
+  const int blk_hi = min(n_blk, blk_lo + a.blocks_per_split);
+  base_rot(blk_lo);
   Raw R;
-  if (PIPE) fetch(0, R);
-  for (int blk = 0; blk < n_blk; ++blk) {
+  if (PIPE) fetch(blk_lo, R);
+  for (int blk = blk_lo; blk < blk_hi; ++blk) {
     const Desc d = desc(blk);
     const bool sinkb = d.sinkb;
     const int t0 = d.t0, n_valid = d.n_valid;
@@ -615,7 +618,7 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
       S.klo[ktk][(pb + 8) ^ sw] = lo;
     }
     __syncthreads();
-    if (PIPE) fetch(blk + 1, R);   // the next block's loads run under this block's products
+    if (PIPE && blk + 1 < blk_hi) fetch(blk + 1, R);   // the next block's loads run under this block's products
     base_rot(blk + 1);             // read after the next block's first barrier
     if (!wave_ok || t0 > p_wave) continue;   // nothing of this block is visible to the wave
 
@@ -676,12 +679,27 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- normalize and store: lane holds channels 16 ct + 4 q4 + i of row n ----
+  // ---- normalize and store (or the split's partial state): lane holds
+  // channels 16 ct + 4 q4 + i of row n ------------------------------------------
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
   if (!row_ok) return;
+  const int64_t rowi = ((int64_t)b * a.n_q + qi) * a.sh.Hq + jh;
+  if (a.splits > 1) {
+    float* rec = a.partial + (rowi * a.splits + blockIdx.z) * (kD + 2);
+    // records are 8-byte aligned (d + 2 floats): scalar stores
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rec[16 * ct + 4 * q4 + i] = o[ct][i];
+    if (q4 == 0) {
+      rec[kD] = m_run;
+      rec[kD + 1] = l_tot;
+    }
+    return;
+  }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int64_t orow = (((int64_t)b * a.n_q + qi) * a.sh.Hq + jh) * kD;
+  const int64_t orow = rowi * kD;
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
@@ -704,7 +722,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (g < 1 || kRows % g != 0 || a.n_q < 1 || a.n_q > a.n_total) return hipErrorInvalidValue;
   const int qt = kRows / g;
   const int tiles = (a.n_q + qt - 1) / qt;
-  const dim3 grid((unsigned)tiles, (unsigned)(a.sh.B * a.sh.Hkv));
+  if (a.splits < 1 || (a.splits > 1 && !a.partial)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tiles, (unsigned)(a.sh.B * a.sh.Hkv), (unsigned)a.splits);
   const DevTensor &k = a.k, &v = a.v;
   auto asym = [](const DevTensor& t, int bits) {
     return (t.quant == KVQ_QUANT_ASYM_MINMAX || t.quant == KVQ_QUANT_ASYM_ABSMAX_OFFSET) && t.bits == bits;

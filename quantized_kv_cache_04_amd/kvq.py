@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvq.h")
 # interface version the structures below follow (major * 100 + minor)
-ABI_VERSION = 103
+ABI_VERSION = 104
 
 # ---- constants mirrored from kvq.h -------------------------------------------
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_DEVICE = 0, -1, -2, -3, -4
@@ -92,9 +92,12 @@ def lib() -> ctypes.CDLL:
                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
         L.kvq_prefill_attention.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(CacheStruct),
                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
-                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.c_uint64, ctypes.c_void_p]
+        L.kvq_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.c_int32,
+                                                  ctypes.c_int64, ctypes.POINTER(ctypes.c_uint64)]
         for fn in ("kvq_cache_bytes", "kvq_cache_layout", "kvq_quantize_append",
-                   "kvq_decode_attention", "kvq_prefill_attention"):
+                   "kvq_decode_attention", "kvq_prefill_attention", "kvq_prefill_workspace_bytes"):
             getattr(L, fn).restype = ctypes.c_int32
         L.kvq_last_error.restype = ctypes.c_char_p
         L.kvq_last_error.argtypes = []
@@ -210,9 +213,10 @@ class Cache:
         return decode_attention(self, q, q_pos=q_pos, sm_scale=sm_scale, out=out,
                                 out_dtype=out_dtype, stream=stream)
 
-    def prefill(self, q, sm_scale: float = 0.0, out=None, out_dtype: str = "f32", stream=None):
+    def prefill(self, q, sm_scale: float = 0.0, out=None, out_dtype: str = "f32", stream=None,
+                workspace=None):
         return prefill_attention(self, q, sm_scale=sm_scale, out=out, out_dtype=out_dtype,
-                                 stream=stream)
+                                 stream=stream, workspace=workspace)
 
 
 def set_decode_events(start=None, stop=None) -> None:
@@ -255,16 +259,36 @@ def decode_attention(cache: Cache, q, q_pos=None, sm_scale: float = 0.0, out=Non
     return out
 
 
+def prefill_workspace_bytes(cfg: Config, n_q: int, n_ctx: int) -> int:
+    out = ctypes.c_uint64(0)
+    _check(lib().kvq_prefill_workspace_bytes(ctypes.byref(cfg), int(n_q), int(n_ctx),
+                                             ctypes.byref(out)))
+    return int(out.value)
+
+
 def prefill_attention(cache: Cache, q, sm_scale: float = 0.0, out=None, out_dtype: str = "f32",
-                      stream=None):
+                      stream=None, workspace=None):
     """Causal attention of the last n_q cached tokens: q [B, n_q, Hq, d] ->
-    out [B, n_q, Hq, d] of ``out_dtype``."""
+    out [B, n_q, Hq, d] of ``out_dtype``.  ``workspace``: a uint8 device
+    tensor for the token-axis split; by default one of the size the library
+    asks for is kept on the cache object (grown when needed); pass an empty
+    tensor for no split."""
     import torch
     if out is None:
         tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[out_dtype]
         out = torch.empty(q.shape, dtype=tdt, device=q.device)
+    n_q = int(q.shape[1])
+    if workspace is None:
+        need = prefill_workspace_bytes(cache.cfg, n_q, cache.n_ctx)
+        ws = getattr(cache, "_prefill_ws", None)
+        if need and (ws is None or ws.numel() < need):
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+            cache._prefill_ws = ws
+        workspace = ws if need else None
+    ws_ptr = workspace.data_ptr() if workspace is not None and workspace.numel() else None
+    ws_len = int(workspace.numel()) if ws_ptr else 0
     cs = cache.struct()
     _check(lib().kvq_prefill_attention(ctypes.byref(cache.cfg), ctypes.byref(cs), q.data_ptr(),
-                                       int(q.shape[1]), float(sm_scale), out.data_ptr(),
-                                       DTYPES[out_dtype], _stream_ptr(stream)))
+                                       n_q, float(sm_scale), out.data_ptr(), DTYPES[out_dtype],
+                                       ws_ptr, ws_len, _stream_ptr(stream)))
     return out

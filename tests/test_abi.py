@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
                           "kvq_decode_attention", "kvq_last_error", "kvq_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvq_abi_version() == kvq.ABI_VERSION == 103
+    assert L.kvq_abi_version() == kvq.ABI_VERSION == 104
 
 
 def _none_cfg(**kw):
@@ -241,9 +241,9 @@ def test_decode_errors_before_launch():
         kvq.ERR_INVALID_ARGUMENT
 
 
-def _prefill(cfg, cs, q, n_q, out, odt=kvq.F32):
+def _prefill(cfg, cs, q, n_q, out, odt=kvq.F32, ws=None, ws_bytes=0):
     return kvq.lib().kvq_prefill_attention(ctypes.byref(cfg), ctypes.byref(cs), q, n_q, 0.0, out,
-                                           odt, None)
+                                           odt, ws, ws_bytes, None)
 
 
 def test_prefill_errors_before_launch():
@@ -258,13 +258,34 @@ def test_prefill_errors_before_launch():
     assert _prefill(cfg, ok, FAKE, 5, None) == kvq.ERR_INVALID_ARGUMENT
     assert _prefill(cfg, ok, FAKE, 5, FAKE, odt=9) == kvq.ERR_INVALID_ARGUMENT
     assert kvq.lib().kvq_prefill_attention(ctypes.byref(cfg), ctypes.byref(ok), FAKE, 5,
-                                           float("inf"), FAKE, kvq.F32, None) == \
+                                           float("inf"), FAKE, kvq.F32, None, 0, None) == \
         kvq.ERR_INVALID_ARGUMENT
+    assert _prefill(cfg, ok, FAKE, 5, FAKE, ws=FAKE + 8, ws_bytes=1 << 20) == kvq.ERR_INVALID_ARGUMENT
+    assert "workspace" in kvq.lib().kvq_last_error().decode()
     # query heads per KV head must divide the 64-row tile
     for hq, hkv in ((12, 4), (96, 1)):
         c = _none_cfg(n_q_heads=hq, n_kv_heads=hkv, max_ctx=100)
         assert _prefill(c, ok, FAKE, 5, FAKE) == kvq.ERR_UNSUPPORTED
         assert "divide 64" in kvq.lib().kvq_last_error().decode()
+
+
+def test_prefill_workspace_sizes():
+    from synth import make_workload
+    # one long sequence with one query head per KV head: few tiles, so the
+    # token axis is split; the size is rows x splits x (d + 2) floats
+    w4 = make_workload(4)
+    cfg = kvq.config_from_workload(w4)
+    n = kvq.prefill_workspace_bytes(cfg, 512, w4.ctx)
+    rows = 1 * 512 * 32
+    assert n > 0 and n % (rows * 130 * 4) == 0 and n // (rows * 130 * 4) <= 64
+    # decode_splits caps the split; a short context does not split
+    cfg1 = kvq.config_from_workload(w4, decode_splits=1)
+    assert kvq.prefill_workspace_bytes(cfg1, 512, w4.ctx) == 0
+    assert kvq.prefill_workspace_bytes(cfg, 16, 200) == 0
+    with pytest.raises(kvq.KvqError):
+        kvq.prefill_workspace_bytes(cfg, 0, 100)
+    with pytest.raises(kvq.KvqError):
+        kvq.prefill_workspace_bytes(cfg, 10, w4.ctx + 1)
 
 
 def test_decode_events_hook():

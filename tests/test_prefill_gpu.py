@@ -105,3 +105,24 @@ def test_prefill_is_deterministic_and_leaves_the_cache_alone():
         assert torch.equal(cache.prefill(q), a)
     torch.cuda.synchronize()
     assert torch.equal(cache.buffer, before)
+
+
+@pytest.mark.parametrize("name,cfg_id,over,chunks,n_q,sink", [
+    ("split_nuq_rope", 4, dict(n_kv_heads=2, ctx=2000), [1900, 100], 100, 0),
+    ("split_serving_sink", 5, dict(batch=1, n_kv_heads=2, ctx=3000), [3000], 64, 40),
+], ids=["split_nuq_rope", "split_serving_sink"])
+def test_token_axis_split_matches_the_unsplit_kernel(name, cfg_id, over, chunks, n_q, sink):
+    """With a workspace the token axis is split over several workgroups and
+    their partial states are merged; without one it is not.  Both match the
+    oracle."""
+    from quantized_kv_cache_04_amd import kvq as K
+    w, cache, kdeq, vdeq = _build(name, cfg_id, over, chunks, sink)
+    assert K.prefill_workspace_bytes(cache.cfg, n_q, w.ctx) > 0
+    q = make_prefill_queries(w, n_q).cuda()
+    split = cache.prefill(q).cpu().numpy()
+    whole = cache.prefill(q, workspace=torch.empty(0, dtype=torch.uint8, device="cuda")).cpu().numpy()
+    ref = oracle_prefill(w, q.cpu(), kdeq, vdeq, w.ctx)
+    for out in (split, whole):
+        ma, rel = attention_errors(out, ref)
+        print(f"[prefill] {name}: max_abs={ma:.3e} rel_l2={rel:.3e}", flush=True)
+        assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)

@@ -359,16 +359,31 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   const int64_t prow = (int64_t)bh * Tcap;   // token record of token 0 of (b, h)
   const float sm2 = a.sm_scale * kLog2e;
 
-  // ---- token range of this wave (whole 32-token blocks) ----------------------
+  // ---- blocks of this wave ----------------------------------------------------
+  // The split's 32-token blocks [blk0, blk1) are dealt out to the four waves
+  // in units of U blocks (one key group for per-channel keys, else one block):
+  // unit i goes to wave i mod 4.  The waves of a workgroup then stream
+  // neighbouring pieces of the same key, value and parameter arrays at any
+  // one time, which the memory system serves faster than four separate runs.
+  // (The host makes blocks_per_split a multiple of U.)
+  const int gblk = KCH ? Gk / kTile : 1;   // blocks per key group
+  const int U = gblk;
   const int blk0 = split * a.blocks_per_split;
   const int nblk_total = (nctx + kTile - 1) / kTile;
   const int blk1 = min(nblk_total, blk0 + a.blocks_per_split);
-  const int nb_split = blk1 - blk0;
-  const int per_wave = (nb_split + 3) / 4;
-  const int wb0 = blk0 + min(nb_split, wave * per_wave);
-  const int wb1 = blk0 + min(nb_split, (wave + 1) * per_wave);
-  // blocks [wb0, wq1) have quantized keys; [wq1, wb1) read the unquantized tail
-  const int wq1 = KCH ? max(wb0, min(wb1, n_full / kTile)) : wb1;
+  // k-th block of this wave
+  auto wblock = [&](int k) { return blk0 + (wave + 4 * (k / U)) * U + k % U; };
+  // number of this wave's blocks below block e (blk0 <= e)
+  auto wcount = [&](int e) {
+    const int nfu = (e - blk0) / U, rem = (e - blk0) % U;
+    const int cf = nfu > wave ? (nfu - wave + 3) / 4 : 0;
+    return cf * U + ((nfu & 3) == wave ? rem : 0);
+  };
+  // blocks [blk0, qend) have quantized keys (per-channel keys: [qend, blk1)
+  // read the unquantized tail); [blk0, fend) hold 32 cached tokens each
+  const int qend = KCH ? max(blk0, min(blk1, n_full / kTile)) : blk1;
+  const int fend = KCH ? qend : max(blk0, min(blk1, nctx / kTile));
+  const int nk_full = wcount(fend);
 
   // query of this lane's column: head j, channels 32m + 8*q4 + e
   const bool head_ok = j < g;
@@ -434,25 +449,25 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   }
 
   // ---- per-channel keys: the wave's key-group parameters, staged in LDS ----------
-  // A ring of a.kp_groups groups per wave, refilled (by the wave alone) when
-  // the next group lies past the staged run.
-  const int gblk = KCH ? Gk / kTile : 1;   // blocks per key group
-  const int last_grp = KCH ? max(wq1 - 1, 0) / gblk : 0;
+  // A ring of a.kp_groups of the wave's groups (every fourth group of the
+  // split), refilled by the wave alone when the next group lies past it.
+  const int last_grp = (KCH && nk_full > 0) ? wblock(nk_full - 1) / gblk : 0;
   const uint32_t* kgrp_base = KCH ? static_cast<const uint32_t*>(K.params) +
                                         (int64_t)bh * (Tcap / Gk) * kD
                                   : nullptr;
   u32x4* const kp_w = kp_lds + wave * a.kp_groups * 32;
   int kp_lo = 0, kp_hi = 0;    // staged groups [kp_lo, kp_hi)
   auto stage_kp = [&](int g0) {
-    const int g1 = min(g0 + a.kp_groups, last_grp + 1);
+    // groups g0, g0 + 4, ..., up to the wave's last group
+    const int ng = min(a.kp_groups, (last_grp - g0) / 4 + 1);
     const u32x4* src = reinterpret_cast<const u32x4*>(kgrp_base + (int64_t)g0 * kD);
-    const int n4 = (g1 - g0) * 32;
+    const int n4 = ng * 32;
     for (int c0 = 0; c0 < n4; c0 += 256) {
       u32x4 v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int c = c0 + u * 64 + lane;
-        if (c < n4) v[u] = src[c];
+        if (c < n4) v[u] = src[(c >> 5) * 128 + (c & 31)];   // group g0 + 4 (c / 32)
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -461,7 +476,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
       }
     }
     kp_lo = g0;
-    kp_hi = g1;
+    kp_hi = g0 + 4 * ng;
     // LDS accesses of one wave complete in order: the reads that follow see
     // these writes from every lane
     __builtin_amdgcn_wave_barrier();
@@ -555,7 +570,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   // to the wave's table, from which every lane reads its own operand.
   auto key_group = [&](int grp) {
     if (grp >= kp_hi) stage_kp(grp);   // wave-uniform
-    const u32x4* prm4 = kp_w + (grp - kp_lo) * 32;
+    const u32x4* prm4 = kp_w + ((grp - kp_lo) >> 2) * 32;
     const int nblocks = g * 16;
     float xs[2][8];
     float zb[2] = {0.f, 0.f};
@@ -898,50 +913,68 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     if (++since_flush == kFlush) flush();
   };
 
-  // ---- hot loop: register pipeline over the blocks with 32 cached tokens and
-  // quantized keys; kStages - 1 blocks are in flight while one is computed.
-  // (Prefetches past the end re-read the last block.)
-  const int wfull = KCH ? wq1 : max(wb0, min(wq1, nctx / kTile));
-  if (wfull > wb0) {
-    const int last = wfull - 1;
+  // ---- hot loop: register pipeline over the wave's blocks with 32 cached
+  // tokens and quantized keys; kStages - 1 blocks are in flight while one is
+  // computed.  (Prefetches past the end re-read the last block.)
+  if (nk_full > 0) {
+    // iterator over wblock(0), wblock(1), ... (scalar): within a unit the
+    // next block follows, after a unit's last block come 3 units of the
+    // other waves
+    struct BlockIter {
+      int blk, u, k;
+    };
+    auto advance = [&](BlockIter& it) {
+      if (it.k + 1 >= nk_full) return;   // stay on the last block
+      ++it.k;
+      if (++it.u == U) {
+        it.u = 0;
+        it.blk += 1 + 3 * U;
+      } else {
+        ++it.blk;
+      }
+    };
+    BlockIter pf{wblock(0), 0, 0}, cb{wblock(0), 0, 0};
+    auto next_load = [&]() { const int b = pf.blk; advance(pf); return b; };
+    auto next_comp = [&]() { const int b = cb.blk; advance(cb); return b; };
     if constexpr (kStages == 3) {
       Buf b0, b1, b2;
-      load(b0, wb0);
-      load(b1, min(wb0 + 1, last));
-      for (int blk = wb0; blk < wfull; blk += 3) {
-        load(b2, min(blk + 2, last));
-        compute(std::false_type{}, b0, blk);
-        if (blk + 1 >= wfull) break;
-        load(b0, min(blk + 3, last));
-        compute(std::false_type{}, b1, blk + 1);
-        if (blk + 2 >= wfull) break;
-        load(b1, min(blk + 4, last));
-        compute(std::false_type{}, b2, blk + 2);
+      load(b0, next_load());
+      load(b1, next_load());
+      for (int k = 0; k < nk_full; k += 3) {
+        load(b2, next_load());
+        compute(std::false_type{}, b0, next_comp());
+        if (k + 1 >= nk_full) break;
+        load(b0, next_load());
+        compute(std::false_type{}, b1, next_comp());
+        if (k + 2 >= nk_full) break;
+        load(b1, next_load());
+        compute(std::false_type{}, b2, next_comp());
       }
     } else {
       Buf b0, b1;
-      load(b0, wb0);
-      for (int blk = wb0; blk < wfull; blk += 2) {
-        load(b1, min(blk + 1, last));
-        compute(std::false_type{}, b0, blk);
-        if (blk + 1 >= wfull) break;
-        load(b0, min(blk + 2, last));
-        compute(std::false_type{}, b1, blk + 1);
+      load(b0, next_load());
+      for (int k = 0; k < nk_full; k += 2) {
+        load(b1, next_load());
+        compute(std::false_type{}, b0, next_comp());
+        if (k + 1 >= nk_full) break;
+        load(b0, next_load());
+        compute(std::false_type{}, b1, next_comp());
       }
     }
   }
-  // per-token keys: the ragged last block of the context
+  // per-token keys: the ragged last block of the context, taken by the wave
+  // its unit falls to
   if constexpr (!KCH) {
-    if (wq1 > wfull) {
+    if (blk1 > fend && ((fend - blk0) & 3) == wave) {
       Buf br;
-      load(br, wfull);
-      compute(std::true_type{}, br, wfull);
+      load(br, fend);
+      compute(std::true_type{}, br, fend);
     }
   }
 
   // ---- per-channel keys: blocks of the unquantized tail ---------------------------
   if constexpr (KCH) {
-    for (int blk = wq1; blk < wb1; ++blk) {
+    for (int blk = qend + wave; blk < blk1; blk += 4) {   // shared out over the waves
       const int t0 = blk * kTile;
       const uint16_t* tail = K.tail + ((int64_t)bh * Gk + (t0 - n_full)) * kD;
       half8 bt[4];

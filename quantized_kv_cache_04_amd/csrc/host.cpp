@@ -455,6 +455,12 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
     if (want > max_q_splits) want = max_q_splits;
     if (want < 1) want = 1;
     a.blocks_per_split = (int)((nblocks + want - 1) / want);
+    if (path == KVQ_PATH_MFMA && cfg->k.layout == KVQ_LAYOUT_PER_CHANNEL) {
+      // the matrix-core kernel deals a split's blocks to its waves one key
+      // group at a time: splits start on a group boundary
+      const int gblk = cfg->k.group_size / kTile;
+      a.blocks_per_split = (a.blocks_per_split + gblk - 1) / gblk * gblk;
+    }
     a.splits = (int)((nblocks + a.blocks_per_split - 1) / a.blocks_per_split);
     if (path == KVQ_PATH_LUT) {
       // ranges of whole 32-token chunks; a workgroup serves 4 KV heads and

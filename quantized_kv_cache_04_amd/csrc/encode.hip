@@ -163,12 +163,36 @@ __global__ __launch_bounds__(256) void enc_rows_kernel(DevShape sh, DevTensor t,
 // One block per (tile, b*Hkv + h) touched by the append.  New tokens of the
 // tile are encoded into LDS, then every dword of the tile that holds a new
 // code is rewritten; bits of older tokens are preserved.
+// KeyTail (optional): keys of a per-channel key cache whose new tokens all
+// go to the unquantized tail in this append (no key group completes).  The
+// first block of each (b, h) then also copies those key rows to the tail,
+// which saves the separate tail launch in the one-token serving step.
+struct KeyTail {
+  uint32_t* tail;      // the key tail region, [B*Hkv][G][kD] 16-bit elements
+  const void* k_new;   // the appended keys
+  int G;               // key group size (tail rows per (b, h))
+  int64_t p_first;     // first token position written to the tail
+  int64_t group_start; // position of tail row 0
+  int n_rows;          // tail rows written per (b, h); 0: no keys here
+};
+
 __global__ __launch_bounds__(256) void enc_vtile_kernel(DevShape sh, DevTensor t, const void* x_new,
-                                                        int64_t n_ctx, int n_new, int64_t tile0) {
+                                                        int64_t n_ctx, int n_new, int64_t tile0,
+                                                        KeyTail kt) {
   __shared__ uint8_t codes[kTile][kD];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int bh = blockIdx.y;
   const int b = bh / sh.Hkv, h = bh % sh.Hkv;
+  if (kt.n_rows > 0 && blockIdx.x == 0) {
+    // one thread per dword (two elements) of a tail row, as enc_kchan_tail_kernel
+    for (int idx = threadIdx.x; idx < kt.n_rows * (kD / 2); idx += 256) {
+      const int64_t p = kt.p_first + idx / (kD / 2);
+      const int w = idx % (kD / 2);
+      const int64_t rin = ((int64_t)b * sh.in_tok + sh.in_off + (p - n_ctx)) * sh.Hkv + h;
+      kt.tail[((int64_t)bh * kt.G + (p - kt.group_start)) * (kD / 2) + w] =
+          static_cast<const uint32_t*>(kt.k_new)[rin * (kD / 2) + w];
+    }
+  }
   const int64_t tile = tile0 + blockIdx.x;
   const int64_t t_begin = tile * kTile;
   const int64_t lo_new = n_ctx, hi_new = n_ctx + n_new;
@@ -472,12 +496,41 @@ hipError_t launch_encode_tensor(const DevShape& sh, const DevTensor& t, bool is_
   } else {
     const int64_t tile0 = n_ctx / kTile, tile1 = (n_ctx + n_new - 1) / kTile;
     hipLaunchKernelGGL(enc_vtile_kernel, dim3((unsigned)(tile1 - tile0 + 1), sh.B * sh.Hkv),
-                       dim3(256), 0, stream, sh, t, x_new, n_ctx, n_new, tile0);
+                       dim3(256), 0, stream, sh, t, x_new, n_ctx, n_new, tile0, KeyTail{});
   }
   if (t.k_out > 0) {
     hipLaunchKernelGGL(enc_outliers_kernel, dim3(n_new, sh.B), dim3(256),
                        (size_t)sh.Hkv * kD * 4, stream, sh, t, x_new, n_ctx, n_new);
   }
+  return hipGetLastError();
+}
+
+// Keys and values of one append.  When the keys are per-channel groups and
+// this append completes none of them (so every new key row goes to the
+// tail), and the values are value tiles without outliers, one launch of
+// enc_vtile_kernel encodes the values and copies the key rows; otherwise the
+// two tensors are encoded one after the other.
+hipError_t launch_encode_kv(const DevShape& sh, const DevTensor& kt, const DevTensor& vt,
+                            const void* k_new, const void* v_new, int64_t n_ctx, int n_new,
+                            hipStream_t stream) {
+  const bool k_tail_only = kt.quant != KVQ_QUANT_NONE && kt.per_channel && kt.k_out == 0 &&
+                           n_ctx / kt.G == (n_ctx + n_new) / kt.G;
+  const bool v_tiles = vt.quant != KVQ_QUANT_NONE && vt.k_out == 0;
+  if (!(k_tail_only && v_tiles)) {
+    const hipError_t e = launch_encode_tensor(sh, kt, true, k_new, n_ctx, n_new, stream);
+    if (e != hipSuccess) return e;
+    return launch_encode_tensor(sh, vt, false, v_new, n_ctx, n_new, stream);
+  }
+  KeyTail tail;
+  tail.tail = reinterpret_cast<uint32_t*>(kt.tail);
+  tail.k_new = k_new;
+  tail.G = kt.G;
+  tail.group_start = (n_ctx / kt.G) * kt.G;
+  tail.p_first = n_ctx;
+  tail.n_rows = n_new;
+  const int64_t tile0 = n_ctx / kTile, tile1 = (n_ctx + n_new - 1) / kTile;
+  hipLaunchKernelGGL(enc_vtile_kernel, dim3((unsigned)(tile1 - tile0 + 1), sh.B * sh.Hkv),
+                     dim3(256), 0, stream, sh, vt, v_new, n_ctx, n_new, tile0, tail);
   return hipGetLastError();
 }
 

@@ -380,10 +380,8 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const vo
     sh.in_off = n_sink_new;
     DevTensor kt = make_dev_tensor(L.k, cache->base, cache->k_codebook, cache->k_scale);
     DevTensor vt = make_dev_tensor(L.v, cache->base, cache->v_codebook, cache->v_scale);
-    st = device_status(launch_encode_tensor(sh, kt, true, k_new, n_q0, n_q_new, s), "encode keys");
-    if (st != KVQ_OK) return st;
-    st = device_status(launch_encode_tensor(sh, vt, false, v_new, n_q0, n_q_new, s),
-                       "encode values");
+    st = device_status(launch_encode_kv(sh, kt, vt, k_new, v_new, n_q0, n_q_new, s),
+                       "encode keys and values");
     if (st != KVQ_OK) return st;
   }
   cache->n_ctx += n_new;

@@ -73,6 +73,10 @@ DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebo
 hipError_t launch_encode_tensor(const DevShape& sh, const DevTensor& t, bool is_key,
                                 const void* x_new, int64_t n_ctx, int n_new,
                                 hipStream_t stream);
+// keys and values of one append (a single launch for the common serving step)
+hipError_t launch_encode_kv(const DevShape& sh, const DevTensor& kt, const DevTensor& vt,
+                            const void* k_new, const void* v_new, int64_t n_ctx, int n_new,
+                            hipStream_t stream);
 // raw copy of input tokens [in_off, in_off + n) to sink rows [pos, pos + n)
 hipError_t launch_encode_sink(const DevShape& sh, uint16_t* sink, int sink_cap, const void* x_new,
                               int64_t pos, int n, hipStream_t stream);

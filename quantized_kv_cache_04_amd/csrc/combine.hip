@@ -4,9 +4,9 @@
 //   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s,
 // the log-sum-exp combination that makes split-K decoding exact.  Each
 // thread reads the m_s and l_s of its head itself (the same addresses for
-// the 128 threads of a head) together with its own o_s[c], eight splits at
-// a time, and folds them in with a running maximum: no barriers, and one
-// round trip to memory for up to eight splits.
+// the 128 threads of a head) together with its own o_s[c], sixteen splits
+// at a time, and folds them in with a running maximum: no barriers, and one
+// round trip to memory for up to sixteen splits.
 #include <hip/hip_runtime.h>
 
 #include "splitk.h"
@@ -23,10 +23,11 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(DecodeArgs a) {
   const int b = (int)(hq / a.sh.Hq), j = (int)(hq % a.sh.Hq);
   const float* rec0 = partial_rec(a, b, j, 0);
   float M = -INFINITY, L = 0.f, O = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float m[8], l[8], o[8];
+  constexpr int kU = 16;   // splits per round trip
+  for (int s0 = 0; s0 < S; s0 += kU) {
+    float m[kU], l[kU], o[kU];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const bool ok = s0 + u < S;
       const float* p = rec0 + (int64_t)(ok ? s0 + u : 0) * (kHeadDim + 2);
       m[u] = ok ? p[kHeadDim] : -INFINITY;
@@ -35,13 +36,13 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(DecodeArgs a) {
     }
     float mc = M;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) mc = fmaxf(mc, m[u]);
+    for (int u = 0; u < kU; ++u) mc = fmaxf(mc, m[u]);
     if (mc == -INFINITY) continue;   // no tokens in these splits yet
     const float r = M == -INFINITY ? 0.f : exp2f(M - mc);
     L *= r;
     O *= r;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const float w = m[u] == -INFINITY ? 0.f : exp2f(m[u] - mc);
       L = __builtin_fmaf(w, l[u], L);
       O = __builtin_fmaf(w, o[u], O);

@@ -1000,11 +1000,13 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
       Buf B;
       load(B, blk);
       softmax_pv(std::true_type{}, sc, B.v, B.vp, nctx - t0);
+      if (++since_flush == kFlush) flush();
     }
   }
 
   // ---- wave result -> LDS (true units) ------------------------------------------
-  flush();
+  // (nothing to move when the last block ended a flush period)
+  if (since_flush > 0) flush();
   float l_sum = 0.f;
 #pragma unroll
   for (int c = 0; c < NC; ++c) l_sum = __builtin_fmaf(l_run[c], pow2i(pe_exp<VB>(c)), l_sum);

@@ -197,3 +197,33 @@ def test_decode_events_bracket_the_streaming_kernel():
     assert torch.equal(out, ref)
     k_ms, call_ms = ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
     assert 0.0 < k_ms <= call_ms, (k_ms, call_ms)
+
+
+# Per-channel key groups of 1, 3 and 8 blocks on the matrix-core kernel: the
+# waves of a workgroup take a split's blocks one key group at a time and the
+# host starts every split on a group boundary.  Splits are chosen so that
+# some waves get no group, some get a partial one, and the unquantized tail
+# is shared out over the waves; one-token appends cross group boundaries.
+# (name, key group size, context, append chunks, decode_splits)
+KCH_CASES = [
+    ("kch_g32_splits3", 32, 700, [300, 1, 1, 398], 3),
+    ("kch_g96_splits5", 96, 1000, [500] + [1] * 97 + [403], 5),
+    ("kch_g256_splits2", 256, 2100, [2000] + [1] * 100, 2),
+    ("kch_g256_one_group", 256, 300, [300], 0),
+    ("kch_g128_splits9", 128, 3000, [2999, 1], 9),
+]
+
+
+@pytest.mark.parametrize("name,G,ctx,chunks,splits", KCH_CASES, ids=[c[0] for c in KCH_CASES])
+def test_per_channel_key_groups_on_matrix_cores(name, G, ctx, chunks, splits):
+    w, inputs, cache, exp, kdeq, vdeq = _run(name, 5, dict(batch=2, n_kv_heads=2, ctx=ctx,
+                                                           k=dict(group_size=G)),
+                                             chunks, decode_path="mfma", decode_splits=splits)
+    bad = compare_regions(cache, exp)
+    assert not bad, "\n".join(bad)
+    q = inputs["q"]
+    out = cache.decode(q.cuda()).cpu().numpy()
+    ref = oracle_attention(w, q, kdeq, vdeq, w.ctx)
+    ma, rel = attention_errors(out, ref)
+    print(f"[parity] {name}: max_abs={ma:.3e} rel_l2={rel:.3e}", flush=True)
+    assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)

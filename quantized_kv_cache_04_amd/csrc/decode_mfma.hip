@@ -786,6 +786,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
       }
       pa[gi] = as_h8(o[0], o[1], o[2], o[3]);
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int nbk = 0; nbk < 8; ++nbk) {
       const uint32_t* seg = vl + (nbk >> 2) * VB;
@@ -797,6 +798,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int pl = 0; pl < kPlanes<VB>; ++pl) oacc[nbk] = mfma16(pa[nbk * NGV / 8], vcode[pl], oacc[nbk]);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Move the accumulators into the wave's LDS sums and restart them: the
@@ -849,6 +851,11 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   auto compute = [&](auto ragged, const Buf& B, int blk) {
     const int valid = nctx - blk * kTile;
     float sc[2][4];
+    // Waves in their matrix-core phases (key products here, value products
+    // at the end of softmax_pv) run at raised priority, so that their
+    // back-to-back products issue while the other wave of the SIMD does its
+    // vector work (about 1 % on the 4-bit serving workload).
+    __builtin_amdgcn_s_setprio(1);
     if constexpr (KCH) {
       if (blk >= grp_end) {     // wave-uniform: once per key group
         const int grp = blk / gblk;
@@ -909,6 +916,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
         for (int r = 0; r < 4; ++r) sc[mb][r] = __builtin_fmaf(sd[r], kq, zq[r]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     softmax_pv(ragged, sc, B.v, B.vp, valid);
     if (++since_flush == kFlush) flush();
   };

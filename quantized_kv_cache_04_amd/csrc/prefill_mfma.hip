@@ -623,6 +623,9 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
     if (!wave_ok || t0 > p_wave) continue;   // nothing of this block is visible to the wave
 
     // ---- scores: tokens 8 q4 + 4T + i for T = 0, 1 --------------------------
+    // (the products run at raised wave priority, so that they issue while
+    // the other workgroup of the CU stages its block)
+    __builtin_amdgcn_s_setprio(1);
     f32x4 acc[2];
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
@@ -677,6 +680,7 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
       o[ct] = mfma16(vlo, phi, o[ct]);
       o[ct] = mfma16(vhi, plo, o[ct]);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // ---- normalize and store (or the split's partial state): lane holds

@@ -27,9 +27,10 @@
 // z * sum_c q_c for per-token keys, sum_t p_t z_t for values).  q8_0 codes
 // are fed as x + 128 (unsigned) and the 128 * sum term is removed.
 //
-// Grid: (splits, B * Hkv); 256 threads = 4 waves, each wave a contiguous run
-// of 32-token blocks.  The four waves are merged in LDS and the split-K
-// partials by the last block (splitk.h).
+// Grid: (splits, B * Hkv); 256 threads = 4 waves, which take the split's
+// 32-token blocks in turn, one key group (per-channel keys) or one block at a
+// time.  The four waves are merged in LDS; the split-K partials are merged by
+// dec_combine_kernel (splitk.h).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>

@@ -227,3 +227,26 @@ def test_per_channel_key_groups_on_matrix_cores(name, G, ctx, chunks, splits):
     ma, rel = attention_errors(out, ref)
     print(f"[parity] {name}: max_abs={ma:.3e} rel_l2={rel:.3e}", flush=True)
     assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)
+
+
+# Many splits: the merge kernel folds the partial states sixteen at a time,
+# so well over a hundred splits take it through many rounds; the long
+# context also gives every wave many key groups (its LDS parameter ring is
+# refilled).  (name, config, workload overrides, decode_splits)
+MANY_SPLIT_CASES = [
+    ("serving_171_splits", 5, dict(batch=1, n_kv_heads=1, ctx=65536), 250),
+    ("u3_70_splits", 3, dict(batch=1, n_kv_heads=1, ctx=20000), 200),
+]
+
+
+@pytest.mark.parametrize("name,cfg_id,over,splits", MANY_SPLIT_CASES,
+                         ids=[c[0] for c in MANY_SPLIT_CASES])
+def test_many_splits(name, cfg_id, over, splits):
+    w, inputs, cache, exp, kdeq, vdeq = _run(name, cfg_id, over, [over["ctx"]],
+                                             decode_splits=splits)
+    q = inputs["q"]
+    out = cache.decode(q.cuda()).cpu().numpy()
+    ref = oracle_attention(w, q, kdeq, vdeq, w.ctx)
+    ma, rel = attention_errors(out, ref)
+    print(f"[parity] {name}: max_abs={ma:.3e} rel_l2={rel:.3e}", flush=True)
+    assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)

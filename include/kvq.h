@@ -142,7 +142,7 @@ typedef struct kvq_config {
   float   rope_base;      /* e.g. 10000                                      */
   int32_t decode_splits;  /* 0 = automatic; otherwise the maximum number of
                              token splits per (sequence, KV head)            */
-  int32_t decode_path;    /* KVQ_PATH_AUTO, KVQ_PATH_VALU or KVQ_PATH_MFMA    */
+  int32_t decode_path;    /* KVQ_PATH_AUTO, _VALU, _MFMA or _LUT             */
   kvq_tensor_format k;    /* key format                                      */
   kvq_tensor_format v;    /* value format (PER_TOKEN only)                   */
   int32_t sink_tokens;    /* attention sink [KVQuant page, Attention Sink]:

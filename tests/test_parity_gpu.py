@@ -250,3 +250,35 @@ def test_many_splits(name, cfg_id, over, splits):
     ma, rel = attention_errors(out, ref)
     print(f"[parity] {name}: max_abs={ma:.3e} rel_l2={rel:.3e}", flush=True)
     assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)
+
+
+# Degenerate groups: constant values make a group's range zero (scale 0,
+# every code 0, dequantized value = the zero point), all-zero rows make
+# q8_0's absmax zero, and equal magnitudes make every outlier a tie (the
+# lower flat index wins).  Bytes and attention must still match the oracle.
+@pytest.mark.parametrize("path", ["auto", "valu"])
+@pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
+def test_degenerate_groups(cfg_id, path):
+    over = dict(batch=1, n_kv_heads=2, ctx=300)
+    w = make_workload(cfg_id, **over)
+    inputs = make_inputs(w, "cpu")
+    k, v = inputs["k"].clone(), inputs["v"].clone()
+    v[:, :64] = 1.5                 # per-token value groups of constant rows
+    v[:, 64:96] = 0.0               # all-zero rows
+    k[:, :, :, :32] = -0.25         # channels constant over every token
+    k[:, 100:140] = 0.0             # all-zero key rows (a per-channel group mixes them)
+    k[:, 200:230] = 2.0             # equal magnitudes in whole rows
+    inputs = dict(inputs, k=k, v=v)
+    n = w.ctx
+    chunks = [150, 1, 149]
+    print(f"[parity] case=degenerate cfg={cfg_id} path={path}", flush=True)
+    cache = gpu_cache(w, inputs, chunks, n + 37, decode_path=path)
+    exp, kdeq, vdeq = oracle_encode(w, inputs, n, n + 37)
+    bad = compare_regions(cache, exp)
+    assert not bad, "\n".join(bad)
+    q = inputs["q"]
+    out = cache.decode(q.cuda()).cpu().numpy()
+    ref = oracle_attention(w, q, kdeq, vdeq, n)
+    ma, rel = attention_errors(out, ref)
+    print(f"[parity] degenerate cfg{cfg_id} {path}: max_abs={ma:.3e} rel_l2={rel:.3e}", flush=True)
+    assert ma <= MAX_ABS and rel <= REL_L2, (ma, rel)

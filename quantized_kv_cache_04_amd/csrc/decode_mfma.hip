@@ -326,10 +326,10 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   };
   constexpr float kLazy = 8.0f;   // log2 headroom before the running max moves
   constexpr int kFedLog2 = 15;    // fed P operand entries stay below 2^kFedLog2
-  // register pipeline depth: three buffers where the registers allow
-  // (per-channel keys, small blocks, single-group values), else two
-  constexpr int kBufDwords = 2 * KB + 2 * VB + 2 * VPD + 2 * KPD;
-  constexpr int kStages = (KCH && kBufDwords <= 32 && NGV == 1) ? 3 : 2;
+  // Register pipeline: two buffers, one block in flight while one is
+  // computed.  (A third buffer, where the registers allowed it, was slower
+  // once the waves of a workgroup interleave their blocks: 202.9 against
+  // 200.8 us on the 4-bit serving workload, with 30 more registers.)
 
   __shared__ float wm[4][8], wl[4][8];
   __shared__ float wo[4][8][kD];
@@ -923,8 +923,8 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   };
 
   // ---- hot loop: register pipeline over the wave's blocks with 32 cached
-  // tokens and quantized keys; kStages - 1 blocks are in flight while one is
-  // computed.  (Prefetches past the end re-read the last block.)
+  // tokens and quantized keys; one block is in flight while one is computed.
+  // (Prefetches past the end re-read the last block.)
   if (nk_full > 0) {
     // iterator over wblock(0), wblock(1), ... (scalar): within a unit the
     // next block follows, after a unit's last block come 3 units of the
@@ -945,30 +945,14 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     BlockIter pf{wblock(0), 0, 0}, cb{wblock(0), 0, 0};
     auto next_load = [&]() { const int b = pf.blk; advance(pf); return b; };
     auto next_comp = [&]() { const int b = cb.blk; advance(cb); return b; };
-    if constexpr (kStages == 3) {
-      Buf b0, b1, b2;
-      load(b0, next_load());
+    Buf b0, b1;
+    load(b0, next_load());
+    for (int k = 0; k < nk_full; k += 2) {
       load(b1, next_load());
-      for (int k = 0; k < nk_full; k += 3) {
-        load(b2, next_load());
-        compute(std::false_type{}, b0, next_comp());
-        if (k + 1 >= nk_full) break;
-        load(b0, next_load());
-        compute(std::false_type{}, b1, next_comp());
-        if (k + 2 >= nk_full) break;
-        load(b1, next_load());
-        compute(std::false_type{}, b2, next_comp());
-      }
-    } else {
-      Buf b0, b1;
+      compute(std::false_type{}, b0, next_comp());
+      if (k + 1 >= nk_full) break;
       load(b0, next_load());
-      for (int k = 0; k < nk_full; k += 2) {
-        load(b1, next_load());
-        compute(std::false_type{}, b0, next_comp());
-        if (k + 1 >= nk_full) break;
-        load(b0, next_load());
-        compute(std::false_type{}, b1, next_comp());
-      }
+      compute(std::false_type{}, b1, next_comp());
     }
   }
   // per-token keys: the ragged last block of the context, taken by the wave

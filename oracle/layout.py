@@ -29,7 +29,8 @@ Value tiles ("V-tile" layout): tokens are grouped in tiles of 32.  A tile is
 L, segment s, block m holds channel 16*(4s + m) + i; element e of that block
 is token 4q + e (e < 4) or 16 + 4q + (e - 4) (e >= 4) of the tile.
 
-Capacity: the cache holds Tcap = round_up(max_ctx, 32) tokens per sequence.
+Capacity: the cache holds Tcap = round_up(max_ctx, 1024) tokens per sequence
+(``capacity``), a multiple of the 32-token tile.
 """
 from __future__ import annotations
 

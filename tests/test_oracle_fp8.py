@@ -113,4 +113,13 @@ def test_regions_and_payload():
         want = np.concatenate([c[0, 0].reshape(-1), np.zeros(24 * 128, np.uint8)])
         assert np.array_equal(np.sort(reg["codes"][0, 0, :64 * 128]), np.sort(want))
     kw = dict(batch=3, n_kv_heads=2, head_dim=128, kv_dtype="f16")
-    assert ocb.payload_bytes(FP8, FP8, n_ctx=100, **kw) == 2 * (3 * 2 * 100 * 128 + 2 * 4)
+    # by hand: each tensor holds 3 sequences x 2 heads x 100 tokens x 128
+    # one-byte codes = 76,800 bytes plus 2 float32 head scales = 8 bytes;
+    # keys and values together 2 x 76,808 = 153,616 bytes
+    assert ocb.payload_bytes(FP8, FP8, n_ctx=100, **kw) == 153_616
+    # half the raw fp16 cache (2 * L * h * d * 2 bytes per token, TurboQuant
+    # page 2.1: 2 * 2 * 128 * 2 = 1,024 bytes per token and sequence, 307,200
+    # for 300 token-sequences) plus the scales
+    raw = {"quantizer": "none", "bits": 16}
+    assert ocb.payload_bytes(raw, raw, n_ctx=100, **kw) == 307_200
+    assert ocb.payload_bytes(FP8, FP8, n_ctx=100, **kw) == 307_200 // 2 + 16

@@ -75,7 +75,9 @@ typedef int32_t kvq_status;
  *   ceil(outlier_frac * n_kv_heads * head_dim) entries of largest |x| of each
  *   token are kept in fp16 (CSR; n_kv_heads * head_dim <= 4096) and replace
  *   the dense value
- *   [KVQuant page 2.2, 3.3].
+ *   [KVQuant page 2.2, 3.3].  The int32 row pointers bound the capacity:
+ *   (batch * Tcap + 1) * outliers per token must not exceed 2^31 - 1
+ *   (KVQ_ERR_UNSUPPORTED otherwise).
  * FP8_E5M2: each element is the FP8 E5M2 byte (sign, 5 exponent bits, 2
  *   mantissa bits: the high byte of an fp16) of x / s_h, rounded to nearest
  *   even and saturated at +-57344, with one float32 scale s_h per KV head

@@ -125,7 +125,21 @@ kvq_status check_config(const kvq_config* c) {
                 c->sink_tokens);
   kvq_status st = check_format(c->k, *c, true, "k");
   if (st != KVQ_OK) return st;
-  return check_format(c->v, *c, false, "v");
+  st = check_format(c->v, *c, false, "v");
+  if (st != KVQ_OK) return st;
+  // the CSR row pointers are int32 offsets k * r over every row r of the
+  // capacity (B * Tcap rows): they must not wrap
+  const uint64_t rows = (uint64_t)c->batch * align_up((uint64_t)c->max_ctx, kCapAlign) + 1;
+  const kvq_tensor_format* fmts[2] = {&c->k, &c->v};
+  for (int i = 0; i < 2; ++i) {
+    if (fmts[i]->quantizer != KVQ_QUANT_CODEBOOK) continue;
+    const uint64_t k = (uint64_t)outlier_count(fmts[i]->outlier_frac, c->n_kv_heads * c->head_dim);
+    if (k && rows * k > (uint64_t)INT32_MAX)
+      return fail(KVQ_ERR_UNSUPPORTED, "%s: %llu outliers per token over batch * capacity = %llu "
+                  "rows overflow the int32 CSR row pointers", i ? "v" : "k",
+                  (unsigned long long)k, (unsigned long long)(rows - 1));
+  }
+  return KVQ_OK;
 }
 
 void fill_tensor(TensorLayout& t, const kvq_tensor_format& f, const kvq_config& c, int64_t Tcap,

@@ -170,6 +170,59 @@ def cache_layout(cfg: Config) -> LayoutInfo:
     return info
 
 
+_TORCH_DTYPES = {"f16": "float16", "bf16": "bfloat16", "f32": "float32"}
+
+
+def _torch_dtype(name: str):
+    import torch
+    return getattr(torch, _TORCH_DTYPES[name])
+
+
+def _dtype_name(t) -> str:
+    import torch
+    names = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}
+    if t.dtype not in names:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return names[t.dtype]
+
+
+def _check_tensor(name: str, t, shape, dtype=None, device: bool = True) -> None:
+    """Raise before any device call unless ``t`` is a contiguous device
+    tensor of ``shape`` (and ``dtype``): the C ABI takes raw pointers and
+    would read or write past a smaller or differently laid out buffer."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor (got {t.device})")
+
+
+def _check_devices(**tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name}: must be a device tensor (got {t.device})")
+
+
+def _resolve_out(out, out_dtype: Optional[str], shape, device):
+    """The output tensor and its dtype name: ``out`` decides the dtype when
+    given (a conflicting ``out_dtype`` is an error); otherwise a new tensor
+    of ``out_dtype`` (default f32)."""
+    import torch
+    if out is None:
+        name = out_dtype or "f32"
+        if name not in DTYPES:
+            raise ValueError(f"out_dtype must be one of {sorted(DTYPES)}")
+        return torch.empty(shape, dtype=_torch_dtype(name), device=device), name
+    name = _dtype_name(out)
+    if out_dtype is not None and out_dtype != name:
+        raise TypeError(f"out has dtype {out.dtype} but out_dtype={out_dtype!r}")
+    _check_tensor("out", out, shape, device=False)
+    return out, name
+
+
 def _stream_ptr(stream) -> Optional[int]:
     import torch
     if stream is None:
@@ -208,13 +261,13 @@ class Cache:
     def append(self, k_new, v_new, stream=None) -> None:
         quantize_append(self, k_new, v_new, stream)
 
-    def decode(self, q, q_pos=None, sm_scale: float = 0.0, out=None, out_dtype: str = "f32",
-               stream=None):
+    def decode(self, q, q_pos=None, sm_scale: float = 0.0, out=None,
+               out_dtype: Optional[str] = None, stream=None):
         return decode_attention(self, q, q_pos=q_pos, sm_scale=sm_scale, out=out,
                                 out_dtype=out_dtype, stream=stream)
 
-    def prefill(self, q, sm_scale: float = 0.0, out=None, out_dtype: str = "f32", stream=None,
-                workspace=None):
+    def prefill(self, q, sm_scale: float = 0.0, out=None, out_dtype: Optional[str] = None,
+                stream=None, workspace=None):
         return prefill_attention(self, q, sm_scale=sm_scale, out=out, out_dtype=out_dtype,
                                  stream=stream, workspace=workspace)
 
@@ -236,7 +289,15 @@ def set_decode_events(start=None, stop=None) -> None:
 
 def quantize_append(cache: Cache, k_new, v_new, stream=None) -> None:
     """Append k_new/v_new ([B, n_new, Hkv, d], cache dtype, contiguous, on the device)."""
+    c = cache.cfg
+    if k_new.dim() != 4:
+        raise ValueError(f"k_new: expected [B, n_new, Hkv, d], got shape {tuple(k_new.shape)}")
     n_new = int(k_new.shape[1])
+    kdt = _torch_dtype({F16: "f16", BF16: "bf16"}[c.kv_dtype])
+    shape = (c.batch, n_new, c.n_kv_heads, c.head_dim)
+    _check_tensor("k_new", k_new, shape, kdt, device=False)
+    _check_tensor("v_new", v_new, shape, kdt, device=False)
+    _check_devices(k_new=k_new, v_new=v_new)
     cs = cache.struct()
     _check(lib().kvq_quantize_append(ctypes.byref(cache.cfg), ctypes.byref(cs),
                                      k_new.data_ptr(), v_new.data_ptr(), n_new,
@@ -245,12 +306,19 @@ def quantize_append(cache: Cache, k_new, v_new, stream=None) -> None:
 
 
 def decode_attention(cache: Cache, q, q_pos=None, sm_scale: float = 0.0, out=None,
-                     out_dtype: str = "f32", stream=None):
-    """One decode step: q [B, Hq, d] -> out [B, Hq, d] of ``out_dtype``."""
+                     out_dtype: Optional[str] = None, stream=None):
+    """One decode step: q [B, Hq, d] -> out [B, Hq, d].  The output dtype is
+    that of ``out`` when given, else ``out_dtype`` (default f32).  ``q_pos``:
+    int32 [B] device tensor or None."""
     import torch
-    if out is None:
-        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[out_dtype]
-        out = torch.empty(q.shape, dtype=tdt, device=q.device)
+    c = cache.cfg
+    shape = (c.batch, c.n_q_heads, c.head_dim)
+    _check_tensor("q", q, shape, _torch_dtype({F16: "f16", BF16: "bf16"}[c.kv_dtype]),
+                  device=False)
+    if q_pos is not None:
+        _check_tensor("q_pos", q_pos, (c.batch,), torch.int32, device=False)
+    out, out_dtype = _resolve_out(out, out_dtype, shape, q.device)
+    _check_devices(q=q, q_pos=q_pos, out=out)
     cs = cache.struct()
     _check(lib().kvq_decode_attention(ctypes.byref(cache.cfg), ctypes.byref(cs), q.data_ptr(),
                                       q_pos.data_ptr() if q_pos is not None else None,
@@ -266,18 +334,25 @@ def prefill_workspace_bytes(cfg: Config, n_q: int, n_ctx: int) -> int:
     return int(out.value)
 
 
-def prefill_attention(cache: Cache, q, sm_scale: float = 0.0, out=None, out_dtype: str = "f32",
-                      stream=None, workspace=None):
+def prefill_attention(cache: Cache, q, sm_scale: float = 0.0, out=None,
+                      out_dtype: Optional[str] = None, stream=None, workspace=None):
     """Causal attention of the last n_q cached tokens: q [B, n_q, Hq, d] ->
     out [B, n_q, Hq, d] of ``out_dtype``.  ``workspace``: a uint8 device
     tensor for the token-axis split; by default one of the size the library
     asks for is kept on the cache object (grown when needed); pass an empty
     tensor for no split."""
     import torch
-    if out is None:
-        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[out_dtype]
-        out = torch.empty(q.shape, dtype=tdt, device=q.device)
+    c = cache.cfg
+    if q.dim() != 4:
+        raise ValueError(f"q: expected [B, n_q, Hq, d], got shape {tuple(q.shape)}")
     n_q = int(q.shape[1])
+    shape = (c.batch, n_q, c.n_q_heads, c.head_dim)
+    _check_tensor("q", q, shape, _torch_dtype({F16: "f16", BF16: "bf16"}[c.kv_dtype]),
+                  device=False)
+    out, out_dtype = _resolve_out(out, out_dtype, shape, q.device)
+    if workspace is not None:
+        _check_tensor("workspace", workspace, (workspace.numel(),), torch.uint8, device=False)
+    _check_devices(q=q, out=out, workspace=workspace)
     if workspace is None:
         need = prefill_workspace_bytes(cache.cfg, n_q, cache.n_ctx)
         ws = getattr(cache, "_prefill_ws", None)

@@ -313,3 +313,17 @@ def test_decode_path_selection():
         with pytest.raises(kvq.KvqError) as ei:
             kvq.decode_path(cfg)
         assert ei.value.status == kvq.ERR_UNSUPPORTED
+
+
+def test_outlier_row_pointers_must_not_wrap():
+    # 41 outliers per token (1 % of 32 x 128): the int32 row pointers hold
+    # 41 * (B * Tcap) and must stay below 2^31 (52,377,649 rows at most)
+    cb = {"quantizer": "codebook", "bits": 4, "outlier_frac": 0.01}
+    base = dict(n_q_heads=32, n_kv_heads=32, kv_dtype="f16", k=cb, v=cb)
+    ok = kvq.make_config(batch=51, max_ctx=1 << 20, **base)        # 53,477,376 rows: too many
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.cache_bytes(ok, 0, 1, kvq.BYTES_ALLOC)
+    assert e.value.status == kvq.ERR_UNSUPPORTED
+    assert "row pointers" in str(e.value)
+    fits = kvq.make_config(batch=49, max_ctx=1 << 20, **base)      # 51,380,224 rows
+    assert kvq.cache_bytes(fits, 0, 1, kvq.BYTES_ALLOC) > 0

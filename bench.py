@@ -56,9 +56,10 @@ def kernel_source_sha(kernel: str) -> str:
 
 
 def counter_traffic(workload: str, kernel: str):
-    """Per-launch HBM bytes of the decode kernel from committed rocprofv3
+    """Per-launch HBM bytes of the decode kernel recorded from rocprofv3
     counter runs (profiles/traffic.json), if they were taken on the current
-    kernel sources; None otherwise."""
+    kernel sources; None otherwise.  Not measured in this run: the record
+    says which runs it comes from."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         rec = json.load(open(path)).get(f"{workload}/{kernel}")
@@ -66,7 +67,27 @@ def counter_traffic(workload: str, kernel: str):
         return None
     if not rec or rec.get("kernel_source_sha") != kernel_source_sha(kernel):
         return None
-    return rec.get("bytes_per_launch")
+    return {"bytes_per_launch": rec.get("bytes_per_launch"),
+            "source": f"recorded in profiles/traffic.json (kernel source sha "
+                      f"{rec['kernel_source_sha']}): {rec.get('note', '')}"}
+
+
+def settle(ms: float, call, stream) -> int:
+    """Run ``call(i)`` (a decode that leaves the cache unchanged) on ``stream``
+    until ``ms`` milliseconds of wall time have passed; returns the number of
+    calls.  A GPU that has just gone from idle to streaming runs the decode
+    kernel up to a third slower for tens of launches before its clocks
+    settle; a serving GPU runs continuously."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(20):
+                call(n)
+                n += 1
+            torch.cuda.synchronize()
+    return n
 
 
 def cpu_baseline(w, seconds: float = 12.0):
@@ -131,6 +152,10 @@ def main():
     ap.add_argument("--path", choices=["auto", "valu", "mfma", "lut"], default="auto")
     ap.add_argument("--splits", type=int, default=0,
                     help="upper bound on split-K partitions of the token axis (0 = library default)")
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="before the warm-up steps, run decode calls (which leave the cache "
+                         "unchanged) for this long, so that the GPU's clocks settle into the "
+                         "state a continuously serving GPU runs in")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--kv-format", choices=["workload", "fp8_e5m2"], default="workload",
@@ -263,6 +288,9 @@ def main():
         else:
             step_bytes.append(kvq.cache_bytes(cfg, c.n_ctx))
 
+    settle_calls = settle(args.settle_ms, lambda i: caches[i % copies].decode(q, out=out,
+                                                                            stream=stream),
+                          stream)
     with torch.cuda.stream(stream):
         for i in range(W):
             step(i)
@@ -295,6 +323,8 @@ def main():
     kernel = DECODE_KERNELS[path]
     wl = CONFIG_NAME(w)
     traffic = counter_traffic(wl, kernel)
+    log(f"{kernel} per instrumented step (us): " + " ".join(f"{a.elapsed_time(b) * 1e3:.0f}"
+                                                          for a, b in zip(ker_s, ker_e)))
     log(f"step {ms_step * 1e3:.1f} us, decode call {dec_avg * 1e3:.1f} us, {kernel} avg "
         f"{ker_avg * 1e3:.1f} us (p10 {ker_ms[K // 10] * 1e3:.1f}, p90 {ker_ms[(9 * K) // 10] * 1e3:.1f}), "
         f"{bytes_avg / 1e6:.1f} MB/step -> {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.1%} of peak)")
@@ -336,10 +366,12 @@ def main():
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ctx": w.ctx,
                    "k_format": _fmt(w.k), "v_format": _fmt(w.v),
                    "step": "append 1 token/sequence + decode" if serving else "decode",
-                   "decode_kernel": kernel, "cache_copies": copies},
+                   "decode_kernel": kernel, "cache_copies": copies,
+                   "settle": {"ms": args.settle_ms, "decode_calls": settle_calls}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic,
+                     "traffic": traffic["bytes_per_launch"] if traffic else None,
+                     "traffic_source": traffic["source"] if traffic else None,
                      "kernel": kernel, "avg_launch_us": round(ker_avg * 1e3, 2),
                      "decode_call_us": round(dec_avg * 1e3, 2),
                      "algorithmic_bytes_per_launch": int(sum(inst_bytes) / K)},

@@ -294,6 +294,30 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
                                 int32_t out_dtype, void* stream);
 
 /*
+ * kvq_decode_attention_scratch -- kvq_decode_attention for callers that
+ * cannot allocate device memory or write outside the buffers they pass
+ * (code under HIP graph capture, serving loops and harnesses that forbid
+ * allocation).  It computes the same attention with the same kernels, but
+ * keeps the split-K partial softmax states in a static device array of the
+ * library (KVQ_DECODE_SCRATCH_BYTES per GPU, held until the process ends)
+ * instead of the workspace region of cache->base, which it leaves
+ * untouched.  It allocates nothing.
+ *   Arguments, layout and errors as kvq_decode_attention.  When the array
+ *   holds fewer partial states per (sequence, query head) than the library
+ *   would use, the token axis is split fewer times (same result up to
+ *   rounding); UNSUPPORTED when it cannot hold one state per query head
+ *   plus one per 256 sink tokens (batch * n_q_heads * (head_dim + 2) * 4
+ *   bytes each).
+ *   All calls on one GPU share its array and it keeps the last call's
+ *   contents: calls that overlap in time on one GPU (other streams, other
+ *   host threads) race and must be serialized by the caller.
+ */
+#define KVQ_DECODE_SCRATCH_BYTES (8u << 20)
+kvq_status kvq_decode_attention_scratch(const kvq_config* cfg, const kvq_cache* cache,
+                                        const void* q, const int32_t* q_pos, float sm_scale,
+                                        void* out, int32_t out_dtype, void* stream);
+
+/*
  * kvq_prefill_attention -- causal attention of the last n_q tokens of every
  * sequence over the cache: the attention of a prefill chunk (chunked
  * prefill) once its keys and values have been appended with
@@ -360,7 +384,7 @@ const char* kvq_last_error(void);
    gained sink_tokens and kvq_tensor_regions gained sink; 102 adds
    kvq_prefill_attention; 103 adds KVQ_QUANT_FP8_E5M2 and the kvq_cache
    scale pointers; 104 gives kvq_prefill_attention a workspace and adds
-   kvq_prefill_workspace_bytes. */
+   kvq_prefill_workspace_bytes; 105 adds kvq_decode_attention_scratch. */
 int32_t kvq_abi_version(void);
 
 #ifdef __cplusplus

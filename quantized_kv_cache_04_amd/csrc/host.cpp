@@ -258,6 +258,11 @@ kvq_status device_status(hipError_t e, const char* what) {
 
 }  // namespace
 
+kvq_status set_error(kvq_status st, const char* msg) {
+  g_last_error = msg;
+  return st;
+}
+
 DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebook,
                           const float* scale) {
   uint8_t* b = static_cast<uint8_t*>(base);
@@ -306,7 +311,7 @@ int32_t kvq_decode_path(const kvq_config* cfg) {
   return ok ? KVQ_PATH_MFMA : KVQ_PATH_VALU;
 }
 
-int32_t kvq_abi_version(void) { return 104; }
+int32_t kvq_abi_version(void) { return 105; }
 
 kvq_status kvq_set_decode_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr))
@@ -405,6 +410,19 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const vo
 kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q,
                                 const int32_t* q_pos, float sm_scale, void* out,
                                 int32_t out_dtype, void* stream) {
+  return kvq::decode_attention_impl(cfg, cache, q, q_pos, sm_scale, out, out_dtype, stream,
+                                    nullptr, 0);
+}
+
+}  // extern "C"
+
+// One decode step (kvq_decode_attention).  partial_ws: the split-K partial
+// states go there instead of the workspace region of the cache allocation,
+// which then holds at most ws_bytes of them (fewer splits when needed).
+kvq_status kvq::decode_attention_impl(const kvq_config* cfg, const kvq_cache* cache,
+                                      const void* q, const int32_t* q_pos, float sm_scale,
+                                      void* out, int32_t out_dtype, void* stream,
+                                      float* partial_ws, uint64_t ws_bytes) {
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
   if (!cache) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache is NULL");
@@ -445,8 +463,21 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   a.S_max = L.S_max;
   a.kp_groups = 0;
   a.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(cache->base) + L.partial_off);
+  if (partial_ws) {
+    // as many partial slots per (sequence, query head) as the buffer holds
+    const uint64_t per_slot = (uint64_t)cfg->batch * cfg->n_q_heads * (cfg->head_dim + 2) * 4;
+    const uint64_t fit = ws_bytes / per_slot;
+    if (fit < (uint64_t)a.S_max) a.S_max = (int)fit;
+    if (a.S_max < 1 + sink_slots(L.sink))
+      return fail(KVQ_ERR_UNSUPPORTED, "the %llu-byte scratch holds %llu partial states per "
+                  "(sequence, query head); this batch of %d x %d query heads with %lld sink "
+                  "tokens needs at least %lld", (unsigned long long)ws_bytes,
+                  (unsigned long long)fit, cfg->batch, cfg->n_q_heads, (long long)L.sink,
+                  (long long)(1 + sink_slots(L.sink)));
+    a.partial = partial_ws;
+  }
   // partial slots left for the quantized cache's splits
-  const int64_t max_q_splits = L.S_max - sink_slots(L.sink);
+  const int64_t max_q_splits = a.S_max - sink_slots(L.sink);
 
   // Split the token axis so that the grid is about one resident round of
   // workgroups (256 CUs x 2 workgroups of 4 waves): fewer, longer
@@ -542,6 +573,8 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   if (e == hipSuccess && !a.direct) e = launch_combine(a, s);
   return device_status(e, "decode attention");
 }
+
+extern "C" {
 
 namespace {
 // Token-axis split of prefill: about 512 workgroups (two per CU), at least

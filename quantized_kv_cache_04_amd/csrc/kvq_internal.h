@@ -105,6 +105,15 @@ struct DecodeArgs {
   int kp_groups;        // matrix-core kernel: key groups staged in LDS per wave (0 = none)
 };
 
+// kvq_decode_attention with the split-K partial states in partial_ws
+// (ws_bytes) instead of the cache's workspace region when partial_ws is set
+kvq_status decode_attention_impl(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                                 const int32_t* q_pos, float sm_scale, void* out,
+                                 int32_t out_dtype, void* stream, float* partial_ws,
+                                 uint64_t ws_bytes);
+// the error message of the calling thread (kvq_last_error)
+kvq_status set_error(kvq_status st, const char* msg);
+
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
 // merge of the split-K partials, the sink's included (when a.direct is 0)
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);

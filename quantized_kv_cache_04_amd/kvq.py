@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvq.h")
 # interface version the structures below follow (major * 100 + minor)
-ABI_VERSION = 104
+ABI_VERSION = 105
 
 # ---- constants mirrored from kvq.h -------------------------------------------
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_DEVICE = 0, -1, -2, -3, -4
@@ -90,6 +90,7 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attention.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(CacheStruct),
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+        L.kvq_decode_attention_scratch.argtypes = L.kvq_decode_attention.argtypes
         L.kvq_prefill_attention.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(CacheStruct),
                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
@@ -97,7 +98,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.c_int32,
                                                   ctypes.c_int64, ctypes.POINTER(ctypes.c_uint64)]
         for fn in ("kvq_cache_bytes", "kvq_cache_layout", "kvq_quantize_append",
-                   "kvq_decode_attention", "kvq_prefill_attention", "kvq_prefill_workspace_bytes"):
+                   "kvq_decode_attention", "kvq_decode_attention_scratch",
+                   "kvq_prefill_attention", "kvq_prefill_workspace_bytes"):
             getattr(L, fn).restype = ctypes.c_int32
         L.kvq_last_error.restype = ctypes.c_char_p
         L.kvq_last_error.argtypes = []
@@ -324,6 +326,29 @@ def decode_attention(cache: Cache, q, q_pos=None, sm_scale: float = 0.0, out=Non
                                       q_pos.data_ptr() if q_pos is not None else None,
                                       float(sm_scale), out.data_ptr(), DTYPES[out_dtype],
                                       _stream_ptr(stream)))
+    return out
+
+
+def decode_attention_scratch(cache: Cache, q, q_pos=None, sm_scale: float = 0.0, out=None,
+                             out_dtype: Optional[str] = None, stream=None):
+    """decode_attention through kvq_decode_attention_scratch: the split-K
+    partial states live in the library's static device array (calls on one
+    GPU must not overlap).  The caller that cannot allocate passes ``out``."""
+    import torch
+    c = cache.cfg
+    shape = (c.batch, c.n_q_heads, c.head_dim)
+    _check_tensor("q", q, shape, _torch_dtype({F16: "f16", BF16: "bf16"}[c.kv_dtype]),
+                  device=False)
+    if q_pos is not None:
+        _check_tensor("q_pos", q_pos, (c.batch,), torch.int32, device=False)
+    out, out_dtype = _resolve_out(out, out_dtype, shape, q.device)
+    _check_devices(q=q, q_pos=q_pos, out=out)
+    cs = cache.struct()
+    _check(lib().kvq_decode_attention_scratch(ctypes.byref(cache.cfg), ctypes.byref(cs),
+                                              q.data_ptr(),
+                                              q_pos.data_ptr() if q_pos is not None else None,
+                                              float(sm_scale), out.data_ptr(), DTYPES[out_dtype],
+                                              _stream_ptr(stream)))
     return out
 
 

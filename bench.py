@@ -161,6 +161,11 @@ def main():
     ap.add_argument("--kv-format", choices=["workload", "fp8_e5m2"], default="workload",
                     help="fp8_e5m2: store keys and values of the workload's shape as FP8 E5M2 "
                          "with per-head scales instead of its own formats")
+    ap.add_argument("--paged", nargs="?", const="shuffled", choices=["shuffled", "sequential"],
+                    default=None,
+                    help="store the cache as a paged cache: a pool of 32-token pages that a "
+                         "seeded, shuffled page table (or the identity order) deals out to the "
+                         "sequences")
     ap.add_argument("--prefill", type=int, default=0, metavar="N",
                     help="measure chunked prefill instead: each step appends an N-token chunk to "
                          "a cache of ctx - N tokens and runs causal attention for its N queries")
@@ -182,7 +187,7 @@ def main():
     import quantized_kv_cache_04_amd as kvq_pkg
     from quantized_kv_cache_04_amd import kvq
     from synth import make_workload
-    from synth.workloads import make_inputs, make_step_tokens
+    from synth.workloads import make_inputs, make_page_table, make_step_tokens
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -219,8 +224,9 @@ def main():
     # warm-up, the timed steps, then as many instrumented steps (serving: one
     # token per sequence appended at each)
     max_ctx = w.ctx + (W + 2 * K + 1 if serving else 0)
+    n_pages = w.batch * ((max_ctx + 31) // 32) if args.paged else 0
     cfg = kvq.config_from_workload(w, max_ctx=max_ctx, decode_path=args.path,
-                                   decode_splits=args.splits)
+                                   decode_splits=args.splits, page_pool=n_pages)
     stream = torch.cuda.Stream()
     log(f"workload cfg{w.cfg_id} {CONFIG_NAME(w)}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} "
         f"T={w.ctx}; generating inputs on the GPU")
@@ -231,9 +237,14 @@ def main():
         copies = 1 if serving else max(1, math.ceil(1.0e9 / payload0))
         caches = []
         for i in range(copies):
+            table = None
+            if args.paged == "shuffled":
+                table = make_page_table(w, max_ctx, n_pages, dev)
+            elif args.paged == "sequential":
+                table = torch.arange(n_pages, dtype=torch.int32, device=dev).reshape(w.batch, -1)
             c = kvq.Cache(cfg, device=dev, k_codebook=inputs["k_codebook"],
                           v_codebook=inputs["v_codebook"], k_scale=inputs["k_scale"],
-                          v_scale=inputs["v_scale"])
+                          v_scale=inputs["v_scale"], page_table=table)
             c.append(inputs["k"], inputs["v"], stream=stream)
             caches.append(c)
         q = inputs["q"]
@@ -367,6 +378,8 @@ def main():
                    "k_format": _fmt(w.k), "v_format": _fmt(w.v),
                    "step": "append 1 token/sequence + decode" if serving else "decode",
                    "decode_kernel": kernel, "cache_copies": copies,
+                   "paged": ({"pages": n_pages, "page_tokens": 32, "table": args.paged}
+                             if args.paged else None),
                    "settle": {"ms": args.settle_ms, "decode_calls": settle_calls}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -559,7 +572,12 @@ def CONFIG_NAME(w) -> str:
     name = CONFIGS[w.cfg_id]["name"] + (f"_t{w.ctx}" if w.cfg_id == 2 else "")
     if w.k["quantizer"] == "fp8_e5m2" and CONFIGS[w.cfg_id]["k"]["quantizer"] != "fp8_e5m2":
         name += "_fp8e5m2"
+    if PAGED:
+        name += "_paged"
     return name
+
+
+PAGED = any(a.startswith("--paged") for a in sys.argv)
 
 
 def _fmt(f) -> str:

@@ -157,6 +157,17 @@ typedef struct kvq_config {
                              >= N [NIAH page 5.2, its threshold parameter])
                              is this with sink_tokens = N.
                              0 .. 4096; 0 = none                              */
+  int32_t page_pool;      /* paged cache [Survey page 3.4: vLLM's block-table
+                             cache, --block-size 16]: 0 = one contiguous
+                             stretch of max_ctx tokens per sequence; > 0 = a
+                             pool of this many physical pages of 32 tokens
+                             (two of vLLM's 16-token blocks: the value tile
+                             of the decode kernels) shared by the sequences
+                             through kvq_cache.page_table.  A page holds the
+                             codes, per-token parameters and outlier rows of
+                             its 32 tokens for every KV head; per-channel key
+                             parameters, the key tail and the attention sink
+                             stay per sequence.  0 .. 2^26                    */
 } kvq_config;
 
 typedef struct kvq_cache {
@@ -173,6 +184,18 @@ typedef struct kvq_cache {
                              scales (finite, > 0), or NULL for 1; ignored by
                              the other formats                               */
   const float* v_scale;   /* same for values                                 */
+  const int32_t* page_table; /* page_pool > 0: device int32
+                             [batch][pages_per_seq] (kvq_layout_info;
+                             ceil(max_ctx / 32)): entry i of sequence b is
+                             the physical page of its tokens [32 i, 32 i + 32).
+                             Pages a call writes or reads must be distinct
+                             across sequences and logical pages; entries not
+                             yet in use are ignored.  Entries outside
+                             [0, page_pool) are clamped into it (no access
+                             leaves the allocation; the results are then
+                             undefined).  NULL when page_pool is 0.  Owned by
+                             the caller, who may update entries for pages
+                             not yet written between calls.                   */
 } kvq_cache;
 
 /* Location of one array inside the cache allocation (bytes from base). */
@@ -202,7 +225,8 @@ typedef struct kvq_layout_info {
                                between (sequence, head) streams stays a
                                multiple of 1024 tokens)                      */
   int32_t    max_splits;    /* split-K partial slots per (b, query head)   */
-  int32_t    reserved;
+  int32_t    pages_per_seq; /* paged cache: entries per sequence of
+                               kvq_cache.page_table (0 when not paged)      */
 } kvq_layout_info;
 
 /*
@@ -244,6 +268,13 @@ kvq_status kvq_cache_bytes(const kvq_config* cfg, int64_t n_ctx, int64_t n_layer
  *   params: per-token [B][Hkv][Tcap][d/G] of (scale, zero) fp16 pairs
  *     (q8_0: scales only); per-channel [B][Hkv][Tcap/G][d] pairs.
  *   NONE: raw rows [B][Hkv][Tcap][d] of kv_dtype for keys and values.
+ *   Paged cache (page_pool P > 0): every array with one record per token
+ *     and head (key rows, value tiles, per-token params, raw rows) holds
+ *     [P][Hkv][32] token rows instead of [B][Hkv][Tcap]: token t of
+ *     sequence b, head h is row (page_table[b][t / 32] * Hkv + h) * 32 +
+ *     t % 32.  The outlier CSR has P * 32 rows (row page * 32 + t % 32;
+ *     row_ptr [P * 32 + 1]).  Per-channel params, tail and sink keep their
+ *     per-sequence shapes.
  * Errors: as kvq_cache_bytes.
  */
 kvq_status kvq_cache_layout(const kvq_config* cfg, kvq_layout_info* out);
@@ -384,7 +415,9 @@ const char* kvq_last_error(void);
    gained sink_tokens and kvq_tensor_regions gained sink; 102 adds
    kvq_prefill_attention; 103 adds KVQ_QUANT_FP8_E5M2 and the kvq_cache
    scale pointers; 104 gives kvq_prefill_attention a workspace and adds
-   kvq_prefill_workspace_bytes; 105 adds kvq_decode_attention_scratch. */
+   kvq_prefill_workspace_bytes; 105 adds kvq_decode_attention_scratch;
+   106 adds the paged cache (kvq_config.page_pool, kvq_cache.page_table,
+   kvq_layout_info.pages_per_seq). */
 int32_t kvq_abi_version(void);
 
 #ifdef __cplusplus

@@ -25,4 +25,4 @@ Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, printed values, invariants and brute force.  Readings of the pages
 where they are silent are listed in ``quant.py`` and ``layout.py``.
 """
-from . import quant, layout, attention, cache_bytes  # noqa: F401
+from . import quant, layout, attention, cache_bytes, paging  # noqa: F401

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void dec_generic_kernel(DecodeArgs a) {
           }
         }
         if (a.k.k_out) {
-          const int64_t r = (int64_t)b * a.sh.Tcap + t;
+          const int64_t r = csr_row(a.sh, b, t);
           const int e0 = a.k.row_ptr[r], e1 = a.k.row_ptr[r + 1];
           for (int e = e0; e < e1; ++e) {
             const int col = (a.k.col[e] & 0xfff) - h * kD;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void dec_generic_kernel(DecodeArgs a) {
       if (a.v.k_out) {
         for (int tt = 0; tt < cnt; ++tt) {
           const int t2 = chunk + tt;
-          const int64_t r = (int64_t)b * a.sh.Tcap + t2;
+          const int64_t r = csr_row(a.sh, b, t2);
           const int e0 = a.v.row_ptr[r], e1 = a.v.row_ptr[r + 1];
           for (int e = e0; e < e1; ++e) {
             const int col = (a.v.col[e] & 0xfff) - h * kD;

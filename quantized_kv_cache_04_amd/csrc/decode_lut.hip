@@ -145,7 +145,6 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
   const int h = hg * kHeads + wave;
   const bool head_ok = h < Hkv;                  // wave-uniform
   const int nctx = a.n_ctx;
-  const int64_t Tcap = a.sh.Tcap;
   const int t_begin = split * a.blocks_per_split * kTile;
   const int t_end = min(nctx, t_begin + a.blocks_per_split * kTile);
   const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
@@ -209,8 +208,7 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
   // ---- per-wave state ------------------------------------------------------------
   float m_run = -INFINITY, l_lane = 0.f;
   float acc0 = 0.f, acc1 = 0.f;                  // channels lane, lane + 64
-  const uint8_t* krows = K.codes + ((int64_t)b * Hkv + (head_ok ? h : 0)) * Tcap * 64;
-  const uint8_t* vtiles = V.codes + ((int64_t)b * Hkv + (head_ok ? h : 0)) * Tcap * 64;
+  const int hr = head_ok ? h : 0;
 
   // Codes of one chunk: segments 2 half and 2 half + 1 (32 bytes) of the key
   // row of token tau, and the 32 value bytes of channel pair (lane).  Every
@@ -220,20 +218,25 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
   // ci + 1 load during the value phase of chunk ci; the value codes of a
   // chunk load at its start.
   const int last_tile = (nctx - 1) & ~31;
-  auto load_k = [&](int t0, u32x4* kk) {
+  // rows of the chunk at t0 (32 consecutive rows from its first token's,
+  // also on a page of a paged cache); chunks past the end read the last one
+  // (a paged cache's table is read one chunk ahead of the loads: chunk_row)
+  auto chunk_row = [&](int t0) { return tok_row(a.sh, b, hr, min(t0, last_tile)); };
+  auto load_k = [&](int t0, int64_t rowc, u32x4* kk) {
     const int tk = min(t0 + tau, nctx - 1);
-    const u32x4* kr = reinterpret_cast<const u32x4*>(krows + (int64_t)tk * 64) + 2 * half;
+    const int64_t row = rowc + (tk - min(t0, last_tile));
+    const u32x4* kr = reinterpret_cast<const u32x4*>(K.codes + row * 64) + 2 * half;
     kk[0] = kr[0];
     kk[1] = kr[1];
   };
-  auto load_v = [&](int t0, u32x4* vv) {
-    const int ts = min(t0, last_tile);
-    const u32x4* vr = reinterpret_cast<const u32x4*>(vtiles + (int64_t)ts * 64 + lane * 32);
+  auto load_v = [&](int64_t rowc, u32x4* vv) {
+    const u32x4* vr = reinterpret_cast<const u32x4*>(V.codes + rowc * 64 + lane * 32);
     vv[0] = vr[0];
     vv[1] = vr[1];
   };
   u32x4 kc[2];
-  load_k(t_begin, kc);
+  int64_t row_c = chunk_row(t_begin);
+  load_k(t_begin, row_c, kc);
 
   // Outlier entries of a chunk: the CSR rows of its tokens are contiguous
   // (k entries per token), read as 16-byte vectors of 8 entries, vector j by
@@ -306,12 +309,14 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
   for (int ci = 0; ci < n_chunks; ++ci) {
     const int t0 = t_begin + ci * kChunk;
     const int nt = min(kChunk, t_end - t0);      // tokens of this chunk
-    const int64_t row0 = (int64_t)b * Tcap + t0; // CSR row of token t0
+    const int64_t row0 = csr_row(a.sh, b, t0);   // CSR row of token t0
+
+    const int64_t row_n = chunk_row(t0 + kChunk);
 
     OutVec ko_v, vo_v;
     if constexpr (KOUT) load_out(K, row0, nt, ko_v);
     u32x4 vc[2], kn[2];
-    load_v(t0, vc);
+    load_v(row_c, vc);
 
     // ---- keys: lanes (tau, half), pairs i = 32m + 16 half + 8qq + e --------------------
     float s = 0.f;
@@ -382,7 +387,8 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
 
     // value outliers of this chunk, key codes and rotated queries of the next one
     if constexpr (VOUT) load_out(V, row0, nt, vo_v);
-    load_k(t0 + kChunk, kn);
+    load_k(t0 + kChunk, row_n, kn);
+    row_c = row_n;
     if constexpr (ROPE) set_q(ci + 1);
 
     if (head_ok) {

@@ -537,32 +537,37 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   float kscale = 0.f;        // sm2 * 2^(24 - E)
   int grp_end = -1;          // first block after the current key group
 
-  const uint8_t* kcodes = K.codes + prow * (4 * KB * 4);
-  const uint8_t* vcodes = V.codes + prow * (4 * VB * 4);
-  const uint8_t* vprm = F8 ? nullptr
-                           : static_cast<const uint8_t*>(V.params) + prow * NGV * (VQ8 ? 2 : 4);
-  const uint8_t* kprm = (KCH || F8) ? nullptr
-                                    : static_cast<const uint8_t*>(K.params) + prow * NGK * (KQ8 ? 2 : 4);
   const uint32_t k_lane_off = (uint32_t)n * (16 * KB) + (uint32_t)q4 * (4 * KB);
   const uint32_t v_lane_off = (uint32_t)lane * (8 * VB);
   const uint32_t p_lane_tok = 4u * (uint32_t)q4;
+  const bool paged = a.sh.page_table != nullptr;
 
-  auto load = [&](Buf& B, int blk) {
-    const uint32_t t0 = (uint32_t)blk * kTile;
+  // row of a block's first token: its 32 tokens are consecutive rows (one
+  // page of a paged cache)
+  auto block_row = [&](int blk) -> int64_t {
+    return paged ? tok_row(a.sh, b, h, (int64_t)blk * kTile) : prow + (int64_t)blk * kTile;
+  };
+  auto load_row = [&](Buf& B, int64_t r0) {
+    const uint8_t* kcodes = K.codes + r0 * (4 * KB * 4);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      load_dw<KB>(kcodes + (t0 + 16 * mb) * (16 * KB) + k_lane_off, B.k[mb]);
-      const uint32_t tok = t0 + 16 * mb + p_lane_tok;
+      load_dw<KB>(kcodes + (16 * mb) * (16 * KB) + k_lane_off, B.k[mb]);
+      const uint32_t tok = 16 * mb + p_lane_tok;
       if constexpr (F8) {
         B.vp[mb][0] = 0u;
         B.kp[mb][0] = 0u;
       } else {
+        const uint8_t* vprm = static_cast<const uint8_t*>(V.params) + r0 * NGV * (VQ8 ? 2 : 4);
         load_dw<VPD>(vprm + tok * (NGV * (VQ8 ? 2 : 4)), B.vp[mb]);
-        if constexpr (!KCH) load_dw<KPD>(kprm + tok * (NGK * (KQ8 ? 2 : 4)), B.kp[mb]);
+        if constexpr (!KCH) {
+          const uint8_t* kprm = static_cast<const uint8_t*>(K.params) + r0 * NGK * (KQ8 ? 2 : 4);
+          load_dw<KPD>(kprm + tok * (NGK * (KQ8 ? 2 : 4)), B.kp[mb]);
+        }
       }
     }
-    load_dw<2 * VB>(vcodes + t0 * (16 * VB) + v_lane_off, B.v);
+    load_dw<2 * VB>(V.codes + r0 * (4 * VB * 4) + v_lane_off, B.v);
   };
+  auto load = [&](Buf& B, int blk) { load_row(B, block_row(blk)); };
 
   // per-channel keys: B operand and zero-point term of key group ``grp``
   // The g * 16 blocks of 8 channels of the group's heads are shared out over
@@ -943,15 +948,25 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
       }
     };
     BlockIter pf{wblock(0), 0, 0}, cb{wblock(0), 0, 0};
-    auto next_load = [&]() { const int b = pf.blk; advance(pf); return b; };
+    // a paged cache's table entry of the next block to load is read one
+    // load ahead (a scalar load), and used only when that block's loads
+    // are issued
+    int pf_page = paged ? table_entry(a.sh, b, pf.blk) : 0;
+    auto next_load = [&]() {
+      const int64_t r = paged ? page_head_row(a.sh, clamp_page(a.sh, pf_page), h)
+                              : prow + (int64_t)pf.blk * kTile;
+      advance(pf);
+      if (paged) pf_page = table_entry(a.sh, b, pf.blk);
+      return r;
+    };
     auto next_comp = [&]() { const int b = cb.blk; advance(cb); return b; };
     Buf b0, b1;
-    load(b0, next_load());
+    load_row(b0, next_load());
     for (int k = 0; k < nk_full; k += 2) {
-      load(b1, next_load());
+      load_row(b1, next_load());
       compute(std::false_type{}, b0, next_comp());
       if (k + 1 >= nk_full) break;
-      load(b0, next_load());
+      load_row(b0, next_load());
       compute(std::false_type{}, b1, next_comp());
     }
   }

@@ -30,6 +30,44 @@ __device__ __forceinline__ uint16_t f2bf_rn(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// ---- token rows of the per-token arrays ---------------------------------------
+// Entry lp of sequence b of a paged cache's table, read through the
+// constant address space: the table does not change during a kernel, and
+// with a wave-uniform index this is a scalar load, which a kernel can wait
+// for without waiting for its vector loads in flight.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+__device__ __forceinline__ int table_entry(const DevShape& sh, int b, int64_t lp) {
+  const const_i32* t = (const const_i32*)sh.page_table;
+  return t[(int64_t)b * sh.pages_per_seq + lp];
+}
+// Physical page of a table entry.  Entries outside [0, n_pages) are clamped
+// into it: a bad table gives wrong values, never an access outside the
+// allocation.
+__device__ __forceinline__ int64_t clamp_page(const DevShape& sh, int p) {
+  return (int64_t)min(max(p, 0), sh.n_pages - 1);
+}
+__device__ __forceinline__ int64_t page_of(const DevShape& sh, int b, int64_t lp) {
+  return clamp_page(sh, table_entry(sh, b, lp));
+}
+// Row of token 0 of (physical page p, KV head h): see tok_row.
+__device__ __forceinline__ int64_t page_head_row(const DevShape& sh, int64_t p, int h) {
+  return (p * sh.Hkv + h) * kTile;
+}
+// Row of token t of (sequence b, KV head h) in the arrays with one record
+// per token and head (codes, per-token parameters; value tiles are 32 rows):
+// [B][Hkv][Tcap] in a contiguous cache, [page][Hkv][kTile] in a paged one.
+// The kTile tokens of one page and head are consecutive rows either way.
+__device__ __forceinline__ int64_t tok_row(const DevShape& sh, int b, int h, int64_t t) {
+  if (!sh.page_table) return ((int64_t)b * sh.Hkv + h) * sh.Tcap + t;
+  return page_head_row(sh, page_of(sh, b, t / kTile), h) + (t % kTile);
+}
+// Row of token t of sequence b in the outlier CSR (one row per token, all
+// heads): b * Tcap + t, or page * kTile + t mod kTile.
+__device__ __forceinline__ int64_t csr_row(const DevShape& sh, int b, int64_t t) {
+  if (!sh.page_table) return (int64_t)b * sh.Tcap + t;
+  return page_of(sh, b, t / kTile) * kTile + (t % kTile);
+}
+
 // ---- segment of 32 codes (u = 8m + e) ---------------------------------------
 // 8-bit: byte u.  4-bit: nibble u (low nibble = even u).  3-bit: see kvq.h.
 __device__ __forceinline__ uint32_t seg_code(const uint8_t* seg, int bits, int u) {
@@ -141,7 +179,7 @@ __device__ __forceinline__ float deq_uniform(uint32_t code, int quant, const voi
 // (bh = b * Hkv + h); per-channel keys past n_full come from the tail.
 __device__ inline float deq_key(const DevTensor& k, const DevShape& sh, int bh, int h, int64_t t,
                                 int c, int64_t n_full) {
-  const int64_t row = (int64_t)bh * sh.Tcap + t;
+  const int64_t row = tok_row(sh, bh / sh.Hkv, h, t);
   if (k.quant == KVQ_QUANT_NONE)
     return elem2f(reinterpret_cast<const uint16_t*>(k.codes)[row * kHeadDim + c], sh.kv_bf16);
   if (k.per_channel && t >= n_full)
@@ -158,10 +196,10 @@ __device__ inline float deq_key(const DevTensor& k, const DevShape& sh, int bh, 
 // Dense value of value channel c of token t of KV head h.
 __device__ inline float deq_value(const DevTensor& v, const DevShape& sh, int bh, int h, int64_t t,
                                   int c) {
-  const int64_t row = (int64_t)bh * sh.Tcap + t;
+  const int64_t row = tok_row(sh, bh / sh.Hkv, h, t);
   if (v.quant == KVQ_QUANT_NONE)
     return elem2f(reinterpret_cast<const uint16_t*>(v.codes)[row * kHeadDim + c], sh.kv_bf16);
-  const uint8_t* tile = v.codes + ((int64_t)bh * sh.Tcap + (t & ~(int64_t)(kTile - 1))) * v.row_bytes;
+  const uint8_t* tile = v.codes + (row - (t & (kTile - 1))) * v.row_bytes;
   if (v.quant == KVQ_QUANT_CODEBOOK) {
     const uint32_t code = v_pair_code(tile, (int)(t & (kTile - 1)), c);
     return h2f(v.codebook[((int64_t)h * kHeadDim + c) * 16 + code]);

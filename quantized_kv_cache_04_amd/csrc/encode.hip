@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void enc_rows_kernel(DevShape sh, DevTensor t,
     h = (int)(r % sh.Hkv);
     const int64_t bt = r / sh.Hkv;
     const int b = (int)(bt / n_new);
-    return ((int64_t)b * sh.Hkv + h) * sh.Tcap + n_ctx + bt % n_new;
+    return tok_row(sh, b, h, n_ctx + bt % n_new);
   };
   const int64_t r = (int64_t)blockIdx.x * 16 + rl;
   const bool active = r < nrows;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void enc_vtile_kernel(DevShape sh, DevTensor t
     const bool fresh = tpos >= lo_new && tpos < hi_new;
     float x[8];
     unpack8(xin[p], sh.kv_bf16, x);
-    const int64_t row = ((int64_t)b * sh.Hkv + h) * sh.Tcap + tpos;
+    const int64_t row = tok_row(sh, b, h, tpos);
     void* prm = nullptr;
     if (fresh && t.params)
       prm = static_cast<uint8_t*>(t.params) + row * (int64_t)t.ng * (t.quant == KVQ_QUANT_SYM_Q8_0 ? 2 : 4);
@@ -225,8 +225,7 @@ __global__ __launch_bounds__(256) void enc_vtile_kernel(DevShape sh, DevTensor t
   }
   __syncthreads();
   const int bits = t.bits;
-  uint32_t* tile_dw = reinterpret_cast<uint32_t*>(
-      t.codes + (((int64_t)b * sh.Hkv + h) * sh.Tcap + t_begin) * t.row_bytes);
+  uint32_t* tile_dw = reinterpret_cast<uint32_t*>(t.codes + tok_row(sh, b, h, t_begin) * t.row_bytes);
   if (t.quant == KVQ_QUANT_CODEBOOK) {
     // pair tiles: byte 32 l + tau = code(tau, l) | code(tau, l + 64) << 4
     for (int W = threadIdx.x; W < 512; W += 256) {
@@ -343,10 +342,10 @@ __global__ __launch_bounds__(256) void enc_kchan_flush_kernel(DevShape sh, DevTe
   }
   __syncthreads();
   const int dw_per_row = 4 * t.bits;
-  uint8_t* rows = t.codes + ((int64_t)bh * sh.Tcap + p0) * t.row_bytes;
   for (int idx = tid; idx < G * dw_per_row; idx += 256) {
     const int k = idx / dw_per_row, W = idx % dw_per_row;
-    reinterpret_cast<uint32_t*>(rows + (int64_t)k * t.row_bytes)[W] =
+    // a group spans G / 32 tiles, each on its own page in a paged cache
+    reinterpret_cast<uint32_t*>(t.codes + tok_row(sh, b, h, p0 + k) * t.row_bytes)[W] =
         k_row_dword(gcodes + k * kD, t.bits, W);
   }
   // The tail's tokens are now quantized: clear the slots they used.
@@ -452,7 +451,7 @@ __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTenso
   __syncthreads();
   uint32_t pos = incl - mine;
   for (int w = 0; w < wave; ++w) pos += wsum[w];
-  const int64_t r = (int64_t)b * sh.Tcap + tpos;
+  const int64_t r = csr_row(sh, b, tpos);
   for (int i = i0; i < i1; ++i) {
     if (keys[i] >= prefix) {
       // column h*d + c in bits 0-11, the replaced dense index in bits 12-15
@@ -464,8 +463,11 @@ __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTenso
     }
   }
   if (tid == 0) {
+    // both ends of the row (every row pointer is k times its index, so
+    // neighbouring tokens write equal values; in a paged cache the next
+    // row may be the first of another page)
+    t.row_ptr[r] = (int32_t)(k * r);
     t.row_ptr[r + 1] = (int32_t)(k * (r + 1));
-    if (tn == 0) t.row_ptr[r] = (int32_t)(k * r);
   }
 }
 

@@ -123,13 +123,16 @@ kvq_status check_config(const kvq_config* c) {
   if (c->sink_tokens < 0 || c->sink_tokens > kMaxSink)
     return fail(KVQ_ERR_INVALID_ARGUMENT, "sink_tokens must be in [0, %d] (got %d)", kMaxSink,
                 c->sink_tokens);
+  if (c->page_pool < 0 || c->page_pool > (1 << 26))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "page_pool must be in [0, 2^26] (got %d)", c->page_pool);
   kvq_status st = check_format(c->k, *c, true, "k");
   if (st != KVQ_OK) return st;
   st = check_format(c->v, *c, false, "v");
   if (st != KVQ_OK) return st;
   // the CSR row pointers are int32 offsets k * r over every row r of the
   // capacity (B * Tcap rows): they must not wrap
-  const uint64_t rows = (uint64_t)c->batch * align_up((uint64_t)c->max_ctx, kCapAlign) + 1;
+  const uint64_t rows = (c->page_pool ? (uint64_t)c->page_pool * kTile
+                                      : (uint64_t)c->batch * align_up((uint64_t)c->max_ctx, kCapAlign)) + 1;
   const kvq_tensor_format* fmts[2] = {&c->k, &c->v};
   for (int i = 0; i < 2; ++i) {
     if (fmts[i]->quantizer != KVQ_QUANT_CODEBOOK) continue;
@@ -142,8 +145,10 @@ kvq_status check_config(const kvq_config* c) {
   return KVQ_OK;
 }
 
+// slots: token records per KV head of the per-token arrays (B * Tcap for a
+// contiguous cache, n_pages * kTile for a paged one)
 void fill_tensor(TensorLayout& t, const kvq_tensor_format& f, const kvq_config& c, int64_t Tcap,
-                 uint64_t& off) {
+                 uint64_t slots, uint64_t& off) {
   const uint64_t B = c.batch, H = c.n_kv_heads, d = c.head_dim;
   t.quant = f.quantizer;
   t.bits = f.quantizer == KVQ_QUANT_NONE ? 16 : f.bits;
@@ -159,18 +164,18 @@ void fill_tensor(TensorLayout& t, const kvq_tensor_format& f, const kvq_config& 
     sz = bytes;
     off = align_up(off + bytes, 256);
   };
-  put(t.codes_off, t.codes_bytes, B * H * (uint64_t)Tcap * t.row_bytes);
+  put(t.codes_off, t.codes_bytes, H * slots * t.row_bytes);
   if (t.G) {
     if (t.per_channel)
       put(t.params_off, t.params_bytes, B * H * (uint64_t)(Tcap / t.G) * d * 4);
     else
-      put(t.params_off, t.params_bytes, B * H * (uint64_t)Tcap * t.ng * t.psize);
+      put(t.params_off, t.params_bytes, H * slots * t.ng * t.psize);
   }
   if (t.per_channel) put(t.tail_off, t.tail_bytes, B * H * (uint64_t)t.G * d * 2);
   if (t.k_out) {
-    put(t.rowptr_off, t.rowptr_bytes, (B * (uint64_t)Tcap + 1) * 4);
-    put(t.col_off, t.col_bytes, B * (uint64_t)Tcap * t.k_out * 2);
-    put(t.val_off, t.val_bytes, B * (uint64_t)Tcap * t.k_out * 2);
+    put(t.rowptr_off, t.rowptr_bytes, (slots + 1) * 4);
+    put(t.col_off, t.col_bytes, slots * t.k_out * 2);
+    put(t.val_off, t.val_bytes, slots * t.k_out * 2);
   }
 }
 
@@ -181,9 +186,12 @@ Layout make_layout(const kvq_config& c) {
   // 4 KB granularity (e.g. 66,016 and 66,080 tokens) ran 15 % slower on
   // MI355X than any multiple of 1024 tokens measured.
   L.Tcap = (int64_t)align_up((uint64_t)c.max_ctx, kCapAlign);
+  L.n_pages = c.page_pool;
+  L.pages_per_seq = c.page_pool ? (int)((c.max_ctx + kTile - 1) / kTile) : 0;
+  const uint64_t slots = c.page_pool ? (uint64_t)c.page_pool * kTile : (uint64_t)c.batch * L.Tcap;
   uint64_t off = 0;
-  fill_tensor(L.k, c.k, c, L.Tcap, off);
-  fill_tensor(L.v, c.v, c, L.Tcap, off);
+  fill_tensor(L.k, c.k, c, L.Tcap, slots, off);
+  fill_tensor(L.v, c.v, c, L.Tcap, slots, off);
   L.sink = c.sink_tokens;
   if (L.sink) {
     const uint64_t sb = (uint64_t)c.batch * c.n_kv_heads * L.sink * c.head_dim * 2;
@@ -246,7 +254,18 @@ kvq_status check_codebooks(const kvq_config& c, const kvq_cache& cache) {
   if ((cache.k_scale && (reinterpret_cast<uintptr_t>(cache.k_scale) & 3u)) ||
       (cache.v_scale && (reinterpret_cast<uintptr_t>(cache.v_scale) & 3u)))
     return fail(KVQ_ERR_INVALID_ARGUMENT, "scale pointers must be 4-byte aligned");
+  if ((c.page_pool > 0) != (cache.page_table != nullptr))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "page_table must be given iff page_pool > 0");
+  if (cache.page_table && (reinterpret_cast<uintptr_t>(cache.page_table) & 3u))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "page_table must be 4-byte aligned");
   return KVQ_OK;
+}
+
+// the paged-cache fields of a kernel's shape
+void set_paging(DevShape& sh, const Layout& L, const kvq_cache& cache) {
+  sh.page_table = L.n_pages ? cache.page_table : nullptr;
+  sh.pages_per_seq = L.pages_per_seq;
+  sh.n_pages = L.n_pages;
 }
 
 kvq_status device_status(hipError_t e, const char* what) {
@@ -311,7 +330,7 @@ int32_t kvq_decode_path(const kvq_config* cfg) {
   return ok ? KVQ_PATH_MFMA : KVQ_PATH_VALU;
 }
 
-int32_t kvq_abi_version(void) { return 105; }
+int32_t kvq_abi_version(void) { return 106; }
 
 kvq_status kvq_set_decode_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr))
@@ -354,6 +373,7 @@ kvq_status kvq_cache_layout(const kvq_config* cfg, kvq_layout_info* out) {
   out->total_bytes = L.total;
   out->capacity = L.Tcap;
   out->max_splits = L.S_max;
+  out->pages_per_seq = L.pages_per_seq;
   return KVQ_OK;
 }
 
@@ -378,6 +398,7 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const vo
   Layout L = make_layout(*cfg);
   DevShape sh{cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, cfg->n_q_heads / cfg->n_kv_heads,
               cfg->kv_dtype == KVQ_BF16, L.Tcap};
+  set_paging(sh, L, *cache);
   sh.in_tok = n_new;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // input tokens that fall below the sink length are copied raw; the rest
@@ -445,6 +466,7 @@ kvq_status kvq::decode_attention_impl(const kvq_config* cfg, const kvq_cache* ca
   DecodeArgs a;
   a.sh = DevShape{cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, cfg->n_q_heads / cfg->n_kv_heads,
                   cfg->kv_dtype == KVQ_BF16, L.Tcap};
+  set_paging(a.sh, L, *cache);
   a.k = make_dev_tensor(L.k, cache->base, cache->k_codebook, cache->k_scale);
   a.v = make_dev_tensor(L.v, cache->base, cache->v_codebook, cache->v_scale);
   a.q = q;
@@ -539,6 +561,7 @@ kvq_status kvq::decode_attention_impl(const kvq_config* cfg, const kvq_cache* ca
       (i == 0 ? sa.k : sa.v) = raw;
     }
     sa.sh.Tcap = L.sink;
+    sa.sh.page_table = nullptr;   // the sink stays per sequence
     sa.n_ctx = n_sink;
     sa.pos0 = 0;
     sa.slot0 = a.splits;
@@ -641,6 +664,7 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
   Layout L = make_layout(*cfg);
   PrefillArgs a;
   a.sh = DevShape{cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, g, cfg->kv_dtype == KVQ_BF16, L.Tcap};
+  set_paging(a.sh, L, *cache);
   a.k = make_dev_tensor(L.k, cache->base, cache->k_codebook, cache->k_scale);
   a.v = make_dev_tensor(L.v, cache->base, cache->v_codebook, cache->v_scale);
   uint8_t* base = static_cast<uint8_t*>(cache->base);

@@ -38,6 +38,8 @@ struct TensorLayout {
 struct Layout {
   TensorLayout k, v;
   int64_t Tcap = 0;          // token capacity per sequence (multiple of 32)
+  int n_pages = 0;           // paged cache: physical pages of kTile tokens (0: contiguous)
+  int pages_per_seq = 0;     // paged cache: page-table entries per sequence
   int sink = 0;              // attention-sink tokens kept raw per sequence
   int S_max = 1;             // partial slots per (b, query head)
   uint64_t partial_off = 0;  // float [B][Hq][S_max][d + 2]
@@ -64,6 +66,12 @@ struct DevShape {
   // appends: the input holds in_tok tokens per sequence; the call encodes
   // input tokens [in_off, in_off + n_new)
   int64_t in_tok = 0, in_off = 0;
+  // paged cache: physical page (kTile tokens of every KV head) of logical
+  // page i of sequence b is page_table[b * pages_per_seq + i]; null for a
+  // contiguous cache
+  const int32_t* page_table = nullptr;
+  int pages_per_seq = 0;
+  int n_pages = 0;
 };
 
 DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebook,

@@ -254,11 +254,11 @@ __device__ __forceinline__ void value_values(int kind, const Raw& R, int c, int 
 // fp32 stage (RoPE follows), values to the fp16 planes.
 template <bool KEY>
 __device__ __forceinline__ void stage_outliers(const DevTensor& ten, PreLds& S, int tid, int b,
-                                               int h, int64_t tq0, int n_valid, int64_t Tcap) {
+                                               int h, int64_t tq0, int n_valid, const DevShape& sh) {
   const int ko = ten.k_out;
   for (int idx = tid; idx < n_valid * ko; idx += 256) {
     const int tk = idx / ko;
-    const int64_t rr = (int64_t)b * Tcap + tq0 + tk;
+    const int64_t rr = csr_row(sh, b, tq0 + tk);
     const int e = ten.row_ptr[rr] + idx % ko;
     if (e >= ten.row_ptr[rr + 1]) continue;
     const int cc = (ten.col[e] & 0xfff) - h * kD;
@@ -393,18 +393,21 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
   auto fetch = [&](int blk, Raw& R) {
     if (blk >= n_blk) return;
     const Desc d = desc(blk);
+    // row of the quantized block's first token (its 32 tokens are
+    // consecutive rows, one page of a paged cache)
+    const int64_t qrow0 = d.sinkb ? 0 : tok_row(a.sh, b, h, d.tq0);
     if (ktk < d.n_valid) {
       const int64_t tq = d.tq0 + ktk;
       if (d.sinkb || kraw || (kpc && tq >= n_full)) {
         const uint16_t* row =
             d.sinkb ? a.k_sink + (sink_row0 + d.t0 + ktk) * kD
-            : kraw  ? reinterpret_cast<const uint16_t*>(a.k.codes) + ((int64_t)bh * Tcap + tq) * kD
+            : kraw  ? reinterpret_cast<const uint16_t*>(a.k.codes) + (qrow0 + ktk) * kD
                     : a.k.tail + ((int64_t)bh * a.k.G + (tq - n_full)) * kD;
         R.kq[0] = *reinterpret_cast<const uint4*>(row + 32 * kmp + 8 * ksq);
         R.kq[1] = *reinterpret_cast<const uint4*>(row + 64 + 32 * kmp + 8 * ksq);
       } else {
         const int bits = kbits;
-        const uint8_t* seg = a.k.codes + ((int64_t)bh * Tcap + tq) * a.k.row_bytes + ksq * 4 * bits;
+        const uint8_t* seg = a.k.codes + (qrow0 + ktk) * a.k.row_bytes + ksq * 4 * bits;
         const uint32_t* w = reinterpret_cast<const uint32_t*>(seg);
         if (bits == 4) {
           R.kc[0] = w[kmp];
@@ -422,11 +425,11 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
               static_cast<const uint32_t*>(a.k.params) + ((int64_t)bh * (Tcap / a.k.G) + tq / a.k.G) * kD + c0);
           R.kq[0] = pp[0]; R.kq[1] = pp[1]; R.kq[2] = pp[16]; R.kq[3] = pp[17];
         } else if (kkind == KVQ_QUANT_SYM_Q8_0) {
-          const uint16_t* pp = static_cast<const uint16_t*>(a.k.params) + ((int64_t)bh * Tcap + tq) * a.k.ng;
+          const uint16_t* pp = static_cast<const uint16_t*>(a.k.params) + (qrow0 + ktk) * a.k.ng;
           R.kpz[0] = pp[c0 / a.k.G];
           R.kpz[1] = pp[(c0 + 64) / a.k.G];
         } else if (kkind != KVQ_QUANT_CODEBOOK && kkind != KVQ_QUANT_FP8_E5M2) {
-          const uint32_t* pp = static_cast<const uint32_t*>(a.k.params) + ((int64_t)bh * Tcap + tq) * a.k.ng;
+          const uint32_t* pp = static_cast<const uint32_t*>(a.k.params) + (qrow0 + ktk) * a.k.ng;
           R.kpz[0] = pp[c0 / a.k.G];
           R.kpz[1] = pp[(c0 + 64) / a.k.G];
         }
@@ -438,11 +441,11 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
         const int tk = 16 * vhv + u;
         const uint16_t* row =
             d.sinkb ? a.v_sink + (sink_row0 + d.t0 + tk) * kD
-                    : reinterpret_cast<const uint16_t*>(a.v.codes) + ((int64_t)bh * Tcap + d.tq0 + tk) * kD;
+                    : reinterpret_cast<const uint16_t*>(a.v.codes) + (qrow0 + tk) * kD;
         R.vp[u] = tk < d.n_valid ? row[vch] : 0u;
       }
     } else {
-      const uint8_t* tile = a.v.codes + ((int64_t)bh * Tcap + d.tq0) * a.v.row_bytes;
+      const uint8_t* tile = a.v.codes + qrow0 * a.v.row_bytes;
       if (vkind == KVQ_QUANT_CODEBOOK) {
         // pair tiles: byte 32 l + tau holds channels l (low nibble) and l + 64
         const uint4 w = *reinterpret_cast<const uint4*>(tile + 32 * (vch & 63) + 16 * vhv);
@@ -467,12 +470,12 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
           const uint16_t* pp = static_cast<const uint16_t*>(a.v.params);
 #pragma unroll
           for (int u = 0; u < 16; ++u)
-            R.vp[u] = pp[((int64_t)bh * Tcap + d.tq0 + 16 * vhv + u) * a.v.ng + vch / a.v.G];
+            R.vp[u] = pp[(qrow0 + 16 * vhv + u) * a.v.ng + vch / a.v.G];
         } else if (vkind != KVQ_QUANT_FP8_E5M2) {
           const uint32_t* pp = static_cast<const uint32_t*>(a.v.params);
 #pragma unroll
           for (int u = 0; u < 16; ++u)
-            R.vp[u] = pp[((int64_t)bh * Tcap + d.tq0 + 16 * vhv + u) * a.v.ng + vch / a.v.G];
+            R.vp[u] = pp[(qrow0 + 16 * vhv + u) * a.v.ng + vch / a.v.G];
         }
       }
     }
@@ -582,8 +585,8 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
     // ---- outliers replace their dense value ------------------------------------
     if (!sinkb && (a.k.k_out > 0 || a.v.k_out > 0)) {
       __syncthreads();
-      if (a.k.k_out > 0) stage_outliers<true>(a.k, S, tid, b, h, tq0, n_valid, Tcap);
-      if (a.v.k_out > 0) stage_outliers<false>(a.v, S, tid, b, h, tq0, n_valid, Tcap);
+      if (a.k.k_out > 0) stage_outliers<true>(a.k, S, tid, b, h, tq0, n_valid, a.sh);
+      if (a.v.k_out > 0) stage_outliers<false>(a.v, S, tid, b, h, tq0, n_valid, a.sh);
     }
     if (kstage) {
       // RoPE at the key's position, then fp16 planes (token ktk, pairs (i, i + 64)

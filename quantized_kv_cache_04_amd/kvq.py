@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvq.h")
 # interface version the structures below follow (major * 100 + minor)
-ABI_VERSION = 105
+ABI_VERSION = 106
 
 # ---- constants mirrored from kvq.h -------------------------------------------
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_DEVICE = 0, -1, -2, -3, -4
@@ -41,13 +41,15 @@ class Config(ctypes.Structure):
                 ("max_ctx", ctypes.c_int64), ("kv_dtype", ctypes.c_int32),
                 ("rope", ctypes.c_int32), ("rope_base", ctypes.c_float),
                 ("decode_splits", ctypes.c_int32), ("decode_path", ctypes.c_int32),
-                ("k", TensorFormat), ("v", TensorFormat), ("sink_tokens", ctypes.c_int32)]
+                ("k", TensorFormat), ("v", TensorFormat), ("sink_tokens", ctypes.c_int32),
+                ("page_pool", ctypes.c_int32)]
 
 
 class CacheStruct(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("k_codebook", ctypes.c_void_p),
                 ("v_codebook", ctypes.c_void_p), ("n_ctx", ctypes.c_int64),
-                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p)]
 
 
 class Region(ctypes.Structure):
@@ -62,7 +64,7 @@ class TensorRegions(ctypes.Structure):
 class LayoutInfo(ctypes.Structure):
     _fields_ = [("k", TensorRegions), ("v", TensorRegions), ("workspace", Region),
                 ("total_bytes", ctypes.c_uint64), ("capacity", ctypes.c_int64),
-                ("max_splits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("max_splits", ctypes.c_int32), ("pages_per_seq", ctypes.c_int32)]
 
 
 class KvqError(RuntimeError):
@@ -135,20 +137,22 @@ def fmt_struct(f: Dict[str, Any]) -> TensorFormat:
 def make_config(*, batch: int, n_q_heads: int, n_kv_heads: int, max_ctx: int,
                 kv_dtype: str, k: Dict[str, Any], v: Dict[str, Any], head_dim: int = 128,
                 rope: bool = False, rope_base: float = 10000.0, decode_splits: int = 0,
-                decode_path: str = "auto", sink_tokens: int = 0) -> Config:
+                decode_path: str = "auto", sink_tokens: int = 0, page_pool: int = 0) -> Config:
     return Config(batch, n_q_heads, n_kv_heads, head_dim, max_ctx, DTYPES[kv_dtype],
                   int(bool(rope)), float(rope_base), int(decode_splits), PATHS[decode_path],
-                  fmt_struct(k), fmt_struct(v), int(sink_tokens))
+                  fmt_struct(k), fmt_struct(v), int(sink_tokens), int(page_pool))
 
 
 def config_from_workload(w, max_ctx: Optional[int] = None, decode_splits: int = 0,
-                         decode_path: str = "auto", sink_tokens: Optional[int] = None) -> Config:
+                         decode_path: str = "auto", sink_tokens: Optional[int] = None,
+                         page_pool: int = 0) -> Config:
     return make_config(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
                        max_ctx=max_ctx if max_ctx is not None else w.ctx, kv_dtype=w.kv_dtype,
                        k=w.k, v=w.v, head_dim=w.head_dim, rope=w.rope, rope_base=w.rope_base,
                        decode_splits=decode_splits, decode_path=decode_path,
                        sink_tokens=(sink_tokens if sink_tokens is not None
-                                    else getattr(w, "sink_tokens", 0)))
+                                    else getattr(w, "sink_tokens", 0)),
+                       page_pool=page_pool)
 
 
 def cache_bytes(cfg: Config, n_ctx: int = 0, n_layers: int = 1, what: int = BYTES_PAYLOAD) -> int:
@@ -235,11 +239,12 @@ def _stream_ptr(stream) -> Optional[int]:
 class Cache:
     """A cache allocation (zero-filled torch uint8 device buffer) plus the
     host-side token count.  Codebooks, when used, are fp16 [Hkv, d, 16]
-    device tensors, FP8 scales float32 [Hkv] device tensors; both must
+    device tensors, FP8 scales float32 [Hkv] device tensors, the page table
+    of a paged cache an int32 [B, pages_per_seq] device tensor; all must
     outlive the cache."""
 
     def __init__(self, cfg: Config, device="cuda", k_codebook=None, v_codebook=None,
-                 k_scale=None, v_scale=None):
+                 k_scale=None, v_scale=None, page_table=None):
         import torch
         self.cfg = cfg
         self.layout = cache_layout(cfg)
@@ -248,12 +253,23 @@ class Cache:
         self.v_codebook = v_codebook.contiguous() if v_codebook is not None else None
         self.k_scale = k_scale.contiguous() if k_scale is not None else None
         self.v_scale = v_scale.contiguous() if v_scale is not None else None
+        self.page_table = None
+        if cfg.page_pool:
+            import torch
+            if page_table is None:
+                raise ValueError("a paged cache (page_pool > 0) needs a page_table")
+            _check_tensor("page_table", page_table, (cfg.batch, self.layout.pages_per_seq),
+                          torch.int32, device=False)
+            self.page_table = page_table
+        elif page_table is not None:
+            raise ValueError("page_table given for a contiguous cache (page_pool = 0)")
         self.n_ctx = 0
 
     def struct(self) -> CacheStruct:
         ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
         return CacheStruct(self.buffer.data_ptr(), ptr(self.k_codebook), ptr(self.v_codebook),
-                           self.n_ctx, ptr(self.k_scale), ptr(self.v_scale))
+                           self.n_ctx, ptr(self.k_scale), ptr(self.v_scale),
+                           ptr(self.page_table))
 
     def region(self, tensor: str, name: str):
         """uint8 view of one array of the allocation (e.g. ("k", "codes"))."""

@@ -6,4 +6,4 @@ arithmetic: both the HIP library's tests and the CPU oracle take their inputs
 from here, and nothing else is shared between them.
 """
 from .workloads import (CONFIGS, Workload, make_workload, make_inputs, config_for,  # noqa: F401
-                        make_prefill_queries)
+                        make_prefill_queries, make_page_table)

@@ -62,7 +62,7 @@ CONFIGS: Dict[int, Dict[str, Any]] = {
 }
 
 _STREAMS = {"k": 0, "v": 1, "q": 2, "mask": 3, "kcb": 4, "vcb": 5, "step_k": 6, "step_v": 7,
-            "step_q": 8, "prefill_q": 9, "kscale": 10, "vscale": 11}
+            "step_q": 8, "prefill_q": 9, "kscale": 10, "vscale": 11, "pages": 12}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -209,3 +209,17 @@ def make_prefill_queries(w: Workload, n_q: int, device: str = "cpu") -> torch.Te
     q = torch.randn((w.batch, n_q, w.n_q_heads, w.head_dim), generator=_gen(w, "prefill_q", device),
                     device=device, dtype=torch.float32)
     return q.to(w.torch_dtype).contiguous()
+
+
+def make_page_table(w: Workload, max_ctx: int, n_pages: int, device: str = "cpu") -> torch.Tensor:
+    """Page table of a paged cache: int32 [B, ceil(max_ctx / 32)], a seeded
+    shuffle of the physical pages [0, n_pages) dealt out to the sequences'
+    logical pages, so that neighbouring logical pages land on scattered,
+    non-contiguous physical pages (with unused pages in between when
+    n_pages exceeds what the sequences need)."""
+    per_seq = (max_ctx + 31) // 32
+    if n_pages < w.batch * per_seq:
+        raise ValueError(f"{n_pages} pages cannot hold {w.batch} x {per_seq}")
+    g = _gen(w, "pages", "cpu")
+    perm = torch.randperm(n_pages, generator=g)
+    return perm[:w.batch * per_seq].reshape(w.batch, per_seq).to(torch.int32).to(device)

@@ -14,6 +14,7 @@ import torch
 
 from oracle import attention as oatt
 from oracle import layout as olay
+from oracle import paging as opag
 from oracle import quant as oq
 from quantized_kv_cache_04_amd import kvq
 
@@ -26,12 +27,13 @@ def to_np32(t: torch.Tensor) -> np.ndarray:
 
 
 def oracle_encode(w, inputs: Dict[str, Optional[torch.Tensor]], n_ctx: int, max_ctx: int,
-                  sink: int = 0):
+                  sink: int = 0, page_table=None, n_pages: int = 0):
     """Oracle encode of the first n_ctx tokens -> (expected regions per tensor, deq K, deq V).
 
     With an attention sink of ``sink`` tokens the first min(sink, n_ctx)
     tokens are expected raw in the "sink" region and the rest as a quantized
-    cache of their own."""
+    cache of their own.  With a page table (paged cache of ``n_pages``
+    pages) the per-token regions are expected on the pages."""
     res = {}
     deq = {}
     for name in ("k", "v"):
@@ -53,6 +55,12 @@ def oracle_encode(w, inputs: Dict[str, Optional[torch.Tensor]], n_ctx: int, max_
             exp = olay.expected_regions(fmt, enc, batch=w.batch, n_kv_heads=w.n_kv_heads,
                                         n_ctx=n_q, max_ctx=max_ctx, kv_dtype=w.kv_dtype,
                                         is_key=(name == "k"))
+            if page_table is not None:
+                exp = opag.paged_regions(exp, np.asarray(page_table), n_pages=n_pages,
+                                         n_ctx=n_q, capacity=olay.capacity(max_ctx),
+                                         per_channel=fmt.get("layout") == "per_channel",
+                                         k_out=oq.outlier_count(fmt.get("outlier_frac", 0.0),
+                                                                w.n_kv_heads * w.head_dim))
         if sink:
             exp["sink"] = olay.sink_region(x, sink, kv_dtype=w.kv_dtype)
         res[name] = exp or None
@@ -60,14 +68,17 @@ def oracle_encode(w, inputs: Dict[str, Optional[torch.Tensor]], n_ctx: int, max_
 
 
 def gpu_cache(w, inputs, chunks: Sequence[int], max_ctx: int, decode_splits: int = 0,
-              decode_path: str = "auto", device: str = "cuda", sink: int = 0) -> kvq.Cache:
-    """Build the cache on the GPU by appending the inputs in ``chunks`` token counts."""
+              decode_path: str = "auto", device: str = "cuda", sink: int = 0,
+              page_table=None, n_pages: int = 0) -> kvq.Cache:
+    """Build the cache on the GPU by appending the inputs in ``chunks`` token
+    counts (a paged cache of ``n_pages`` pages when ``page_table`` is given)."""
     cfg = kvq.config_from_workload(w, max_ctx=max_ctx, decode_splits=decode_splits,
-                                   decode_path=decode_path, sink_tokens=sink)
+                                   decode_path=decode_path, sink_tokens=sink,
+                                   page_pool=n_pages if page_table is not None else 0)
     dev = lambda t: t.to(device) if t is not None else None  # noqa: E731
     cache = kvq.Cache(cfg, device=device, k_codebook=dev(inputs["k_codebook"]),
                       v_codebook=dev(inputs["v_codebook"]), k_scale=dev(inputs.get("k_scale")),
-                      v_scale=dev(inputs.get("v_scale")))
+                      v_scale=dev(inputs.get("v_scale")), page_table=dev(page_table))
     kd = inputs["k"].to(device)
     vd = inputs["v"].to(device)
     t = 0

@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
                           "kvq_decode_attention", "kvq_last_error", "kvq_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvq_abi_version() == kvq.ABI_VERSION == 105
+    assert L.kvq_abi_version() == kvq.ABI_VERSION == 106
 
 
 def _none_cfg(**kw):
@@ -327,3 +327,38 @@ def test_outlier_row_pointers_must_not_wrap():
     assert "row pointers" in str(e.value)
     fits = kvq.make_config(batch=49, max_ctx=1 << 20, **base)      # 51,380,224 rows
     assert kvq.cache_bytes(fits, 0, 1, kvq.BYTES_ALLOC) > 0
+
+
+def test_paged_layout_and_table_checks():
+    u4 = {"quantizer": "asym_minmax", "bits": 4, "group_size": 128, "layout": "per_token"}
+    pc = {"quantizer": "asym_minmax", "bits": 4, "group_size": 128, "layout": "per_channel"}
+    cfg = kvq.make_config(batch=3, n_q_heads=8, n_kv_heads=2, max_ctx=100, kv_dtype="f16",
+                          k=pc, v=u4, page_pool=17)
+    li = kvq.cache_layout(cfg)
+    assert li.pages_per_seq == 4                       # ceil(100 / 32)
+    # per-token arrays hold pages x heads x 32 token rows
+    assert li.k.codes.bytes == 17 * 2 * 32 * 64
+    assert li.v.codes.bytes == 17 * 2 * 32 * 64
+    assert li.v.params.bytes == 17 * 2 * 32 * 1 * 4
+    # per-channel key params and the tail stay per sequence (capacity 1024)
+    assert li.k.params.bytes == 3 * 2 * (1024 // 128) * 128 * 4
+    assert li.k.tail.bytes == 3 * 2 * 128 * 128 * 2
+    # the payload (bytes a decode reads) does not depend on paging
+    flat = kvq.make_config(batch=3, n_q_heads=8, n_kv_heads=2, max_ctx=100, kv_dtype="f16",
+                           k=pc, v=u4)
+    assert kvq.cache_bytes(cfg, 77) == kvq.cache_bytes(flat, 77)
+    # a table is required exactly when the cache is paged
+    L = kvq.lib()
+    q = ctypes.c_void_p(FAKE)
+    cs = kvq.CacheStruct(FAKE, None, None, 5, None, None, None)
+    assert L.kvq_decode_attention(ctypes.byref(cfg), ctypes.byref(cs), q, None, 0.0, q,
+                                  kvq.F32, None) == kvq.ERR_INVALID_ARGUMENT
+    assert "page_table" in L.kvq_last_error().decode()
+    cs = kvq.CacheStruct(FAKE, None, None, 5, None, None, FAKE)
+    assert L.kvq_decode_attention(ctypes.byref(flat), ctypes.byref(cs), q, None, 0.0, q,
+                                  kvq.F32, None) == kvq.ERR_INVALID_ARGUMENT
+    assert "page_table" in L.kvq_last_error().decode()
+    bad = kvq.make_config(batch=1, n_q_heads=1, n_kv_heads=1, max_ctx=64, kv_dtype="f16",
+                          k=u4, v=u4, page_pool=-1)
+    with pytest.raises(kvq.KvqError):
+        kvq.cache_layout(bad)

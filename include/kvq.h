@@ -128,6 +128,25 @@ typedef struct kvq_tensor_format {
   int32_t group_size;     /* see the layouts; ignored by NONE and CODEBOOK   */
   int32_t layout;         /* KVQ_LAYOUT_*                                    */
   float   outlier_frac;   /* CODEBOOK only: 0 or a fraction in (0, 0.25]     */
+  int32_t window_overlap; /* PER_CHANNEL keys with ASYM_MINMAX or
+                             ASYM_ABSMAX_OFFSET: the scale and zero of the
+                             group of tokens [g G, g G + G) come from the
+                             window [g G - window_overlap, g G + G) (clipped
+                             at the first quantized token): sliding windows
+                             that advance by G and overlap by window_overlap
+                             tokens [TurboQuant page 3.1: parameters from a
+                             sliding window's extrema; 6, problem 1: a window
+                             overlap of 64 tokens].  0 (none) or a multiple
+                             of 32 up to 256; 0 for every other format.  The
+                             key tail then keeps G + window_overlap rows.    */
+  const int32_t* head_group_size; /* PER_TOKEN layouts of ASYM_MINMAX,
+                             ASYM_ABSMAX_OFFSET or SYM_Q8_0: NULL (every KV
+                             head uses group_size), or a host array of
+                             n_kv_heads group sizes in {32, 64, 128}, one per
+                             KV head [Memory-killer page 2.3 and 5.3: finer
+                             groups for the heads that are sensitive to
+                             quantization, coarser ones for stable heads].
+                             Read during each call only; at most 64 KV heads. */
 } kvq_tensor_format;
 
 typedef struct kvq_config {
@@ -417,7 +436,8 @@ const char* kvq_last_error(void);
    scale pointers; 104 gives kvq_prefill_attention a workspace and adds
    kvq_prefill_workspace_bytes; 105 adds kvq_decode_attention_scratch;
    106 adds the paged cache (kvq_config.page_pool, kvq_cache.page_table,
-   kvq_layout_info.pages_per_seq). */
+   kvq_layout_info.pages_per_seq); 107 adds kvq_tensor_format.window_overlap
+   and head_group_size. */
 int32_t kvq_abi_version(void);
 
 #ifdef __cplusplus

@@ -222,10 +222,8 @@ def expected_regions(fmt: Dict, enc: Dict[str, np.ndarray], *, batch: int, n_kv_
             ng = enc["scale"].shape[2]
             p[:, :, :ng, :, 0] = enc["scale"]
             p[:, :, :ng, :, 1] = enc["zero"]
-            tail = np.zeros((B, H, G, D), dtype=np.uint16)
-            t = enc["tail"]
-            tail[:, :, :t.shape[2], :] = to_bits(t, kv_dtype)
-            out["tail"] = tail
+            out["tail"] = tail_ring(enc["tail_rows"], G, int(fmt.get("window_overlap", 0)),
+                                    n_ctx, kv_dtype)
         out["params"] = p
     elif q == "sym_q8_0":
         p = np.zeros((B, H, Tcap, D // G), dtype=np.float16)
@@ -250,6 +248,24 @@ def expected_regions(fmt: Dict, enc: Dict[str, np.ndarray], *, batch: int, n_kv_
         out["row_ptr"] = row_ptr.astype(np.int32)
         out["col"] = col
         out["val"] = val
+    return out
+
+
+def tail_ring(raw: np.ndarray, G: int, overlap: int, n_ctx: int, kv_dtype: str) -> np.ndarray:
+    """Byte image [B, H, G + overlap, d] of the unquantized key tail of a
+    per-channel key cache after n_ctx tokens: a ring of G + overlap rows in
+    which token p sits at row p mod (G + overlap).  It holds the tokens of
+    the unfinished group [n_full, n_ctx), n_full = floor(n_ctx / G) * G, and
+    the ``overlap`` tokens before n_full that the next group's window reads
+    (``raw`` [B, H, n_ctx, d]: every token's float32 value); other rows are
+    zero.  Without overlap, row i holds token n_full + i."""
+    raw = np.asarray(raw, dtype=np.float32)
+    B, H = raw.shape[:2]
+    R = G + overlap
+    n_full = (n_ctx // G) * G
+    out = np.zeros((B, H, R, D), dtype=np.uint16)
+    for p in range(max(0, n_full - overlap), n_ctx):
+        out[:, :, p % R, :] = to_bits(raw[:, :, p, :], kv_dtype)
     return out
 
 

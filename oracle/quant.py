@@ -175,7 +175,10 @@ def encode_tensor(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None,
     * ``tail`` float32 [B, H, T - Tq, d]: per-channel keys of the unfinished
       group stay unquantized (reading: the pages quantize only complete
       groups of appended rows -- NIAH page section 1.1, KVQuant page
-      section 3.4 -- and say nothing of partial groups),
+      section 3.4 -- and say nothing of partial groups); ``tail_rows`` is
+      every token's raw value, from which the tail's byte image is drawn,
+    * per-channel groups with ``window_overlap`` > 0 take their scale and
+      zero from a window reaching that many tokens back (``_windowed_groups``),
     * ``cols``/``vals`` for codebook outliers ([B, T, k]),
     * ``deq`` float64 [B, H, T, d]: the values attention sees.
 
@@ -253,24 +256,72 @@ def encode_tensor(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None,
         # Per-channel keys, groups of G consecutive tokens (KVQuant page,
         # section 2.2; Survey page, section 2.4's per-position groups).
         nq = (T // G) * G
-        g = xt[:, :, :nq, :].reshape(B, H, T // G, G, d)
-        g = np.swapaxes(g, -1, -2)                      # [B, H, ng, d, G]
-        if q == "asym_minmax":
-            c, s, z = asym_minmax(g, bits)
-        elif q == "asym_absmax_offset":
-            c, s, z = asym_absmax_offset(g, bits)
+        overlap = int(fmt.get("window_overlap", 0))
+        if overlap:
+            c, s, z = _windowed_groups(xt[:, :, :nq, :], q, bits, G, overlap)
         else:
-            raise ValueError(f"{q} has no per-channel form")
+            g = xt[:, :, :nq, :].reshape(B, H, T // G, G, d)
+            g = np.swapaxes(g, -1, -2)                      # [B, H, ng, d, G]
+            if q == "asym_minmax":
+                c, s, z = asym_minmax(g, bits)
+            elif q == "asym_absmax_offset":
+                c, s, z = asym_absmax_offset(g, bits)
+            else:
+                raise ValueError(f"{q} has no per-channel form")
         deq_q = c.astype(np.float64) * s.astype(np.float64)[..., None] + z.astype(np.float64)[..., None]
         out["codes"] = np.swapaxes(c, -1, -2).reshape(B, H, nq, d)
         out["scale"] = s                                  # [B, H, ng, d]
         out["zero"] = z
         out["tail"] = xt[:, :, nq:, :].copy()
+        out["tail_rows"] = xt.copy()     # the raw tokens the tail ring draws from
         deq = np.concatenate([np.swapaxes(deq_q, -1, -2).reshape(B, H, nq, d),
                               xt[:, :, nq:, :].astype(np.float64)], axis=2)
         out["deq"] = deq
         return out
     raise ValueError(layout)
+
+
+def window_params(win: np.ndarray, quantizer: str, bits: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(scale, zero) fp16 from the statistics of a window (last axis), by the
+    rule of ``quantizer``: min-max (asym_minmax) or the TurboQuant page's
+    absmax / (2^(b-1) - 1) with a min offset (asym_absmax_offset)."""
+    win = np.asarray(win, dtype=F32)
+    lo = win.min(axis=-1)
+    if quantizer == "asym_minmax":
+        s = f16((win.max(axis=-1) - lo) / F32(2 ** bits - 1))
+    elif quantizer == "asym_absmax_offset":
+        s = f16(np.abs(win).max(axis=-1) / F32(2 ** (bits - 1) - 1))
+    else:
+        raise ValueError(f"{quantizer} has no window form")
+    return s, f16(lo)
+
+
+def _windowed_groups(xq: np.ndarray, quantizer: str, bits: int, G: int, overlap: int):
+    """Per-channel token groups whose statistics come from overlapping
+    sliding windows (TurboQuant page, section 3.1: quantization parameters
+    from a sliding window's extrema; section 6, problem 1: a window overlap
+    of 64 tokens against edge effects).
+
+    Reading: the windows advance by G tokens and overlap by ``overlap``:
+    window g spans tokens [g G - overlap, g G + G) (clipped at token 0), and
+    token t is quantized with the parameters of the window whose last G
+    tokens hold it, g = t // G.  Looking back rather than ahead lets a group
+    be encoded as soon as its own tokens are in, as an append-only cache
+    needs.  ``xq`` [B, H, ng * G, d]; returns codes [B, H, ng, d, G] and
+    scale, zero [B, H, ng, d]."""
+    B, H, nq, d = xq.shape
+    ng = nq // G
+    codes = np.zeros((B, H, ng, d, G), dtype=np.int32)
+    scale = np.zeros((B, H, ng, d), dtype=np.float16)
+    zero = np.zeros((B, H, ng, d), dtype=np.float16)
+    for g in range(ng):
+        win = np.swapaxes(xq[:, :, max(0, g * G - overlap):(g + 1) * G, :], -1, -2)  # [B, H, d, W]
+        core = np.swapaxes(xq[:, :, g * G:(g + 1) * G, :], -1, -2)                   # [B, H, d, G]
+        s, z = window_params(win, quantizer, bits)
+        codes[:, :, g] = _div_codes(core - z.astype(F32)[..., None], s[..., None], 0, 2 ** bits - 1)
+        scale[:, :, g] = s
+        zero[:, :, g] = z
+    return codes, scale, zero
 
 
 def encode_with_sink(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None,

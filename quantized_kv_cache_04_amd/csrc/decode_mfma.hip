@@ -984,7 +984,8 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   if constexpr (KCH) {
     for (int blk = qend + wave; blk < blk1; blk += 4) {   // shared out over the waves
       const int t0 = blk * kTile;
-      const uint16_t* tail = K.tail + ((int64_t)bh * Gk + (t0 - n_full)) * kD;
+      // 32 consecutive rows of the tail ring (its size is a multiple of 32)
+      const uint16_t* tail = K.tail + ((int64_t)bh * K.tail_rows + t0 % K.tail_rows) * kD;
       half8 bt[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {

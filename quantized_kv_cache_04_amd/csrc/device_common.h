@@ -183,7 +183,7 @@ __device__ inline float deq_key(const DevTensor& k, const DevShape& sh, int bh, 
   if (k.quant == KVQ_QUANT_NONE)
     return elem2f(reinterpret_cast<const uint16_t*>(k.codes)[row * kHeadDim + c], sh.kv_bf16);
   if (k.per_channel && t >= n_full)
-    return elem2f(k.tail[((int64_t)bh * k.G + (t - n_full)) * kHeadDim + c], sh.kv_bf16);
+    return elem2f(k.tail[((int64_t)bh * k.tail_rows + t % k.tail_rows) * kHeadDim + c], sh.kv_bf16);
   const uint32_t code = k_row_code(k.codes + row * k.row_bytes, k.bits, c);
   if (k.quant == KVQ_QUANT_CODEBOOK) return h2f(k.codebook[((int64_t)h * kHeadDim + c) * 16 + code]);
   if (k.quant == KVQ_QUANT_FP8_E5M2) return e5m2_to_f(code) * fp8_scale(k, h);

@@ -168,11 +168,10 @@ __global__ __launch_bounds__(256) void enc_rows_kernel(DevShape sh, DevTensor t,
 // first block of each (b, h) then also copies those key rows to the tail,
 // which saves the separate tail launch in the one-token serving step.
 struct KeyTail {
-  uint32_t* tail;      // the key tail region, [B*Hkv][G][kD] 16-bit elements
+  uint32_t* tail;      // the key tail ring, [B*Hkv][R][kD] 16-bit elements
   const void* k_new;   // the appended keys
-  int G;               // key group size (tail rows per (b, h))
+  int R;               // ring rows per (b, h): token p sits at row p mod R
   int64_t p_first;     // first token position written to the tail
-  int64_t group_start; // position of tail row 0
   int n_rows;          // tail rows written per (b, h); 0: no keys here
 };
 
@@ -189,7 +188,7 @@ __global__ __launch_bounds__(256) void enc_vtile_kernel(DevShape sh, DevTensor t
       const int64_t p = kt.p_first + idx / (kD / 2);
       const int w = idx % (kD / 2);
       const int64_t rin = ((int64_t)b * sh.in_tok + sh.in_off + (p - n_ctx)) * sh.Hkv + h;
-      kt.tail[((int64_t)bh * kt.G + (p - kt.group_start)) * (kD / 2) + w] =
+      kt.tail[((int64_t)bh * kt.R + p % kt.R) * (kD / 2) + w] =
           static_cast<const uint32_t*>(kt.k_new)[rin * (kD / 2) + w];
     }
   }
@@ -285,13 +284,14 @@ __global__ __launch_bounds__(256) void enc_kchan_flush_kernel(DevShape sh, DevTe
   const int b = bh / sh.Hkv, h = bh % sh.Hkv;
   const int64_t gi = g0 + blockIdx.x;
   const int64_t p0 = gi * G;
-  const uint16_t* tail = t.tail + (int64_t)bh * G * kD;
+  const int R = t.tail_rows;
+  const uint16_t* tail = t.tail + (int64_t)bh * R * kD;   // ring: token p at row p mod R
   for (int idx = tid; idx < G * (kD / 8); idx += 256) {
     const int k = idx / (kD / 8), u = idx % (kD / 8);
     const int64_t p = p0 + k;
     const uint4* src;
     if (p < n_ctx) {
-      src = reinterpret_cast<const uint4*>(tail + (int64_t)k * kD);
+      src = reinterpret_cast<const uint4*>(tail + (p % R) * kD);
     } else {
       const int64_t rin = ((int64_t)b * sh.in_tok + sh.in_off + (p - n_ctx)) * sh.Hkv + h;
       src = reinterpret_cast<const uint4*>(x_new) + rin * (kD / 8);
@@ -304,6 +304,24 @@ __global__ __launch_bounds__(256) void enc_kchan_flush_kernel(DevShape sh, DevTe
   float lo = INFINITY, hi = -INFINITY, am = 0.0f;
   for (int k = k0; k < k1; ++k) {
     const float x = elem2f(raw[k * kD + c], sh.kv_bf16);
+    lo = fminf(lo, x);
+    hi = fmaxf(hi, x);
+    am = fmaxf(am, fabsf(x));
+  }
+  // the window reaches overlap tokens back, into the previous group (never
+  // before token 0): from the tail ring, or from this append's input
+  const int64_t w0 = p0 - t.overlap > 0 ? p0 - t.overlap : 0;
+  const int64_t wn = p0 - w0, wk0 = half * (wn / 2), wk1 = half ? wn : wn / 2;
+  for (int64_t k = wk0; k < wk1; ++k) {
+    const int64_t p = w0 + k;
+    uint16_t e;
+    if (p < n_ctx) {
+      e = tail[(p % R) * kD + c];
+    } else {
+      const int64_t rin = ((int64_t)b * sh.in_tok + sh.in_off + (p - n_ctx)) * sh.Hkv + h;
+      e = static_cast<const uint16_t*>(x_new)[rin * kD + c];
+    }
+    const float x = elem2f(e, sh.kv_bf16);
     lo = fminf(lo, x);
     hi = fmaxf(hi, x);
     am = fmaxf(am, fabsf(x));
@@ -348,25 +366,45 @@ __global__ __launch_bounds__(256) void enc_kchan_flush_kernel(DevShape sh, DevTe
     reinterpret_cast<uint32_t*>(t.codes + tok_row(sh, b, h, p0 + k) * t.row_bytes)[W] =
         k_row_dword(gcodes + k * kD, t.bits, W);
   }
-  // The tail's tokens are now quantized: clear the slots they used.
-  if (p0 < n_ctx) {
-    const int used = (int)(n_ctx - p0);
-    uint16_t* tw = t.tail + (int64_t)bh * G * kD;
-    for (int idx = tid; idx < used * kD; idx += 256) tw[idx] = 0;
+  // (the tail ring is brought up to date by enc_kchan_ring_kernel once
+  // every group of the append is encoded)
+}
+
+// Rewrite the key tail ring after an append that completed groups: row s
+// holds the latest token p < n1 with p = s mod R if p is still needed
+// (p >= live_start: the next window's reach back and the unfinished
+// group), copied from the input when it arrived in this append; other rows
+// are cleared.  One block per (row, b * Hkv + h), a thread per dword.
+__global__ __launch_bounds__(64) void enc_kchan_ring_kernel(DevShape sh, DevTensor t,
+                                                            const void* x_new, int64_t n_ctx,
+                                                            int n_new, int64_t live_start) {
+  const int bh = blockIdx.y;
+  const int b = bh / sh.Hkv, h = bh % sh.Hkv;
+  const int R = t.tail_rows, s = blockIdx.x;
+  const int64_t n1 = n_ctx + n_new;
+  const int64_t back = ((n1 - 1 - s) % R + R) % R;
+  const int64_t p = n1 - 1 - back;               // = s mod R, in [n1 - R, n1)
+  uint32_t* dst = reinterpret_cast<uint32_t*>(t.tail + ((int64_t)bh * R + s) * kD) + threadIdx.x;
+  if (p < 0 || p < live_start) {
+    *dst = 0u;
+  } else if (p >= n_ctx) {
+    const int64_t rin = ((int64_t)b * sh.in_tok + sh.in_off + (p - n_ctx)) * sh.Hkv + h;
+    *dst = static_cast<const uint32_t*>(x_new)[rin * (kD / 2) + threadIdx.x];
   }
 }
 
-// Copy tokens of the unfinished last group into the tail.
+// Copy new tokens of the unfinished last group into the tail ring (an
+// append that completes no group).
 __global__ __launch_bounds__(64) void enc_kchan_tail_kernel(DevShape sh, DevTensor t,
                                                             const void* x_new, int64_t n_ctx,
-                                                            int n_new, int64_t p_first,
-                                                            int64_t group_start) {
+                                                            int n_new, int64_t p_first) {
   const int bh = blockIdx.y;
   const int b = bh / sh.Hkv, h = bh % sh.Hkv;
   const int64_t p = p_first + blockIdx.x;
   const int64_t rin = ((int64_t)b * sh.in_tok + sh.in_off + (p - n_ctx)) * sh.Hkv + h;
   const uint32_t pair = static_cast<const uint32_t*>(x_new)[rin * (kD / 2) + threadIdx.x];
-  uint32_t* dst = reinterpret_cast<uint32_t*>(t.tail + ((int64_t)bh * t.G + (p - group_start)) * kD);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(
+      t.tail + ((int64_t)bh * t.tail_rows + p % t.tail_rows) * kD);
   dst[threadIdx.x] = pair;
 }
 
@@ -486,14 +524,16 @@ hipError_t launch_encode_tensor(const DevShape& sh, const DevTensor& t, bool is_
     const int64_t n1 = n_ctx + n_new;
     const int64_t g_first = n_ctx / G, g_end = n1 / G;   // groups [g_first, g_end) complete now
     if (g_end > g_first) {
+      // encode the completed groups (their windows read the ring as it
+      // was), then bring the ring up to date
       hipLaunchKernelGGL(enc_kchan_flush_kernel, dim3((unsigned)(g_end - g_first), sh.B * sh.Hkv),
                          dim3(256), (size_t)G * kD * 3, stream, sh, t, x_new, n_ctx, n_new, g_first);
-    }
-    const int64_t group_start = g_end * G;
-    const int64_t p_first = n_ctx > group_start ? n_ctx : group_start;
-    if (n1 > p_first) {
-      hipLaunchKernelGGL(enc_kchan_tail_kernel, dim3((unsigned)(n1 - p_first), sh.B * sh.Hkv),
-                         dim3(64), 0, stream, sh, t, x_new, n_ctx, n_new, p_first, group_start);
+      const int64_t live = g_end * G - t.overlap;
+      hipLaunchKernelGGL(enc_kchan_ring_kernel, dim3((unsigned)t.tail_rows, sh.B * sh.Hkv),
+                         dim3(64), 0, stream, sh, t, x_new, n_ctx, n_new, live > 0 ? live : 0);
+    } else {
+      hipLaunchKernelGGL(enc_kchan_tail_kernel, dim3((unsigned)n_new, sh.B * sh.Hkv),
+                         dim3(64), 0, stream, sh, t, x_new, n_ctx, n_new, n_ctx);
     }
   } else {
     const int64_t tile0 = n_ctx / kTile, tile1 = (n_ctx + n_new - 1) / kTile;
@@ -526,8 +566,7 @@ hipError_t launch_encode_kv(const DevShape& sh, const DevTensor& kt, const DevTe
   KeyTail tail;
   tail.tail = reinterpret_cast<uint32_t*>(kt.tail);
   tail.k_new = k_new;
-  tail.G = kt.G;
-  tail.group_start = (n_ctx / kt.G) * kt.G;
+  tail.R = kt.tail_rows;
   tail.p_first = n_ctx;
   tail.n_rows = n_new;
   const int64_t tile0 = n_ctx / kTile, tile1 = (n_ctx + n_new - 1) / kTile;

@@ -46,6 +46,17 @@ kvq_status check_format(const kvq_tensor_format& f, const kvq_config& c, bool is
   const int d = c.head_dim;
   if (f.quantizer != KVQ_QUANT_CODEBOOK && f.outlier_frac != 0.0f)
     return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: outlier_frac is only valid for CODEBOOK", name);
+  if (f.window_overlap != 0) {
+    if (f.layout != KVQ_LAYOUT_PER_CHANNEL ||
+        (f.quantizer != KVQ_QUANT_ASYM_MINMAX && f.quantizer != KVQ_QUANT_ASYM_ABSMAX_OFFSET))
+      return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: window_overlap applies to per-channel keys "
+                  "with ASYM_MINMAX or ASYM_ABSMAX_OFFSET only", name);
+    if (f.window_overlap < 0 || f.window_overlap > 256 || f.window_overlap % kTile)
+      return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: window_overlap must be a multiple of 32 in "
+                  "[0, 256] (got %d)", name, f.window_overlap);
+  }
+  if (f.head_group_size)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: per-head group sizes are not supported", name);
   if (f.layout != KVQ_LAYOUT_PER_TOKEN && f.layout != KVQ_LAYOUT_PER_CHANNEL)
     return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: unknown layout %d", name, f.layout);
   switch (f.quantizer) {
@@ -171,7 +182,8 @@ void fill_tensor(TensorLayout& t, const kvq_tensor_format& f, const kvq_config& 
     else
       put(t.params_off, t.params_bytes, H * slots * t.ng * t.psize);
   }
-  if (t.per_channel) put(t.tail_off, t.tail_bytes, B * H * (uint64_t)t.G * d * 2);
+  t.overlap = t.per_channel ? f.window_overlap : 0;
+  if (t.per_channel) put(t.tail_off, t.tail_bytes, B * H * (uint64_t)(t.G + t.overlap) * d * 2);
   if (t.k_out) {
     put(t.rowptr_off, t.rowptr_bytes, (slots + 1) * 4);
     put(t.col_off, t.col_bytes, slots * t.k_out * 2);
@@ -293,6 +305,8 @@ DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebo
   t.row_bytes = tl.row_bytes;
   t.ng = tl.ng;
   t.k_out = tl.k_out;
+  t.overlap = tl.overlap;
+  t.tail_rows = tl.G + tl.overlap;
   t.codes = b + tl.codes_off;
   t.params = tl.params_bytes ? b + tl.params_off : nullptr;
   t.tail = tl.tail_bytes ? reinterpret_cast<uint16_t*>(b + tl.tail_off) : nullptr;
@@ -330,7 +344,7 @@ int32_t kvq_decode_path(const kvq_config* cfg) {
   return ok ? KVQ_PATH_MFMA : KVQ_PATH_VALU;
 }
 
-int32_t kvq_abi_version(void) { return 106; }
+int32_t kvq_abi_version(void) { return 107; }
 
 kvq_status kvq_set_decode_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr))

@@ -26,6 +26,7 @@ struct TensorLayout {
   int ng = 0;           // groups per token (per-token layouts)
   int psize = 0;        // bytes per group parameter record (4: scale+zero, 2: scale)
   int k_out = 0;        // outliers kept per token (CODEBOOK)
+  int overlap = 0;      // per-channel keys: tokens the statistics window reaches back
   uint64_t codes_off = 0, codes_bytes = 0;
   uint64_t params_off = 0, params_bytes = 0;
   uint64_t tail_off = 0, tail_bytes = 0;
@@ -50,6 +51,10 @@ struct Layout {
 // Device-side view of one tensor, passed by value to kernels.
 struct DevTensor {
   int quant, bits, G, per_channel, row_bytes, ng, k_out;
+  // per-channel keys: the window reaches ``overlap`` tokens back, and the
+  // unquantized tail is a ring of tail_rows = G + overlap rows in which
+  // token t sits at row t mod tail_rows
+  int overlap, tail_rows;
   uint8_t* codes;
   void* params;
   uint16_t* tail;

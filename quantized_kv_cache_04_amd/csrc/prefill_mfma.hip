@@ -402,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
         const uint16_t* row =
             d.sinkb ? a.k_sink + (sink_row0 + d.t0 + ktk) * kD
             : kraw  ? reinterpret_cast<const uint16_t*>(a.k.codes) + (qrow0 + ktk) * kD
-                    : a.k.tail + ((int64_t)bh * a.k.G + (tq - n_full)) * kD;
+                    : a.k.tail + ((int64_t)bh * a.k.tail_rows + tq % a.k.tail_rows) * kD;
         R.kq[0] = *reinterpret_cast<const uint4*>(row + 32 * kmp + 8 * ksq);
         R.kq[1] = *reinterpret_cast<const uint4*>(row + 64 + 32 * kmp + 8 * ksq);
       } else {

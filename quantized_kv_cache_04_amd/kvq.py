@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvq.h")
 # interface version the structures below follow (major * 100 + minor)
-ABI_VERSION = 106
+ABI_VERSION = 107
 
 # ---- constants mirrored from kvq.h -------------------------------------------
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_DEVICE = 0, -1, -2, -3, -4
@@ -32,7 +32,8 @@ DTYPES = {"f16": F16, "bf16": BF16, "f32": F32}
 class TensorFormat(ctypes.Structure):
     _fields_ = [("quantizer", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("layout", ctypes.c_int32),
-                ("outlier_frac", ctypes.c_float)]
+                ("outlier_frac", ctypes.c_float), ("window_overlap", ctypes.c_int32),
+                ("head_group_size", ctypes.POINTER(ctypes.c_int32))]
 
 
 class Config(ctypes.Structure):
@@ -130,17 +131,29 @@ def _check(st: int) -> None:
 
 
 def fmt_struct(f: Dict[str, Any]) -> TensorFormat:
-    return TensorFormat(QUANT[f["quantizer"]], int(f["bits"]), int(f.get("group_size", 0)),
-                        LAYOUT[f.get("layout", "per_token")], float(f.get("outlier_frac", 0.0)))
+    """The C struct of a format dict.  Per-head group sizes
+    (``head_group_size``, a list) go to a host int32 array that the struct
+    keeps alive."""
+    hg = f.get("head_group_size")
+    arr = (ctypes.c_int32 * len(hg))(*[int(v) for v in hg]) if hg else None
+    t = TensorFormat(QUANT[f["quantizer"]], int(f["bits"]), int(f.get("group_size", 0)),
+                     LAYOUT[f.get("layout", "per_token")], float(f.get("outlier_frac", 0.0)),
+                     int(f.get("window_overlap", 0)),
+                     ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)) if arr is not None else None)
+    t._keep = arr
+    return t
 
 
 def make_config(*, batch: int, n_q_heads: int, n_kv_heads: int, max_ctx: int,
                 kv_dtype: str, k: Dict[str, Any], v: Dict[str, Any], head_dim: int = 128,
                 rope: bool = False, rope_base: float = 10000.0, decode_splits: int = 0,
                 decode_path: str = "auto", sink_tokens: int = 0, page_pool: int = 0) -> Config:
-    return Config(batch, n_q_heads, n_kv_heads, head_dim, max_ctx, DTYPES[kv_dtype],
-                  int(bool(rope)), float(rope_base), int(decode_splits), PATHS[decode_path],
-                  fmt_struct(k), fmt_struct(v), int(sink_tokens), int(page_pool))
+    kf, vf = fmt_struct(k), fmt_struct(v)
+    cfg = Config(batch, n_q_heads, n_kv_heads, head_dim, max_ctx, DTYPES[kv_dtype],
+                 int(bool(rope)), float(rope_base), int(decode_splits), PATHS[decode_path],
+                 kf, vf, int(sink_tokens), int(page_pool))
+    cfg._keep = (kf._keep, vf._keep)   # per-head group-size arrays the struct points to
+    return cfg
 
 
 def config_from_workload(w, max_ctx: Optional[int] = None, decode_splits: int = 0,

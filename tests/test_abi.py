@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
                           "kvq_decode_attention", "kvq_last_error", "kvq_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvq_abi_version() == kvq.ABI_VERSION == 106
+    assert L.kvq_abi_version() == kvq.ABI_VERSION == 107
 
 
 def _none_cfg(**kw):

@@ -43,6 +43,9 @@ def tensor_payload(fmt: Dict, *, batch: int, n_kv_heads: int, head_dim: int, n_c
         nf = (n // G) * G
         return B * H * (nf * rb + (nf // G) * d * 4 + (n - nf) * d * ESIZE[kv_dtype])
     psize = 2 if q == "sym_q8_0" else 4
+    if fmt.get("head_group_size"):
+        # a group size per KV head: each head's own groups per token
+        return B * n * (H * rb + sum(d // int(g) for g in fmt["head_group_size"]) * psize)
     return B * H * n * (rb + (d // G) * psize)
 
 

@@ -212,7 +212,9 @@ def expected_regions(fmt: Dict, enc: Dict[str, np.ndarray], *, batch: int, n_kv_
         packed[:, :, c.shape[2]:, :] = 0
     out["codes"] = packed.reshape(B, H, Tcap * rb)
     layout = fmt.get("layout", "per_token")
-    if q in ("asym_minmax", "asym_absmax_offset"):
+    if q in ("asym_minmax", "asym_absmax_offset", "sym_q8_0") and fmt.get("head_group_size"):
+        out["params"] = per_head_params(fmt, enc, B, H, Tcap, n_ctx)
+    elif q in ("asym_minmax", "asym_absmax_offset"):
         if layout == "per_token":
             p = np.zeros((B, H, Tcap, D // G, 2), dtype=np.float16)
             p[:, :, :n_ctx, :, 0] = enc["scale"]
@@ -249,6 +251,26 @@ def expected_regions(fmt: Dict, enc: Dict[str, np.ndarray], *, batch: int, n_kv_
         out["col"] = col
         out["val"] = val
     return out
+
+
+def per_head_params(fmt: Dict, enc: Dict, B: int, H: int, Tcap: int, n_ctx: int) -> np.ndarray:
+    """Parameter image of a per-token format with a group size per KV head:
+    for each sequence, head 0's [Tcap][d / G_0] records, then head 1's, ...
+    (a record: fp16 scale, zero; q8_0: fp16 scale).  Flat fp16 array."""
+    q8 = fmt["quantizer"] == "sym_q8_0"
+    blocks = []
+    for b in range(B):
+        for h in range(H):
+            ng = D // int(fmt["head_group_size"][h])
+            if q8:
+                p = np.zeros((Tcap, ng), dtype=np.float16)
+                p[:n_ctx] = enc["scale"][h][b]
+            else:
+                p = np.zeros((Tcap, ng, 2), dtype=np.float16)
+                p[:n_ctx, :, 0] = enc["scale"][h][b]
+                p[:n_ctx, :, 1] = enc["zero"][h][b]
+            blocks.append(p.reshape(-1))
+    return np.concatenate(blocks)
 
 
 def tail_ring(raw: np.ndarray, G: int, overlap: int, n_ctx: int, kv_dtype: str) -> np.ndarray:

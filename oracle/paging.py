@@ -58,14 +58,18 @@ def _gather_pages(img: np.ndarray, table: np.ndarray, n_pages: int, used: int) -
 
 
 def paged_regions(regions: Dict[str, np.ndarray], table: np.ndarray, *, n_pages: int,
-                  n_ctx: int, capacity: int, per_channel: bool,
-                  k_out: int = 0) -> Dict[str, np.ndarray]:
+                  n_ctx: int, capacity: int, per_channel: bool, k_out: int = 0,
+                  head_ng=None, rec_halves: int = 2) -> Dict[str, np.ndarray]:
     """Byte images of one tensor's regions in a paged cache of ``n_pages``
     pages, from its contiguous images over ``capacity`` tokens per sequence
     (codes [B, H, capacity * row bytes]; per-token params [B, H, capacity,
     ...]; CSR over B * capacity rows) and the page table [B, pages_per_seq].
     Pages that no entry below ceil(n_ctx / 32) names stay zero.  The tail
-    and per-channel params (``per_channel``) keep their contiguous images."""
+    and per-channel params (``per_channel``) keep their contiguous images.
+    With a group size per KV head (``head_ng``: groups per token of each
+    head; ``rec_halves``: fp16 values per record) the contiguous params
+    hold, per sequence, head 0's [capacity][head_ng[0]] records, then head
+    1's, ...; a page holds, per head in turn, its 32 tokens' records."""
     table = np.asarray(table, dtype=np.int64)
     used = (n_ctx + PAGE - 1) // PAGE
     B = table.shape[0]
@@ -77,6 +81,21 @@ def paged_regions(regions: Dict[str, np.ndarray], table: np.ndarray, *, n_pages:
             H = img.shape[1]
             pages = img.reshape(B, H, npg, -1)            # 32 rows, or one value tile
             out[name] = _gather_pages(pages, table, n_pages, used).reshape(n_pages, H, -1)
+        elif name == "params" and head_ng is not None:
+            flat = img.reshape(-1)
+            tot = sum(head_ng) * rec_halves
+            per_seq = flat.reshape(B, capacity * tot)
+            dst = np.zeros((n_pages, PAGE * tot), dtype=img.dtype)
+            for b in range(B):
+                off = 0
+                for h, ng in enumerate(head_ng):
+                    w = ng * rec_halves                # values per token of head h
+                    head = per_seq[b, capacity * off:capacity * (off + w)].reshape(capacity, w)
+                    for i in range(used):
+                        dst[table[b][i], PAGE * off:PAGE * (off + w)] = \
+                            head[PAGE * i:PAGE * (i + 1)].reshape(-1)
+                    off += w
+            out[name] = dst
         elif name == "params" and not per_channel:
             H = img.shape[1]
             pages = img.reshape((B, H, npg, PAGE) + img.shape[3:])

@@ -229,6 +229,21 @@ def encode_tensor(x: np.ndarray, fmt: Dict, codebook: np.ndarray = None,
         out["deq"] = np.transpose(deq, (0, 2, 1, 3))
         return out
 
+    if layout == "per_token" and fmt.get("head_group_size"):
+        # a group size per KV head (Memory-killer page, sections 2.3 and
+        # 5.3: finer groups for the heads that are sensitive to quantization)
+        # -- each head is its own per-token tensor; scale and zero become
+        # per-head lists of [B, T, d / G_h] arrays
+        parts = [encode_tensor(x[:, :, h:h + 1, :], dict(fmt, group_size=int(gh),
+                                                           head_group_size=None))
+                 for h, gh in enumerate(fmt["head_group_size"])]
+        out["codes"] = np.concatenate([p["codes"] for p in parts], axis=1)
+        out["deq"] = np.concatenate([p["deq"] for p in parts], axis=1)
+        out["scale"] = [p["scale"][:, 0] for p in parts]
+        if "zero" in parts[0]:
+            out["zero"] = [p["zero"][:, 0] for p in parts]
+        return out
+
     if layout == "per_token":
         if d % G:
             raise ValueError("group size must divide head_dim")

@@ -344,6 +344,9 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 
   const int split = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.sh.Hkv, h = bh % a.sh.Hkv;
+  // per-head group sizes: this launch serves the KV heads whose values
+  // (and per-token keys) have NGV groups per token
+  if (a.head_class && a.v.ngh[h] != a.head_class) return;
   // the wave index is uniform: keep it (and all block bookkeeping) scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -542,12 +545,16 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   const uint32_t p_lane_tok = 4u * (uint32_t)q4;
   const bool paged = a.sh.page_table != nullptr;
 
-  // row of a block's first token: its 32 tokens are consecutive rows (one
-  // page of a paged cache)
-  auto block_row = [&](int blk) -> int64_t {
-    return paged ? tok_row(a.sh, b, h, (int64_t)blk * kTile) : prow + (int64_t)blk * kTile;
+  // (a block's 32 tokens are consecutive rows from its first token's row:
+  // one page of a paged cache)
+  // first parameter record of a block (token t0, row r0, page of a paged
+  // cache): r0 * NG, or the per-head record layout
+  auto prec = [&](const DevTensor& T, int NG, int64_t r0, int64_t t0, int64_t page) -> int64_t {
+    if (!T.per_head) return r0 * NG;
+    const int64_t tot = T.ng_pre[a.sh.Hkv], pre = T.ng_pre[h];
+    return paged ? (int64_t)kTile * (page * tot + pre) : a.sh.Tcap * ((int64_t)b * tot + pre) + t0 * NG;
   };
-  auto load_row = [&](Buf& B, int64_t r0) {
+  auto load_row = [&](Buf& B, int64_t r0, int64_t t0, int64_t page) {
     const uint8_t* kcodes = K.codes + r0 * (4 * KB * 4);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -557,17 +564,23 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
         B.vp[mb][0] = 0u;
         B.kp[mb][0] = 0u;
       } else {
-        const uint8_t* vprm = static_cast<const uint8_t*>(V.params) + r0 * NGV * (VQ8 ? 2 : 4);
+        const uint8_t* vprm = static_cast<const uint8_t*>(V.params) +
+                              prec(V, NGV, r0, t0, page) * (VQ8 ? 2 : 4);
         load_dw<VPD>(vprm + tok * (NGV * (VQ8 ? 2 : 4)), B.vp[mb]);
         if constexpr (!KCH) {
-          const uint8_t* kprm = static_cast<const uint8_t*>(K.params) + r0 * NGK * (KQ8 ? 2 : 4);
+          const uint8_t* kprm = static_cast<const uint8_t*>(K.params) +
+                                prec(K, NGK, r0, t0, page) * (KQ8 ? 2 : 4);
           load_dw<KPD>(kprm + tok * (NGK * (KQ8 ? 2 : 4)), B.kp[mb]);
         }
       }
     }
     load_dw<2 * VB>(V.codes + r0 * (4 * VB * 4) + v_lane_off, B.v);
   };
-  auto load = [&](Buf& B, int blk) { load_row(B, block_row(blk)); };
+  auto load = [&](Buf& B, int blk) {
+    const int64_t page = paged ? page_of(a.sh, b, blk) : 0;
+    load_row(B, paged ? page_head_row(a.sh, page, h) : prow + (int64_t)blk * kTile,
+             (int64_t)blk * kTile, page);
+  };
 
   // per-channel keys: B operand and zero-point term of key group ``grp``
   // The g * 16 blocks of 8 channels of the group's heads are shared out over
@@ -952,21 +965,22 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     // load ahead (a scalar load), and used only when that block's loads
     // are issued
     int pf_page = paged ? table_entry(a.sh, b, pf.blk) : 0;
-    auto next_load = [&]() {
-      const int64_t r = paged ? page_head_row(a.sh, clamp_page(a.sh, pf_page), h)
-                              : prow + (int64_t)pf.blk * kTile;
+    auto next_load = [&](Buf& B) {
+      const int64_t page = paged ? clamp_page(a.sh, pf_page) : 0;
+      const int64_t t0 = (int64_t)pf.blk * kTile;
+      const int64_t r = paged ? page_head_row(a.sh, page, h) : prow + t0;
       advance(pf);
       if (paged) pf_page = table_entry(a.sh, b, pf.blk);
-      return r;
+      load_row(B, r, t0, page);
     };
     auto next_comp = [&]() { const int b = cb.blk; advance(cb); return b; };
     Buf b0, b1;
-    load_row(b0, next_load());
+    next_load(b0);
     for (int k = 0; k < nk_full; k += 2) {
-      load_row(b1, next_load());
+      next_load(b1);
       compute(std::false_type{}, b0, next_comp());
       if (k + 1 >= nk_full) break;
-      load_row(b0, next_load());
+      next_load(b0);
       compute(std::false_type{}, b1, next_comp());
     }
   }
@@ -1102,13 +1116,21 @@ bool uniform(const kvq_tensor_format& f) {
 
 }  // namespace
 
+// group size of KV head h of a per-token format
+int head_group(const kvq_tensor_format& f, int h) {
+  return f.head_group_size ? f.head_group_size[h] : f.group_size;
+}
+
 bool mfma_config_supported(const kvq_config& c) {
   if (c.k.quantizer == KVQ_QUANT_FP8_E5M2 && c.v.quantizer == KVQ_QUANT_FP8_E5M2)
     return !c.rope && c.n_q_heads / c.n_kv_heads <= 8;
   if (!uniform(c.k) || !uniform(c.v) || c.rope) return false;
   if (c.n_q_heads / c.n_kv_heads > 8) return false;
   if (c.k.layout == KVQ_LAYOUT_PER_CHANNEL) return c.kv_dtype == KVQ_F16;
-  return c.k.group_size == c.v.group_size;
+  // per-token keys: each KV head's key and value groups of one size
+  for (int h = 0; h < c.n_kv_heads; ++h)
+    if (head_group(c.k, h) != head_group(c.v, h)) return false;
+  return true;
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a_in, hipStream_t s) {
@@ -1122,6 +1144,41 @@ hipError_t launch_decode_mfma(const DecodeArgs& a_in, hipStream_t s) {
     const int gblk = a.k.G / kTile;
     const int groups = (per_wave + gblk - 1) / gblk + 1;
     a.kp_groups = groups < kMaxKpGroups ? groups : kMaxKpGroups;
+  }
+  if (a.v.per_head || a.k.per_head) {
+    // per-head group sizes: one launch per number of groups per token, over
+    // the KV heads that have it (the other workgroups return at once)
+    bool seen[5] = {false, false, false, false, false};
+    for (int h = 0; h < a.sh.Hkv; ++h) seen[a.v.per_head ? a.v.ngh[h] : a.v.ng] = true;
+    for (int c : {1, 2, 4}) {
+      if (!seen[c]) continue;
+      DecodeArgs ac = a;
+      ac.head_class = c;
+      ac.v.ng = c;
+      if (!ac.k.per_channel) ac.k.ng = c;
+      if (!ac.v.per_head) {   // uniform values with per-head keys: one class
+        ac.head_class = 0;
+      }
+      bool ok = false;
+      if (ac.k.per_channel) {
+        switch (ac.k.bits) {
+          case 3: ok = launch_kch<3>(ac, s); break;
+          case 4: ok = launch_kch<4>(ac, s); break;
+          case 8: ok = launch_kch<8>(ac, s); break;
+        }
+      } else if (ac.k.quant == KVQ_QUANT_SYM_Q8_0) {
+        ok = launch_ktok<8, true>(ac, s);
+      } else {
+        switch (ac.k.bits) {
+          case 3: ok = launch_ktok<3, false>(ac, s); break;
+          case 4: ok = launch_ktok<4, false>(ac, s); break;
+          case 8: ok = launch_ktok<8, false>(ac, s); break;
+        }
+      }
+      if (!ok) return hipErrorNotSupported;
+      if (!ac.head_class) break;
+    }
+    return hipGetLastError();
   }
   bool ok = false;
   if (a.k.quant == KVQ_QUANT_FP8_E5M2 && a.v.quant == KVQ_QUANT_FP8_E5M2) {

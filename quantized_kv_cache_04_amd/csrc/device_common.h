@@ -61,6 +61,28 @@ __device__ __forceinline__ int64_t tok_row(const DevShape& sh, int b, int h, int
   if (!sh.page_table) return ((int64_t)b * sh.Hkv + h) * sh.Tcap + t;
   return page_head_row(sh, page_of(sh, b, t / kTile), h) + (t % kTile);
 }
+// Index of the first parameter record of token t of (sequence b, KV head h)
+// in a per-token parameter array (records of one token are consecutive):
+// tok_row * ng for one group size; with a group size per head the heads'
+// records of a sequence (or page) follow one another,
+// [B][h][Tcap][ngh[h]] or [page][h][kTile][ngh[h]].
+__device__ __forceinline__ int64_t prm_rec(const DevTensor& p, const DevShape& sh, int b, int h,
+                                           int64_t t) {
+  if (!p.per_head) return tok_row(sh, b, h, t) * p.ng;
+  const int64_t tot = p.ng_pre[sh.Hkv], pre = p.ng_pre[h], nh = p.ngh[h];
+  if (!sh.page_table) return sh.Tcap * ((int64_t)b * tot + pre) + t * nh;
+  return (int64_t)kTile * (page_of(sh, b, t / kTile) * tot + pre) + (t % kTile) * nh;
+}
+// The tensor as head h sees it: its group size and groups per token.
+__device__ __forceinline__ DevTensor head_view(const DevTensor& p, int h) {
+  DevTensor v = p;
+  if (p.per_head) {
+    v.ng = p.ngh[h];
+    v.G = kHeadDim / p.ngh[h];
+  }
+  return v;
+}
+
 // Row of token t of sequence b in the outlier CSR (one row per token, all
 // heads): b * Tcap + t, or page * kTile + t mod kTile.
 __device__ __forceinline__ int64_t csr_row(const DevShape& sh, int b, int64_t t) {
@@ -190,7 +212,8 @@ __device__ inline float deq_key(const DevTensor& k, const DevShape& sh, int bh, 
   if (k.per_channel)
     return deq_uniform(code, k.quant, k.params,
                        ((int64_t)bh * (sh.Tcap / k.G) + t / k.G) * kHeadDim + c);
-  return deq_uniform(code, k.quant, k.params, row * k.ng + c / k.G);
+  return deq_uniform(code, k.quant, k.params,
+                     prm_rec(k, sh, bh / sh.Hkv, h, t) + c / head_view(k, h).G);
 }
 
 // Dense value of value channel c of token t of KV head h.
@@ -206,7 +229,8 @@ __device__ inline float deq_value(const DevTensor& v, const DevShape& sh, int bh
   }
   const uint32_t code = v_tile_code(tile, v.bits, (int)(t & (kTile - 1)), c);
   if (v.quant == KVQ_QUANT_FP8_E5M2) return e5m2_to_f(code) * fp8_scale(v, h);
-  return deq_uniform(code, v.quant, v.params, row * v.ng + c / v.G);
+  return deq_uniform(code, v.quant, v.params,
+                     prm_rec(v, sh, bh / sh.Hkv, h, t) + c / head_view(v, h).G);
 }
 
 }  // namespace kvq

@@ -143,9 +143,13 @@ __global__ __launch_bounds__(256) void enc_rows_kernel(DevShape sh, DevTensor t,
   float x[8];
   unpack8(v, sh.kv_bf16, x);
   void* prm = nullptr;
-  if (active && t.params)
-    prm = static_cast<uint8_t*>(t.params) + row * (int64_t)t.ng * (t.quant == KVQ_QUANT_SYM_Q8_0 ? 2 : 4);
-  const uint2 cq = encode8(t, h, j8, x, prm);
+  if (active && t.params) {
+    const int64_t bt = r / sh.Hkv;
+    prm = static_cast<uint8_t*>(t.params) +
+          prm_rec(t, sh, (int)(bt / n_new), h, n_ctx + bt % n_new) *
+              (t.quant == KVQ_QUANT_SYM_Q8_0 ? 2 : 4);
+  }
+  const uint2 cq = encode8(head_view(t, h), h, j8, x, prm);
   *reinterpret_cast<uint2*>(&rowc[rl][8 * j8]) = cq;
   __syncthreads();
   const int dw_row = 4 * t.bits;
@@ -215,11 +219,11 @@ __global__ __launch_bounds__(256) void enc_vtile_kernel(DevShape sh, DevTensor t
     const bool fresh = tpos >= lo_new && tpos < hi_new;
     float x[8];
     unpack8(xin[p], sh.kv_bf16, x);
-    const int64_t row = tok_row(sh, b, h, tpos);
     void* prm = nullptr;
     if (fresh && t.params)
-      prm = static_cast<uint8_t*>(t.params) + row * (int64_t)t.ng * (t.quant == KVQ_QUANT_SYM_Q8_0 ? 2 : 4);
-    const uint2 cq = encode8(t, h, j8, x, prm);
+      prm = static_cast<uint8_t*>(t.params) +
+            prm_rec(t, sh, b, h, tpos) * (t.quant == KVQ_QUANT_SYM_Q8_0 ? 2 : 4);
+    const uint2 cq = encode8(head_view(t, h), h, j8, x, prm);
     if (fresh) *reinterpret_cast<uint2*>(&codes[tau][8 * j8]) = cq;
   }
   __syncthreads();

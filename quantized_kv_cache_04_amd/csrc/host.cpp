@@ -55,8 +55,22 @@ kvq_status check_format(const kvq_tensor_format& f, const kvq_config& c, bool is
       return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: window_overlap must be a multiple of 32 in "
                   "[0, 256] (got %d)", name, f.window_overlap);
   }
-  if (f.head_group_size)
-    return fail(KVQ_ERR_UNSUPPORTED, "%s: per-head group sizes are not supported", name);
+  if (f.head_group_size) {
+    if (f.layout != KVQ_LAYOUT_PER_TOKEN ||
+        (f.quantizer != KVQ_QUANT_ASYM_MINMAX && f.quantizer != KVQ_QUANT_ASYM_ABSMAX_OFFSET &&
+         f.quantizer != KVQ_QUANT_SYM_Q8_0))
+      return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: head_group_size applies to per-token "
+                  "ASYM_MINMAX, ASYM_ABSMAX_OFFSET or SYM_Q8_0 formats only", name);
+    if (c.n_kv_heads > kMaxHeadsPH)
+      return fail(KVQ_ERR_UNSUPPORTED, "%s: per-head group sizes need n_kv_heads <= %d", name,
+                  kMaxHeadsPH);
+    for (int h = 0; h < c.n_kv_heads; ++h) {
+      const int g = f.head_group_size[h];
+      if (g != 32 && g != 64 && g != 128)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: head_group_size[%d] must be 32, 64 or 128 "
+                    "(got %d)", name, h, g);
+    }
+  }
   if (f.layout != KVQ_LAYOUT_PER_TOKEN && f.layout != KVQ_LAYOUT_PER_CHANNEL)
     return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: unknown layout %d", name, f.layout);
   switch (f.quantizer) {
@@ -96,6 +110,7 @@ kvq_status check_format(const kvq_tensor_format& f, const kvq_config& c, bool is
       return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: unknown quantizer %d", name, f.quantizer);
   }
   if (f.layout == KVQ_LAYOUT_PER_TOKEN) {
+    if (f.head_group_size) return KVQ_OK;   // group_size is not used
     if (f.group_size != 32 && f.group_size != 64 && f.group_size != 128)
       return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: per-token group_size must be 32, 64 or 128 "
                   "(got %d)", name, f.group_size);
@@ -167,7 +182,18 @@ void fill_tensor(TensorLayout& t, const kvq_tensor_format& f, const kvq_config& 
   t.G = (f.quantizer == KVQ_QUANT_NONE || f.quantizer == KVQ_QUANT_CODEBOOK ||
          f.quantizer == KVQ_QUANT_FP8_E5M2) ? 0 : f.group_size;
   t.row_bytes = (int)(d * t.bits / 8);
+  t.per_head = f.head_group_size != nullptr;
+  if (t.per_head) {
+    t.ng_pre[0] = 0;
+    for (uint64_t h = 0; h < H; ++h) {
+      t.ngh[h] = (uint8_t)(d / f.head_group_size[h]);
+      t.ng_pre[h + 1] = (uint16_t)(t.ng_pre[h] + t.ngh[h]);
+    }
+    t.G = f.head_group_size[0];   // per-head formats read ngh / ng_pre instead
+  }
   t.ng = (t.G && !t.per_channel) ? (int)(d / t.G) : 0;
+  // parameter records per token over all heads
+  const uint64_t ng_all = t.per_head ? t.ng_pre[H] : H * (uint64_t)t.ng;
   t.psize = f.quantizer == KVQ_QUANT_SYM_Q8_0 ? 2 : 4;
   t.k_out = f.quantizer == KVQ_QUANT_CODEBOOK ? outlier_count(f.outlier_frac, (int)(H * d)) : 0;
   auto put = [&](uint64_t& o, uint64_t& sz, uint64_t bytes) {
@@ -180,7 +206,7 @@ void fill_tensor(TensorLayout& t, const kvq_tensor_format& f, const kvq_config& 
     if (t.per_channel)
       put(t.params_off, t.params_bytes, B * H * (uint64_t)(Tcap / t.G) * d * 4);
     else
-      put(t.params_off, t.params_bytes, H * slots * t.ng * t.psize);
+      put(t.params_off, t.params_bytes, slots * ng_all * t.psize);
   }
   t.overlap = t.per_channel ? f.window_overlap : 0;
   if (t.per_channel) put(t.tail_off, t.tail_bytes, B * H * (uint64_t)(t.G + t.overlap) * d * 2);
@@ -241,7 +267,8 @@ uint64_t tensor_payload(const TensorLayout& t, const kvq_config& c, int64_t n) {
     uint64_t nf = (uint64_t)(n / t.G) * t.G;
     return B * H * (nf * t.row_bytes + (nf / t.G) * d * 4 + ((uint64_t)n - nf) * d * 2);
   }
-  return B * H * (uint64_t)n * (t.row_bytes + (uint64_t)t.ng * t.psize);
+  const uint64_t ng_all = t.per_head ? t.ng_pre[H] : H * (uint64_t)t.ng;
+  return B * (uint64_t)n * (H * t.row_bytes + ng_all * t.psize);
 }
 
 void fill_regions(kvq_tensor_regions& r, const TensorLayout& t) {
@@ -307,6 +334,9 @@ DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebo
   t.k_out = tl.k_out;
   t.overlap = tl.overlap;
   t.tail_rows = tl.G + tl.overlap;
+  t.per_head = tl.per_head;
+  memcpy(t.ngh, tl.ngh, sizeof t.ngh);
+  memcpy(t.ng_pre, tl.ng_pre, sizeof t.ng_pre);
   t.codes = b + tl.codes_off;
   t.params = tl.params_bytes ? b + tl.params_off : nullptr;
   t.tail = tl.tail_bytes ? reinterpret_cast<uint16_t*>(b + tl.tail_off) : nullptr;

@@ -14,6 +14,7 @@ constexpr int kTile = 32;          // tokens per value tile / decode block
 constexpr int kCapAlign = 1024;    // token capacity granularity (a multiple of kTile)
 constexpr int kMaxSink = 4096;     // attention-sink tokens kept raw per sequence
 constexpr int kSinkSplitTokens = 256;   // a split of the sink spans at least this many tokens
+constexpr int kMaxHeadsPH = 64;     // KV heads of a format with per-head group sizes
 
 // Host-side description of one cache tensor (keys or values) and where its
 // arrays sit in the allocation.
@@ -27,6 +28,11 @@ struct TensorLayout {
   int psize = 0;        // bytes per group parameter record (4: scale+zero, 2: scale)
   int k_out = 0;        // outliers kept per token (CODEBOOK)
   int overlap = 0;      // per-channel keys: tokens the statistics window reaches back
+  // per-token groups with a size per KV head: groups per token of head h
+  // and their prefix sums (ng_pre[Hkv] = groups per token over all heads)
+  int per_head = 0;
+  uint8_t ngh[kMaxHeadsPH] = {};
+  uint16_t ng_pre[kMaxHeadsPH + 1] = {};
   uint64_t codes_off = 0, codes_bytes = 0;
   uint64_t params_off = 0, params_bytes = 0;
   uint64_t tail_off = 0, tail_bytes = 0;
@@ -55,6 +61,13 @@ struct DevTensor {
   // unquantized tail is a ring of tail_rows = G + overlap rows in which
   // token t sits at row t mod tail_rows
   int overlap, tail_rows;
+  // per-token groups with a size per KV head (per_head = 1): head h has
+  // ngh[h] groups of 128 / ngh[h] channels per token, and its parameter
+  // records follow those of heads 0 .. h-1 (ng_pre[h] records per token
+  // before it, ng_pre[Hkv] in all); G and ng are then unused
+  int per_head;
+  uint8_t ngh[kMaxHeadsPH];
+  uint16_t ng_pre[kMaxHeadsPH + 1];
   uint8_t* codes;
   void* params;
   uint16_t* tail;
@@ -116,6 +129,8 @@ struct DecodeArgs {
   int S_max;
   float* partial;       // [B][Hq][S_max][d + 2]
   int kp_groups;        // matrix-core kernel: key groups staged in LDS per wave (0 = none)
+  int head_class = 0;   // matrix-core kernel, per-head group sizes: only the KV heads
+                        // whose values have this many groups per token (0 = all)
 };
 
 // kvq_decode_attention with the split-K partial states in partial_ws

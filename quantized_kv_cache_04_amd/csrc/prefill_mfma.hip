@@ -372,6 +372,8 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
   const int kkind = fmt_kind<KF>(a.k), vkind = fmt_kind<VF>(a.v);
   const int kbits = fmt_bits<KF>(a.k), vbits = fmt_bits<VF>(a.v);
   const bool kpc = fmt_pc<KF>(a.k);
+  // group sizes and groups per token of this workgroup's head
+  const int kG = head_view(a.k, h).G, vG = head_view(a.v, h).G, vng = head_view(a.v, h).ng;
   const bool kraw = kkind == KVQ_QUANT_NONE, vraw = vkind == KVQ_QUANT_NONE;
   const bool kstage = a.k.k_out > 0;   // keys go through the fp32 stage (outliers, then RoPE)
   const float ksc = fp8_scale(a.k, h), vsc = fp8_scale(a.v, h);
@@ -425,13 +427,13 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
               static_cast<const uint32_t*>(a.k.params) + ((int64_t)bh * (Tcap / a.k.G) + tq / a.k.G) * kD + c0);
           R.kq[0] = pp[0]; R.kq[1] = pp[1]; R.kq[2] = pp[16]; R.kq[3] = pp[17];
         } else if (kkind == KVQ_QUANT_SYM_Q8_0) {
-          const uint16_t* pp = static_cast<const uint16_t*>(a.k.params) + (qrow0 + ktk) * a.k.ng;
-          R.kpz[0] = pp[c0 / a.k.G];
-          R.kpz[1] = pp[(c0 + 64) / a.k.G];
+          const uint16_t* pp = static_cast<const uint16_t*>(a.k.params) + prm_rec(a.k, a.sh, b, h, tq);
+          R.kpz[0] = pp[c0 / kG];
+          R.kpz[1] = pp[(c0 + 64) / kG];
         } else if (kkind != KVQ_QUANT_CODEBOOK && kkind != KVQ_QUANT_FP8_E5M2) {
-          const uint32_t* pp = static_cast<const uint32_t*>(a.k.params) + (qrow0 + ktk) * a.k.ng;
-          R.kpz[0] = pp[c0 / a.k.G];
-          R.kpz[1] = pp[(c0 + 64) / a.k.G];
+          const uint32_t* pp = static_cast<const uint32_t*>(a.k.params) + prm_rec(a.k, a.sh, b, h, tq);
+          R.kpz[0] = pp[c0 / kG];
+          R.kpz[1] = pp[(c0 + 64) / kG];
         }
       }
     }
@@ -466,16 +468,17 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
             R.vc[2 * q + 1] = w[2];
           }
         }
+        // the block's tokens are consecutive records of one (sequence, head)
         if (vkind == KVQ_QUANT_SYM_Q8_0) {
-          const uint16_t* pp = static_cast<const uint16_t*>(a.v.params);
+          const uint16_t* pp = static_cast<const uint16_t*>(a.v.params) +
+                               prm_rec(a.v, a.sh, b, h, d.tq0 + 16 * vhv) + vch / vG;
 #pragma unroll
-          for (int u = 0; u < 16; ++u)
-            R.vp[u] = pp[(qrow0 + 16 * vhv + u) * a.v.ng + vch / a.v.G];
+          for (int u = 0; u < 16; ++u) R.vp[u] = pp[u * vng];
         } else if (vkind != KVQ_QUANT_FP8_E5M2) {
-          const uint32_t* pp = static_cast<const uint32_t*>(a.v.params);
+          const uint32_t* pp = static_cast<const uint32_t*>(a.v.params) +
+                               prm_rec(a.v, a.sh, b, h, d.tq0 + 16 * vhv) + vch / vG;
 #pragma unroll
-          for (int u = 0; u < 16; ++u)
-            R.vp[u] = pp[(qrow0 + 16 * vhv + u) * a.v.ng + vch / a.v.G];
+          for (int u = 0; u < 16; ++u) R.vp[u] = pp[u * vng];
         }
       }
     }

@@ -60,7 +60,10 @@ def oracle_encode(w, inputs: Dict[str, Optional[torch.Tensor]], n_ctx: int, max_
                                          n_ctx=n_q, capacity=olay.capacity(max_ctx),
                                          per_channel=fmt.get("layout") == "per_channel",
                                          k_out=oq.outlier_count(fmt.get("outlier_frac", 0.0),
-                                                                w.n_kv_heads * w.head_dim))
+                                                                w.n_kv_heads * w.head_dim),
+                                         head_ng=([w.head_dim // g for g in fmt["head_group_size"]]
+                                                  if fmt.get("head_group_size") else None),
+                                         rec_halves=1 if fmt["quantizer"] == "sym_q8_0" else 2)
         if sink:
             exp["sink"] = olay.sink_region(x, sink, kv_dtype=w.kv_dtype)
         res[name] = exp or None

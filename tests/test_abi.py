@@ -362,3 +362,58 @@ def test_paged_layout_and_table_checks():
                           k=u4, v=u4, page_pool=-1)
     with pytest.raises(kvq.KvqError):
         kvq.cache_layout(bad)
+
+
+def test_per_head_group_sizes_layout_and_checks():
+    pc = {"quantizer": "asym_minmax", "bits": 4, "group_size": 128, "layout": "per_channel"}
+    ph = {"quantizer": "asym_minmax", "bits": 4, "group_size": 0, "layout": "per_token",
+          "head_group_size": [32, 128, 64]}
+    cfg = kvq.make_config(batch=2, n_q_heads=6, n_kv_heads=3, max_ctx=1000, kv_dtype="f16",
+                          k=pc, v=ph)
+    li = kvq.cache_layout(cfg)
+    # (4 + 1 + 2) records of 4 bytes per token over 2 x 1024 tokens
+    assert li.v.params.bytes == 2 * 1024 * 7 * 4
+    want = ocb.payload_bytes(pc, ph, batch=2, n_kv_heads=3, head_dim=128, n_ctx=777)
+    assert kvq.cache_bytes(cfg, 777) == want
+    assert kvq.decode_path(cfg) == "mfma"
+    # per-token keys with other group sizes than the values: general kernel
+    k64 = {"quantizer": "asym_minmax", "bits": 4, "group_size": 64, "layout": "per_token"}
+    mixed = kvq.make_config(batch=1, n_q_heads=3, n_kv_heads=3, max_ctx=64, kv_dtype="f16",
+                            k=k64, v=ph)
+    assert kvq.decode_path(mixed) == "valu"
+    for bad, status in (
+            (dict(ph, head_group_size=[32, 48, 64]), kvq.ERR_INVALID_ARGUMENT),
+            (dict(pc, head_group_size=[32, 32, 32]), kvq.ERR_INVALID_ARGUMENT),
+            ({"quantizer": "codebook", "bits": 4, "head_group_size": [32, 32, 32]},
+             kvq.ERR_INVALID_ARGUMENT)):
+        c = kvq.make_config(batch=1, n_q_heads=3, n_kv_heads=3, max_ctx=64, kv_dtype="f16",
+                            k=pc, v=bad) if bad is not pc else None
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.cache_layout(c)
+        assert e.value.status == status
+    many = dict(ph, head_group_size=[32] * 65)
+    c = kvq.make_config(batch=1, n_q_heads=65, n_kv_heads=65, max_ctx=64, kv_dtype="f16",
+                        k=pc, v=many)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.cache_layout(c)
+    assert e.value.status == kvq.ERR_UNSUPPORTED
+
+
+def test_window_overlap_checks():
+    pc = {"quantizer": "asym_minmax", "bits": 4, "group_size": 128, "layout": "per_channel",
+          "window_overlap": 64}
+    u4 = {"quantizer": "asym_minmax", "bits": 4, "group_size": 128, "layout": "per_token"}
+    cfg = kvq.make_config(batch=2, n_q_heads=4, n_kv_heads=2, max_ctx=500, kv_dtype="f16",
+                          k=pc, v=u4)
+    li = kvq.cache_layout(cfg)
+    assert li.k.tail.bytes == 2 * 2 * (128 + 64) * 128 * 2     # the ring of G + overlap rows
+    flat = kvq.make_config(batch=2, n_q_heads=4, n_kv_heads=2, max_ctx=500, kv_dtype="f16",
+                           k=dict(pc, window_overlap=0), v=u4)
+    assert kvq.cache_bytes(cfg, 300) == kvq.cache_bytes(flat, 300)
+    for bad in (dict(pc, window_overlap=48), dict(pc, window_overlap=288),
+                dict(u4, window_overlap=32)):
+        c = kvq.make_config(batch=1, n_q_heads=2, n_kv_heads=2, max_ctx=64, kv_dtype="f16",
+                            k=bad, v=u4)
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.cache_layout(c)
+        assert e.value.status == kvq.ERR_INVALID_ARGUMENT

@@ -7,8 +7,8 @@ heads of dimension d), the TurboQuant page's section 2.1 formula; element
 counts follow the Memory-killer page's section 1.2 (2 * L * H * D * S).
 Quantized formats count packed codes, fp16 scale (+ zero) per group, the
 fp16 tail of an unfinished per-channel group, the CSR outliers (4-byte row
-pointer + 2-byte column + 2-byte value per kept entry) and the fp16
-codebooks.  With an attention sink of S tokens (KVQuant page, "Attention
+pointer + 2-byte column + 2-byte value per kept entry + a one-byte count
+of the row's entries per KV head) and the fp16 codebooks.  With an attention sink of S tokens (KVQuant page, "Attention
 Sink"), the first min(S, n) tokens cost their raw fp16/bf16 bytes and the
 format applies to the remaining n - min(S, n) tokens.
 """
@@ -37,7 +37,9 @@ def tensor_payload(fmt: Dict, *, batch: int, n_kv_heads: int, head_dim: int, n_c
         total = B * H * n * rb + H * d * 16 * 2
         k = outlier_count(fmt.get("outlier_frac", 0.0), H * d)
         if k:
-            total += B * n * (4 + 4 * k)
+            # row pointer, k (column, value) pairs, a one-byte count per head
+            # (rows of whole 16-byte units)
+            total += B * n * (4 + 4 * k + (H + 15) // 16 * 16)
         return total
     if fmt.get("layout", "per_token") == "per_channel":
         nf = (n // G) * G

@@ -108,6 +108,13 @@ def paged_regions(regions: Dict[str, np.ndarray], table: np.ndarray, *, n_pages:
                     rp[r] = k_out * r
                     rp[r + 1] = k_out * (r + 1)
             out[name] = rp.astype(np.int32)
+        elif name == "head_count":
+            src = img.reshape(B, capacity, -1)
+            dst = np.zeros((n_pages * PAGE, src.shape[2]), dtype=img.dtype)
+            for b in range(B):
+                for t in range(n_ctx):
+                    dst[csr_row(table, b, t)] = src[b, t]
+            out[name] = dst
         elif name in ("col", "val"):
             src = img.reshape(B, capacity, k_out)
             dst = np.zeros((n_pages * PAGE, k_out), dtype=img.dtype)

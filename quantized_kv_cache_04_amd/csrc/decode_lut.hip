@@ -27,10 +27,12 @@
 //    both 4-bit indices of a lane in one byte per token, and one LDS dword
 //    per (centroid, lane) holds both channels' centroids, so lane l always
 //    reads bank l;
-//  * outliers (CSR rows of one token over all heads) are compacted per wave
-//    to the entries of the workgroup's heads and enter as (val - centroid)
-//    corrections: to the chunk's scores for keys, to LDS channel sums for
-//    values.
+//  * outliers: a token's CSR row holds its outliers over all heads in
+//    column order, with a count per head; each wave reads only its head's
+//    entries (the lanes of a token share them) and adds (val - centroid)
+//    corrections to the token's score for keys and, through the wave's LDS
+//    channel sums, to the value sums.  Waves of a workgroup never wait for
+//    each other inside the token loop.
 //
 // Each wave leaves an (o, m, l) partial per split, or the output when the
 // context is one split and there is no attention sink.
@@ -49,7 +51,6 @@ constexpr int kD = kHeadDim;
 constexpr int kChunk = 32;      // tokens per chunk: one value tile
 constexpr int kHeads = 4;       // KV heads per workgroup, one per wave
 constexpr int kPairs = kD / 2;
-constexpr int kRingK = 16;      // compacted key outlier slots per wave
 constexpr int kResync = 32;     // chunks between exact evaluations of the query rotation
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -58,15 +59,8 @@ struct __align__(16) LutLds {
   uint16_t kt[kHeads][kD][16];     // key centroids, fp16 [head][channel][index]         16 KB
   uint32_t vt[kHeads][16][64];     // value centroids: (index, l) -> C(l) | C(l+64) << 16 16 KB
   float2 qr[kHeads][kPairs];       // query pairs * sm_scale * log2(e), rotated to the chunk
-  union {                          // wave w only ever touches row w of either
-    float p[kHeads][kChunk];       // probabilities of the chunk (value phase)
-    uint32_t ring_k[kHeads][kRingK][2];   // compacted key outliers (key phase)
-  };
-  // Value outlier sums of the chunk.  Entries [h][0, 32) double as head h's
-  // key outlier corrections of the chunk's scores: the two are live in turn
-  // (key phase up to the softmax, then value phase), each is cleared by the
-  // head's wave after use, and barriers order every clear before the next use.
-  float vcorr[kHeads][kD];
+  float p[kHeads][kChunk];         // probabilities of the chunk, one row per wave
+  float vcorr[kHeads][kD];         // value outlier sums of the chunk, one row per wave
 };
 // three workgroups per CU: the 160 KB of LDS is allocated in units of 1280 bytes
 static_assert(sizeof(LutLds) <= 42 * 1280, "three workgroups per CU");
@@ -238,83 +232,94 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
   int64_t row_c = chunk_row(t_begin);
   load_k(t_begin, row_c, kc);
 
-  // Outlier entries of a chunk: the CSR rows of its tokens are contiguous
-  // (k entries per token), read as 16-byte vectors of 8 entries, vector j by
-  // thread j (32 tokens x at most 64 entries: 256 vectors).  A vector may run
-  // up to 7 entries past the chunk's rows (still inside the allocation: every
-  // outlier array is followed by another region); vectors past the chunk
-  // re-read its last one.  Entries past the chunk fail the e < n_ent test.
-  struct OutVec { u32x4 col, val; };
-  auto load_out = [&](const DevTensor& T, int64_t row0, int nt, OutVec& o) {
-    const int64_t e0 = row0 * T.k_out;
-    const int nv = (nt * T.k_out + 7) / 8;
-    const u32x4* cv = reinterpret_cast<const u32x4*>(T.col + e0);
-    const u32x4* vv = reinterpret_cast<const u32x4*>(T.val + e0);
-    const int vi = min(tid, nv - 1);
-    o.col = cv[vi];
-    o.val = vv[vi];
+  // ---- dense-and-sparse outliers ---------------------------------------------------------
+  // The CSR row of a token holds its outliers over all heads in column order,
+  // and the row's count per KV head says where each head's entries lie: the
+  // wave's head h finds its entries of token tau at sum(count[0 .. h-1]) ..
+  // + count[h] and reads only those.  Lanes (tau, 0) and (tau, 1) take the
+  // even and the odd ones.  The counts of a chunk are loaded one chunk ahead
+  // and its entries before its key phase, so their latency hides under the
+  // lookups; no workgroup barrier is involved.
+  constexpr int kEnt = 4;                        // entries a lane loads ahead per tensor
+  const int hq = hr >> 2, hb = hr & 3;           // head's count dword and byte
+  const uint32_t lo_mask = hb == 0 ? 0u : (0x01010101u >> (8 * (4 - hb)));
+  // a row's counts: one byte per head, rows of whole 16-byte units (two
+  // 16-byte loads cover 32 heads; the second only for heads 16 and up)
+  struct Cnt { uint32_t w[8]; };
+  auto load_cnt = [&](const DevTensor& T, int64_t row0, int nt, Cnt& c) {
+    const int64_t r = row0 + min(tau, nt - 1);
+    const u32x4* p = reinterpret_cast<const u32x4*>(T.hcnt + r * ((Hkv + 15) / 16 * 16));
+    const u32x4 a0 = p[0];
+    const u32x4 a1 = hq >= 4 ? p[1] : u32x4{0u, 0u, 0u, 0u};
+    c.w[0] = a0.x; c.w[1] = a0.y; c.w[2] = a0.z; c.w[3] = a0.w;
+    c.w[4] = a1.x; c.w[5] = a1.y; c.w[6] = a1.z; c.w[7] = a1.w;
   };
-  // Calls f(ww, tau, c, dense index, value) for the entries of this
-  // workgroup's heads.  Each wave compacts the matching entries among those
-  // its threads loaded into its ring (ballot + lane count) and works through
-  // the ring once it is full: about one entry in eight belongs to the
-  // workgroup, so the per-entry work then runs on a ring's worth of lanes.
-  // A step that matches more entries than the ring holds applies them in
-  // place.
-  auto for_entries = [&](const DevTensor& T, int nt, const OutVec& o, uint32_t (*ring)[2],
-                         int slots, auto&& f) {
-    const int ko = T.k_out;
-    const int n_ent = nt * ko;
-    const float inv_k = 1.0f / (float)ko;
-    auto apply = [&](uint32_t col, int e, uint32_t valbits) {
-      // token of entry e: floor(e / k), exact in float for e < 2^16
-      const int te = (int)(((float)e + 0.5f) * inv_k);
-      const int ww = (int)((col & 0xfffu) >> 7) - hg * kHeads;
-      f(ww, te, (int)(col & (kD - 1)), col >> 12, h2f((uint16_t)valbits));
-    };
-    int qn = 0;                                    // ring fill, wave-uniform
-    auto drain = [&]() {
-      __builtin_amdgcn_wave_barrier();             // ring writes of this wave land first
-      if (lane < qn) apply(ring[lane][0] & 0xffffu, (int)(ring[lane][0] >> 16), ring[lane][1]);
-      __builtin_amdgcn_wave_barrier();             // reads done before the ring refills
-      qn = 0;
-    };
-    const uint32_t cw[4] = {o.col.x, o.col.y, o.col.z, o.col.w};
-    const uint32_t vw[4] = {o.val.x, o.val.y, o.val.z, o.val.w};
+  // first entry and number of entries of head hr in the row
+  auto seg = [&](const Cnt& c, int& first, int& num) {
+    uint32_t acc = 0;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const int e = 8 * tid + x;                   // entry index within the chunk
-      const uint32_t col = (cw[x >> 1] >> (16 * (x & 1))) & 0xffffu;
-      // head of the flat index (col & 0xfff) >> 7; its group: bits 9-11
-      const bool hit = e < n_ent && ((col >> 9) & 7u) == (uint32_t)hg;
-      const uint32_t valbits = (vw[x >> 1] >> (16 * (x & 1))) & 0xffffu;
-      const uint64_t mask = __ballot(hit);
-      const int cnt = __popcll(mask);
-      if (slots > 0 && qn + cnt > slots) drain();
-      if (cnt > slots) {                           // more than the ring holds: in place
-        if (hit) apply(col, e, valbits);
-      } else {
-        if (hit) {
-          const int slot = qn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-          ring[slot][0] = col | ((uint32_t)e << 16);
-          ring[slot][1] = valbits;
-        }
-        qn += cnt;
+    for (int j = 0; j < 8; ++j)
+      if (j < hq) acc = __builtin_amdgcn_udot4(c.w[j], 0x01010101u, acc, false);
+    uint32_t wq = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j == hq) wq = c.w[j];
+    first = (int)__builtin_amdgcn_udot4(wq, lo_mask, acc, false);
+    num = (int)((wq >> (8 * hb)) & 0xffu);
+  };
+  // an entry's column and value as the two halves of one register
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  struct Ent { u16x2 cv[kEnt]; int first, num; };
+  auto find_ent = [&](const Cnt& c, int nt, Ent& e) {
+    seg(c, e.first, e.num);
+    if (tau >= nt || !head_ok) e.num = 0;
+  };
+  auto load_ent = [&](const DevTensor& T, int64_t row0, Ent& e) {
+    const int64_t base = (row0 + tau) * T.k_out + e.first;
+#pragma unroll
+    for (int u = 0; u < kEnt; ++u) {
+      const int j = 2 * u + half;
+      e.cv[u] = u16x2{0, 0};
+      if (j < e.num) {
+        e.cv[u].x = T.col[base + j];
+        e.cv[u].y = T.val[base + j];
       }
     }
-    if (qn > 0) drain();
   };
+  // f(channel in the head, dense index, value) for the entries of the
+  // lane's share
+  auto for_ent = [&](const DevTensor& T, int64_t row0, const Ent& e, auto&& f) {
+#pragma unroll
+    for (int u = 0; u < kEnt; ++u) {
+      if (2 * u + half < e.num) f((int)(e.cv[u].x & (kD - 1)), (uint32_t)e.cv[u].x >> 12, h2f(e.cv[u].y));
+    }
+    // more than 2 kEnt entries in one head of one token: the rest in turn
+    const int64_t base = (row0 + tau) * T.k_out + e.first;
+    for (int j = 2 * kEnt + half; j < e.num; j += 2) {
+      const uint32_t col = T.col[base + j];
+      f((int)(col & (kD - 1)), col >> 12, h2f(T.val[base + j]));
+    }
+  };
+
+  Cnt kcn, vcn;
+  {
+    const int nt0 = min(kChunk, t_end - t_begin);
+    const int64_t r0 = csr_row(a.sh, b, t_begin);
+    if constexpr (KOUT) load_cnt(K, r0, nt0, kcn);
+    if constexpr (VOUT) load_cnt(V, r0, nt0, vcn);
+  }
 
   for (int ci = 0; ci < n_chunks; ++ci) {
     const int t0 = t_begin + ci * kChunk;
     const int nt = min(kChunk, t_end - t0);      // tokens of this chunk
     const int64_t row0 = csr_row(a.sh, b, t0);   // CSR row of token t0
-
     const int64_t row_n = chunk_row(t0 + kChunk);
 
-    OutVec ko_v, vo_v;
-    if constexpr (KOUT) load_out(K, row0, nt, ko_v);
+    // where this chunk's outlier entries of the head lie; its key entries
+    // (the value entries load after the key phase)
+    Ent ke, ve;
+    if constexpr (KOUT) { find_ent(kcn, nt, ke); load_ent(K, row0, ke); }
+    if constexpr (VOUT) find_ent(vcn, nt, ve);
     u32x4 vc[2], kn[2];
     load_v(row_c, vc);
 
@@ -363,40 +368,44 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
             }
           }
         }
+      // key outliers of this lane's share: (value - centroid) * coefficient
+      if constexpr (KOUT) {
+        for_ent(K, row0, ke, [&](int c, uint32_t code, float val) {
+          const float delta = val - h2f(S.kt[wave][c][code]);
+          const int i = c & (kPairs - 1);
+          const float2 q2 = S.qr[wave][i];
+          float coef;
+          if constexpr (ROPE) {
+            const float2 cs = S.e[i][tau];
+            coef = c < kPairs ? q2.x * cs.x + q2.y * cs.y : q2.y * cs.x - q2.x * cs.y;
+          } else {
+            coef = c < kPairs ? q2.x : q2.y;
+          }
+          s = __builtin_fmaf(delta, coef, s);
+        });
+      }
       s += swap_halves(s);                           // both halves of token tau
     }
+    // the rotated queries of this chunk are consumed (each wave rotates its
+    // own head's queries; LDS accesses of one wave complete in order)
+    __builtin_amdgcn_wave_barrier();
 
-    // ---- key outliers: (value - centroid) * coefficient into the scores ----------------
-    if constexpr (KOUT) {
-      for_entries(K, nt, ko_v, S.ring_k[wave], kRingK,
-                  [&](int ww, int te, int c, uint32_t code, float val) {
-        const float delta = val - h2f(S.kt[ww][c][code]);
-        const int i = c & (kPairs - 1);
-        const float2 q2 = S.qr[ww][i];
-        float coef;
-        if constexpr (ROPE) {
-          const float2 cs = S.e[i][te];
-          coef = c < kPairs ? q2.x * cs.x + q2.y * cs.y : q2.y * cs.x - q2.x * cs.y;
-        } else {
-          coef = c < kPairs ? q2.x : q2.y;
-        }
-        atomicAdd(&S.vcorr[ww][te], delta * coef);    // key correction of token te
-      });
-    }
-    if constexpr (KOUT || ROPE) __syncthreads();   // scores complete; rotated queries consumed
-
-    // value outliers of this chunk, key codes and rotated queries of the next one
-    if constexpr (VOUT) load_out(V, row0, nt, vo_v);
+    // this chunk's value entries; key codes, rotated queries and outlier
+    // counts of the next chunk
+    if constexpr (VOUT) load_ent(V, row0, ve);
     load_k(t0 + kChunk, row_n, kn);
     row_c = row_n;
     if constexpr (ROPE) set_q(ci + 1);
+    if (ci + 1 < n_chunks) {
+      const int t1 = t0 + kChunk;
+      const int nt1 = min(kChunk, t_end - t1);
+      const int64_t r1 = csr_row(a.sh, b, t1);
+      if constexpr (KOUT) load_cnt(K, r1, nt1, kcn);
+      if constexpr (VOUT) load_cnt(V, r1, nt1, vcn);
+    }
 
     if (head_ok) {
       // ---- online softmax ----------------------------------------------------------
-      if constexpr (KOUT) {
-        s += S.vcorr[wave][tau];                   // key correction; both halves read first
-        if (half == 0) S.vcorr[wave][tau] = 0.f;
-      }
       if (tau >= nt) s = -INFINITY;
       const float m_new = fmaxf(m_run, wave_max(s));
       const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -432,30 +441,23 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
           acc1 = __builtin_fmaf(p4[k], half_hi(c1), acc1);
         }
       }
-    }
 
-    // ---- value outliers: p * (value - centroid) into LDS channel sums ------------------
-    if constexpr (VOUT) {
-      __syncthreads();                               // p of every head complete
-      for_entries(V, nt, vo_v, S.ring_k[wave], 0,   // no ring: p is live
-                  [&](int ww, int te, int c, uint32_t code, float val) {
-        const uint32_t cc = S.vt[ww][code][c & (kPairs - 1)];
-        const float dense = c < kPairs ? half_lo(cc) : half_hi(cc);
-        atomicAdd(&S.vcorr[ww][c], S.p[ww][te] * (val - dense));
-      });
-      __syncthreads();                               // sums complete
-      if (head_ok) {
+      // ---- value outliers: p * (value - centroid) into the wave's channel sums ----------
+      if constexpr (VOUT) {
+        for_ent(V, row0, ve, [&](int c, uint32_t code, float val) {
+          const uint32_t cc = S.vt[wave][code][c & (kPairs - 1)];
+          const float dense = c < kPairs ? half_lo(cc) : half_hi(cc);
+          atomicAdd(&S.vcorr[wave][c], pt * (val - dense));
+        });
+        // LDS accesses of one wave complete in order: the sums are complete
+        __builtin_amdgcn_wave_barrier();
         acc0 += S.vcorr[wave][lane];
         acc1 += S.vcorr[wave][lane + 64];
         S.vcorr[wave][lane] = 0.f;
         S.vcorr[wave][lane + 64] = 0.f;
+        __builtin_amdgcn_wave_barrier();
       }
-      if constexpr (KOUT) __syncthreads();           // cleared before the next key corrections
     }
-    // next rotated queries complete; score corrections read and cleared
-    // before the next chunk adds to them (with value outliers, their
-    // barriers order this)
-    if constexpr ((ROPE || KOUT) && !VOUT) __syncthreads();
 
 #pragma unroll
     for (int i = 0; i < 2; ++i) kc[i] = kn[i];
@@ -487,13 +489,10 @@ void launch_r(const DecodeArgs& a, unsigned grid, hipStream_t s) {
 
 }  // namespace
 
-bool lut_config_supported(const kvq_config& c, int k_out_k, int k_out_v) {
-  // a chunk's outlier rows are read as one vector of 8 entries per thread:
-  // at most 64 outliers per token
+bool lut_config_supported(const kvq_config& c, int, int) {
   return c.k.quantizer == KVQ_QUANT_CODEBOOK && c.v.quantizer == KVQ_QUANT_CODEBOOK &&
          c.k.bits == 4 && c.v.bits == 4 && c.n_q_heads == c.n_kv_heads &&
-         c.k.layout == KVQ_LAYOUT_PER_TOKEN && c.v.layout == KVQ_LAYOUT_PER_TOKEN &&
-         k_out_k <= 64 && k_out_v <= 64;
+         c.k.layout == KVQ_LAYOUT_PER_TOKEN && c.v.layout == KVQ_LAYOUT_PER_TOKEN;
 }
 
 hipError_t launch_decode_lut(const DecodeArgs& a, hipStream_t s) {

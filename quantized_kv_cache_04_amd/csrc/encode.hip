@@ -425,6 +425,7 @@ __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTenso
   __shared__ uint32_t hist[4][256];
   __shared__ uint32_t sel[2];                             // digit, remaining rank
   __shared__ uint32_t wsum[4];
+  __shared__ uint32_t hcount[32];                         // kept entries per KV head
   const int n = sh.Hkv * kD;
   const int k = t.k_out;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -433,6 +434,7 @@ __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTenso
   const uint16_t* xr = static_cast<const uint16_t*>(x_new) + ((int64_t)b * sh.in_tok + sh.in_off + tn) * n;
   for (int i = tid; i < n; i += 256)
     keys[i] = ((uint32_t)(xr[i] & 0x7fffu) << 16) | (0xffffu - (uint32_t)i);
+  if (tid < 32) hcount[tid] = 0u;   // (the barriers of the passes order this)
   uint32_t prefix = 0, mask = 0, kk = (uint32_t)k;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = pass < 3 ? 23 - 8 * pass : 0;
@@ -502,8 +504,13 @@ __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTenso
       // outliers are kept in fp16: a bf16 input is rounded to nearest-even
       t.val[r * k + pos] = sh.kv_bf16 ? f2h_rn(bf2f(xr[i])) : xr[i];
       ++pos;
+      atomicAdd(&hcount[i / kD], 1u);
     }
   }
+  __syncthreads();
+  // how many of the row's entries each KV head holds
+  // (rows of 16-byte units; the padding bytes stay zero)
+  if (tid < sh.Hkv) t.hcnt[r * ((sh.Hkv + 15) / 16 * 16) + tid] = (uint8_t)hcount[tid];
   if (tid == 0) {
     // both ends of the row (every row pointer is k times its index, so
     // neighbouring tokens write equal values; in a paged cache the next

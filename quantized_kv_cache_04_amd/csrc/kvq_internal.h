@@ -39,6 +39,7 @@ struct TensorLayout {
   uint64_t rowptr_off = 0, rowptr_bytes = 0;
   uint64_t col_off = 0, col_bytes = 0;
   uint64_t val_off = 0, val_bytes = 0;
+  uint64_t hcnt_off = 0, hcnt_bytes = 0;   // outliers: uint8 [rows][Hkv] per-head counts
   uint64_t sink_off = 0, sink_bytes = 0;   // attention sink: raw [B, Hkv, sink, d]
 };
 
@@ -74,6 +75,7 @@ struct DevTensor {
   int32_t* row_ptr;
   uint16_t* col;
   uint16_t* val;
+  uint8_t* hcnt;              // outliers: entries of each CSR row per KV head [rows][Hkv]
   const uint16_t* codebook;   // fp16 [Hkv][d][16]
   const float* hscale;        // FP8: float32 scale per KV head (null = 1)
 };
@@ -149,7 +151,7 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
 bool mfma_config_supported(const kvq_config& c);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // Whether the lookup-table kernel handles this configuration (4-bit codebook
-// keys and values, one query head per KV head, at most 64 outliers per token;
+// keys and values, one query head per KV head;
 // k_out_*: outliers per token of keys and values).
 bool lut_config_supported(const kvq_config& c, int k_out_k, int k_out_v);
 // a.splits = token ranges per sequence, each of a.blocks_per_split 32-token chunks

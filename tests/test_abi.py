@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
                           "kvq_decode_attention", "kvq_last_error", "kvq_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvq_abi_version() == kvq.ABI_VERSION == 107
+    assert L.kvq_abi_version() == kvq.ABI_VERSION == 108
 
 
 def _none_cfg(**kw):
@@ -65,7 +65,7 @@ def test_layout_regions_fit_and_do_not_overlap(cfg_id):
     assert li.capacity % 32 == 0 and li.capacity >= w.ctx
     regs = []
     for t in ("k", "v"):
-        for name in ("codes", "params", "tail", "row_ptr", "col", "val"):
+        for name in ("codes", "params", "tail", "row_ptr", "col", "val", "head_count"):
             r = getattr(getattr(li, t), name)
             if r.bytes:
                 assert r.offset % 256 == 0
@@ -105,7 +105,7 @@ def test_sink_regions(cfg_id, sink):
         assert r.bytes == want
         if sink:
             assert r.offset % 256 == 0
-        for name in ("codes", "params", "tail", "row_ptr", "col", "val", "sink"):
+        for name in ("codes", "params", "tail", "row_ptr", "col", "val", "sink", "head_count"):
             rr = getattr(getattr(li, t), name)
             if rr.bytes:
                 regs.append((rr.offset, rr.offset + rr.bytes))
@@ -302,9 +302,12 @@ def test_decode_path_selection():
     assert kvq.decode_path(kvq.config_from_workload(w4, decode_path="valu")) == "valu"
     w4g = make_workload(4, n_kv_heads=2, gqa=2, ctx=64)       # codebook with a GQA group
     assert kvq.decode_path(kvq.config_from_workload(w4g)) == "valu"
-    # more than 64 outliers per token: the general kernel
+    # any number of outliers per token and of KV heads runs on the
+    # lookup-table kernel
     w4k = make_workload(4, n_kv_heads=4, ctx=64, k={"outlier_frac": 0.25})
-    assert kvq.decode_path(kvq.config_from_workload(w4k)) == "valu"
+    assert kvq.decode_path(kvq.config_from_workload(w4k)) == "lut"
+    w4o = make_workload(4, n_kv_heads=6, ctx=64)
+    assert kvq.decode_path(kvq.config_from_workload(w4o)) == "lut"
     w5 = make_workload(5, batch=1, n_kv_heads=2, ctx=256)
     assert kvq.decode_path(kvq.config_from_workload(w5)) == "mfma"
     for cfg in (kvq.config_from_workload(w5, decode_path="lut"),

@@ -129,3 +129,19 @@ def test_outlier_column_carries_the_dense_index():
     assert reg["col"][:2].tolist() == [36869, 77 | 3 << 12]
     assert reg["val"][:2].tolist() == [7.5, -6.0]
     assert reg["row_ptr"][:3].tolist() == [0, 2, 0]
+
+
+def test_outlier_counts_per_head():
+    # three heads (count rows padded to 16 bytes), three outliers per token:
+    # token 0 at columns 5 (head 0), 130 and 200 (head 1) -> counts 1, 2, 0;
+    # token 1 at columns 0, 1 (head 0) and 300 (head 2) -> counts 2, 0, 1
+    codes = np.zeros((1, 3, 2, 128), dtype=np.int64)
+    enc = {"codes": codes, "cols": np.array([[[5, 130, 200], [0, 1, 300]]]),
+           "vals": np.ones((1, 2, 3), dtype=np.float32)}
+    fmt = {"quantizer": "codebook", "bits": 4, "outlier_frac": 3 / 384}
+    reg = layout.expected_regions(fmt, enc, batch=1, n_kv_heads=3, n_ctx=2, max_ctx=32,
+                                  kv_dtype="f16", is_key=True)
+    hc = reg["head_count"]
+    assert hc.shape == (1024, 16)
+    assert hc[0].tolist() == [1, 2] + [0] * 14 and hc[1].tolist() == [2, 0, 1] + [0] * 13
+    assert not hc[2:].any()

@@ -38,22 +38,6 @@ __device__ __forceinline__ float deq_v(const DecodeArgs& a, int bh, int h, int t
   return deq_value(a.v, a.sh, bh, h, t, c);
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
-
-__device__ __forceinline__ void rope_cs(const double* theta, int dt, int i, float& cs, float& sn) {
-  const double ang = (double)dt * theta[i];
-  const double two_pi = 6.283185307179586476925286766559;
-  const double red = ang - two_pi * rint(ang / two_pi);
-  sincosf((float)red, &sn, &cs);
-}
-
 __global__ __launch_bounds__(256) void dec_generic_kernel(DecodeArgs a) {
   __shared__ float qs[JB][kD];
   __shared__ double theta[kD / 2];
@@ -96,8 +80,8 @@ __global__ __launch_bounds__(256) void dec_generic_kernel(DecodeArgs a) {
           const float k0 = deq_k(a, bh, h, t, i, n_full);
           const float k1 = deq_k(a, bh, h, t, i + kD / 2, n_full);
           if (a.rope) {
-            float cs, sn;
-            rope_cs(theta, a.pos0 + t - p, i, cs, sn);
+            const float2 r = rope_cs(theta[i], (int64_t)a.pos0 + t - p);
+            const float cs = r.x, sn = r.y;
 #pragma unroll
             for (int jj = 0; jj < JB; ++jj) {
               if (jj < nj) {
@@ -121,7 +105,7 @@ __global__ __launch_bounds__(256) void dec_generic_kernel(DecodeArgs a) {
             const int i = col & (kD / 2 - 1);
             const bool upper = col >= kD / 2;
             float cs = 1.f, sn = 0.f;
-            if (a.rope) rope_cs(theta, a.pos0 + t - p, i, cs, sn);
+            if (a.rope) { const float2 r = rope_cs(theta[i], (int64_t)a.pos0 + t - p); cs = r.x; sn = r.y; }
 #pragma unroll
             for (int jj = 0; jj < JB; ++jj) {
               if (jj < nj) {

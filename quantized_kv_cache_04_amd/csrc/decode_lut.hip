@@ -65,50 +65,6 @@ struct __align__(16) LutLds {
 // three workgroups per CU: the 160 KB of LDS is allocated in units of 1280 bytes
 static_assert(sizeof(LutLds) <= 42 * 1280, "three workgroups per CU");
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
-}
-// the pair (x[l], x[l ^ 16]) and (x[l], x[l ^ 32]) by the gfx950 row swaps
-__device__ __forceinline__ float swap16(float x) {
-  const int xi = __builtin_bit_cast(int, x);
-  auto c = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
-  return __builtin_bit_cast(float, (int)((__lane_id() & 16) ? c[0] : c[1]));
-}
-// x of lane l ^ 32
-__device__ __forceinline__ float swap_halves(float x) {
-  const int xi = __builtin_bit_cast(int, x);
-  auto c = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
-  return __builtin_bit_cast(float, (int)((__lane_id() & 32) ? c[0] : c[1]));
-}
-// maximum / sum over the wave: rotations within each row of 16, then rows
-__device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp_f<0x128>(x));   // row_ror:8
-  x = fmaxf(x, dpp_f<0x124>(x));   // row_ror:4
-  x = fmaxf(x, dpp_f<0x122>(x));   // row_ror:2
-  x = fmaxf(x, dpp_f<0x121>(x));   // row_ror:1
-  x = fmaxf(x, swap16(x));
-  return fmaxf(x, swap_halves(x));
-}
-__device__ __forceinline__ float wave_sum(float x) {
-  x += dpp_f<0x128>(x);
-  x += dpp_f<0x124>(x);
-  x += dpp_f<0x122>(x);
-  x += dpp_f<0x121>(x);
-  x += swap16(x);
-  return x + swap_halves(x);
-}
-// (cos, sin) of dt * theta, the angle formed and reduced in float64
-__device__ __forceinline__ float2 rope_cs(double theta, int64_t dt) {
-  const double ang = (double)dt * theta;
-  const double two_pi = 6.283185307179586476925286766559;
-  const double red = ang - two_pi * rint(ang / two_pi);
-  float sn, cs;
-  sincosf((float)red, &sn, &cs);
-  return make_float2(cs, sn);
-}
-
 __device__ __forceinline__ float half_lo(uint32_t w) {
   return (float)__builtin_bit_cast(half2v, w)[0];
 }

@@ -59,55 +59,6 @@ __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
-}
-
-// value of lane (lane + 8) mod 16 within each row of 16 lanes
-__device__ __forceinline__ float dpp_ror8(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
-}
-
-// Reductions over the 4 rows of 16 lanes (lanes l, l^16, l^32, l^48) with
-// the gfx950 row-swap permutes: of the pair returned by permlane{16,32}_swap
-// of (x, x), one element is x[l] and the other x[l ^ 16] (resp. 32).
-__device__ __forceinline__ float rows_max(float x) {
-  const int xi = __builtin_bit_cast(int, x);
-  auto a = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
-  x = fmaxf(__builtin_bit_cast(float, (int)a[0]), __builtin_bit_cast(float, (int)a[1]));
-  const int yi = __builtin_bit_cast(int, x);
-  auto c = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
-  return fmaxf(__builtin_bit_cast(float, (int)c[0]), __builtin_bit_cast(float, (int)c[1]));
-}
-__device__ __forceinline__ float rows_sum(float x) {
-  const int xi = __builtin_bit_cast(int, x);
-  auto a = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
-  x = __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
-  const int yi = __builtin_bit_cast(int, x);
-  auto c = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
-  return __builtin_bit_cast(float, (int)c[0]) + __builtin_bit_cast(float, (int)c[1]);
-}
-// maximum over the whole wave: rotations within each row of 16, then rows
-__device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp_f<0x128>(x));   // row_ror:8
-  x = fmaxf(x, dpp_f<0x124>(x));   // row_ror:4
-  x = fmaxf(x, dpp_f<0x122>(x));   // row_ror:2
-  x = fmaxf(x, dpp_f<0x121>(x));   // row_ror:1
-  return rows_max(x);
-}
-
-// x of lane l ^ 32 (the other half of the wave)
-__device__ __forceinline__ float swap_halves(float x) {
-  const int xi = __builtin_bit_cast(int, x);
-  auto c = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
-  const bool upper = (__lane_id() & 32) != 0;
-  return __builtin_bit_cast(float, (int)(upper ? c[0] : c[1]));
-}
-
-
 // 2^e for integer e in [-126, 127]
 __device__ __forceinline__ float pow2i(int e) {
   return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
@@ -624,7 +575,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float z = zb[u];
-      z += dpp_ror8(z);
+      z += dpp_f<0x128>(z);
       z += dpp_f<0x124>(z);
       z += dpp_f<0x122>(z);
       z += dpp_f<0x121>(z);
@@ -665,7 +616,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float x = sc[mb][r] + dpp_ror8(sc[mb][r]);
+        const float x = sc[mb][r] + dpp_f<0x128>(sc[mb][r]);
         t[mb][r] = tok_ok(mb, r) ? x : -INFINITY;
         bmax = fmaxf(bmax, t[mb][r]);
       }
@@ -839,7 +790,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
       float vb = 0.f;
 #pragma unroll
       for (int c = 0; c < NC; ++c) vb = __builtin_fmaf(vbias[gi][c], pow2i(pe_exp<VB>(c)), vb);
-      const float tot = VQ8 ? rows_sum(voff[gi] + dpp_ror8(voff[gi])) : rows_sum(vb);
+      const float tot = VQ8 ? rows_sum(voff[gi] + dpp_f<0x128>(voff[gi])) : rows_sum(vb);
 #pragma unroll
       for (int r = 0; r < 4; ++r) vb_row[gi][r] = __shfl(tot, 4 * (q4 & 1) + r, 64);
     }

@@ -233,4 +233,73 @@ __device__ inline float deq_value(const DevTensor& v, const DevShape& sh, int bh
                      prm_rec(v, sh, bh / sh.Hkv, h, t) + c / head_view(v, h).G);
 }
 
+// ---- cross-lane reductions (wave of 64 lanes) -----------------------------------
+// x of lane l + k (row rotations within each row of 16 lanes, by DPP)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// x of lane l ^ 16 and of lane l ^ 32, by the gfx950 row swaps: of the pair
+// permlane{16,32}_swap returns for (x, x), one element is x[l] and the
+// other the partner's
+__device__ __forceinline__ float swap16(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  auto c = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  return __builtin_bit_cast(float, (int)((__lane_id() & 16) ? c[0] : c[1]));
+}
+__device__ __forceinline__ float swap_halves(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  auto c = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __builtin_bit_cast(float, (int)((__lane_id() & 32) ? c[0] : c[1]));
+}
+// maximum / sum over the 4 rows of 16 lanes (lanes l, l^16, l^32, l^48);
+// both elements of a swap pair enter symmetrically, so every lane gets the
+// same bits
+__device__ __forceinline__ float rows_max(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  auto a = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  x = fmaxf(__builtin_bit_cast(float, (int)a[0]), __builtin_bit_cast(float, (int)a[1]));
+  const int yi = __builtin_bit_cast(int, x);
+  auto c = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)c[0]), __builtin_bit_cast(float, (int)c[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  auto a = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  x = __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
+  const int yi = __builtin_bit_cast(int, x);
+  auto c = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
+  return __builtin_bit_cast(float, (int)c[0]) + __builtin_bit_cast(float, (int)c[1]);
+}
+// maximum / sum over the whole wave: rotations within each row of 16, then
+// across the rows
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<0x128>(x));   // row_ror:8
+  x = fmaxf(x, dpp_f<0x124>(x));   // row_ror:4
+  x = fmaxf(x, dpp_f<0x122>(x));   // row_ror:2
+  x = fmaxf(x, dpp_f<0x121>(x));   // row_ror:1
+  return rows_max(x);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f<0x128>(x);
+  x += dpp_f<0x124>(x);
+  x += dpp_f<0x122>(x);
+  x += dpp_f<0x121>(x);
+  return rows_sum(x);
+}
+
+// ---- rotary embedding --------------------------------------------------------------
+// (cos, sin) of the rotation by dt * theta.  The angle is formed and reduced
+// to [-pi, pi] in float64, so that no error grows with the position, and
+// only the reduced angle goes through the float32 sincosf.
+__device__ __forceinline__ float2 rope_cs(double theta, int64_t dt) {
+  const double ang = (double)dt * theta;
+  const double two_pi = 6.283185307179586476925286766559;
+  const double red = ang - two_pi * rint(ang / two_pi);
+  float sn, cs;
+  sincosf((float)red, &sn, &cs);
+  return make_float2(cs, sn);
+}
+
 }  // namespace kvq

@@ -83,12 +83,6 @@ __device__ __forceinline__ void split8(const float x[8], uint4& hi, uint4& lo) {
 
 __device__ __forceinline__ half8 as_h8(uint4 v) { return __builtin_bit_cast(half8, v); }
 
-__device__ __forceinline__ void rope_cs(double theta, int64_t pos, float& cs, float& sn) {
-  const double ang = (double)pos * theta;
-  const double two_pi = 6.283185307179586476925286766559;
-  sincosf((float)(ang - two_pi * rint(ang / two_pi)), &sn, &cs);
-}
-
 // rotation by the sum of two angles given as (cos, sin) pairs
 __device__ __forceinline__ void rot_add(float2 a, float2 b, float& cs, float& sn) {
   cs = a.x * b.x - a.y * b.y;
@@ -297,9 +291,7 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
   if (a.rope) {
     __syncthreads();
     for (int idx = tid; idx < kBlk * (kD / 2); idx += 256) {
-      float cs, sn;
-      rope_cs(S.theta[idx % (kD / 2)], idx / (kD / 2), cs, sn);
-      S.rt[idx / (kD / 2)][idx % (kD / 2)] = float2{cs, sn};
+      S.rt[idx / (kD / 2)][idx % (kD / 2)] = rope_cs(S.theta[idx % (kD / 2)], idx / (kD / 2));
     }
   }
   if (fmt_kind<KF>(a.k) == KVQ_QUANT_CODEBOOK)
@@ -337,8 +329,8 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float cs, sn;
-          rope_cs(S.theta[32 * ks + 8 * q4 + e], p_row, cs, sn);
+          const float2 r = rope_cs(S.theta[32 * ks + 8 * q4 + e], p_row);
+          const float cs = r.x, sn = r.y;
           const float x0 = x[ks][e], x1 = x[ks + 2][e];
           x[ks][e] = x0 * cs - x1 * sn;
           x[ks + 2][e] = x1 * cs + x0 * sn;
@@ -487,9 +479,7 @@ __global__ __launch_bounds__(256, 2) void pre_mfma_kernel(PrefillArgs a) {
   // (cos, sin) of the first position of block blk into rb[blk & 1]
   auto base_rot = [&](int blk) {
     if (a.rope && blk < n_blk && tid < kD / 2) {
-      float cs, sn;
-      rope_cs(S.theta[tid], desc(blk).t0, cs, sn);
-      S.rb[blk & 1][tid] = float2{cs, sn};
+      S.rb[blk & 1][tid] = rope_cs(S.theta[tid], desc(blk).t0);
     }
   };
   // this workgroup's split of the blocks

@@ -172,15 +172,23 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
   // also on a page of a paged cache); chunks past the end read the last one
   // (a paged cache's table is read one chunk ahead of the loads: chunk_row)
   auto chunk_row = [&](int t0) { return tok_row(a.sh, b, hr, min(t0, last_tile)); };
+  // Addresses are a wave-uniform base plus a 32-bit lane offset, so that
+  // the loads take their base from scalar registers; the empty asm keeps the
+  // compiler from folding the lane offset into a per-lane 64-bit pointer
+  // held across the loop.
+  auto at = [](const uint8_t* base, uint32_t off) {
+    asm volatile("" : "+v"(off));
+    return base + off;
+  };
   auto load_k = [&](int t0, int64_t rowc, u32x4* kk) {
     const int tk = min(t0 + tau, nctx - 1);
-    const int64_t row = rowc + (tk - min(t0, last_tile));
-    const u32x4* kr = reinterpret_cast<const u32x4*>(K.codes + row * 64) + 2 * half;
+    const uint32_t off = (uint32_t)(tk - min(t0, last_tile)) * 64u + (uint32_t)half * 32u;
+    const u32x4* kr = reinterpret_cast<const u32x4*>(at(K.codes + rowc * 64, off));
     kk[0] = kr[0];
     kk[1] = kr[1];
   };
   auto load_v = [&](int64_t rowc, u32x4* vv) {
-    const u32x4* vr = reinterpret_cast<const u32x4*>(V.codes + rowc * 64 + lane * 32);
+    const u32x4* vr = reinterpret_cast<const u32x4*>(at(V.codes + rowc * 64, (uint32_t)lane * 32u));
     vv[0] = vr[0];
     vv[1] = vr[1];
   };
@@ -203,8 +211,9 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
   // 16-byte loads cover 32 heads; the second only for heads 16 and up)
   struct Cnt { uint32_t w[8]; };
   auto load_cnt = [&](const DevTensor& T, int64_t row0, int nt, Cnt& c) {
-    const int64_t r = row0 + min(tau, nt - 1);
-    const u32x4* p = reinterpret_cast<const u32x4*>(T.hcnt + r * ((Hkv + 15) / 16 * 16));
+    const int stride = (Hkv + 15) / 16 * 16;
+    const u32x4* p = reinterpret_cast<const u32x4*>(at(T.hcnt + row0 * stride,
+                                                       (uint32_t)(min(tau, nt - 1) * stride)));
     const u32x4 a0 = p[0];
     const u32x4 a1 = hq >= 4 ? p[1] : u32x4{0u, 0u, 0u, 0u};
     c.w[0] = a0.x; c.w[1] = a0.y; c.w[2] = a0.z; c.w[3] = a0.w;

@@ -81,17 +81,22 @@ def test_both_decode_kernels_agree_with_oracle(name, cfg_id, over, chunks):
 LUT_CASES = [
     ("lut_nuq_4heads", dict(n_kv_heads=4, ctx=700), [700], 0),
     ("lut_nuq_32heads_chunks", dict(ctx=300), [100, 1, 199], 0),
-    # 41 outliers per token over 47 chunks of 32 tokens (rows straddle the
-    # 8-entry vectors)
+    # 41 outliers per token over 47 chunks of 32 tokens, about 41 entries of
+    # each head per chunk
     ("lut_32heads_multichunk", dict(ctx=1500), [1500], 0),
     # one range of 129 chunks: the query rotation is evaluated exactly at
-    # chunks 32, 64, 96 and 128, and the last chunk holds a single token;
-    # with 4 heads every outlier belongs to the one head group, so compaction
-    # steps overflow the ring and apply entries in place
+    # chunks 32, 64, 96 and 128, and the last chunk holds a single token
     ("lut_one_range_resync", dict(n_kv_heads=4, ctx=4097), [4097], 1),
     # 6 KV heads with outliers and RoPE: the two empty waves of the second
-    # group still load and filter outlier vectors
+    # group list no entries
     ("lut_6heads_outliers_rope", dict(n_kv_heads=6, ctx=400), [400], 2),
+    # lists longer than a wave: 13 outliers per token over 2 heads (about
+    # 200 entries of a head per chunk, taken 64 at a time)
+    ("lut_long_outlier_lists", dict(n_kv_heads=2, ctx=500, k=dict(outlier_frac=0.05),
+                                    v=dict(outlier_frac=0.05)), [500], 2),
+    # one head, a quarter of its values outliers: 1024 entries per chunk
+    ("lut_one_head_quarter_outliers", dict(n_kv_heads=1, ctx=300, k=dict(outlier_frac=0.25),
+                                           v=dict(outlier_frac=0.25)), [250, 50], 0),
     # 6 KV heads: the second group of 4 has two empty waves
     ("lut_no_outliers_no_rope", dict(n_kv_heads=6, ctx=333, rope=False,
                                      k=dict(outlier_frac=0.0), v=dict(outlier_frac=0.0)), [333], 0),

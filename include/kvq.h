@@ -73,8 +73,8 @@ typedef int32_t kvq_status;
  * CODEBOOK: 4-bit index of the nearest of 16 fp16 centroids of that
  *   (kv head, channel), ties to the lower index; optionally the
  *   ceil(outlier_frac * n_kv_heads * head_dim) entries of largest |x| of each
- *   token are kept in fp16 (CSR; n_kv_heads * head_dim <= 4096; with a
- *   count of each row's entries per KV head) and replace the dense value
+ *   token are kept in fp16 (CSR; n_kv_heads * head_dim <= 4096; with the
+ *   end of each KV head's entries in each row) and replace the dense value
  *   [KVQuant page 2.2, 3.3].  The int32 row pointers bound the capacity:
  *   (batch * Tcap + 1) * outliers per token must not exceed 2^31 - 1
  *   (KVQ_ERR_UNSUPPORTED otherwise).
@@ -232,12 +232,12 @@ typedef struct kvq_tensor_regions {
                           12-15 the dense codebook index at that position  */
   kvq_region val;      /* outliers: fp16 value                              */
   kvq_region sink;     /* attention sink: kv_dtype [B, Hkv, sink_tokens, d] */
-  kvq_region head_count; /* outliers: uint8 [rows][round_up(Hkv, 16)], the
-                          number of a CSR row's entries that fall in each KV
-                          head, zero-padded to 16-byte rows (the row's
-                          entries of head h are its entries
-                          sum(count[0 .. h-1]) .. + count[h]: the segment a
-                          kernel serving one head reads)                  */
+  kvq_region head_end; /* outliers: uint16 [rows][round_up(Hkv, 8)]: entry
+                          h of a CSR row is the number of the row's entries
+                          that fall in KV heads 0 .. h, zero-padded to
+                          16-byte rows (the row's entries of head h are its
+                          entries end[h-1] .. end[h] - 1, end[-1] = 0: the
+                          segment a kernel serving one head reads)        */
 } kvq_tensor_regions;
 
 typedef struct kvq_layout_info {
@@ -444,7 +444,8 @@ const char* kvq_last_error(void);
    106 adds the paged cache (kvq_config.page_pool, kvq_cache.page_table,
    kvq_layout_info.pages_per_seq); 107 adds kvq_tensor_format.window_overlap
    and head_group_size; 108 adds the per-head outlier counts
-   (kvq_tensor_regions.head_count). */
+   (kvq_tensor_regions.head_count); 109 replaces them by per-head end
+   offsets (kvq_tensor_regions.head_end). */
 int32_t kvq_abi_version(void);
 
 #ifdef __cplusplus

@@ -183,10 +183,10 @@ def expected_regions(fmt: Dict, enc: Dict[str, np.ndarray], *, batch: int, n_kv_
       [B, H, Tcap // G, d, 2];
     * ``tail`` (per-channel): [B, H, G, d] raw bits of the unfinished group
       (uint16), zero beyond it;
-    * ``head_count`` uint8 [B * Tcap, round_up(H, 16)]: of each CSR row's k
-      entries, how many lie in each KV head, zero-padded to 16 bytes (a
-      row's entries of head h are then the ones after the counts of heads
-      0 .. h-1);
+    * ``head_end`` uint16 [B * Tcap, round_up(H, 8)]: for each CSR row and
+      KV head h, how many of the row's k entries lie in heads 0 .. h (rows
+      zero-padded to 16 bytes); the row's entries of head h are then its
+      entries head_end[h - 1] .. head_end[h] - 1 (head_end[-1] = 0);
     * ``row_ptr`` int32 [B * Tcap + 1], ``col`` uint16 and ``val`` fp16
       [B * Tcap * k]: CSR over rows r = b * Tcap + t, with
       row_ptr[b * Tcap + t] = k * (b * Tcap + t) for t = 0..n_ctx; a column
@@ -254,14 +254,14 @@ def expected_regions(fmt: Dict, enc: Dict[str, np.ndarray], *, batch: int, n_kv_
         out["row_ptr"] = row_ptr.astype(np.int32)
         out["col"] = col
         out["val"] = val
-        # entries of each row per KV head: how many of the row's columns
-        # h * d + c fall in head h
-        # (rows padded with zero bytes to whole 16-byte units)
-        hc = np.zeros((B * Tcap, (H + 15) // 16 * 16), dtype=np.uint8)
+        # end of each KV head's entries in each row: how many of the row's
+        # columns h * d + c fall in heads 0 .. h
+        # (rows padded with zeros to whole 16-byte units)
+        he = np.zeros((B * Tcap, (H + 7) // 8 * 8), dtype=np.uint16)
         for b in range(B):
             for t in range(n_ctx):
-                hc[b * Tcap + t, :H] = np.bincount(cols[b, t] // D, minlength=H)
-        out["head_count"] = hc
+                he[b * Tcap + t, :H] = np.cumsum(np.bincount(cols[b, t] // D, minlength=H))
+        out["head_end"] = he
     return out
 
 

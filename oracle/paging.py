@@ -108,7 +108,7 @@ def paged_regions(regions: Dict[str, np.ndarray], table: np.ndarray, *, n_pages:
                     rp[r] = k_out * r
                     rp[r + 1] = k_out * (r + 1)
             out[name] = rp.astype(np.int32)
-        elif name == "head_count":
+        elif name == "head_end":
             src = img.reshape(B, capacity, -1)
             dst = np.zeros((n_pages * PAGE, src.shape[2]), dtype=img.dtype)
             for b in range(B):

@@ -28,7 +28,7 @@
 //    per (centroid, lane) holds both channels' centroids, so lane l always
 //    reads bank l;
 //  * outliers: a token's CSR row holds its outliers over all heads in
-//    column order, with a count per head; each wave reads only its head's
+//    column order, with an end offset per head; each wave reads only its head's
 //    entries (the lanes of a token share them) and adds (val - centroid)
 //    corrections to the token's score for keys and, through the wave's LDS
 //    channel sums, to the value sums.  Waves of a workgroup never wait for
@@ -198,39 +198,28 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
 
   // ---- dense-and-sparse outliers ---------------------------------------------------------
   // The CSR row of a token holds its outliers over all heads in column order,
-  // and the row's count per KV head says where each head's entries lie: the
-  // wave's head h finds its entries of token tau at sum(count[0 .. h-1]) ..
-  // + count[h] and reads only those.  Lanes (tau, 0) and (tau, 1) take the
-  // even and the odd ones.  The counts of a chunk are loaded one chunk ahead
-  // and its entries before its key phase, so their latency hides under the
-  // lookups; no workgroup barrier is involved.
+  // and the row's end offset per KV head says where each head's entries lie:
+  // the wave's head h finds its entries of token tau at end[h-1] .. end[h]
+  // - 1 and reads only those.  Lanes (tau, 0) and (tau, 1) take the even and
+  // the odd ones.  The offsets of a chunk are loaded one chunk ahead and its
+  // entries before its key phase, so their latency hides under the lookups;
+  // no workgroup barrier is involved.
   constexpr int kEnt = 4;                        // entries a lane loads ahead per tensor
-  const int hq = hr >> 2, hb = hr & 3;           // head's count dword and byte
-  const uint32_t lo_mask = hb == 0 ? 0u : (0x01010101u >> (8 * (4 - hb)));
-  // a row's counts: one byte per head, rows of whole 16-byte units (two
-  // 16-byte loads cover 32 heads; the second only for heads 16 and up)
-  struct Cnt { uint32_t w[8]; };
+  // the head's two end offsets in the row of token tau (rows of round_up(Hkv,
+  // 8) entries): the end of the heads before it and its own
+  struct Cnt { uint32_t lo, hi; };
   auto load_cnt = [&](const DevTensor& T, int64_t row0, int nt, Cnt& c) {
-    const int stride = (Hkv + 15) / 16 * 16;
-    const u32x4* p = reinterpret_cast<const u32x4*>(at(T.hcnt + row0 * stride,
-                                                       (uint32_t)(min(tau, nt - 1) * stride)));
-    const u32x4 a0 = p[0];
-    const u32x4 a1 = hq >= 4 ? p[1] : u32x4{0u, 0u, 0u, 0u};
-    c.w[0] = a0.x; c.w[1] = a0.y; c.w[2] = a0.z; c.w[3] = a0.w;
-    c.w[4] = a1.x; c.w[5] = a1.y; c.w[6] = a1.z; c.w[7] = a1.w;
+    const int stride = (Hkv + 7) / 8 * 8;
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(
+        at(reinterpret_cast<const uint8_t*>(T.hend + row0 * stride + hr),
+           (uint32_t)(min(tau, nt - 1) * stride * 2)));
+    c.hi = p[0];
+    c.lo = hr > 0 ? (uint32_t)p[-1] : 0u;
   };
   // first entry and number of entries of head hr in the row
   auto seg = [&](const Cnt& c, int& first, int& num) {
-    uint32_t acc = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < hq) acc = __builtin_amdgcn_udot4(c.w[j], 0x01010101u, acc, false);
-    uint32_t wq = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j == hq) wq = c.w[j];
-    first = (int)__builtin_amdgcn_udot4(wq, lo_mask, acc, false);
-    num = (int)((wq >> (8 * hb)) & 0xffu);
+    first = (int)c.lo;
+    num = (int)c.hi - (int)c.lo;
   };
   // an entry's column and value as the two halves of one register
   typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));

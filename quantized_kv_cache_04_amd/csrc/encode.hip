@@ -508,9 +508,13 @@ __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTenso
     }
   }
   __syncthreads();
-  // how many of the row's entries each KV head holds
-  // (rows of 16-byte units; the padding bytes stay zero)
-  if (tid < sh.Hkv) t.hcnt[r * ((sh.Hkv + 15) / 16 * 16) + tid] = (uint8_t)hcount[tid];
+  // where each KV head's entries of the row end: the number of its entries
+  // in heads 0 .. tid (rows of 16-byte units; the padding stays zero)
+  if (tid < sh.Hkv) {
+    uint32_t end = 0;
+    for (int hh = 0; hh <= tid; ++hh) end += hcount[hh];
+    t.hend[r * ((sh.Hkv + 7) / 8 * 8) + tid] = (uint16_t)end;
+  }
   if (tid == 0) {
     // both ends of the row (every row pointer is k times its index, so
     // neighbouring tokens write equal values; in a paged cache the next

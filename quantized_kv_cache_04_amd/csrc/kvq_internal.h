@@ -39,7 +39,7 @@ struct TensorLayout {
   uint64_t rowptr_off = 0, rowptr_bytes = 0;
   uint64_t col_off = 0, col_bytes = 0;
   uint64_t val_off = 0, val_bytes = 0;
-  uint64_t hcnt_off = 0, hcnt_bytes = 0;   // outliers: uint8 [rows][Hkv] per-head counts
+  uint64_t hend_off = 0, hend_bytes = 0;   // outliers: uint16 [rows][round_up(Hkv, 8)] per-head ends
   uint64_t sink_off = 0, sink_bytes = 0;   // attention sink: raw [B, Hkv, sink, d]
 };
 
@@ -75,7 +75,7 @@ struct DevTensor {
   int32_t* row_ptr;
   uint16_t* col;
   uint16_t* val;
-  uint8_t* hcnt;              // outliers: entries of each CSR row per KV head [rows][Hkv]
+  uint16_t* hend;             // outliers: end of each KV head's entries in each CSR row
   const uint16_t* codebook;   // fp16 [Hkv][d][16]
   const float* hscale;        // FP8: float32 scale per KV head (null = 1)
 };

@@ -104,7 +104,7 @@ def compare_regions(cache: kvq.Cache, expected) -> List[str]:
         exp = expected[name]
         if exp is None:
             continue
-        for reg in ("codes", "params", "tail", "row_ptr", "col", "val", "sink", "head_count"):
+        for reg in ("codes", "params", "tail", "row_ptr", "col", "val", "sink", "head_end"):
             if reg not in exp:
                 continue
             got = cache.region(name, reg).cpu().numpy()

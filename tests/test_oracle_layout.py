@@ -131,17 +131,18 @@ def test_outlier_column_carries_the_dense_index():
     assert reg["row_ptr"][:3].tolist() == [0, 2, 0]
 
 
-def test_outlier_counts_per_head():
-    # three heads (count rows padded to 16 bytes), three outliers per token:
-    # token 0 at columns 5 (head 0), 130 and 200 (head 1) -> counts 1, 2, 0;
-    # token 1 at columns 0, 1 (head 0) and 300 (head 2) -> counts 2, 0, 1
+def test_outlier_head_ends():
+    # three heads (rows padded to 8 entries), three outliers per token:
+    # token 0 at columns 5 (head 0), 130 and 200 (head 1) -> counts 1, 2, 0,
+    # ends 1, 3, 3; token 1 at columns 0, 1 (head 0) and 300 (head 2) ->
+    # counts 2, 0, 1, ends 2, 2, 3
     codes = np.zeros((1, 3, 2, 128), dtype=np.int64)
     enc = {"codes": codes, "cols": np.array([[[5, 130, 200], [0, 1, 300]]]),
            "vals": np.ones((1, 2, 3), dtype=np.float32)}
     fmt = {"quantizer": "codebook", "bits": 4, "outlier_frac": 3 / 384}
     reg = layout.expected_regions(fmt, enc, batch=1, n_kv_heads=3, n_ctx=2, max_ctx=32,
                                   kv_dtype="f16", is_key=True)
-    hc = reg["head_count"]
-    assert hc.shape == (1024, 16)
-    assert hc[0].tolist() == [1, 2] + [0] * 14 and hc[1].tolist() == [2, 0, 1] + [0] * 13
-    assert not hc[2:].any()
+    he = reg["head_end"]
+    assert he.shape == (1024, 8) and he.dtype == np.uint16
+    assert he[0].tolist() == [1, 3, 3] + [0] * 5 and he[1].tolist() == [2, 2, 3] + [0] * 5
+    assert not he[2:].any()

@@ -73,8 +73,9 @@ typedef int32_t kvq_status;
  * CODEBOOK: 4-bit index of the nearest of 16 fp16 centroids of that
  *   (kv head, channel), ties to the lower index; optionally the
  *   ceil(outlier_frac * n_kv_heads * head_dim) entries of largest |x| of each
- *   token are kept in fp16 (CSR; n_kv_heads * head_dim <= 4096; with the
- *   end of each KV head's entries in each row) and replace the dense value
+ *   token are kept in fp16 (CSR; n_kv_heads * head_dim <= 4096; with a
+ *   per-tile index of the same entries grouped by KV head, which decode
+ *   reads) and replace the dense value
  *   [KVQuant page 2.2, 3.3].  The int32 row pointers bound the capacity:
  *   (batch * Tcap + 1) * outliers per token must not exceed 2^31 - 1
  *   (KVQ_ERR_UNSUPPORTED otherwise).
@@ -232,12 +233,16 @@ typedef struct kvq_tensor_regions {
                           12-15 the dense codebook index at that position  */
   kvq_region val;      /* outliers: fp16 value                              */
   kvq_region sink;     /* attention sink: kv_dtype [B, Hkv, sink_tokens, d] */
-  kvq_region head_end; /* outliers: uint16 [rows][round_up(Hkv, 8)]: entry
-                          h of a CSR row is the number of the row's entries
-                          that fall in KV heads 0 .. h, zero-padded to
-                          16-byte rows (the row's entries of head h are its
-                          entries end[h-1] .. end[h] - 1, end[-1] = 0: the
-                          segment a kernel serving one head reads)        */
+  kvq_region tile_off; /* outliers: uint16 [rows / 32][round_up(Hkv + 1, 8)]:
+                          for the tile of 32 CSR rows (32 tokens; a page of
+                          a paged cache), where KV head h's entries start in
+                          the tile's block of tile_ent; [Hkv] the tile's
+                          count; zero padding                             */
+  kvq_region tile_ent; /* outliers: uint32 [rows / 32][32 * k]: the tile's
+                          entries grouped by KV head, each head's in token
+                          order (a token's in column order): bits 0-6
+                          channel, 7-11 token in the tile, 12-15 the dense
+                          index replaced, 16-31 the fp16 value            */
 } kvq_tensor_regions;
 
 typedef struct kvq_layout_info {
@@ -257,8 +262,8 @@ typedef struct kvq_layout_info {
 /*
  * kvq_cache_bytes -- size of the cache.  Host only; touches no device.
  *   what = KVQ_BYTES_PAYLOAD: bytes that hold n_ctx tokens (packed codes,
- *     scale/zero parameters, the unquantized per-channel tail, CSR outliers,
- *     codebooks), times n_layers.  With NONE for both tensors this is
+ *     scale/zero parameters, the unquantized per-channel tail, outliers as
+ *     the per-tile index that decode streams, codebooks), times n_layers.  With NONE for both tensors this is
  *     exactly 2 * n_layers * n_kv_heads * head_dim * 2 * n_ctx * batch, the
  *     per-token formula of the TurboQuant page (section 2.1), which gives
  *     327,680 bytes per token for Llama-2-70B (L = 80, h = 8, d = 128).
@@ -298,7 +303,7 @@ kvq_status kvq_cache_bytes(const kvq_config* cfg, int64_t n_ctx, int64_t n_layer
  *     [P][Hkv][32] token rows instead of [B][Hkv][Tcap]: token t of
  *     sequence b, head h is row (page_table[b][t / 32] * Hkv + h) * 32 +
  *     t % 32.  The outlier CSR has P * 32 rows (row page * 32 + t % 32;
- *     row_ptr [P * 32 + 1]).  Per-channel params, tail and sink keep their
+ *     row_ptr [P * 32 + 1]) and the per-tile index one tile per page.  Per-channel params, tail and sink keep their
  *     per-sequence shapes.
  * Errors: as kvq_cache_bytes.
  */
@@ -445,7 +450,8 @@ const char* kvq_last_error(void);
    kvq_layout_info.pages_per_seq); 107 adds kvq_tensor_format.window_overlap
    and head_group_size; 108 adds the per-head outlier counts
    (kvq_tensor_regions.head_count); 109 replaces them by per-head end
-   offsets (kvq_tensor_regions.head_end). */
+   offsets (kvq_tensor_regions.head_end); 110 replaces those by the
+   per-tile index (kvq_tensor_regions.tile_off, tile_ent). */
 int32_t kvq_abi_version(void);
 
 #ifdef __cplusplus

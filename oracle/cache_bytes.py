@@ -37,9 +37,10 @@ def tensor_payload(fmt: Dict, *, batch: int, n_kv_heads: int, head_dim: int, n_c
         total = B * H * n * rb + H * d * 16 * 2
         k = outlier_count(fmt.get("outlier_frac", 0.0), H * d)
         if k:
-            # row pointer, k (column, value) pairs, a two-byte end offset per
-            # head (rows of whole 16-byte units)
-            total += B * n * (4 + 4 * k + (H + 7) // 8 * 16)
+            # the per-tile index decode streams: 4 bytes per entry, and the
+            # head offsets of each tile the n tokens touch (rows of whole
+            # 16-byte units)
+            total += B * (n * 4 * k + (n + 31) // 32 * ((H + 8) // 8 * 16))
         return total
     if fmt.get("layout", "per_token") == "per_channel":
         nf = (n // G) * G

@@ -183,10 +183,9 @@ def expected_regions(fmt: Dict, enc: Dict[str, np.ndarray], *, batch: int, n_kv_
       [B, H, Tcap // G, d, 2];
     * ``tail`` (per-channel): [B, H, G, d] raw bits of the unfinished group
       (uint16), zero beyond it;
-    * ``head_end`` uint16 [B * Tcap, round_up(H, 8)]: for each CSR row and
-      KV head h, how many of the row's k entries lie in heads 0 .. h (rows
-      zero-padded to 16 bytes); the row's entries of head h are then its
-      entries head_end[h - 1] .. head_end[h] - 1 (head_end[-1] = 0);
+    * ``tile_off`` uint16 [B * Tcap / 32, round_up(H + 1, 8)] and
+      ``tile_ent`` uint32 [B * Tcap / 32, 32 k]: the outliers of each tile
+      of 32 tokens grouped by KV head (``outlier_tiles``);
     * ``row_ptr`` int32 [B * Tcap + 1], ``col`` uint16 and ``val`` fp16
       [B * Tcap * k]: CSR over rows r = b * Tcap + t, with
       row_ptr[b * Tcap + t] = k * (b * Tcap + t) for t = 0..n_ctx; a column
@@ -254,15 +253,49 @@ def expected_regions(fmt: Dict, enc: Dict[str, np.ndarray], *, batch: int, n_kv_
         out["row_ptr"] = row_ptr.astype(np.int32)
         out["col"] = col
         out["val"] = val
-        # end of each KV head's entries in each row: how many of the row's
-        # columns h * d + c fall in heads 0 .. h
-        # (rows padded with zeros to whole 16-byte units)
-        he = np.zeros((B * Tcap, (H + 7) // 8 * 8), dtype=np.uint16)
-        for b in range(B):
-            for t in range(n_ctx):
-                he[b * Tcap + t, :H] = np.cumsum(np.bincount(cols[b, t] // D, minlength=H))
-        out["head_end"] = he
+        out["tile_off"], out["tile_ent"] = outlier_tiles(
+            cols, np.asarray(enc["vals"]), dense, batch=B, n_kv_heads=H, capacity=Tcap, n_ctx=n_ctx)
     return out
+
+
+def outlier_tiles(cols: np.ndarray, vals: np.ndarray, dense: np.ndarray, *, batch: int,
+                  n_kv_heads: int, capacity: int, n_ctx: int):
+    """Per-tile index of the outliers (this library's layout; the pages
+    keep outliers in CSR without fixing a byte layout -- KVQuant page,
+    section 3.3).  For tile j of sequence b (tokens 32 j .. 32 j + 31) and
+    KV head h, the entries of its tokens in token order, each token's in
+    column order, one uint32 each: channel c (bits 0-6), token in the tile
+    (7-11), dense codebook index replaced (12-15), fp16 value bits (16-31).
+    ``tile_off[tile, h]`` is where head h's entries start in the tile's
+    block of 32 k entries, ``tile_off[tile, H]`` the tile's count; rows of
+    round_up(H + 1, 8) entries, tiles b * capacity / 32 + j.
+
+    ``cols`` [B, n_ctx, k] (columns h * d + c, ascending per token),
+    ``vals`` [B, n_ctx, k], ``dense`` [B, H, n_ctx, d] codebook indices."""
+    B, H = batch, n_kv_heads
+    k = cols.shape[-1]
+    ntile = capacity // 32
+    o_row = (H + 8) // 8 * 8
+    toff = np.zeros((B * ntile, o_row), dtype=np.uint16)
+    tent = np.zeros((B * ntile, 32 * k), dtype=np.uint32)
+    vbits = np.asarray(vals, dtype=np.float32).astype(np.float16).view(np.uint16).astype(np.uint32)
+    for b in range(B):
+        for j in range((n_ctx + 31) // 32):
+            lists = [[] for _ in range(H)]
+            for t in range(32 * j, min(32 * j + 32, n_ctx)):
+                for e in range(k):
+                    col = int(cols[b, t, e])
+                    h, c = col // D, col % D
+                    code = int(dense[b, h, t, c])
+                    lists[h].append(c | ((t - 32 * j) << 7) | (code << 12) | (int(vbits[b, t, e]) << 16))
+            row = b * ntile + j
+            off = 0
+            for h in range(H):
+                toff[row, h] = off
+                tent[row, off:off + len(lists[h])] = lists[h]
+                off += len(lists[h])
+            toff[row, H] = off
+    return toff, tent
 
 
 def per_head_params(fmt: Dict, enc: Dict, B: int, H: int, Tcap: int, n_ctx: int) -> np.ndarray:

@@ -18,7 +18,8 @@ page gives the block size and the block table, not a byte layout):
   ``(b * H + h) * Tcap + t``; a value tile is 32 consecutive rows either way;
 * the outlier CSR (one row per token, all heads) holds token t of sequence b
   at row ``table[b][t // 32] * 32 + t % 32``, and row_ptr[r] = k * r at both
-  ends of every written row;
+  ends of every written row; the per-tile outlier index has one tile per
+  page;
 * per-channel key parameters, the unquantized key tail and the attention
   sink keep their per-sequence arrays.
 
@@ -108,12 +109,13 @@ def paged_regions(regions: Dict[str, np.ndarray], table: np.ndarray, *, n_pages:
                     rp[r] = k_out * r
                     rp[r + 1] = k_out * (r + 1)
             out[name] = rp.astype(np.int32)
-        elif name == "head_end":
-            src = img.reshape(B, capacity, -1)
-            dst = np.zeros((n_pages * PAGE, src.shape[2]), dtype=img.dtype)
+        elif name in ("tile_off", "tile_ent"):
+            # one tile of the per-tile outlier index per page
+            src = img.reshape(B, npg, -1)
+            dst = np.zeros((n_pages, src.shape[2]), dtype=img.dtype)
             for b in range(B):
-                for t in range(n_ctx):
-                    dst[csr_row(table, b, t)] = src[b, t]
+                for i in range(used):
+                    dst[table[b][i]] = src[b, i]
             out[name] = dst
         elif name in ("col", "val"):
             src = img.reshape(B, capacity, k_out)

@@ -197,71 +197,39 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
   load_k(t_begin, row_c, kc);
 
   // ---- dense-and-sparse outliers ---------------------------------------------------------
-  // The CSR row of a token holds its outliers over all heads in column order,
-  // and the row's end offset per KV head says where each head's entries lie:
-  // the wave's head h finds its entries of token tau at end[h-1] .. end[h]
-  // - 1 and reads only those.  Lanes (tau, 0) and (tau, 1) take the even and
-  // the odd ones.  The offsets of a chunk are loaded one chunk ahead and its
-  // entries before its key phase, so their latency hides under the lookups;
-  // no workgroup barrier is involved.
-  constexpr int kEnt = 4;                        // entries a lane loads ahead per tensor
-  // the head's two end offsets in the row of token tau (rows of round_up(Hkv,
-  // 8) entries): the end of the heads before it and its own
-  struct Cnt { uint32_t lo, hi; };
-  auto load_cnt = [&](const DevTensor& T, int64_t row0, int nt, Cnt& c) {
-    const int stride = (Hkv + 7) / 8 * 8;
-    const uint16_t* p = reinterpret_cast<const uint16_t*>(
-        at(reinterpret_cast<const uint8_t*>(T.hend + row0 * stride + hr),
-           (uint32_t)(min(tau, nt - 1) * stride * 2)));
-    c.hi = p[0];
-    c.lo = hr > 0 ? (uint32_t)p[-1] : 0u;
+  // A tile of 32 tokens (one chunk) indexes its outliers by KV head: the
+  // wave's head h finds its entries of the chunk, in token order, at
+  // off[h] .. off[h + 1] - 1 of the tile's block (offsets read with scalar
+  // loads).  Lane j takes entry j; lists longer than 64 entries are taken
+  // 64 at a time.  An entry is one dword: channel (bits 0-6), token in the
+  // tile (7-11), the dense index it replaces (12-15) and its fp16 value
+  // (16-31).  The key entries of a chunk load at its start, the value
+  // entries after its key phase; no workgroup barrier is involved.
+  typedef __attribute__((address_space(4))) const uint32_t const_u32;
+  const int o_row = (Hkv + 8) / 8 * 8;           // offsets per tile: round_up(Hkv + 1, 8)
+  struct Lst { uint32_t ent; int n; int64_t base, blk; };
+  // entry base + i of the list (i < n; any other lane reads the tile's first)
+  auto ent_at = [&](const DevTensor& T, const Lst& L, int i) -> uint32_t {
+    const int64_t e = i < L.n ? L.base + i : L.blk;
+    return T.tent[e];
   };
-  // first entry and number of entries of head hr in the row
-  auto seg = [&](const Cnt& c, int& first, int& num) {
-    first = (int)c.lo;
-    num = (int)c.hi - (int)c.lo;
+  auto make_list = [&](const DevTensor& T, int64_t row0, Lst& L) {
+    const int64_t tile = row0 >> 5;
+    const const_u32* o = (const const_u32*)(T.toff + tile * o_row);
+    const uint32_t w0 = o[hr >> 1], w1 = o[(hr + 1) >> 1];
+    const uint32_t a0 = (hr & 1) ? (w0 >> 16) : (w0 & 0xffffu);
+    const uint32_t a1 = (hr & 1) ? (w1 & 0xffffu) : (w0 >> 16);
+    L.n = head_ok ? (int)(a1 - a0) : 0;
+    L.blk = tile * ((int64_t)kTile * T.k_out);
+    L.base = L.blk + a0;
+    L.ent = ent_at(T, L, lane);
   };
-  // an entry's column and value as the two halves of one register
-  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-  struct Ent { u16x2 cv[kEnt]; int first, num; };
-  auto find_ent = [&](const Cnt& c, int nt, Ent& e) {
-    seg(c, e.first, e.num);
-    if (tau >= nt || !head_ok) e.num = 0;
+  // f(entry, valid) for every entry of the list, 64 at a time (every lane
+  // takes part in each call)
+  auto for_list = [&](const DevTensor& T, const Lst& L, auto&& f) {
+    f(L.ent, lane < L.n);
+    for (int i0 = 64; i0 < L.n; i0 += 64) f(ent_at(T, L, i0 + lane), i0 + lane < L.n);
   };
-  auto load_ent = [&](const DevTensor& T, int64_t row0, Ent& e) {
-    const int64_t base = (row0 + tau) * T.k_out + e.first;
-#pragma unroll
-    for (int u = 0; u < kEnt; ++u) {
-      const int j = 2 * u + half;
-      e.cv[u] = u16x2{0, 0};
-      if (j < e.num) {
-        e.cv[u].x = T.col[base + j];
-        e.cv[u].y = T.val[base + j];
-      }
-    }
-  };
-  // f(channel in the head, dense index, value) for the entries of the
-  // lane's share
-  auto for_ent = [&](const DevTensor& T, int64_t row0, const Ent& e, auto&& f) {
-#pragma unroll
-    for (int u = 0; u < kEnt; ++u) {
-      if (2 * u + half < e.num) f((int)(e.cv[u].x & (kD - 1)), (uint32_t)e.cv[u].x >> 12, h2f(e.cv[u].y));
-    }
-    // more than 2 kEnt entries in one head of one token: the rest in turn
-    const int64_t base = (row0 + tau) * T.k_out + e.first;
-    for (int j = 2 * kEnt + half; j < e.num; j += 2) {
-      const uint32_t col = T.col[base + j];
-      f((int)(col & (kD - 1)), col >> 12, h2f(T.val[base + j]));
-    }
-  };
-
-  Cnt kcn, vcn;
-  {
-    const int nt0 = min(kChunk, t_end - t_begin);
-    const int64_t r0 = csr_row(a.sh, b, t_begin);
-    if constexpr (KOUT) load_cnt(K, r0, nt0, kcn);
-    if constexpr (VOUT) load_cnt(V, r0, nt0, vcn);
-  }
 
   for (int ci = 0; ci < n_chunks; ++ci) {
     const int t0 = t_begin + ci * kChunk;
@@ -271,9 +239,8 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
 
     // where this chunk's outlier entries of the head lie; its key entries
     // (the value entries load after the key phase)
-    Ent ke, ve;
-    if constexpr (KOUT) { find_ent(kcn, nt, ke); load_ent(K, row0, ke); }
-    if constexpr (VOUT) find_ent(vcn, nt, ve);
+    Lst kl, vl;
+    if constexpr (KOUT) make_list(K, row0, kl);
     u32x4 vc[2], kn[2];
     load_v(row_c, vc);
 
@@ -322,23 +289,32 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
             }
           }
         }
-      // key outliers of this lane's share: (value - centroid) * coefficient
-      if constexpr (KOUT) {
-        for_ent(K, row0, ke, [&](int c, uint32_t code, float val) {
-          const float delta = val - h2f(S.kt[wave][c][code]);
-          const int i = c & (kPairs - 1);
-          const float2 q2 = S.qr[wave][i];
-          float coef;
-          if constexpr (ROPE) {
-            const float2 cs = S.e[i][tau];
-            coef = c < kPairs ? q2.x * cs.x + q2.y * cs.y : q2.y * cs.x - q2.x * cs.y;
-          } else {
-            coef = c < kPairs ? q2.x : q2.y;
-          }
-          s = __builtin_fmaf(delta, coef, s);
-        });
-      }
       s += swap_halves(s);                           // both halves of token tau
+      // key outliers: (value - centroid) * coefficient into the wave's
+      // per-token sums (the first 32 of its channel sums, zero here)
+      if constexpr (KOUT) {
+        for_list(K, kl, [&](uint32_t ent, bool valid) {
+          if (valid) {
+            const int te = (int)((ent >> 7) & 31u), c = (int)(ent & (kD - 1));
+            const float delta = h2f((uint16_t)(ent >> 16)) - h2f(S.kt[wave][c][(ent >> 12) & 15u]);
+            const int i = c & (kPairs - 1);
+            const float2 q2 = S.qr[wave][i];
+            float coef;
+            if constexpr (ROPE) {
+              const float2 cs = S.e[i][te];
+              coef = c < kPairs ? q2.x * cs.x + q2.y * cs.y : q2.y * cs.x - q2.x * cs.y;
+            } else {
+              coef = c < kPairs ? q2.x : q2.y;
+            }
+            atomicAdd(&S.vcorr[wave][te], delta * coef);
+          }
+        });
+        // LDS accesses of one wave complete in order: the sums are complete
+        __builtin_amdgcn_wave_barrier();
+        s += S.vcorr[wave][tau];
+        __builtin_amdgcn_wave_barrier();
+        if (half == 0) S.vcorr[wave][tau] = 0.f;
+      }
     }
     // the rotated queries of this chunk are consumed (each wave rotates its
     // own head's queries; LDS accesses of one wave complete in order)
@@ -346,17 +322,10 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
 
     // this chunk's value entries; key codes, rotated queries and outlier
     // counts of the next chunk
-    if constexpr (VOUT) load_ent(V, row0, ve);
+    if constexpr (VOUT) make_list(V, row0, vl);
     load_k(t0 + kChunk, row_n, kn);
     row_c = row_n;
     if constexpr (ROPE) set_q(ci + 1);
-    if (ci + 1 < n_chunks) {
-      const int t1 = t0 + kChunk;
-      const int nt1 = min(kChunk, t_end - t1);
-      const int64_t r1 = csr_row(a.sh, b, t1);
-      if constexpr (KOUT) load_cnt(K, r1, nt1, kcn);
-      if constexpr (VOUT) load_cnt(V, r1, nt1, vcn);
-    }
 
     if (head_ok) {
       // ---- online softmax ----------------------------------------------------------
@@ -398,10 +367,14 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
 
       // ---- value outliers: p * (value - centroid) into the wave's channel sums ----------
       if constexpr (VOUT) {
-        for_ent(V, row0, ve, [&](int c, uint32_t code, float val) {
-          const uint32_t cc = S.vt[wave][code][c & (kPairs - 1)];
-          const float dense = c < kPairs ? half_lo(cc) : half_hi(cc);
-          atomicAdd(&S.vcorr[wave][c], pt * (val - dense));
+        for_list(V, vl, [&](uint32_t ent, bool valid) {
+          const float pe = __shfl(pt, (int)((ent >> 7) & 31u), 64);   // p of the entry's token
+          if (valid) {
+            const int c = (int)(ent & (kD - 1));
+            const uint32_t cc = S.vt[wave][(ent >> 12) & 15u][c & (kPairs - 1)];
+            const float dense = c < kPairs ? half_lo(cc) : half_hi(cc);
+            atomicAdd(&S.vcorr[wave][c], pe * (h2f((uint16_t)(ent >> 16)) - dense));
+          }
         });
         // LDS accesses of one wave complete in order: the sums are complete
         __builtin_amdgcn_wave_barrier();

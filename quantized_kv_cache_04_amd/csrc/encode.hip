@@ -425,7 +425,6 @@ __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTenso
   __shared__ uint32_t hist[4][256];
   __shared__ uint32_t sel[2];                             // digit, remaining rank
   __shared__ uint32_t wsum[4];
-  __shared__ uint32_t hcount[32];                         // kept entries per KV head
   const int n = sh.Hkv * kD;
   const int k = t.k_out;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -434,7 +433,6 @@ __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTenso
   const uint16_t* xr = static_cast<const uint16_t*>(x_new) + ((int64_t)b * sh.in_tok + sh.in_off + tn) * n;
   for (int i = tid; i < n; i += 256)
     keys[i] = ((uint32_t)(xr[i] & 0x7fffu) << 16) | (0xffffu - (uint32_t)i);
-  if (tid < 32) hcount[tid] = 0u;   // (the barriers of the passes order this)
   uint32_t prefix = 0, mask = 0, kk = (uint32_t)k;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = pass < 3 ? 23 - 8 * pass : 0;
@@ -504,16 +502,7 @@ __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTenso
       // outliers are kept in fp16: a bf16 input is rounded to nearest-even
       t.val[r * k + pos] = sh.kv_bf16 ? f2h_rn(bf2f(xr[i])) : xr[i];
       ++pos;
-      atomicAdd(&hcount[i / kD], 1u);
     }
-  }
-  __syncthreads();
-  // where each KV head's entries of the row end: the number of its entries
-  // in heads 0 .. tid (rows of 16-byte units; the padding stays zero)
-  if (tid < sh.Hkv) {
-    uint32_t end = 0;
-    for (int hh = 0; hh <= tid; ++hh) end += hcount[hh];
-    t.hend[r * ((sh.Hkv + 7) / 8 * 8) + tid] = (uint16_t)end;
   }
   if (tid == 0) {
     // both ends of the row (every row pointer is k times its index, so
@@ -522,6 +511,63 @@ __global__ __launch_bounds__(256) void enc_outliers_kernel(DevShape sh, DevTenso
     t.row_ptr[r] = (int32_t)(k * r);
     t.row_ptr[r + 1] = (int32_t)(k * (r + 1));
   }
+}
+
+// ---- per-tile outlier index (CODEBOOK with outliers) ------------------------
+// The decode kernels read a tile's outliers grouped by KV head: for the tile
+// of 32 tokens and head h, the entries of its tokens in token order (each
+// token's in column order), one dword each -- channel (bits 0-6), token in
+// the tile (7-11), the dense index it replaces (12-15), fp16 value (16-31);
+// off[h] is where head h's entries start in the tile's block of 32 k
+// entries, off[Hkv] the tile's count.  One block per (tile that this append
+// touches, sequence) rebuilds the tile from its tokens' CSR rows.
+__global__ __launch_bounds__(256) void enc_otile_kernel(DevShape sh, DevTensor t, int64_t n_total,
+                                                        int64_t tile0) {
+  __shared__ uint32_t cnt[kTile][33];   // entries of (token, head); then their rank offsets
+  __shared__ uint32_t pos[kTile][33];   // where (token, head)'s entries start in the head's list
+  __shared__ uint32_t hoff[33];         // where each head's list starts in the tile's block
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y;
+  const int64_t t0 = (tile0 + blockIdx.x) * kTile;
+  const int nt = (int)min((int64_t)kTile, n_total - t0);
+  const int H = sh.Hkv, k = t.k_out;
+  const int64_t r0 = csr_row(sh, b, t0);          // rows r0 .. r0 + nt - 1 (one page)
+  const int64_t tile = r0 / kTile;
+  const int o_row = (H + 8) / 8 * 8;
+  for (int i = tid; i < kTile * 33; i += 256) (&cnt[0][0])[i] = 0u;
+  __syncthreads();
+  const int ne = nt * k;
+  for (int i = tid; i < ne; i += 256)
+    atomicAdd(&cnt[i / k][(t.col[r0 * k + i] & 0xfffu) >> 7], 1u);
+  __syncthreads();
+  // head h's list: its tokens in turn
+  if (tid < H) {
+    uint32_t acc = 0;
+    for (int tau = 0; tau < kTile; ++tau) { pos[tau][tid] = acc; acc += cnt[tau][tid]; }
+    hoff[tid] = acc;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t acc = 0;
+    for (int h = 0; h < H; ++h) { const uint32_t c = hoff[h]; hoff[h] = acc; acc += c; }
+    hoff[H] = acc;
+  }
+  // a token's row holds its entries in column order: the first of head h
+  // in the row is the sum of its counts over the heads before
+  if (tid < kTile) {
+    uint32_t acc = 0;
+    for (int h = 0; h < H; ++h) { const uint32_t c = cnt[tid][h]; cnt[tid][h] = acc; acc += c; }
+  }
+  __syncthreads();
+  uint32_t* blk = t.tent + tile * ((int64_t)kTile * k);
+  for (int i = tid; i < ne; i += 256) {
+    const int tau = i / k, j = i - tau * k;
+    const uint32_t col = t.col[r0 * k + i];
+    const int h = (int)((col & 0xfffu) >> 7);
+    const uint32_t dst = hoff[h] + pos[tau][h] + ((uint32_t)j - cnt[tau][h]);
+    blk[dst] = (col & 0xf07fu) | ((uint32_t)tau << 7) | ((uint32_t)t.val[r0 * k + i] << 16);
+  }
+  for (int h = tid; h < o_row; h += 256) t.toff[tile * o_row + h] = h <= H ? (uint16_t)hoff[h] : 0;
 }
 
 }  // namespace
@@ -558,6 +604,9 @@ hipError_t launch_encode_tensor(const DevShape& sh, const DevTensor& t, bool is_
   if (t.k_out > 0) {
     hipLaunchKernelGGL(enc_outliers_kernel, dim3(n_new, sh.B), dim3(256),
                        (size_t)sh.Hkv * kD * 4, stream, sh, t, x_new, n_ctx, n_new);
+    const int64_t tile0 = n_ctx / kTile, tile1 = (n_ctx + n_new - 1) / kTile;
+    hipLaunchKernelGGL(enc_otile_kernel, dim3((unsigned)(tile1 - tile0 + 1), sh.B), dim3(256), 0,
+                       stream, sh, t, n_ctx + n_new, tile0);
   }
   return hipGetLastError();
 }

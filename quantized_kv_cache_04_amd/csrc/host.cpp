@@ -214,7 +214,9 @@ void fill_tensor(TensorLayout& t, const kvq_tensor_format& f, const kvq_config& 
     put(t.rowptr_off, t.rowptr_bytes, (slots + 1) * 4);
     put(t.col_off, t.col_bytes, slots * t.k_out * 2);
     put(t.val_off, t.val_bytes, slots * t.k_out * 2);
-    put(t.hend_off, t.hend_bytes, slots * ((H + 7) / 8 * 16));
+    // the per-tile index: offsets per head, entries grouped by head
+    put(t.toff_off, t.toff_bytes, (slots / kTile) * ((H + 8) / 8 * 16));
+    put(t.tent_off, t.tent_bytes, slots * t.k_out * 4);
   }
 }
 
@@ -261,7 +263,10 @@ uint64_t tensor_payload(const TensorLayout& t, const kvq_config& c, int64_t n) {
   uint64_t total;
   if (t.quant == KVQ_QUANT_CODEBOOK) {
     total = B * H * (uint64_t)n * t.row_bytes + H * d * 16 * 2;
-    if (t.k_out) total += B * (uint64_t)n * (4 + 4 * (uint64_t)t.k_out + (H + 7) / 8 * 16);
+    // outliers: the per-tile index the decode kernels stream (entries of the
+    // n tokens and the offsets of their tiles)
+    if (t.k_out)
+      total += B * ((uint64_t)n * 4 * t.k_out + (((uint64_t)n + kTile - 1) / kTile) * ((H + 8) / 8 * 16));
     return total;
   }
   if (t.per_channel) {
@@ -279,7 +284,8 @@ void fill_regions(kvq_tensor_regions& r, const TensorLayout& t) {
   r.row_ptr = {t.rowptr_off, t.rowptr_bytes};
   r.col = {t.col_off, t.col_bytes};
   r.val = {t.val_off, t.val_bytes};
-  r.head_end = {t.hend_off, t.hend_bytes};
+  r.tile_off = {t.toff_off, t.toff_bytes};
+  r.tile_ent = {t.tent_off, t.tent_bytes};
   r.sink = {t.sink_off, t.sink_bytes};
 }
 
@@ -345,7 +351,8 @@ DevTensor make_dev_tensor(const TensorLayout& tl, void* base, const void* codebo
   t.row_ptr = tl.rowptr_bytes ? reinterpret_cast<int32_t*>(b + tl.rowptr_off) : nullptr;
   t.col = tl.col_bytes ? reinterpret_cast<uint16_t*>(b + tl.col_off) : nullptr;
   t.val = tl.val_bytes ? reinterpret_cast<uint16_t*>(b + tl.val_off) : nullptr;
-  t.hend = tl.hend_bytes ? reinterpret_cast<uint16_t*>(b + tl.hend_off) : nullptr;
+  t.toff = tl.toff_bytes ? reinterpret_cast<uint16_t*>(b + tl.toff_off) : nullptr;
+  t.tent = tl.tent_bytes ? reinterpret_cast<uint32_t*>(b + tl.tent_off) : nullptr;
   t.codebook = static_cast<const uint16_t*>(codebook);
   t.hscale = tl.quant == KVQ_QUANT_FP8_E5M2 ? scale : nullptr;
   return t;
@@ -377,7 +384,7 @@ int32_t kvq_decode_path(const kvq_config* cfg) {
   return ok ? KVQ_PATH_MFMA : KVQ_PATH_VALU;
 }
 
-int32_t kvq_abi_version(void) { return 109; }
+int32_t kvq_abi_version(void) { return 110; }
 
 kvq_status kvq_set_decode_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr))

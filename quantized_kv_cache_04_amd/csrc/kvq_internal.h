@@ -39,7 +39,8 @@ struct TensorLayout {
   uint64_t rowptr_off = 0, rowptr_bytes = 0;
   uint64_t col_off = 0, col_bytes = 0;
   uint64_t val_off = 0, val_bytes = 0;
-  uint64_t hend_off = 0, hend_bytes = 0;   // outliers: uint16 [rows][round_up(Hkv, 8)] per-head ends
+  uint64_t toff_off = 0, toff_bytes = 0;   // outliers: uint16 [tiles][round_up(Hkv + 1, 8)]
+  uint64_t tent_off = 0, tent_bytes = 0;   // outliers: uint32 [tiles][32 k] grouped by head
   uint64_t sink_off = 0, sink_bytes = 0;   // attention sink: raw [B, Hkv, sink, d]
 };
 
@@ -75,7 +76,8 @@ struct DevTensor {
   int32_t* row_ptr;
   uint16_t* col;
   uint16_t* val;
-  uint16_t* hend;             // outliers: end of each KV head's entries in each CSR row
+  uint16_t* toff;             // outliers: per tile, where each KV head's entries start
+  uint32_t* tent;             // outliers: per tile, the entries grouped by KV head
   const uint16_t* codebook;   // fp16 [Hkv][d][16]
   const float* hscale;        // FP8: float32 scale per KV head (null = 1)
 };

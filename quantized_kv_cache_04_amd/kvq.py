@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvq.h")
 # interface version the structures below follow (major * 100 + minor)
-ABI_VERSION = 109
+ABI_VERSION = 110
 
 # ---- constants mirrored from kvq.h -------------------------------------------
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_DEVICE = 0, -1, -2, -3, -4
@@ -59,7 +59,7 @@ class Region(ctypes.Structure):
 
 class TensorRegions(ctypes.Structure):
     _fields_ = [("codes", Region), ("params", Region), ("tail", Region), ("row_ptr", Region),
-                ("col", Region), ("val", Region), ("sink", Region), ("head_end", Region)]
+                ("col", Region), ("val", Region), ("sink", Region), ("tile_off", Region), ("tile_ent", Region)]
 
 
 class LayoutInfo(ctypes.Structure):

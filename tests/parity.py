@@ -104,7 +104,7 @@ def compare_regions(cache: kvq.Cache, expected) -> List[str]:
         exp = expected[name]
         if exp is None:
             continue
-        for reg in ("codes", "params", "tail", "row_ptr", "col", "val", "sink", "head_end"):
+        for reg in ("codes", "params", "tail", "row_ptr", "col", "val", "sink", "tile_off", "tile_ent"):
             if reg not in exp:
                 continue
             got = cache.region(name, reg).cpu().numpy()

@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
                           "kvq_decode_attention", "kvq_last_error", "kvq_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvq_abi_version() == kvq.ABI_VERSION == 109
+    assert L.kvq_abi_version() == kvq.ABI_VERSION == 110
 
 
 def _none_cfg(**kw):
@@ -65,7 +65,7 @@ def test_layout_regions_fit_and_do_not_overlap(cfg_id):
     assert li.capacity % 32 == 0 and li.capacity >= w.ctx
     regs = []
     for t in ("k", "v"):
-        for name in ("codes", "params", "tail", "row_ptr", "col", "val", "head_end"):
+        for name in ("codes", "params", "tail", "row_ptr", "col", "val", "tile_off", "tile_ent"):
             r = getattr(getattr(li, t), name)
             if r.bytes:
                 assert r.offset % 256 == 0
@@ -105,7 +105,7 @@ def test_sink_regions(cfg_id, sink):
         assert r.bytes == want
         if sink:
             assert r.offset % 256 == 0
-        for name in ("codes", "params", "tail", "row_ptr", "col", "val", "sink", "head_end"):
+        for name in ("codes", "params", "tail", "row_ptr", "col", "val", "sink", "tile_off", "tile_ent"):
             rr = getattr(getattr(li, t), name)
             if rr.bytes:
                 regs.append((rr.offset, rr.offset + rr.bytes))

@@ -47,12 +47,12 @@ def test_groups_2048_by_64():
 
 
 # Config 4 by hand: per tensor, 131,072 tokens x 32 heads x 64 code bytes =
-# 268,435,456; CSR 131,072 x (4 + 41 x 4) = 22,020,096; per-head end
-# offsets 131,072 x 32 x 2 = 8,388,608; codebooks 32 x 128 x 16 x 2 =
-# 131,072 -> x 2 tensors = 597,950,464.
+# 268,435,456; the per-tile outlier index: 131,072 x 41 entries x 4 bytes =
+# 21,495,808 and 4,096 tiles x 40 offsets x 2 bytes = 327,680; codebooks
+# 32 x 128 x 16 x 2 = 131,072 -> x 2 tensors = 580,780,032.
 @pytest.mark.parametrize("cfg_id,ctx,expected", [
     (1, None, 155_648), (2, 4096, 2_228_224), (2, 8192, 4_456_448), (2, 16384, 8_912_896),
-    (3, None, 117_440_512), (4, None, 597_950_464), (5, None, 1_140_850_688)])
+    (3, None, 117_440_512), (4, None, 580_780_032), (5, None, 1_140_850_688)])
 def test_workload_payloads(cfg_id, ctx, expected):
     w = make_workload(cfg_id, ctx=ctx)
     v = cb.payload_bytes(w.k, w.v, batch=w.batch, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,

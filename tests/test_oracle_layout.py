@@ -131,18 +131,27 @@ def test_outlier_column_carries_the_dense_index():
     assert reg["row_ptr"][:3].tolist() == [0, 2, 0]
 
 
-def test_outlier_head_ends():
-    # three heads (rows padded to 8 entries), three outliers per token:
-    # token 0 at columns 5 (head 0), 130 and 200 (head 1) -> counts 1, 2, 0,
-    # ends 1, 3, 3; token 1 at columns 0, 1 (head 0) and 300 (head 2) ->
-    # counts 2, 0, 1, ends 2, 2, 3
+def test_outlier_tile_index():
+    # three heads, three outliers per token, two tokens in tile 0:
+    # token 0 at columns 5 (head 0, channel 5), 130 (head 1, channel 2) and
+    # 200 (head 1, channel 72); token 1 at columns 0, 1 (head 0) and 300
+    # (head 2, channel 44).  Head lists in token order: head 0 = (t0 c5,
+    # t1 c0, t1 c1), head 1 = (t0 c2, t0 c72), head 2 = (t1 c44) -> offsets
+    # 0, 3, 5 and the count 6.  An entry is c | token << 7 | code << 12 |
+    # fp16 bits << 16: values 1.0 (0x3c00) except -2.0 (0xc000) at column
+    # 200, whose dense index is 9.
     codes = np.zeros((1, 3, 2, 128), dtype=np.int64)
-    enc = {"codes": codes, "cols": np.array([[[5, 130, 200], [0, 1, 300]]]),
-           "vals": np.ones((1, 2, 3), dtype=np.float32)}
+    codes[0, 1, 0, 72] = 9
+    vals = np.ones((1, 2, 3), dtype=np.float32)
+    vals[0, 0, 2] = -2.0
+    enc = {"codes": codes, "cols": np.array([[[5, 130, 200], [0, 1, 300]]]), "vals": vals}
     fmt = {"quantizer": "codebook", "bits": 4, "outlier_frac": 3 / 384}
     reg = layout.expected_regions(fmt, enc, batch=1, n_kv_heads=3, n_ctx=2, max_ctx=32,
                                   kv_dtype="f16", is_key=True)
-    he = reg["head_end"]
-    assert he.shape == (1024, 8) and he.dtype == np.uint16
-    assert he[0].tolist() == [1, 3, 3] + [0] * 5 and he[1].tolist() == [2, 2, 3] + [0] * 5
-    assert not he[2:].any()
+    off, ent = reg["tile_off"], reg["tile_ent"]
+    assert off.shape == (32, 8) and off.dtype == np.uint16        # 1024 tokens / 32
+    assert ent.shape == (32, 96) and ent.dtype == np.uint32       # 32 tokens x 3 entries
+    assert off[0].tolist() == [0, 3, 5, 6, 0, 0, 0, 0]
+    assert [hex(int(x)) for x in ent[0, :6]] == [
+        "0x3c000005", "0x3c000080", "0x3c000081", "0x3c000002", "0xc0009048", "0x3c0000ac"]
+    assert not ent[0, 6:].any() and not off[1:].any() and not ent[1:].any()

@@ -24,7 +24,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
 # per-source extra flags: the encoder must not contract (x - z) / s chains
 EXTRA = {"encode.hip": ["-ffp-contract=off"]}
 SOURCES = ["host.cpp", "encode.hip", "decode_generic.hip", "decode_mfma.hip", "decode_lut.hip",
-           "combine.hip", "prefill_mfma.hip", "scratch.hip"]
+           "combine.hip", "prefill_mfma.hip", "prefill_codes.hip", "scratch.hip"]
 
 
 def hipcc() -> str:

@@ -180,5 +180,9 @@ struct PrefillArgs {
 };
 // 64 query rows per workgroup: Hq / Hkv must divide 64
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// The code-operand prefill kernel for the uniform formats it is compiled
+// for (same grid, splits and partial records); false, with nothing
+// launched, for any other configuration.
+bool launch_prefill_codes(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace kvq

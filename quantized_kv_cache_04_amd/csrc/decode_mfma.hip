@@ -173,7 +173,9 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
       float s = 0.f, so = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += qv[m][e];
-      bq[m] = pair_operand<KB>(qv[m], sc, lo_mask);
+      u32x4 hi, lo;
+      pair_operand_fixed<KB>(qv[m], sc, hi, lo);
+      bq[m] = __builtin_bit_cast(half8, hi_lane ? hi : lo);
       if constexpr (KQ8) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) so += (float)bq[m][e];
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
         const int hd = bi >> 4, cb = bi & 15;
         if (cb == 0) zb_tab[wave][hd] = z;
         u32x4 hi, lo;
-        pair_operand_hilo<KB>(xs[u], s2, hi, lo);
+        pair_operand_fixed<KB>(xs[u], s2, hi, lo);
         kb_tab[wave][hd][0][cb] = hi;
         kb_tab[wave][hd][1][cb] = lo;
       }

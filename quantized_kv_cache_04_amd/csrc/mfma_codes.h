@@ -180,39 +180,10 @@ __device__ __forceinline__ constexpr int pe_class(int r) { return VB == 3 ? r : 
 template <int VB>
 __device__ __forceinline__ constexpr int pe_exp(int cls) { return VB == 3 ? 2 * cls : (VB == 4 ? 4 * cls : 0); }
 
-// Operand in "pair order" from 8 values x[e] (e = 0..7): pair r = (x[r], x[r + 4])
-// each divided by the unpack factor of the other operand, scaled by ``sc`` and
-// split into the high or low fp16 part.
-template <int BITS>
-__device__ __forceinline__ half8 pair_operand(const float x[8], float sc, float lo_mask) {
-  uint32_t o[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float f = sc * pair_factor<BITS>(r);
-    o[r] = hilo2(x[r] * f, x[r + 4] * f, lo_mask);
-  }
-  return as_h8(o[0], o[1], o[2], o[3]);
-}
-
-// Both fp16 parts of the pair-order operand of 8 values (see pair_operand):
-// hi = x rounded to nearest, lo = (x - hi) rounded to nearest.
-template <int BITS>
-__device__ __forceinline__ void pair_operand_hilo(const float x[8], float sc, u32x4& hi, u32x4& lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float f = sc * pair_factor<BITS>(r);
-    const float a = x[r] * f, b = x[r + 4] * f;
-    const half2v hv = cvt_pk_rn(a, b);
-    h[r] = __builtin_bit_cast(uint32_t, hv);
-    l[r] = __builtin_bit_cast(uint32_t, cvt_pk_rn(a - (float)hv[0], b - (float)hv[1]));
-  }
-  hi = u32x4{h[0], h[1], h[2], h[3]};
-  lo = u32x4{l[0], l[1], l[2], l[3]};
-}
-
-// Both fp16 parts of the pair-order operand of 8 values, the high part on a
-// fixed grid: with |x * sc| <= 2^14 for every value the wave feeds, hi is
+// Operand in "pair order" from 8 values x[e] (e = 0..7): pair r = (x[r],
+// x[r + 4]) times sc and divided by the unpack factor of the other operand,
+// as fp16 high and low parts.  The high part sits on a fixed grid: with
+// |x * sc| <= 2^14 for every value the wave feeds, hi is
 // x * sc * pair_factor rounded to a multiple of 16 * pair_factor (at most
 // 1024 steps, exact in fp16), lo = the rest rounded to nearest.  Every
 // high-part product with a code is then an integer multiple of 16 * 2^-24,

@@ -194,14 +194,14 @@ __device__ __forceinline__ constexpr int pe_exp(int cls) { return VB == 3 ? 2 * 
 template <int BITS>
 __device__ __forceinline__ void pair_operand_fixed(const float x[8], float sc, u32x4& hi, u32x4& lo) {
   uint32_t h[4], l[4];
+  const float c16 = sc * 0.0625f;   // x * sc / 16: the grid index (all factors are powers of two)
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float f = sc * pair_factor<BITS>(r);
-    const float step = 16.0f * pair_factor<BITS>(r), inv = 1.0f / step;   // powers of two
-    const float a = x[r] * f, b = x[r + 4] * f;
-    const float ha = __builtin_rintf(a * inv) * step, hb = __builtin_rintf(b * inv) * step;
+    const float step = 16.0f * pair_factor<BITS>(r);
+    const float ha = __builtin_rintf(x[r] * c16) * step, hb = __builtin_rintf(x[r + 4] * c16) * step;
     h[r] = __builtin_bit_cast(uint32_t, cvt_pk_rn(ha, hb));
-    l[r] = __builtin_bit_cast(uint32_t, cvt_pk_rn(a - ha, b - hb));
+    l[r] = __builtin_bit_cast(uint32_t, cvt_pk_rn(__builtin_fmaf(x[r], f, -ha), __builtin_fmaf(x[r + 4], f, -hb)));
   }
   hi = u32x4{h[0], h[1], h[2], h[3]};
   lo = u32x4{l[0], l[1], l[2], l[3]};

@@ -20,10 +20,10 @@
 //    tile.  The QK^T result layout (lane (q, n): tokens 4q + r and
 //    16 + 4q + r of row n) is that A operand as it stands.
 // The high and low parts are two instructions into one accumulator, the low
-// parts first: the matrix cores keep only so many bits below the largest
-// term of a sum, so small low-part products added into a larger sum would
-// lose theirs.  For the same reason each block's value products go into a
-// fresh accumulator, which joins the running sums in fp32.
+// parts first.  The matrix cores keep only so many bits below the largest
+// product of an instruction: the query operand's high part therefore sits
+// on a fixed grid (pair_operand_fixed), which makes the high-part products
+// of the scores add up exactly.
 // Each wave owns 16 rows and streams every block of its range itself; the
 // four waves of a workgroup read the same bytes at about the same time,
 // which the vector cache serves.  Per 32-token block a wave spends 32
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const half2v sz = __builtin_bit_cast(half2v, pz[e]);   // (scale, zero)
-        const float qe = q_el(m, e);
+        const float qe = h2f((uint16_t)(qw[m][e >> 1] >> (16 * (e & 1))));   // fp16 keys and queries
         xs[m][e] = qe * (float)sz[0];
         mx = fmaxf(mx, fabsf(xs[m][e]));
         zb = __builtin_fmaf(qe, (float)sz[1], zb);
@@ -298,16 +298,14 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
         half8 kcode[4][kPlanes<KB>];
 #pragma unroll
         for (int m = 0; m < 4; ++m) code_planes<KB, KQ8>(B.k[mb], m, kcode[m]);
-        f32x4 cl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-          for (int pl = 0; pl < kPlanes<KB>; ++pl) cl = mfma16(kcode[m][pl], bql[m], cl);
+          for (int pl = 0; pl < kPlanes<KB>; ++pl) c = mfma16(kcode[m][pl], bql[m], c);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
           for (int pl = 0; pl < kPlanes<KB>; ++pl) c = mfma16(kcode[m][pl], bqh[m], c);
-        c += cl;
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[mb][r] = c[r] * kscale + kb2[pe_class<VB>(r)];
       }
@@ -329,16 +327,14 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
             else
               code_planes<KB, KQ8>(B.k[mb], m, kcode[m]);
           }
-          f32x4 cl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m)
 #pragma unroll
-            for (int pl = 0; pl < kPlanes<KB>; ++pl) cl = mfma16(kcode[m][pl], bql[m], cl);
+            for (int pl = 0; pl < kPlanes<KB>; ++pl) c = mfma16(kcode[m][pl], bql[m], c);
 #pragma unroll
           for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m)
 #pragma unroll
             for (int pl = 0; pl < kPlanes<KB>; ++pl) c = mfma16(kcode[m][pl], bqh[m], c);
-          c += cl;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const uint32_t* d = B.kp[mb];
@@ -550,15 +546,10 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
         vcode[0] = fp8_block(seg, nbk & 3);
       else
         code_planes<VB, VQ8, true>(seg, nbk & 3, vcode);
-      // the block's low parts first, then its high parts, into a fresh sum
-      // that joins the running one in fp32: added straight into a sum of
-      // many blocks, the small low-part products would lose their low bits
-      f32x4 t = {0.f, 0.f, 0.f, 0.f}, tl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int pl = 0; pl < kPlanes<VB>; ++pl) tl = mfma16(pal[nbk * NGV / 8], vcode[pl], tl);
+      for (int pl = 0; pl < kPlanes<VB>; ++pl) oacc[nbk] = mfma16(pal[nbk * NGV / 8], vcode[pl], oacc[nbk]);
 #pragma unroll
-      for (int pl = 0; pl < kPlanes<VB>; ++pl) t = mfma16(pah[nbk * NGV / 8], vcode[pl], t);
-      oacc[nbk] += t + tl;
+      for (int pl = 0; pl < kPlanes<VB>; ++pl) oacc[nbk] = mfma16(pah[nbk * NGV / 8], vcode[pl], oacc[nbk]);
     }
     __builtin_amdgcn_s_setprio(0);
   };

@@ -40,7 +40,8 @@ def log(*a):
 
 
 KERNEL_SOURCES = {"dec_mfma_kernel": "decode_mfma.hip", "dec_lut_kernel": "decode_lut.hip",
-                  "dec_generic_kernel": "decode_generic.hip", "pre_mfma_kernel": "prefill_mfma.hip"}
+                  "dec_generic_kernel": "decode_generic.hip", "pre_mfma_kernel": "prefill_mfma.hip",
+                  "pre_codes_kernel": "prefill_codes.hip"}
 
 
 def kernel_source_sha(kernel: str) -> str:
@@ -497,7 +498,9 @@ def bench_prefill(args, w, dev):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
-                     "traffic": None, "kernel": "pre_mfma_kernel",
+                     "traffic": None,
+                     "kernel": ("pre_codes_kernel" if kvq.prefill_kernel(cfg) == "codes"
+                                else "pre_mfma_kernel"),
                      "avg_launch_us": round(pre_avg * 1e3, 2),
                      "append_us": round(app_avg * 1e3, 2),
                      "algorithmic_flops_per_launch": flops},

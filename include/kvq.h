@@ -419,6 +419,21 @@ kvq_status kvq_prefill_workspace_bytes(const kvq_config* cfg, int32_t n_q, int64
                                        uint64_t* out_bytes);
 
 /*
+ * kvq_prefill_kernel -- which kernel kvq_prefill_attention runs for this
+ * configuration: KVQ_PREFILL_CODES (the packed codes enter the matrix cores
+ * as exact fp16 operands, the scales the query and probability operands;
+ * 4-bit per-channel keys with 4-bit values in per-token groups of 128 or 32
+ * channels and fp16 data, 3-bit keys and values in per-token groups of 64,
+ * q8_0 keys and values in blocks of 32, and FP8 E5M2; no attention sink, no
+ * RoPE, one group size for every KV head) or KVQ_PREFILL_STAGED (each
+ * block dequantized into LDS as fp16 high and low parts: every format).
+ * Host only.  Returns a negative status for an invalid configuration.
+ */
+#define KVQ_PREFILL_CODES  1
+#define KVQ_PREFILL_STAGED 2
+int32_t kvq_prefill_kernel(const kvq_config* cfg);
+
+/*
  * kvq_decode_path -- which decode kernel kvq_decode_attention runs for this
  * configuration: KVQ_PATH_VALU, KVQ_PATH_MFMA or KVQ_PATH_LUT (what KVQ_PATH_AUTO resolves
  * to, or the forced path).  Host only.  Returns a negative status for an
@@ -451,7 +466,8 @@ const char* kvq_last_error(void);
    and head_group_size; 108 adds the per-head outlier counts
    (kvq_tensor_regions.head_count); 109 replaces them by per-head end
    offsets (kvq_tensor_regions.head_end); 110 replaces those by the
-   per-tile index (kvq_tensor_regions.tile_off, tile_ent). */
+   per-tile index (kvq_tensor_regions.tile_off, tile_ent); 111 adds
+   kvq_prefill_kernel. */
 int32_t kvq_abi_version(void);
 
 #ifdef __cplusplus

@@ -384,7 +384,13 @@ int32_t kvq_decode_path(const kvq_config* cfg) {
   return ok ? KVQ_PATH_MFMA : KVQ_PATH_VALU;
 }
 
-int32_t kvq_abi_version(void) { return 110; }
+int32_t kvq_prefill_kernel(const kvq_config* cfg) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  return prefill_codes_supported(*cfg) ? KVQ_PREFILL_CODES : KVQ_PREFILL_STAGED;
+}
+
+int32_t kvq_abi_version(void) { return 111; }
 
 kvq_status kvq_set_decode_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr))
@@ -734,6 +740,7 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
   a.sm_scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)cfg->head_dim));
   a.rope = cfg->rope;
   a.rope_base = cfg->rope_base;
+  a.codes = prefill_codes_supported(*cfg) ? 1 : 0;
   // the split, as far as the workspace holds it
   int splits = prefill_splits(*cfg, n_q, cache->n_ctx);
   const uint64_t per_split = prefill_ws_bytes(*cfg, n_q, 2) / 2;

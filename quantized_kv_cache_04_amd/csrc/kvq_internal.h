@@ -174,15 +174,19 @@ struct PrefillArgs {
   float sm_scale;            // resolved
   int rope;
   float rope_base;
+  int codes;                 // 1: the code-operand kernel (prefill_codes_supported)
   int splits;                // token-axis splits (grid z); > 1: partial states to partial
   int blocks_per_split;      // 32-token blocks per split
   float* partial;            // [B][n_q][Hq][splits][d + 2] (o, m, l) when splits > 1
 };
 // 64 query rows per workgroup: Hq / Hkv must divide 64
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
-// The code-operand prefill kernel for the uniform formats it is compiled
-// for (same grid, splits and partial records); false, with nothing
-// launched, for any other configuration.
+// Whether the code-operand prefill kernel serves this configuration (the
+// staging kernel serves every other one).
+bool prefill_codes_supported(const kvq_config& c);
+// The code-operand prefill kernel (same grid, splits and partial records
+// as the staging one); false, with nothing launched, for formats it is not
+// compiled for.
 bool launch_prefill_codes(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace kvq

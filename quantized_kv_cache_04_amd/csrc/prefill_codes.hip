@@ -689,10 +689,30 @@ bool asym(const DevTensor& t, int bits) {
 
 }  // namespace
 
+// The formats the kernel is compiled for (launch_prefill_codes below), with
+// no sink, no RoPE and one group size for every KV head.
+bool prefill_codes_supported(const kvq_config& c) {
+  if (c.sink_tokens > 0 || c.rope || c.k.head_group_size || c.v.head_group_size) return false;
+  if (c.n_q_heads % c.n_kv_heads != 0 || kRowsWG % (c.n_q_heads / c.n_kv_heads) != 0) return false;
+  const kvq_tensor_format &k = c.k, &v = c.v;
+  auto asym = [](const kvq_tensor_format& f, int bits) {
+    return (f.quantizer == KVQ_QUANT_ASYM_MINMAX || f.quantizer == KVQ_QUANT_ASYM_ABSMAX_OFFSET) &&
+           f.bits == bits;
+  };
+  auto tok = [](const kvq_tensor_format& f, int G) {
+    return f.layout == KVQ_LAYOUT_PER_TOKEN && f.group_size == G;
+  };
+  if (k.quantizer == KVQ_QUANT_FP8_E5M2 && v.quantizer == KVQ_QUANT_FP8_E5M2) return true;
+  if (asym(k, 4) && k.layout == KVQ_LAYOUT_PER_CHANNEL && c.kv_dtype == KVQ_F16 && asym(v, 4) &&
+      (tok(v, 128) || tok(v, 32)))
+    return true;
+  if (asym(k, 3) && tok(k, 64) && asym(v, 3) && tok(v, 64)) return true;
+  return k.quantizer == KVQ_QUANT_SYM_Q8_0 && tok(k, 32) && v.quantizer == KVQ_QUANT_SYM_Q8_0 &&
+         tok(v, 32);
+}
+
 bool launch_prefill_codes(const PrefillArgs& a, hipStream_t s) {
   const DevTensor &k = a.k, &v = a.v;
-  // formats and features this kernel covers; the staging kernel takes the rest
-  if (a.sink_cap > 0 || a.rope || k.k_out > 0 || v.k_out > 0 || k.per_head || v.per_head) return false;
   const int g = a.sh.g;
   if (g < 1 || kRowsWG % g != 0) return false;
   const int qt = kRowsWG / g;

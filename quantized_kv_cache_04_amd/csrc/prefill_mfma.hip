@@ -723,7 +723,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int qt = kRows / g;
   const int tiles = (a.n_q + qt - 1) / qt;
   if (a.splits < 1 || (a.splits > 1 && !a.partial)) return hipErrorInvalidValue;
-  if (launch_prefill_codes(a, stream)) return hipGetLastError();
+  if (a.codes) return launch_prefill_codes(a, stream) ? hipGetLastError() : hipErrorNotSupported;
   const dim3 grid((unsigned)tiles, (unsigned)(a.sh.B * a.sh.Hkv), (unsigned)a.splits);
   const DevTensor &k = a.k, &v = a.v;
   auto asym = [](const DevTensor& t, int bits) {

@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvq.h")
 # interface version the structures below follow (major * 100 + minor)
-ABI_VERSION = 110
+ABI_VERSION = 111
 
 # ---- constants mirrored from kvq.h -------------------------------------------
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_DEVICE = 0, -1, -2, -3, -4
@@ -26,6 +26,7 @@ QUANT = {"none": 0, "asym_minmax": 1, "asym_absmax_offset": 2, "sym_q8_0": 3, "c
 LAYOUT = {"per_token": 0, "per_channel": 1}
 BYTES_PAYLOAD, BYTES_ALLOC = 0, 1
 PATHS = {"auto": 0, "valu": 1, "mfma": 2, "lut": 3}
+PREFILL_CODES, PREFILL_STAGED = 1, 2   # kvq_prefill_kernel results
 DTYPES = {"f16": F16, "bf16": BF16, "f32": F32}
 
 
@@ -114,6 +115,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_set_decode_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.kvq_decode_path.restype = ctypes.c_int32
         L.kvq_decode_path.argtypes = [ctypes.POINTER(Config)]
+        L.kvq_prefill_kernel.restype = ctypes.c_int32
+        L.kvq_prefill_kernel.argtypes = [ctypes.POINTER(Config)]
         _lib = L
     return _lib
 
@@ -181,6 +184,14 @@ def decode_path(cfg: Config) -> str:
     if r < 0:
         _check(r)
     return {PATHS["valu"]: "valu", PATHS["mfma"]: "mfma", PATHS["lut"]: "lut"}[r]
+
+
+def prefill_kernel(cfg: Config) -> str:
+    """"codes" or "staged": the prefill kernel the library runs for ``cfg``."""
+    r = lib().kvq_prefill_kernel(ctypes.byref(cfg))
+    if r < 0:
+        _check(r)
+    return {PREFILL_CODES: "codes", PREFILL_STAGED: "staged"}[r]
 
 
 def cache_layout(cfg: Config) -> LayoutInfo:

@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
                           "kvq_decode_attention", "kvq_last_error", "kvq_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvq_abi_version() == kvq.ABI_VERSION == 110
+    assert L.kvq_abi_version() == kvq.ABI_VERSION == 111
 
 
 def _none_cfg(**kw):
@@ -293,6 +293,29 @@ def test_decode_events_hook():
     assert L.kvq_set_decode_events(FAKE, None) == kvq.ERR_INVALID_ARGUMENT
     assert L.kvq_set_decode_events(None, FAKE) == kvq.ERR_INVALID_ARGUMENT
     assert L.kvq_set_decode_events(None, None) == kvq.OK
+
+
+def test_prefill_kernel_selection():
+    """The code-operand prefill kernel takes the uniform formats it is
+    compiled for; everything else runs on the staging kernel."""
+    from synth import make_workload
+    cfg = kvq.config_from_workload
+    for cid in (1, 2, 3, 5):     # 4-bit per-channel K with values in groups of 32 / 128, q8_0, 3-bit
+        assert kvq.prefill_kernel(cfg(make_workload(cid, ctx=256))) == "codes", cid
+    assert kvq.prefill_kernel(cfg(make_workload(4, ctx=256))) == "staged"   # codebooks, RoPE
+    w5 = make_workload(5, ctx=256)
+    assert kvq.prefill_kernel(cfg(w5, sink_tokens=4)) == "staged"
+    w5v = make_workload(5, ctx=256, v={"group_size": 64})
+    assert kvq.prefill_kernel(cfg(w5v)) == "staged"           # no instantiation for 2 value groups
+    w3 = make_workload(3, ctx=256, k={"group_size": 32}, v={"group_size": 32})
+    assert kvq.prefill_kernel(cfg(w3)) == "staged"
+    w5b = make_workload(5, ctx=256, kv_dtype="bf16")           # bf16 per-channel key tail
+    assert kvq.prefill_kernel(cfg(w5b)) == "staged"
+    fp8 = dict(quantizer="fp8_e5m2", bits=8, group_size=0, layout="per_token", outlier_frac=0.0)
+    assert kvq.prefill_kernel(cfg(make_workload(5, ctx=256, k=fp8, v=fp8))) == "codes"
+    bad = cfg(w5)
+    bad.head_dim = 64
+    assert kvq.lib().kvq_prefill_kernel(ctypes.byref(bad)) < 0
 
 
 def test_decode_path_selection():

@@ -70,6 +70,22 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
   constexpr float kCmax = VQ8 ? 127.0f : (float)((1 << VB) - 1);
   constexpr int kFlush = 16;
 
+  // byte codes (q8_0, FP8): the waves share the unpacking of the blocks that
+  // every row of the workgroup sees whole.  (Shared 4-bit unpacking was
+  // slower, 22.3 against 20.5 ms on the serving shape: there the barrier per
+  // block and the LDS round trip cost more than the masks they save; for byte
+  // codes the per-wave loads and byte permutes cost more: FP8 403 -> 519
+  // TFLOP/s, q8_0 260 -> 278.)
+  constexpr bool SHARE = KB == 8 && VB == 8;
+  struct SBuf {               // one wave's share of a block, and the parameters
+    uint32_t k[2 * KB / 4];   // key blocks m0, m0 + 1 of token 16 mb_s + n, segment q4
+    uint32_t v[2 * VB / 4];   // value blocks nb0, nb0 + 1 of the lane's tile bytes
+    uint32_t vp[2][VPD];
+    uint32_t kp[2][KPD];
+  };
+  // MFMA operands of the block, by lane: [buffer][4 mb + m][lane] and [buffer][nb][lane]
+  __shared__ u32x4 kop[SHARE ? 2 : 1][SHARE ? 8 : 1][64];
+  __shared__ u32x4 vop[SHARE ? 2 : 1][SHARE ? 8 : 1][64];
   __shared__ float wo[4][16][kD];    // per wave and row: output sums (true units)
   __shared__ float wml[4][16][2];    // per wave and row: running max, sum of p
 
@@ -288,16 +304,66 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
     load_dw<2 * VB>(V.codes + r0 * (4 * VB * 4) + v_lane_off, B.v);
   };
 
+  // ---- shared unpacking (one-plane formats): wave w loads and unpacks key
+  // blocks m = 2 (w & 1), +1 of tokens 16 (w >> 1) + (0..15) and value blocks
+  // nb = 2 w, 2 w + 1, for every lane's slot of those operands ----------------------
+  const int mb_s = wave >> 1, m0 = 2 * (wave & 1), nb0 = 2 * wave;
+  auto load_share = [&](SBuf& S, int64_t r0) {
+    const uint8_t* kcodes = K.codes + r0 * (4 * KB * 4);
+    // a block of 8 codes is KB bytes of the lane's segment
+    load_dw<2 * KB / 4>(kcodes + (16 * mb_s) * (16 * KB) + k_lane_off + m0 * KB, S.k);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const uint32_t tok = 16 * mb + p_lane_tok;
+      if constexpr (F8) {
+        S.vp[mb][0] = 0u;
+        S.kp[mb][0] = 0u;
+      } else {
+        const uint8_t* vprm = static_cast<const uint8_t*>(V.params) + r0 * NGV * (VQ8 ? 2 : 4);
+        load_dw<VPD>(vprm + tok * (NGV * (VQ8 ? 2 : 4)), S.vp[mb]);
+        if constexpr (!KCH) {
+          const uint8_t* kprm = static_cast<const uint8_t*>(K.params) + r0 * NGK * (KQ8 ? 2 : 4);
+          load_dw<KPD>(kprm + tok * (NGK * (KQ8 ? 2 : 4)), S.kp[mb]);
+        } else {
+          S.kp[mb][0] = 0u;
+        }
+      }
+    }
+    load_dw<2 * VB / 4>(V.codes + r0 * (4 * VB * 4) + v_lane_off + nb0 * VB, S.v);
+  };
+  auto produce = [&](const SBuf& S, int buf) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      half8 o[1];
+      if constexpr (F8)
+        o[0] = fp8_block(S.k, j);
+      else
+        code_planes<KB, KQ8>(S.k, j, o);
+      kop[buf][4 * mb_s + m0 + j][lane] = __builtin_bit_cast(u32x4, o[0]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      half8 o[1];
+      if constexpr (F8)
+        o[0] = fp8_block(S.v, j);
+      else
+        code_planes<VB, VQ8, true>(S.v, j, o);
+      vop[buf][nb0 + j][lane] = __builtin_bit_cast(u32x4, o[0]);
+    }
+  };
+
   // ---- scores of a block with quantized keys: sc = t + mref, per token pair
   // class (the class bias is in kb2 / tbias) -----------------------------------
-  auto scores_q = [&](const Buf& B, float sc[2][4]) {
+  // kcode_of(mb, m, out): the key operand(s) of tokens 16 mb + (0..15),
+  // channels 32 m + (0..31); kp: the per-token key parameters
+  auto scores_q = [&](const uint32_t (*kp)[KPD], auto&& kcode_of, float sc[2][4]) {
     if constexpr (KCH) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
         half8 kcode[4][kPlanes<KB>];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) code_planes<KB, KQ8>(B.k[mb], m, kcode[m]);
+        for (int m = 0; m < 4; ++m) kcode_of(mb, m, kcode[m]);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -321,12 +387,7 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
           f32x4 c = {0.f, 0.f, 0.f, 0.f};
           half8 kcode[4][kPlanes<KB>];
 #pragma unroll
-          for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m) {
-            if constexpr (F8)
-              kcode[m][0] = fp8_block(B.k[mb], m);
-            else
-              code_planes<KB, KQ8>(B.k[mb], m, kcode[m]);
-          }
+          for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m) kcode_of(mb, m, kcode[m]);
 #pragma unroll
           for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m)
 #pragma unroll
@@ -337,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
             for (int pl = 0; pl < kPlanes<KB>; ++pl) c = mfma16(kcode[m][pl], bqh[m], c);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t* d = B.kp[mb];
+            const uint32_t* d = kp[mb];
             if constexpr (F8) {
               sd[r] += c[r];
             } else if constexpr (KQ8) {
@@ -383,7 +444,10 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
   // ---- softmax and P.V of one block (t0: its first token).  MASKED (an
   // integral_constant): the causal mask per row and the end of the cache
   // apply; the other blocks are seen whole by every row of the wave.
-  auto softmax_pv = [&](auto masked, float sc[2][4], const Buf& B, int t0) {
+  // vp_in: value parameters of the lane's 8 tokens; vcode_of(nb, out): the
+  // value operand(s) of channels 16 nb + (0..15)
+  auto softmax_pv = [&](auto masked, float sc[2][4], const uint32_t (*vp_in)[VPD], auto&& vcode_of,
+                        int t0) {
     constexpr bool MASKED = decltype(masked)::value;
     auto vis = [&](int mb, int r) { return !MASKED || t0 + 16 * mb + 4 * q4 + r <= p_row; };
     auto present = [&](int mb, int r) { return !MASKED || t0 + 16 * mb + 4 * q4 + r < a.n_total; };
@@ -438,7 +502,7 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int w = 0; w < VPD; ++w) {
-        uint32_t d = B.vp[mb][w];
+        uint32_t d = vp_in[mb][w];
         if constexpr (MASKED) {
           if constexpr (VQ8) {   // two entries (token r = entry / NGV) per dword
             const uint32_t lo = present(mb, (2 * w) / NGV) ? 0x0000ffffu : 0u;
@@ -540,12 +604,8 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int nbk = 0; nbk < 8; ++nbk) {
-      const uint32_t* seg = B.v + (nbk >> 2) * VB;
       half8 vcode[kPlanes<VB>];
-      if constexpr (F8)
-        vcode[0] = fp8_block(seg, nbk & 3);
-      else
-        code_planes<VB, VQ8, true>(seg, nbk & 3, vcode);
+      vcode_of(nbk, vcode);
 #pragma unroll
       for (int pl = 0; pl < kPlanes<VB>; ++pl) oacc[nbk] = mfma16(pal[nbk * NGV / 8], vcode[pl], oacc[nbk]);
 #pragma unroll
@@ -588,44 +648,110 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
     since_flush = 0;
   };
 
-  // ---- blocks seen whole by every row: register pipeline, one block in
-  // flight while one is computed (the prefetch past the last re-reads it) ----
-  const int nf = f_end - blk_lo;
-  if (nf > 0) {
-    int pf = blk_lo, cb = blk_lo;
-    // a paged cache's table entry of the next block to load is read one load
-    // ahead (a scalar load)
-    int pf_page = paged ? table_entry(a.sh, b, pf) : 0;
-    auto next_load = [&](Buf& B) {
-      const int64_t r0 =
-          paged ? page_head_row(a.sh, clamp_page(a.sh, pf_page), h) : prow + (int64_t)pf * kTile;
-      if (pf + 1 < f_end) ++pf;
-      if (paged) pf_page = table_entry(a.sh, b, pf);
-      load_row(B, r0);
+  // operands straight from a block's registers
+  auto kregs = [](const Buf& B) {
+    return [&B](int mb, int m, half8* o) {
+      if constexpr (F8)
+        o[0] = fp8_block(B.k[mb], m);
+      else
+        code_planes<KB, KQ8>(B.k[mb], m, o);
     };
-    auto compute = [&](const Buf& B) {
-      const int blk = cb++;
-      float sc[2][4];
-      __builtin_amdgcn_s_setprio(1);
-      group_for(blk);
-      scores_q(B, sc);
-      __builtin_amdgcn_s_setprio(0);
-      softmax_pv(std::false_type{}, sc, B, blk * kTile);
-      if (++since_flush == kFlush) flush();
+  };
+  auto vregs = [](const Buf& B) {
+    return [&B](int nb, half8* o) {
+      const uint32_t* seg = B.v + (nb >> 2) * VB;
+      if constexpr (F8)
+        o[0] = fp8_block(seg, nb & 3);
+      else
+        code_planes<VB, VQ8, true>(seg, nb & 3, o);
     };
-    Buf b0, b1;
-    next_load(b0);
-    for (int k = 0; k < nf; k += 2) {
-      next_load(b1);
-      compute(b0);
-      if (k + 1 >= nf) break;
-      next_load(b0);
-      compute(b1);
+  };
+  // the next block to load, one load ahead of the block computed; a paged
+  // cache's table entry of it is read one load ahead (a scalar load), and the
+  // prefetch past the last block re-reads it
+  int pf = blk_lo, cb = blk_lo, pf_end = blk_lo;
+  int pf_page = 0;
+  auto start_loads = [&](int end) {
+    pf = cb = blk_lo;
+    pf_end = end;
+    if (paged) pf_page = table_entry(a.sh, b, pf);
+  };
+  auto next_row = [&]() {
+    const int64_t r0 = paged ? page_head_row(a.sh, clamp_page(a.sh, pf_page), h) : prow + (int64_t)pf * kTile;
+    if (pf + 1 < pf_end) ++pf;
+    if (paged) pf_page = table_entry(a.sh, b, pf);
+    return r0;
+  };
+
+  int w_from = f_end;   // first block of the wave's own masked loop
+  if constexpr (SHARE) {
+    // ---- blocks every row of the workgroup sees whole: the four waves unpack
+    // a quarter of each block's codes into a double-buffered LDS operand area
+    // (one barrier per block) and all read every operand from it ----------------
+    const int p_wg = base + tile * qt;   // the workgroup's first (earliest) row
+    const int fs_end = max(blk_lo, min(min(blk_hi, KCH ? qend : blk_hi), (p_wg + 1) / kTile));
+    w_from = fs_end;
+    const int ns = fs_end - blk_lo;   // uniform over the workgroup
+    if (ns > 0) {
+      start_loads(fs_end);
+      auto compute = [&](const SBuf& S, int buf) {
+        const int blk = cb++;
+        float sc[2][4];
+        __builtin_amdgcn_s_setprio(1);
+        group_for(blk);
+        scores_q(S.kp, [&](int mb, int m, half8* o) { o[0] = __builtin_bit_cast(half8, kop[buf][4 * mb + m][lane]); }, sc);
+        __builtin_amdgcn_s_setprio(0);
+        softmax_pv(std::false_type{}, sc, S.vp,
+                   [&](int nb, half8* o) { o[0] = __builtin_bit_cast(half8, vop[buf][nb][lane]); }, blk * kTile);
+        if (++since_flush == kFlush) flush();
+      };
+      // A wave writes buffer i & 1 for block i only after the barrier of
+      // block i - 1, which every wave passes after computing block i - 2, the
+      // last reader of that buffer.
+      SBuf s0, s1;
+      load_share(s0, next_row());
+      for (int k = 0; k < ns; k += 2) {
+        produce(s0, 0);
+        __syncthreads();
+        load_share(s1, next_row());
+        compute(s0, 0);
+        if (k + 1 >= ns) break;
+        produce(s1, 1);
+        __syncthreads();
+        load_share(s0, next_row());
+        compute(s1, 1);
+      }
+    }
+  } else {
+    // ---- blocks every row of the wave sees whole: register pipeline, one
+    // block in flight while one is computed -----------------------------------------
+    const int nf = f_end - blk_lo;
+    if (nf > 0) {
+      start_loads(f_end);
+      auto compute = [&](const Buf& B) {
+        const int blk = cb++;
+        float sc[2][4];
+        __builtin_amdgcn_s_setprio(1);
+        group_for(blk);
+        scores_q(B.kp, kregs(B), sc);
+        __builtin_amdgcn_s_setprio(0);
+        softmax_pv(std::false_type{}, sc, B.vp, vregs(B), blk * kTile);
+        if (++since_flush == kFlush) flush();
+      };
+      Buf b0, b1;
+      load_row(b0, next_row());
+      for (int k = 0; k < nf; k += 2) {
+        load_row(b1, next_row());
+        compute(b0);
+        if (k + 1 >= nf) break;
+        load_row(b0, next_row());
+        compute(b1);
+      }
     }
   }
   // ---- the wave's other blocks: seen in part (causal mask), or keys in the
   // unquantized tail -----------------------------------------------------------------
-  for (int blk = f_end; blk < wblk_hi; ++blk) {
+  for (int blk = max(w_from, blk_lo); blk < wblk_hi; ++blk) {
     Buf B;
     load_row(B, block_row(blk));
     float sc[2][4];
@@ -633,9 +759,9 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
       scores_tail(blk, sc);
     } else {
       group_for(blk);
-      scores_q(B, sc);
+      scores_q(B.kp, kregs(B), sc);
     }
-    softmax_pv(std::true_type{}, sc, B, blk * kTile);
+    softmax_pv(std::true_type{}, sc, B.vp, vregs(B), blk * kTile);
     if (++since_flush == kFlush) flush();
   }
   if (since_flush > 0) flush();

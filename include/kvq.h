@@ -445,9 +445,12 @@ int32_t kvq_decode_path(const kvq_config* cfg);
  * kvq_set_decode_events -- optional instrumentation for profiling.  With
  * start and stop non-NULL hipEvent_t handles (created by the caller, which
  * keeps ownership), the next kvq_decode_attention call on this host thread
- * records start on its stream right before the token-streaming kernel and
- * stop right after it, so that start..stop brackets that kernel alone (not
- * the split merge).  The next call that passes validation and launches
+ * has them recorded at the start and at the end of its token-streaming
+ * kernel (hipExtLaunchKernel; the first and the last launch when a
+ * configuration needs several), so that start..stop is that kernel's
+ * execution alone: not the dispatch gap before it, the sink's kernel or the
+ * split merge.  Without a streaming kernel (no quantized tokens) both are
+ * recorded back to back.  The next call that passes validation and launches
  * uses them and clears them; NULL, NULL clears them without a launch.  Host only; returns KVQ_OK, or INVALID_ARGUMENT when exactly
  * one of the two is NULL.
  */

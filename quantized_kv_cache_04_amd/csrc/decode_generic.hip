@@ -21,6 +21,7 @@
 #include <hip/hip_runtime.h>
 
 #include "splitk.h"
+#include "timed_launch.h"
 
 namespace kvq {
 namespace {
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(256) void dec_generic_kernel(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(dec_generic_kernel, dim3(a.splits, a.sh.B * a.sh.Hkv), dim3(256), 0, stream, a);
+  launch_timed(dec_generic_kernel, dim3(a.splits, a.sh.B * a.sh.Hkv), dim3(256), 0u, stream, a);
   return hipGetLastError();
 }
 

@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 
 #include "splitk.h"
+#include "timed_launch.h"
 
 namespace kvq {
 namespace {
@@ -408,10 +409,10 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
 template <bool ROPE>
 void launch_r(const DecodeArgs& a, unsigned grid, hipStream_t s) {
   const bool ko = a.k.k_out > 0, vo = a.v.k_out > 0;
-  if (ko && vo) hipLaunchKernelGGL((dec_lut_kernel<ROPE, true, true>), dim3(grid), dim3(256), 0, s, a);
-  else if (ko) hipLaunchKernelGGL((dec_lut_kernel<ROPE, true, false>), dim3(grid), dim3(256), 0, s, a);
-  else if (vo) hipLaunchKernelGGL((dec_lut_kernel<ROPE, false, true>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((dec_lut_kernel<ROPE, false, false>), dim3(grid), dim3(256), 0, s, a);
+  if (ko && vo) launch_timed(dec_lut_kernel<ROPE, true, true>, dim3(grid), dim3(256), 0u, s, a);
+  else if (ko) launch_timed(dec_lut_kernel<ROPE, true, false>, dim3(grid), dim3(256), 0u, s, a);
+  else if (vo) launch_timed(dec_lut_kernel<ROPE, false, true>, dim3(grid), dim3(256), 0u, s, a);
+  else launch_timed(dec_lut_kernel<ROPE, false, false>, dim3(grid), dim3(256), 0u, s, a);
 }
 
 }  // namespace

@@ -37,6 +37,7 @@
 
 #include "mfma_codes.h"
 #include "splitk.h"
+#include "timed_launch.h"
 
 namespace kvq {
 namespace {
@@ -809,8 +810,8 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 template <int KB, bool KCH, bool KQ8, int NGK, int VB, bool VQ8, int NGV, bool F8 = false>
 void launch_t(const DecodeArgs& a, hipStream_t s) {
   const size_t lds = KCH ? (size_t)4 * a.kp_groups * 32 * sizeof(u32x4) : 0;
-  hipLaunchKernelGGL((dec_mfma_kernel<KB, KCH, KQ8, NGK, VB, VQ8, NGV, F8>),
-                     dim3(a.splits, a.sh.B * a.sh.Hkv), dim3(256), lds, s, a);
+  launch_timed(dec_mfma_kernel<KB, KCH, KQ8, NGK, VB, VQ8, NGV, F8>, dim3(a.splits, a.sh.B * a.sh.Hkv),
+               dim3(256), (uint32_t)lds, s, a);
 }
 
 template <int KB, bool KCH, bool KQ8, int NGK, int NGV>
@@ -888,9 +889,17 @@ hipError_t launch_decode_mfma(const DecodeArgs& a_in, hipStream_t s) {
     // the KV heads that have it (the other workgroups return at once)
     bool seen[5] = {false, false, false, false, false};
     for (int h = 0; h < a.sh.Hkv; ++h) seen[a.v.per_head ? a.v.ngh[h] : a.v.ng] = true;
+    // launches: one per class (one in all for uniform values); the profiling
+    // events go to the first and the last
+    int last = 0, first = 0;
+    for (int c : {4, 2, 1}) if (seen[c]) first = c;
+    for (int c : {1, 2, 4}) if (seen[c]) last = c;
+    if (!a.v.per_head) last = first;
     for (int c : {1, 2, 4}) {
       if (!seen[c]) continue;
       DecodeArgs ac = a;
+      ac.ev_start = c == first ? a.ev_start : nullptr;
+      ac.ev_stop = c == last ? a.ev_stop : nullptr;
       ac.head_class = c;
       ac.v.ng = c;
       if (!ac.k.per_channel) ac.k.ng = c;

@@ -645,13 +645,19 @@ kvq_status kvq::decode_attention_impl(const kvq_config* cfg, const kvq_cache* ca
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
   g_ev_start = g_ev_stop = nullptr;
-  hipError_t e = ev0 ? hipEventRecord(ev0, s) : hipSuccess;
-  if (e == hipSuccess && a.n_ctx > 0) {
+  hipError_t e = hipSuccess;
+  if (a.n_ctx > 0) {
+    // the profiling events are recorded at the streaming kernel's own start
+    // and end (the sink's kernel and the merge are not part of it)
+    a.ev_start = ev0;
+    a.ev_stop = ev1;
     e = path == KVQ_PATH_MFMA ? launch_decode_mfma(a, s)
         : path == KVQ_PATH_LUT ? launch_decode_lut(a, s)
                                : launch_decode_generic(a, s);
+  } else if (ev0) {   // no streaming kernel: an empty interval
+    e = hipEventRecord(ev0, s);
+    if (e == hipSuccess) e = hipEventRecord(ev1, s);
   }
-  if (e == hipSuccess && ev1) e = hipEventRecord(ev1, s);
   if (e == hipSuccess && n_sink > 0) e = launch_decode_generic(sa, s);
   if (e == hipSuccess && !a.direct) e = launch_combine(a, s);
   return device_status(e, "decode attention");

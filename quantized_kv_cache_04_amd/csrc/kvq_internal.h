@@ -135,6 +135,9 @@ struct DecodeArgs {
   int kp_groups;        // matrix-core kernel: key groups staged in LDS per wave (0 = none)
   int head_class = 0;   // matrix-core kernel, per-head group sizes: only the KV heads
                         // whose values have this many groups per token (0 = all)
+  // profiling (kvq_set_decode_events): recorded at the start and the end of
+  // the streaming kernel (the first and the last of its launches)
+  hipEvent_t ev_start = nullptr, ev_stop = nullptr;
 };
 
 // kvq_decode_attention with the split-K partial states in partial_ws

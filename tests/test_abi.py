@@ -302,6 +302,12 @@ def test_prefill_kernel_selection():
     cfg = kvq.config_from_workload
     for cid in (1, 2, 3, 5):     # 4-bit per-channel K with values in groups of 32 / 128, q8_0, 3-bit
         assert kvq.prefill_kernel(cfg(make_workload(cid, ctx=256))) == "codes", cid
+    # the cases of the GPU token-axis split test cover both kernels
+    for cid, over, sink, want in ((4, dict(n_kv_heads=2, ctx=2000), 0, "staged"),
+                                  (5, dict(batch=1, n_kv_heads=2, ctx=3000), 40, "staged"),
+                                  (5, dict(batch=1, n_kv_heads=2, ctx=3001), 0, "codes"),
+                                  (2, dict(ctx=4000), 0, "codes")):
+        assert kvq.prefill_kernel(cfg(make_workload(cid, **over), sink_tokens=sink)) == want
     assert kvq.prefill_kernel(cfg(make_workload(4, ctx=256))) == "staged"   # codebooks, RoPE
     w5 = make_workload(5, ctx=256)
     assert kvq.prefill_kernel(cfg(w5, sink_tokens=4)) == "staged"

@@ -107,10 +107,19 @@ def test_prefill_is_deterministic_and_leaves_the_cache_alone():
     assert torch.equal(cache.buffer, before)
 
 
-@pytest.mark.parametrize("name,cfg_id,over,chunks,n_q,sink", [
+SPLIT_CASES = [
+    # the staging kernel (codebooks with RoPE; a sink)
     ("split_nuq_rope", 4, dict(n_kv_heads=2, ctx=2000), [1900, 100], 100, 0),
     ("split_serving_sink", 5, dict(batch=1, n_kv_heads=2, ctx=3000), [3000], 64, 40),
-], ids=["split_nuq_rope", "split_serving_sink"])
+    # the code-operand kernel: per-channel keys with their tail, and q8_0
+    # (whose waves share the unpacking)
+    ("split_serving", 5, dict(batch=1, n_kv_heads=2, ctx=3001), [2900, 101], 101, 0),
+    ("split_q8_0", 2, dict(ctx=4000), [4000], 70, 0),
+]
+
+
+@pytest.mark.parametrize("name,cfg_id,over,chunks,n_q,sink", SPLIT_CASES,
+                         ids=[c[0] for c in SPLIT_CASES])
 def test_token_axis_split_matches_the_unsplit_kernel(name, cfg_id, over, chunks, n_q, sink):
     """With a workspace the token axis is split over several workgroups and
     their partial states are merged; without one it is not.  Both match the

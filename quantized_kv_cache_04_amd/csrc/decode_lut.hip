@@ -27,12 +27,12 @@
 //    both 4-bit indices of a lane in one byte per token, and one LDS dword
 //    per (centroid, lane) holds both channels' centroids, so lane l always
 //    reads bank l;
-//  * outliers: a token's CSR row holds its outliers over all heads in
-//    column order, with an end offset per head; each wave reads only its head's
-//    entries (the lanes of a token share them) and adds (val - centroid)
-//    corrections to the token's score for keys and, through the wave's LDS
-//    channel sums, to the value sums.  Waves of a workgroup never wait for
-//    each other inside the token loop.
+//  * outliers: every 32-token tile indexes its outliers by KV head (the
+//    per-tile index next to the CSR rows); each wave reads its head's
+//    entries of the chunk, one per lane, and adds (val - centroid)
+//    corrections to the token's score for keys (through LDS per-token sums)
+//    and, through the wave's LDS channel sums, to the value sums.  Waves of
+//    a workgroup never wait for each other inside the token loop.
 //
 // Each wave leaves an (o, m, l) partial per split, or the output when the
 // context is one split and there is no attention sink.

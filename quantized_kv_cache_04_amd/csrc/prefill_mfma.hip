@@ -243,21 +243,25 @@ __device__ __forceinline__ void value_values(int kind, const Raw& R, int c, int 
 }
 
 // Outliers replace their dense value in the staged tile (quantized tokens
-// tq0 + tk, tk < n_valid): entry e of the CSR row of token tk (all heads of
-// the token) per thread; entries of other heads are skipped.  Keys go to the
-// fp32 stage (RoPE follows), values to the fp16 planes.
+// tq0 + tk, tk < n_valid).  The tile's per-tile index lists the KV head's
+// entries contiguously (off[h] .. off[h + 1] - 1 of the tile's block, one
+// dword each: channel, token in the tile, the dense index replaced, fp16
+// value), so one offset read and one load per entry find them, thread i
+// taking entry i.  Keys go to the fp32 stage (RoPE follows), values to the
+// fp16 planes.
 template <bool KEY>
 __device__ __forceinline__ void stage_outliers(const DevTensor& ten, PreLds& S, int tid, int b,
                                                int h, int64_t tq0, int n_valid, const DevShape& sh) {
-  const int ko = ten.k_out;
-  for (int idx = tid; idx < n_valid * ko; idx += 256) {
-    const int tk = idx / ko;
-    const int64_t rr = csr_row(sh, b, tq0 + tk);
-    const int e = ten.row_ptr[rr] + idx % ko;
-    if (e >= ten.row_ptr[rr + 1]) continue;
-    const int cc = (ten.col[e] & 0xfff) - h * kD;
-    if (cc < 0 || cc >= kD) continue;
-    const float v = h2f(ten.val[e]);
+  const int64_t tile = csr_row(sh, b, tq0) >> 5;   // the block is one tile (a page when paged)
+  const int o_row = (sh.Hkv + 8) / 8 * 8;
+  const uint16_t* off = ten.toff + tile * o_row;
+  const int e0 = off[h], e1 = off[h + 1];
+  const uint32_t* ent = ten.tent + tile * ((int64_t)kTile * ten.k_out);
+  for (int i = e0 + tid; i < e1; i += 256) {
+    const uint32_t en = ent[i];
+    const int tk = (int)((en >> 7) & 31u), cc = (int)(en & (kD - 1));
+    if (tk >= n_valid) continue;
+    const float v = h2f((uint16_t)(en >> 16));
     if (KEY) {
       S.kf[tk][cc] = v;
     } else {

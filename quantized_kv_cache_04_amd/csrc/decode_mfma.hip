@@ -548,13 +548,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int nbk = 0; nbk < 8; ++nbk) {
       const uint32_t* seg = vl + (nbk >> 2) * VB;
-      half8 vcode[kPlanes<VB>];
-      if constexpr (F8)
-        vcode[0] = fp8_block(seg, nbk & 3);
-      else
-        code_planes<VB, VQ8, true>(seg, nbk & 3, vcode);
-#pragma unroll
-      for (int pl = 0; pl < kPlanes<VB>; ++pl) oacc[nbk] = mfma16(pa[nbk * NGV / 8], vcode[pl], oacc[nbk]);
+      oacc[nbk] = mfma16(pa[nbk * NGV / 8], code_block<VB, VQ8, true, F8>(seg, nbk & 3), oacc[nbk]);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -624,12 +618,7 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
       for (int mb = 0; mb < 2; ++mb) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          half8 kcode[kPlanes<KB>];
-          code_planes<KB, KQ8>(B.k[mb], m, kcode);
-#pragma unroll
-          for (int pl = 0; pl < kPlanes<KB>; ++pl) c = mfma16(kcode[pl], bk[m], c);
-        }
+        for (int m = 0; m < 4; ++m) c = mfma16(seg_block<KB, KQ8>(B.k[mb], m), bk[m], c);
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[mb][r] = c[r] * kscale + kb2[pe_class<VB>(r)];
       }
@@ -645,15 +634,8 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
         for (int gi = 0; gi < NGK; ++gi) {
           f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m) {
-            half8 kcode[kPlanes<KB>];
-            if constexpr (F8)
-              kcode[0] = fp8_block(B.k[mb], m);
-            else
-              code_planes<KB, KQ8>(B.k[mb], m, kcode);
-#pragma unroll
-            for (int pl = 0; pl < kPlanes<KB>; ++pl) c = mfma16(kcode[pl], bq[m], c);
-          }
+          for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m)
+            c = mfma16(code_block<KB, KQ8, false, F8>(B.k[mb], m), bq[m], c);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const uint32_t* d = B.kp[mb];

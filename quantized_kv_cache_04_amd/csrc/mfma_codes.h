@@ -83,25 +83,21 @@ struct Unpack<4> {
 
 template <>
 struct Unpack<3> {
-  // Two operands (bit planes): pair r's low two bits as lo2 * 4^r and its
-  // high bit as hi1 * 4 * 4^r, so the two products add up to code * 4^r (the
-  // factor 4^-r sits in the other operand).  dlo = D[m / 2] holds the low
-  // bits of pair r at bit 2r (+ 8 for odd m); d2 holds the high bit at
-  // H = 8 (m / 2) + 2r + (m % 2), which one shift per block moves to 2r + 2.
-  // FLIP complements the odd pairs: their low and high bits both sit under
-  // the mask 0xcccc of each half.
+  // Pair r as code * 4^r (the factor 4^-r sits in the other operand): its
+  // low two bits come from dlo = D[m / 2] at bit 2r (+ 8 for odd m), its high
+  // bit from d2, where it sits at H = 8 (m / 2) + 2r + (m % 2) and one shift
+  // per block moves it to 2r + 2.  The two fields are disjoint, so one AND
+  // and one AND-OR give the whole code.  FLIP complements the odd pairs:
+  // their low and high bits both sit under the mask 0xcccc of each half.
   template <bool FLIP>
-  __device__ static __forceinline__ void run(uint32_t dlo, uint32_t d2, int m, uint32_t lo[4],
-                                             uint32_t hi[4]) {
+  __device__ static __forceinline__ void run(uint32_t dlo, uint32_t d2, int m, uint32_t out[4]) {
     if (FLIP) { dlo ^= 0xccccccccu; d2 ^= 0xccccccccu; }
     const uint32_t l = (m & 1) ? (dlo >> 8) : dlo;
     const int sh = 8 * (m >> 1) + (m & 1) - 2;
     const uint32_t h = sh >= 0 ? (d2 >> sh) : (d2 << (-sh));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      lo[r] = l & (0x00030003u << (2 * r));
-      hi[r] = h & (0x00010001u << (2 * r + 2));
-    }
+    for (int r = 0; r < 4; ++r)
+      out[r] = (l & (0x00030003u << (2 * r))) | (h & (0x00010001u << (2 * r + 2)));
   }
 };
 
@@ -116,15 +112,18 @@ struct Unpack<8> {
   }
 };
 
-// codes of block m of a segment of BITS-bit codes held in ``seg`` dwords.
-// FLIP: the odd pairs hold the complemented codes (2^BITS - 1) - c (signed
-// 8-bit: 127 - q, the complement of the offset code q + 128).
+// codes of block m of a segment of BITS-bit codes held in ``seg`` dwords
+// (3-bit codes: the 12-byte segment of 32 codes, low-bit dwords D[0..1] and
+// the high-bit dword D[2]).  FLIP: the odd pairs hold the complemented codes
+// (2^BITS - 1) - c (signed 8-bit: 127 - q, the complement of the offset code
+// q + 128).
 template <int BITS, bool SIGNED, bool FLIP = false>
 __device__ __forceinline__ half8 seg_block(const uint32_t* seg, int m) {
-  static_assert(BITS != 3, "3-bit codes unpack into two planes: code_planes");
   uint32_t o[4];
   if constexpr (BITS == 4) {
     Unpack<4>::run<FLIP>(seg[m], o);
+  } else if constexpr (BITS == 3) {
+    Unpack<3>::run<FLIP>(seg[m >> 1], seg[2], m, o);
   } else {
     // pair r takes byte r of both dwords: bytes 1 and 3 are the odd pairs
     constexpr uint32_t kFlipMask = SIGNED ? 0x7f807f80u : 0xff00ff00u;
@@ -133,22 +132,6 @@ __device__ __forceinline__ half8 seg_block(const uint32_t* seg, int m) {
     Unpack<8>::run(d0, d1, o);
   }
   return as_h8(o[0], o[1], o[2], o[3]);
-}
-
-// MFMA operands per block of BITS-bit codes (3-bit codes: two bit planes)
-template <int BITS>
-constexpr int kPlanes = BITS == 3 ? 2 : 1;
-
-template <int BITS, bool SIGNED, bool FLIP = false>
-__device__ __forceinline__ void code_planes(const uint32_t* seg, int m, half8 out[kPlanes<BITS>]) {
-  if constexpr (BITS == 3) {
-    uint32_t lo[4], hi[4];
-    Unpack<3>::run<FLIP>(seg[m >> 1], seg[2], m, lo, hi);
-    out[0] = as_h8(lo[0], lo[1], lo[2], lo[3]);
-    out[1] = as_h8(hi[0], hi[1], hi[2], hi[3]);
-  } else {
-    out[0] = seg_block<BITS, SIGNED, FLIP>(seg, m);
-  }
 }
 
 // FP8 E5M2 block m of a segment of byte codes: the bytes become the high
@@ -161,6 +144,15 @@ __device__ __forceinline__ half8 fp8_block(const uint32_t* seg, int m) {
   for (int r = 0; r < 4; ++r)
     o[r] = __builtin_amdgcn_perm(d1, d0, ((uint32_t)(4 + r) << 24) | 0x000c0000u | ((uint32_t)r << 8) | 0x0cu);
   return as_h8(o[0], o[1], o[2], o[3]);
+}
+
+// operand of block m of a segment: FP8 E5M2 bytes (F8) or BITS-bit codes
+template <int BITS, bool SIGNED, bool FLIP, bool F8>
+__device__ __forceinline__ half8 code_block(const uint32_t* seg, int m) {
+  if constexpr (F8)
+    return fp8_block(seg, m);
+  else
+    return seg_block<BITS, SIGNED, FLIP>(seg, m);
 }
 
 // factor of pair r that the other operand of a code operand must carry

@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
     load_dw<2 * VB>(V.codes + r0 * (4 * VB * 4) + v_lane_off, B.v);
   };
 
-  // ---- shared unpacking (one-plane formats): wave w loads and unpacks key
+  // ---- shared unpacking (byte formats): wave w loads and unpacks key
   // blocks m = 2 (w & 1), +1 of tokens 16 (w >> 1) + (0..15) and value blocks
   // nb = 2 w, 2 w + 1, for every lane's slot of those operands ----------------------
   const int mb_s = wave >> 1, m0 = 2 * (wave & 1), nb0 = 2 * wave;
@@ -333,45 +333,29 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
   };
   auto produce = [&](const SBuf& S, int buf) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      half8 o[1];
-      if constexpr (F8)
-        o[0] = fp8_block(S.k, j);
-      else
-        code_planes<KB, KQ8>(S.k, j, o);
-      kop[buf][4 * mb_s + m0 + j][lane] = __builtin_bit_cast(u32x4, o[0]);
-    }
+    for (int j = 0; j < 2; ++j)
+      kop[buf][4 * mb_s + m0 + j][lane] = __builtin_bit_cast(u32x4, code_block<KB, KQ8, false, F8>(S.k, j));
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      half8 o[1];
-      if constexpr (F8)
-        o[0] = fp8_block(S.v, j);
-      else
-        code_planes<VB, VQ8, true>(S.v, j, o);
-      vop[buf][nb0 + j][lane] = __builtin_bit_cast(u32x4, o[0]);
-    }
+    for (int j = 0; j < 2; ++j)
+      vop[buf][nb0 + j][lane] = __builtin_bit_cast(u32x4, code_block<VB, VQ8, true, F8>(S.v, j));
   };
 
   // ---- scores of a block with quantized keys: sc = t + mref, per token pair
   // class (the class bias is in kb2 / tbias) -----------------------------------
-  // kcode_of(mb, m, out): the key operand(s) of tokens 16 mb + (0..15),
+  // kcode_of(mb, m): the key operand of tokens 16 mb + (0..15),
   // channels 32 m + (0..31); kp: the per-token key parameters
   auto scores_q = [&](const uint32_t (*kp)[KPD], auto&& kcode_of, float sc[2][4]) {
     if constexpr (KCH) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
-        half8 kcode[4][kPlanes<KB>];
+        half8 kcode[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) kcode_of(mb, m, kcode[m]);
+        for (int m = 0; m < 4; ++m) kcode[m] = kcode_of(mb, m);
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < 4; ++m) c = mfma16(kcode[m], bql[m], c);
 #pragma unroll
-          for (int pl = 0; pl < kPlanes<KB>; ++pl) c = mfma16(kcode[m][pl], bql[m], c);
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int pl = 0; pl < kPlanes<KB>; ++pl) c = mfma16(kcode[m][pl], bqh[m], c);
+        for (int m = 0; m < 4; ++m) c = mfma16(kcode[m], bqh[m], c);
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[mb][r] = c[r] * kscale + kb2[pe_class<VB>(r)];
       }
@@ -385,17 +369,13 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
 #pragma unroll
         for (int gi = 0; gi < NGK; ++gi) {
           f32x4 c = {0.f, 0.f, 0.f, 0.f};
-          half8 kcode[4][kPlanes<KB>];
+          half8 kcode[4];
 #pragma unroll
-          for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m) kcode_of(mb, m, kcode[m]);
+          for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m) kcode[m] = kcode_of(mb, m);
 #pragma unroll
-          for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m)
+          for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m) c = mfma16(kcode[m], bql[m], c);
 #pragma unroll
-            for (int pl = 0; pl < kPlanes<KB>; ++pl) c = mfma16(kcode[m][pl], bql[m], c);
-#pragma unroll
-          for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m)
-#pragma unroll
-            for (int pl = 0; pl < kPlanes<KB>; ++pl) c = mfma16(kcode[m][pl], bqh[m], c);
+          for (int m = gi * 4 / NGK; m < (gi + 1) * 4 / NGK; ++m) c = mfma16(kcode[m], bqh[m], c);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const uint32_t* d = kp[mb];
@@ -444,8 +424,8 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
   // ---- softmax and P.V of one block (t0: its first token).  MASKED (an
   // integral_constant): the causal mask per row and the end of the cache
   // apply; the other blocks are seen whole by every row of the wave.
-  // vp_in: value parameters of the lane's 8 tokens; vcode_of(nb, out): the
-  // value operand(s) of channels 16 nb + (0..15)
+  // vp_in: value parameters of the lane's 8 tokens; vcode_of(nb): the
+  // value operand of channels 16 nb + (0..15)
   auto softmax_pv = [&](auto masked, float sc[2][4], const uint32_t (*vp_in)[VPD], auto&& vcode_of,
                         int t0) {
     constexpr bool MASKED = decltype(masked)::value;
@@ -604,12 +584,9 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int nbk = 0; nbk < 8; ++nbk) {
-      half8 vcode[kPlanes<VB>];
-      vcode_of(nbk, vcode);
-#pragma unroll
-      for (int pl = 0; pl < kPlanes<VB>; ++pl) oacc[nbk] = mfma16(pal[nbk * NGV / 8], vcode[pl], oacc[nbk]);
-#pragma unroll
-      for (int pl = 0; pl < kPlanes<VB>; ++pl) oacc[nbk] = mfma16(pah[nbk * NGV / 8], vcode[pl], oacc[nbk]);
+      const half8 vcode = vcode_of(nbk);
+      oacc[nbk] = mfma16(pal[nbk * NGV / 8], vcode, oacc[nbk]);
+      oacc[nbk] = mfma16(pah[nbk * NGV / 8], vcode, oacc[nbk]);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -650,21 +627,10 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
 
   // operands straight from a block's registers
   auto kregs = [](const Buf& B) {
-    return [&B](int mb, int m, half8* o) {
-      if constexpr (F8)
-        o[0] = fp8_block(B.k[mb], m);
-      else
-        code_planes<KB, KQ8>(B.k[mb], m, o);
-    };
+    return [&B](int mb, int m) { return code_block<KB, KQ8, false, F8>(B.k[mb], m); };
   };
   auto vregs = [](const Buf& B) {
-    return [&B](int nb, half8* o) {
-      const uint32_t* seg = B.v + (nb >> 2) * VB;
-      if constexpr (F8)
-        o[0] = fp8_block(seg, nb & 3);
-      else
-        code_planes<VB, VQ8, true>(seg, nb & 3, o);
-    };
+    return [&B](int nb) { return code_block<VB, VQ8, true, F8>(B.v + (nb >> 2) * VB, nb & 3); };
   };
   // the next block to load, one load ahead of the block computed; a paged
   // cache's table entry of it is read one load ahead (a scalar load), and the
@@ -699,10 +665,10 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
         float sc[2][4];
         __builtin_amdgcn_s_setprio(1);
         group_for(blk);
-        scores_q(S.kp, [&](int mb, int m, half8* o) { o[0] = __builtin_bit_cast(half8, kop[buf][4 * mb + m][lane]); }, sc);
+        scores_q(S.kp, [&](int mb, int m) { return __builtin_bit_cast(half8, kop[buf][4 * mb + m][lane]); }, sc);
         __builtin_amdgcn_s_setprio(0);
         softmax_pv(std::false_type{}, sc, S.vp,
-                   [&](int nb, half8* o) { o[0] = __builtin_bit_cast(half8, vop[buf][nb][lane]); }, blk * kTile);
+                   [&](int nb) { return __builtin_bit_cast(half8, vop[buf][nb][lane]); }, blk * kTile);
         if (++since_flush == kFlush) flush();
       };
       // A wave writes buffer i & 1 for block i only after the barrier of

@@ -281,22 +281,26 @@ def main():
         c = caches[i % copies]
         if inst is not None:
             st_s[inst].record(stream)
-        if serving:
-            kn, vn, qn = steps_tok[i]
-            c.append(kn, vn, stream=stream)
-            if inst is not None:
-                flush_step.append(bool(k_group) and c.n_ctx % k_group == 0)
-            qq = qn
-        else:
-            qq = q
-        if inst is not None:
             dec_s[inst].record(stream)
             kvq.set_decode_events(ker_s[inst], ker_e[inst])
-        c.decode(qq, out=out, stream=stream)
+        streamed = c.n_ctx          # tokens the streaming kernel reads (serving: fused steps)
+        if serving:
+            # one call appends the token and decodes over the cache that holds
+            # it; the streaming kernel reads the tokens cached before the step
+            # unless the append closes a key group (then append, then decode)
+            kn, vn, qn = steps_tok[i]
+            fused = kvq.append_decode_fused(cfg, c.n_ctx)
+            c.append_decode(kn, vn, qn, out=out, stream=stream)
+            if not fused:
+                streamed = c.n_ctx
+            if inst is not None:
+                flush_step.append(bool(k_group) and c.n_ctx % k_group == 0)
+        else:
+            c.decode(q, out=out, stream=stream)
         if inst is not None:
             dec_e[inst].record(stream)
             st_e[inst].record(stream)
-            inst_bytes.append(kvq.cache_bytes(cfg, c.n_ctx))
+            inst_bytes.append(kvq.cache_bytes(cfg, streamed))
         else:
             step_bytes.append(kvq.cache_bytes(cfg, c.n_ctx))
 
@@ -377,7 +381,8 @@ def main():
         "config": {"workload": wl, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ctx": w.ctx,
                    "k_format": _fmt(w.k), "v_format": _fmt(w.v),
-                   "step": "append 1 token/sequence + decode" if serving else "decode",
+                   "step": ("append 1 token/sequence + decode (one kvq_append_decode call)"
+                            if serving else "decode"),
                    "decode_kernel": kernel, "cache_copies": copies,
                    "paged": ({"pages": n_pages, "page_tokens": 32, "table": args.paged}
                              if args.paged else None),

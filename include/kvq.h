@@ -355,6 +355,42 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
                                 int32_t out_dtype, void* stream);
 
 /*
+ * kvq_append_decode -- one serving step: append one token per sequence and
+ * decode over the cache that now holds it.  Cache bytes, n_ctx and out are
+ * those of kvq_quantize_append(cfg, cache, k_new, v_new, 1, stream)
+ * followed by kvq_decode_attention(cfg, cache, q, q_pos, sm_scale, out,
+ * out_dtype, stream): the same bytes, the same attention to rounding
+ * (NIAH page 1.1 and 2.2: only the appended row is quantized; Memory-killer
+ * page 1.3 and 4.2: each generated token streams the cache once).
+ * Where kvq_append_decode_fused says so, the append takes no launch of its
+ * own: the decode kernels stream the n_ctx tokens cached before the step,
+ * and the launch that merges their split softmax states also encodes the
+ * new token into the cache and adds its term (key and value as the codes
+ * just written stand for them).  Otherwise the two calls run in turn.
+ *   k_new, v_new: device [B][1][Hkv][d] of kv_dtype, contiguous.  q, q_pos,
+ *   sm_scale, out, out_dtype: as kvq_decode_attention; q is the new
+ *   token's query (position n_ctx before the call).  On success n_ctx
+ *   grows by one.  Writes the workspace region of cache->base, as decode.
+ * Errors: INVALID_ARGUMENT and UNSUPPORTED as the two calls, CAPACITY when
+ *   n_ctx == max_ctx (before any launch), DEVICE.
+ */
+kvq_status kvq_append_decode(const kvq_config* cfg, kvq_cache* cache, const void* k_new,
+                             const void* v_new, const void* q, const int32_t* q_pos,
+                             float sm_scale, void* out, int32_t out_dtype, void* stream);
+
+/*
+ * kvq_append_decode_fused -- 1 when kvq_append_decode on a cache of n_ctx
+ * tokens runs the fused step, 0 when it runs the two calls in turn.  Fused:
+ * keys and values in ASYM_MINMAX, ASYM_ABSMAX_OFFSET, SYM_Q8_0, FP8_E5M2 or
+ * raw storage (so no codebook or outliers), per-token keys or per-channel
+ * keys whose current group stays open after the append (the token goes to
+ * the unquantized tail), no RoPE, n_ctx >= sink_tokens, at most 128 query
+ * heads per KV head.  Host only; a negative status for an invalid
+ * configuration or n_ctx outside [0, max_ctx).
+ */
+int32_t kvq_append_decode_fused(const kvq_config* cfg, int64_t n_ctx);
+
+/*
  * kvq_decode_attention_scratch -- kvq_decode_attention for callers that
  * cannot allocate device memory or write outside the buffers they pass
  * (code under HIP graph capture, serving loops and harnesses that forbid
@@ -470,7 +506,8 @@ const char* kvq_last_error(void);
    (kvq_tensor_regions.head_count); 109 replaces them by per-head end
    offsets (kvq_tensor_regions.head_end); 110 replaces those by the
    per-tile index (kvq_tensor_regions.tile_off, tile_ent); 111 adds
-   kvq_prefill_kernel. */
+   kvq_prefill_kernel; 112 adds kvq_append_decode and
+   kvq_append_decode_fused. */
 int32_t kvq_abi_version(void);
 
 #ifdef __cplusplus

@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
+#include "splitk.h"
 
 namespace kvq {
 namespace {
@@ -44,19 +45,28 @@ __device__ __forceinline__ uint32_t cb_code(const uint16_t* cb, float x) {
 // per-token uniform formats the group statistics are reduced over the G/8
 // lanes of the group.  Writes the group's parameters (first lane of each
 // group) at ``prm_row`` unless it is null, and returns the 8 codes as bytes
-// (two's complement for q8_0).
+// (two's complement for q8_0).  ``dq`` (optional) receives the values the
+// codes stand for, as the decode kernels reconstruct them.
 __device__ __forceinline__ uint2 encode8(const DevTensor& t, int h, int j8, const float x[8],
-                                         void* prm_row) {
+                                         void* prm_row, float* dq = nullptr) {
   const int c0 = 8 * j8;
   uint32_t q[8];
   if (t.quant == KVQ_QUANT_CODEBOOK) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[e] = cb_code(t.codebook + ((int64_t)h * kD + c0 + e) * 16, x[e]);
+    if (dq) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dq[e] = h2f(t.codebook[((int64_t)h * kD + c0 + e) * 16 + q[e]]);
+    }
   } else if (t.quant == KVQ_QUANT_FP8_E5M2) {
     // one float32 division per element, as the format defines it
     const float s = fp8_scale(t, h);
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[e] = f_to_e5m2(x[e] / s);
+    if (dq) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dq[e] = e5m2_to_f(q[e]) * s;
+    }
   } else {
     float lo = x[0], hi = x[0], am = fabsf(x[0]);
 #pragma unroll
@@ -81,6 +91,7 @@ __device__ __forceinline__ uint2 encode8(const DevTensor& t, int h, int j8, cons
         float v = s == 0.0f ? 0.0f : rintf(x[e] / s);
         v = fminf(fmaxf(v, -128.0f), 127.0f);
         q[e] = (uint32_t)((int)v & 0xff);
+        if (dq) dq[e] = v * s;
       }
       if (writer) static_cast<uint16_t*>(prm_row)[grp] = sh;
     } else {
@@ -96,6 +107,7 @@ __device__ __forceinline__ uint2 encode8(const DevTensor& t, int h, int j8, cons
       for (int e = 0; e < 8; ++e) {
         float v = s == 0.0f ? 0.0f : rintf((x[e] - z) / s);
         q[e] = (uint32_t)fminf(fmaxf(v, 0.0f), qmax);
+        if (dq) dq[e] = (float)q[e] * s + z;
       }
       if (writer) static_cast<uint32_t*>(prm_row)[grp] = (uint32_t)sh | ((uint32_t)zh << 16);
     }
@@ -276,6 +288,180 @@ __global__ __launch_bounds__(256) void enc_vtile_kernel(DevShape sh, DevTensor t
     if (nm == 0) continue;
     if (nm != 0xffffffffu) nb |= tile_dw[W] & ~nm;
     tile_dw[W] = nb;
+  }
+}
+
+// ---- one serving step: the new token, appended and merged ------------------------
+// One workgroup per (sequence b, KV head h), run after the decode kernels
+// have streamed the tokens cached before the step into split partial
+// states.  It encodes the step's token (position pos of the quantized
+// cache) exactly as an append of it would -- wave 0 the value, wave 1 the
+// key, 16 lanes of 8 channels each -- and merges, for the g query heads of
+// h, the partial states with the new token's own term: score q_j . k (k and
+// v as the codes just written stand for them), l = 1, o = v.  That is the
+// log-sum-exp merge of the combine kernel with one more state, so the
+// result is the decode over the cache that holds the token.
+// 128 threads (one channel each) per query head, up to 8 heads at once
+// (more heads take further passes).  Everything that does not wait for the
+// new token -- the query channel, up to kU split states, the value-tile
+// dwords the token shares with older tokens -- is loaded first, so that the
+// step waits for memory about once.
+struct NewToken {
+  const void* k_new;   // [B][1][Hkv][d] of the cache dtype
+  const void* v_new;
+  int64_t pos;         // its position in the quantized cache
+};
+
+constexpr int kAppendPassHeads = 8;
+
+__global__ __launch_bounds__(128 * kAppendPassHeads) void dec_append_merge_kernel(DecodeArgs a,
+                                                                                  NewToken nt) {
+  __shared__ uint8_t kcode[kD], vcode[kD];
+  __shared__ float kdq[kD], vdq[kD];
+  __shared__ float red[2 * kAppendPassHeads];
+  const int tid = threadIdx.x, nthr = blockDim.x, wave = tid >> 6, lane = tid & 63;
+  const DevShape& sh = a.sh;
+  const int bh = blockIdx.x, b = bh / sh.Hkv, h = bh % sh.Hkv;
+  const int64_t p = nt.pos;
+  const int g = sh.g, hs = nthr >> 7, jj = tid >> 7, c = tid & (kD - 1);
+  const int S = a.n_partials;
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q) + ((int64_t)b * sh.Hq + (int64_t)h * g) * kD;
+
+  // ---- loads that do not wait for the new token ----------------------------------
+  const uint4 raw = wave < 2 && lane < 16
+      ? static_cast<const uint4*>(wave == 0 ? nt.v_new : nt.k_new)[(int64_t)bh * (kD / 8) + lane]
+      : uint4{0u, 0u, 0u, 0u};
+  float qv = elem2f(qg[(int64_t)jj * kD + c], sh.kv_bf16);
+  constexpr int kU = 16;   // split states per round trip
+  float m[kU], l[kU], o[kU];
+  const float* rec = partial_rec(a, b, h * g + jj, 0);
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const bool ok = u < S;
+    const float* pr = rec + (int64_t)(ok ? u : 0) * (kD + 2);
+    m[u] = ok ? pr[kD] : -INFINITY;
+    l[u] = ok ? pr[kD + 1] : 0.f;
+    o[u] = ok ? pr[c] : 0.f;
+  }
+  // value tile: the 32 * bits dwords of the lanes 16 q + i (i < 16) that hold token tau
+  const bool vtile = a.v.quant != KVQ_QUANT_NONE;
+  const int vbits = a.v.bits, tau = (int)(p & (kTile - 1)), tq = (tau & 15) >> 2;
+  uint32_t* tile_dw = reinterpret_cast<uint32_t*>(a.v.codes + tok_row(sh, b, h, p - tau) * a.v.row_bytes);
+  int tw[2];
+  uint32_t told[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = tid + k * nthr;
+    tw[k] = -1;
+    told[k] = 0u;
+    if (vtile && idx < 32 * vbits) {
+      const int i = idx / (2 * vbits), rem = idx - i * 2 * vbits;
+      tw[k] = (16 * tq + i) * (2 * vbits) + rem;
+      told[k] = tile_dw[tw[k]];
+    }
+  }
+
+  // ---- encode the token (waves 0 and 1), fold the first split states ----------------
+  if (wave < 2 && lane < 16) {
+    const bool val = wave == 0;
+    const DevTensor& t = val ? a.v : a.k;
+    const int j8 = lane;
+    float x[8], dq[8];
+    unpack8(raw, sh.kv_bf16, x);
+    if (t.quant == KVQ_QUANT_NONE) {
+      reinterpret_cast<uint4*>(t.codes)[tok_row(sh, b, h, p) * (kD / 8) + j8] = raw;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dq[e] = x[e];
+    } else if (!val && t.per_channel) {
+      // a per-channel key whose group stays open: the unquantized tail ring
+      reinterpret_cast<uint4*>(t.tail)[((int64_t)bh * t.tail_rows + p % t.tail_rows) * (kD / 8) + j8] = raw;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dq[e] = x[e];
+    } else {
+      void* prm = t.params ? static_cast<uint8_t*>(t.params) +
+                                 prm_rec(t, sh, b, h, p) * (t.quant == KVQ_QUANT_SYM_Q8_0 ? 2 : 4)
+                           : nullptr;
+      const uint2 cq = encode8(head_view(t, h), h, j8, x, prm, dq);
+      *reinterpret_cast<uint2*>(&(val ? vcode : kcode)[8 * j8]) = cq;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) (val ? vdq : kdq)[8 * j8 + e] = dq[e];
+  }
+  float M = -INFINITY, L = 0.f, O = 0.f;   // merged split states of head jj
+  auto fold = [&](const float* mu, const float* lu, const float* ou) {
+    float mc = M;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) mc = fmaxf(mc, mu[u]);
+    if (mc == -INFINITY) return;
+    const float r = M == -INFINITY ? 0.f : exp2f(M - mc);
+    L *= r;
+    O *= r;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float w = mu[u] == -INFINITY ? 0.f : exp2f(mu[u] - mc);
+      L = __builtin_fmaf(w, lu[u], L);
+      O = __builtin_fmaf(w, ou[u], O);
+    }
+    M = mc;
+  };
+  fold(m, l, o);
+  __syncthreads();
+
+  // ---- the token's codes into the cache layouts ------------------------------------
+  if (a.k.quant != KVQ_QUANT_NONE && !a.k.per_channel) {
+    uint32_t* row = reinterpret_cast<uint32_t*>(a.k.codes + tok_row(sh, b, h, p) * a.k.row_bytes);
+    for (int W = tid; W < 4 * a.k.bits; W += nthr) row[W] = k_row_dword(kcode, a.k.bits, W);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    if (tw[k] < 0) continue;
+    const int W = tw[k], Lw = W / (2 * vbits), sw = (W / vbits) & 1, j = W % vbits, i = Lw & 15;
+    uint32_t nb = 0, nm = 0;
+    seg_dword_fields(vbits, j, [&](int u, int shf, int wd, int field) {
+      const int mm = u >> 3, e = u & 7;
+      if ((e & 3) == (tau & 3) && (e >> 2) == (tau >> 4)) {   // token 4 tq + e or 16 + 4 tq + e - 4
+        nb |= field_value(vcode[16 * (4 * sw + mm) + i], field) << shf;
+        nm |= ((1u << wd) - 1u) << shf;
+      }
+    });
+    if (nm != 0) tile_dw[W] = (told[k] & ~nm) | nb;
+  }
+
+  // ---- per pass of up to 8 heads: the token's score, then the merge -------------
+  const float sm2 = a.sm_scale * 1.4426950408889634f;   // base-2 scores, as the decode kernels
+  const float kc = kdq[c], vc = vdq[c];
+  for (int j0 = 0; j0 < g; j0 += hs) {
+    const int j = j0 + jj;
+    const bool act = j < g;
+    if (j0 > 0) {
+      // a later pass: its query channel and split states
+      qv = act ? elem2f(qg[(int64_t)j * kD + c], sh.kv_bf16) : 0.f;
+      M = -INFINITY;
+      L = O = 0.f;
+      __syncthreads();   // the previous pass has read red
+    }
+    const float d = wave_sum(qv * kc);
+    if (lane == 0) red[wave] = d;
+    __syncthreads();
+    if (!act) continue;
+    const float* rj = partial_rec(a, b, h * g + j, 0);
+    for (int s0 = j0 > 0 ? 0 : kU; s0 < S; s0 += kU) {   // states beyond those folded
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const bool ok = s0 + u < S;
+        const float* pr = rj + (int64_t)(ok ? s0 + u : 0) * (kD + 2);
+        m[u] = ok ? pr[kD] : -INFINITY;
+        l[u] = ok ? pr[kD + 1] : 0.f;
+        o[u] = ok ? pr[c] : 0.f;
+      }
+      fold(m, l, o);
+    }
+    // the new token: m = its score, l = 1, o = its value
+    const float sn = (red[2 * jj] + red[2 * jj + 1]) * sm2;
+    const float mc = fmaxf(M, sn);
+    const float r = M == -INFINITY ? 0.f : exp2f(M - mc), wn = exp2f(sn - mc);
+    store_out(a, ((int64_t)b * sh.Hq + h * g + j) * kD + c,
+              __builtin_fmaf(wn, vc, O * r) / __builtin_fmaf(wn, 1.0f, L * r));
   }
 }
 
@@ -646,6 +832,14 @@ hipError_t launch_encode_kv(const DevShape& sh, const DevTensor& kt, const DevTe
   const int64_t tile0 = n_ctx / kTile, tile1 = (n_ctx + n_new - 1) / kTile;
   hipLaunchKernelGGL(enc_vtile_kernel, dim3((unsigned)(tile1 - tile0 + 1), sh.B * sh.Hkv),
                      dim3(256), 0, stream, sh, vt, v_new, n_ctx, n_new, tile0, tail);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_merge(const DecodeArgs& a, const void* k_new, const void* v_new,
+                               int64_t pos, hipStream_t stream) {
+  const int heads = a.sh.g < kAppendPassHeads ? a.sh.g : kAppendPassHeads;
+  hipLaunchKernelGGL(dec_append_merge_kernel, dim3((unsigned)(a.sh.B * a.sh.Hkv)),
+                     dim3(128 * heads), 0, stream, a, NewToken{k_new, v_new, pos});
   return hipGetLastError();
 }
 

@@ -390,7 +390,7 @@ int32_t kvq_prefill_kernel(const kvq_config* cfg) {
   return prefill_codes_supported(*cfg) ? KVQ_PREFILL_CODES : KVQ_PREFILL_STAGED;
 }
 
-int32_t kvq_abi_version(void) { return 111; }
+int32_t kvq_abi_version(void) { return 112; }
 
 kvq_status kvq_set_decode_events(void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr))
@@ -495,6 +495,59 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
                                     nullptr, 0);
 }
 
+namespace {
+// uniform quantizers, FP8 and raw storage: the formats whose one-token
+// append the merge launch encodes itself
+bool append_merge_format(const kvq_tensor_format& f) {
+  return f.quantizer == KVQ_QUANT_NONE || f.quantizer == KVQ_QUANT_ASYM_MINMAX ||
+         f.quantizer == KVQ_QUANT_ASYM_ABSMAX_OFFSET || f.quantizer == KVQ_QUANT_SYM_Q8_0 ||
+         f.quantizer == KVQ_QUANT_FP8_E5M2;
+}
+}  // namespace
+
+int32_t kvq_append_decode_fused(const kvq_config* cfg, int64_t n_ctx) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (n_ctx < 0 || n_ctx >= cfg->max_ctx)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "n_ctx must be in [0, max_ctx) for an append of one "
+                "token (got %lld)", (long long)n_ctx);
+  if (cfg->rope || n_ctx < cfg->sink_tokens) return 0;
+  if (!append_merge_format(cfg->k) || !append_merge_format(cfg->v)) return 0;
+  if (cfg->n_q_heads / cfg->n_kv_heads > kvq::kMaxAppendHeads) return 0;
+  if (cfg->k.layout == KVQ_LAYOUT_PER_CHANNEL) {
+    // the key must go to the tail: its group stays open after the append
+    const int64_t nq = n_ctx - cfg->sink_tokens, G = cfg->k.group_size;
+    if (nq / G != (nq + 1) / G) return 0;
+  }
+  return 1;
+}
+
+kvq_status kvq_append_decode(const kvq_config* cfg, kvq_cache* cache, const void* k_new,
+                             const void* v_new, const void* q, const int32_t* q_pos,
+                             float sm_scale, void* out, int32_t out_dtype, void* stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!cache) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (cache->n_ctx < 0 || cache->n_ctx > cfg->max_ctx)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "cache->n_ctx out of range");
+  if (cache->n_ctx + 1 > cfg->max_ctx)
+    return fail(KVQ_ERR_CAPACITY, "append of 1 token at n_ctx %lld exceeds max_ctx %lld",
+                (long long)cache->n_ctx, (long long)cfg->max_ctx);
+  const int32_t fused = kvq_append_decode_fused(cfg, cache->n_ctx);
+  if (fused < 0) return fused;
+  if (!fused) {
+    st = kvq_quantize_append(cfg, cache, k_new, v_new, 1, stream);
+    if (st != KVQ_OK) return st;
+    return kvq_decode_attention(cfg, cache, q, q_pos, sm_scale, out, out_dtype, stream);
+  }
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "k_new and v_new must be 16-byte aligned device pointers");
+  st = kvq::decode_attention_impl(cfg, cache, q, q_pos, sm_scale, out, out_dtype, stream, nullptr,
+                                  0, k_new, v_new);
+  if (st == KVQ_OK) cache->n_ctx += 1;
+  return st;
+}
+
 }  // extern "C"
 
 // One decode step (kvq_decode_attention).  partial_ws: the split-K partial
@@ -503,13 +556,15 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
 kvq_status kvq::decode_attention_impl(const kvq_config* cfg, const kvq_cache* cache,
                                       const void* q, const int32_t* q_pos, float sm_scale,
                                       void* out, int32_t out_dtype, void* stream,
-                                      float* partial_ws, uint64_t ws_bytes) {
+                                      float* partial_ws, uint64_t ws_bytes, const void* k_new,
+                                      const void* v_new) {
+  const bool fused = k_new != nullptr;
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
   if (!cache) return fail(KVQ_ERR_INVALID_ARGUMENT, "cache is NULL");
   if (!cache->base || !aligned16(cache->base))
     return fail(KVQ_ERR_INVALID_ARGUMENT, "cache->base must be a 16-byte aligned device pointer");
-  if (cache->n_ctx < 1 || cache->n_ctx > cfg->max_ctx)
+  if (cache->n_ctx < (fused ? 0 : 1) || cache->n_ctx > cfg->max_ctx - (fused ? 1 : 0))
     return fail(KVQ_ERR_INVALID_ARGUMENT, "n_ctx must be in [1, max_ctx] (got %lld): attention "
                 "over an empty cache is undefined", (long long)cache->n_ctx);
   st = check_codebooks(*cfg, *cache);
@@ -540,7 +595,7 @@ kvq_status kvq::decode_attention_impl(const kvq_config* cfg, const kvq_cache* ca
   const int n_sink = (int)(cache->n_ctx < L.sink ? cache->n_ctx : L.sink);
   a.n_ctx = (int)(cache->n_ctx - n_sink);
   a.pos0 = n_sink;
-  a.q_last = (int)cache->n_ctx - 1;
+  a.q_last = (int)cache->n_ctx - (fused ? 0 : 1);
   a.slot0 = 0;
   a.S_max = L.S_max;
   a.kp_groups = 0;
@@ -640,7 +695,7 @@ kvq_status kvq::decode_attention_impl(const kvq_config* cfg, const kvq_cache* ca
   // a streaming kernel writes the output itself only when its one split
   // holds every token; otherwise the partial states are merged
   a.n_partials = sa.n_partials = a.splits + sa.splits;
-  a.direct = sa.direct = a.n_partials == 1 ? 1 : 0;
+  a.direct = sa.direct = a.n_partials == 1 && !fused ? 1 : 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
@@ -659,8 +714,11 @@ kvq_status kvq::decode_attention_impl(const kvq_config* cfg, const kvq_cache* ca
     if (e == hipSuccess) e = hipEventRecord(ev1, s);
   }
   if (e == hipSuccess && n_sink > 0) e = launch_decode_generic(sa, s);
-  if (e == hipSuccess && !a.direct) e = launch_combine(a, s);
-  return device_status(e, "decode attention");
+  if (e == hipSuccess && fused)
+    e = launch_append_merge(a, k_new, v_new, a.n_ctx, s);
+  else if (e == hipSuccess && !a.direct)
+    e = launch_combine(a, s);
+  return device_status(e, fused ? "append and decode" : "decode attention");
 }
 
 extern "C" {

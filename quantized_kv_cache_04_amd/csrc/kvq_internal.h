@@ -15,6 +15,7 @@ constexpr int kCapAlign = 1024;    // token capacity granularity (a multiple of 
 constexpr int kMaxSink = 4096;     // attention-sink tokens kept raw per sequence
 constexpr int kSinkSplitTokens = 256;   // a split of the sink spans at least this many tokens
 constexpr int kMaxHeadsPH = 64;     // KV heads of a format with per-head group sizes
+constexpr int kMaxAppendHeads = 128;   // query heads per KV head of the fused append step
 
 // Host-side description of one cache tensor (keys or values) and where its
 // arrays sit in the allocation.
@@ -141,17 +142,26 @@ struct DecodeArgs {
 };
 
 // kvq_decode_attention with the split-K partial states in partial_ws
-// (ws_bytes) instead of the cache's workspace region when partial_ws is set
+// (ws_bytes) instead of the cache's workspace region when partial_ws is set.
+// With k_new and v_new (the fused step of kvq_append_decode), the decode
+// streams the cache->n_ctx cached tokens and the merge launch appends one
+// token per sequence and adds its term; the caller advances n_ctx.
 kvq_status decode_attention_impl(const kvq_config* cfg, const kvq_cache* cache, const void* q,
                                  const int32_t* q_pos, float sm_scale, void* out,
                                  int32_t out_dtype, void* stream, float* partial_ws,
-                                 uint64_t ws_bytes);
+                                 uint64_t ws_bytes, const void* k_new = nullptr,
+                                 const void* v_new = nullptr);
 // the error message of the calling thread (kvq_last_error)
 kvq_status set_error(kvq_status st, const char* msg);
 
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
 // merge of the split-K partials, the sink's included (when a.direct is 0)
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
+// One serving step's new token (kvq_append_decode): encode it at position
+// pos of the quantized cache and merge its attention term with the split
+// partial states of a (a.direct is 0; a.n_partials may be 0).
+hipError_t launch_append_merge(const DecodeArgs& a, const void* k_new, const void* v_new,
+                               int64_t pos, hipStream_t stream);
 // Whether the matrix-core kernel handles this configuration's formats.
 bool mfma_config_supported(const kvq_config& c);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);

@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvq.h")
 # interface version the structures below follow (major * 100 + minor)
-ABI_VERSION = 111
+ABI_VERSION = 112
 
 # ---- constants mirrored from kvq.h -------------------------------------------
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_DEVICE = 0, -1, -2, -3, -4
@@ -95,6 +95,12 @@ def lib() -> ctypes.CDLL:
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
         L.kvq_decode_attention_scratch.argtypes = L.kvq_decode_attention.argtypes
+        L.kvq_append_decode.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(CacheStruct),
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_void_p]
+        L.kvq_append_decode_fused.restype = ctypes.c_int32
+        L.kvq_append_decode_fused.argtypes = [ctypes.POINTER(Config), ctypes.c_int64]
         L.kvq_prefill_attention.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(CacheStruct),
                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
@@ -102,7 +108,7 @@ def lib() -> ctypes.CDLL:
         L.kvq_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.c_int32,
                                                   ctypes.c_int64, ctypes.POINTER(ctypes.c_uint64)]
         for fn in ("kvq_cache_bytes", "kvq_cache_layout", "kvq_quantize_append",
-                   "kvq_decode_attention", "kvq_decode_attention_scratch",
+                   "kvq_decode_attention", "kvq_decode_attention_scratch", "kvq_append_decode",
                    "kvq_prefill_attention", "kvq_prefill_workspace_bytes"):
             getattr(L, fn).restype = ctypes.c_int32
         L.kvq_last_error.restype = ctypes.c_char_p
@@ -308,6 +314,11 @@ class Cache:
         return decode_attention(self, q, q_pos=q_pos, sm_scale=sm_scale, out=out,
                                 out_dtype=out_dtype, stream=stream)
 
+    def append_decode(self, k_new, v_new, q, q_pos=None, sm_scale: float = 0.0, out=None,
+                      out_dtype: Optional[str] = None, stream=None):
+        return append_decode(self, k_new, v_new, q, q_pos=q_pos, sm_scale=sm_scale, out=out,
+                             out_dtype=out_dtype, stream=stream)
+
     def prefill(self, q, sm_scale: float = 0.0, out=None, out_dtype: Optional[str] = None,
                 stream=None, workspace=None):
         return prefill_attention(self, q, sm_scale=sm_scale, out=out, out_dtype=out_dtype,
@@ -366,6 +377,40 @@ def decode_attention(cache: Cache, q, q_pos=None, sm_scale: float = 0.0, out=Non
                                       q_pos.data_ptr() if q_pos is not None else None,
                                       float(sm_scale), out.data_ptr(), DTYPES[out_dtype],
                                       _stream_ptr(stream)))
+    return out
+
+
+def append_decode_fused(cfg: Config, n_ctx: int) -> bool:
+    """Whether append_decode on a cache of n_ctx tokens runs the fused step."""
+    r = lib().kvq_append_decode_fused(ctypes.byref(cfg), int(n_ctx))
+    if r < 0:
+        _check(r)
+    return bool(r)
+
+
+def append_decode(cache: Cache, k_new, v_new, q, q_pos=None, sm_scale: float = 0.0, out=None,
+                  out_dtype: Optional[str] = None, stream=None):
+    """One serving step: append k_new/v_new ([B, 1, Hkv, d]) and decode q
+    ([B, Hq, d]) over the cache that holds them (kvq_append_decode)."""
+    import torch
+    c = cache.cfg
+    kdt = _torch_dtype({F16: "f16", BF16: "bf16"}[c.kv_dtype])
+    tok_shape = (c.batch, 1, c.n_kv_heads, c.head_dim)
+    _check_tensor("k_new", k_new, tok_shape, kdt, device=False)
+    _check_tensor("v_new", v_new, tok_shape, kdt, device=False)
+    shape = (c.batch, c.n_q_heads, c.head_dim)
+    _check_tensor("q", q, shape, kdt, device=False)
+    if q_pos is not None:
+        _check_tensor("q_pos", q_pos, (c.batch,), torch.int32, device=False)
+    out, out_dtype = _resolve_out(out, out_dtype, shape, q.device)
+    _check_devices(k_new=k_new, v_new=v_new, q=q, q_pos=q_pos, out=out)
+    cs = cache.struct()
+    _check(lib().kvq_append_decode(ctypes.byref(cache.cfg), ctypes.byref(cs), k_new.data_ptr(),
+                                   v_new.data_ptr(), q.data_ptr(),
+                                   q_pos.data_ptr() if q_pos is not None else None,
+                                   float(sm_scale), out.data_ptr(), DTYPES[out_dtype],
+                                   _stream_ptr(stream)))
+    cache.n_ctx = int(cs.n_ctx)
     return out
 
 

@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
                           "kvq_decode_attention", "kvq_last_error", "kvq_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvq_abi_version() == kvq.ABI_VERSION == 111
+    assert L.kvq_abi_version() == kvq.ABI_VERSION == 112
 
 
 def _none_cfg(**kw):
@@ -322,6 +322,31 @@ def test_prefill_kernel_selection():
     bad = cfg(w5)
     bad.head_dim = 64
     assert kvq.lib().kvq_prefill_kernel(ctypes.byref(bad)) < 0
+
+
+def test_append_decode_fused_selection():
+    """kvq_append_decode fuses the append into the merge launch for the
+    uniform, FP8 and raw formats without RoPE, once the sink is full, and for
+    per-channel keys only while the key group stays open."""
+    from synth import make_workload
+    cfg = kvq.config_from_workload
+    fused = kvq.append_decode_fused
+    for cid in (1, 2, 3):
+        assert fused(cfg(make_workload(cid, ctx=512)), 100), cid
+    c5 = cfg(make_workload(5, batch=1, n_kv_heads=2, ctx=1024))   # per-channel keys, G = 128
+    assert fused(c5, 0) and fused(c5, 126) and fused(c5, 128)
+    assert not fused(c5, 127) and not fused(c5, 255)            # the append closes a group
+    assert not fused(cfg(make_workload(4, ctx=512)), 100)       # codebooks, outliers, RoPE
+    fp8 = dict(quantizer="fp8_e5m2", bits=8, group_size=0, layout="per_token", outlier_frac=0.0)
+    assert fused(cfg(make_workload(5, ctx=512, k=fp8, v=fp8)), 77)
+    c5s = cfg(make_workload(5, batch=1, n_kv_heads=2, ctx=1024), sink_tokens=40)
+    assert not fused(c5s, 39)                                   # the token goes to the sink
+    assert fused(c5s, 40) and not fused(c5s, 40 + 127) and fused(c5s, 40 + 128)
+    c1 = cfg(make_workload(1, ctx=512))
+    for bad in (-1, int(c1.max_ctx)):
+        with pytest.raises(kvq.KvqError) as ei:
+            fused(c1, bad)
+        assert ei.value.status == kvq.ERR_INVALID_ARGUMENT
 
 
 def test_decode_path_selection():

@@ -1,0 +1,138 @@
+"""GPU parity of the serving step kvq_append_decode (append one token per
+sequence, then decode over the cache that holds it), through the C ABI.
+
+Each case builds a cache of n0 tokens and then takes one-token steps, each
+with append_decode on one cache and with append followed by decode on a
+second cache built the same way.  At every step the fused step's output
+must match the oracle's float64 attention over the dequantized cache of the
+tokens so far (max-abs <= 2e-3, relative L2 <= 1e-3) and the two-call
+output to relative L2 <= 1e-4 (the two compute the new token's term in a
+different order of rounding; a token left out or counted twice moves the
+output by about 1 / n_ctx).  After the last step both caches must hold the
+oracle's bytes exactly.
+
+The cases start from an empty cache, run steps where the fused launch
+does not apply (a per-channel key group that the append closes, tokens
+that go to the attention sink) between fused ones, and cover every format
+family the fused launch encodes: 4-bit min-max with per-channel keys
+(windows included), q8_0, 3-bit absmax-offset, FP8 E5M2, group sizes per
+head, a paged cache and bf16 caches.
+"""
+import numpy as np
+import pytest
+import torch
+
+from synth import make_inputs, make_page_table, make_workload
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from parity import (MAX_ABS, REL_L2, attention_errors, compare_regions, gpu_cache,  # noqa: E402
+                    oracle_attention, oracle_encode)
+from quantized_kv_cache_04_amd import kvq  # noqa: E402
+
+FP8 = dict(quantizer="fp8_e5m2", bits=8, group_size=0, layout="per_token", outlier_frac=0.0)
+TWO_CALL_REL = 1e-4
+
+
+def _kwin(q, bits, G, overlap):
+    return dict(quantizer=q, bits=bits, group_size=G, layout="per_channel", outlier_frac=0.0,
+                window_overlap=overlap)
+
+
+def _heads(q, bits, sizes):
+    return dict(quantizer=q, bits=bits, group_size=0, layout="per_token", outlier_frac=0.0,
+                head_group_size=list(sizes))
+
+
+# (name, config, sizes and formats, cached tokens n0, sink, paged)
+# the steps run from n0 to the workload's ctx
+CASES = [
+    ("tiny_u4_groups_of_64", 1, dict(ctx=140), 100, 0, False),       # closes the group at 128
+    ("q8_0_gqa8", 2, dict(ctx=300), 288, 0, False),
+    ("u3_bf16", 3, dict(batch=2, n_kv_heads=2, ctx=200), 161, 0, False),
+    ("serving", 5, dict(batch=3, n_kv_heads=2, ctx=300), 250, 0, False),   # closes 256
+    ("serving_from_empty", 5, dict(batch=2, n_kv_heads=2, ctx=36), 0, 0, False),
+    ("serving_sink", 5, dict(batch=2, n_kv_heads=2, ctx=70), 30, 40, False),
+    ("serving_paged", 5, dict(batch=2, n_kv_heads=2, ctx=300), 240, 0, True),
+    ("serving_bf16", 5, dict(batch=2, n_kv_heads=2, ctx=100, kv_dtype="bf16"), 60, 0, False),
+    ("fp8", 5, dict(batch=2, n_kv_heads=2, ctx=180, k=FP8, v=FP8), 150, 0, False),
+    ("turboquant_windows", 5, dict(batch=2, n_kv_heads=2, ctx=400,
+                                   k=_kwin("asym_absmax_offset", 4, 192, 64)), 370, 0, False),
+    ("heads_u3", 3, dict(batch=2, n_kv_heads=2, ctx=220,
+                         k=_heads("asym_absmax_offset", 3, [32, 64]),
+                         v=_heads("asym_absmax_offset", 3, [32, 64])), 190, 0, False),
+]
+
+
+def _query(q, i):
+    """The query of step i: the base query rotated along the channels."""
+    return torch.roll(q, shifts=3 * i, dims=2).contiguous()
+
+
+@pytest.mark.parametrize("name,cfg_id,over,n0,sink,paged", CASES, ids=[c[0] for c in CASES])
+def test_append_decode_steps(name, cfg_id, over, n0, sink, paged):
+    print(f"[append_decode] case={name} cfg={cfg_id} over={over} n0={n0} sink={sink} "
+          f"paged={paged}", flush=True)
+    w = make_workload(cfg_id, **over)
+    inputs = make_inputs(w, "cpu")
+    max_ctx = w.ctx + 7
+    table, n_pages = None, 0
+    if paged:
+        n_pages = w.batch * ((max_ctx + 31) // 32) + 5
+        table = make_page_table(w, max_ctx, n_pages)
+    chunks = [n0] if n0 else []
+    fused_c = gpu_cache(w, inputs, chunks, max_ctx, sink=sink, page_table=table, n_pages=n_pages)
+    two_c = gpu_cache(w, inputs, chunks, max_ctx, sink=sink, page_table=table, n_pages=n_pages)
+    kd, vd, q0 = inputs["k"].cuda(), inputs["v"].cuda(), inputs["q"].cuda()
+    kinds = []
+    for t in range(n0, w.ctx):
+        kn, vn = kd[:, t:t + 1].contiguous(), vd[:, t:t + 1].contiguous()
+        q = _query(q0, t)
+        kinds.append(kvq.append_decode_fused(fused_c.cfg, t))
+        out = fused_c.append_decode(kn, vn, q)
+        two_c.append(kn, vn)
+        out2 = two_c.decode(q)
+        assert fused_c.n_ctx == two_c.n_ctx == t + 1
+        o, o2 = out.cpu().numpy(), out2.cpu().numpy()
+        _, kdeq, vdeq = oracle_encode(w, inputs, t + 1, max_ctx, sink=sink)
+        ref = oracle_attention(w, q.cpu(), kdeq, vdeq, t + 1)
+        ma, rel = attention_errors(o, ref)
+        _, rel2 = attention_errors(o, o2.astype(np.float64))
+        assert ma <= MAX_ABS and rel <= REL_L2, (t, kinds[-1], ma, rel)
+        assert rel2 <= TWO_CALL_REL, (t, kinds[-1], rel2)
+    print(f"[append_decode] {name}: {sum(kinds)} fused steps of {len(kinds)}", flush=True)
+    assert any(kinds)
+    exp, _, _ = oracle_encode(w, inputs, w.ctx, max_ctx, sink=sink, page_table=table,
+                              n_pages=n_pages)
+    for cache in (fused_c, two_c):
+        bad = compare_regions(cache, exp)
+        assert not bad, "\n".join(bad)
+
+
+@pytest.mark.parametrize("odt", ["f16", "bf16"])
+def test_half_outputs(odt):
+    """Half outputs of the fused step are its f32 outputs rounded."""
+    w = make_workload(5, batch=2, n_kv_heads=2, ctx=100)
+    inputs = make_inputs(w, "cpu")
+    caches = [gpu_cache(w, inputs, [99], 107) for _ in range(2)]
+    kn = inputs["k"][:, 99:100].contiguous().cuda()
+    vn = inputs["v"][:, 99:100].contiguous().cuda()
+    q = inputs["q"].cuda()
+    o32 = caches[0].append_decode(kn, vn, q)
+    oh = caches[1].append_decode(kn, vn, q, out_dtype=odt)
+    want = o32.to(torch.float16 if odt == "f16" else torch.bfloat16)
+    assert torch.equal(oh, want)
+
+
+def test_capacity_is_checked_before_any_launch():
+    w = make_workload(1, ctx=64)
+    inputs = make_inputs(w, "cpu")
+    cache = gpu_cache(w, inputs, [64], 64)
+    cache.n_ctx = int(cache.cfg.max_ctx)        # a full cache
+    kn = inputs["k"][:, :1].contiguous().cuda()
+    with pytest.raises(kvq.KvqError) as ei:
+        cache.append_decode(kn, kn, inputs["q"].cuda())
+    assert ei.value.status == kvq.ERR_CAPACITY

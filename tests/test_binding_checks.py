@@ -76,3 +76,23 @@ def test_prefill_query_out_workspace():
         c.prefill(q, workspace=torch.empty(64, dtype=torch.float32))
     with pytest.raises(ValueError, match="device"):
         c.prefill(q, workspace=torch.empty(0, dtype=torch.uint8))
+
+
+def test_append_decode_arguments():
+    c = _cache()
+    tok = torch.zeros(2, 1, 2, 128, dtype=torch.float16)
+    q = torch.zeros(2, 8, 128, dtype=torch.float16)
+    with pytest.raises(ValueError, match="shape"):
+        c.append_decode(torch.zeros(2, 2, 2, 128, dtype=torch.float16), tok, q)   # two tokens
+    with pytest.raises(ValueError, match="shape"):
+        c.append_decode(tok, tok, torch.zeros(2, 2, 128, dtype=torch.float16))
+    with pytest.raises(TypeError, match="dtype"):
+        c.append_decode(tok, tok.bfloat16(), q)
+    with pytest.raises(ValueError, match="contiguous"):
+        c.append_decode(tok, torch.zeros(2, 1, 2, 256, dtype=torch.float16)[..., :128], q)
+    with pytest.raises(TypeError, match="out_dtype"):
+        c.append_decode(tok, tok, q, out=torch.empty(2, 8, 128, dtype=torch.float16),
+                        out_dtype="f32")
+    with pytest.raises(ValueError, match="device"):
+        c.append_decode(tok, tok, q)
+    assert c.n_ctx == 0

@@ -7,7 +7,10 @@
 // log-sum-exp weights (dec_combine_kernel).  Keeping the merge in its own
 // launch avoids device-scope fences in the streaming kernel: on a GPU whose
 // L2 is split across chiplets such a fence writes back and invalidates the
-// whole L2 of the chiplet.
+// whole L2 of the chiplet.  (Merging in the last workgroup of each
+// sequence and KV head measured slower both with a fence per workgroup and
+// with the partial states stored and read at device scope, past the L2s:
+// each workgroup then waits for its stores before it may count itself.)
 #pragma once
 
 #include "device_common.h"

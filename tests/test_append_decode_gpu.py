@@ -11,8 +11,8 @@ different order of rounding; a token left out or counted twice moves the
 output by about 1 / n_ctx).  After the last step both caches must hold the
 oracle's bytes exactly.
 
-The cases start from an empty cache, run steps where the fused launch
-does not apply (a per-channel key group that the append closes, tokens
+The cases start from an empty cache, reach 32 split states per head and
+16 query heads per KV head, run steps where the fused launch does not apply (a per-channel key group that the append closes, tokens
 that go to the attention sink) between fused ones, and cover every format
 family the fused launch encodes: 4-bit min-max with per-channel keys
 (windows included), q8_0, 3-bit absmax-offset, FP8 E5M2, group sizes per
@@ -64,6 +64,11 @@ CASES = [
     ("heads_u3", 3, dict(batch=2, n_kv_heads=2, ctx=220,
                          k=_heads("asym_absmax_offset", 3, [32, 64]),
                          v=_heads("asym_absmax_offset", 3, [32, 64])), 190, 0, False),
+    # 32 split states per head (the merge reads them in two rounds of 16)
+    ("q8_0_32_splits", 2, dict(ctx=8200), 8192, 0, False),
+    # 16 query heads per KV head (two passes of 8; the general decode
+    # kernel) with 32 split states each
+    ("gqa16_32_splits", 2, dict(ctx=8199, gqa=16, n_kv_heads=1), 8192, 0, False),
 ]
 
 

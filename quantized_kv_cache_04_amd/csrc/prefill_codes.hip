@@ -73,7 +73,8 @@ __global__ __launch_bounds__(256, 2) void pre_codes_kernel(PrefillArgs a) {
   // byte codes (q8_0, FP8): the waves share the unpacking of the blocks that
   // every row of the workgroup sees whole.  (Shared 4-bit unpacking was
   // slower, 22.3 against 20.5 ms on the serving shape: there the barrier per
-  // block and the LDS round trip cost more than the masks they save; for byte
+  // block and the LDS round trip cost more than the masks they save, and so
+  // they did for 3-bit codes, 359 -> 340 TFLOP/s on the config-3 shape; for byte
   // codes the per-wave loads and byte permutes cost more: FP8 403 -> 519
   // TFLOP/s, q8_0 260 -> 278.)
   constexpr bool SHARE = KB == 8 && VB == 8;

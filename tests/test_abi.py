@@ -241,6 +241,30 @@ def test_decode_errors_before_launch():
         kvq.ERR_INVALID_ARGUMENT
 
 
+def _append_decode(cfg, cs, k, v, q, out, odt=kvq.F32):
+    return kvq.lib().kvq_append_decode(ctypes.byref(cfg), ctypes.byref(cs), k, v, q, None, 0.0,
+                                       out, odt, None)
+
+
+def test_append_decode_errors_before_launch():
+    cfg = _none_cfg(max_ctx=100)          # raw storage: a step that fuses
+    assert kvq.append_decode_fused(cfg, 10)
+    full = kvq.CacheStruct(FAKE, None, None, 100)
+    assert _append_decode(cfg, full, FAKE, FAKE, FAKE, FAKE) == kvq.ERR_CAPACITY
+    assert full.n_ctx == 100
+    ok = kvq.CacheStruct(FAKE, None, None, 10)
+    assert _append_decode(cfg, ok, None, FAKE, FAKE, FAKE) == kvq.ERR_INVALID_ARGUMENT
+    assert _append_decode(cfg, ok, FAKE, FAKE + 4, FAKE, FAKE) == kvq.ERR_INVALID_ARGUMENT
+    assert _append_decode(cfg, ok, FAKE, FAKE, FAKE + 8, FAKE) == kvq.ERR_INVALID_ARGUMENT
+    assert _append_decode(cfg, ok, FAKE, FAKE, FAKE, None) == kvq.ERR_INVALID_ARGUMENT
+    assert _append_decode(cfg, ok, FAKE, FAKE, FAKE, FAKE, odt=7) == kvq.ERR_INVALID_ARGUMENT
+    assert _append_decode(cfg, kvq.CacheStruct(None, None, None, 10), FAKE, FAKE, FAKE, FAKE) == \
+        kvq.ERR_INVALID_ARGUMENT
+    assert ok.n_ctx == 10                 # state unchanged by every refusal
+    assert kvq.lib().kvq_append_decode(ctypes.byref(cfg), None, FAKE, FAKE, FAKE, None, 0.0, FAKE,
+                                       kvq.F32, None) == kvq.ERR_INVALID_ARGUMENT
+
+
 def _prefill(cfg, cs, q, n_q, out, odt=kvq.F32, ws=None, ws_bytes=0):
     return kvq.lib().kvq_prefill_attention(ctypes.byref(cfg), ctypes.byref(cs), q, n_q, 0.0, out,
                                            odt, ws, ws_bytes, None)

@@ -89,6 +89,49 @@ def test_full_size_sampled_slices(cfg_id, ctx, slices):
         assert ma <= MAX_ABS and rel <= REL_L2, (b, h, ma, rel)
 
 
+def test_full_size_serving_steps():
+    """The step bench.py times, at the serving workload's full size: a cache
+    of 65,535 tokens, then two kvq_append_decode steps -- the first closes a
+    per-channel key group (append, then decode), the second fuses.  Sampled
+    slices' bytes and the second step's attention against the oracle."""
+    w = make_workload(5, ctx=65537)
+    print(f"[fullsize] serving steps B={w.batch} Hkv={w.n_kv_heads} T={w.ctx}", flush=True)
+    extra = 7
+    inputs = make_inputs(w, "cuda")
+    cfg = kvq.config_from_workload(w, max_ctx=w.ctx + extra)
+    cache = kvq.Cache(cfg, device="cuda")
+    n0 = w.ctx - 2
+    cache.append(inputs["k"][:, :n0].contiguous(), inputs["v"][:, :n0].contiguous())
+    assert [kvq.append_decode_fused(cfg, n) for n in (n0, n0 + 1)] == [False, True]
+    for t in (n0, n0 + 1):
+        out = cache.append_decode(inputs["k"][:, t:t + 1].contiguous(),
+                                  inputs["v"][:, t:t + 1].contiguous(), inputs["q"])
+    torch.cuda.synchronize()
+    assert cache.n_ctx == w.ctx
+    g = w.gqa
+    for b, h in [(0, 0), (9, 3), (15, 7)]:
+        enc = {}
+        for name, fmt in (("k", w.k), ("v", w.v)):
+            x = to_np32(inputs[name][b:b + 1, :, h:h + 1, :])
+            enc[name] = oq.encode_tensor(x, fmt, None)
+            exp = olay.expected_regions(fmt, enc[name], batch=1, n_kv_heads=1, n_ctx=w.ctx,
+                                        max_ctx=w.ctx + extra, kv_dtype=w.kv_dtype,
+                                        is_key=(name == "k"))
+            for reg, arr in exp.items():
+                got = _slice_bytes(cache, w, name, reg, b, h)
+                want = _as_bytes(arr)
+                diff = np.nonzero(got != want)[0]
+                assert got.shape == want.shape and diff.size == 0, \
+                    f"{name}.{reg} of slice ({b}, {h}): {diff.size} bytes differ"
+        q = to_np32(inputs["q"][b:b + 1, h * g:(h + 1) * g])
+        ref = oatt.decode_attention(q, enc["k"]["deq"], enc["v"]["deq"], n_ctx=w.ctx)
+        got = out[b:b + 1, h * g:(h + 1) * g].cpu().numpy()
+        ma, rel = attention_errors(got, ref)
+        print(f"[fullsize] serving step slice=({b},{h}) max_abs={ma:.2e} rel_l2={rel:.2e}",
+              flush=True)
+        assert ma <= MAX_ABS and rel <= REL_L2, (b, h, ma, rel)
+
+
 def test_full_size_codebook_workload():
     """KVQuant-shaped layer: 32 heads, 131072 tokens, codebooks, 1% outliers, RoPE."""
     w = make_workload(4)

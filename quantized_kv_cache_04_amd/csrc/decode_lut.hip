@@ -105,15 +105,26 @@ __global__ __launch_bounds__(256, 3) void dec_lut_kernel(DecodeArgs a) {
 
   // ---- tables ------------------------------------------------------------------
   if (head_ok) {
-    // key centroids: the head's [128][16] fp16 block, copied as dwords
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(K.codebook) + (int64_t)h * kD * 8;
-    uint32_t* dst = reinterpret_cast<uint32_t*>(&S.kt[wave][0][0]);
-    for (int i = lane; i < kD * 8; i += 64) dst[i] = src[i];
-    // value centroids of channels lane and lane + 64, interleaved per index
-    const uint16_t* vc = V.codebook + (int64_t)h * kD * 16;
+    // key centroids: the head's [128][16] fp16 block (4 KB), four 16-byte
+    // loads a lane, all issued before the first LDS write
+    const u32x4* src = reinterpret_cast<const u32x4*>(K.codebook) + (int64_t)h * kD * 2;
+    u32x4* dst = reinterpret_cast<u32x4*>(&S.kt[wave][0][0]);
+    u32x4 kcb[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      S.vt[wave][e][lane] = (uint32_t)vc[lane * 16 + e] | ((uint32_t)vc[(lane + 64) * 16 + e] << 16);
+    for (int k = 0; k < 4; ++k) kcb[k] = src[64 * k + lane];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dst[64 * k + lane] = kcb[k];
+    // value centroids of channels lane and lane + 64 (32 bytes each, two
+    // 16-byte loads), interleaved per index: dword e = C_lane[e] | C_lane+64[e] << 16
+    const u32x4* vc = reinterpret_cast<const u32x4*>(V.codebook) + (int64_t)h * kD * 2;
+    const u32x4 va[2] = {vc[2 * lane], vc[2 * lane + 1]};
+    const u32x4 vb[2] = {vc[2 * (lane + 64)], vc[2 * (lane + 64) + 1]};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t x = va[k >> 2][k & 3], y = vb[k >> 2][k & 3];   // indices 2k, 2k + 1
+      S.vt[wave][2 * k][lane] = __builtin_amdgcn_perm(y, x, 0x05040100u);
+      S.vt[wave][2 * k + 1][lane] = __builtin_amdgcn_perm(y, x, 0x07060302u);
+    }
   }
   // thread (head qw, pair qi) owns one query pair: q * sm_scale * log2(e)
   const int qw = tid >> 6, qi = tid & 63, qh = hg * kHeads + qw;

@@ -131,10 +131,19 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
   const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
                        ((int64_t)b * a.sh.Hq + h * g + (head_ok ? j : 0)) * kD + 8 * q4;
   {
+    // 4 elements a thread (256 threads); every load is issued before the
+    // first LDS write (rows j >= g read row g - 1 and store zeros)
     const uint16_t* qg = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.sh.Hq + h * g) * kD;
-    for (int idx = threadIdx.x; idx < 8 * kD; idx += blockDim.x) {
-      const int jj = idx / kD, c = idx % kD;
-      q_lds[jj][c] = jj < g ? elem2f(qg[jj * kD + c], a.sh.kv_bf16) : 0.0f;
+    uint16_t qe[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = threadIdx.x + 256 * k, jj = idx / kD, c = idx % kD;
+      qe[k] = qg[min(jj, g - 1) * kD + c];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = threadIdx.x + 256 * k, jj = idx / kD, c = idx % kD;
+      q_lds[jj][c] = jj < g ? elem2f(qe[k], a.sh.kv_bf16) : 0.0f;
     }
   }
   __syncthreads();
@@ -206,11 +215,13 @@ __global__ __launch_bounds__(256) void dec_mfma_kernel(DecodeArgs a) {
     const u32x4* src = reinterpret_cast<const u32x4*>(kgrp_base + (int64_t)g0 * kD);
     const int n4 = ng * 32;
     for (int c0 = 0; c0 < n4; c0 += 256) {
+      // unconditional loads (indices clamped into the staged groups), so that
+      // all four are in flight at once
       u32x4 v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int c = c0 + u * 64 + lane;
-        if (c < n4) v[u] = src[(c >> 5) * 128 + (c & 31)];   // group g0 + 4 (c / 32)
+        const int c = min(c0 + u * 64 + lane, n4 - 1);
+        v[u] = src[(c >> 5) * 128 + (c & 31)];   // group g0 + 4 (c / 32)
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
